@@ -1,0 +1,23 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP library through its Python binding, on cuda:0."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import matrix_aware_optimizers_amd as mao
+    mao.load()
+    return mao
