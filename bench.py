@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Optimizer-step benchmark on one MI355X.
+
+Default workload: one Muon step (momentum, 5 Newton-Schulz quintic iterations
+in bf16 MFMA with fp32 accumulation, sqrt(m/n)-scaled update with decoupled
+weight decay) over the weight matrices of one Llama-style 8B layer -- QKV
+4096x6144, O 4096x4096, gate 14336x4096, up 14336x4096, down 4096x14336 -- in
+one grouped call (one launch per Newton-Schulz stage for the whole layer).
+bf16 weights and gradients, fp32 momentum, synthetic seeded gradients
+(Gaussian plus a rank-16 component), a ring of two gradients per matrix so
+every step reads fresh data. Inputs are resident in HBM before timing.
+
+Prints one JSON line: steps/s of the whole job, the dominant kernel's
+roofline (the Newton-Schulz contraction, from HIP events around every launch
+inside the timed region) and the fp64 CPU oracle's rate on a bounded sample.
+
+Other workloads (--workload): moe (128-expert bank, batched Muon+), c1
+(256x512 fp32 Muon and SOAP), soap8b (the 8B layer under SOAP), foam760m
+(GPT-2-760M-shaped set under FOAM plus the AdamW embedding).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "optimizer steps/sec on 8B-layer matrix set; NS+rotation GEMM MFMA % of peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def ns_alg_flops(m: int, n: int, k: int = 5) -> float:
+    """Algorithmic flops of k quintic iterations on an m x n matrix (symmetric
+    products at half cost): per iteration a^2 b (X X^T) + a^3 (A A) + 2 a^2 b
+    (B X), a = min, b = max."""
+    a, b = min(m, n), max(m, n)
+    return k * (3.0 * a * a * b + a ** 3)
+
+
+# ---------------------------------------------------------------------------
+# Muon workloads
+# ---------------------------------------------------------------------------
+
+class MuonWorkload:
+    def __init__(self, groups_spec, dtype="bf16", norm_mode="none", seed_config="c2"):
+        import torch
+
+        import matrix_aware_optimizers_amd as mao
+        import synth
+        self.mao = mao
+        self.lib = mao.load()
+        self.hp = mao.muon_hparams(lr=1e-3, mu=0.95, weight_decay=0.1, eps=1e-7, ns_steps=5,
+                                   ns_dtype="bf16", norm_mode=norm_mode)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.tensors = []
+        self.shapes = []
+        for name, specs in groups_spec:
+            cnt = len(specs)
+            m, n = specs[0].rows, specs[0].cols
+            self.shapes.append((cnt, m, n))
+            W = torch.empty((cnt, m, n), dtype=tdt, device="cuda")
+            Gs = [torch.empty((cnt, m, n), dtype=tdt, device="cuda") for _ in range(2)]
+            for b, sp in enumerate(specs):
+                W[b].copy_(torch.from_numpy(synth.init_weight(seed_config, sp)))
+                for k in range(2):
+                    Gs[k][b].copy_(torch.from_numpy(synth.gradient(seed_config, sp, k + 1)))
+            M = torch.zeros((cnt, m, n), dtype=torch.float32, device="cuda")
+            self.tensors.append((W, Gs, M))
+        ng = len(self.tensors)
+        self.ng = ng
+        self.Ws = (mao.Batch * ng)(*[mao.batch(W) for W, _, _ in self.tensors])
+        self.Ms = (mao.Batch * ng)(*[mao.batch(M) for _, _, M in self.tensors])
+        self.Gs = [(mao.Batch * ng)(*[mao.batch(Gs[k]) for _, Gs, _ in self.tensors])
+                   for k in range(2)]
+        need = self.lib.muon_batched_workspace_size(ng, self.Ws, ctypes.byref(self.hp))
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+
+    def step(self, i: int):
+        st = self.lib.muon_step_batched(self.ng, self.Ws, self.Gs[i % 2], self.Ms,
+                                        ctypes.byref(self.hp), ctypes.c_void_p(self.ws.data_ptr()),
+                                        self.ws.numel(), None, self.stream)
+        if st != 0:
+            self.mao._check(st, "muon_step_batched")
+
+    def ns_flops(self) -> float:
+        return sum(c * ns_alg_flops(m, n) for c, m, n in self.shapes)
+
+
+def llama8b_groups():
+    import synth
+    return [(s.name, [s]) for s in synth.specs("c2")]
+
+
+def moe_groups():
+    import synth
+    sp = synth.specs("c4")
+    out = []
+    for j, name in enumerate(("gate", "up", "down")):
+        out.append((name, [s for s in sp if s.name.endswith("." + name)]))
+    return out
+
+
+def cpu_baseline_muon(sample_rows: int, sample_cols: int, total_ns_flops: float,
+                      seed_config: str, spec_index: int):
+    """The oracle (fp64, NumPy) on one matrix of the set, scaled to the whole
+    step by Newton-Schulz flops."""
+    import oracle
+    import synth
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((d.get("num_threads", 1) for d in info), default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    spec = synth.MatrixSpec("sample", sample_rows, sample_cols, spec_index)
+    w = synth.bf16_round(synth.init_weight(seed_config, spec)).astype(np.float64)
+    g = synth.bf16_round(synth.gradient(seed_config, spec, 1)).astype(np.float64)
+    mom = np.zeros_like(w)
+    t0 = time.perf_counter()
+    oracle.muon_step(w, g, mom, lr=1e-3, mu=0.95, weight_decay=0.1, ns_steps=5)
+    dt = time.perf_counter() - t0
+    scale = total_ns_flops / ns_alg_flops(sample_rows, sample_cols)
+    return {"value": 1.0 / (dt * scale), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"one fp64 Muon step (5 iterations) of the {sample_rows}x{sample_cols} "
+                       f"matrix took {dt:.2f} s; scaled by Newton-Schulz flops "
+                       f"(x{scale:.2f}) to the whole set")}
+
+
+def run_muon(args, workload_name, groups, norm_mode, sample):
+    import torch
+
+    import matrix_aware_optimizers_amd as mao
+    log(f"setting up {workload_name}")
+    wl = MuonWorkload(groups, norm_mode=norm_mode, seed_config=sample[2])
+    log("warmup")
+    for i in range(args.warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    mao.timing_collect()
+    mao.timing_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        wl.step(args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    mao.timing_enable(False)
+    tim = mao.timing_collect()
+    ms = start.elapsed_time(end) / args.steps
+    ns_ms = sum(tim[k][0] for k in ("ns_gram", "ns_square", "ns_apply"))
+    ns_cnt = sum(tim[k][1] for k in ("ns_gram", "ns_square", "ns_apply"))
+    ns_fl = sum(tim[k][2] for k in ("ns_gram", "ns_square", "ns_apply"))
+    achieved = ns_fl / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
+    log(f"{ms:.3f} ms/step; NS launches {ns_cnt}, {ns_ms / max(ns_cnt, 1):.3f} ms avg, "
+        f"{achieved:.1f} TFLOP/s")
+    per_tag = {k: {"ms_total": round(v[0], 4), "launches": v[1],
+                   "tflops": round(v[2] / (v[0] * 1e-3) / 1e12, 2) if v[0] > 0 else 0.0}
+               for k, v in tim.items() if v[1] > 0}
+    line = {
+        "metric": METRIC,
+        "value": 1000.0 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload_name,
+                   "matrices": [f"{c}x{m}x{n}" for c, m, n in wl.shapes],
+                   "ns_steps": 5, "ns_dtype": "bf16", "norm_mode": norm_mode,
+                   "weights": "bf16", "momentum": "fp32"},
+        "step_tflops_alg": wl.ns_flops() / (ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "gemm_nt_kernel (Newton-Schulz X X^T, A A, B X)",
+                     "launches": ns_cnt, "avg_launch_ms": ns_ms / max(ns_cnt, 1),
+                     "alg_tflop_per_launch": ns_fl / max(ns_cnt, 1) / 1e12},
+        "kernels": per_tag,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline_muon(sample[0], sample[1], wl.ns_flops(), sample[2],
+                                                 sample[3])
+    return line
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b",
+                    choices=["llama8b", "moe"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build's step runs whole matrices on one device "
+              "and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "llama8b":
+        line = run_muon(args, "llama8b_layer_muon_bf16", llama8b_groups(), "none",
+                        (4096, 4096, "c2", 1))
+    else:
+        line = run_muon(args, "moe128_expert_bank_muonplus_bf16", moe_groups(), "col_row",
+                        (1536, 2048, "c4", 0))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,332 @@
+/*
+ * mao.h -- C ABI of the matrix-aware optimizer step library (libmao.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call advances one weight matrix (or a group of same-shape matrices) by
+ * one optimizer step, entirely on the GPU, asynchronously on the caller's HIP
+ * stream. Sources for every operation are cited at the entry point, by page
+ * title and section:
+ *
+ *   [SMB]  "SOAP, Muon, and Beyond" review (dimensionstp.github.io)
+ *   [PX]   picx.dev summary of the same paper (numbered equations)
+ *   [FOAM] "Factored One-sided Adam-Moment for Practical and Scalable SOAP"
+ *          review
+ *   [M+]   "Muon+: Towards Better Muon via One Additional Normalization Step"
+ *          (gist.science)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Matrices are row-major device views: element (i, j) of a mao_mat lives at
+ *   data + i*ld + j (in elements of its dtype); ld >= cols, ld a multiple of
+ *   8, data 16-byte aligned. A strided view (ld > cols) lets a caller step a
+ *   logical sub-matrix of a fused tensor, e.g. one of Q, K, V inside a fused
+ *   QKV weight ([SMB] section 3-2 (2): fused QKV is split into logical
+ *   matrices before orthogonalisation).
+ * - Ownership: the caller owns every buffer (weights, gradients, optimizer
+ *   state, workspace, outputs). The library allocates no device memory and
+ *   keeps no device state between calls. Sizes of the workspace come from the
+ *   *_workspace_size queries; the workspace must be 256-byte aligned. The
+ *   caller supplies the 1-based step counter t.
+ * - Updates are in place: W and the state buffers are overwritten; G is
+ *   read-only.
+ * - Errors: every entry point validates all arguments on the host before it
+ *   enqueues anything and returns a mao_status; an invalid call enqueues
+ *   nothing. mao_last_error() gives a thread-local message for the last
+ *   failure. A failed kernel launch returns MAO_E_HIP; faults inside kernels
+ *   surface at the caller's next synchronisation, as for any HIP work.
+ * - No call synchronises the device or the stream, and none allocates; all
+ *   work runs on `stream` (a hipStream_t; NULL = the null stream). Results are
+ *   deterministic: the same inputs on the same stream order give bitwise the
+ *   same outputs (no floating-point atomics).
+ * - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MAO_H
+#define MAO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MAO_API __attribute__((visibility("default")))
+#else
+#define MAO_API
+#endif
+
+#define MAO_ABI_VERSION 1
+#define MAO_MAX_GROUPS 8
+
+typedef enum {
+  MAO_OK = 0,
+  MAO_E_NULL = 1,        /* a required pointer is NULL */
+  MAO_E_SHAPE = 2,       /* sizes < 1, or shapes that do not agree */
+  MAO_E_DTYPE = 3,       /* unsupported dtype for that argument */
+  MAO_E_LAYOUT = 4,      /* ld < cols, ld not a multiple of 8, misaligned */
+  MAO_E_ALIAS = 5,       /* two buffers that must be distinct overlap */
+  MAO_E_HPARAM = 6,      /* hyperparameter out of range */
+  MAO_E_WORKSPACE = 7,   /* workspace NULL, misaligned or too small */
+  MAO_E_HIP = 8,         /* a HIP runtime call or launch failed */
+  MAO_E_UNSUPPORTED = 9  /* a valid request this build does not serve */
+} mao_status;
+
+typedef enum { MAO_F32 = 0, MAO_BF16 = 1 } mao_dtype;
+
+/* Row-major device matrix view. */
+typedef struct {
+  void* data;
+  int64_t rows, cols, ld;
+  int32_t dtype; /* mao_dtype */
+} mao_mat;
+
+/* A group of `count` same-shape row-major matrices, matrix b at
+ * data + b*stride (elements). stride >= rows*ld. */
+typedef struct {
+  void* data;
+  int64_t count, rows, cols, ld, stride;
+  int32_t dtype; /* mao_dtype */
+} mao_batch;
+
+/* ------------------------------------------------------------------------ */
+/* Muon / Muon+                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Muon+ normalisation direction ([M+] section 2, step 3). */
+typedef enum {
+  MAO_NORM_NONE = 0,
+  MAO_NORM_ROW = 1,
+  MAO_NORM_COL = 2,
+  MAO_NORM_COL_ROW = 3, /* columns first, then rows */
+  MAO_NORM_ROW_COL = 4
+} mao_norm_mode;
+
+typedef struct {
+  float lr;            /* learning rate, >= 0 */
+  float mu;            /* momentum, 0 <= mu < 1 */
+  float weight_decay;  /* decoupled, >= 0 */
+  float eps;           /* > 0: X0 = M / (||M||_F + eps) (1e-7 in [SMB] 3-2 (2)) */
+  int32_t ns_steps;    /* Newton-Schulz iterations, 0..64 */
+  const float* ns_coeffs; /* host array [ns_steps][3] of (a, b, c), or NULL for
+                             the classical quintic (15/8, -10/8, 3/8) */
+  int32_t ns_dtype;    /* MAO_BF16: bf16 MFMA with fp32 accumulation;
+                          MAO_F32: fp32 MFMA */
+  int32_t norm_mode;   /* mao_norm_mode */
+  float norm_eps;      /* > 0, denominator guard of the Muon+ pass */
+} mao_muon_hparams;
+
+/* Workspace bytes for one muon_step on a rows x cols matrix. */
+MAO_API size_t muon_workspace_size(int64_t rows, int64_t cols, const mao_muon_hparams* hp);
+
+/*
+ * muon_step -- one Muon (Muon+) step on one matrix.
+ * [M+] section 2 (steps 1-4); [SMB] sections 2-1 (polar factor UV^T) and
+ * 3-2 (2) (Newton-Schulz recipe, eps, weight decay).
+ *
+ *   M <- mu M + (1 - mu) G
+ *   X_0 = M / (||M||_F + eps), on the wide orientation (rows <= cols; a tall
+ *         matrix is transposed internally)
+ *   for k < ns_steps: A = X X^T; B = b_k A + c_k A A; X <- a_k X + B X
+ *   O = Norm^(norm_mode)(X)   (Muon+; scale-preserving: each column (row) is
+ *         rescaled to ||O||_F / sqrt(cols) (||O||_F / sqrt(rows)))
+ *   U = sqrt(rows / cols) * O
+ *   W <- W - lr (weight_decay W + U)
+ *
+ * W: rows x cols, bf16 or fp32 (bf16 results are rounded to nearest even).
+ * G: rows x cols, bf16 or fp32. M: rows x cols, fp32 momentum (state).
+ * update_out: NULL, or a device fp32 buffer of rows*cols (dense, ld = cols)
+ *   that receives U (the update before the learning rate).
+ * W, G, M and update_out must not overlap.
+ */
+MAO_API mao_status muon_step(mao_mat W, mao_mat G, mao_mat M, const mao_muon_hparams* hp,
+                     void* workspace, size_t workspace_bytes, float* update_out,
+                     void* stream);
+
+/* Workspace bytes for muon_step_batched over these groups. */
+MAO_API size_t muon_batched_workspace_size(int32_t ngroups, const mao_batch* W,
+                                   const mao_muon_hparams* hp);
+
+/*
+ * muon_step_batched -- the muon_step above on every matrix of up to
+ * MAO_MAX_GROUPS groups of same-shape matrices (e.g. the gate, up and down
+ * banks of all experts of an MoE layer), with one launch per Newton-Schulz
+ * stage covering every matrix. Each matrix is stepped exactly as muon_step
+ * would step it alone. Groups may have different shapes.
+ * W[g], G[g], M[g] describe group g (same count/rows/cols); W and G bf16 or
+ * fp32, M fp32. update_out: NULL, or ngroups batches of fp32 receiving U.
+ */
+MAO_API mao_status muon_step_batched(int32_t ngroups, const mao_batch* W, const mao_batch* G,
+                             const mao_batch* M, const mao_muon_hparams* hp,
+                             void* workspace, size_t workspace_bytes,
+                             const mao_batch* update_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* SOAP with the real-time eigenbasis refresh                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  float lr, beta1, beta2; /* 0 <= beta < 1 */
+  float eps;              /* > 0, Adam denominator sqrt(v_hat) + eps */
+  float weight_decay;     /* decoupled, >= 0 */
+  int32_t refresh_every;  /* 1: refresh every step; k > 1: at t = 1, k+1, ...;
+                             0: basis frozen */
+} mao_soap_hparams;
+
+/* SOAP optimizer state, all fp32, rows = m, cols = n of W.
+ * Initial values: M = V = L = R = 0, QL = I_m, QR = I_n. */
+typedef struct {
+  mao_mat M;  /* m x n momentum (original space) */
+  mao_mat V;  /* m x n second moment (rotated space) */
+  mao_mat L;  /* m x m factor EMA of G G^T */
+  mao_mat R;  /* n x n factor EMA of G^T G */
+  mao_mat QL; /* m x m basis, columns = basis vectors */
+  mao_mat QR; /* n x n basis, columns = basis vectors */
+} mao_soap_state;
+
+MAO_API size_t soap_workspace_size(int64_t rows, int64_t cols, const mao_soap_hparams* hp);
+
+/*
+ * soap_step -- one SOAP step with per-step basis refresh by one QR
+ * power-iteration step. [SMB] section 1-1 (factor EMAs), section 3-2 (3)
+ * (rotation, Adam in the eigenbasis, rotation back) and 3-2 (4) (real-time
+ * update: current gradient first, then refresh with QR, then precondition the
+ * same step); [PX] Eq. (1).
+ *
+ *   M <- b1 M + (1-b1) G
+ *   L <- b2 L + (1-b2) G G^T;  R <- b2 R + (1-b2) G^T G
+ *   if refresh(t): QL <- qr(L QL), QR <- qr(R QR)  (Householder, diag(R) >= 0)
+ *   G~ = QL^T G QR;  M~ = QL^T M QR
+ *   V <- b2 V + (1-b2) G~ . G~
+ *   N = (M~ / (1-b1^t)) / (sqrt(V / (1-b2^t)) + eps)
+ *   U = QL N QR^T;  W <- W - lr (weight_decay W + U)
+ *
+ * Every contraction runs in fp32 (fp32 MFMA). W, G: bf16 or fp32.
+ * update_out: NULL or fp32 rows*cols (dense) receiving U. t >= 1.
+ */
+MAO_API mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* state, int64_t t,
+                     const mao_soap_hparams* hp, void* workspace, size_t workspace_bytes,
+                     float* update_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* FOAM                                                                      */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int32_t pf; /* >= 1: the refresh criterion is evaluated at t = 1, pf+1, ... */
+  float tol;  /* >= 0: refresh when rho > tol */
+} mao_foam_hparams;
+
+/* FOAM state, fp32, W is m x n. Initial: M = R = 0, QR = I_n, r = c = 0.
+ * aux: device float[4] written by every step: aux[0] = rho of the last
+ * evaluated criterion, aux[1] = 1 if this step refreshed else 0, aux[2] = tau,
+ * aux[3] = 1 if this step evaluated the criterion else 0. */
+typedef struct {
+  mao_mat M;  /* m x n momentum */
+  mao_mat R;  /* n x n factor EMA of G^T G */
+  mao_mat QR; /* n x n basis, columns = basis vectors */
+  float* r;   /* m, EMA of row means of G_rot^2 */
+  float* c;   /* n, EMA of column means of G_rot^2 */
+  float* aux; /* 4 floats */
+} mao_foam_state;
+
+MAO_API size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hparams* hp);
+
+/*
+ * foam_step -- one FOAM step: input-side rotation only and a factored second
+ * moment. [FOAM] section 1 (G_rot = G QR; r, c EMAs of row / column means of
+ * G_rot^2; V_hat = tau r_hat c_hat^T, tau = tr(R_hat)/(|r_hat|_1 |c_hat|_1))
+ * and section 3 (R EMA; adaptive-tolerance refresh with pf, tol; bias-corrected
+ * Adam in the rotated space).
+ *
+ *   M <- b1 M + (1-b1) G;  R <- b2 R + (1-b2) G^T G
+ *   if (t-1) % pf == 0: D = QR^T R QR, rho = ||D - diag D||_F / ||D||_F;
+ *                       if rho > tol: QR <- qr(R QR)       (decided on device)
+ *   G_rot = G QR;  M_rot = M QR
+ *   r <- b2 r + (1-b2) rowmean(G_rot^2);  c <- b2 c + (1-b2) colmean(G_rot^2)
+ *   tau = tr(R / (1-b2^t)) / (|r_hat|_1 |c_hat|_1)  (0 if r = c = 0)
+ *   N = (M_rot / (1-b1^t)) / (sqrt(tau r_hat c_hat^T) + eps)
+ *   U = N QR^T;  W <- W - lr (weight_decay W + U)
+ */
+MAO_API mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* state, int64_t t,
+                     const mao_foam_hparams* hp, void* workspace, size_t workspace_bytes,
+                     float* update_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* AdamW (flat)                                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * adamw_step -- AdamW on n contiguous elements ([SMB] section 1-1; the FOAM
+ * review, section 4, keeps embeddings on AdamW):
+ *   m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2
+ *   u = (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps);  w <- w - lr (wd w + u)
+ * w: bf16 or fp32 (w_dtype); g: bf16 or fp32 (g_dtype); m, v fp32.
+ * update_out: NULL or fp32[n].
+ */
+MAO_API mao_status adamw_step(void* w, int32_t w_dtype, const void* g, int32_t g_dtype, float* m,
+                      float* v, int64_t n, int64_t t, float lr, float beta1, float beta2,
+                      float eps, float weight_decay, float* update_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Building blocks exposed for kernel-level checks                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * mao_gemm_nt -- D = alpha * A B^T + beta * C0, the contraction every step
+ * above is built from. A: M x K, B: N x K (row-major, both K-contiguous),
+ * C0/D: M x N. in_dtype: MAO_BF16 (bf16 MFMA) or MAO_F32 (fp32 MFMA) for A
+ * and B; C0 and D fp32. C0 may be NULL (beta ignored) and may equal D.
+ * symmetric != 0 computes only the lower triangle of a square result
+ * (A == B, M == N) and mirrors it (SYRK).
+ */
+MAO_API mao_status mao_gemm_nt(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                       int64_t lda, const void* B, int64_t ldb, int32_t in_dtype, float beta,
+                       const float* C0, int64_t ldc0, float* D, int64_t ldd, int32_t symmetric,
+                       void* stream);
+
+/* Workspace bytes for mao_qr on an n x n matrix. */
+MAO_API size_t mao_qr_workspace_size(int64_t n);
+
+/*
+ * mao_qr -- Q of the Householder QR of a square fp32 matrix P (row-major,
+ * n x n), with column signs chosen so that diag(R) >= 0 -- the refresh
+ * primitive of soap_step and foam_step ([SMB] section 3-2 (4): per-step QR of
+ * the power-iteration product). P is read only; Q (n x n, row-major) is
+ * written. P and Q must not overlap.
+ */
+MAO_API mao_status mao_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Measurement instrumentation (not part of any optimizer step)              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * mao_timing_enable -- when on != 0, every contraction launch made by the
+ * library is bracketed by two HIP events recorded on its stream, tagged by
+ * what it computes (0: Newton-Schulz Gram X X^T, 1: Newton-Schulz A A,
+ * 2: Newton-Schulz B X, 3: other contractions, 4: QR updates) with its
+ * algorithmic flop count (symmetric products at half cost). Off by default;
+ * this is the only host-side state the library keeps, and it exists for
+ * benchmarking only.
+ * mao_timing_collect -- waits for the recorded events, sums elapsed
+ * milliseconds, launch counts and flops per tag into the caller's arrays of
+ * ntags entries, releases the events and returns the number of launches.
+ */
+MAO_API void mao_timing_enable(int on);
+MAO_API int mao_timing_collect(double* ms, int64_t* count, double* flops, int ntags);
+
+/* ------------------------------------------------------------------------ */
+/* Status                                                                    */
+/* ------------------------------------------------------------------------ */
+
+MAO_API const char* mao_status_string(mao_status s);
+MAO_API const char* mao_last_error(void); /* thread-local detail of the last failure */
+MAO_API int mao_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MAO_H */

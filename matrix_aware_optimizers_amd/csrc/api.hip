@@ -1,0 +1,707 @@
+// C ABI of libmao: host-side validation, workspace carving and the ordering
+// of the kernels of each optimizer step on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "common.hpp"
+#include "elementwise.hpp"
+#include "gemm.hpp"
+#include "qr.hpp"
+
+namespace mao {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+namespace {
+
+#define MAO_FAIL(code, ...)       \
+  do {                            \
+    ::mao::set_error(__VA_ARGS__); \
+    return (code);                \
+  } while (0)
+
+size_t dtype_size(int dt) { return dt == MAO_BF16 ? 2 : 4; }
+bool dtype_ok(int dt) { return dt == MAO_F32 || dt == MAO_BF16; }
+bool finite(float x) { return isfinite(x) != 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range mat_range(const void* p, int64_t count, int64_t rows, int64_t cols, int64_t ld,
+                int64_t stride, size_t es) {
+  const int64_t last = (count - 1) * stride + (rows - 1) * ld + cols;
+  return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(last * (int64_t)es)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+mao_status check_mat(const char* name, const void* data, int64_t rows, int64_t cols, int64_t ld,
+                     int dtype, bool f32_only) {
+  if (!data) MAO_FAIL(MAO_E_NULL, "%s: NULL data", name);
+  if (rows < 1 || cols < 1) MAO_FAIL(MAO_E_SHAPE, "%s: rows=%lld cols=%lld", name, (long long)rows, (long long)cols);
+  if (rows > (1 << 20) || cols > (1 << 20)) MAO_FAIL(MAO_E_SHAPE, "%s: dimension above 2^20", name);
+  if (!dtype_ok(dtype) || (f32_only && dtype != MAO_F32)) MAO_FAIL(MAO_E_DTYPE, "%s: unsupported dtype %d", name, dtype);
+  if (ld < cols || ld % 8 != 0) MAO_FAIL(MAO_E_LAYOUT, "%s: ld=%lld (cols=%lld) must be >= cols and a multiple of 8", name, (long long)ld, (long long)cols);
+  if ((uintptr_t)data % 16 != 0) MAO_FAIL(MAO_E_LAYOUT, "%s: data not 16-byte aligned", name);
+  return MAO_OK;
+}
+
+mao_status check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return MAO_OK;
+  if (!ws) MAO_FAIL(MAO_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)ws % 256 != 0) MAO_FAIL(MAO_E_WORKSPACE, "workspace not 256-byte aligned");
+  if (have < need) MAO_FAIL(MAO_E_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return MAO_OK;
+}
+
+mao_status check_beta(const char* name, float b) {
+  if (!finite(b) || b < 0.f || b >= 1.f) MAO_FAIL(MAO_E_HPARAM, "%s=%g outside [0, 1)", name, (double)b);
+  return MAO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Muon
+// ---------------------------------------------------------------------------
+
+struct MuonGroupBufs {
+  int rows, cols, a, b, count;
+  bool wide;  // rows <= cols
+  int64_t ldx, ldxt, lda;
+  void* X[2];
+  void* Xt[2];
+  void* A;
+  void* Bm;
+  float* partial;
+  int nrb;
+  float* scale;
+  float *ss_r, *ss_c, *rs, *cs, *sq;
+};
+
+void carve_muon(Carver& c, int ng, const int64_t* rows, const int64_t* cols, const int64_t* count,
+                const mao_muon_hparams* hp, MuonGroupBufs* out) {
+  const size_t es = dtype_size(hp->ns_dtype);
+  for (int g = 0; g < ng; ++g) {
+    MuonGroupBufs& B = out[g];
+    B.rows = (int)rows[g];
+    B.cols = (int)cols[g];
+    B.count = (int)count[g];
+    B.wide = B.rows <= B.cols;
+    B.a = std::min(B.rows, B.cols);
+    B.b = std::max(B.rows, B.cols);
+    B.ldx = round_up(B.b, 64);
+    B.ldxt = round_up(B.a, 64);
+    B.lda = round_up(B.a, 64);
+    for (int k = 0; k < 2; ++k) {
+      B.X[k] = c.take<char>((size_t)B.count * B.a * B.ldx * es);
+      B.Xt[k] = c.take<char>((size_t)B.count * B.b * B.ldxt * es);
+    }
+    B.A = c.take<char>((size_t)B.count * B.a * B.lda * es);
+    B.Bm = c.take<char>((size_t)B.count * B.a * B.lda * es);
+    B.nrb = rowblocks_for(B.rows, B.count);
+    B.partial = c.take<float>((size_t)B.count * B.nrb);
+    B.scale = c.take<float>(B.count);
+    if (hp->norm_mode != MAO_NORM_NONE) {
+      B.ss_r = c.take<float>((size_t)B.count * B.rows);
+      B.ss_c = c.take<float>((size_t)B.count * B.cols);
+      B.rs = c.take<float>((size_t)B.count * B.rows);
+      B.cs = c.take<float>((size_t)B.count * B.cols);
+      B.sq = c.take<float>((size_t)B.count * std::max(B.rows, B.cols));
+    } else {
+      B.ss_r = B.ss_c = B.rs = B.cs = B.sq = nullptr;
+    }
+  }
+}
+
+mao_status check_muon_hp(const mao_muon_hparams* hp) {
+  if (!hp) MAO_FAIL(MAO_E_NULL, "hparams is NULL");
+  if (!finite(hp->lr) || hp->lr < 0.f) MAO_FAIL(MAO_E_HPARAM, "lr=%g", (double)hp->lr);
+  MAO_TRY(check_beta("mu", hp->mu));
+  if (!finite(hp->weight_decay) || hp->weight_decay < 0.f) MAO_FAIL(MAO_E_HPARAM, "weight_decay=%g", (double)hp->weight_decay);
+  if (!finite(hp->eps) || hp->eps <= 0.f) MAO_FAIL(MAO_E_HPARAM, "eps=%g must be > 0", (double)hp->eps);
+  if (hp->ns_steps < 0 || hp->ns_steps > 64) MAO_FAIL(MAO_E_HPARAM, "ns_steps=%d outside 0..64", hp->ns_steps);
+  if (hp->ns_dtype != MAO_F32 && hp->ns_dtype != MAO_BF16) MAO_FAIL(MAO_E_DTYPE, "ns_dtype=%d", hp->ns_dtype);
+  if (hp->norm_mode < 0 || hp->norm_mode > 4) MAO_FAIL(MAO_E_HPARAM, "norm_mode=%d", hp->norm_mode);
+  if (hp->norm_mode != 0 && (!finite(hp->norm_eps) || hp->norm_eps <= 0.f)) MAO_FAIL(MAO_E_HPARAM, "norm_eps=%g", (double)hp->norm_eps);
+  if (hp->ns_coeffs) {
+    for (int i = 0; i < 3 * hp->ns_steps; ++i)
+      if (!finite(hp->ns_coeffs[i])) MAO_FAIL(MAO_E_HPARAM, "ns_coeffs[%d] not finite", i);
+  }
+  return MAO_OK;
+}
+
+mao_status check_batch(const char* name, const mao_batch& b, bool f32_only) {
+  MAO_TRY(check_mat(name, b.data, b.rows, b.cols, b.ld, b.dtype, f32_only));
+  if (b.count < 1) MAO_FAIL(MAO_E_SHAPE, "%s: count=%lld", name, (long long)b.count);
+  if (b.count > 1 && b.stride < b.rows * b.ld) MAO_FAIL(MAO_E_LAYOUT, "%s: stride=%lld < rows*ld", name, (long long)b.stride);
+  if (b.count > 1 && b.stride % 8 != 0) MAO_FAIL(MAO_E_LAYOUT, "%s: stride must be a multiple of 8", name);
+  return MAO_OK;
+}
+
+Range batch_range(const mao_batch& b) {
+  return mat_range(b.data, b.count, b.rows, b.cols, b.ld, b.count > 1 ? b.stride : 0, dtype_size(b.dtype));
+}
+
+mao_status validate_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const mao_batch* M,
+                         const mao_muon_hparams* hp, const mao_batch* out) {
+  MAO_TRY(check_muon_hp(hp));
+  if (ng < 1 || ng > MAO_MAX_GROUPS) MAO_FAIL(MAO_E_SHAPE, "ngroups=%d outside 1..%d", ng, MAO_MAX_GROUPS);
+  if (!W || !G || !M) MAO_FAIL(MAO_E_NULL, "W, G or M array is NULL");
+  std::vector<Range> ranges;
+  for (int g = 0; g < ng; ++g) {
+    MAO_TRY(check_batch("W", W[g], false));
+    MAO_TRY(check_batch("G", G[g], false));
+    MAO_TRY(check_batch("M", M[g], true));
+    if (G[g].rows != W[g].rows || G[g].cols != W[g].cols || M[g].rows != W[g].rows ||
+        M[g].cols != W[g].cols || G[g].count != W[g].count || M[g].count != W[g].count)
+      MAO_FAIL(MAO_E_SHAPE, "group %d: W, G, M shapes or counts differ", g);
+    ranges.push_back(batch_range(W[g]));
+    ranges.push_back(batch_range(G[g]));
+    ranges.push_back(batch_range(M[g]));
+    if (out && out[g].data) {
+      MAO_TRY(check_batch("update_out", out[g], true));
+      if (out[g].rows != W[g].rows || out[g].cols != W[g].cols || out[g].count != W[g].count)
+        MAO_FAIL(MAO_E_SHAPE, "group %d: update_out shape differs from W", g);
+      ranges.push_back(batch_range(out[g]));
+    }
+  }
+  for (size_t i = 0; i < ranges.size(); ++i)
+    for (size_t j = i + 1; j < ranges.size(); ++j)
+      if (overlap(ranges[i], ranges[j])) MAO_FAIL(MAO_E_ALIAS, "buffers %zu and %zu overlap", i, j);
+  return MAO_OK;
+}
+
+size_t muon_ws(int32_t ng, const mao_batch* W, const mao_muon_hparams* hp) {
+  int64_t rows[MAO_MAX_GROUPS], cols[MAO_MAX_GROUPS], count[MAO_MAX_GROUPS];
+  for (int g = 0; g < ng; ++g) {
+    rows[g] = W[g].rows;
+    cols[g] = W[g].cols;
+    count[g] = W[g].count;
+  }
+  MuonGroupBufs bufs[MAO_MAX_GROUPS];
+  Carver c(nullptr);
+  carve_muon(c, ng, rows, cols, count, hp, bufs);
+  return c.used + 256;
+}
+
+mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const mao_batch* M,
+                    const mao_muon_hparams* hp, void* ws, const mao_batch* out, hipStream_t s) {
+  int64_t rows[MAO_MAX_GROUPS], cols[MAO_MAX_GROUPS], count[MAO_MAX_GROUPS];
+  for (int g = 0; g < ng; ++g) {
+    rows[g] = W[g].rows;
+    cols[g] = W[g].cols;
+    count[g] = W[g].count;
+  }
+  MuonGroupBufs bufs[MAO_MAX_GROUPS];
+  Carver c(ws);
+  carve_muon(c, ng, rows, cols, count, hp, bufs);
+  const int xdt = hp->ns_dtype;
+  const int xflags = xdt == MAO_F32 ? (GF_D_F32 | GF_C0_F32) : 0;
+
+  // momentum, norm, X0 in both orientations
+  for (int g = 0; g < ng; ++g) {
+    MuonGroupBufs& B = bufs[g];
+    const int64_t mstride = M[g].count > 1 ? M[g].stride : 0;
+    const int64_t gstride = G[g].count > 1 ? G[g].stride : 0;
+    MAO_TRY(ema_sumsq(view(M[g].data, M[g].ld, mstride), view(G[g].data, G[g].ld, gstride),
+                      G[g].dtype, B.rows, B.cols, B.count, hp->mu, B.partial, B.nrb, s));
+    MAO_TRY(finalize_inv_norm(B.partial, B.nrb, B.count, hp->eps, B.scale, s));
+    View xa = view(B.X[0], B.ldx, (int64_t)B.a * B.ldx);
+    View xb = view(B.Xt[0], B.ldxt, (int64_t)B.b * B.ldxt);
+    MAO_TRY(scale_cast_transpose(view(M[g].data, M[g].ld, mstride), B.rows, B.cols, B.count,
+                                 B.scale, B.wide ? xa : xb, B.wide ? xb : xa, xdt, s));
+  }
+
+  // Newton-Schulz: A = X X^T; Bm = b A + c A A; X' = a X + Bm X
+  for (int k = 0; k < hp->ns_steps; ++k) {
+    const float ca = hp->ns_coeffs ? hp->ns_coeffs[3 * k + 0] : 15.f / 8.f;
+    const float cb = hp->ns_coeffs ? hp->ns_coeffs[3 * k + 1] : -10.f / 8.f;
+    const float cc = hp->ns_coeffs ? hp->ns_coeffs[3 * k + 2] : 3.f / 8.f;
+    const int cur = k & 1, nxt = cur ^ 1;
+    GemmProblem p[MAO_MAX_GROUPS];
+    for (int g = 0; g < ng; ++g) {
+      MuonGroupBufs& B = bufs[g];
+      p[g] = gemm_problem(B.a, B.a, B.b, 1.f, B.X[cur], B.ldx, B.X[cur], B.ldx, 0.f, nullptr, 0,
+                          B.A, B.lda, GF_SYRK | xflags);
+      p[g].batch = B.count;
+      p[g].sA = p[g].sB = (int64_t)B.a * B.ldx;
+      p[g].sD = (int64_t)B.a * B.lda;
+    }
+    MAO_TRY(launch_gemm(xdt, p, ng, s, TAG_NS_GRAM));
+    for (int g = 0; g < ng; ++g) {
+      MuonGroupBufs& B = bufs[g];
+      p[g] = gemm_problem(B.a, B.a, B.a, cc, B.A, B.lda, B.A, B.lda, cb, B.A, B.lda, B.Bm, B.lda,
+                          GF_SYRK | xflags);
+      p[g].batch = B.count;
+      p[g].sA = p[g].sB = p[g].sC0 = p[g].sD = (int64_t)B.a * B.lda;
+    }
+    MAO_TRY(launch_gemm(xdt, p, ng, s, TAG_NS_SQUARE));
+    for (int g = 0; g < ng; ++g) {
+      MuonGroupBufs& B = bufs[g];
+      p[g] = gemm_problem(B.a, B.b, B.a, 1.f, B.Bm, B.lda, B.Xt[cur], B.ldxt, ca, B.X[cur], B.ldx,
+                          B.X[nxt], B.ldx, xflags);
+      p[g].Dt = B.Xt[nxt];
+      p[g].lddt = B.ldxt;
+      p[g].batch = B.count;
+      p[g].sA = (int64_t)B.a * B.lda;
+      p[g].sB = p[g].sDt = (int64_t)B.b * B.ldxt;
+      p[g].sC0 = p[g].sD = (int64_t)B.a * B.ldx;
+    }
+    MAO_TRY(launch_gemm(xdt, p, ng, s, TAG_NS_APPLY));
+  }
+
+  // Muon+ normalisation and the update, in W's orientation
+  const int fin = hp->ns_steps & 1;
+  for (int g = 0; g < ng; ++g) {
+    MuonGroupBufs& B = bufs[g];
+    View xa = view(B.X[fin], B.ldx, (int64_t)B.a * B.ldx);
+    View xb = view(B.Xt[fin], B.ldxt, (int64_t)B.b * B.ldxt);
+    View O = B.wide ? xa : xb;   // rows x cols
+    View Ot = B.wide ? xb : xa;  // cols x rows
+    const float* rs = nullptr;
+    const float* cs = nullptr;
+    const int mode = hp->norm_mode;
+    if (mode == MAO_NORM_COL || mode == MAO_NORM_COL_ROW) {
+      MAO_TRY(row_sumsq(Ot, xdt, B.cols, B.rows, B.count, nullptr, B.ss_c, s));
+      MAO_TRY(equalise_scales(B.ss_c, B.cols, B.count, hp->norm_eps, B.cs, B.sq, s));
+      cs = B.cs;
+      if (mode == MAO_NORM_COL_ROW) {
+        MAO_TRY(row_sumsq(O, xdt, B.rows, B.cols, B.count, B.sq, B.ss_r, s));
+        MAO_TRY(equalise_scales(B.ss_r, B.rows, B.count, hp->norm_eps, B.rs, nullptr, s));
+        rs = B.rs;
+      }
+    } else if (mode == MAO_NORM_ROW || mode == MAO_NORM_ROW_COL) {
+      MAO_TRY(row_sumsq(O, xdt, B.rows, B.cols, B.count, nullptr, B.ss_r, s));
+      MAO_TRY(equalise_scales(B.ss_r, B.rows, B.count, hp->norm_eps, B.rs, B.sq, s));
+      rs = B.rs;
+      if (mode == MAO_NORM_ROW_COL) {
+        MAO_TRY(row_sumsq(Ot, xdt, B.cols, B.rows, B.count, B.sq, B.ss_c, s));
+        MAO_TRY(equalise_scales(B.ss_c, B.cols, B.count, hp->norm_eps, B.cs, nullptr, s));
+        cs = B.cs;
+      }
+    }
+    const float scale = sqrtf((float)B.rows / (float)B.cols);
+    View outv = view(nullptr, 0, 0);
+    if (out && out[g].data) outv = view(out[g].data, out[g].ld, out[g].count > 1 ? out[g].stride : 0);
+    MAO_TRY(apply_update(view(W[g].data, W[g].ld, W[g].count > 1 ? W[g].stride : 0), W[g].dtype,
+                         O, xdt, B.rows, B.cols, B.count, hp->lr, hp->weight_decay, scale, rs, cs,
+                         outv, s));
+  }
+  return MAO_OK;
+}
+
+mao_batch as_batch(const mao_mat& m) {
+  mao_batch b;
+  b.data = m.data;
+  b.count = 1;
+  b.rows = m.rows;
+  b.cols = m.cols;
+  b.ld = m.ld;
+  b.stride = m.rows * m.ld;
+  b.dtype = m.dtype;
+  return b;
+}
+
+// ---------------------------------------------------------------------------
+// SOAP / FOAM shared helpers
+// ---------------------------------------------------------------------------
+
+struct RotBufs {
+  float* Gf;   // m x n fp32 copy of G (when G is bf16)
+  float* Gtf;  // n x m fp32 transpose of G
+  float* EL;   // m x m  (SOAP only)
+  float* ER;   // n x n
+  float* S;    // max^2 QR input
+  float* T2t;  // n x m
+  float* Gtil; // m x n
+  float* Mtil; // m x n
+  float* U;    // m x n
+  float* D;    // n x n (FOAM check)
+  float* small;// FOAM: tau, flag, moment work
+  int* flag;
+  QrWork qr;
+  int64_t ldm, ldn;  // padded leading dims for m- and n-long rows
+};
+
+void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R) {
+  R.ldm = round_up(m, 64);
+  R.ldn = round_up(n, 64);
+  const int big = std::max(m, n);
+  const int64_t ldb = round_up(big, 64);
+  R.Gf = g_bf16 ? c.take<float>((size_t)m * R.ldn) : nullptr;
+  R.Gtf = c.take<float>((size_t)n * R.ldm);
+  R.EL = soap ? c.take<float>((size_t)m * R.ldm) : nullptr;
+  R.ER = c.take<float>((size_t)n * R.ldn);
+  R.S = c.take<float>((size_t)big * ldb);
+  R.T2t = c.take<float>((size_t)n * R.ldm);
+  R.Gtil = c.take<float>((size_t)m * R.ldn);
+  R.Mtil = c.take<float>((size_t)m * R.ldn);
+  R.U = c.take<float>((size_t)m * R.ldn);
+  R.D = soap ? nullptr : c.take<float>((size_t)n * R.ldn);
+  R.small = soap ? nullptr : c.take<float>(64 + foam_moments_work_floats(m, n) + 2 * (size_t)n);
+  R.flag = soap ? nullptr : c.take<int>(4);
+  R.qr = carve_qr_work(c, big);
+}
+
+mao_status check_step_common(const mao_mat& W, const mao_mat& G, int64_t t) {
+  MAO_TRY(check_mat("W", W.data, W.rows, W.cols, W.ld, W.dtype, false));
+  MAO_TRY(check_mat("G", G.data, G.rows, G.cols, G.ld, G.dtype, false));
+  if (G.rows != W.rows || G.cols != W.cols) MAO_FAIL(MAO_E_SHAPE, "G shape differs from W");
+  if (t < 1) MAO_FAIL(MAO_E_HPARAM, "t=%lld must be >= 1", (long long)t);
+  return MAO_OK;
+}
+
+mao_status check_state_mat(const char* name, const mao_mat& x, int64_t rows, int64_t cols) {
+  MAO_TRY(check_mat(name, x.data, x.rows, x.cols, x.ld, x.dtype, true));
+  if (x.rows != rows || x.cols != cols) MAO_FAIL(MAO_E_SHAPE, "%s is %lldx%lld, expected %lldx%lld", name, (long long)x.rows, (long long)x.cols, (long long)rows, (long long)cols);
+  return MAO_OK;
+}
+
+Range mrange(const mao_mat& x) { return mat_range(x.data, 1, x.rows, x.cols, x.ld, 0, dtype_size(x.dtype)); }
+
+mao_status check_no_overlap(std::vector<Range>& r) {
+  for (size_t i = 0; i < r.size(); ++i)
+    for (size_t j = i + 1; j < r.size(); ++j)
+      if (overlap(r[i], r[j])) MAO_FAIL(MAO_E_ALIAS, "buffers %zu and %zu overlap", i, j);
+  return MAO_OK;
+}
+
+mao_status check_adam_hp(float lr, float b1, float b2, float eps, float wd) {
+  if (!finite(lr) || lr < 0.f) MAO_FAIL(MAO_E_HPARAM, "lr=%g", (double)lr);
+  MAO_TRY(check_beta("beta1", b1));
+  MAO_TRY(check_beta("beta2", b2));
+  if (!finite(eps) || eps <= 0.f) MAO_FAIL(MAO_E_HPARAM, "eps=%g must be > 0", (double)eps);
+  if (!finite(wd) || wd < 0.f) MAO_FAIL(MAO_E_HPARAM, "weight_decay=%g", (double)wd);
+  return MAO_OK;
+}
+
+// D = A B^T (fp32), optional transposed copy only.
+mao_status nt32(int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                float* D, int64_t ldd, float* Dt, int64_t lddt, hipStream_t s,
+                const int* pred = nullptr) {
+  GemmProblem p = gemm_problem(M, N, K, 1.f, A, lda, B, ldb, 0.f, nullptr, 0, D, ldd, GF_D_F32);
+  p.Dt = Dt;
+  p.lddt = lddt;
+  p.pred = pred;
+  return launch_gemm(MAO_F32, &p, 1, s);
+}
+
+// F <- beta F + (1 - beta) X X^T (fp32 SYRK, in place)
+mao_status syrk_ema(int N, int K, const float* X, int64_t ldx, float beta, float* F, int64_t ldf,
+                    hipStream_t s) {
+  GemmProblem p = gemm_problem(N, N, K, 1.f - beta, X, ldx, X, ldx, beta, F, ldf, F, ldf,
+                               GF_SYRK | GF_D_F32 | GF_C0_F32);
+  return launch_gemm(MAO_F32, &p, 1, s);
+}
+
+}  // namespace
+}  // namespace mao
+
+using namespace mao;
+
+extern "C" {
+
+const char* mao_status_string(mao_status s) {
+  switch (s) {
+    case MAO_OK: return "ok";
+    case MAO_E_NULL: return "null pointer";
+    case MAO_E_SHAPE: return "bad shape";
+    case MAO_E_DTYPE: return "unsupported dtype";
+    case MAO_E_LAYOUT: return "bad layout or alignment";
+    case MAO_E_ALIAS: return "overlapping buffers";
+    case MAO_E_HPARAM: return "hyperparameter out of range";
+    case MAO_E_WORKSPACE: return "workspace missing or too small";
+    case MAO_E_HIP: return "HIP runtime error";
+    case MAO_E_UNSUPPORTED: return "unsupported request";
+  }
+  return "unknown status";
+}
+
+const char* mao_last_error(void) { return g_err; }
+
+int mao_abi_version(void) { return MAO_ABI_VERSION; }
+
+size_t muon_workspace_size(int64_t rows, int64_t cols, const mao_muon_hparams* hp) {
+  if (!hp || rows < 1 || cols < 1) return 0;
+  mao_batch b = {nullptr, 1, rows, cols, round_up(cols, 8), rows * round_up(cols, 8), MAO_F32};
+  return muon_ws(1, &b, hp);
+}
+
+size_t muon_batched_workspace_size(int32_t ngroups, const mao_batch* W, const mao_muon_hparams* hp) {
+  if (!hp || !W || ngroups < 1 || ngroups > MAO_MAX_GROUPS) return 0;
+  for (int g = 0; g < ngroups; ++g)
+    if (W[g].rows < 1 || W[g].cols < 1 || W[g].count < 1) return 0;
+  return muon_ws(ngroups, W, hp);
+}
+
+mao_status muon_step_batched(int32_t ngroups, const mao_batch* W, const mao_batch* G,
+                             const mao_batch* M, const mao_muon_hparams* hp, void* workspace,
+                             size_t workspace_bytes, const mao_batch* update_out, void* stream) {
+  MAO_TRY(validate_muon(ngroups, W, G, M, hp, update_out));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, muon_ws(ngroups, W, hp)));
+  return run_muon(ngroups, W, G, M, hp, workspace, update_out, (hipStream_t)stream);
+}
+
+mao_status muon_step(mao_mat W, mao_mat G, mao_mat M, const mao_muon_hparams* hp, void* workspace,
+                     size_t workspace_bytes, float* update_out, void* stream) {
+  mao_batch w = as_batch(W), g = as_batch(G), m = as_batch(M);
+  mao_batch o = {update_out, 1, W.rows, W.cols, W.cols, W.rows * W.cols, MAO_F32};
+  if (update_out && W.cols % 8 != 0) {
+    // dense fp32 output rows are not 8-aligned: still valid, checked as a flat buffer
+    o.ld = W.cols;
+  }
+  MAO_TRY(check_muon_hp(hp));
+  if (update_out && (uintptr_t)update_out % 16 != 0) MAO_FAIL(MAO_E_LAYOUT, "update_out not 16-byte aligned");
+  if (update_out && W.cols % 4 != 0) MAO_FAIL(MAO_E_LAYOUT, "update_out needs cols %% 4 == 0");
+  // validate W/G/M, then the dense output separately (its ld is cols)
+  MAO_TRY(validate_muon(1, &w, &g, &m, hp, nullptr));
+  if (update_out) {
+    std::vector<Range> r = {batch_range(w), batch_range(g), batch_range(m),
+                            mat_range(update_out, 1, W.rows, W.cols, W.cols, 0, 4)};
+    MAO_TRY(check_no_overlap(r));
+  }
+  MAO_TRY(check_workspace(workspace, workspace_bytes, muon_ws(1, &w, hp)));
+  return run_muon(1, &w, &g, &m, hp, workspace, update_out ? &o : nullptr, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+
+size_t soap_workspace_size(int64_t rows, int64_t cols, const mao_soap_hparams* hp) {
+  if (!hp || rows < 1 || cols < 1) return 0;
+  Carver c(nullptr);
+  RotBufs R;
+  carve_rot(c, (int)rows, (int)cols, true, true, R);
+  return c.used + 256;
+}
+
+mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
+                     const mao_soap_hparams* hp, void* workspace, size_t workspace_bytes,
+                     float* update_out, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (!st || !hp) MAO_FAIL(MAO_E_NULL, "state or hparams is NULL");
+  MAO_TRY(check_step_common(W, G, t));
+  MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
+  if (hp->refresh_every < 0) MAO_FAIL(MAO_E_HPARAM, "refresh_every=%d", hp->refresh_every);
+  const int m = (int)W.rows, n = (int)W.cols;
+  MAO_TRY(check_state_mat("M", st->M, m, n));
+  MAO_TRY(check_state_mat("V", st->V, m, n));
+  MAO_TRY(check_state_mat("L", st->L, m, m));
+  MAO_TRY(check_state_mat("R", st->R, n, n));
+  MAO_TRY(check_state_mat("QL", st->QL, m, m));
+  MAO_TRY(check_state_mat("QR", st->QR, n, n));
+  if (update_out && ((uintptr_t)update_out % 16 != 0 || n % 4 != 0))
+    MAO_FAIL(MAO_E_LAYOUT, "update_out must be 16-byte aligned with cols %% 4 == 0");
+  std::vector<Range> rr = {mrange(W), mrange(G), mrange(st->M), mrange(st->V), mrange(st->L),
+                           mrange(st->R), mrange(st->QL), mrange(st->QR)};
+  if (update_out) rr.push_back(mat_range(update_out, 1, m, n, n, 0, 4));
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, soap_workspace_size(m, n, hp)));
+
+  Carver c(workspace);
+  RotBufs R;
+  carve_rot(c, m, n, true, true, R);
+  const float b1 = hp->beta1, b2 = hp->beta2;
+  float* M = (float*)st->M.data;
+  float* L = (float*)st->L.data;
+  float* Rf = (float*)st->R.data;
+  float* QL = (float*)st->QL.data;
+  float* QR = (float*)st->QR.data;
+  const int64_t ldM = st->M.ld, ldL = st->L.ld, ldR = st->R.ld, ldQL = st->QL.ld, ldQR = st->QR.ld;
+
+  // 1. momentum
+  MAO_TRY(ema_sumsq(view(M, ldM), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr, rowblocks_for(m, 1), s));
+  // fp32 G and G^T
+  const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
+  const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
+  MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
+                             view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
+  // 2. factor EMAs with the current gradient
+  MAO_TRY(syrk_ema(m, n, Gf, ldG, b2, L, ldL, s));
+  MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s));
+  // 3. refresh: Q <- qr(F Q); S = (F Q)^T = Q^T F stored row-major
+  MAO_TRY(transpose(view(QL, ldQL), view(R.EL, R.ldm), m, m, 1, MAO_F32, s));
+  MAO_TRY(transpose(view(QR, ldQR), view(R.ER, R.ldn), n, n, 1, MAO_F32, s));
+  const bool refresh = hp->refresh_every > 0 && ((t - 1) % hp->refresh_every) == 0;
+  if (refresh) {
+    const int64_t ldS = round_up(std::max(m, n), 64);
+    MAO_TRY(nt32(m, m, m, R.EL, R.ldm, L, ldL, R.S, ldS, nullptr, 0, s));
+    MAO_TRY(qr_core(R.S, ldS, m, R.EL, R.ldm, QL, ldQL, R.qr, nullptr, s));
+    MAO_TRY(nt32(n, n, n, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));
+    MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, QR, ldQR, R.qr, nullptr, s));
+  }
+  // 4. rotations: G~ = E_L (G E_R^T) via the transposed intermediate
+  MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, nullptr, 0, R.T2t, R.ldm, s));
+  MAO_TRY(nt32(m, n, m, R.EL, R.ldm, R.T2t, R.ldm, R.Gtil, R.ldn, nullptr, 0, s));
+  MAO_TRY(nt32(m, n, n, M, ldM, R.ER, R.ldn, nullptr, 0, R.T2t, R.ldm, s));
+  MAO_TRY(nt32(m, n, m, R.EL, R.ldm, R.T2t, R.ldm, R.Mtil, R.ldn, nullptr, 0, s));
+  // 5. Adam in the eigenbasis (N written over G~)
+  const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
+  const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
+  MAO_TRY(soap_adam(view(R.Gtil, R.ldn), view(R.Mtil, R.ldn), view(st->V.data, st->V.ld), m, n, b2,
+                    bc1, bc2, hp->eps, s));
+  // 6. back: U = Q_L (N Q_R^T)
+  MAO_TRY(nt32(m, n, n, R.Gtil, R.ldn, QR, ldQR, nullptr, 0, R.T2t, R.ldm, s));
+  float* U = update_out ? update_out : R.U;
+  const int64_t ldU = update_out ? n : R.ldn;
+  MAO_TRY(nt32(m, n, m, QL, ldQL, R.T2t, R.ldm, U, ldU, nullptr, 0, s));
+  // 7. W update
+  return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
+                      hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+}
+
+// ---------------------------------------------------------------------------
+
+size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hparams* hp) {
+  if (!hp || rows < 1 || cols < 1) return 0;
+  Carver c(nullptr);
+  RotBufs R;
+  carve_rot(c, (int)rows, (int)cols, false, true, R);
+  return c.used + 256;
+}
+
+mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
+                     const mao_foam_hparams* hp, void* workspace, size_t workspace_bytes,
+                     float* update_out, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (!st || !hp) MAO_FAIL(MAO_E_NULL, "state or hparams is NULL");
+  MAO_TRY(check_step_common(W, G, t));
+  MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
+  if (hp->pf < 1) MAO_FAIL(MAO_E_HPARAM, "pf=%d must be >= 1", hp->pf);
+  if (!(hp->tol >= 0.f)) MAO_FAIL(MAO_E_HPARAM, "tol=%g must be >= 0", (double)hp->tol);
+  const int m = (int)W.rows, n = (int)W.cols;
+  MAO_TRY(check_state_mat("M", st->M, m, n));
+  MAO_TRY(check_state_mat("R", st->R, n, n));
+  MAO_TRY(check_state_mat("QR", st->QR, n, n));
+  if (!st->r || !st->c || !st->aux) MAO_FAIL(MAO_E_NULL, "r, c or aux is NULL");
+  if (((uintptr_t)st->r | (uintptr_t)st->c | (uintptr_t)st->aux) % 4 != 0) MAO_FAIL(MAO_E_LAYOUT, "r, c, aux misaligned");
+  if (update_out && ((uintptr_t)update_out % 16 != 0 || n % 4 != 0))
+    MAO_FAIL(MAO_E_LAYOUT, "update_out must be 16-byte aligned with cols %% 4 == 0");
+  std::vector<Range> rr = {mrange(W), mrange(G), mrange(st->M), mrange(st->R), mrange(st->QR),
+                           Range{(uintptr_t)st->r, (uintptr_t)(st->r + m)},
+                           Range{(uintptr_t)st->c, (uintptr_t)(st->c + n)},
+                           Range{(uintptr_t)st->aux, (uintptr_t)(st->aux + 4)}};
+  if (update_out) rr.push_back(mat_range(update_out, 1, m, n, n, 0, 4));
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, foam_workspace_size(m, n, hp)));
+
+  Carver c(workspace);
+  RotBufs R;
+  carve_rot(c, m, n, false, true, R);
+  const float b1 = hp->beta1, b2 = hp->beta2;
+  float* M = (float*)st->M.data;
+  float* Rf = (float*)st->R.data;
+  float* QR = (float*)st->QR.data;
+  const int64_t ldM = st->M.ld, ldR = st->R.ld, ldQR = st->QR.ld;
+  float* tau = R.small;
+  float* work = R.small + 64;
+
+  MAO_TRY(ema_sumsq(view(M, ldM), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr, rowblocks_for(m, 1), s));
+  const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
+  const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
+  MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
+                             view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
+  MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s));
+  MAO_TRY(transpose(view(QR, ldQR), view(R.ER, R.ldn), n, n, 1, MAO_F32, s));
+  if ((t - 1) % hp->pf == 0) {
+    const int64_t ldS = R.ldn;
+    MAO_TRY(nt32(n, n, n, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));       // Q^T R
+    MAO_TRY(nt32(n, n, n, R.S, ldS, R.ER, R.ldn, R.D, R.ldn, nullptr, 0, s));    // Q^T R Q
+    MAO_TRY(offdiag_check(view(R.D, R.ldn), n, hp->tol, work, st->aux, R.flag, s));
+    MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, QR, ldQR, R.qr, R.flag, s));
+  } else {
+    MAO_TRY(no_check(st->aux, R.flag, s));
+  }
+  // rotate: G_rot = G Q_R, M_rot = M Q_R
+  MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s));
+  MAO_TRY(nt32(m, n, n, M, ldM, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0, s));
+  const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
+  const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
+  MAO_TRY(foam_moments(view(R.Gtil, R.ldn), m, n, b2, bc2, Rf, ldR, st->r, st->c, work, tau,
+                       st->aux, s));
+  MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), m, n, st->r, st->c, tau, bc1, bc2, hp->eps, s));
+  float* U = update_out ? update_out : R.U;
+  const int64_t ldU = update_out ? n : R.ldn;
+  MAO_TRY(nt32(m, n, n, R.Mtil, R.ldn, QR, ldQR, U, ldU, nullptr, 0, s));
+  return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
+                      hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+}
+
+// ---------------------------------------------------------------------------
+
+mao_status adamw_step(void* w, int32_t w_dtype, const void* g, int32_t g_dtype, float* m, float* v,
+                      int64_t n, int64_t t, float lr, float beta1, float beta2, float eps,
+                      float weight_decay, float* update_out, void* stream) {
+  if (!w || !g || !m || !v) MAO_FAIL(MAO_E_NULL, "w, g, m or v is NULL");
+  if (n < 1) MAO_FAIL(MAO_E_SHAPE, "n=%lld", (long long)n);
+  if (!dtype_ok(w_dtype) || !dtype_ok(g_dtype)) MAO_FAIL(MAO_E_DTYPE, "w or g dtype");
+  if (t < 1) MAO_FAIL(MAO_E_HPARAM, "t=%lld must be >= 1", (long long)t);
+  MAO_TRY(check_adam_hp(lr, beta1, beta2, eps, weight_decay));
+  if (((uintptr_t)w | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v | (uintptr_t)update_out) % 16 != 0)
+    MAO_FAIL(MAO_E_LAYOUT, "buffers must be 16-byte aligned");
+  std::vector<Range> rr = {Range{(uintptr_t)w, (uintptr_t)w + n * dtype_size(w_dtype)},
+                           Range{(uintptr_t)g, (uintptr_t)g + n * dtype_size(g_dtype)},
+                           Range{(uintptr_t)m, (uintptr_t)(m + n)},
+                           Range{(uintptr_t)v, (uintptr_t)(v + n)}};
+  if (update_out) rr.push_back(Range{(uintptr_t)update_out, (uintptr_t)(update_out + n)});
+  MAO_TRY(check_no_overlap(rr));
+  const float bc1 = (float)(1.0 - pow((double)beta1, (double)t));
+  const float bc2 = (float)(1.0 - pow((double)beta2, (double)t));
+  return adamw(w, w_dtype, g, g_dtype, m, v, n, lr, beta1, beta2, bc1, bc2, eps, weight_decay,
+               update_out, (hipStream_t)stream);
+}
+
+mao_status mao_gemm_nt(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, int32_t in_dtype, float beta, const float* C0,
+                       int64_t ldc0, float* D, int64_t ldd, int32_t symmetric, void* stream) {
+  if (!A || !B || !D) MAO_FAIL(MAO_E_NULL, "A, B or D is NULL");
+  if (M < 1 || N < 1 || K < 1 || M > (1 << 20) || N > (1 << 20) || K > (1 << 20)) MAO_FAIL(MAO_E_SHAPE, "M, N, K");
+  if (!dtype_ok(in_dtype)) MAO_FAIL(MAO_E_DTYPE, "in_dtype=%d", in_dtype);
+  if (lda < K || ldb < K || lda % 8 || ldb % 8 || ldd < N || ldd % 8 || (C0 && (ldc0 < N || ldc0 % 8)))
+    MAO_FAIL(MAO_E_LAYOUT, "leading dimensions");
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D | (uintptr_t)C0) % 16 != 0) MAO_FAIL(MAO_E_LAYOUT, "alignment");
+  if (symmetric && (M != N || A != B || lda != ldb)) MAO_FAIL(MAO_E_SHAPE, "symmetric needs A == B and M == N");
+  if (!finite(alpha) || !finite(beta)) MAO_FAIL(MAO_E_HPARAM, "alpha/beta");
+  GemmProblem p = gemm_problem((int)M, (int)N, (int)K, alpha, A, lda, B, ldb, beta, C0, ldc0, D, ldd,
+                               GF_D_F32 | GF_C0_F32 | (symmetric ? GF_SYRK : 0));
+  return launch_gemm(in_dtype, &p, 1, (hipStream_t)stream);
+}
+
+size_t mao_qr_workspace_size(int64_t n) {
+  if (n < 1 || n > (1 << 20)) return 0;
+  const int64_t ld = round_up(n, 64);
+  Carver c(nullptr);
+  c.take<float>((size_t)n * ld);
+  c.take<float>((size_t)n * ld);
+  carve_qr_work(c, (int)n);
+  return c.used + 256;
+}
+
+mao_status mao_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  MAO_TRY(check_mat("P", P, n, n, ldp, MAO_F32, true));
+  MAO_TRY(check_mat("Q", Q, n, n, ldq, MAO_F32, true));
+  std::vector<Range> rr = {mat_range(P, 1, n, n, ldp, 0, 4), mat_range(Q, 1, n, n, ldq, 0, 4)};
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, mao_qr_workspace_size(n)));
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t ld = round_up(n, 64);
+  Carver c(workspace);
+  float* S = c.take<float>((size_t)n * ld);
+  float* E = c.take<float>((size_t)n * ld);
+  QrWork w = carve_qr_work(c, (int)n);
+  MAO_TRY(transpose(view((void*)P, ldp), view(S, ld), (int)n, (int)n, 1, MAO_F32, s));
+  return qr_core(S, ld, (int)n, E, ld, Q, ldq, w, nullptr, s);
+}
+
+}  // extern "C"

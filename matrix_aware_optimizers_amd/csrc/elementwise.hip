@@ -1,0 +1,614 @@
+// Memory-bound passes: EMAs, norms, Muon+ scaling, rotated-space Adam,
+// FOAM's factored moment, weight updates and transposes.
+//
+// Access pattern: every pass streams row-major matrices in 4-element chunks
+// (16-byte fp32 / 8-byte bf16 vector accesses; leading dimensions are
+// multiples of 8 elements, so chunk addresses are aligned), with a block
+// owning a contiguous range of rows of one matrix of a batch (blockIdx.y).
+// Reductions write one partial per block and a second pass sums the
+// partials in a fixed order: no atomics, bitwise-repeatable results.
+#include "elementwise.hpp"
+
+#include <algorithm>
+
+namespace mao {
+
+namespace {
+
+constexpr int kBlock = 256;
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float* p, float v[4]) {
+    float4 x = *(const float4*)p;
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float v[4]) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct Vec4<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float v[4]) {
+    uint2 u = *(const uint2*)p;
+    v[0] = bf16_to_f32((bf16_t)(u.x & 0xffff));
+    v[1] = bf16_to_f32((bf16_t)(u.x >> 16));
+    v[2] = bf16_to_f32((bf16_t)(u.y & 0xffff));
+    v[3] = bf16_to_f32((bf16_t)(u.y >> 16));
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float v[4]) {
+    uint2 u;
+    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *(uint2*)p = u;
+  }
+};
+
+// Load up to 4 elements starting at column j of a row with `cols` columns.
+template <typename T>
+__device__ __forceinline__ void load4(const T* row, int j, int cols, float v[4]) {
+  if (j + 4 <= cols) {
+    Vec4<T>::load(row + j, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (j + e < cols) ? load_f32<T>(row + j + e) : 0.f;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* row, int j, int cols, const float v[4]) {
+  if (j + 4 <= cols) {
+    Vec4<T>::store(row + j, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j + e < cols) store_f32<T>(row + j + e, v[e]);
+  }
+}
+
+// Row range of this block for a matrix split into nrb row-blocks.
+__device__ __forceinline__ void row_range(int rows, int nrb, int& r0, int& r1) {
+  const int per = (rows + nrb - 1) / nrb;
+  r0 = blockIdx.x * per;
+  r1 = min(rows, r0 + per);
+}
+
+// ---------------------------------------------------------------------------
+
+template <typename TG>
+__global__ __launch_bounds__(kBlock) void ema_sumsq_kernel(View M, View G, int rows, int cols,
+                                                           float beta, float* partial, int nrb) {
+  const int b = blockIdx.y;
+  float* Mb = (float*)M.p + (int64_t)b * M.stride;
+  const TG* Gb = (const TG*)G.p + (int64_t)b * G.stride;
+  int r0, r1;
+  row_range(rows, nrb, r0, r1);
+  const int c4 = (cols + 3) >> 2;
+  const int64_t nq = (int64_t)max(0, r1 - r0) * c4;
+  const float om = 1.f - beta;
+  float acc = 0.f;
+  for (int64_t q = threadIdx.x; q < nq; q += kBlock) {
+    const int i = r0 + (int)(q / c4);
+    const int j = (int)(q % c4) * 4;
+    float m[4], g[4];
+    float* mrow = Mb + (int64_t)i * M.ld;
+    load4<float>(mrow, j, cols, m);
+    load4<TG>(Gb + (int64_t)i * G.ld, j, cols, g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[e] = beta * m[e] + om * g[e];
+      acc += m[e] * m[e];
+    }
+    store4<float>(mrow, j, cols, m);
+  }
+  if (partial) {
+    __shared__ float sc[16];
+    const float tot = block_sum(acc, sc);
+    if (threadIdx.x == 0) partial[(int64_t)b * nrb + blockIdx.x] = tot;
+  }
+}
+
+// One block per matrix: fixed-order sum of the per-block partials.
+__global__ __launch_bounds__(kBlock) void finalize_inv_norm_kernel(const float* partial, int nrb,
+                                                                   float eps, float* scale) {
+  const int b = blockIdx.x;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < nrb; i += kBlock) s += (double)partial[(int64_t)b * nrb + i];
+  __shared__ double sc[16];
+  s = block_sum_d(s, sc);
+  if (threadIdx.x == 0) scale[b] = (float)(1.0 / (sqrt(s) + (double)eps));
+}
+
+// 64 x 64 tiles through LDS: direct copy and transposed copy, optional scale.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(kBlock) void transpose_kernel(View In, int rows, int cols,
+                                                           const float* scale, View Dir, View Tr) {
+  __shared__ float tile[64][65];
+  const int b = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const float s = scale ? scale[b] : 1.f;
+  const TI* in = (const TI*)In.p + (int64_t)b * In.stride;
+  TO* dir = Dir.p ? (TO*)Dir.p + (int64_t)b * Dir.stride : nullptr;
+  TO* tr = Tr.p ? (TO*)Tr.p + (int64_t)b * Tr.stride : nullptr;
+  const int t = threadIdx.x;
+  const int cc = (t & 15) * 4;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = (t >> 4) + 16 * p;
+    const int i = i0 + r, j = j0 + cc;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (i < rows && j < cols) {
+      load4<TI>(in + (int64_t)i * In.ld, j, cols, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= s;
+      if (dir) store4<TO>(dir + (int64_t)i * Dir.ld, j, cols, v);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[r][cc + e] = v[e];
+  }
+  if (!tr) return;
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int c = (t >> 4) + 16 * p;  // original column
+    const int jj = j0 + c, ii = i0 + cc;
+    if (jj < cols && ii < rows) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = tile[cc + e][c];
+      store4<TO>(tr + (int64_t)jj * Tr.ld, ii, rows, v);
+    }
+  }
+}
+
+template <typename TX>
+__global__ __launch_bounds__(kBlock) void row_sumsq_kernel(View X, int rows, int cols,
+                                                           const float* w, float* ss) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (i >= rows) return;
+  const TX* row = (const TX*)X.p + (int64_t)b * X.stride + (int64_t)i * X.ld;
+  const float* wb = w ? w + (int64_t)b * cols : nullptr;
+  float acc = 0.f;
+  for (int j = lane * 4; j < cols; j += 256) {
+    float v[4];
+    load4<TX>(row, j, cols, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float wt = (wb && j + e < cols) ? wb[j + e] : 1.f;
+      acc += wt * v[e] * v[e];
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) ss[(int64_t)b * rows + i] = acc;
+}
+
+__global__ __launch_bounds__(kBlock) void equalise_kernel(const float* ss, int n, float eps,
+                                                          float* scale, float* sq) {
+  const int b = blockIdx.x;
+  const float* s = ss + (int64_t)b * n;
+  float acc = 0.f;
+  for (int j = threadIdx.x; j < n; j += kBlock) acc += s[j];
+  __shared__ float sc[16];
+  const float tot = block_sum(acc, sc);
+  const float target = sqrtf(tot / (float)n);
+  for (int j = threadIdx.x; j < n; j += kBlock) {
+    const float v = target / (sqrtf(s[j]) + eps);
+    scale[(int64_t)b * n + j] = v;
+    if (sq) sq[(int64_t)b * n + j] = v * v;
+  }
+}
+
+template <typename TW, typename TO>
+__global__ __launch_bounds__(kBlock) void update_kernel(View W, View O, int rows, int cols,
+                                                        float lr, float wd, float s,
+                                                        const float* rs, const float* cs,
+                                                        View Out, int nrb) {
+  const int b = blockIdx.y;
+  TW* Wb = (TW*)W.p + (int64_t)b * W.stride;
+  const TO* Ob = (const TO*)O.p + (int64_t)b * O.stride;
+  float* outb = Out.p ? (float*)Out.p + (int64_t)b * Out.stride : nullptr;
+  const float* rsb = rs ? rs + (int64_t)b * rows : nullptr;
+  const float* csb = cs ? cs + (int64_t)b * cols : nullptr;
+  int r0, r1;
+  row_range(rows, nrb, r0, r1);
+  const int c4 = (cols + 3) >> 2;
+  const int64_t nq = (int64_t)max(0, r1 - r0) * c4;
+  for (int64_t q = threadIdx.x; q < nq; q += kBlock) {
+    const int i = r0 + (int)(q / c4);
+    const int j = (int)(q % c4) * 4;
+    float w[4], o[4];
+    TW* wrow = Wb + (int64_t)i * W.ld;
+    load4<TW>(wrow, j, cols, w);
+    load4<TO>(Ob + (int64_t)i * O.ld, j, cols, o);
+    const float si = s * (rsb ? rsb[i] : 1.f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float cj = (csb && j + e < cols) ? csb[j + e] : 1.f;
+      o[e] = si * cj * o[e];
+      w[e] = w[e] - lr * (wd * w[e] + o[e]);
+    }
+    store4<TW>(wrow, j, cols, w);
+    if (outb) store4<float>(outb + (int64_t)i * Out.ld, j, cols, o);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void soap_adam_kernel(View Gt, View Mt, View V, int rows,
+                                                           int cols, float beta2, float bc1,
+                                                           float bc2, float eps, int nrb) {
+  int r0, r1;
+  row_range(rows, nrb, r0, r1);
+  const int c4 = (cols + 3) >> 2;
+  const int64_t nq = (int64_t)max(0, r1 - r0) * c4;
+  const float ob = 1.f - beta2, ib1 = 1.f / bc1, ib2 = 1.f / bc2;
+  for (int64_t q = threadIdx.x; q < nq; q += kBlock) {
+    const int i = r0 + (int)(q / c4);
+    const int j = (int)(q % c4) * 4;
+    float g[4], m[4], v[4];
+    float* grow = (float*)Gt.p + (int64_t)i * Gt.ld;
+    float* vrow = (float*)V.p + (int64_t)i * V.ld;
+    load4<float>(grow, j, cols, g);
+    load4<float>((const float*)Mt.p + (int64_t)i * Mt.ld, j, cols, m);
+    load4<float>(vrow, j, cols, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = beta2 * v[e] + ob * g[e] * g[e];
+      g[e] = (m[e] * ib1) / (sqrtf(v[e] * ib2) + eps);
+    }
+    store4<float>(vrow, j, cols, v);
+    store4<float>(grow, j, cols, g);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void fill_identity_kernel(View E, int n, const int* pred) {
+  if (pred && *pred == 0) return;
+  const int64_t total = (int64_t)n * n;
+  for (int64_t q = blockIdx.x * (int64_t)kBlock + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * kBlock) {
+    const int i = (int)(q / n), j = (int)(q % n);
+    ((float*)E.p)[(int64_t)i * E.ld + j] = (i == j) ? 1.f : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void fill_kernel(float* p, int64_t n, float v) {
+  for (int64_t q = blockIdx.x * (int64_t)kBlock + threadIdx.x; q < n; q += (int64_t)gridDim.x * kBlock)
+    p[q] = v;
+}
+
+// ---- FOAM factored moment -------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void col_partial_kernel(View X, int rows, int cols, int nrb,
+                                                             float* colpart) {
+  const int j = blockIdx.x * kBlock + threadIdx.x;
+  if (j >= cols) return;
+  int r0, r1;
+  const int per = (rows + nrb - 1) / nrb;
+  r0 = blockIdx.y * per;
+  r1 = min(rows, r0 + per);
+  float acc = 0.f;
+  for (int i = r0; i < r1; ++i) {
+    const float v = ((const float*)X.p)[(int64_t)i * X.ld + j];
+    acc += v * v;
+  }
+  colpart[(int64_t)blockIdx.y * cols + j] = acc;
+}
+
+__global__ __launch_bounds__(1024) void foam_finalize_kernel(
+    const float* rowss, const float* colpart, int nrb, int m, int n, float beta2, float bc2,
+    const float* R, int64_t ldR, float* r, float* c, float* tau_out, float* aux) {
+  __shared__ float sc[16];
+  const float ob = 1.f - beta2;
+  float sr = 0.f, scs = 0.f, tr = 0.f;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) {
+    const float v = beta2 * r[i] + ob * (rowss[i] / (float)n);
+    r[i] = v;
+    sr += v;
+  }
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    float s = 0.f;
+    for (int k = 0; k < nrb; ++k) s += colpart[(int64_t)k * n + j];
+    const float v = beta2 * c[j] + ob * (s / (float)m);
+    c[j] = v;
+    scs += v;
+    tr += R[(int64_t)j * ldR + j];
+  }
+  sr = block_sum(sr, sc);
+  scs = block_sum(scs, sc);
+  tr = block_sum(tr, sc);
+  if (threadIdx.x == 0) {
+    const double denom = ((double)sr / bc2) * ((double)scs / bc2);
+    const float tau = denom > 0.0 ? (float)(((double)tr / bc2) / denom) : 0.f;
+    tau_out[0] = tau;
+    if (aux) aux[2] = tau;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void foam_precond_kernel(View Mr, int m, int n,
+                                                              const float* r, const float* c,
+                                                              const float* tau, float bc1,
+                                                              float bc2, float eps, int nrb) {
+  int r0, r1;
+  row_range(m, nrb, r0, r1);
+  const int c4 = (n + 3) >> 2;
+  const int64_t nq = (int64_t)max(0, r1 - r0) * c4;
+  const float t = tau[0], ib1 = 1.f / bc1, ib2 = 1.f / bc2;
+  for (int64_t q = threadIdx.x; q < nq; q += kBlock) {
+    const int i = r0 + (int)(q / c4);
+    const int j = (int)(q % c4) * 4;
+    float* row = (float*)Mr.p + (int64_t)i * Mr.ld;
+    float x[4];
+    load4<float>(row, j, n, x);
+    const float ri = r[i] * ib2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float cj = (j + e < n) ? c[j + e] * ib2 : 0.f;
+      x[e] = (x[e] * ib1) / (sqrtf(t * ri * cj) + eps);
+    }
+    store4<float>(row, j, n, x);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void offdiag_rows_kernel(View D, int n, float* work) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const float* row = (const float*)D.p + (int64_t)i * D.ld;
+  float off = 0.f;
+  for (int j = lane * 4; j < n; j += 256) {
+    float v[4];
+    load4<float>(row, j, n, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j + e != i) off += v[e] * v[e];
+  }
+  off = wave_sum(off);
+  if (lane == 0) {
+    const float d = row[i];
+    work[i] = off;
+    work[n + i] = d * d;
+  }
+}
+
+__global__ __launch_bounds__(1024) void offdiag_final_kernel(const float* work, int n, float tol,
+                                                             float* aux, int* flag) {
+  __shared__ double sc[16];
+  double off = 0.0, dg = 0.0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    off += work[i];
+    dg += work[n + i];
+  }
+  off = block_sum_d(off, sc);
+  dg = block_sum_d(dg, sc);
+  if (threadIdx.x == 0) {
+    const double total = off + dg;
+    const float rho = total > 0.0 ? (float)sqrt(off / total) : 0.f;
+    const int f = rho > tol ? 1 : 0;
+    aux[0] = rho;
+    aux[1] = (float)f;
+    aux[3] = 1.f;
+    *flag = f;
+  }
+}
+
+__global__ void no_check_kernel(float* aux, int* flag) {
+  aux[1] = 0.f;
+  aux[3] = 0.f;
+  *flag = 0;
+}
+
+template <typename TW, typename TG>
+__global__ __launch_bounds__(kBlock) void adamw_kernel(TW* w, const TG* g, float* m, float* v,
+                                                       int64_t n, float lr, float beta1,
+                                                       float beta2, float bc1, float bc2,
+                                                       float eps, float wd, float* out) {
+  const int64_t n4 = (n + 3) >> 2;
+  const float ob1 = 1.f - beta1, ob2 = 1.f - beta2, ib1 = 1.f / bc1, ib2 = 1.f / bc2;
+  for (int64_t q = blockIdx.x * (int64_t)kBlock + threadIdx.x; q < n4;
+       q += (int64_t)gridDim.x * kBlock) {
+    const int64_t base = q * 4;
+    const int cnt = (int)min((int64_t)4, n - base);
+    float ww[4], gg[4], mm[4], vv[4];
+    load4<TW>(w + base, 0, cnt, ww);
+    load4<TG>(g + base, 0, cnt, gg);
+    load4<float>(m + base, 0, cnt, mm);
+    load4<float>(v + base, 0, cnt, vv);
+    float uu[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mm[e] = beta1 * mm[e] + ob1 * gg[e];
+      vv[e] = beta2 * vv[e] + ob2 * gg[e] * gg[e];
+      uu[e] = (mm[e] * ib1) / (sqrtf(vv[e] * ib2) + eps);
+      ww[e] = ww[e] - lr * (wd * ww[e] + uu[e]);
+    }
+    store4<TW>(w + base, 0, cnt, ww);
+    store4<float>(m + base, 0, cnt, mm);
+    store4<float>(v + base, 0, cnt, vv);
+    if (out) store4<float>(out + base, 0, cnt, uu);
+  }
+}
+
+int grid_for(int64_t work, int per_block = 4 * kBlock) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > 8192) g = 8192;
+  return (int)g;
+}
+
+}  // namespace
+
+int rowblocks_for(int64_t rows, int64_t batch) {
+  // about 2048 blocks over the whole batch, at least one row each
+  int64_t want = (2048 + batch - 1) / batch;
+  if (want < 1) want = 1;
+  if (want > rows) want = rows;
+  if (want > 65535) want = 65535;
+  return (int)want;
+}
+
+mao_status ema_sumsq(View M, View G, int g_dtype, int rows, int cols, int batch, float beta,
+                     float* partial, int nrb, hipStream_t s) {
+  dim3 grid(nrb, batch);
+  if (g_dtype == MAO_BF16)
+    hipLaunchKernelGGL(ema_sumsq_kernel<bf16_t>, grid, dim3(kBlock), 0, s, M, G, rows, cols, beta, partial, nrb);
+  else
+    hipLaunchKernelGGL(ema_sumsq_kernel<float>, grid, dim3(kBlock), 0, s, M, G, rows, cols, beta, partial, nrb);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status finalize_inv_norm(const float* partial, int nrb, int batch, float eps, float* scale,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(finalize_inv_norm_kernel, dim3(batch), dim3(kBlock), 0, s, partial, nrb, eps, scale);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status scale_cast_transpose(View M, int rows, int cols, int batch, const float* scale,
+                                View direct, View trans, int x_dtype, hipStream_t s) {
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
+  if (x_dtype == MAO_BF16)
+    hipLaunchKernelGGL((transpose_kernel<float, bf16_t>), grid, dim3(kBlock), 0, s, M, rows, cols, scale, direct, trans);
+  else
+    hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(kBlock), 0, s, M, rows, cols, scale, direct, trans);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status cast_transpose_f32(View in, int in_dtype, int rows, int cols, View direct, View trans,
+                              hipStream_t s) {
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, 1);
+  if (in_dtype == MAO_BF16)
+    hipLaunchKernelGGL((transpose_kernel<bf16_t, float>), grid, dim3(kBlock), 0, s, in, rows, cols, (const float*)nullptr, direct, trans);
+  else
+    hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(kBlock), 0, s, in, rows, cols, (const float*)nullptr, direct, trans);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status transpose(View in, View out, int rows, int cols, int batch, int dtype, hipStream_t s) {
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
+  View none = view(nullptr, 0, 0);
+  if (dtype == MAO_BF16)
+    hipLaunchKernelGGL((transpose_kernel<bf16_t, bf16_t>), grid, dim3(kBlock), 0, s, in, rows, cols, (const float*)nullptr, none, out);
+  else
+    hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(kBlock), 0, s, in, rows, cols, (const float*)nullptr, none, out);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status row_sumsq(View X, int x_dtype, int rows, int cols, int batch, const float* w,
+                     float* ss, hipStream_t s) {
+  dim3 grid((rows + 3) / 4, batch);
+  if (x_dtype == MAO_BF16)
+    hipLaunchKernelGGL(row_sumsq_kernel<bf16_t>, grid, dim3(kBlock), 0, s, X, rows, cols, w, ss);
+  else
+    hipLaunchKernelGGL(row_sumsq_kernel<float>, grid, dim3(kBlock), 0, s, X, rows, cols, w, ss);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status equalise_scales(const float* ss, int n, int batch, float eps, float* scale, float* sq,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(equalise_kernel, dim3(batch), dim3(kBlock), 0, s, ss, n, eps, scale, sq);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status apply_update(View W, int w_dtype, View O, int o_dtype, int rows, int cols, int batch,
+                        float lr, float wd, float sc, const float* rs, const float* cs, View out,
+                        hipStream_t s) {
+  const int nrb = rowblocks_for(rows, batch);
+  dim3 grid(nrb, batch);
+#define MAO_UPD(TW, TO)                                                                    \
+  hipLaunchKernelGGL((update_kernel<TW, TO>), grid, dim3(kBlock), 0, s, W, O, rows, cols, lr, \
+                     wd, sc, rs, cs, out, nrb)
+  if (w_dtype == MAO_BF16 && o_dtype == MAO_BF16) MAO_UPD(bf16_t, bf16_t);
+  else if (w_dtype == MAO_BF16) MAO_UPD(bf16_t, float);
+  else if (o_dtype == MAO_BF16) MAO_UPD(float, bf16_t);
+  else MAO_UPD(float, float);
+#undef MAO_UPD
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status soap_adam(View Gt, View Mt, View V, int rows, int cols, float beta2, float bc1,
+                     float bc2, float eps, hipStream_t s) {
+  const int nrb = rowblocks_for(rows, 1);
+  hipLaunchKernelGGL(soap_adam_kernel, dim3(nrb), dim3(kBlock), 0, s, Gt, Mt, V, rows, cols, beta2, bc1, bc2, eps, nrb);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status fill_identity(View E, int n, const int* pred, hipStream_t s) {
+  hipLaunchKernelGGL(fill_identity_kernel, dim3(grid_for((int64_t)n * n)), dim3(kBlock), 0, s, E, n, pred);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n)), dim3(kBlock), 0, s, p, n, v);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status foam_moments(View Gr, int m, int n, float beta2, float bc2, const float* R, int64_t ldR,
+                        float* r, float* c, float* work, float* tau_out, float* aux,
+                        hipStream_t s) {
+  // work: rowss[m] then colpart[nrb * n]
+  float* rowss = work;
+  float* colpart = work + round_up(m, 64);
+  const int nrb = (int)std::min<int64_t>(64, std::max<int64_t>(1, m / 32));
+  hipLaunchKernelGGL(row_sumsq_kernel<float>, dim3((m + 3) / 4, 1), dim3(kBlock), 0, s, Gr, m, n, (const float*)nullptr, rowss);
+  MAO_LAUNCH_CHECK();
+  hipLaunchKernelGGL(col_partial_kernel, dim3((n + kBlock - 1) / kBlock, nrb), dim3(kBlock), 0, s, Gr, m, n, nrb, colpart);
+  MAO_LAUNCH_CHECK();
+  hipLaunchKernelGGL(foam_finalize_kernel, dim3(1), dim3(1024), 0, s, rowss, colpart, nrb, m, n, beta2, bc2, R, ldR, r, c, tau_out, aux);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+int64_t foam_moments_work_floats(int m, int n) {
+  const int nrb = (int)std::min<int64_t>(64, std::max<int64_t>(1, m / 32));
+  return round_up(m, 64) + (int64_t)nrb * n;
+}
+
+mao_status foam_precondition(View Mr, int m, int n, const float* r, const float* c,
+                             const float* tau, float bc1, float bc2, float eps, hipStream_t s) {
+  const int nrb = rowblocks_for(m, 1);
+  hipLaunchKernelGGL(foam_precond_kernel, dim3(nrb), dim3(kBlock), 0, s, Mr, m, n, r, c, tau, bc1, bc2, eps, nrb);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status offdiag_check(View D, int n, float tol, float* work, float* aux, int* flag,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(offdiag_rows_kernel, dim3((n + 3) / 4), dim3(kBlock), 0, s, D, n, work);
+  MAO_LAUNCH_CHECK();
+  hipLaunchKernelGGL(offdiag_final_kernel, dim3(1), dim3(1024), 0, s, work, n, tol, aux, flag);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status no_check(float* aux, int* flag, hipStream_t s) {
+  hipLaunchKernelGGL(no_check_kernel, dim3(1), dim3(1), 0, s, aux, flag);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status adamw(void* w, int w_dtype, const void* g, int g_dtype, float* m, float* v, int64_t n,
+                 float lr, float beta1, float beta2, float bc1, float bc2, float eps, float wd,
+                 float* out, hipStream_t s) {
+  const int grid = grid_for((n + 3) / 4, kBlock);
+#define MAO_ADAM(TW, TG)                                                                      \
+  hipLaunchKernelGGL((adamw_kernel<TW, TG>), dim3(grid), dim3(kBlock), 0, s, (TW*)w,           \
+                     (const TG*)g, m, v, n, lr, beta1, beta2, bc1, bc2, eps, wd, out)
+  if (w_dtype == MAO_BF16 && g_dtype == MAO_BF16) MAO_ADAM(bf16_t, bf16_t);
+  else if (w_dtype == MAO_BF16) MAO_ADAM(bf16_t, float);
+  else if (g_dtype == MAO_BF16) MAO_ADAM(float, bf16_t);
+  else MAO_ADAM(float, float);
+#undef MAO_ADAM
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+}  // namespace mao

@@ -1,0 +1,345 @@
+// NT contraction on CDNA4 matrix cores.
+//
+// D[i][j] = alpha * sum_k A[i][k] * B[j][k] + beta * C0[i][j]
+//
+// Both operands are K-contiguous (row-major M x K and N x K), which is the
+// layout every contraction of the optimizer steps is arranged into (the
+// Newton-Schulz Grams X X^T and A A, the product B X through the transposed
+// copy of X that the previous product writes, and the SOAP / FOAM rotations
+// through transposed copies of the bases). One launch covers up to
+// kMaxProblems problems, each a strided batch, so a whole layer's (or a whole
+// expert bank's) Newton-Schulz stage is one dispatch.
+//
+// Tiling: 256 threads = 4 wavefronts in 2 x 2; a workgroup tile is BM x BN,
+// each wavefront owns (BM/2) x (BN/2) as 32 x 32 MFMA blocks. A K-slice of the
+// tile is 128 bytes per row (64 bf16 or 32 fp32), staged global -> registers
+// -> LDS with double buffering (the next slice is fetched into registers while
+// the current one feeds the MFMAs). LDS rows are padded to 144 bytes so the
+// 16-byte reads of 32 consecutive rows spread over the banks. Each lane reads
+// one contiguous half of a row (64 bytes); the K order inside a slice is
+// permuted consistently for both operands, which leaves the sum unchanged.
+//
+// Epilogue: alpha/beta blend with C0 (bf16 or fp32), optional row scale,
+// store of D and/or its transpose Dt (bf16 or fp32). In SYRK mode only tiles
+// on or below the diagonal run and each writes its mirror image too; the
+// diagonal tiles write each off-diagonal pair once, so the result is exactly
+// symmetric.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, so consecutive
+// block ids are remapped to consecutive tiles on the same XCD (its L2), and
+// tiles are rastered in groups of 8 tile-rows so that neighbours share
+// operand panels.
+#include "gemm.hpp"
+
+namespace mao {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;  // K bytes per tile row per slice
+constexpr int kLdsRow = 144;    // padded LDS row stride (bytes)
+
+template <typename T> struct InCfg;
+template <> struct InCfg<bf16_t> { static constexpr int EPC = 8; };
+template <> struct InCfg<float> { static constexpr int EPC = 4; };
+
+template <typename T>
+__device__ __forceinline__ uint4 load_chunk(const T* row, int k, int K) {
+  constexpr int EPC = InCfg<T>::EPC;
+  if (k + EPC <= K) return *(const uint4*)(row + k);
+  union {
+    uint4 v;
+    T e[EPC];
+  } u;
+  u.v = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < EPC; ++i)
+    if (k + i < K) u.e[i] = row[k + i];
+  return u.v;
+}
+
+__device__ __forceinline__ float c0_at(const void* C0, bool f32, int64_t off) {
+  return f32 ? ((const float*)C0)[off] : bf16_to_f32(((const bf16_t*)C0)[off]);
+}
+
+__device__ __forceinline__ void store_at(void* D, bool f32, int64_t off, float v) {
+  if (f32)
+    ((float*)D)[off] = v;
+  else
+    ((bf16_t*)D)[off] = f32_to_bf16(v);
+}
+
+template <typename TIn, int BM, int BN>
+__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
+  constexpr int EPC = InCfg<TIn>::EPC;
+  constexpr int BK = kRowBytes / (int)sizeof(TIn);
+  constexpr int CA = BM * 8 / kThreads;
+  constexpr int CB = BN * 8 / kThreads;
+  constexpr int FM = BM / 64, FN = BN / 64;
+  constexpr int kStage = (BM + BN) * kLdsRow;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStage];
+
+  // ---- which tile ------------------------------------------------------
+  const int total = args.total_tiles;
+  const int bid = blockIdx.x;
+  const int per = total >> 3, rem = total & 7;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int t = xcd * per + min(xcd, rem) + idx;
+  int pi = 0;
+  for (int q = 1; q < args.nprob; ++q)
+    if (t >= args.p[q].tile_begin) pi = q;
+  const GemmProblem& P = args.p[pi];
+  if (P.pred != nullptr && *P.pred == 0) return;
+
+  int local = t - P.tile_begin;
+  const int b = local / P.tiles_per_batch;
+  local -= b * P.tiles_per_batch;
+  int tm, tn;
+  const bool syrk = (P.flags & GF_SYRK) != 0;
+  if (syrk) {
+    tm = (int)((sqrtf(8.f * (float)local + 1.f) - 1.f) * 0.5f);
+    while (tm > 0 && tm * (tm + 1) / 2 > local) --tm;
+    while ((tm + 1) * (tm + 2) / 2 <= local) ++tm;
+    tn = local - tm * (tm + 1) / 2;
+  } else {
+    constexpr int G = 8;
+    const int per_group = G * P.tiles_n;
+    const int grp = local / per_group;
+    const int first_m = grp * G;
+    const int gsz = min(G, P.tiles_m - first_m);
+    const int in = local - grp * per_group;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = P.M, N = P.N, K = P.K;
+  const TIn* A = (const TIn*)P.A + (int64_t)b * P.sA;
+  const TIn* B = (const TIn*)P.B + (int64_t)b * P.sB;
+  const int64_t lda = P.lda, ldb = P.ldb;
+
+  uint4 ra[CA], rb[CB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < CA; ++c) {
+      const int q = threadIdx.x + c * kThreads;
+      const int row = q >> 3, ch = q & 7;
+      const int gm = m0 + row;
+      ra[c] = (gm < M) ? load_chunk<TIn>(A + (int64_t)gm * lda, k0 + ch * EPC, K)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int q = threadIdx.x + c * kThreads;
+      const int row = q >> 3, ch = q & 7;
+      const int gn = n0 + row;
+      rb[c] = (gn < N) ? load_chunk<TIn>(B + (int64_t)gn * ldb, k0 + ch * EPC, K)
+                       : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int stage) {
+    unsigned char* base = lds + stage * kStage;
+#pragma unroll
+    for (int c = 0; c < CA; ++c) {
+      const int q = threadIdx.x + c * kThreads;
+      *(uint4*)(base + (q >> 3) * kLdsRow + (q & 7) * 16) = ra[c];
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int q = threadIdx.x + c * kThreads;
+      *(uint4*)(base + (BM + (q >> 3)) * kLdsRow + (q & 7) * 16) = rb[c];
+    }
+  };
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  auto compute = [&](int stage) {
+    const unsigned char* base = lds + stage * kStage;
+    uint4 af[FM][4], bfr[FN][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const unsigned char* p = base + (wm * (BM / 2) + i * 32 + r32) * kLdsRow + h * 64;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) af[i][c] = *(const uint4*)(p + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const unsigned char* p = base + (BM + wn * (BN / 2) + j * 32 + r32) * kLdsRow + h * 64;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bfr[j][c] = *(const uint4*)(p + c * 16);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (sizeof(TIn) == 2) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, af[i][c]), __builtin_bit_cast(bf16x8_t, bfr[j][c]),
+                acc[i][j], 0, 0, 0);
+          } else {
+            const uint32_t* a4 = (const uint32_t*)&af[i][c];
+            const uint32_t* b4 = (const uint32_t*)&bfr[j][c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                  __uint_as_float(a4[e]), __uint_as_float(b4[e]), acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload((kt + 1) * BK);
+      compute(cur);
+      if (kt + 1 < nk) lstore(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue ---------------------------------------------------------
+  const bool diag = syrk && (tm == tn);
+  const bool d32 = (P.flags & GF_D_F32) != 0;
+  const bool c32 = (P.flags & GF_C0_F32) != 0;
+  const int dsz = d32 ? 4 : 2, csz = c32 ? 4 : 2;
+  void* D = P.D ? (void*)((char*)P.D + (int64_t)b * P.sD * dsz) : nullptr;
+  void* Tt = syrk ? D : (P.Dt ? (void*)((char*)P.Dt + (int64_t)b * P.sDt * dsz) : nullptr);
+  const int64_t ldt = syrk ? P.ldd : P.lddt;
+  const void* C0 = P.C0 ? (const void*)((const char*)P.C0 + (int64_t)b * P.sC0 * csz) : nullptr;
+  const float alpha = P.alpha, beta = P.beta;
+  const float* rs = P.row_scale;
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * (BN / 2) + j * 32 + r32;
+      const int rbase = m0 + wm * (BM / 2) + i * 32 + 4 * h;
+      if (col >= N) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = rbase + 8 * g;
+        if (r0 >= M) continue;
+        float vals[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = r0 + e;
+          float v = alpha * acc[i][j][4 * g + e];
+          if (r < M) {
+            if (C0) v += beta * c0_at(C0, c32, (int64_t)r * P.ldc0 + col);
+            if (rs) v *= rs[r];
+          }
+          vals[e] = v;
+        }
+        if (D) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = r0 + e;
+            if (r < M && (!diag || r >= col)) store_at(D, d32, (int64_t)r * P.ldd + col, vals[e]);
+          }
+        }
+        if (Tt) {
+          if (!diag && r0 + 3 < M) {
+            const int64_t off = (int64_t)col * ldt + r0;
+            if (d32) {
+              *(float4*)((float*)Tt + off) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+            } else {
+              uint2 pk;
+              pk.x = (uint32_t)f32_to_bf16(vals[0]) | ((uint32_t)f32_to_bf16(vals[1]) << 16);
+              pk.y = (uint32_t)f32_to_bf16(vals[2]) | ((uint32_t)f32_to_bf16(vals[3]) << 16);
+              *(uint2*)((bf16_t*)Tt + off) = pk;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = r0 + e;
+              if (r < M && (!diag || r > col)) store_at(Tt, d32, (int64_t)col * ldt + r, vals[e]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename TIn, int BM, int BN>
+mao_status launch_cfg(GemmArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_nt_kernel<TIn, BM, BN>), dim3(args.total_tiles), dim3(kThreads), 0,
+                     stream, args);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+int count_tiles(GemmProblem* probs, int nprob, int bm) {
+  int64_t total = 0;
+  for (int i = 0; i < nprob; ++i) {
+    GemmProblem& p = probs[i];
+    if (p.M <= 0 || p.N <= 0 || p.batch <= 0) continue;
+    const int64_t tmi = ceil_div(p.M, bm), tni = ceil_div(p.N, bm);
+    total += (int64_t)p.batch * ((p.flags & GF_SYRK) ? tmi * (tmi + 1) / 2 : tmi * tni);
+  }
+  return (int)total;
+}
+
+}  // namespace
+
+mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t stream, int tag) {
+  if (nprob <= 0) return MAO_OK;
+  if (nprob > kMaxProblems) {
+    set_error("launch_gemm: %d problems > %d", nprob, kMaxProblems);
+    return MAO_E_UNSUPPORTED;
+  }
+  const int bm = count_tiles(probs, nprob, 128) >= 512 ? 128 : 64;
+  GemmArgs args = {};
+  int n = 0, total = 0;
+  for (int i = 0; i < nprob; ++i) {
+    GemmProblem p = probs[i];
+    if (p.M <= 0 || p.N <= 0 || p.batch <= 0) continue;
+    p.tiles_m = (int)ceil_div(p.M, bm);
+    p.tiles_n = (int)ceil_div(p.N, bm);
+    p.tiles_per_batch = (p.flags & GF_SYRK) ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
+    p.tile_begin = total;
+    total += p.batch * p.tiles_per_batch;
+    args.p[n++] = p;
+  }
+  if (n == 0) return MAO_OK;
+  args.nprob = n;
+  args.total_tiles = total;
+  void* ev = nullptr;
+  const bool timed = timing_on();
+  if (timed) timing_record_begin(stream, &ev);
+  mao_status st;
+  if (in_dtype == MAO_BF16)
+    st = bm == 128 ? launch_cfg<bf16_t, 128, 128>(args, stream) : launch_cfg<bf16_t, 64, 64>(args, stream);
+  else
+    st = bm == 128 ? launch_cfg<float, 128, 128>(args, stream) : launch_cfg<float, 64, 64>(args, stream);
+  if (timed) {
+    double flops = 0.0;
+    for (int i = 0; i < n; ++i) {
+      const GemmProblem& p = args.p[i];
+      const double mnk = (double)p.M * p.N * p.K * p.batch;
+      flops += (p.flags & GF_SYRK) ? mnk : 2.0 * mnk;
+    }
+    timing_record_end(stream, ev, tag, flops);
+  }
+  return st;
+}
+
+}  // namespace mao

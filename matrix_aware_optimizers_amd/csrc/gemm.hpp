@@ -1,0 +1,70 @@
+// NT contraction D = alpha * A B^T + beta * C0 on MFMA (gfx950), grouped over
+// up to kMaxProblems problems (each a strided batch) in one launch.
+#pragma once
+
+#include "common.hpp"
+
+namespace mao {
+
+enum GemmFlags : int {
+  GF_SYRK = 1,     // square symmetric result: lower-triangular tiles only, mirrored
+  GF_D_F32 = 2,    // D / Dt stored fp32 (else bf16)
+  GF_C0_F32 = 4,   // C0 stored fp32 (else bf16)
+};
+
+constexpr int kMaxProblems = 8;
+
+struct GemmProblem {
+  const void* A;     // M x K, row-major, lda (elements of the input dtype)
+  const void* B;     // N x K, row-major, ldb
+  const void* C0;    // M x N or nullptr
+  void* D;           // M x N or nullptr
+  void* Dt;          // N x M (transposed copy of D) or nullptr
+  const float* row_scale;  // D row i multiplied by row_scale[i] (or nullptr)
+  const int* pred;   // skip the problem when *pred == 0 (or nullptr)
+  int64_t lda, ldb, ldc0, ldd, lddt;
+  int64_t sA, sB, sC0, sD, sDt;  // batch strides (elements)
+  float alpha, beta;
+  int M, N, K, batch;
+  int flags;
+  // filled by the launcher
+  int tiles_m, tiles_n, tiles_per_batch, tile_begin;
+};
+
+struct GemmArgs {
+  GemmProblem p[kMaxProblems];
+  int nprob;
+  int total_tiles;
+};
+
+// What a launch computes, for the optional event timing (instrumentation).
+enum GemmTag : int { TAG_NS_GRAM = 0, TAG_NS_SQUARE = 1, TAG_NS_APPLY = 2, TAG_OTHER = 3,
+                     TAG_QR = 4, TAG_COUNT = 8 };
+
+// Enqueue one grouped launch. in_dtype: MAO_BF16 or MAO_F32. All problems of
+// a launch share the input dtype. Host-side shape checks are the caller's.
+mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t stream,
+                       int tag = TAG_OTHER);
+
+// Instrumentation: when enabled, every contraction launch is bracketed by HIP
+// events on its stream, with its algorithmic flop count (symmetric products
+// at half cost). Off by default.
+bool timing_on();
+void timing_record_begin(hipStream_t s, void** start);
+void timing_record_end(hipStream_t s, void* start, int tag, double flops);
+
+// Convenience for a single problem.
+inline GemmProblem gemm_problem(int M, int N, int K, float alpha, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, float beta, const void* C0,
+                                int64_t ldc0, void* D, int64_t ldd, int flags) {
+  GemmProblem p = {};
+  p.A = A; p.B = B; p.C0 = C0; p.D = D; p.Dt = nullptr;
+  p.row_scale = nullptr; p.pred = nullptr;
+  p.lda = lda; p.ldb = ldb; p.ldc0 = ldc0; p.ldd = ldd; p.lddt = 0;
+  p.alpha = alpha; p.beta = beta;
+  p.M = M; p.N = N; p.K = K; p.batch = 1;
+  p.flags = flags;
+  return p;
+}
+
+}  // namespace mao

@@ -1,0 +1,203 @@
+"""SOAP, FOAM and AdamW parity against the fp64 oracle (GPU).
+
+SOAP and FOAM are checked teacher-forced: at every step the oracle starts from
+the GPU's state after the previous step and the same gradient, so each step is
+judged on its own. The refreshed basis is checked by what defines it
+(orthonormal columns, Q^T P upper triangular with a non-negative diagonal, and
+agreement with the oracle's Q where P is well conditioned); the oracle then
+finishes the step with the GPU's basis and V, U must match to 1e-4 (fp32).
+Before the factors have been full rank for two steps (t < ceil(b/a) + 2) the
+basis completion is arbitrary and the elementwise Adam step is not
+rotation-equivariant, so those steps are reported, not gated.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import bf16_round
+from tests.helpers import log, rel, to_dev, to_host, w_bound
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def _soap_state_dev(m, n):
+    import torch
+    z = lambda r, c: torch.zeros((r, c), dtype=torch.float32, device="cuda")
+    return {"M": z(m, n), "V": z(m, n), "L": z(m, m), "R": z(n, n),
+            "QL": torch.eye(m, dtype=torch.float32, device="cuda"),
+            "QR": torch.eye(n, dtype=torch.float32, device="cuda")}
+
+
+def _host_soap(st):
+    return oracle.SoapState(*(to_host(st[k]) for k in ("M", "V", "L", "R", "QL", "QR")))
+
+
+def _check_basis(q, p, q_ref, tag):
+    """q: GPU basis; p: the oracle's power-iteration product; q_ref: its QR."""
+    n = q.shape[0]
+    orth = np.abs(q.T @ q - np.eye(n)).max()
+    assert orth < 1e-4, f"{tag}: orthogonality {orth}"
+    rr = q.T @ p
+    scale = np.linalg.norm(p)
+    assert np.linalg.norm(np.tril(rr, -1)) <= 1e-4 * scale, f"{tag}: Q^T P not triangular"
+    assert np.all(np.diag(rr) >= -1e-5 * scale), f"{tag}: negative diagonal"
+    s = np.linalg.svd(p, compute_uv=False)
+    kappa = s[0] / s[-1] if s[-1] > 0 else np.inf
+    if kappa * 2.0 ** -24 <= 1e-5:
+        fe = rel(q, q_ref)
+        assert fe < 1e-4, f"{tag}: forward error {fe} at kappa {kappa:.1e}"
+
+
+def _run_soap(gpu_lib, m, n, steps, grad, dtype="f32", refresh_every=1):
+    import torch
+    W = to_dev(synth.init_weight("c1", synth.MatrixSpec("w", m, n, 7)), dtype)
+    st = _soap_state_dev(m, n)
+    out = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    t0 = math.ceil(max(m, n) / min(m, n)) + 2
+    free_w = to_host(W)
+    free_state = oracle.soap_init(m, n)
+    for t in range(1, steps + 1):
+        g = grad(t)
+        if dtype == "bf16":
+            g = bf16_round(g)
+        prev = _host_soap(st)
+        w_prev = to_host(W)
+        gpu_lib.soap_step(W, to_dev(g, dtype), st, t, update_out=out, refresh_every=refresh_every,
+                          **HP)
+        torch.cuda.synchronize()
+        new = _host_soap(st)
+        # EMAs from the GPU's previous state
+        _, ref, _, info = oracle.soap_step(w_prev, g, prev, t, refresh_every=refresh_every, **HP)
+        assert rel(new.M, ref.M) < 1e-5 and rel(new.L, ref.L) < 1e-5 and rel(new.R, ref.R) < 1e-5
+        if "PL" in info:
+            _check_basis(new.QL, info["PL"], ref.QL, f"t={t} QL")
+            _check_basis(new.QR, info["PR"], ref.QR, f"t={t} QR")
+        # finish the step with the GPU's basis
+        w_ref, ref2, upd_ref, _ = oracle.soap_step(w_prev, g, prev, t, refresh_every=0,
+                                                   q_override=(new.QL, new.QR), **HP)
+        eu = rel(to_host(out), upd_ref)
+        ev = rel(new.V, ref2.V)
+        free_w, free_state, free_upd, _ = oracle.soap_step(free_w, g, free_state, t,
+                                                           refresh_every=refresh_every, **HP)
+        log(f"  soap t={t}: update {eu:.2e}  V {ev:.2e}  (free-running {rel(to_host(out), free_upd):.2e})")
+        if t >= t0:
+            assert eu < 1e-4 and ev < 1e-4, f"t={t}: update {eu}, V {ev}"
+            if dtype == "f32":
+                assert rel(to_host(W), w_ref) < 1e-5
+
+
+def test_soap_c1_teacher_forced(gpu_lib):
+    """256x512 fp32, Q_L = Q_R = I at t = 1, refresh every step, 10 steps."""
+    log("soap c1")
+    spec = synth.specs("c1")[0]
+    _run_soap(gpu_lib, 256, 512, 10, lambda t: synth.gradient("c1", spec, t))
+
+
+def test_soap_kronecker_ragged(gpu_lib):
+    """Kronecker-structured gradients (k^-1 spectra) on a ragged tall shape."""
+    log("soap kronecker 328x200")
+    spec = synth.MatrixSpec("k", 328, 200, 3)
+    _run_soap(gpu_lib, 328, 200, 6, lambda t: synth.kronecker_gradient("c3", spec, t))
+
+
+def test_soap_bf16_gradient_and_frozen_basis(gpu_lib):
+    log("soap bf16 frozen")
+    spec = synth.MatrixSpec("k", 96, 160, 4)
+    _run_soap(gpu_lib, 96, 160, 4, lambda t: synth.kronecker_gradient("c3", spec, t),
+              dtype="bf16", refresh_every=0)
+
+
+# ---------------------------------------------------------------------------
+
+def _foam_state_dev(m, n):
+    import torch
+    return {"M": torch.zeros((m, n), dtype=torch.float32, device="cuda"),
+            "R": torch.zeros((n, n), dtype=torch.float32, device="cuda"),
+            "QR": torch.eye(n, dtype=torch.float32, device="cuda"),
+            "r": torch.zeros(m, dtype=torch.float32, device="cuda"),
+            "c": torch.zeros(n, dtype=torch.float32, device="cuda"),
+            "aux": torch.zeros(8, dtype=torch.float32, device="cuda")}
+
+
+def _host_foam(st):
+    return oracle.FoamState(to_host(st["M"]), to_host(st["R"]), to_host(st["QR"]),
+                            to_host(st["r"]), to_host(st["c"]))
+
+
+@pytest.mark.parametrize("m,n,pf", [(160, 96, 3), (96, 264, 4)])
+def test_foam_teacher_forced(gpu_lib, m, n, pf):
+    import torch
+    log(f"foam {m}x{n} pf={pf}")
+    spec = synth.MatrixSpec("f", m, n, 5)
+    W = to_dev(synth.init_weight("c5", spec))
+    st = _foam_state_dev(m, n)
+    out = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    t0 = math.ceil(max(m, n) / min(m, n)) + 2
+    for t in range(1, 10):
+        g = synth.kronecker_gradient("c5", spec, t)
+        prev = _host_foam(st)
+        w_prev = to_host(W)
+        gpu_lib.foam_step(W, to_dev(g), st, t, update_out=out, pf=pf, tol=0.1, **HP)
+        torch.cuda.synchronize()
+        new = _host_foam(st)
+        aux = to_host(st["aux"])
+        _, ref, _, info = oracle.foam_step(w_prev, g, prev, t, pf=pf, tol=0.1, **HP)
+        assert bool(aux[3]) == info["checked"]
+        assert rel(new.M, ref.M) < 1e-5 and rel(new.R, ref.R) < 1e-5
+        decision = info["refreshed"]
+        if info["checked"]:
+            assert abs(aux[0] - info["rho"]) < 1e-4
+            if abs(info["rho"] - 0.1) > 1e-4:
+                assert bool(aux[1]) == info["refreshed"]
+            decision = bool(aux[1])
+            if decision:
+                _check_basis(new.QR, info["P"], ref.QR, f"t={t} QR")
+        if not decision:
+            assert np.array_equal(new.QR, prev.QR)
+        w_ref, ref2, upd_ref, info2 = oracle.foam_step(w_prev, g, prev, t, pf=pf, tol=0.1,
+                                                       q_override=new.QR,
+                                                       refresh_override=decision, **HP)
+        eu = rel(to_host(out), upd_ref)
+        er, ec = rel(new.r, ref2.r), rel(new.c, ref2.c)
+        log(f"  foam t={t}: update {eu:.2e} r {er:.2e} c {ec:.2e} rho {aux[0]:.3f} refresh {decision}")
+        if t >= t0:
+            assert eu < 1e-4 and er < 1e-4 and ec < 1e-4
+            assert abs(aux[2] - info2["tau"]) <= 1e-4 * abs(info2["tau"])
+            assert rel(to_host(W), w_ref) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+def test_adamw_flat_ragged(gpu_lib, wdt):
+    import torch
+    n = 1_000_003
+    r = np.random.default_rng(17)
+    w = (0.02 * r.standard_normal(n)).astype(np.float32)
+    if wdt == "bf16":
+        w = bf16_round(w)
+    W = to_dev(w, wdt)
+    m = torch.zeros(n, dtype=torch.float32, device="cuda")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda")
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    mr, vr = np.zeros(n), np.zeros(n)
+    for t in range(1, 4):
+        g = r.standard_normal(n).astype(np.float32)
+        w_prev = to_host(W)
+        gpu_lib.adamw_step(W, to_dev(g), m, v, t, update_out=out, **HP)
+        torch.cuda.synchronize()
+        w_ref, mr, vr, u_ref = oracle.adamw_step(w_prev, g, mr, vr, t, **HP)
+        assert rel(to_host(out), u_ref) < 1e-5
+        assert rel(to_host(m), mr) < 1e-6 and rel(to_host(v), vr) < 1e-6
+        if wdt == "bf16":
+            lr_term = HP["lr"] * (HP["weight_decay"] * w_prev + to_host(out))
+            w_expect = w_prev - lr_term
+            assert np.all(np.abs(to_host(W) - bf16_round(w_expect.astype(np.float32))) <=
+                          w_bound(w_expect, w_prev, lr_term))
+        else:
+            assert rel(to_host(W), w_ref) < 1e-6
