@@ -56,7 +56,8 @@ def ns_alg_flops(m: int, n: int, k: int = 5) -> float:
 # ---------------------------------------------------------------------------
 
 class MuonWorkload:
-    def __init__(self, groups_spec, dtype="bf16", norm_mode="none", seed_config="c2"):
+    def __init__(self, groups_spec, dtype="bf16", norm_mode="none", seed_config="c2",
+                 ns_dtype="bf16"):
         import torch
 
         import matrix_aware_optimizers_amd as mao
@@ -64,7 +65,7 @@ class MuonWorkload:
         self.mao = mao
         self.lib = mao.load()
         self.hp = mao.muon_hparams(lr=1e-3, mu=0.95, weight_decay=0.1, eps=1e-7, ns_steps=5,
-                                   ns_dtype="bf16", norm_mode=norm_mode)
+                                   ns_dtype=ns_dtype, norm_mode=norm_mode)
         tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.tensors = []
         self.shapes = []
@@ -142,12 +143,13 @@ def cpu_baseline_muon(sample_rows: int, sample_cols: int, total_ns_flops: float,
                        f"(x{scale:.2f}) to the whole set")}
 
 
-def run_muon(args, workload_name, groups, norm_mode, sample):
+def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
     import torch
 
     import matrix_aware_optimizers_amd as mao
     log(f"setting up {workload_name}")
-    wl = MuonWorkload(groups, norm_mode=norm_mode, seed_config=sample[2])
+    wl = MuonWorkload(groups, dtype=dtype, norm_mode=norm_mode, seed_config=sample[2],
+                      ns_dtype=dtype)
     log("warmup")
     for i in range(args.warmup):
         wl.step(i)
@@ -184,16 +186,19 @@ def run_muon(args, workload_name, groups, norm_mode, sample):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": workload_name,
                    "matrices": [f"{c}x{m}x{n}" for c, m, n in wl.shapes],
-                   "ns_steps": 5, "ns_dtype": "bf16", "norm_mode": norm_mode,
-                   "weights": "bf16", "momentum": "fp32"},
+                   "ns_steps": 5, "ns_dtype": dtype, "norm_mode": norm_mode,
+                   "weights": dtype, "momentum": "fp32"},
         "step_tflops_alg": wl.ns_flops() / (ms * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "gemm_nt_kernel (Newton-Schulz X X^T, A A, B X)",
+        "roofline": {"bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": achieved / (PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS),
+                     "traffic": None,
+                     "kernel": "Newton-Schulz contraction (X X^T, A A, B X)",
                      "launches": ns_cnt, "avg_launch_ms": ns_ms / max(ns_cnt, 1),
                      "alg_tflop_per_launch": ns_fl / max(ns_cnt, 1) / 1e12},
         "kernels": per_tag,
@@ -206,6 +211,158 @@ def run_muon(args, workload_name, groups, norm_mode, sample):
 
 
 # ---------------------------------------------------------------------------
+# SOAP / FOAM workloads
+# ---------------------------------------------------------------------------
+
+def _padded_empty(torch, rows, cols, dtype):
+    ld = (cols + 7) // 8 * 8
+    return torch.empty((rows, ld), dtype=dtype, device="cuda")[:, :cols]
+
+
+def soap_alg_flops(m, n, refresh=True):
+    """SYRK m^2 n + n^2 m (half cost), refresh 2(m^3 + n^3) (F Q) + 8/3 (m^3 + n^3)
+    (Householder QR with explicit Q), rotations 2 x (2mn(m + n)) forward (G, M)
+    and 2mn(m + n) back."""
+    f = m * m * n + n * n * m + 6.0 * m * n * (m + n)
+    if refresh:
+        f += (2.0 + 8.0 / 3.0) * (m ** 3 + n ** 3)
+    return f
+
+
+def foam_alg_flops(m, n, checked=False, refreshed=False):
+    """SYRK n^2 m (half cost), rotations 2 x 2mn^2 (G, M) + back 2mn^2; a check
+    adds 4 n^3, a refresh 8/3 n^3."""
+    f = n * n * m + 6.0 * m * n * n
+    if checked:
+        f += 4.0 * n ** 3
+    if refreshed:
+        f += 8.0 / 3.0 * n ** 3
+    return f
+
+
+class SoapLikeWorkload:
+    """A set of matrices stepped one after another by soap_step or foam_step
+    (one shared workspace), with a ring of two gradients per matrix."""
+
+    def __init__(self, kind, config, specs, g_dtype, w_dtype, pf=10, tol=0.1):
+        import torch
+
+        import matrix_aware_optimizers_amd as mao
+        import synth
+        self.mao, self.lib, self.kind = mao, mao.load(), kind
+        self.items = []
+        tg = torch.bfloat16 if g_dtype == "bf16" else torch.float32
+        tw = torch.bfloat16 if w_dtype == "bf16" else torch.float32
+        if kind == "soap":
+            self.hp = mao.soap_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+                                       refresh_every=1)
+        else:
+            self.hp = mao.foam_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+                                       pf=pf, tol=tol)
+        need = 0
+        for sp in specs:
+            m, n = sp.rows, sp.cols
+            W = _padded_empty(torch, m, n, tw)
+            W.copy_(torch.from_numpy(synth.init_weight(config, sp)))
+            Gs = []
+            for k in range(2):
+                G = _padded_empty(torch, m, n, tg)
+                G.copy_(torch.from_numpy(synth.gradient(config, sp, k + 1)))
+                Gs.append(G)
+            z = lambda r, c: _padded_empty(torch, r, c, torch.float32).zero_()
+            if kind == "soap":
+                st = {"M": z(m, n), "V": z(m, n), "L": z(m, m), "R": z(n, n),
+                      "QL": z(m, m), "QR": z(n, n)}
+                st["QL"].fill_diagonal_(1.0)
+                st["QR"].fill_diagonal_(1.0)
+                cst = mao.soap_state(st["M"], st["V"], st["L"], st["R"], st["QL"], st["QR"])
+                need = max(need, self.lib.soap_workspace_size(m, n, ctypes.byref(self.hp)))
+            else:
+                st = {"M": z(m, n), "R": z(n, n), "QR": z(n, n),
+                      "r": torch.zeros(m, device="cuda"), "c": torch.zeros(n, device="cuda"),
+                      "aux": torch.zeros(4, device="cuda")}
+                st["QR"].fill_diagonal_(1.0)
+                cst = mao.FoamStateC(mao.mat(st["M"]), mao.mat(st["R"]), mao.mat(st["QR"]),
+                                     st["r"].data_ptr(), st["c"].data_ptr(), st["aux"].data_ptr())
+                need = max(need, self.lib.foam_workspace_size(m, n, ctypes.byref(self.hp)))
+            self.items.append((sp, W, Gs, st, cst, mao.mat(W), [mao.mat(G) for G in Gs]))
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.embedding = None
+        torch.cuda.synchronize()
+
+    def add_embedding(self, rows, cols):
+        import torch
+
+        import synth
+        w = (0.02 * torch.randn(rows, cols, generator=torch.Generator().manual_seed(5))).cuda()
+        g = [torch.from_numpy(synth.embedding_gradient(k + 1, rows, cols)).cuda() for k in range(2)]
+        self.embedding = (w, g, torch.zeros_like(w), torch.zeros_like(w))
+
+    def step(self, t: int):
+        fn = self.lib.soap_step if self.kind == "soap" else self.lib.foam_step
+        for sp, W, Gs, st, cst, wm, gms in self.items:
+            rc = fn(wm, gms[t % 2], ctypes.byref(cst), t, ctypes.byref(self.hp),
+                    ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), None, self.stream)
+            if rc != 0:
+                self.mao._check(rc, self.kind + "_step")
+        if self.embedding is not None:
+            w, g, m, v = self.embedding
+            rc = self.lib.adamw_step(w.data_ptr(), 0, g[t % 2].data_ptr(), 0, m.data_ptr(),
+                                     v.data_ptr(), w.numel(), t, 1e-3, 0.9, 0.95, 1e-8, 0.1, None,
+                                     self.stream)
+            if rc != 0:
+                self.mao._check(rc, "adamw_step")
+
+
+def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, embedding=None):
+    import torch
+
+    import matrix_aware_optimizers_amd as mao
+    log(f"setting up {workload_name} ({len(specs)} matrices)")
+    wl = SoapLikeWorkload(kind, config, specs, g_dtype, w_dtype)
+    if embedding:
+        wl.add_embedding(*embedding)
+    log("warmup")
+    t = 1
+    for _ in range(args.warmup):
+        wl.step(t)
+        t += 1
+    torch.cuda.synchronize()
+    mao.timing_collect()
+    mao.timing_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        wl.step(t)
+        t += 1
+    end.record()
+    torch.cuda.synchronize()
+    mao.timing_enable(False)
+    tim = mao.timing_collect()
+    ms = start.elapsed_time(end) / args.steps
+    per_tag = {k: {"ms_total": round(v[0], 4), "launches": v[1],
+                   "tflops": round(v[2] / (v[0] * 1e-3) / 1e12, 2) if v[0] > 0 else 0.0}
+               for k, v in tim.items() if v[1] > 0}
+    gemm_ms = sum(v[0] for v in tim.values())
+    gemm_fl = sum(v[2] for v in tim.values())
+    achieved = gemm_fl / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
+    log(f"{ms:.3f} ms/step; contractions {gemm_ms / args.steps:.3f} ms/step at {achieved:.1f} TFLOP/s")
+    return {
+        "metric": METRIC, "value": 1000.0 / ms, "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": workload_name, "matrices": len(specs), "optimizer": kind,
+                   "gradients": g_dtype, "weights": w_dtype},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
+                     "kernel": "gemm_nt_kernel<float> (all fp32 contractions)"},
+        "kernels": per_tag,
+    }
+
+
+# ---------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -213,8 +370,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b",
-                    choices=["llama8b", "moe"])
+                    choices=["llama8b", "moe", "c1muon", "c1soap", "soap8b", "foam760m",
+                             "soap760m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (a known-size reference "
+                         "for profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build's step runs whole matrices on one device "
@@ -224,12 +385,39 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB read + 1 GiB written")
+        del src, dst
     if args.workload == "llama8b":
         line = run_muon(args, "llama8b_layer_muon_bf16", llama8b_groups(), "none",
                         (4096, 4096, "c2", 1))
-    else:
+    elif args.workload == "moe":
         line = run_muon(args, "moe128_expert_bank_muonplus_bf16", moe_groups(), "col_row",
                         (1536, 2048, "c4", 0))
+    elif args.workload == "c1muon":
+        import synth
+        line = run_muon(args, "single_256x512_muon_f32", [("w", synth.specs("c1"))], "none",
+                        (256, 512, "c1", 0), dtype="f32")
+    elif args.workload == "c1soap":
+        import synth
+        line = run_soaplike(args, "single_256x512_soap_f32", "soap", "c1", synth.specs("c1"),
+                            "f32", "f32")
+    elif args.workload == "soap8b":
+        import synth
+        line = run_soaplike(args, "llama8b_layer_soap", "soap", "c3", synth.specs("c3"),
+                            "bf16", "bf16")
+    elif args.workload == "foam760m":
+        import synth
+        line = run_soaplike(args, "gpt2_760m_foam", "foam", "c5", synth.specs("c5"), "f32", "f32",
+                            embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH))
+    else:
+        import synth
+        line = run_soaplike(args, "gpt2_760m_soap", "soap", "c5", synth.specs("c5"), "f32", "f32")
     print(json.dumps(line), flush=True)
 
 

@@ -117,8 +117,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
   const TIn* B = (const TIn*)P.B + (int64_t)b * P.sB;
   const int64_t lda = P.lda, ldb = P.ldb;
 
-  uint4 ra[CA], rb[CB];
-  auto gload = [&](int k0) {
+  // Two register sets in flight: while slice k is multiplied out of LDS, the
+  // slices k+1 and k+2 are on their way from memory.
+  uint4 ra0[CA], rb0[CB], ra1[CA], rb1[CB];
+  auto gload = [&](uint4* ra, uint4* rb, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
       const int q = threadIdx.x + c * kThreads;
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
                        : make_uint4(0, 0, 0, 0);
     }
   };
-  auto lstore = [&](int stage) {
+  auto lstore = [&](const uint4* ra, const uint4* rb, int stage) __attribute__((always_inline)) {
     unsigned char* base = lds + stage * kStage;
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
@@ -164,32 +166,26 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
 
   auto compute = [&](int stage) {
     const unsigned char* base = lds + stage * kStage;
-    uint4 af[FM][4], bfr[FN][4];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const unsigned char* p = base + (wm * (BM / 2) + i * 32 + r32) * kLdsRow + h * 64;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) af[i][c] = *(const uint4*)(p + c * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const unsigned char* p = base + (BM + wn * (BN / 2) + j * 32 + r32) * kLdsRow + h * 64;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bfr[j][c] = *(const uint4*)(p + c * 16);
-    }
+    const unsigned char* pa = base + (wm * (BM / 2) + r32) * kLdsRow + h * 64;
+    const unsigned char* pb = base + (BM + wn * (BN / 2) + r32) * kLdsRow + h * 64;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      uint4 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *(const uint4*)(pa + i * 32 * kLdsRow + c * 16);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *(const uint4*)(pb + j * 32 * kLdsRow + c * 16);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           if constexpr (sizeof(TIn) == 2) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, af[i][c]), __builtin_bit_cast(bf16x8_t, bfr[j][c]),
+                __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bfr[j]),
                 acc[i][j], 0, 0, 0);
           } else {
-            const uint32_t* a4 = (const uint32_t*)&af[i][c];
-            const uint32_t* b4 = (const uint32_t*)&bfr[j][c];
+            const uint32_t* a4 = (const uint32_t*)&af[i];
+            const uint32_t* b4 = (const uint32_t*)&bfr[j];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
@@ -202,19 +198,26 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
 
   const int nk = (K + BK - 1) / BK;
   if (nk > 0) {
-    gload(0);
-    lstore(0);
+    gload(ra0, rb0, 0);
+    if (nk > 1) gload(ra1, rb1, BK);
+    lstore(ra0, rb0, 0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * BK);
-      compute(cur);
-      if (kt + 1 < nk) lstore(cur ^ 1);
+    // invariant at the top of iteration kt: LDS stage kt&1 holds slice kt,
+    // set (kt&1 ? 0 : 1) holds slice kt+1 (in flight)
+    for (int kt = 0; kt < nk; kt += 2) {
+      if (kt + 2 < nk) gload(ra0, rb0, (kt + 2) * BK);
+      compute(0);
+      if (kt + 1 < nk) lstore(ra1, rb1, 1);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      if (kt + 3 < nk) gload(ra1, rb1, (kt + 3) * BK);
+      compute(1);
+      if (kt + 2 < nk) lstore(ra0, rb0, 0);
       __syncthreads();
     }
   }
 
-  // ---- epilogue ---------------------------------------------------------
+  // ---- epilogue: one 64-row slab of the tile at a time through LDS --------
   const bool diag = syrk && (tm == tn);
   const bool d32 = (P.flags & GF_D_F32) != 0;
   const bool c32 = (P.flags & GF_C0_F32) != 0;
@@ -226,53 +229,102 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
   const float alpha = P.alpha, beta = P.beta;
   const float* rs = P.row_scale;
 
+  constexpr int SLD = BN + 1;  // padded slab row (floats)
+  float* slab = (float*)lds;
+  constexpr int CPR = BN / 4;         // 4-wide chunks per slab row
+  constexpr int RPI = kThreads / CPR; // slab rows per pass of the block
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * (BN / 2) + j * 32 + r32;
-      const int rbase = m0 + wm * (BM / 2) + i * 32 + 4 * h;
-      if (col >= N) continue;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = rbase + 8 * g;
-        if (r0 >= M) continue;
-        float vals[4];
+      for (int v = 0; v < 16; ++v) {
+        const int sr = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int sc = wn * (BN / 2) + j * 32 + r32;
+        slab[sr * SLD + sc] = acc[i][j][v];
+      }
+    __syncthreads();
+    // direct: D[r][c] = alpha acc + beta C0, row-scaled; final values kept in LDS
+    const int c4 = (threadIdx.x % CPR) * 4;
+    const int gcol = n0 + c4;
+    for (int sr = threadIdx.x / CPR; sr < 64; sr += RPI) {
+      const int grow = m0 + (sr >> 5) * (BM / 2) + i * 32 + (sr & 31);
+      float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = r0 + e;
-          float v = alpha * acc[i][j][4 * g + e];
-          if (r < M) {
-            if (C0) v += beta * c0_at(C0, c32, (int64_t)r * P.ldc0 + col);
-            if (rs) v *= rs[r];
+      for (int e = 0; e < 4; ++e) v[e] = alpha * slab[sr * SLD + c4 + e];
+      if (grow < M) {
+        const bool full = gcol + 3 < N;
+        if (C0) {
+          const int64_t off = (int64_t)grow * P.ldc0 + gcol;
+          if (full && c32) {
+            const float4 c = *(const float4*)((const float*)C0 + off);
+            v[0] += beta * c.x; v[1] += beta * c.y; v[2] += beta * c.z; v[3] += beta * c.w;
+          } else if (full) {
+            const uint2 c = *(const uint2*)((const bf16_t*)C0 + off);
+            v[0] += beta * bf16_to_f32((bf16_t)(c.x & 0xffff));
+            v[1] += beta * bf16_to_f32((bf16_t)(c.x >> 16));
+            v[2] += beta * bf16_to_f32((bf16_t)(c.y & 0xffff));
+            v[3] += beta * bf16_to_f32((bf16_t)(c.y >> 16));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gcol + e < N) v[e] += beta * c0_at(C0, c32, off + e);
           }
-          vals[e] = v;
+        }
+        if (rs) {
+          const float sc = rs[grow];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= sc;
         }
         if (D) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = r0 + e;
-            if (r < M && (!diag || r >= col)) store_at(D, d32, (int64_t)r * P.ldd + col, vals[e]);
-          }
-        }
-        if (Tt) {
-          if (!diag && r0 + 3 < M) {
-            const int64_t off = (int64_t)col * ldt + r0;
+          const int64_t off = (int64_t)grow * P.ldd + gcol;
+          if (full && !diag) {
             if (d32) {
-              *(float4*)((float*)Tt + off) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+              *(float4*)((float*)D + off) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
               uint2 pk;
-              pk.x = (uint32_t)f32_to_bf16(vals[0]) | ((uint32_t)f32_to_bf16(vals[1]) << 16);
-              pk.y = (uint32_t)f32_to_bf16(vals[2]) | ((uint32_t)f32_to_bf16(vals[3]) << 16);
-              *(uint2*)((bf16_t*)Tt + off) = pk;
+              pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+              pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+              *(uint2*)((bf16_t*)D + off) = pk;
             }
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = r0 + e;
-              if (r < M && (!diag || r > col)) store_at(Tt, d32, (int64_t)col * ldt + r, vals[e]);
-            }
+            for (int e = 0; e < 4; ++e)
+              if (gcol + e < N && (!diag || grow >= gcol + e)) store_at(D, d32, off + e, v[e]);
           }
+        }
+      }
+      if (Tt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) slab[sr * SLD + c4 + e] = v[e];
+      }
+    }
+    if (Tt) {
+      __syncthreads();
+      // transposed: Tt[c][r .. r+3] from four consecutive slab rows
+      const int sr4 = (threadIdx.x & 15) * 4;
+      const int grow = m0 + (sr4 >> 5) * (BM / 2) + i * 32 + (sr4 & 31);
+      for (int sc = threadIdx.x >> 4; sc < BN; sc += kThreads / 16) {
+        const int gc = n0 + sc;
+        if (gc >= N || grow >= M) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = slab[(sr4 + e) * SLD + sc];
+        const int64_t off = (int64_t)gc * ldt + grow;
+        if (!diag && grow + 3 < M) {
+          if (d32) {
+            *(float4*)((float*)Tt + off) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+            *(uint2*)((bf16_t*)Tt + off) = pk;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (grow + e < M && (!diag || grow + e > gc)) store_at(Tt, d32, off + e, v[e]);
         }
       }
     }
@@ -306,7 +358,8 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
     set_error("launch_gemm: %d problems > %d", nprob, kMaxProblems);
     return MAO_E_UNSUPPORTED;
   }
-  const int bm = count_tiles(probs, nprob, 128) >= 512 ? 128 : 64;
+  const int bm = (in_dtype == MAO_BF16 && count_tiles(probs, nprob, 256) >= 128) ? 256
+                 : count_tiles(probs, nprob, 128) >= 512 ? 128 : 64;
   GemmArgs args = {};
   int n = 0, total = 0;
   for (int i = 0; i < nprob; ++i) {
@@ -327,7 +380,8 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
   if (timed) timing_record_begin(stream, &ev);
   mao_status st;
   if (in_dtype == MAO_BF16)
-    st = bm == 128 ? launch_cfg<bf16_t, 128, 128>(args, stream) : launch_cfg<bf16_t, 64, 64>(args, stream);
+    st = bm == 256 ? launch_gemm_bf16_direct(args, stream)
+         : bm == 128 ? launch_cfg<bf16_t, 128, 128>(args, stream) : launch_cfg<bf16_t, 64, 64>(args, stream);
   else
     st = bm == 128 ? launch_cfg<float, 128, 128>(args, stream) : launch_cfg<float, 64, 64>(args, stream);
   if (timed) {

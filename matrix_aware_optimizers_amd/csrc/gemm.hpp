@@ -46,6 +46,10 @@ enum GemmTag : int { TAG_NS_GRAM = 0, TAG_NS_SQUARE = 1, TAG_NS_APPLY = 2, TAG_O
 mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t stream,
                        int tag = TAG_OTHER);
 
+// bf16 path for large problems: 256 x 256 tiles, operands streamed into a
+// four-stage LDS ring (gemm_bf16.hip). Same semantics as gemm_nt_kernel.
+mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream);
+
 // Instrumentation: when enabled, every contraction launch is bracketed by HIP
 // events on its stream, with its algorithmic flop count (symmetric products
 // at half cost). Off by default.

@@ -1,0 +1,435 @@
+// Large bf16 NT contractions (the Newton-Schulz products) with operands
+// streamed straight from memory into LDS.
+//
+// D[i][j] = alpha * sum_k A[i][k] * B[j][k] + beta * C0[i][j], bf16 inputs,
+// fp32 accumulation on v_mfma_f32_32x32x16_bf16.
+//
+// Workgroup tile 256 x 256, 4 wavefronts in 2 x 2, each wavefront 128 x 128
+// (4 x 4 MFMA blocks, 256 fp32 accumulators per lane). K advances in slices of
+// 32 elements (64 bytes per tile row). Slices go global -> LDS with
+// global_load_lds_dwordx4 (no staging registers) into a ring of four LDS
+// stages, so three slices are in flight while one is multiplied; each stage is
+// its own LDS object, which lets the wait on the oldest slice be an exact
+// vmcnt rather than a full drain. Inside a stage a row's four 16-byte chunks
+// are XOR-permuted by bits 1-3 of the row index, so the 16-byte MFMA operand
+// reads of 16 consecutive rows hit distinct banks. A partial last slice
+// (K not a multiple of 32) goes through registers with zero fill.
+//
+// Rows beyond M (or N) read a clamped, valid row; they only feed output rows
+// (columns) that are never stored.
+//
+// The epilogue stages each 32 x 256 band of the tile through LDS: coalesced
+// stores of D, C0 blend, optional row scale, and the transposed copy (or the
+// SYRK mirror) written from LDS columns.
+#include "gemm.hpp"
+
+#include <type_traits>
+
+namespace mao {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+constexpr int TB = 256;          // tile rows and columns
+constexpr int KS = 32;           // K elements per slice
+constexpr int ROWB = 64;         // bytes per tile row per slice
+constexpr int STAGE = 2 * TB * ROWB;  // A and B of one slice: 32 KB
+constexpr int LPT = (TB * ROWB / 16) / 256;  // 16-byte loads per thread per operand = 4
+constexpr int SLAB_LD = TB + 1;
+constexpr int SLAB_BYTES = 32 * SLAB_LD * 4;  // 32 rows of the output tile
+
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (gfx9 field layout:
+// vmcnt low bits [3:0], high bits [15:14], expcnt [6:4], lgkmcnt [11:8]).
+#define MAO_VMCNT(n) ((((n) & 0xf)) | (0x7 << 4) | (0xf << 8) | ((((n) >> 4) & 0x3) << 14))
+template <int N>
+__device__ __forceinline__ void vm_wait_c() { __builtin_amdgcn_s_waitcnt(MAO_VMCNT(N)); }
+#define vm_wait(n) vm_wait_c<(n)>()
+
+__device__ __forceinline__ float c0_load(const void* C0, bool f32, int64_t off) {
+  return f32 ? ((const float*)C0)[off] : bf16_to_f32(((const bf16_t*)C0)[off]);
+}
+
+__device__ __forceinline__ void d_store(void* D, bool f32, int64_t off, float v) {
+  if (f32)
+    ((float*)D)[off] = v;
+  else
+    ((bf16_t*)D)[off] = f32_to_bf16(v);
+}
+
+// Interior, non-diagonal tiles: stores straight from the accumulators. Lane
+// (h, r32) of block (i, j) holds rows 8g + 4h + e (g, e < 4) of column r32;
+// each store instruction covers 32 consecutive columns of two rows, and the
+// transposed copy takes four consecutive rows as one vector.
+template <bool D32, bool C32>
+__device__ __forceinline__ void epilogue_block(const f32x16_t& a, int r_base, int col, float alpha,
+                                               float beta, const void* C0, int64_t ldc0,
+                                               const float* rs, void* D, int64_t ldd, void* Tt,
+                                               int64_t ldt) {
+  typedef typename std::conditional<D32, float, bf16_t>::type TD;
+  typedef typename std::conditional<C32, float, bf16_t>::type TC;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int r0 = r_base + 8 * g;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = alpha * a[4 * g + e];
+      if (C0) v[e] += beta * load_f32<TC>((const TC*)C0 + (int64_t)(r0 + e) * ldc0 + col);
+      if (rs) v[e] *= rs[r0 + e];
+    }
+    if (D) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_f32<TD>((TD*)D + (int64_t)(r0 + e) * ldd + col, v[e]);
+    }
+    if (Tt) {
+      TD* q = (TD*)Tt + (int64_t)col * ldt + r0;
+      if constexpr (D32) {
+        *(float4*)q = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(uint2*)q = pk;
+      }
+    }
+  }
+}
+
+// Interior, non-diagonal tiles: stores straight from the accumulators. Lane
+// (h, r32) of block (i, j) holds rows 8g + 4h + e (g, e < 4) of column r32;
+// each store instruction covers 32 consecutive columns of two rows, and the
+// transposed copy takes four consecutive rows as one vector. Blocks are named
+// one by one so every accumulator index is a constant.
+template <bool D32, bool C32>
+__device__ __forceinline__ void epilogue_direct(const f32x16_t (&acc)[4][4], int m0, int n0,
+                                                int wm, int wn, int h, int r32, float alpha,
+                                                float beta, const void* C0, int64_t ldc0,
+                                                const float* rs, void* D, int64_t ldd, void* Tt,
+                                                int64_t ldt) {
+#define MAO_EPI(I, J)                                                                        \
+  epilogue_block<D32, C32>(acc[I][J], m0 + wm * 128 + (I) * 32 + 4 * h,                       \
+                           n0 + wn * 128 + (J) * 32 + r32, alpha, beta, C0, ldc0, rs, D, ldd, \
+                           Tt, ldt);
+  MAO_EPI(0, 0) MAO_EPI(0, 1) MAO_EPI(0, 2) MAO_EPI(0, 3)
+  MAO_EPI(1, 0) MAO_EPI(1, 1) MAO_EPI(1, 2) MAO_EPI(1, 3)
+  MAO_EPI(2, 0) MAO_EPI(2, 1) MAO_EPI(2, 2) MAO_EPI(2, 3)
+  MAO_EPI(3, 0) MAO_EPI(3, 1) MAO_EPI(3, 2) MAO_EPI(3, 3)
+#undef MAO_EPI
+}
+
+__global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE > SLAB_BYTES ? STAGE : SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[STAGE];
+
+  // ---- tile --------------------------------------------------------------
+  const int total = args.total_tiles;
+  const int bid = blockIdx.x;
+  const int per = total >> 3, rem = total & 7;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int t = xcd * per + min(xcd, rem) + idx;
+  int pi = 0;
+  for (int q = 1; q < args.nprob; ++q)
+    if (t >= args.p[q].tile_begin) pi = q;
+  const GemmProblem& P = args.p[pi];
+  if (P.pred != nullptr && *P.pred == 0) return;
+  int local = t - P.tile_begin;
+  const int b = local / P.tiles_per_batch;
+  local -= b * P.tiles_per_batch;
+  int tm, tn;
+  const bool syrk = (P.flags & GF_SYRK) != 0;
+  if (syrk) {
+    tm = (int)((sqrtf(8.f * (float)local + 1.f) - 1.f) * 0.5f);
+    while (tm > 0 && tm * (tm + 1) / 2 > local) --tm;
+    while ((tm + 1) * (tm + 2) / 2 <= local) ++tm;
+    tn = local - tm * (tm + 1) / 2;
+  } else {
+    constexpr int G = 8;
+    const int per_group = G * P.tiles_n;
+    const int grp = local / per_group;
+    const int first_m = grp * G;
+    const int gsz = min(G, P.tiles_m - first_m);
+    const int in = local - grp * per_group;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+  }
+  const int m0 = tm * TB, n0 = tn * TB;
+  const int M = P.M, N = P.N, K = P.K;
+  const bf16_t* A = (const bf16_t*)P.A + (int64_t)b * P.sA;
+  const bf16_t* B = (const bf16_t*)P.B + (int64_t)b * P.sB;
+  const int64_t lda = P.lda, ldb = P.ldb;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // Per-thread source rows / chunks of its LPT direct loads per operand.
+  const bf16_t* asrc[LPT];
+  const bf16_t* bsrc[LPT];
+#pragma unroll
+  for (int p = 0; p < LPT; ++p) {
+    const int L = (p * 4 + wave) * 64 + lane;  // 16-byte slot in the operand tile
+    const int row = L >> 2, slot = L & 3;
+    const int ch = slot ^ swz(row);
+    const int ra = min(m0 + row, M - 1), rb = min(n0 + row, N - 1);
+    asrc[p] = A + (int64_t)ra * lda + ch * 8;
+    bsrc[p] = B + (int64_t)rb * ldb + ch * 8;
+  }
+  auto issue = [&](unsigned char* stage, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < LPT; ++p)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[p] + k0),
+                                       (lds_void_t*)(stage + (p * 4 + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int p = 0; p < LPT; ++p)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[p] + k0),
+                                       (lds_void_t*)(stage + TB * ROWB + (p * 4 + wave) * 1024), 16,
+                                       0, 0);
+  };
+
+  // MFMA operand reads: lane (h, r32) reads chunk 2h + s of its rows.
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int arow = wm * 128 + r32, brow = wn * 128 + r32;
+  const int ga = swz(arow), gb = swz(brow);  // same for rows +32, +64, +96
+  const int aoff0 = arow * ROWB + (((2 * h + 0) ^ ga) << 4);
+  const int aoff1 = arow * ROWB + (((2 * h + 1) ^ ga) << 4);
+  const int boff0 = TB * ROWB + brow * ROWB + (((2 * h + 0) ^ gb) << 4);
+  const int boff1 = TB * ROWB + brow * ROWB + (((2 * h + 1) ^ gb) << 4);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  auto compute = [&](const unsigned char* stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 af[4], bfr[4];
+      const int ao = s ? aoff1 : aoff0, bo = s ? boff1 : boff0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const uint4*)(stage + ao + i * 32 * ROWB);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = *(const uint4*)(stage + bo + j * 32 * ROWB);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bfr[j]), acc[i][j],
+              0, 0, 0);
+    }
+  };
+
+  // ---- main loop over full slices: 4-stage ring ------------------------------
+  // Every step waits for its slice and then issues the slice three ahead; past
+  // the end it reloads the last slice into a stage nobody reads again, so the
+  // loop has no branches and two slices (16 loads per thread) are always
+  // younger than the one being waited for. The barrier also certifies that
+  // every wave has finished reading the stage about to be refilled.
+  const int nkf = K / KS;  // full slices
+#define MAO_RING_STEP(CUR, NXT, K)                                   \
+  {                                                                  \
+    vm_wait(2 * 2 * LPT);                                            \
+    asm volatile("" ::: "memory");                                   \
+    __builtin_amdgcn_s_barrier();                                    \
+    asm volatile("" ::: "memory");                                   \
+    issue(NXT, min((K) + 3, nkf - 1) * KS);                          \
+    compute(CUR);                                                    \
+  }
+  int kt = 0;
+  if (nkf > 0) {
+    issue(st0, 0);
+    issue(st1, min(1, nkf - 1) * KS);
+    issue(st2, min(2, nkf - 1) * KS);
+    for (; kt + 4 <= nkf; kt += 4) {
+      MAO_RING_STEP(st0, st3, kt)
+      MAO_RING_STEP(st1, st0, kt + 1)
+      MAO_RING_STEP(st2, st1, kt + 2)
+      MAO_RING_STEP(st3, st2, kt + 3)
+    }
+    const int r = nkf - kt;
+    if (r > 0) MAO_RING_STEP(st0, st3, kt)
+    if (r > 1) MAO_RING_STEP(st1, st0, kt + 1)
+    if (r > 2) MAO_RING_STEP(st2, st1, kt + 2)
+  }
+#undef MAO_RING_STEP
+
+  // ---- partial last slice through registers ------------------------------
+  const int ktail = nkf * KS;
+  if (ktail < K) {
+    vm_wait(0);
+    asm volatile("" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < LPT; ++p) {
+      const int L = (p * 4 + wave) * 64 + lane;
+      const int row = L >> 2, slot = L & 3;
+      const int ch = slot ^ swz(row);
+      const int k = ktail + ch * 8;
+      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+      union U {
+        uint4 v;
+        bf16_t e[8];
+      } ua, ub;
+      ua.v = va;
+      ub.v = vb;
+      if (m0 + row < M)
+        for (int e = 0; e < 8; ++e)
+          if (k + e < K) ua.e[e] = A[(int64_t)(m0 + row) * lda + k + e];
+      if (n0 + row < N)
+        for (int e = 0; e < 8; ++e)
+          if (k + e < K) ub.e[e] = B[(int64_t)(n0 + row) * ldb + k + e];
+      *(uint4*)(st0 + L * 16) = ua.v;
+      *(uint4*)(st0 + TB * ROWB + L * 16) = ub.v;
+    }
+    __syncthreads();
+    compute(st0);
+  }
+  vm_wait(0);
+  asm volatile("" ::: "memory");
+  __syncthreads();
+
+  // ---- epilogue through LDS, 32 rows of the tile at a time ------------------
+  const bool diag = syrk && (tm == tn);
+  const bool d32 = (P.flags & GF_D_F32) != 0;
+  const bool c32 = (P.flags & GF_C0_F32) != 0;
+  const int dsz = d32 ? 4 : 2, csz = c32 ? 4 : 2;
+  void* D = P.D ? (void*)((char*)P.D + (int64_t)b * P.sD * dsz) : nullptr;
+  void* Tt = syrk ? D : (P.Dt ? (void*)((char*)P.Dt + (int64_t)b * P.sDt * dsz) : nullptr);
+  const int64_t ldt = syrk ? P.ldd : P.lddt;
+  const void* C0 = P.C0 ? (const void*)((const char*)P.C0 + (int64_t)b * P.sC0 * csz) : nullptr;
+  const float alpha = P.alpha, beta = P.beta;
+  const float* rs = P.row_scale;
+  if (!diag && !Tt && m0 + TB <= M && n0 + TB <= N) {
+    if (d32 && c32)
+      epilogue_direct<true, true>(acc, m0, n0, wm, wn, h, r32, alpha, beta, C0, P.ldc0, rs, D, P.ldd, Tt, ldt);
+    else if (d32)
+      epilogue_direct<true, false>(acc, m0, n0, wm, wn, h, r32, alpha, beta, C0, P.ldc0, rs, D, P.ldd, Tt, ldt);
+    else if (c32)
+      epilogue_direct<false, true>(acc, m0, n0, wm, wn, h, r32, alpha, beta, C0, P.ldc0, rs, D, P.ldd, Tt, ldt);
+    else
+      epilogue_direct<false, false>(acc, m0, n0, wm, wn, h, r32, alpha, beta, C0, P.ldc0, rs, D, P.ldd, Tt, ldt);
+    return;
+  }
+  float* slab = (float*)st0;
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // band rows: wm == half, block i -> tile rows half*128 + i*32 + [0, 32)
+      __syncthreads();
+      if (wm == half) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int sr = 8 * (v >> 2) + 4 * h + (v & 3);
+            const int sc = wn * 128 + j * 32 + r32;
+            slab[sr * SLAB_LD + sc] = acc[i][j][v];
+          }
+      }
+      __syncthreads();
+      const int rbase = m0 + half * 128 + i * 32;
+      // direct pass: thread -> 4 consecutive columns of rows sr, sr+4, ...
+      const int c4 = (threadIdx.x & 63) * 4;
+      const int gcol = n0 + c4;
+      for (int sr = threadIdx.x >> 6; sr < 32; sr += 4) {
+        const int grow = rbase + sr;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = alpha * slab[sr * SLAB_LD + c4 + e];
+        if (grow < M) {
+          const bool full = gcol + 3 < N;
+          if (C0) {
+            const int64_t off = (int64_t)grow * P.ldc0 + gcol;
+            if (full && c32) {
+              const float4 c = *(const float4*)((const float*)C0 + off);
+              v[0] += beta * c.x; v[1] += beta * c.y; v[2] += beta * c.z; v[3] += beta * c.w;
+            } else if (full) {
+              const uint2 c = *(const uint2*)((const bf16_t*)C0 + off);
+              v[0] += beta * bf16_to_f32((bf16_t)(c.x & 0xffff));
+              v[1] += beta * bf16_to_f32((bf16_t)(c.x >> 16));
+              v[2] += beta * bf16_to_f32((bf16_t)(c.y & 0xffff));
+              v[3] += beta * bf16_to_f32((bf16_t)(c.y >> 16));
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (gcol + e < N) v[e] += beta * c0_load(C0, c32, off + e);
+            }
+          }
+          if (rs) {
+            const float sc = rs[grow];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= sc;
+          }
+          if (D) {
+            const int64_t off = (int64_t)grow * P.ldd + gcol;
+            if (full && !diag) {
+              if (d32) {
+                *(float4*)((float*)D + off) = make_float4(v[0], v[1], v[2], v[3]);
+              } else {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                *(uint2*)((bf16_t*)D + off) = pk;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (gcol + e < N && (!diag || grow >= gcol + e)) d_store(D, d32, off + e, v[e]);
+            }
+          }
+        }
+        if (Tt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) slab[sr * SLAB_LD + c4 + e] = v[e];
+        }
+      }
+      if (Tt) {
+        __syncthreads();
+        const int sr4 = (threadIdx.x & 7) * 4;
+        const int grow = rbase + sr4;
+        for (int sc = threadIdx.x >> 3; sc < TB; sc += 32) {
+          const int gc = n0 + sc;
+          if (gc >= N || grow >= M) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = slab[(sr4 + e) * SLAB_LD + sc];
+          const int64_t off = (int64_t)gc * ldt + grow;
+          if (!diag && grow + 3 < M) {
+            if (d32) {
+              *(float4*)((float*)Tt + off) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              uint2 pk;
+              pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+              pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+              *(uint2*)((bf16_t*)Tt + off) = pk;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (grow + e < M && (!diag || grow + e > gc)) d_store(Tt, d32, off + e, v[e]);
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_bf16_dl_kernel, dim3(args.total_tiles), dim3(256), 0, stream, args);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+}  // namespace mao

@@ -118,13 +118,20 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelArgs a) {
     float* pb = a.part + (size_t)(jj & 1) * G * NB;
     if (t < NB) pb[g * NB + t] = qs[0][t] + qs[1][t] + qs[2][t] + qs[3][t];
     grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
-    if (t < NB) {
+    {
+      // every thread sums a quarter of the workgroups' partials of one value
+      // (independent loads in flight together), then a fixed-order combine
+      const int v = t & 63, q = t >> 6;
       float s = 0.f;
-      if (t >= jj && t < nb)
-        for (int gg = 0; gg < G; ++gg) s += pb[gg * NB + t];
-      tot[t] = s;
-      dgv[t] = (t >= jj && t < nb) ? dgb[t] : 0.f;
+      if (v >= jj && v < nb) {
+#pragma unroll 8
+        for (int gg = q; gg < G; gg += 4) s += pb[gg * NB + v];
+      }
+      qs[q][v] = s;
+      if (t < NB) dgv[t] = (t >= jj && t < nb) ? dgb[t] : 0.f;
     }
+    __syncthreads();
+    if (t < NB) tot[t] = qs[0][t] + qs[1][t] + qs[2][t] + qs[3][t];
     __syncthreads();
     const float alpha = dgv[jj], sig2 = tot[jj];
     float beta, tau, scal;
@@ -170,8 +177,12 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelArgs a) {
   if (g == 0) {
     for (int e = t; e < NB * NB; e += TPB) {
       float s = 0.f;
-      for (int gg = 0; gg < G; ++gg) s += a.gram[(size_t)gg * NB * NB + e];
-      red[e >> 6][e & 63] = s;
+      const int i = e >> 6, k = e & 63;
+      if (i < k && k < nb) {
+#pragma unroll 8
+        for (int gg = 0; gg < G; ++gg) s += a.gram[(size_t)gg * NB * NB + e];
+      }
+      red[i][k] = s;
     }
     for (int e = t; e < NB * NB; e += TPB) {
       const int i = e >> 6, k = e & 63;

@@ -12,7 +12,9 @@ from tests.helpers import log, rel, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 GEMM_SHAPES = [(1, 1, 1), (64, 64, 64), (130, 77, 203), (300, 257, 500), (513, 129, 64),
-               (1024, 1000, 1536)]
+               (1024, 1000, 1536),
+               # large enough for the 256 x 256 streamed bf16 kernel, ragged in M, N, K
+               (4100, 2052, 1060), (2304, 4352, 8)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -35,7 +37,8 @@ def test_gemm_nt_matches_fp64(gpu_lib, dtype, shape):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n,k", [(1, 5), (70, 33), (200, 1000), (513, 300)])
+@pytest.mark.parametrize("n,k", [(1, 5), (70, 33), (200, 1000), (513, 300), (4100, 1000),
+                                 (4352, 96)])
 def test_syrk_is_exactly_symmetric(gpu_lib, dtype, n, k):
     import torch
     log(f"syrk {dtype} {n}x{k}")
