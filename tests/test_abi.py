@@ -1,0 +1,172 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/mao.h declares, and rejects invalid calls with the documented status
+codes before touching the device.
+
+Invalid calls use fake, never-dereferenced device addresses; every call here
+is invalid, so none of them reaches a kernel launch. They are skipped when a
+GPU is present, to keep a mistake in validation from ever launching a kernel
+on a fake address.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import matrix_aware_optimizers_amd as mao
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mao.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_LAYOUT, E_ALIAS, E_HPARAM, E_WORKSPACE = 0, 1, 2, 3, 4, 5, 6, 7
+FAKE = 0x7F0000000000  # 256-aligned, never dereferenced
+
+
+def _declared():
+    src = open(HEADER).read()
+    return re.findall(r"MAO_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mao.load()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding's table covers the same set
+    assert set(names) == set(mao.EXPORTS) - set(), sorted(set(names) ^ set(mao.EXPORTS))
+
+
+def test_status_strings_and_version():
+    lib = mao.load()
+    assert lib.mao_abi_version() == 1
+    for code in range(10):
+        assert lib.mao_status_string(code)
+    assert lib.mao_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries():
+    lib = mao.load()
+    hp = mao.muon_hparams(ns_dtype="bf16")
+    a = lib.muon_workspace_size(4096, 4096, ctypes.byref(hp))
+    b = lib.muon_workspace_size(14336, 4096, ctypes.byref(hp))
+    assert 0 < a < b
+    hp32 = mao.muon_hparams(ns_dtype="f32")
+    assert lib.muon_workspace_size(4096, 4096, ctypes.byref(hp32)) > a
+    assert lib.muon_workspace_size(0, 4, ctypes.byref(hp)) == 0
+    sh = mao.soap_hparams()
+    assert lib.soap_workspace_size(256, 512, ctypes.byref(sh)) > 0
+    fh = mao.foam_hparams()
+    assert lib.foam_workspace_size(1536, 6144, ctypes.byref(fh)) > 0
+    assert lib.mao_qr_workspace_size(300) > 0
+    assert lib.mao_qr_workspace_size(0) == 0
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+needs_no_gpu = pytest.mark.skipif(_gpu_present(), reason="fake-address validation runs host-only")
+
+
+def _mat(ptr, rows, cols, ld, dtype=mao.F32):
+    return mao.Mat(ptr, rows, cols, ld, dtype)
+
+
+@needs_no_gpu
+def test_muon_validation_codes():
+    lib = mao.load()
+    hp = mao.muon_hparams(lr=1e-3, mu=0.95)
+    ws_need = lib.muon_workspace_size(8, 16, ctypes.byref(hp))
+    W = _mat(FAKE, 8, 16, 16, mao.BF16)
+    G = _mat(FAKE + (1 << 20), 8, 16, 16, mao.BF16)
+    M = _mat(FAKE + (2 << 20), 8, 16, 16)
+    ws = ctypes.c_void_p(FAKE + (4 << 20))
+
+    def call(W=W, G=G, M=M, hp=hp, ws=ws, ws_bytes=ws_need, out=None):
+        return lib.muon_step(W, G, M, ctypes.byref(hp), ws, ws_bytes, out, None)
+
+    assert call(W=_mat(None, 8, 16, 16)) == E_NULL
+    assert call(G=_mat(FAKE + (1 << 20), 8, 15, 16, mao.BF16)) == E_SHAPE
+    assert call(W=_mat(FAKE, 0, 16, 16)) == E_SHAPE
+    assert call(W=_mat(FAKE, 8, 16, 12)) == E_LAYOUT            # ld not a multiple of 8
+    assert call(W=_mat(FAKE, 8, 16, 8)) == E_LAYOUT             # ld < cols
+    assert call(W=_mat(FAKE + 4, 8, 16, 16)) == E_LAYOUT        # misaligned
+    assert call(M=_mat(FAKE + (2 << 20), 8, 16, 16, mao.BF16)) == E_DTYPE  # momentum must be fp32
+    assert call(W=_mat(FAKE, 8, 16, 16, 7)) == E_DTYPE
+    assert call(G=_mat(FAKE + 64, 8, 16, 16, mao.BF16)) == E_ALIAS
+    assert call(hp=mao.muon_hparams(mu=1.0)) == E_HPARAM
+    assert call(hp=mao.muon_hparams(eps=0.0)) == E_HPARAM
+    assert call(hp=mao.muon_hparams(ns_steps=65)) == E_HPARAM
+    assert call(hp=mao.muon_hparams(lr=float("nan"))) == E_HPARAM
+    assert call(ws=None) == E_WORKSPACE
+    assert call(ws_bytes=ws_need - 1) == E_WORKSPACE
+    assert call(ws=ctypes.c_void_p(FAKE + (4 << 20) + 16)) == E_WORKSPACE
+    assert b"workspace" in lib.mao_last_error()
+
+
+@needs_no_gpu
+def test_batched_validation_codes():
+    lib = mao.load()
+    hp = mao.muon_hparams()
+    W = (mao.Batch * 1)(mao.Batch(FAKE, 3, 8, 16, 16, 8 * 16, mao.BF16))
+    G = (mao.Batch * 1)(mao.Batch(FAKE + (1 << 20), 3, 8, 16, 16, 8 * 16, mao.BF16))
+    M = (mao.Batch * 1)(mao.Batch(FAKE + (2 << 20), 3, 8, 16, 16, 8 * 16, mao.F32))
+    need = lib.muon_batched_workspace_size(1, W, ctypes.byref(hp))
+    ws = ctypes.c_void_p(FAKE + (4 << 20))
+    assert lib.muon_step_batched(0, W, G, M, ctypes.byref(hp), ws, need, None, None) == E_SHAPE
+    assert lib.muon_step_batched(9, W, G, M, ctypes.byref(hp), ws, need, None, None) == E_SHAPE
+    Wbad = (mao.Batch * 1)(mao.Batch(FAKE, 3, 8, 16, 16, 100, mao.BF16))  # stride < rows*ld
+    assert lib.muon_step_batched(1, Wbad, G, M, ctypes.byref(hp), ws, need, None, None) == E_LAYOUT
+    Mbad = (mao.Batch * 1)(mao.Batch(FAKE + (2 << 20), 2, 8, 16, 16, 8 * 16, mao.F32))
+    assert lib.muon_step_batched(1, W, G, Mbad, ctypes.byref(hp), ws, need, None, None) == E_SHAPE
+
+
+@needs_no_gpu
+def test_soap_foam_adamw_qr_gemm_validation_codes():
+    lib = mao.load()
+    m, n = 8, 16
+    sh = mao.soap_hparams()
+    st = mao.SoapStateC(_mat(FAKE + (1 << 20), m, n, n), _mat(FAKE + (2 << 20), m, n, n),
+                        _mat(FAKE + (3 << 20), m, m, 8), _mat(FAKE + (4 << 20), n, n, n),
+                        _mat(FAKE + (5 << 20), m, m, 8), _mat(FAKE + (6 << 20), n, n, n))
+    W = _mat(FAKE, m, n, n)
+    G = _mat(FAKE + (7 << 20), m, n, n)
+    need = lib.soap_workspace_size(m, n, ctypes.byref(sh))
+    ws = ctypes.c_void_p(FAKE + (16 << 20))
+    assert lib.soap_step(W, G, None, 1, ctypes.byref(sh), ws, need, None, None) == E_NULL
+    assert lib.soap_step(W, G, ctypes.byref(st), 0, ctypes.byref(sh), ws, need, None, None) == E_HPARAM
+    bad = mao.SoapStateC(st.M, st.V, _mat(FAKE + (3 << 20), n, n, n), st.R, st.QL, st.QR)
+    assert lib.soap_step(W, G, ctypes.byref(bad), 1, ctypes.byref(sh), ws, need, None, None) == E_SHAPE
+    assert lib.soap_step(W, G, ctypes.byref(st), 1, ctypes.byref(mao.soap_hparams(beta2=1.0)), ws,
+                         need, None, None) == E_HPARAM
+    assert lib.soap_step(W, G, ctypes.byref(st), 1, ctypes.byref(sh), ws, need - 1, None,
+                         None) == E_WORKSPACE
+
+    fh = mao.foam_hparams()
+    fst = mao.FoamStateC(_mat(FAKE + (1 << 20), m, n, n), _mat(FAKE + (4 << 20), n, n, n),
+                         _mat(FAKE + (6 << 20), n, n, n), FAKE + (8 << 20), FAKE + (9 << 20),
+                         FAKE + (10 << 20))
+    fneed = lib.foam_workspace_size(m, n, ctypes.byref(fh))
+    assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(mao.foam_hparams(pf=0)), ws,
+                         fneed, None, None) == E_HPARAM
+    fst2 = mao.FoamStateC(fst.M, fst.R, fst.QR, None, fst.c, fst.aux)
+    assert lib.foam_step(W, G, ctypes.byref(fst2), 1, ctypes.byref(fh), ws, fneed, None,
+                         None) == E_NULL
+
+    assert lib.adamw_step(FAKE, 0, FAKE + 4096, 0, FAKE + 8192, FAKE + 12288, 0, 1, 1e-3, 0.9,
+                          0.95, 1e-8, 0.0, None, None) == E_SHAPE
+    assert lib.adamw_step(FAKE, 0, FAKE + 64, 0, FAKE + 8192, FAKE + 12288, 100, 1, 1e-3, 0.9,
+                          0.95, 1e-8, 0.0, None, None) == E_ALIAS
+    assert lib.adamw_step(FAKE, 5, FAKE + 4096, 0, FAKE + 8192, FAKE + 12288, 100, 1, 1e-3, 0.9,
+                          0.95, 1e-8, 0.0, None, None) == E_DTYPE
+
+    assert lib.mao_qr(FAKE, 12, FAKE + (1 << 20), 16, 12, ws, 1 << 30, None) == E_LAYOUT
+    assert lib.mao_qr(FAKE, 16, FAKE + 64, 16, 12, ws, 1 << 30, None) == E_ALIAS
+    assert lib.mao_gemm_nt(4, 4, 4, 1.0, FAKE, 8, FAKE + 4096, 8, 1, 0.0, None, 0, FAKE + 8192, 8,
+                           1, None) == E_SHAPE  # symmetric needs A == B
+    assert lib.mao_gemm_nt(4, 4, 0, 1.0, FAKE, 8, FAKE, 8, 1, 0.0, None, 0, FAKE + 8192, 8, 0,
+                           None) == E_SHAPE
