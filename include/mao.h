@@ -273,17 +273,24 @@ MAO_API mao_status adamw_step(void* w, int32_t w_dtype, const void* g, int32_t g
 /* Building blocks exposed for kernel-level checks                           */
 /* ------------------------------------------------------------------------ */
 
+/* mode bits of mao_gemm_nt */
+#define MAO_GEMM_SYMMETRIC 1 /* lower triangle of a square result, mirrored (SYRK) */
+#define MAO_GEMM_B_KMAJOR 2  /* B stored K x N: D = alpha A B + beta C0 */
+
 /*
  * mao_gemm_nt -- D = alpha * A B^T + beta * C0, the contraction every step
  * above is built from. A: M x K, B: N x K (row-major, both K-contiguous),
  * C0/D: M x N. in_dtype: MAO_BF16 (bf16 MFMA) or MAO_F32 (fp32 MFMA) for A
  * and B; C0 and D fp32. C0 may be NULL (beta ignored) and may equal D.
- * symmetric != 0 computes only the lower triangle of a square result
- * (A == B, M == N) and mirrors it (SYRK).
+ * mode: 0, or MAO_GEMM_SYMMETRIC -- only the lower triangle of a square
+ * result is computed (A == B, M == N) and mirrored -- or MAO_GEMM_B_KMAJOR --
+ * B is stored K x N (ldb >= N), bf16 only: the Newton-Schulz product B X
+ * reads X this way. Other bits: MAO_E_HPARAM; unsupported combinations:
+ * MAO_E_UNSUPPORTED.
  */
 MAO_API mao_status mao_gemm_nt(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                        int64_t lda, const void* B, int64_t ldb, int32_t in_dtype, float beta,
-                       const float* C0, int64_t ldc0, float* D, int64_t ldd, int32_t symmetric,
+                       const float* C0, int64_t ldc0, float* D, int64_t ldd, int32_t mode,
                        void* stream);
 
 /* Workspace bytes for mao_qr on an n x n matrix. */

@@ -327,8 +327,9 @@ def timing_collect() -> dict:
     return {TIMING_TAGS[i]: (ms[i], cnt[i], fl[i]) for i in range(n)}
 
 
-def gemm_nt(A, B, *, alpha=1.0, beta=0.0, C0=None, out=None, symmetric=False):
-    """D = alpha A B^T + beta C0 through the library's MFMA kernel (fp32 out)."""
+def gemm_nt(A, B, *, alpha=1.0, beta=0.0, C0=None, out=None, symmetric=False, b_kmajor=False):
+    """D = alpha A B^T + beta C0 through the library's MFMA kernel (fp32 out).
+    With ``b_kmajor`` B is K x N and D = alpha A B + beta C0 (bf16 only)."""
     lib = load()
     if A.dtype != B.dtype:
         raise TypeError("A and B must share a dtype")
@@ -337,12 +338,14 @@ def gemm_nt(A, B, *, alpha=1.0, beta=0.0, C0=None, out=None, symmetric=False):
     B = A if (symmetric and same) else padded(B)
     if C0 is not None:
         C0 = padded(C0)
+    n = B.shape[1] if b_kmajor else B.shape[0]
     if out is None:
-        out = empty_matrix(A.shape[0], B.shape[0], device=A.device)
-    _check(lib.mao_gemm_nt(A.shape[0], B.shape[0], A.shape[1], alpha, _ptr(A), A.stride(0),
+        out = empty_matrix(A.shape[0], n, device=A.device)
+    mode = (1 if symmetric else 0) | (2 if b_kmajor else 0)
+    _check(lib.mao_gemm_nt(A.shape[0], n, A.shape[1], alpha, _ptr(A), A.stride(0),
                            _ptr(B), B.stride(0), dtype_code(A), beta, _ptr(C0),
                            C0.stride(0) if C0 is not None else 0, _ptr(out), out.stride(0),
-                           1 if symmetric else 0, _stream()), "mao_gemm_nt")
+                           mode, _stream()), "mao_gemm_nt")
     return out
 
 

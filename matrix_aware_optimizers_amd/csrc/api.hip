@@ -100,9 +100,9 @@ void carve_muon(Carver& c, int ng, const int64_t* rows, const int64_t* cols, con
     B.wide = B.rows <= B.cols;
     B.a = std::min(B.rows, B.cols);
     B.b = std::max(B.rows, B.cols);
-    B.ldx = round_up(B.b, 64);
-    B.ldxt = round_up(B.a, 64);
-    B.lda = round_up(B.a, 64);
+    B.ldx = ws_ld(B.b);
+    B.ldxt = ws_ld(B.a);
+    B.lda = ws_ld(B.a);
     for (int k = 0; k < 2; ++k) {
       B.X[k] = c.take<char>((size_t)B.count * B.a * B.ldx * es);
       B.Xt[k] = c.take<char>((size_t)B.count * B.b * B.ldxt * es);
@@ -208,8 +208,14 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
   carve_muon(c, ng, rows, cols, count, hp, bufs);
   const int xdt = hp->ns_dtype;
   const int xflags = xdt == MAO_F32 ? (GF_D_F32 | GF_C0_F32) : 0;
+  // bf16: the product B X reads X as its K x N operand, so only X (wide
+  // orientation) is kept between iterations; fp32 keeps X and X^T (both
+  // operands K-contiguous). The final update needs X^T too when W is tall or
+  // Muon+ sums along the other axis: then the last iteration also writes it.
+  const bool kmajor = xdt == MAO_BF16;
+  auto need_t = [&](const MuonGroupBufs& B) { return !kmajor || !B.wide || hp->norm_mode != MAO_NORM_NONE; };
 
-  // momentum, norm, X0 in both orientations
+  // momentum, norm, X0 (and X0^T where it is read)
   for (int g = 0; g < ng; ++g) {
     MuonGroupBufs& B = bufs[g];
     const int64_t mstride = M[g].count > 1 ? M[g].stride : 0;
@@ -218,7 +224,8 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
                       G[g].dtype, B.rows, B.cols, B.count, hp->mu, B.partial, B.nrb, s));
     MAO_TRY(finalize_inv_norm(B.partial, B.nrb, B.count, hp->eps, B.scale, s));
     View xa = view(B.X[0], B.ldx, (int64_t)B.a * B.ldx);
-    View xb = view(B.Xt[0], B.ldxt, (int64_t)B.b * B.ldxt);
+    View xb = (!kmajor || (hp->ns_steps == 0 && need_t(B))) ? view(B.Xt[0], B.ldxt, (int64_t)B.b * B.ldxt)
+                                                             : view(nullptr, 0, 0);
     MAO_TRY(scale_cast_transpose(view(M[g].data, M[g].ld, mstride), B.rows, B.cols, B.count,
                                  B.scale, B.wide ? xa : xb, B.wide ? xb : xa, xdt, s));
   }
@@ -249,13 +256,21 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
     MAO_TRY(launch_gemm(xdt, p, ng, s, TAG_NS_SQUARE));
     for (int g = 0; g < ng; ++g) {
       MuonGroupBufs& B = bufs[g];
-      p[g] = gemm_problem(B.a, B.b, B.a, 1.f, B.Bm, B.lda, B.Xt[cur], B.ldxt, ca, B.X[cur], B.ldx,
-                          B.X[nxt], B.ldx, xflags);
-      p[g].Dt = B.Xt[nxt];
-      p[g].lddt = B.ldxt;
+      if (kmajor)
+        p[g] = gemm_problem(B.a, B.b, B.a, 1.f, B.Bm, B.lda, B.X[cur], B.ldx, ca, B.X[cur], B.ldx,
+                            B.X[nxt], B.ldx, xflags | GF_B_KMAJOR);
+      else
+        p[g] = gemm_problem(B.a, B.b, B.a, 1.f, B.Bm, B.lda, B.Xt[cur], B.ldxt, ca, B.X[cur], B.ldx,
+                            B.X[nxt], B.ldx, xflags);
+      const bool last = k + 1 == hp->ns_steps;
+      if (!kmajor || (last && need_t(B))) {
+        p[g].Dt = B.Xt[nxt];
+        p[g].lddt = B.ldxt;
+        p[g].sDt = (int64_t)B.b * B.ldxt;
+      }
       p[g].batch = B.count;
       p[g].sA = (int64_t)B.a * B.lda;
-      p[g].sB = p[g].sDt = (int64_t)B.b * B.ldxt;
+      p[g].sB = kmajor ? (int64_t)B.a * B.ldx : (int64_t)B.b * B.ldxt;
       p[g].sC0 = p[g].sD = (int64_t)B.a * B.ldx;
     }
     MAO_TRY(launch_gemm(xdt, p, ng, s, TAG_NS_APPLY));
@@ -335,10 +350,10 @@ struct RotBufs {
 };
 
 void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R) {
-  R.ldm = round_up(m, 64);
-  R.ldn = round_up(n, 64);
+  R.ldm = ws_ld(m);
+  R.ldn = ws_ld(n);
   const int big = std::max(m, n);
-  const int64_t ldb = round_up(big, 64);
+  const int64_t ldb = ws_ld(big);
   R.Gf = g_bf16 ? c.take<float>((size_t)m * R.ldn) : nullptr;
   R.Gtf = c.take<float>((size_t)n * R.ldm);
   R.EL = soap ? c.take<float>((size_t)m * R.ldm) : nullptr;
@@ -534,7 +549,7 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
   MAO_TRY(transpose(view(QR, ldQR), view(R.ER, R.ldn), n, n, 1, MAO_F32, s));
   const bool refresh = hp->refresh_every > 0 && ((t - 1) % hp->refresh_every) == 0;
   if (refresh) {
-    const int64_t ldS = round_up(std::max(m, n), 64);
+    const int64_t ldS = ws_ld(std::max(m, n));
     MAO_TRY(nt32(m, m, m, R.EL, R.ldm, L, ldL, R.S, ldS, nullptr, 0, s));
     MAO_TRY(qr_core(R.S, ldS, m, R.EL, R.ldm, QL, ldQL, R.qr, nullptr, s));
     MAO_TRY(nt32(n, n, n, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));
@@ -663,23 +678,27 @@ mao_status adamw_step(void* w, int32_t w_dtype, const void* g, int32_t g_dtype, 
 
 mao_status mao_gemm_nt(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
                        const void* B, int64_t ldb, int32_t in_dtype, float beta, const float* C0,
-                       int64_t ldc0, float* D, int64_t ldd, int32_t symmetric, void* stream) {
+                       int64_t ldc0, float* D, int64_t ldd, int32_t mode, void* stream) {
   if (!A || !B || !D) MAO_FAIL(MAO_E_NULL, "A, B or D is NULL");
   if (M < 1 || N < 1 || K < 1 || M > (1 << 20) || N > (1 << 20) || K > (1 << 20)) MAO_FAIL(MAO_E_SHAPE, "M, N, K");
   if (!dtype_ok(in_dtype)) MAO_FAIL(MAO_E_DTYPE, "in_dtype=%d", in_dtype);
-  if (lda < K || ldb < K || lda % 8 || ldb % 8 || ldd < N || ldd % 8 || (C0 && (ldc0 < N || ldc0 % 8)))
+  if (mode & ~(MAO_GEMM_SYMMETRIC | MAO_GEMM_B_KMAJOR)) MAO_FAIL(MAO_E_HPARAM, "mode=%d", mode);
+  const bool sym = (mode & MAO_GEMM_SYMMETRIC) != 0, bkm = (mode & MAO_GEMM_B_KMAJOR) != 0;
+  if (sym && bkm) MAO_FAIL(MAO_E_UNSUPPORTED, "symmetric with a K x N operand B");
+  if (bkm && in_dtype != MAO_BF16) MAO_FAIL(MAO_E_UNSUPPORTED, "a K x N operand B needs bf16 inputs");
+  if (lda < K || ldb < (bkm ? N : K) || lda % 8 || ldb % 8 || ldd < N || ldd % 8 || (C0 && (ldc0 < N || ldc0 % 8)))
     MAO_FAIL(MAO_E_LAYOUT, "leading dimensions");
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D | (uintptr_t)C0) % 16 != 0) MAO_FAIL(MAO_E_LAYOUT, "alignment");
-  if (symmetric && (M != N || A != B || lda != ldb)) MAO_FAIL(MAO_E_SHAPE, "symmetric needs A == B and M == N");
+  if (sym && (M != N || A != B || lda != ldb)) MAO_FAIL(MAO_E_SHAPE, "symmetric needs A == B and M == N");
   if (!finite(alpha) || !finite(beta)) MAO_FAIL(MAO_E_HPARAM, "alpha/beta");
   GemmProblem p = gemm_problem((int)M, (int)N, (int)K, alpha, A, lda, B, ldb, beta, C0, ldc0, D, ldd,
-                               GF_D_F32 | GF_C0_F32 | (symmetric ? GF_SYRK : 0));
+                               GF_D_F32 | GF_C0_F32 | (sym ? GF_SYRK : 0) | (bkm ? GF_B_KMAJOR : 0));
   return launch_gemm(in_dtype, &p, 1, (hipStream_t)stream);
 }
 
 size_t mao_qr_workspace_size(int64_t n) {
   if (n < 1 || n > (1 << 20)) return 0;
-  const int64_t ld = round_up(n, 64);
+  const int64_t ld = ws_ld(n);
   Carver c(nullptr);
   c.take<float>((size_t)n * ld);
   c.take<float>((size_t)n * ld);
@@ -695,7 +714,7 @@ mao_status mao_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n,
   MAO_TRY(check_no_overlap(rr));
   MAO_TRY(check_workspace(workspace, workspace_bytes, mao_qr_workspace_size(n)));
   hipStream_t s = (hipStream_t)stream;
-  const int64_t ld = round_up(n, 64);
+  const int64_t ld = ws_ld(n);
   Carver c(workspace);
   float* S = c.take<float>((size_t)n * ld);
   float* E = c.take<float>((size_t)n * ld);

@@ -105,6 +105,12 @@ void set_error(const char* fmt, ...);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Leading dimension (elements) of a workspace matrix whose rows hold n
+// elements: a multiple of 64 plus 64 more, so that consecutive rows never sit
+// a multiple of 4 KiB apart (row strides that are large powers of two send the
+// same K-slice of many rows to the same memory channel).
+inline int64_t ws_ld(int64_t n) { return round_up(n, 64) + 64; }
 inline int64_t ceil_div(int64_t x, int64_t a) { return (x + a - 1) / a; }
 
 // Bump allocator over the caller's workspace (or a size-only dry run when

@@ -358,7 +358,20 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
     set_error("launch_gemm: %d problems > %d", nprob, kMaxProblems);
     return MAO_E_UNSUPPORTED;
   }
-  const int bm = (in_dtype == MAO_BF16 && count_tiles(probs, nprob, 256) >= 128) ? 256
+  // A K x N operand B is read only by the 256 x 256 bf16 kernel; a launch
+  // takes one B layout for all its problems.
+  int nkm = 0;
+  for (int i = 0; i < nprob; ++i) nkm += (probs[i].flags & GF_B_KMAJOR) ? 1 : 0;
+  if (nkm != 0) {
+    bool ok = nkm == nprob && in_dtype == MAO_BF16;
+    for (int i = 0; i < nprob; ++i) ok = ok && !(probs[i].flags & GF_SYRK);
+    if (!ok) {
+      set_error("launch_gemm: a K x N operand B needs bf16 inputs, no SYRK, and the same layout "
+                "for every problem of the launch");
+      return MAO_E_UNSUPPORTED;
+    }
+  }
+  const int bm = (in_dtype == MAO_BF16 && (nkm != 0 || count_tiles(probs, nprob, 256) >= 128)) ? 256
                  : count_tiles(probs, nprob, 128) >= 512 ? 128 : 64;
   GemmArgs args = {};
   int n = 0, total = 0;

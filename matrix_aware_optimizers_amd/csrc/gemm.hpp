@@ -10,6 +10,7 @@ enum GemmFlags : int {
   GF_SYRK = 1,     // square symmetric result: lower-triangular tiles only, mirrored
   GF_D_F32 = 2,    // D / Dt stored fp32 (else bf16)
   GF_C0_F32 = 4,   // C0 stored fp32 (else bf16)
+  GF_B_KMAJOR = 8, // B stored K x N (row-major, ldb >= N): D = alpha A B (bf16 only)
 };
 
 constexpr int kMaxProblems = 8;

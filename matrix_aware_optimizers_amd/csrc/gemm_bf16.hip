@@ -42,6 +42,13 @@ constexpr int SLAB_BYTES = 32 * SLAB_LD * 4;  // 32 rows of the output tile
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
+// K x N operand B: a slice is 32 k-rows of 512 bytes (the tile's 256 columns);
+// 16-byte chunk c of k-row r sits at chunk c ^ bkswz(r), so the transposing
+// reads of four consecutive k-rows hit distinct banks.
+constexpr int BKROW = TB * 2;
+__device__ __forceinline__ int bkswz(int krow) { return (krow & 3) << 2; }
+typedef short lds_v4i16_t __attribute__((ext_vector_type(4), address_space(3)));
+
 // s_waitcnt vmcnt(n), expcnt and lgkmcnt unconstrained (gfx9 field layout:
 // vmcnt low bits [3:0], high bits [15:14], expcnt [6:4], lgkmcnt [11:8]).
 #define MAO_VMCNT(n) ((((n) & 0xf)) | (0x7 << 4) | (0xf << 8) | ((((n) >> 4) & 0x3) << 14))
@@ -121,6 +128,7 @@ __device__ __forceinline__ void epilogue_direct(const f32x16_t (&acc)[4][4], int
 #undef MAO_EPI
 }
 
+template <bool BKM>
 __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE > SLAB_BYTES ? STAGE : SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
@@ -166,7 +174,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // Per-thread source rows / chunks of its LPT direct loads per operand.
+  // Per-thread sources of its LPT direct loads per operand. A (and B when it
+  // is N x K): load p covers 16-byte slot (p * 4 + wave) * 64 + lane of the
+  // tile, i.e. row slot / 4, chunk slot % 4 (permuted by swz). B when it is
+  // K x N: load p covers k-rows 8 p + 2 wave + lane / 32 of the slice, chunk
+  // lane % 32 of the row's 512 bytes (permuted by bkswz); columns past the
+  // edge re-read the last valid chunk.
   const bf16_t* asrc[LPT];
   const bf16_t* bsrc[LPT];
 #pragma unroll
@@ -174,10 +187,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
     const int L = (p * 4 + wave) * 64 + lane;  // 16-byte slot in the operand tile
     const int row = L >> 2, slot = L & 3;
     const int ch = slot ^ swz(row);
-    const int ra = min(m0 + row, M - 1), rb = min(n0 + row, N - 1);
+    const int ra = min(m0 + row, M - 1);
     asrc[p] = A + (int64_t)ra * lda + ch * 8;
-    bsrc[p] = B + (int64_t)rb * ldb + ch * 8;
+    if constexpr (BKM) {
+      const int kr = 8 * p + 2 * wave + (lane >> 5);
+      const int lc = (lane & 31) ^ bkswz(kr);
+      const int col = min(n0 + 8 * lc, (N - 1) & ~7);
+      bsrc[p] = B + (int64_t)kr * ldb + col;
+    } else {
+      const int rb = min(n0 + row, N - 1);
+      bsrc[p] = B + (int64_t)rb * ldb + ch * 8;
+    }
   }
+  // K offset k0 (elements) of a slice: along rows of A (and of an N x K B),
+  // down the rows of a K x N B.
+  const int64_t bstep = BKM ? ldb : 1;
   auto issue = [&](unsigned char* stage, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < LPT; ++p)
@@ -185,12 +209,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
                                        (lds_void_t*)(stage + (p * 4 + wave) * 1024), 16, 0, 0);
 #pragma unroll
     for (int p = 0; p < LPT; ++p)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[p] + k0),
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[p] + (int64_t)k0 * bstep),
                                        (lds_void_t*)(stage + TB * ROWB + (p * 4 + wave) * 1024), 16,
                                        0, 0);
   };
 
-  // MFMA operand reads: lane (h, r32) reads chunk 2h + s of its rows.
+  // MFMA operand reads. Sub-step s of a slice multiplies K elements
+  // 16 h + 8 s .. + 7 of lane half h (the same permutation on both operands).
+  // A (and an N x K B): lane (h, r32) reads 16-byte chunk 2 h + s of its rows.
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
   const int arow = wm * 128 + r32, brow = wn * 128 + r32;
@@ -199,6 +225,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   const int aoff1 = arow * ROWB + (((2 * h + 1) ^ ga) << 4);
   const int boff0 = TB * ROWB + brow * ROWB + (((2 * h + 0) ^ gb) << 4);
   const int boff1 = TB * ROWB + brow * ROWB + (((2 * h + 1) ^ gb) << 4);
+  // K x N B: two transposing 8-byte reads per fragment. In each group of 16
+  // lanes, lane i names k-row (i / 4) and columns 4 (i % 4) .. + 3 of the
+  // group's 4 x 16 block and receives column i of it, four k in order.
+  const int ti = lane & 15, tg = (lane >> 4) & 1;
+  int bko[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int krow = 16 * h + (ti >> 2);
+    const int chunk = wn * 16 + ((j * 4) ^ bkswz(krow)) + 2 * tg + ((ti >> 1) & 1);
+    bko[j] = TB * ROWB + krow * BKROW + (chunk << 4) + 8 * (ti & 1);
+  }
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -208,60 +245,102 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  auto compute = [&](const unsigned char* stage) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 af[4], bfr[4];
-      const int ao = s ? aoff1 : aoff0, bo = s ? boff1 : boff0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const uint4*)(stage + ao + i * 32 * ROWB);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = *(const uint4*)(stage + bo + j * 32 * ROWB);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bfr[j]), acc[i][j],
-              0, 0, 0);
-    }
-  };
+  // B fragment j of sub-step SUB from stage STG (either layout)
+#define MAO_BFRAG(STG, SUB, J, DST)                                                          \
+  if constexpr (BKM) {                                                                      \
+    const unsigned char* q_ = STG + bko[J] + (SUB) * 8 * BKROW;                             \
+    const uint2 lo_ = __builtin_bit_cast(                                                   \
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(q_)));                \
+    const uint2 hi_ = __builtin_bit_cast(                                                   \
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(q_ + 4 * BKROW)));    \
+    DST = make_uint4(lo_.x, lo_.y, hi_.x, hi_.y);                                           \
+  } else {                                                                                  \
+    DST = *(const uint4*)(STG + ((SUB) ? boff1 : boff0) + (J) * 32 * ROWB);                 \
+  }
+#define MAO_READ(STG, SUB, FA, FB)                                                          \
+  {                                                                                         \
+    const int ao_ = (SUB) ? aoff1 : aoff0;                                                  \
+    FA[0] = *(const uint4*)(STG + ao_);                                                     \
+    MAO_BFRAG(STG, SUB, 0, FB[0])                                                           \
+    FA[1] = *(const uint4*)(STG + ao_ + 32 * ROWB);                                         \
+    MAO_BFRAG(STG, SUB, 1, FB[1])                                                           \
+    FA[2] = *(const uint4*)(STG + ao_ + 64 * ROWB);                                         \
+    MAO_BFRAG(STG, SUB, 2, FB[2])                                                           \
+    FA[3] = *(const uint4*)(STG + ao_ + 96 * ROWB);                                         \
+    MAO_BFRAG(STG, SUB, 3, FB[3])                                                           \
+  }
+#define MAO_MF(FA, FB, I, J)                                                                \
+  acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, FA[I]),   \
+                                                      __builtin_bit_cast(bf16x8_t, FB[J]),   \
+                                                      acc[I][J], 0, 0, 0);
+#define MAO_MFMA16(FA, FB)                                                                  \
+  MAO_MF(FA, FB, 0, 0) MAO_MF(FA, FB, 0, 1) MAO_MF(FA, FB, 1, 0) MAO_MF(FA, FB, 1, 1)       \
+  MAO_MF(FA, FB, 0, 2) MAO_MF(FA, FB, 1, 2) MAO_MF(FA, FB, 2, 0) MAO_MF(FA, FB, 2, 1)       \
+  MAO_MF(FA, FB, 2, 2) MAO_MF(FA, FB, 0, 3) MAO_MF(FA, FB, 1, 3) MAO_MF(FA, FB, 2, 3)       \
+  MAO_MF(FA, FB, 3, 0) MAO_MF(FA, FB, 3, 1) MAO_MF(FA, FB, 3, 2) MAO_MF(FA, FB, 3, 3)
+  // Instruction order inside a sub-step: an operand read (and, in the second
+  // sub-step, a direct load) after each of the first MFMAs.
+#define MAO_SCHED(NR, NV)                                                                   \
+  {                                                                                         \
+    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                    \
+      if (q_ < (NV)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                     \
+      if (q_ < (NR)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     \
+    }                                                                                       \
+  }
 
-  // ---- main loop over full slices: 4-stage ring ------------------------------
-  // Every step waits for its slice and then issues the slice three ahead; past
-  // the end it reloads the last slice into a stage nobody reads again, so the
-  // loop has no branches and two slices (16 loads per thread) are always
-  // younger than the one being waited for. The barrier also certifies that
-  // every wave has finished reading the stage about to be refilled.
+  // ---- main loop over full slices: 4-stage ring, pipelined operand reads ----
+  // Slice k sits in stage k % 4. Step k multiplies sub-step 0 from fragments
+  // read during the previous step while it reads sub-step 1; it then waits
+  // for slice k + 1 (slice k + 2, 8 loads per thread, may still be in
+  // flight), and after the barrier -- which also certifies that every
+  // wave is done with the stage of slice k - 1 -- refills that stage with
+  // slice k + 3 and reads sub-step 0 of slice k + 1 under the MFMAs of
+  // sub-step 1. Past the end the last slice is reloaded into a stage nobody
+  // reads again, so the loop has no branches.
   const int nkf = K / KS;  // full slices
-#define MAO_RING_STEP(CUR, NXT, K)                                   \
-  {                                                                  \
-    vm_wait(2 * 2 * LPT);                                            \
-    asm volatile("" ::: "memory");                                   \
-    __builtin_amdgcn_s_barrier();                                    \
-    asm volatile("" ::: "memory");                                   \
-    issue(NXT, min((K) + 3, nkf - 1) * KS);                          \
-    compute(CUR);                                                    \
+  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+#define MAO_RING_STEP(CUR, NXT, REF, K)                                 \
+  {                                                                     \
+    MAO_READ(CUR, 1, fa1, fb1)                                          \
+    MAO_MFMA16(fa0, fb0)                                                \
+    MAO_SCHED(BKM ? 12 : 8, 0)                                          \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    vm_wait(2 * LPT);                                                   \
+    asm volatile("" ::: "memory");                                      \
+    __builtin_amdgcn_s_barrier();                                       \
+    asm volatile("" ::: "memory");                                      \
+    issue(REF, min((K) + 3, nkf - 1) * KS);                             \
+    MAO_READ(NXT, 0, fa0, fb0)                                          \
+    MAO_MFMA16(fa1, fb1)                                                \
+    MAO_SCHED(BKM ? 12 : 8, 2 * LPT)                                    \
+    __builtin_amdgcn_sched_barrier(0);                                  \
   }
   int kt = 0;
   if (nkf > 0) {
     issue(st0, 0);
     issue(st1, min(1, nkf - 1) * KS);
     issue(st2, min(2, nkf - 1) * KS);
+    vm_wait(2 * 2 * LPT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    MAO_READ(st0, 0, fa0, fb0)
+    __builtin_amdgcn_sched_barrier(0);
     for (; kt + 4 <= nkf; kt += 4) {
-      MAO_RING_STEP(st0, st3, kt)
-      MAO_RING_STEP(st1, st0, kt + 1)
-      MAO_RING_STEP(st2, st1, kt + 2)
-      MAO_RING_STEP(st3, st2, kt + 3)
+      MAO_RING_STEP(st0, st1, st3, kt)
+      MAO_RING_STEP(st1, st2, st0, kt + 1)
+      MAO_RING_STEP(st2, st3, st1, kt + 2)
+      MAO_RING_STEP(st3, st0, st2, kt + 3)
     }
     const int r = nkf - kt;
-    if (r > 0) MAO_RING_STEP(st0, st3, kt)
-    if (r > 1) MAO_RING_STEP(st1, st0, kt + 1)
-    if (r > 2) MAO_RING_STEP(st2, st1, kt + 2)
+    if (r > 0) MAO_RING_STEP(st0, st1, st3, kt)
+    if (r > 1) MAO_RING_STEP(st1, st2, st0, kt + 1)
+    if (r > 2) MAO_RING_STEP(st2, st3, st1, kt + 2)
   }
 #undef MAO_RING_STEP
 
-  // ---- partial last slice through registers ------------------------------
+  // ---- partial last slice through registers (zero fill past K) ------------
   const int ktail = nkf * KS;
   if (ktail < K) {
     vm_wait(0);
@@ -270,28 +349,45 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
 #pragma unroll
     for (int p = 0; p < LPT; ++p) {
       const int L = (p * 4 + wave) * 64 + lane;
-      const int row = L >> 2, slot = L & 3;
-      const int ch = slot ^ swz(row);
-      const int k = ktail + ch * 8;
-      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
       union U {
         uint4 v;
         bf16_t e[8];
       } ua, ub;
-      ua.v = va;
-      ub.v = vb;
-      if (m0 + row < M)
-        for (int e = 0; e < 8; ++e)
-          if (k + e < K) ua.e[e] = A[(int64_t)(m0 + row) * lda + k + e];
-      if (n0 + row < N)
-        for (int e = 0; e < 8; ++e)
-          if (k + e < K) ub.e[e] = B[(int64_t)(n0 + row) * ldb + k + e];
+      ua.v = make_uint4(0, 0, 0, 0);
+      ub.v = make_uint4(0, 0, 0, 0);
+      {
+        const int row = L >> 2, slot = L & 3;
+        const int k = ktail + (slot ^ swz(row)) * 8;
+        if (m0 + row < M)
+          for (int e = 0; e < 8; ++e)
+            if (k + e < K) ua.e[e] = A[(int64_t)(m0 + row) * lda + k + e];
+        if constexpr (!BKM) {
+          if (n0 + row < N)
+            for (int e = 0; e < 8; ++e)
+              if (k + e < K) ub.e[e] = B[(int64_t)(n0 + row) * ldb + k + e];
+        }
+      }
+      if constexpr (BKM) {
+        const int kr = L >> 5;
+        const int col = n0 + 8 * ((L & 31) ^ bkswz(kr));
+        if (ktail + kr < K)
+          for (int e = 0; e < 8; ++e)
+            if (col + e < N) ub.e[e] = B[(int64_t)(ktail + kr) * ldb + col + e];
+      }
       *(uint4*)(st0 + L * 16) = ua.v;
       *(uint4*)(st0 + TB * ROWB + L * 16) = ub.v;
     }
     __syncthreads();
-    compute(st0);
+    MAO_READ(st0, 0, fa0, fb0)
+    MAO_MFMA16(fa0, fb0)
+    MAO_READ(st0, 1, fa1, fb1)
+    MAO_MFMA16(fa1, fb1)
   }
+#undef MAO_READ
+#undef MAO_BFRAG
+#undef MAO_MF
+#undef MAO_MFMA16
+#undef MAO_SCHED
   vm_wait(0);
   asm volatile("" ::: "memory");
   __syncthreads();
@@ -427,7 +523,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
 }  // namespace
 
 mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL(gemm_bf16_dl_kernel, dim3(args.total_tiles), dim3(256), 0, stream, args);
+  if (args.p[0].flags & GF_B_KMAJOR)
+    hipLaunchKernelGGL(gemm_bf16_dl_kernel<true>, dim3(args.total_tiles), dim3(256), 0, stream, args);
+  else
+    hipLaunchKernelGGL(gemm_bf16_dl_kernel<false>, dim3(args.total_tiles), dim3(256), 0, stream, args);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }

@@ -170,3 +170,11 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
                            1, None) == E_SHAPE  # symmetric needs A == B
     assert lib.mao_gemm_nt(4, 4, 0, 1.0, FAKE, 8, FAKE, 8, 1, 0.0, None, 0, FAKE + 8192, 8, 0,
                            None) == E_SHAPE
+    assert lib.mao_gemm_nt(4, 4, 4, 1.0, FAKE, 8, FAKE + 4096, 8, 1, 0.0, None, 0, FAKE + 8192, 8,
+                           4, None) == E_HPARAM  # unknown mode bit
+    assert lib.mao_gemm_nt(4, 4, 4, 1.0, FAKE, 8, FAKE, 8, 1, 0.0, None, 0, FAKE + 8192, 8, 3,
+                           None) == 9  # symmetric with a K x N B: unsupported
+    assert lib.mao_gemm_nt(4, 4, 4, 1.0, FAKE, 8, FAKE + 4096, 8, 0, 0.0, None, 0, FAKE + 8192, 8,
+                           2, None) == 9  # K x N B needs bf16
+    assert lib.mao_gemm_nt(4, 12, 4, 1.0, FAKE, 8, FAKE + 4096, 8, 1, 0.0, None, 0, FAKE + 8192,
+                           16, 2, None) == 4  # K x N B: ldb < N

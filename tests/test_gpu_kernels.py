@@ -36,6 +36,29 @@ def test_gemm_nt_matches_fp64(gpu_lib, dtype, shape):
     assert rel(to_host(D), ref) < 1e-5
 
 
+# B stored K x N (the Newton-Schulz product B X reads X this way): ragged in
+# every dimension, K below one slice, K with a partial last slice, N below one
+# 16-byte chunk
+KMAJOR_SHAPES = [(1, 1, 1), (8, 8, 8), (64, 64, 64), (300, 520, 96), (130, 77, 203),
+                 (4100, 2052, 1060), (1536, 2048, 1536), (33, 1001, 2050), (520, 6, 40)]
+
+
+@pytest.mark.parametrize("shape", KMAJOR_SHAPES)
+def test_gemm_b_kmajor_matches_fp64(gpu_lib, shape):
+    import torch
+    M, N, K = shape
+    log(f"gemm bf16 B K-major {shape}")
+    r = np.random.default_rng(300 + M + N + K)
+    a = bf16_round(r.standard_normal((M, K)).astype(np.float32))
+    b = bf16_round(r.standard_normal((K, N)).astype(np.float32))
+    c0 = r.standard_normal((M, N)).astype(np.float32)
+    A, B, C0 = to_dev(a, "bf16"), to_dev(b, "bf16"), to_dev(c0)
+    D = gpu_lib.gemm_nt(A, B, alpha=0.75, beta=-0.5, C0=C0, b_kmajor=True)
+    torch.cuda.synchronize()
+    ref = 0.75 * (a.astype(np.float64) @ b.astype(np.float64)) - 0.5 * c0
+    assert rel(to_host(D), ref) < 1e-5
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("n,k", [(1, 5), (70, 33), (200, 1000), (513, 300), (4100, 1000),
                                  (4352, 96)])
