@@ -31,6 +31,8 @@
 // operand panels.
 #include "gemm.hpp"
 
+#include <utility>
+
 namespace mao {
 
 namespace {
@@ -80,18 +82,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStage];
 
   // ---- which tile ------------------------------------------------------
-  const int total = args.total_tiles;
-  const int bid = blockIdx.x;
-  const int per = total >> 3, rem = total & 7;
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int t = xcd * per + min(xcd, rem) + idx;
-  int pi = 0;
-  for (int q = 1; q < args.nprob; ++q)
-    if (t >= args.p[q].tile_begin) pi = q;
+  int pi, local;
+  xcd_tile(args, blockIdx.x, pi, local);
   const GemmProblem& P = args.p[pi];
   if (P.pred != nullptr && *P.pred == 0) return;
-
-  int local = t - P.tile_begin;
   const int b = local / P.tiles_per_batch;
   local -= b * P.tiles_per_batch;
   int tm, tn;
@@ -373,10 +367,15 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
   }
   const int bm = (in_dtype == MAO_BF16 && (nkm != 0 || count_tiles(probs, nprob, 256) >= 128)) ? 256
                  : count_tiles(probs, nprob, 128) >= 512 ? 128 : 64;
+  // Longest K first: the last tiles to start are the short ones.
+  int order[kMaxProblems];
+  for (int i = 0; i < nprob; ++i) order[i] = i;
+  for (int i = 1; i < nprob; ++i)
+    for (int j = i; j > 0 && probs[order[j]].K > probs[order[j - 1]].K; --j) std::swap(order[j], order[j - 1]);
   GemmArgs args = {};
   int n = 0, total = 0;
   for (int i = 0; i < nprob; ++i) {
-    GemmProblem p = probs[i];
+    GemmProblem p = probs[order[i]];
     if (p.M <= 0 || p.N <= 0 || p.batch <= 0) continue;
     p.tiles_m = (int)ceil_div(p.M, bm);
     p.tiles_n = (int)ceil_div(p.N, bm);

@@ -38,6 +38,34 @@ struct GemmArgs {
   int total_tiles;
 };
 
+// Tile of workgroup `bid`: problem `pi`, tile `local` within it (batch-major).
+// Workgroups reach the 8 XCDs round-robin (bid % 8). Each problem's tiles are
+// cut into 8 contiguous runs, one per XCD, so that every XCD gets the same
+// share of every problem (balanced when the problems of a launch differ in K)
+// and a run of neighbouring tiles that share operand panels in its L2; an XCD
+// walks its runs problem by problem. Run lengths follow the round-robin deal of
+// the concatenated tile list, which makes the map a bijection onto the tiles.
+__device__ __forceinline__ void xcd_tile(const GemmArgs& a, int bid, int& pi, int& local) {
+  const int x = bid & 7;
+  int idx = bid >> 3, off = 0;
+  pi = 0;
+  local = 0;
+  for (int q = 0; q < a.nprob; ++q) {
+    const int n = a.p[q].batch * a.p[q].tiles_per_batch;
+    const int base = n >> 3, r = n & 7, o = off & 7;
+    const int mine = base + ((((x - o) & 7) < r) ? 1 : 0);
+    if (idx < mine) {
+      int extra = 0;
+      for (int xx = 0; xx < x; ++xx) extra += (((xx - o) & 7) < r) ? 1 : 0;
+      pi = q;
+      local = x * base + extra + idx;
+      return;
+    }
+    idx -= mine;
+    off += n;
+  }
+}
+
 // What a launch computes, for the optional event timing (instrumentation).
 enum GemmTag : int { TAG_NS_GRAM = 0, TAG_NS_SQUARE = 1, TAG_NS_APPLY = 2, TAG_OTHER = 3,
                      TAG_QR = 4, TAG_COUNT = 8 };

@@ -136,17 +136,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char st3[STAGE];
 
   // ---- tile --------------------------------------------------------------
-  const int total = args.total_tiles;
-  const int bid = blockIdx.x;
-  const int per = total >> 3, rem = total & 7;
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int t = xcd * per + min(xcd, rem) + idx;
-  int pi = 0;
-  for (int q = 1; q < args.nprob; ++q)
-    if (t >= args.p[q].tile_begin) pi = q;
+  int pi, local;
+  xcd_tile(args, blockIdx.x, pi, local);
   const GemmProblem& P = args.p[pi];
   if (P.pred != nullptr && *P.pred == 0) return;
-  int local = t - P.tile_begin;
   const int b = local / P.tiles_per_batch;
   local -= b * P.tiles_per_batch;
   int tm, tn;
