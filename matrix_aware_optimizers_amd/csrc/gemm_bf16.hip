@@ -1,29 +1,34 @@
-// Large bf16 NT contractions (the Newton-Schulz products) with operands
-// streamed straight from memory into LDS.
+// Large bf16 contractions (the Newton-Schulz products) with operands streamed
+// straight from memory into LDS.
 //
-// D[i][j] = alpha * sum_k A[i][k] * B[j][k] + beta * C0[i][j], bf16 inputs,
-// fp32 accumulation on v_mfma_f32_32x32x16_bf16.
+// D[i][j] = alpha * sum_k A[i][k] * B(j, k) + beta * C0[i][j], bf16 inputs,
+// fp32 accumulation on v_mfma_f32_32x32x16_bf16. B is either N x K (rows
+// K-contiguous, as A) or K x N (the Newton-Schulz product B X reads X this
+// way, so no transposed copy of X is ever written).
 //
 // Workgroup tile 256 x 256, 4 wavefronts in 2 x 2, each wavefront 128 x 128
 // (4 x 4 MFMA blocks, 256 fp32 accumulators per lane). K advances in slices of
-// 32 elements (64 bytes per tile row). Slices go global -> LDS with
-// global_load_lds_dwordx4 (no staging registers) into a ring of four LDS
-// stages, so three slices are in flight while one is multiplied; each stage is
-// its own LDS object, which lets the wait on the oldest slice be an exact
-// vmcnt rather than a full drain. Inside a stage a row's four 16-byte chunks
-// are XOR-permuted by bits 1-3 of the row index, so the 16-byte MFMA operand
-// reads of 16 consecutive rows hit distinct banks. A partial last slice
-// (K not a multiple of 32) goes through registers with zero fill.
+// 32 elements. Slices go global -> LDS with global_load_lds_dwordx4 (no
+// staging registers) into a ring of four LDS stages, each its own LDS object,
+// which lets the wait on a slice be an exact vmcnt rather than a full drain.
+// The operand fragments of the next 16-deep MFMA step are read from LDS while
+// the current step's MFMAs run (software pipelining pinned with scheduling
+// groups). A K-contiguous tile keeps 64 bytes per row per slice, its four
+// 16-byte chunks XOR-permuted by row bits 1-3 so that the 16-byte reads of 16
+// consecutive rows hit distinct banks. A K x N tile keeps 32 k-rows of 512
+// bytes, chunk bits 2-3 XOR-permuted by k-row bits 0-1, and is read with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): each group of 16 lanes
+// turns a 4 x 16 block into 16 columns of four consecutive k. A partial last
+// slice (K not a multiple of 32) goes through registers with zero fill.
 //
-// Rows beyond M (or N) read a clamped, valid row; they only feed output rows
-// (columns) that are never stored.
+// Rows (columns) beyond M or N read a clamped, valid row (chunk); they only
+// feed outputs that are never stored.
 //
-// The epilogue stages each 32 x 256 band of the tile through LDS: coalesced
-// stores of D, C0 blend, optional row scale, and the transposed copy (or the
-// SYRK mirror) written from LDS columns.
+// Epilogue: interior tiles go through LDS in two halves of 128 rows and are
+// written as whole rows in 16- or 32-byte pieces (C0 blend and row scale on
+// the way). Edge tiles, a transposed copy Dt, and the SYRK mirror use 32-row
+// bands through LDS with the transposed copy written from LDS columns.
 #include "gemm.hpp"
-
-#include <type_traits>
 
 namespace mao {
 
@@ -65,67 +70,6 @@ __device__ __forceinline__ void d_store(void* D, bool f32, int64_t off, float v)
     ((float*)D)[off] = v;
   else
     ((bf16_t*)D)[off] = f32_to_bf16(v);
-}
-
-// Interior, non-diagonal tiles: stores straight from the accumulators. Lane
-// (h, r32) of block (i, j) holds rows 8g + 4h + e (g, e < 4) of column r32;
-// each store instruction covers 32 consecutive columns of two rows, and the
-// transposed copy takes four consecutive rows as one vector.
-template <bool D32, bool C32>
-__device__ __forceinline__ void epilogue_block(const f32x16_t& a, int r_base, int col, float alpha,
-                                               float beta, const void* C0, int64_t ldc0,
-                                               const float* rs, void* D, int64_t ldd, void* Tt,
-                                               int64_t ldt) {
-  typedef typename std::conditional<D32, float, bf16_t>::type TD;
-  typedef typename std::conditional<C32, float, bf16_t>::type TC;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int r0 = r_base + 8 * g;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = alpha * a[4 * g + e];
-      if (C0) v[e] += beta * load_f32<TC>((const TC*)C0 + (int64_t)(r0 + e) * ldc0 + col);
-      if (rs) v[e] *= rs[r0 + e];
-    }
-    if (D) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) store_f32<TD>((TD*)D + (int64_t)(r0 + e) * ldd + col, v[e]);
-    }
-    if (Tt) {
-      TD* q = (TD*)Tt + (int64_t)col * ldt + r0;
-      if constexpr (D32) {
-        *(float4*)q = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *(uint2*)q = pk;
-      }
-    }
-  }
-}
-
-// Interior, non-diagonal tiles: stores straight from the accumulators. Lane
-// (h, r32) of block (i, j) holds rows 8g + 4h + e (g, e < 4) of column r32;
-// each store instruction covers 32 consecutive columns of two rows, and the
-// transposed copy takes four consecutive rows as one vector. Blocks are named
-// one by one so every accumulator index is a constant.
-template <bool D32, bool C32>
-__device__ __forceinline__ void epilogue_direct(const f32x16_t (&acc)[4][4], int m0, int n0,
-                                                int wm, int wn, int h, int r32, float alpha,
-                                                float beta, const void* C0, int64_t ldc0,
-                                                const float* rs, void* D, int64_t ldd, void* Tt,
-                                                int64_t ldt) {
-#define MAO_EPI(I, J)                                                                        \
-  epilogue_block<D32, C32>(acc[I][J], m0 + wm * 128 + (I) * 32 + 4 * h,                       \
-                           n0 + wn * 128 + (J) * 32 + r32, alpha, beta, C0, ldc0, rs, D, ldd, \
-                           Tt, ldt);
-  MAO_EPI(0, 0) MAO_EPI(0, 1) MAO_EPI(0, 2) MAO_EPI(0, 3)
-  MAO_EPI(1, 0) MAO_EPI(1, 1) MAO_EPI(1, 2) MAO_EPI(1, 3)
-  MAO_EPI(2, 0) MAO_EPI(2, 1) MAO_EPI(2, 2) MAO_EPI(2, 3)
-  MAO_EPI(3, 0) MAO_EPI(3, 1) MAO_EPI(3, 2) MAO_EPI(3, 3)
-#undef MAO_EPI
 }
 
 template <bool BKM>
@@ -397,14 +341,79 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   const float alpha = P.alpha, beta = P.beta;
   const float* rs = P.row_scale;
   if (!diag && !Tt && m0 + TB <= M && n0 + TB <= N) {
-    if (d32 && c32)
-      epilogue_direct<true, true>(acc, m0, n0, wm, wn, h, r32, alpha, beta, C0, P.ldc0, rs, D, P.ldd, Tt, ldt);
-    else if (d32)
-      epilogue_direct<true, false>(acc, m0, n0, wm, wn, h, r32, alpha, beta, C0, P.ldc0, rs, D, P.ldd, Tt, ldt);
-    else if (c32)
-      epilogue_direct<false, true>(acc, m0, n0, wm, wn, h, r32, alpha, beta, C0, P.ldc0, rs, D, P.ldd, Tt, ldt);
-    else
-      epilogue_direct<false, false>(acc, m0, n0, wm, wn, h, r32, alpha, beta, C0, P.ldc0, rs, D, P.ldd, Tt, ldt);
+    // Interior tiles: the fp32 tile goes through LDS in two halves of 128 rows
+    // (four 32-row bands, one per stage buffer); then each thread finishes 8
+    // consecutive columns of a row -- C0 read and D written in 16-byte (bf16)
+    // or 32-byte (fp32) pieces, one whole row per 32 lanes. Column bit 5 is
+    // flipped on band rows with bit 2 set (the lane half h of an accumulator),
+    // so both lane halves of a write hit different banks.
+#define MAO_BAND(I, ST)                                                                   \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                         \
+    _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                      \
+      const int rb_ = 8 * (v >> 2) + 4 * h + (v & 3);                                     \
+      const int col_ = (wn * 128 + j * 32 + r32) ^ (h << 5);                              \
+      ((float*)ST)[rb_ * TB + col_] = acc[I][j][v];                                       \
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+        MAO_BAND(0, st0)
+        MAO_BAND(1, st1)
+        MAO_BAND(2, st2)
+        MAO_BAND(3, st3)
+      }
+      __syncthreads();
+      const int c8 = (threadIdx.x & 31) * 8;
+      const int64_t gcol = n0 + c8;
+      for (int it = 0; it < 16; ++it) {
+        const int row = it * 8 + (threadIdx.x >> 5);
+        const int band = row >> 5, rb = row & 31;
+        const unsigned char* bp = band == 0 ? st0 : band == 1 ? st1 : band == 2 ? st2 : st3;
+        const float* src = (const float*)bp + rb * TB + (c8 ^ (((rb >> 2) & 1) << 5));
+        const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+        float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= alpha;
+        const int64_t grow = m0 + half * 128 + row;
+        if (C0) {
+          if (c32) {
+            const float* cp = (const float*)C0 + grow * P.ldc0 + gcol;
+            const float4 y0 = *(const float4*)cp, y1 = *(const float4*)(cp + 4);
+            v[0] += beta * y0.x; v[1] += beta * y0.y; v[2] += beta * y0.z; v[3] += beta * y0.w;
+            v[4] += beta * y1.x; v[5] += beta * y1.y; v[6] += beta * y1.z; v[7] += beta * y1.w;
+          } else {
+            const uint4 y = *(const uint4*)((const bf16_t*)C0 + grow * P.ldc0 + gcol);
+            const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[2 * e] += beta * bf16_to_f32((bf16_t)(w[e] & 0xffff));
+              v[2 * e + 1] += beta * bf16_to_f32((bf16_t)(w[e] >> 16));
+            }
+          }
+        }
+        if (rs) {
+          const float sc = rs[grow];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= sc;
+        }
+        if (D) {
+          if (d32) {
+            float* dp = (float*)D + grow * P.ldd + gcol;
+            *(float4*)dp = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)(dp + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          } else {
+            uint4 pk;
+            pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+            pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+            pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+            *(uint4*)((bf16_t*)D + grow * P.ldd + gcol) = pk;
+          }
+        }
+      }
+      __syncthreads();
+    }
+#undef MAO_BAND
     return;
   }
   float* slab = (float*)st0;
