@@ -65,6 +65,51 @@ __device__ __forceinline__ void store4(T* row, int j, int cols, const float v[4]
   }
 }
 
+// 8 consecutive elements starting at column j (a multiple of 8) of a row with
+// `cols` columns: 2 x 16-byte (fp32) or one 16-byte (bf16) access, element
+// by element at the ragged end.
+template <typename T>
+__device__ __forceinline__ void load8(const T* row, int j, int cols, float v[8]) {
+  if (j + 8 <= cols) {
+    if constexpr (sizeof(T) == 4) {
+      Vec4<float>::load((const float*)row + j, v);
+      Vec4<float>::load((const float*)row + j + 4, v + 4);
+    } else {
+      const uint4 u = *(const uint4*)(row + j);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = bf16_to_f32((bf16_t)(w[e] & 0xffff));
+        v[2 * e + 1] = bf16_to_f32((bf16_t)(w[e] >> 16));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (j + e < cols) ? load_f32<T>(row + j + e) : 0.f;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* row, int j, int cols, const float v[8]) {
+  if (j + 8 <= cols) {
+    if constexpr (sizeof(T) == 4) {
+      Vec4<float>::store((float*)row + j, v);
+      Vec4<float>::store((float*)row + j + 4, v + 4);
+    } else {
+      uint4 u;
+      u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+      u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+      *(uint4*)(row + j) = u;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (j + e < cols) store_f32<T>(row + j + e, v[e]);
+  }
+}
+
 // Row range of this block for a matrix split into nrb row-blocks.
 __device__ __forceinline__ void row_range(int rows, int nrb, int& r0, int& r1) {
   const int per = (rows + nrb - 1) / nrb;
@@ -74,31 +119,51 @@ __device__ __forceinline__ void row_range(int rows, int nrb, int& r0, int& r1) {
 
 // ---------------------------------------------------------------------------
 
+// The 8-column chunks of this block's rows, numbered row by row: chunk q is
+// row r0 + q / c8, columns 8 (q % c8) .. + 7 (32-bit arithmetic).
+struct Chunks {
+  int r0;
+  unsigned c8, n;
+  __device__ __forceinline__ void at(unsigned q, int& i, int& j) const {
+    const unsigned ii = q / c8;
+    i = r0 + (int)ii;
+    j = (int)(q - ii * c8) * 8;
+  }
+};
+
+__device__ __forceinline__ Chunks block_chunks(int rows, int cols, int nrb) {
+  int r0, r1;
+  row_range(rows, nrb, r0, r1);
+  Chunks c;
+  c.r0 = r0;
+  c.c8 = (unsigned)((cols + 7) >> 3);
+  c.n = (unsigned)max(0, r1 - r0) * c.c8;
+  return c;
+}
+
 template <typename TG>
 __global__ __launch_bounds__(kBlock) void ema_sumsq_kernel(View M, View G, int rows, int cols,
                                                            float beta, float* partial, int nrb) {
   const int b = blockIdx.y;
   float* Mb = (float*)M.p + (int64_t)b * M.stride;
   const TG* Gb = (const TG*)G.p + (int64_t)b * G.stride;
-  int r0, r1;
-  row_range(rows, nrb, r0, r1);
-  const int c4 = (cols + 3) >> 2;
-  const int64_t nq = (int64_t)max(0, r1 - r0) * c4;
+  const Chunks ch = block_chunks(rows, cols, nrb);
   const float om = 1.f - beta;
   float acc = 0.f;
-  for (int64_t q = threadIdx.x; q < nq; q += kBlock) {
-    const int i = r0 + (int)(q / c4);
-    const int j = (int)(q % c4) * 4;
-    float m[4], g[4];
+#pragma unroll 2
+  for (unsigned q = threadIdx.x; q < ch.n; q += kBlock) {
+    int i, j;
+    ch.at(q, i, j);
+    float m[8], g[8];
     float* mrow = Mb + (int64_t)i * M.ld;
-    load4<float>(mrow, j, cols, m);
-    load4<TG>(Gb + (int64_t)i * G.ld, j, cols, g);
+    load8<float>(mrow, j, cols, m);
+    load8<TG>(Gb + (int64_t)i * G.ld, j, cols, g);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       m[e] = beta * m[e] + om * g[e];
       acc += m[e] * m[e];
     }
-    store4<float>(mrow, j, cols, m);
+    store8<float>(mrow, j, cols, m);
   }
   if (partial) {
     __shared__ float sc[16];
@@ -160,6 +225,27 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(View In, int rows, in
   }
 }
 
+// Direct-only variant of transpose_kernel: out = scale * in, cast.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(kBlock) void scale_cast_kernel(View In, int rows, int cols,
+                                                            const float* scale, View Out, int nrb) {
+  const int b = blockIdx.y;
+  const TI* in = (const TI*)In.p + (int64_t)b * In.stride;
+  TO* out = (TO*)Out.p + (int64_t)b * Out.stride;
+  const float sc = scale ? scale[b] : 1.f;
+  const Chunks ch = block_chunks(rows, cols, nrb);
+#pragma unroll 2
+  for (unsigned q = threadIdx.x; q < ch.n; q += kBlock) {
+    int i, j;
+    ch.at(q, i, j);
+    float v[8];
+    load8<TI>(in + (int64_t)i * In.ld, j, cols, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= sc;
+    store8<TO>(out + (int64_t)i * Out.ld, j, cols, v);
+  }
+}
+
 template <typename TX>
 __global__ __launch_bounds__(kBlock) void row_sumsq_kernel(View X, int rows, int cols,
                                                            const float* w, float* ss) {
@@ -210,53 +296,49 @@ __global__ __launch_bounds__(kBlock) void update_kernel(View W, View O, int rows
   float* outb = Out.p ? (float*)Out.p + (int64_t)b * Out.stride : nullptr;
   const float* rsb = rs ? rs + (int64_t)b * rows : nullptr;
   const float* csb = cs ? cs + (int64_t)b * cols : nullptr;
-  int r0, r1;
-  row_range(rows, nrb, r0, r1);
-  const int c4 = (cols + 3) >> 2;
-  const int64_t nq = (int64_t)max(0, r1 - r0) * c4;
-  for (int64_t q = threadIdx.x; q < nq; q += kBlock) {
-    const int i = r0 + (int)(q / c4);
-    const int j = (int)(q % c4) * 4;
-    float w[4], o[4];
+  const Chunks ch = block_chunks(rows, cols, nrb);
+#pragma unroll 2
+  for (unsigned q = threadIdx.x; q < ch.n; q += kBlock) {
+    int i, j;
+    ch.at(q, i, j);
+    float w[8], o[8];
     TW* wrow = Wb + (int64_t)i * W.ld;
-    load4<TW>(wrow, j, cols, w);
-    load4<TO>(Ob + (int64_t)i * O.ld, j, cols, o);
+    load8<TW>(wrow, j, cols, w);
+    load8<TO>(Ob + (int64_t)i * O.ld, j, cols, o);
     const float si = s * (rsb ? rsb[i] : 1.f);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       const float cj = (csb && j + e < cols) ? csb[j + e] : 1.f;
       o[e] = si * cj * o[e];
       w[e] = w[e] - lr * (wd * w[e] + o[e]);
     }
-    store4<TW>(wrow, j, cols, w);
-    if (outb) store4<float>(outb + (int64_t)i * Out.ld, j, cols, o);
+    store8<TW>(wrow, j, cols, w);
+    if (outb) store8<float>(outb + (int64_t)i * Out.ld, j, cols, o);
   }
 }
 
 __global__ __launch_bounds__(kBlock) void soap_adam_kernel(View Gt, View Mt, View V, int rows,
                                                            int cols, float beta2, float bc1,
                                                            float bc2, float eps, int nrb) {
-  int r0, r1;
-  row_range(rows, nrb, r0, r1);
-  const int c4 = (cols + 3) >> 2;
-  const int64_t nq = (int64_t)max(0, r1 - r0) * c4;
+  const Chunks ch = block_chunks(rows, cols, nrb);
   const float ob = 1.f - beta2, ib1 = 1.f / bc1, ib2 = 1.f / bc2;
-  for (int64_t q = threadIdx.x; q < nq; q += kBlock) {
-    const int i = r0 + (int)(q / c4);
-    const int j = (int)(q % c4) * 4;
-    float g[4], m[4], v[4];
+#pragma unroll 2
+  for (unsigned q = threadIdx.x; q < ch.n; q += kBlock) {
+    int i, j;
+    ch.at(q, i, j);
+    float g[8], m[8], v[8];
     float* grow = (float*)Gt.p + (int64_t)i * Gt.ld;
     float* vrow = (float*)V.p + (int64_t)i * V.ld;
-    load4<float>(grow, j, cols, g);
-    load4<float>((const float*)Mt.p + (int64_t)i * Mt.ld, j, cols, m);
-    load4<float>(vrow, j, cols, v);
+    load8<float>(grow, j, cols, g);
+    load8<float>((const float*)Mt.p + (int64_t)i * Mt.ld, j, cols, m);
+    load8<float>(vrow, j, cols, v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       v[e] = beta2 * v[e] + ob * g[e] * g[e];
       g[e] = (m[e] * ib1) / (sqrtf(v[e] * ib2) + eps);
     }
-    store4<float>(vrow, j, cols, v);
-    store4<float>(grow, j, cols, g);
+    store8<float>(vrow, j, cols, v);
+    store8<float>(grow, j, cols, g);
   }
 }
 
@@ -327,24 +409,22 @@ __global__ __launch_bounds__(kBlock) void foam_precond_kernel(View Mr, int m, in
                                                               const float* r, const float* c,
                                                               const float* tau, float bc1,
                                                               float bc2, float eps, int nrb) {
-  int r0, r1;
-  row_range(m, nrb, r0, r1);
-  const int c4 = (n + 3) >> 2;
-  const int64_t nq = (int64_t)max(0, r1 - r0) * c4;
+  const Chunks ch = block_chunks(m, n, nrb);
   const float t = tau[0], ib1 = 1.f / bc1, ib2 = 1.f / bc2;
-  for (int64_t q = threadIdx.x; q < nq; q += kBlock) {
-    const int i = r0 + (int)(q / c4);
-    const int j = (int)(q % c4) * 4;
+#pragma unroll 2
+  for (unsigned q = threadIdx.x; q < ch.n; q += kBlock) {
+    int i, j;
+    ch.at(q, i, j);
     float* row = (float*)Mr.p + (int64_t)i * Mr.ld;
-    float x[4];
-    load4<float>(row, j, n, x);
+    float x[8];
+    load8<float>(row, j, n, x);
     const float ri = r[i] * ib2;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       const float cj = (j + e < n) ? c[j + e] * ib2 : 0.f;
       x[e] = (x[e] * ib1) / (sqrtf(t * ri * cj) + eps);
     }
-    store4<float>(row, j, n, x);
+    store8<float>(row, j, n, x);
   }
 }
 
@@ -465,6 +545,16 @@ mao_status finalize_inv_norm(const float* partial, int nrb, int batch, float eps
 
 mao_status scale_cast_transpose(View M, int rows, int cols, int batch, const float* scale,
                                 View direct, View trans, int x_dtype, hipStream_t s) {
+  if (trans.p == nullptr) {
+    if (direct.p == nullptr) return MAO_OK;
+    const int nrb = rowblocks_for(rows, batch);
+    if (x_dtype == MAO_BF16)
+      hipLaunchKernelGGL((scale_cast_kernel<float, bf16_t>), dim3(nrb, batch), dim3(kBlock), 0, s, M, rows, cols, scale, direct, nrb);
+    else
+      hipLaunchKernelGGL((scale_cast_kernel<float, float>), dim3(nrb, batch), dim3(kBlock), 0, s, M, rows, cols, scale, direct, nrb);
+    MAO_LAUNCH_CHECK();
+    return MAO_OK;
+  }
   dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
   if (x_dtype == MAO_BF16)
     hipLaunchKernelGGL((transpose_kernel<float, bf16_t>), grid, dim3(kBlock), 0, s, M, rows, cols, scale, direct, trans);
