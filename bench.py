@@ -43,6 +43,82 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# Fabric traffic of the Newton-Schulz contraction, from two rocprofv3 --pmc
+# runs of the default workload (FETCH_SIZE, then WRITE_SIZE; KiB per
+# dispatch), each scaled by what the same counter reads for a 1 GiB
+# device-to-device copy (--calibrate-copy). It describes the kernel sources it
+# was taken on and is reported only while they are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_contraction_llama8b_layer_traffic.json")
+GEMM_SOURCES = [os.path.join(ROOT, "matrix_aware_optimizers_amd", "csrc", f)
+                for f in ("gemm_bf16.hip", "gemm.hip", "gemm.hpp", "common.hpp")]
+NS_KERNEL = "gemm_bf16_dl_kernel"
+COPY_KERNEL = "copyBuffer"
+
+
+def gemm_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per Newton-Schulz launch from the committed counter summary, or
+    None when the contraction sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != gemm_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def write_traffic(fetch_csv: str, write_csv: str, command: str):
+    """Summarise two rocprofv3 counter CSVs (FETCH_SIZE, WRITE_SIZE) of the
+    default workload run with --calibrate-copy into TRAFFIC_FILE."""
+    import csv
+
+    def per_kernel(path, counter):
+        ns, copy = [], []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if NS_KERNEL in r["Kernel_Name"]:
+                    ns.append(v)
+                elif COPY_KERNEL in r["Kernel_Name"]:
+                    copy.append(v)
+        if not ns or len(copy) != 1:
+            raise SystemExit(f"{path}: expected Newton-Schulz dispatches and one calibration copy")
+        return sum(ns) / len(ns), copy[0], len(ns)
+
+    f_ns, f_copy, n = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_ns, w_copy, _ = per_kernel(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    f_scale, w_scale = gib_kib / f_copy, gib_kib / w_copy
+    rec = {
+        "kernel": NS_KERNEL,
+        "workload": "llama8b_layer_muon_bf16",
+        "dispatches": n,
+        "fetch_kib_per_launch": round(f_ns, 1),
+        "write_kib_per_launch": round(w_ns, 1),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "bytes_per_launch": round((f_ns * f_scale + w_ns * w_scale) * 1024.0),
+        "source_sha256": gemm_source_digest(),
+        "command": command,
+    }
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
 def ns_alg_flops(m: int, n: int, k: int = 5) -> float:
     """Algorithmic flops of k quintic iterations on an m x n matrix (symmetric
     products at half cost): per iteration a^2 b (X X^T) + a^3 (A A) + 2 a^2 b
@@ -197,7 +273,7 @@ def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
                      "peak": PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s",
                      "frac": achieved / (PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS),
-                     "traffic": None,
+                     "traffic": recorded_traffic() if workload_name == "llama8b_layer_muon_bf16" else None,
                      "kernel": "Newton-Schulz contraction (X X^T, A A, B X)",
                      "launches": ns_cnt, "avg_launch_ms": ns_ms / max(ns_cnt, 1),
                      "alg_tflop_per_launch": ns_fl / max(ns_cnt, 1) / 1e12},
@@ -376,7 +452,15 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (a known-size reference "
                          "for profiler byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 counter CSVs of this workload into the "
+                         "committed traffic record, then exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic,
+                      command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python3 "
+                              "bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy")
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build's step runs whole matrices on one device "
               "and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
