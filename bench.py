@@ -401,18 +401,25 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
         wl.add_embedding(*embedding)
     log("warmup")
     t = 1
+    w0 = time.perf_counter()
     for _ in range(args.warmup):
         wl.step(t)
         t += 1
     torch.cuda.synchronize()
+    # steps of a second or more: wait for each step and say so, so that a long
+    # run keeps printing (the added host wait per step is microseconds)
+    slow = (time.perf_counter() - w0) / max(args.warmup, 1) > 1.0
     mao.timing_collect()
     mao.timing_enable(True)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         wl.step(t)
         t += 1
+        if slow:
+            torch.cuda.synchronize()
+            log(f"step {i + 1}/{args.steps} done")
     end.record()
     torch.cuda.synchronize()
     mao.timing_enable(False)

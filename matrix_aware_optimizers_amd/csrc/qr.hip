@@ -59,6 +59,7 @@ struct PanelArgs {
   unsigned* counter;
   int* err;
   const int* pred;
+  const int* pred2;  // run only when *pred2 != 0 (the fast panel gave up)
 };
 
 __device__ void grid_barrier(unsigned* counter, unsigned target, int* err) {
@@ -82,6 +83,7 @@ __device__ void grid_barrier(unsigned* counter, unsigned target, int* err) {
 
 __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelArgs a) {
   if (a.pred != nullptr && *a.pred == 0) return;
+  if (a.pred2 != nullptr && *a.pred2 == 0) return;
   __shared__ float X[NB][LDX];
   __shared__ float red[NB][LDX];
   __shared__ float Tl[NB][NB + 1];
@@ -93,7 +95,14 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelArgs a) {
   const int r = j0 + g * TPB + t;
   const bool valid = r < n;
 
-  for (int k = 0; k < NB; ++k) X[k][t] = (valid && k < nb) ? a.S[(int64_t)(j0 + k) * a.ldS + r] : 0.f;
+  for (int k0 = 0; k0 < NB; k0 += 16) {
+    float xv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      xv[u] = (valid && k0 + u < nb) ? a.S[(int64_t)(j0 + k0 + u) * a.ldS + r] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) X[k0 + u][t] = xv[u];
+  }
   __syncthreads();
 
   unsigned bar = 0;
@@ -207,14 +216,346 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelArgs a) {
   if (valid) {
     float* zf = a.Zf + (int64_t)(r - j0) * NB;
     float* zo = a.Zo + (int64_t)(r - j0) * NB;
+    float vr[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) vr[i] = (i < nb) ? X[i][t] : 0.f;
     for (int c = 0; c < NB; ++c) {
-      float sf = 0.f, so = 0.f;
-      for (int i = 0; i < nb; ++i) {
-        sf += X[i][t] * Tl[c][i];
-        so += X[i][t] * Tl[i][c];
+      float sf[4] = {0.f, 0.f, 0.f, 0.f}, so[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        sf[i & 3] = fmaf(vr[i], Tl[c][i], sf[i & 3]);
+        so[i & 3] = fmaf(vr[i], Tl[i][c], so[i & 3]);
       }
-      zf[c] = sf;
-      zo[c] = so;
+      zf[c] = (sf[0] + sf[1]) + (sf[2] + sf[3]);
+      zo[c] = (so[0] + so[1]) + (so[2] + so[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fast panel: the same outputs (V, T, signs, V T^T, V T) from seven grid
+// synchronisations instead of one per column.
+//
+// 1. Shifted CholeskyQR3 in fp64 arithmetic on the fp32 panel A (len x nb):
+//    three passes of Gram G = Y^T Y (fp64 sums of exact fp64 products),
+//    Cholesky G (+ s I on the first pass) = R^T R, Y <- Y R^{-1}; the first
+//    pass's shift s = 11 (len nb + nb (nb+1)) 2^-53 tr(G) makes the
+//    factorisation well defined for any numerically full-rank panel, the two
+//    plain passes restore orthogonality. Q = the third pass's Y.
+// 2. Householder representation rebuilt from Q: with D = diag(d), d = +-1,
+//    the first nb columns of H = I - Y T Y^T equal Q D, so [I; 0] - Q D =
+//    Y (T Y1^T) is an LU factorisation (Y unit lower trapezoidal, Y1 its top
+//    block). It is computed without pivoting, choosing d_j = sign of the
+//    eliminated diagonal entry of -Q1 so that every pivot is 1 + |.| >= 1;
+//    then T = U Y1^{-T}, the rows of Y below the top block are -q D U^{-1},
+//    and R~ = D R, so column j of Q gets the sign d_j.
+// Any breakdown -- a zero or non-finite Cholesky pivot, or a third-pass Gram
+// diagonal away from 1 -- is decided identically by every workgroup, which
+// then all return; the per-column Householder panel runs instead (a flag).
+constexpr int NU = NB * (NB + 1) / 2;   // packed upper-triangular entries
+constexpr int LDG = NB + 1;             // padded fp64 LDS row
+
+struct CholArgs {
+  const float* S;
+  int64_t ldS;
+  int n, j0, nb;
+  float* V;
+  int64_t ldV;
+  float* Zf;
+  float* Zo;
+  float* sign;
+  float* T;        // 4096 floats: T, broadcast to every workgroup
+  double* part;    // G x NU per-workgroup Gram partials
+  double* gram;    // NU reduced Gram entries
+  double* bcast;   // U (NB x NB) then d (NB)
+  unsigned* counter;
+  int* err;
+  const int* pred;
+  int* fail;       // set to 1 when the panel falls back to the Householder kernel
+};
+
+__device__ __forceinline__ int upk(int i, int k) { return i * NB - (i * (i - 1)) / 2 + (k - i); }
+
+__global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
+  if (a.pred != nullptr && *a.pred == 0) return;
+  __shared__ float X[NB][LDX];      // current Y (fp32), later V
+  __shared__ double Gs[NB][LDG];    // Gram / LU work
+  __shared__ double Rt[NB][LDG];    // Cholesky factor, transposed (Rt[k][l] = R[l][k]); later U
+  __shared__ float Tl[NB][NB + 1];
+  __shared__ double dinv[NB];
+  __shared__ float dsg[NB];
+  __shared__ double red64[TPB];
+  __shared__ int bad;
+
+  const int t = threadIdx.x, g = blockIdx.x, G = gridDim.x;
+  const int n = a.n, j0 = a.j0, nb = a.nb, len = n - j0;
+  const int r = j0 + g * TPB + t;
+  const bool valid = r < n;
+  const int li = g * TPB + t;  // row of the panel
+
+  for (int k0 = 0; k0 < NB; k0 += 16) {
+    float xv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      xv[u] = (valid && k0 + u < nb) ? a.S[(int64_t)(j0 + k0 + u) * a.ldS + r] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) X[k0 + u][t] = xv[u];
+  }
+  if (t == 0) bad = 0;
+
+  unsigned bar = 0;
+  double y[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) y[k] = 0.0;
+
+  for (int pass = 0; pass < 3; ++pass) {
+    __syncthreads();
+    // ---- partial Gram of this workgroup's rows: 36 upper 8 x 8 blocks x 7 row chunks
+    {
+      double acc[8][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) acc[u][w] = 0.0;
+      const int blk = t % 36, chunk = t / 36;
+      int bi = 0, rem = blk;
+      while (rem >= 8 - bi) {
+        rem -= 8 - bi;
+        ++bi;
+      }
+      const int bk = bi + rem;
+      if (chunk < 7) {
+        const int r0 = chunk * 37, r1 = min(TPB, r0 + 37);
+        for (int q = r0; q < r1; ++q) {
+          double va[8], vb[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            va[u] = (double)X[bi * 8 + u][q];
+            vb[u] = (double)X[bk * 8 + u][q];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) acc[u][w] = fma(va[u], vb[w], acc[u][w]);
+        }
+      }
+      for (int c = 0; c < 7; ++c) {
+        __syncthreads();
+        if (chunk == c) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+              const int i = bi * 8 + u, k = bk * 8 + w;
+              if (i <= k) Gs[i][k] = (c == 0 ? 0.0 : Gs[i][k]) + acc[u][w];
+            }
+        }
+      }
+      __syncthreads();
+      for (int idx = t; idx < NB * NB; idx += TPB) {
+        const int i = idx / NB, k = idx % NB;
+        if (i <= k) a.part[(size_t)g * NU + upk(i, k)] = Gs[i][k];
+      }
+    }
+    grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+    // ---- reduce the partials: workgroup g owns a contiguous range of entries;
+    // `sub` threads share an entry, each summing every sub-th partial (loads
+    // in flight together), then one of them adds the sub sums in order.
+    {
+      const int per = (NU + G - 1) / G;
+      const int e0 = g * per, e1 = min(NU, e0 + per);
+      const int sub = max(1, min(16, TPB / per));
+      const int slots = (TPB / sub) * sub;
+      for (int base = e0; base < e1; base += TPB / sub) {
+        const int e = base + t / sub, q = t % sub;
+        double sum = 0.0;
+        if (t < slots && e < e1) {
+          int gg = q;
+          for (; gg + 3 * sub < G; gg += 4 * sub) {
+            const double v0 = a.part[(size_t)gg * NU + e];
+            const double v1 = a.part[(size_t)(gg + sub) * NU + e];
+            const double v2 = a.part[(size_t)(gg + 2 * sub) * NU + e];
+            const double v3 = a.part[(size_t)(gg + 3 * sub) * NU + e];
+            sum += v0;
+            sum += v1;
+            sum += v2;
+            sum += v3;
+          }
+          for (; gg < G; gg += sub) sum += a.part[(size_t)gg * NU + e];
+        }
+        __syncthreads();
+        red64[t] = sum;
+        __syncthreads();
+        if (t < slots && q == 0 && e < e1) {
+          double tot = 0.0;
+          for (int u = 0; u < sub; ++u) tot += red64[t + u];
+          a.gram[e] = tot;
+        }
+        __syncthreads();
+      }
+    }
+    grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+    // ---- Gram into LDS (symmetric), identity on the padded columns, shift
+    {
+      double gv[NB * NB / TPB];
+#pragma unroll
+      for (int u = 0; u < NB * NB / TPB; ++u) {
+        const int idx = t + u * TPB, i = idx >> 6, k = idx & 63;
+        gv[u] = (i < nb && k < nb) ? a.gram[i <= k ? upk(i, k) : upk(k, i)] : (i == k ? 1.0 : 0.0);
+      }
+#pragma unroll
+      for (int u = 0; u < NB * NB / TPB; ++u) {
+        const int idx = t + u * TPB;
+        Gs[idx >> 6][idx & 63] = gv[u];
+      }
+    }
+    __syncthreads();
+    if (pass == 2) {
+      // the second pass left Q nearly orthonormal: its Gram diagonal is ~1
+      if (t < nb && !(fabs(Gs[t][t] - 1.0) < 1e-3)) bad = 1;
+    }
+    if (pass == 0 && t == 0) {
+      double tr = 0.0;
+      for (int k = 0; k < nb; ++k) tr += Gs[k][k];
+      const double sh = 11.0 * ((double)len * nb + (double)nb * (nb + 1)) * 0x1p-53 * tr;
+      for (int k = 0; k < nb; ++k) Gs[k][k] += sh;
+    }
+    // ---- Cholesky G = R^T R, row k of R into Rt[.][k]
+    for (int k = 0; k < NB; ++k) {
+      __syncthreads();
+      const double piv = Gs[k][k];
+      if (!(piv > 1e-300) || !(piv < 1e300)) {
+        if (t == 0) bad = 1;
+      }
+      const double rkk = sqrt(fmax(piv, 1e-300));
+      if (t >= k && t < NB) Rt[t][k] = (t == k) ? rkk : Gs[k][t] / rkk;
+      if (t == 0) dinv[k] = 1.0 / rkk;
+      __syncthreads();
+      for (int i = k + 1 + (t >> 4); i < NB; i += 16)
+        for (int j = i + (t & 15); j < NB; j += 16) Gs[i][j] -= Rt[i][k] * Rt[j][k];
+    }
+    __syncthreads();
+    if (bad) {
+      if (g == 0 && t == 0) *a.fail = 1;
+      return;  // every workgroup decided alike
+    }
+    // ---- Y <- Y R^{-1} for this thread's row (forward substitution)
+#pragma unroll
+    for (int k = 0; k < NB; ++k) y[k] = (double)X[k][t];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      y[k] *= dinv[k];
+#pragma unroll
+      for (int j = k + 1; j < NB; ++j) y[j] = fma(-y[k], Rt[j][k], y[j]);
+    }
+    if (pass < 2) {
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < NB; ++k) X[k][t] = (float)y[k];
+    }
+  }
+
+  // ---- reconstruction: LU of -Q1 (top nb x nb block) with sign choice, T
+  __syncthreads();
+  if (g == 0) {
+    if (t < nb) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (k < nb) Gs[t][k] = -y[k];
+    }
+    for (int j = 0; j < nb; ++j) {
+      __syncthreads();
+      const double zjj = Gs[j][j];
+      const double dj = zjj >= 0.0 ? 1.0 : -1.0;
+      const double ujj = 1.0 + dj * zjj;
+      if (t == 0) {
+        dsg[j] = (float)dj;
+        Rt[j][j] = ujj;  // U diagonal (Rt reused for U, stored U[i][c] at Rt[i][c])
+      }
+      if (t > j && t < nb) Gs[t][j] = dj * Gs[t][j] / ujj;  // L[t][j]
+      __syncthreads();
+      for (int rr = j + 1 + (t >> 4); rr < nb; rr += 16)
+        for (int cc = j + 1 + (t & 15); cc < nb; cc += 16) Gs[rr][cc] -= Gs[rr][j] * Gs[j][cc];
+    }
+    __syncthreads();
+    // U strictly upper: U[i][c] = d_c Z[i][c]
+    for (int idx = t; idx < nb * nb; idx += TPB) {
+      const int i = idx / nb, c = idx % nb;
+      if (i < c) Rt[i][c] = (double)dsg[c] * Gs[i][c];
+    }
+    __syncthreads();
+    // T = U L^{-T}: row i, t_ij = U_ij - sum_{i <= l < j} t_il L_jl
+    if (t < nb) {
+      const int i = t;
+      double trow[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) trow[j] = (j >= i && j < nb) ? Rt[i][j] : 0.0;
+#pragma unroll
+      for (int l = 0; l < NB; ++l) {
+        if (l >= i && l < nb) {
+#pragma unroll
+          for (int j = l + 1; j < NB; ++j)
+            if (j < nb) trow[j] = fma(-trow[l], Gs[j][l], trow[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) a.T[i * NB + j] = (j >= i && j < nb) ? (float)trow[j] : 0.f;
+    } else if (t < NB) {
+      for (int j = 0; j < NB; ++j) a.T[t * NB + j] = 0.f;
+    }
+    for (int e = t; e < nb * nb; e += TPB) {
+      const int i = e / nb, c = e % nb;
+      a.bcast[i * NB + c] = (i <= c) ? Rt[i][c] : 0.0;
+    }
+    if (t < nb) {
+      a.bcast[NB * NB + t] = (double)dsg[t];
+      a.sign[j0 + t] = dsg[t];
+    }
+  }
+  grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+  if (g != 0) {
+    for (int e = t; e < nb * nb; e += TPB) Rt[e / nb][e % nb] = a.bcast[(e / nb) * NB + e % nb];
+    if (t < nb) dsg[t] = (float)a.bcast[NB * NB + t];
+  }
+  for (int e = t; e < NB * NB; e += TPB) Tl[e >> 6][e & 63] = a.T[e];
+  __syncthreads();
+
+  // ---- rows of Y: top block from L, the rest -q D U^{-1}
+  if (li < nb) {
+    for (int k = 0; k < NB; ++k) X[k][t] = (k < li) ? (float)Gs[li][k] : (k == li ? 1.f : 0.f);
+  } else {
+    double z[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) z[k] = (k < nb) ? -(double)dsg[k] * y[k] : 0.0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (k < nb) {
+        z[k] = z[k] / Rt[k][k];
+#pragma unroll
+        for (int j = k + 1; j < NB; ++j)
+          if (j < nb) z[j] = fma(-z[k], Rt[k][j], z[j]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) X[k][t] = valid ? (float)z[k] : 0.f;
+  }
+  __syncthreads();
+  if (valid) {
+    for (int k = 0; k < nb; ++k) a.V[(int64_t)k * a.ldV + li] = X[k][t];
+    float* zf = a.Zf + (int64_t)li * NB;
+    float* zo = a.Zo + (int64_t)li * NB;
+    float vr[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) vr[i] = (i < nb) ? X[i][t] : 0.f;
+    for (int c = 0; c < NB; ++c) {
+      float sf[4] = {0.f, 0.f, 0.f, 0.f}, so[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        sf[i & 3] = fmaf(vr[i], Tl[c][i], sf[i & 3]);
+        so[i & 3] = fmaf(vr[i], Tl[i][c], so[i & 3]);
+      }
+      zf[c] = (sf[0] + sf[1]) + (sf[2] + sf[3]);
+      zo[c] = (so[0] + so[1]) + (so[2] + so[3]);
     }
   }
 }
@@ -259,8 +600,12 @@ QrWork carve_qr_work(Carver& c, int n) {
   w.dg = c.take<float>(2 * NB);
   w.gram = c.take<float>((size_t)G * NB * NB);
   w.T = c.take<float>(NB * NB);
-  w.counters = c.take<unsigned>(panels(n));
+  w.counters = c.take<unsigned>(2 * panels(n));
   w.err = c.take<int>(1);
+  w.fail = c.take<int>(panels(n));
+  w.part64 = c.take<double>((size_t)G * NU);
+  w.gram64 = c.take<double>(NU);
+  w.bcast = c.take<double>(NB * NB + NB);
   return w;
 }
 
@@ -273,7 +618,8 @@ size_t qr_work_bytes(int n) {
 mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout, int64_t ldQ,
                    QrWork& w, const int* pred, hipStream_t stream) {
   const int np = panels(n);
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, w.counters, np, w.err);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, w.counters, 2 * np, w.err);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, (unsigned*)w.fail, np, w.err);
   MAO_LAUNCH_CHECK();
 
   // offsets of the packed panels
@@ -308,6 +654,29 @@ mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Q
     a.counter = w.counters + p;
     a.err = w.err;
     a.pred = pred;
+    a.pred2 = w.fail + p;
+    CholArgs ca;
+    ca.S = S;
+    ca.ldS = ldS;
+    ca.n = n;
+    ca.j0 = j0;
+    ca.nb = nb;
+    ca.V = a.V;
+    ca.ldV = a.ldV;
+    ca.Zf = a.Zf;
+    ca.Zo = a.Zo;
+    ca.sign = w.sign;
+    ca.T = w.T;
+    ca.part = w.part64;
+    ca.gram = w.gram64;
+    ca.bcast = w.bcast;
+    ca.counter = w.counters + np + p;
+    ca.err = w.err;
+    ca.pred = pred;
+    ca.fail = w.fail + p;
+    void* cargs[] = {&ca};
+    MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_chol_kernel, dim3(G), dim3(TPB),
+                                             cargs, 0, stream));
     void* kargs[] = {&a};
     MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_kernel, dim3(G), dim3(TPB),
                                              kargs, 0, stream));

@@ -18,8 +18,12 @@ struct QrWork {
   float* dg;         // 2 x 64
   float* gram;       // Gmax x 4096
   float* T;          // 4096
-  unsigned* counters;// panels
+  unsigned* counters;// 2 x panels (per-column panel kernel, CholeskyQR panel kernel)
   int* err;          // barrier timeout flag
+  int* fail;         // panels: 1 when the CholeskyQR panel fell back
+  double* part64;    // Gmax x 2080 Gram partials
+  double* gram64;    // 2080
+  double* bcast;     // 64 x 64 + 64
 };
 
 size_t qr_work_bytes(int n);
