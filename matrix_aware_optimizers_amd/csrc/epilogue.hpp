@@ -1,0 +1,192 @@
+// Epilogue of a 256 x 256 fp32 accumulator tile (4 wavefronts in 2 x 2, each
+// 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32 results), shared by the
+// streamed bf16 kernel and the fp32 rank-k update kernel.
+//
+// D = alpha * acc + beta * C0, rows scaled by row_scale, written to D and/or
+// its transpose Dt (the SYRK mirror when D == Dt on a symmetric result).
+//
+// The tile goes through LDS in two halves of 128 rows, as four 32-row bands of
+// 256 floats (one 32 KB buffer each). Row pass: each thread finishes 8
+// consecutive columns of a row -- C0 read and D written in 16- (bf16) or
+// 32-byte (fp32) pieces, one whole row per 32 lanes -- and, when a transposed
+// copy is due, puts the finished values back. Column pass: 16 lanes cover 128
+// consecutive rows of one column and write them as one row of Dt. Columns
+// are XOR-permuted in groups of 8 by the row (bits 3-4 from row bits 3-4, bit
+// 5 from row bit 2 and the band), so accumulator writes are conflict-free and
+// column reads meet at most two-way. A diagonal SYRK tile writes D on and
+// below the diagonal and the mirror strictly above it. With CHECKED, rows
+// past M and columns past N are skipped (edge tiles).
+#pragma once
+
+#include "common.hpp"
+
+namespace mao {
+
+__device__ __forceinline__ float c0_load(const void* C0, bool f32, int64_t off) {
+  return f32 ? ((const float*)C0)[off] : bf16_to_f32(((const bf16_t*)C0)[off]);
+}
+
+__device__ __forceinline__ void d_store(void* D, bool f32, int64_t off, float v) {
+  if (f32)
+    ((float*)D)[off] = v;
+  else
+    ((bf16_t*)D)[off] = f32_to_bf16(v);
+}
+
+__device__ __forceinline__ int epi_swz(int rb, int band) {
+  return ((((rb) >> 3) & 3) << 3) | (((((rb) >> 2) ^ (band)) & 1) << 5);
+}
+
+__device__ __forceinline__ void store8_any(void* P, bool f32, int64_t off, const float* v) {
+  if (f32) {
+    float* dp = (float*)P + off;
+    *(float4*)dp = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(dp + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 pk;
+    pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+    pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    *(uint4*)((bf16_t*)P + off) = pk;
+  }
+}
+
+struct EpiArgs {
+  int m0, n0, M, N;
+  float alpha, beta;
+  const void* C0;
+  int64_t ldc0;
+  bool c32;
+  const float* rs;
+  void* D;
+  int64_t ldd;
+  bool d32;
+  void* Tt;
+  int64_t ldt;
+  bool diag;
+};
+
+template <bool CHECKED>
+__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], float* b0, float* b1,
+                                                float* b2, float* b3, const EpiArgs& e) {
+  constexpr int TB = 256;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+#define MAO_BAND(I, ST)                                                                   \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j)                                           \
+  _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                        \
+    const int rb_ = 8 * (v >> 2) + 4 * h + (v & 3);                                       \
+    const int col_ = (wn * 128 + j * 32 + r32) ^ epi_swz(rb_, I);                         \
+    (ST)[rb_ * TB + col_] = acc[I][j][v];                                                 \
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+      MAO_BAND(0, b0)
+      MAO_BAND(1, b1)
+      MAO_BAND(2, b2)
+      MAO_BAND(3, b3)
+    }
+    __syncthreads();
+    {
+      const int c8 = (threadIdx.x & 31) * 8;
+      const int64_t gcol = e.n0 + c8;
+      const bool cfull = !CHECKED || gcol + 8 <= e.N;
+      // four rows at a time: their C0 pieces are all requested before any is
+      // used, so the memory latency is paid once per group, not per row
+      for (int it0 = 0; it0 < 16; it0 += 4) {
+        float cv[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t grow = e.m0 + half * 128 + (it0 + u) * 8 + (threadIdx.x >> 5);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) cv[u][q] = 0.f;
+          if (!e.C0 || (CHECKED && (grow >= e.M || gcol >= e.N))) continue;
+          const int64_t off = grow * e.ldc0 + gcol;
+          if (cfull && e.c32) {
+            const float* cp = (const float*)e.C0 + off;
+            const float4 y0 = *(const float4*)cp, y1 = *(const float4*)(cp + 4);
+            cv[u][0] = y0.x; cv[u][1] = y0.y; cv[u][2] = y0.z; cv[u][3] = y0.w;
+            cv[u][4] = y1.x; cv[u][5] = y1.y; cv[u][6] = y1.z; cv[u][7] = y1.w;
+          } else if (cfull) {
+            const uint4 y = *(const uint4*)((const bf16_t*)e.C0 + off);
+            const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              cv[u][2 * q] = bf16_to_f32((bf16_t)(w[q] & 0xffff));
+              cv[u][2 * q + 1] = bf16_to_f32((bf16_t)(w[q] >> 16));
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (gcol + q < e.N) cv[u][q] = c0_load(e.C0, e.c32, off + q);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = (it0 + u) * 8 + (threadIdx.x >> 5);
+          const int band = row >> 5, rb = row & 31;
+          float* bp = band == 0 ? b0 : band == 1 ? b1 : band == 2 ? b2 : b3;
+          float* src = bp + rb * TB + (c8 ^ epi_swz(rb, band));
+          const int64_t grow = e.m0 + half * 128 + row;
+          if (CHECKED && (grow >= e.M || gcol >= e.N)) continue;
+          const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+          float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = e.alpha * v[q] + (e.C0 ? e.beta * cv[u][q] : 0.f);
+          if (e.rs) {
+            const float sc = e.rs[grow];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= sc;
+          }
+          if (e.D) {
+            const int64_t off = grow * e.ldd + gcol;
+            if (cfull && (!e.diag || grow >= gcol + 7)) {
+              store8_any(e.D, e.d32, off, v);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 8; ++q)
+                if ((!CHECKED || gcol + q < e.N) && (!e.diag || grow >= gcol + q))
+                  d_store(e.D, e.d32, off + q, v[q]);
+            }
+          }
+          if (e.Tt) {
+            *(float4*)src = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          }
+        }
+      }
+    }
+    if (e.Tt) {
+      __syncthreads();
+      const int rgrp = threadIdx.x & 15;
+      const int band = rgrp >> 2, rb0 = (rgrp & 3) * 8;
+      const float* bp = band == 0 ? b0 : band == 1 ? b1 : band == 2 ? b2 : b3;
+      const int64_t grow = e.m0 + half * 128 + rgrp * 8;
+      const bool rfull = !CHECKED || grow + 8 <= e.M;
+      for (int it = 0; it < 16; ++it) {
+        const int c = it * 16 + (threadIdx.x >> 4);
+        const int64_t gc = e.n0 + c;
+        if (CHECKED && (gc >= e.N || grow >= e.M)) continue;
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = bp[(rb0 + q) * TB + (c ^ epi_swz(rb0 + q, band))];
+        const int64_t off = gc * e.ldt + grow;
+        if (rfull && (!e.diag || grow > gc)) {
+          store8_any(e.Tt, e.d32, off, v);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if ((!CHECKED || grow + q < e.M) && (!e.diag || grow + q > gc))
+              d_store(e.Tt, e.d32, off + q, v[q]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#undef MAO_BAND
+}
+
+}  // namespace mao

@@ -365,7 +365,12 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
       return MAO_E_UNSUPPORTED;
     }
   }
-  const int bm = (in_dtype == MAO_BF16 && (nkm != 0 || count_tiles(probs, nprob, 256) >= 128)) ? 256
+  // fp32 rank-k updates (k <= 64, the QR updates) stream their result once:
+  // the 256 x 256 rank kernel moves it in whole rows.
+  bool rank = in_dtype == MAO_F32 && nkm == 0;
+  for (int i = 0; i < nprob; ++i) rank = rank && probs[i].K <= 64 && !(probs[i].flags & GF_SYRK);
+  rank = rank && count_tiles(probs, nprob, 256) >= 16;
+  const int bm = (rank || (in_dtype == MAO_BF16 && (nkm != 0 || count_tiles(probs, nprob, 256) >= 128))) ? 256
                  : count_tiles(probs, nprob, 128) >= 512 ? 128 : 64;
   // Longest K first: the last tiles to start are the short ones.
   int order[kMaxProblems];
@@ -391,7 +396,9 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
   const bool timed = timing_on();
   if (timed) timing_record_begin(stream, &ev);
   mao_status st;
-  if (in_dtype == MAO_BF16)
+  if (rank)
+    st = launch_gemm_f32_rank(args, stream);
+  else if (in_dtype == MAO_BF16)
     st = bm == 256 ? launch_gemm_bf16_direct(args, stream)
          : bm == 128 ? launch_cfg<bf16_t, 128, 128>(args, stream) : launch_cfg<bf16_t, 64, 64>(args, stream);
   else

@@ -79,6 +79,9 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
 // four-stage LDS ring (gemm_bf16.hip). Same semantics as gemm_nt_kernel.
 mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream);
 
+// fp32 rank-k updates, k <= 64, 256 x 256 tiles (gemm_f32_rank.hip).
+mao_status launch_gemm_f32_rank(GemmArgs& args, hipStream_t stream);
+
 // Instrumentation: when enabled, every contraction launch is bracketed by HIP
 // events on its stream, with its algorithmic flop count (symmetric products
 // at half cost). Off by default.

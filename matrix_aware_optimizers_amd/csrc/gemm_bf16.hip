@@ -28,6 +28,7 @@
 // written as whole rows in 16- or 32-byte pieces (C0 blend and row scale on
 // the way). Edge tiles, a transposed copy Dt, and the SYRK mirror use 32-row
 // bands through LDS with the transposed copy written from LDS columns.
+#include "epilogue.hpp"
 #include "gemm.hpp"
 
 namespace mao {
@@ -61,16 +62,7 @@ template <int N>
 __device__ __forceinline__ void vm_wait_c() { __builtin_amdgcn_s_waitcnt(MAO_VMCNT(N)); }
 #define vm_wait(n) vm_wait_c<(n)>()
 
-__device__ __forceinline__ float c0_load(const void* C0, bool f32, int64_t off) {
-  return f32 ? ((const float*)C0)[off] : bf16_to_f32(((const bf16_t*)C0)[off]);
-}
 
-__device__ __forceinline__ void d_store(void* D, bool f32, int64_t off, float v) {
-  if (f32)
-    ((float*)D)[off] = v;
-  else
-    ((bf16_t*)D)[off] = f32_to_bf16(v);
-}
 
 template <bool BKM>
 __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
@@ -341,130 +333,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   const float alpha = P.alpha, beta = P.beta;
   const float* rs = P.row_scale;
   if (m0 + TB <= M && n0 + TB <= N) {
-    // Interior tiles: the fp32 tile goes through LDS in two halves of 128 rows
-    // (four 32-row bands, one per stage buffer). Row pass: each thread
-    // finishes 8 consecutive columns of a row -- C0 read and D written in 16-
-    // (bf16) or 32-byte (fp32) pieces, one whole row per 32 lanes -- and, when
-    // a transposed copy is due, puts the finished values back. Column pass:
-    // 16 lanes cover 128 consecutive rows of one column and write them as one
-    // row of Dt (or of the SYRK mirror). Columns are XOR-permuted in groups of
-    // 8 by the row (bits 3-4 from row bits 3-4, bit 5 from row bit 2 and the
-    // band), so accumulator writes are conflict-free and column reads meet at
-    // most two-way. A diagonal SYRK tile writes D on and below the diagonal
-    // and the mirror strictly above it.
-#define MAO_SWZ(RB, BAND) (((((RB) >> 3) & 3) << 3) | (((((RB) >> 2) ^ (BAND)) & 1) << 5))
-#define MAO_BAND(I, ST)                                                                   \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                         \
-    _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                      \
-      const int rb_ = 8 * (v >> 2) + 4 * h + (v & 3);                                     \
-      const int col_ = (wn * 128 + j * 32 + r32) ^ MAO_SWZ(rb_, I);                       \
-      ((float*)ST)[rb_ * TB + col_] = acc[I][j][v];                                       \
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (wm == half) {
-        MAO_BAND(0, st0)
-        MAO_BAND(1, st1)
-        MAO_BAND(2, st2)
-        MAO_BAND(3, st3)
-      }
-      __syncthreads();
-      {
-        const int c8 = (threadIdx.x & 31) * 8;
-        const int64_t gcol = n0 + c8;
-        for (int it = 0; it < 16; ++it) {
-          const int row = it * 8 + (threadIdx.x >> 5);
-          const int band = row >> 5, rb = row & 31;
-          unsigned char* bp = band == 0 ? st0 : band == 1 ? st1 : band == 2 ? st2 : st3;
-          float* src = (float*)bp + rb * TB + (c8 ^ MAO_SWZ(rb, band));
-          const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
-          float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= alpha;
-          const int64_t grow = m0 + half * 128 + row;
-          if (C0) {
-            if (c32) {
-              const float* cp = (const float*)C0 + grow * P.ldc0 + gcol;
-              const float4 y0 = *(const float4*)cp, y1 = *(const float4*)(cp + 4);
-              v[0] += beta * y0.x; v[1] += beta * y0.y; v[2] += beta * y0.z; v[3] += beta * y0.w;
-              v[4] += beta * y1.x; v[5] += beta * y1.y; v[6] += beta * y1.z; v[7] += beta * y1.w;
-            } else {
-              const uint4 y = *(const uint4*)((const bf16_t*)C0 + grow * P.ldc0 + gcol);
-              const uint32_t w[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                v[2 * e] += beta * bf16_to_f32((bf16_t)(w[e] & 0xffff));
-                v[2 * e + 1] += beta * bf16_to_f32((bf16_t)(w[e] >> 16));
-              }
-            }
-          }
-          if (rs) {
-            const float sc = rs[grow];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] *= sc;
-          }
-          if (D) {
-            if (!diag || grow >= gcol + 7) {
-              if (d32) {
-                float* dp = (float*)D + grow * P.ldd + gcol;
-                *(float4*)dp = make_float4(v[0], v[1], v[2], v[3]);
-                *(float4*)(dp + 4) = make_float4(v[4], v[5], v[6], v[7]);
-              } else {
-                uint4 pk;
-                pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-                pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-                *(uint4*)((bf16_t*)D + grow * P.ldd + gcol) = pk;
-              }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (grow >= gcol + e) d_store(D, d32, grow * P.ldd + gcol + e, v[e]);
-            }
-          }
-          if (Tt) {
-            *(float4*)src = make_float4(v[0], v[1], v[2], v[3]);
-            *(float4*)(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
-          }
-        }
-      }
-      if (Tt) {
-        __syncthreads();
-        const int rgrp = threadIdx.x & 15;
-        const int band = rgrp >> 2, rb0 = (rgrp & 3) * 8;
-        const unsigned char* bp = band == 0 ? st0 : band == 1 ? st1 : band == 2 ? st2 : st3;
-        const int64_t grow = m0 + half * 128 + rgrp * 8;
-        for (int it = 0; it < 16; ++it) {
-          const int c = it * 16 + (threadIdx.x >> 4);
-          const int64_t gc = n0 + c;
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = ((const float*)bp)[(rb0 + e) * TB + (c ^ MAO_SWZ(rb0 + e, band))];
-          const int64_t off = gc * ldt + grow;
-          if (!diag || grow > gc) {
-            if (d32) {
-              *(float4*)((float*)Tt + off) = make_float4(v[0], v[1], v[2], v[3]);
-              *(float4*)((float*)Tt + off + 4) = make_float4(v[4], v[5], v[6], v[7]);
-            } else {
-              uint4 pk;
-              pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-              pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-              pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-              pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-              *(uint4*)((bf16_t*)Tt + off) = pk;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (grow + e > gc) d_store(Tt, d32, off + e, v[e]);
-          }
-        }
-      }
-      __syncthreads();
-    }
-#undef MAO_BAND
-#undef MAO_SWZ
+    EpiArgs ea;
+    ea.m0 = m0; ea.n0 = n0; ea.M = M; ea.N = N;
+    ea.alpha = alpha; ea.beta = beta;
+    ea.C0 = C0; ea.ldc0 = P.ldc0; ea.c32 = c32;
+    ea.rs = rs;
+    ea.D = D; ea.ldd = P.ldd; ea.d32 = d32;
+    ea.Tt = Tt; ea.ldt = ldt;
+    ea.diag = diag;
+    staged_epilogue<false>(acc, (float*)st0, (float*)st1, (float*)st2, (float*)st3, ea);
     return;
   }
   float* slab = (float*)st0;

@@ -14,7 +14,9 @@ pytestmark = pytest.mark.gpu
 GEMM_SHAPES = [(1, 1, 1), (64, 64, 64), (130, 77, 203), (300, 257, 500), (513, 129, 64),
                (1024, 1000, 1536),
                # large enough for the 256 x 256 streamed bf16 kernel, ragged in M, N, K
-               (4100, 2052, 1060), (2304, 4352, 8)]
+               (4100, 2052, 1060), (2304, 4352, 8),
+               # rank-k updates (k <= 64) on the fp32 256 x 256 rank kernel
+               (1500, 1300, 64), (4100, 2052, 40), (1030, 1030, 1)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -80,7 +82,7 @@ def test_syrk_is_exactly_symmetric(gpu_lib, dtype, n, k):
     assert rel(d, ref) < 1e-5
 
 
-@pytest.mark.parametrize("n", [1, 5, 64, 65, 130, 300, 700])
+@pytest.mark.parametrize("n", [1, 5, 64, 65, 130, 300, 700, 1100])
 def test_qr_matches_oracle(gpu_lib, n):
     import torch
     log(f"qr n={n}")
