@@ -565,6 +565,50 @@ __global__ void zero_u32_kernel(unsigned* p, int n, int* err) {
   if (threadIdx.x == 0) *err = 0;
 }
 
+// Skinny products W = A B^T (M x nb, K long -- the V^T projections of the
+// trailing matrix and of E) have too few output tiles to occupy the chip, so
+// K is cut into up to KSPLIT chunks (one grouped launch, partial products into
+// `parts`) and the partials are summed in a fixed order.
+constexpr int KSPLIT = 4;
+
+__global__ __launch_bounds__(256) void sum_parts_kernel(float* out, const float* parts,
+                                                        int64_t part_stride, int nparts,
+                                                        int64_t count, const int* pred) {
+  if (pred != nullptr && *pred == 0) return;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * 256) {
+    float s = parts[i];
+    for (int q = 1; q < nparts; ++q) s += parts[q * part_stride + i];
+    out[i] = s;
+  }
+}
+
+mao_status skinny_product(int M, int nb, int K, const float* A, int64_t lda, const float* B,
+                          int64_t ldb, float* W, float* parts, const int* pred, hipStream_t stream) {
+  const int chunk = (int)round_up((K + KSPLIT - 1) / KSPLIT, 64);
+  const int nparts = (K + chunk - 1) / chunk;
+  if (nparts <= 1 || M < 1024) {
+    GemmProblem p1 = gemm_problem(M, nb, K, 1.f, A, lda, B, ldb, 0.f, nullptr, 0, W, NB, GF_D_F32);
+    p1.pred = pred;
+    return launch_gemm(MAO_F32, &p1, 1, stream, TAG_QR);
+  }
+  GemmProblem pr[KSPLIT];
+  const int64_t stride = (int64_t)M * NB;
+  for (int q = 0; q < nparts; ++q) {
+    const int k0 = q * chunk, kc = std::min(chunk, K - k0);
+    pr[q] = gemm_problem(M, nb, kc, 1.f, A + k0, lda, B + k0, ldb, 0.f, nullptr, 0,
+                         parts + q * stride, NB, GF_D_F32);
+    pr[q].pred = pred;
+  }
+  MAO_TRY(launch_gemm(MAO_F32, pr, nparts, stream, TAG_QR));
+  const int64_t count = (int64_t)M * NB;
+  const int blocks = (int)std::min<int64_t>(1024, (count + 255) / 256);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks), dim3(256), 0, stream, W, parts, stride,
+                     nparts, count, pred);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
 int panels(int n) { return (n + NB - 1) / NB; }
 int max_groups(int n) { return (n + TPB - 1) / TPB; }
 
@@ -595,6 +639,7 @@ QrWork carve_qr_work(Carver& c, int n) {
   w.zo = c.take<float>(zo_floats(n));
   w.zf = c.take<float>((size_t)n * NB);
   w.wbuf = c.take<float>((size_t)n * NB);
+  w.wparts = c.take<float>((size_t)KSPLIT * n * NB);
   w.sign = c.take<float>(n);
   w.part = c.take<float>((size_t)2 * G * NB);
   w.dg = c.take<float>(2 * NB);
@@ -684,10 +729,7 @@ mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Q
     if (mt > 0) {
       float* Strail = S + (int64_t)(j0 + nb) * ldS + j0;
       // W = S_trail V^T   (mt x nb)
-      GemmProblem p1 = gemm_problem(mt, nb, len, 1.f, Strail, ldS, a.V, a.ldV, 0.f, nullptr, 0,
-                                    w.wbuf, NB, GF_D_F32);
-      p1.pred = pred;
-      MAO_TRY(launch_gemm(MAO_F32, &p1, 1, stream, TAG_QR));
+      MAO_TRY(skinny_product(mt, nb, len, Strail, ldS, a.V, a.ldV, w.wbuf, w.wparts, pred, stream));
       // S_trail -= W Zf^T  (mt x len)
       GemmProblem p2 = gemm_problem(mt, len, nb, -1.f, w.wbuf, NB, w.zf, NB, 1.f, Strail, ldS,
                                     Strail, ldS, GF_D_F32 | GF_C0_F32);
@@ -701,10 +743,8 @@ mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Q
   for (int p = np - 1; p >= 0; --p) {
     const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
     float* Esub = E + (int64_t)j0 * ldE + j0;
-    GemmProblem p1 = gemm_problem(len, nb, len, 1.f, Esub, ldE, w.vstore + vo[p], round_up(len, 8),
-                                  0.f, nullptr, 0, w.wbuf, NB, GF_D_F32);
-    p1.pred = pred;
-    MAO_TRY(launch_gemm(MAO_F32, &p1, 1, stream, TAG_QR));
+    MAO_TRY(skinny_product(len, nb, len, Esub, ldE, w.vstore + vo[p], round_up(len, 8), w.wbuf,
+                           w.wparts, pred, stream));
     GemmProblem p2 = gemm_problem(len, len, nb, -1.f, w.wbuf, NB, w.zo + zo[p], NB, 1.f, Esub, ldE,
                                   Esub, ldE, GF_D_F32 | GF_C0_F32);
     p2.pred = pred;

@@ -13,6 +13,7 @@ struct QrWork {
   float* zo;         // packed V T panels (orgqr)
   float* zf;         // one V T^T panel (n x 64)
   float* wbuf;       // n x 64 intermediate
+  float* wparts;     // 4 x n x 64 split-K partials of it
   float* sign;       // n
   float* part;       // 2 x Gmax x 64
   float* dg;         // 2 x 64
