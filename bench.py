@@ -336,7 +336,9 @@ class SoapLikeWorkload:
             self.hp = mao.foam_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
                                        pf=pf, tol=tol)
         need = 0
-        for sp in specs:
+        for idx, sp in enumerate(specs):
+            if idx % 16 == 15:
+                log(f"  {idx + 1}/{len(specs)} matrices set up")
             m, n = sp.rows, sp.cols
             W = _padded_empty(torch, m, n, tw)
             W.copy_(torch.from_numpy(synth.init_weight(config, sp)))
