@@ -50,7 +50,8 @@ def log(msg: str):
 # was taken on and is reported only while they are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_contraction_llama8b_layer_traffic.json")
 GEMM_SOURCES = [os.path.join(ROOT, "matrix_aware_optimizers_amd", "csrc", f)
-                for f in ("gemm_bf16.hip", "gemm.hip", "gemm.hpp", "epilogue.hpp", "common.hpp")]
+                for f in ("gemm_bf16.hip", "gemm.hip", "gemm.hpp", "epilogue.hpp", "tiled.hpp",
+                          "common.hpp")]
 NS_KERNEL = "gemm_bf16_dl_kernel"
 COPY_KERNEL = "copyBuffer"
 

@@ -10,6 +10,7 @@
 #include "common.hpp"
 #include "elementwise.hpp"
 #include "gemm.hpp"
+#include "tiled.hpp"
 #include "qr.hpp"
 
 namespace mao {
@@ -78,6 +79,8 @@ mao_status check_beta(const char* name, float b) {
 struct MuonGroupBufs {
   int rows, cols, a, b, count;
   bool wide;  // rows <= cols
+  bool t32;   // X, A, Bm tiled (tiled.hpp) between iterations
+  int64_t ap, bp;  // a, b padded to whole 256 x 256 tiles (tiled storage)
   int64_t ldx, ldxt, lda;
   void* X[2];
   void* Xt[2];
@@ -89,9 +92,21 @@ struct MuonGroupBufs {
   float *ss_r, *ss_c, *rs, *cs, *sq;
 };
 
+// The bf16 Newton-Schulz products keep X, A and Bm tiled (tiled.hpp) when
+// they run on the 256 x 256 kernel anyway: at least one iteration and 128 or
+// more 256 x 256 tiles in the product B X over all groups.
+bool muon_tiled(int ng, const int64_t* rows, const int64_t* cols, const int64_t* count,
+                const mao_muon_hparams* hp) {
+  if (hp->ns_dtype != MAO_BF16 || hp->ns_steps < 1) return false;
+  int64_t tiles = 0;
+  for (int g = 0; g < ng; ++g) tiles += count[g] * ceil_div(rows[g], 256) * ceil_div(cols[g], 256);
+  return tiles >= 128;
+}
+
 void carve_muon(Carver& c, int ng, const int64_t* rows, const int64_t* cols, const int64_t* count,
                 const mao_muon_hparams* hp, MuonGroupBufs* out) {
   const size_t es = dtype_size(hp->ns_dtype);
+  const bool t32 = muon_tiled(ng, rows, cols, count, hp);
   for (int g = 0; g < ng; ++g) {
     MuonGroupBufs& B = out[g];
     B.rows = (int)rows[g];
@@ -103,12 +118,19 @@ void carve_muon(Carver& c, int ng, const int64_t* rows, const int64_t* cols, con
     B.ldx = ws_ld(B.b);
     B.ldxt = ws_ld(B.a);
     B.lda = ws_ld(B.a);
+    B.t32 = t32;
+    B.ap = t32_pad(B.a);
+    B.bp = t32_pad(B.b);
+    // X[k] holds the tiled iterate, and the row-major result after the last
+    // iteration: room for either
+    const size_t xsz = t32 ? std::max(B.a * B.ldx, B.ap * B.bp) : B.a * B.ldx;
+    const size_t asz = t32 ? B.ap * B.ap : B.a * B.lda;
     for (int k = 0; k < 2; ++k) {
-      B.X[k] = c.take<char>((size_t)B.count * B.a * B.ldx * es);
+      B.X[k] = c.take<char>((size_t)B.count * xsz * es);
       B.Xt[k] = c.take<char>((size_t)B.count * B.b * B.ldxt * es);
     }
-    B.A = c.take<char>((size_t)B.count * B.a * B.lda * es);
-    B.Bm = c.take<char>((size_t)B.count * B.a * B.lda * es);
+    B.A = c.take<char>((size_t)B.count * asz * es);
+    B.Bm = c.take<char>((size_t)B.count * asz * es);
     B.nrb = rowblocks_for(B.rows, B.count);
     B.partial = c.take<float>((size_t)B.count * B.nrb);
     B.scale = c.take<float>(B.count);
@@ -223,6 +245,11 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
     MAO_TRY(ema_sumsq(view(M[g].data, M[g].ld, mstride), view(G[g].data, G[g].ld, gstride),
                       G[g].dtype, B.rows, B.cols, B.count, hp->mu, B.partial, B.nrb, s));
     MAO_TRY(finalize_inv_norm(B.partial, B.nrb, B.count, hp->eps, B.scale, s));
+    if (B.t32) {
+      MAO_TRY(scale_cast_tiled(view(M[g].data, M[g].ld, mstride), B.rows, B.cols, B.count, B.scale,
+                               !B.wide, B.X[0], B.ap, B.bp, B.ap * B.bp, s));
+      continue;
+    }
     View xa = view(B.X[0], B.ldx, (int64_t)B.a * B.ldx);
     View xb = (!kmajor || (hp->ns_steps == 0 && need_t(B))) ? view(B.Xt[0], B.ldxt, (int64_t)B.b * B.ldxt)
                                                              : view(nullptr, 0, 0);
@@ -237,6 +264,50 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
     const float cc = hp->ns_coeffs ? hp->ns_coeffs[3 * k + 2] : 3.f / 8.f;
     const int cur = k & 1, nxt = cur ^ 1;
     GemmProblem p[MAO_MAX_GROUPS];
+    const bool last = k + 1 == hp->ns_steps;
+    if (bufs[0].t32) {
+      // tiled: a I joins the square step, Bm = a I + b A + c A A, so the
+      // product X' = Bm X reads no C0; the last one writes X row-major (and
+      // X^T where it is read)
+      for (int g = 0; g < ng; ++g) {
+        MuonGroupBufs& B = bufs[g];
+        const int64_t sx = B.ap * B.bp, sa = B.ap * B.ap;
+        p[g] = gemm_problem(B.a, B.a, B.b, 1.f, B.X[cur], B.bp, B.X[cur], B.bp, 0.f, nullptr, 0,
+                            B.A, B.ap, GF_SYRK | GF_T32 | GF_D_T32);
+        p[g].batch = B.count;
+        p[g].sA = p[g].sB = sx;
+        p[g].sD = sa;
+      }
+      MAO_TRY(launch_gemm(xdt, p, ng, s, TAG_NS_GRAM));
+      for (int g = 0; g < ng; ++g) {
+        MuonGroupBufs& B = bufs[g];
+        const int64_t sa = B.ap * B.ap;
+        p[g] = gemm_problem(B.a, B.a, B.a, cc, B.A, B.ap, B.A, B.ap, cb, B.A, B.ap, B.Bm, B.ap,
+                            GF_SYRK | GF_T32 | GF_D_T32 | GF_C0_T32);
+        p[g].dadd = ca;
+        p[g].batch = B.count;
+        p[g].sA = p[g].sB = p[g].sC0 = p[g].sD = sa;
+      }
+      MAO_TRY(launch_gemm(xdt, p, ng, s, TAG_NS_SQUARE));
+      for (int g = 0; g < ng; ++g) {
+        MuonGroupBufs& B = bufs[g];
+        const int64_t sx = B.ap * B.bp;
+        p[g] = gemm_problem(B.a, B.b, B.a, 1.f, B.Bm, B.ap, B.X[cur], B.bp, 0.f, nullptr, 0,
+                            B.X[nxt], last ? B.ldx : B.bp,
+                            GF_T32 | GF_B_KMAJOR | (last ? 0 : GF_D_T32));
+        if (last && need_t(B)) {
+          p[g].Dt = B.Xt[nxt];
+          p[g].lddt = B.ldxt;
+          p[g].sDt = (int64_t)B.b * B.ldxt;
+        }
+        p[g].batch = B.count;
+        p[g].sA = B.ap * B.ap;
+        p[g].sB = sx;
+        p[g].sD = last ? (int64_t)B.a * B.ldx : sx;
+      }
+      MAO_TRY(launch_gemm(xdt, p, ng, s, TAG_NS_APPLY));
+      continue;
+    }
     for (int g = 0; g < ng; ++g) {
       MuonGroupBufs& B = bufs[g];
       p[g] = gemm_problem(B.a, B.a, B.b, 1.f, B.X[cur], B.ldx, B.X[cur], B.ldx, 0.f, nullptr, 0,
@@ -262,7 +333,6 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
       else
         p[g] = gemm_problem(B.a, B.b, B.a, 1.f, B.Bm, B.lda, B.Xt[cur], B.ldxt, ca, B.X[cur], B.ldx,
                             B.X[nxt], B.ldx, xflags);
-      const bool last = k + 1 == hp->ns_steps;
       if (!kmajor || (last && need_t(B))) {
         p[g].Dt = B.Xt[nxt];
         p[g].lddt = B.ldxt;

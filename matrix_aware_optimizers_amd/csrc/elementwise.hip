@@ -8,6 +8,7 @@
 // Reductions write one partial per block and a second pass sums the
 // partials in a fixed order: no atomics, bitwise-repeatable results.
 #include "elementwise.hpp"
+#include "tiled.hpp"
 
 #include <algorithm>
 
@@ -243,6 +244,55 @@ __global__ __launch_bounds__(kBlock) void scale_cast_kernel(View In, int rows, i
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] *= sc;
     store8<TO>(out + (int64_t)i * Out.ld, j, cols, v);
+  }
+}
+
+// X0 = scale * M (or its transpose) cast to bf16 in the tiled layout
+// (tiled.hpp), pad zero: a 64 x 64 region of X per block through LDS, then
+// written as whole 1 KB half-blocks (thread q of a 128-chunk block writes its
+// q-th 16-byte chunk, so consecutive lanes write consecutive addresses).
+__global__ __launch_bounds__(kBlock) void x0_tiled_kernel(View In, int rows, int cols,
+                                                          const float* scale, bool trans,
+                                                          bf16_t* X, int64_t xcp, int64_t xstride) {
+  __shared__ float tile[64][65];
+  const int b = blockIdx.z;
+  const int i0 = blockIdx.y * 64, k0 = blockIdx.x * 64;  // region of X
+  const int sr0 = trans ? k0 : i0, sc0 = trans ? i0 : k0;  // region of M
+  const float s = scale ? scale[b] : 1.f;
+  const float* in = (const float*)In.p + (int64_t)b * In.stride;
+  const int t = threadIdx.x;
+  const int cc = (t & 15) * 4;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = (t >> 4) + 16 * p;
+    const int i = sr0 + r, j = sc0 + cc;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (i < rows && j < cols) {
+      load4<float>(in + (int64_t)i * In.ld, j, cols, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= s;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[r][cc + e] = v[e];
+  }
+  __syncthreads();
+  bf16_t* xb = X + (int64_t)b * xstride;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = t + p * kBlock;            // chunk of the region, 0..511
+    const int blk = q >> 7, r = (q >> 2) & 31, pc = q & 3;
+    const int lc = pc ^ t32_swz(r);          // logical chunk stored at pc
+    const int ri = (blk >> 1) * 32 + r;      // row of X in the region
+    const int ck = (blk & 1) * 32 + lc * 8;  // first column of X in the region
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = trans ? tile[ck + e][ri] : tile[ri][ck + e];
+    uint4 pk;
+    pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+    pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    *(uint4*)(xb + t32_off(i0 + ri, k0 + ck, xcp)) = pk;
   }
 }
 
@@ -560,6 +610,21 @@ mao_status scale_cast_transpose(View M, int rows, int cols, int batch, const flo
     hipLaunchKernelGGL((transpose_kernel<float, bf16_t>), grid, dim3(kBlock), 0, s, M, rows, cols, scale, direct, trans);
   else
     hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(kBlock), 0, s, M, rows, cols, scale, direct, trans);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status scale_cast_tiled(View M, int rows, int cols, int batch, const float* scale, bool trans,
+                            void* X, int64_t xrp, int64_t xcp, int64_t xstride, hipStream_t s) {
+  const int64_t a = trans ? cols : rows, bb = trans ? rows : cols;
+  if (xrp % 64 || xcp % 256 || xrp < a || xcp < bb) {
+    set_error("scale_cast_tiled: padded %lld x %lld does not hold %lld x %lld", (long long)xrp,
+              (long long)xcp, (long long)a, (long long)bb);
+    return MAO_E_LAYOUT;
+  }
+  dim3 grid((unsigned)(xcp / 64), (unsigned)(xrp / 64), batch);
+  hipLaunchKernelGGL(x0_tiled_kernel, grid, dim3(kBlock), 0, s, M, rows, cols, scale, trans,
+                     (bf16_t*)X, xcp, xstride);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }

@@ -34,6 +34,12 @@ mao_status finalize_inv_norm(const float* partial, int nrb, int batch, float eps
 mao_status scale_cast_transpose(View M, int rows, int cols, int batch, const float* scale,
                                 View direct, View trans, int x_dtype, hipStream_t s);
 
+// X0 = scale[b] * M (trans: its transpose), bf16, written tiled (tiled.hpp)
+// into X of padded size xrp x xcp (xrp a multiple of 64, xcp of 256) with
+// the pad zeroed; batch b at X + b * xstride.
+mao_status scale_cast_tiled(View M, int rows, int cols, int batch, const float* scale, bool trans,
+                            void* X, int64_t xrp, int64_t xcp, int64_t xstride, hipStream_t s);
+
 // fp32 copies of a bf16 or fp32 matrix: direct[i][j] = in[i][j] and
 // trans[j][i] = in[i][j] (either may be nullptr).
 mao_status cast_transpose_f32(View in, int in_dtype, int rows, int cols, View direct, View trans,

@@ -15,10 +15,14 @@
 // 5 from row bit 2 and the band), so accumulator writes are conflict-free and
 // column reads meet at most two-way. A diagonal SYRK tile writes D on and
 // below the diagonal and the mirror strictly above it. With CHECKED, rows
-// past M and columns past N are skipped (edge tiles).
+// past M and columns past N are skipped (edge tiles). C0, D and Dt may each be
+// tiled (tiled.hpp); a run of 8 columns starting at a multiple of 8 is one
+// contiguous chunk in either layout. A diagonal term dadd is added to D[i][i]
+// for i < M (never to the zero pad of a tiled D).
 #pragma once
 
 #include "common.hpp"
+#include "tiled.hpp"
 
 namespace mao {
 
@@ -65,6 +69,9 @@ struct EpiArgs {
   void* Tt;
   int64_t ldt;
   bool diag;
+  // tiled storage (tiled.hpp): the ld fields are then padded widths
+  bool c_t32 = false, d_t32 = false, t_t32 = false;
+  float dadd = 0.f;  // added to D[i][i], i < M
 };
 
 template <bool CHECKED>
@@ -104,7 +111,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], flo
 #pragma unroll
           for (int q = 0; q < 8; ++q) cv[u][q] = 0.f;
           if (!e.C0 || (CHECKED && (grow >= e.M || gcol >= e.N))) continue;
-          const int64_t off = grow * e.ldc0 + gcol;
+          const int64_t off = e.c_t32 ? t32_off(grow, gcol, e.ldc0) : grow * e.ldc0 + gcol;
           if (cfull && e.c32) {
             const float* cp = (const float*)e.C0 + off;
             const float4 y0 = *(const float4*)cp, y1 = *(const float4*)(cp + 4);
@@ -136,13 +143,18 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], flo
           float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[q] = e.alpha * v[q] + (e.C0 ? e.beta * cv[u][q] : 0.f);
+          if (e.dadd != 0.f && grow < e.M) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (grow == gcol + q) v[q] += e.dadd;
+          }
           if (e.rs) {
             const float sc = e.rs[grow];
 #pragma unroll
             for (int q = 0; q < 8; ++q) v[q] *= sc;
           }
           if (e.D) {
-            const int64_t off = grow * e.ldd + gcol;
+            const int64_t off = e.d_t32 ? t32_off(grow, gcol, e.ldd) : grow * e.ldd + gcol;
             if (cfull && (!e.diag || grow >= gcol + 7)) {
               store8_any(e.D, e.d32, off, v);
             } else {
@@ -173,7 +185,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], flo
         float v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] = bp[(rb0 + q) * TB + (c ^ epi_swz(rb0 + q, band))];
-        const int64_t off = gc * e.ldt + grow;
+        const int64_t off = e.t_t32 ? t32_off(gc, grow, e.ldt) : gc * e.ldt + grow;
         if (rfull && (!e.diag || grow > gc)) {
           store8_any(e.Tt, e.d32, off, v);
         } else {

@@ -365,12 +365,35 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
       return MAO_E_UNSUPPORTED;
     }
   }
+  // Tiled operands are read only by the 256 x 256 bf16 kernel, all problems
+  // of the launch alike; a tiled D there is written pad included, so it takes
+  // no row scale and no separate transposed copy.
+  int nt = 0, ntio = 0;
+  for (int i = 0; i < nprob; ++i) {
+    nt += (probs[i].flags & GF_T32) ? 1 : 0;
+    ntio += ((probs[i].flags & (GF_D_T32 | GF_C0_T32)) || probs[i].dadd != 0.f) ? 1 : 0;
+  }
+  if (nt != 0 || ntio != 0) {
+    bool ok = nt == nprob && in_dtype == MAO_BF16;
+    for (int i = 0; i < nprob; ++i) {
+      const GemmProblem& p = probs[i];
+      ok = ok && !p.row_scale && !((p.flags & GF_D_T32) && p.Dt && !(p.flags & GF_SYRK));
+      ok = ok && p.lda % 256 == 0 && p.ldb % 256 == 0;
+      ok = ok && (!(p.flags & GF_D_T32) || p.ldd % 256 == 0) && (!(p.flags & GF_C0_T32) || p.ldc0 % 256 == 0);
+    }
+    if (!ok) {
+      set_error("launch_gemm: tiled operands (and a diagonal term) need bf16 inputs, the same "
+                "layout for every problem, padded widths that are multiples of 256, and no row "
+                "scale or separate Dt with a tiled D");
+      return MAO_E_UNSUPPORTED;
+    }
+  }
   // fp32 rank-k updates (k <= 64, the QR updates) stream their result once:
   // the 256 x 256 rank kernel moves it in whole rows.
   bool rank = in_dtype == MAO_F32 && nkm == 0;
   for (int i = 0; i < nprob; ++i) rank = rank && probs[i].K <= 64 && !(probs[i].flags & GF_SYRK);
   rank = rank && count_tiles(probs, nprob, 256) >= 16;
-  const int bm = (rank || (in_dtype == MAO_BF16 && (nkm != 0 || count_tiles(probs, nprob, 256) >= 128))) ? 256
+  const int bm = (rank || (in_dtype == MAO_BF16 && (nkm != 0 || nt != 0 || count_tiles(probs, nprob, 256) >= 128))) ? 256
                  : count_tiles(probs, nprob, 128) >= 512 ? 128 : 64;
   // Longest K first: the last tiles to start are the short ones.
   int order[kMaxProblems];

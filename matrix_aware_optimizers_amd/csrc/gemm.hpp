@@ -11,6 +11,12 @@ enum GemmFlags : int {
   GF_D_F32 = 2,    // D / Dt stored fp32 (else bf16)
   GF_C0_F32 = 4,   // C0 stored fp32 (else bf16)
   GF_B_KMAJOR = 8, // B stored K x N (row-major, ldb >= N): D = alpha A B (bf16 only)
+  // Tiled operands (tiled.hpp; bf16, 256 x 256 kernel only): A, and B in the
+  // orientation GF_B_KMAJOR names, are tiled with lda / ldb their padded
+  // widths; every tile, K included, lies inside the zero-padded storage.
+  GF_T32 = 16,
+  GF_D_T32 = 32,   // D (and the SYRK mirror) written tiled, ldd its padded width
+  GF_C0_T32 = 64,  // C0 read tiled, ldc0 its padded width
 };
 
 constexpr int kMaxProblems = 8;
@@ -26,6 +32,7 @@ struct GemmProblem {
   int64_t lda, ldb, ldc0, ldd, lddt;
   int64_t sA, sB, sC0, sD, sDt;  // batch strides (elements)
   float alpha, beta;
+  float dadd;        // added to D[i][i] (tiled launches only; 0 otherwise)
   int M, N, K, batch;
   int flags;
   // filled by the launcher

@@ -24,10 +24,15 @@
 // Rows (columns) beyond M or N read a clamped, valid row (chunk); they only
 // feed outputs that are never stored.
 //
-// Epilogue: interior tiles go through LDS in two halves of 128 rows and are
-// written as whole rows in 16- or 32-byte pieces (C0 blend and row scale on
-// the way). Edge tiles, a transposed copy Dt, and the SYRK mirror use 32-row
-// bands through LDS with the transposed copy written from LDS columns.
+// Tiled operands (tiled.hpp) are zero-padded to whole tiles: a slice is then
+// copied with no clamping, every direct load reading 1 KB in one piece, and
+// a K x N slice sits in LDS as 8 blocks of 32 k-rows x 64 bytes.
+//
+// Epilogue (epilogue.hpp): interior tiles, and every tile of a tiled D, go
+// through LDS in two halves of 128 rows and are written as whole rows in 16-
+// or 32-byte pieces (C0 blend, row scale, transposed copy or SYRK mirror on
+// the way). Edge tiles of a row-major D use 32-row bands through LDS (the
+// tiled kernels use the checked staged epilogue instead).
 #include "epilogue.hpp"
 #include "gemm.hpp"
 
@@ -64,7 +69,7 @@ __device__ __forceinline__ void vm_wait_c() { __builtin_amdgcn_s_waitcnt(MAO_VMC
 
 
 
-template <bool BKM>
+template <bool BKM, bool T32>
 __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE > SLAB_BYTES ? STAGE : SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
@@ -109,10 +114,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   // K x N: load p covers k-rows 8 p + 2 wave + lane / 32 of the slice, chunk
   // lane % 32 of the row's 512 bytes (permuted by bkswz); columns past the
   // edge re-read the last valid chunk.
+  //
+  // Tiled operands: load p of wave w copies half-block (p * 4 + w) of the
+  // slice, 1 KB read whole: block (8 tm + q / 2, slice) of A (and of an N x K
+  // B), block (slice, 8 tn + q / 2) of a K x N B.
   const bf16_t* asrc[LPT];
   const bf16_t* bsrc[LPT];
 #pragma unroll
   for (int p = 0; p < LPT; ++p) {
+    if constexpr (T32) {
+      const int q = p * 4 + wave;
+      const int64_t half = (q & 1) * 512 + lane * 8;
+      asrc[p] = A + (int64_t)(tm * 8 + (q >> 1)) * (lda >> 5) * 1024 + half;
+      if constexpr (BKM)
+        bsrc[p] = B + (int64_t)(tn * 8 + (q >> 1)) * 1024 + half;
+      else
+        bsrc[p] = B + (int64_t)(tn * 8 + (q >> 1)) * (ldb >> 5) * 1024 + half;
+      continue;
+    }
     const int L = (p * 4 + wave) * 64 + lane;  // 16-byte slot in the operand tile
     const int row = L >> 2, slot = L & 3;
     const int ch = slot ^ swz(row);
@@ -129,12 +148,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
     }
   }
   // K offset k0 (elements) of a slice: along rows of A (and of an N x K B),
-  // down the rows of a K x N B.
-  const int64_t bstep = BKM ? ldb : 1;
+  // down the rows of a K x N B. Tiled: the next block of the block row (1024
+  // elements per 32 k), or the next block row of a K x N B (32 ldb).
+  const int64_t astep = T32 ? 32 : 1;
+  const int64_t bstep = BKM ? ldb : astep;
   auto issue = [&](unsigned char* stage, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < LPT; ++p)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[p] + k0),
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[p] + (int64_t)k0 * astep),
                                        (lds_void_t*)(stage + (p * 4 + wave) * 1024), 16, 0, 0);
 #pragma unroll
     for (int p = 0; p < LPT; ++p)
@@ -161,9 +182,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   int bko[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int krow = 16 * h + (ti >> 2);
-    const int chunk = wn * 16 + ((j * 4) ^ bkswz(krow)) + 2 * tg + ((ti >> 1) & 1);
-    bko[j] = TB * ROWB + krow * BKROW + (chunk << 4) + 8 * (ti & 1);
+    if constexpr (T32) {
+      // tiled K x N slice in LDS: 8 blocks of 32 k-rows x 64 bytes; read
+      // (sub-step j / 2, upper four k j % 2) of fragment 0, fragments J at
+      // +2 KB. Four k-rows of one block span all 64 banks.
+      const int krow = 16 * h + 8 * (j >> 1) + 4 * (j & 1) + (ti >> 2);
+      const int chunk = (2 * tg + ((ti >> 1) & 1)) ^ t32_swz(krow);
+      bko[j] = TB * ROWB + wn * 4 * 2048 + krow * 64 + (chunk << 4) + 8 * (ti & 1);
+    } else {
+      const int krow = 16 * h + (ti >> 2);
+      const int chunk = wn * 16 + ((j * 4) ^ bkswz(krow)) + 2 * tg + ((ti >> 1) & 1);
+      bko[j] = TB * ROWB + krow * BKROW + (chunk << 4) + 8 * (ti & 1);
+    }
   }
 
   f32x16_t acc[4][4];
@@ -176,7 +206,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
 
   // B fragment j of sub-step SUB from stage STG (either layout)
 #define MAO_BFRAG(STG, SUB, J, DST)                                                          \
-  if constexpr (BKM) {                                                                      \
+  if constexpr (BKM && T32) {                                                               \
+    const uint2 lo_ = __builtin_bit_cast(                                                   \
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                     \
+                   (lds_v4i16_t*)(STG + bko[2 * (SUB)] + (J) * 2048)));                     \
+    const uint2 hi_ = __builtin_bit_cast(                                                   \
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                     \
+                   (lds_v4i16_t*)(STG + bko[2 * (SUB) + 1] + (J) * 2048)));                 \
+    DST = make_uint4(lo_.x, lo_.y, hi_.x, hi_.y);                                           \
+  } else if constexpr (BKM) {                                                               \
     const unsigned char* q_ = STG + bko[J] + (SUB) * 8 * BKROW;                             \
     const uint2 lo_ = __builtin_bit_cast(                                                   \
         uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(q_)));                \
@@ -227,7 +265,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   // slice k + 3 and reads sub-step 0 of slice k + 1 under the MFMAs of
   // sub-step 1. Past the end the last slice is reloaded into a stage nobody
   // reads again, so the loop has no branches.
-  const int nkf = K / KS;  // full slices
+  const int nkf = T32 ? (K + KS - 1) / KS : K / KS;  // full slices (tiled: zero pad past K)
   uint4 fa0[4], fb0[4], fa1[4], fb1[4];
 #define MAO_RING_STEP(CUR, NXT, REF, K)                                 \
   {                                                                     \
@@ -271,7 +309,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
 
   // ---- partial last slice through registers (zero fill past K) ------------
   const int ktail = nkf * KS;
-  if (ktail < K) {
+  if (!T32 && ktail < K) {
     vm_wait(0);
     asm volatile("" ::: "memory");
     __syncthreads();
@@ -332,7 +370,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   const void* C0 = P.C0 ? (const void*)((const char*)P.C0 + (int64_t)b * P.sC0 * csz) : nullptr;
   const float alpha = P.alpha, beta = P.beta;
   const float* rs = P.row_scale;
-  if (m0 + TB <= M && n0 + TB <= N) {
+  // A tiled D is written whole, pad included (the pad of every operand is
+  // zero, so it stays zero); a row-major D or Dt stops at M x N.
+  const bool dt32 = (P.flags & GF_D_T32) != 0;
+  if ((m0 + TB <= M && n0 + TB <= N) || (T32 && dt32)) {
     EpiArgs ea;
     ea.m0 = m0; ea.n0 = n0; ea.M = M; ea.N = N;
     ea.alpha = alpha; ea.beta = beta;
@@ -341,7 +382,25 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
     ea.D = D; ea.ldd = P.ldd; ea.d32 = d32;
     ea.Tt = Tt; ea.ldt = ldt;
     ea.diag = diag;
+    ea.c_t32 = (P.flags & GF_C0_T32) != 0;
+    ea.d_t32 = dt32;
+    ea.t_t32 = syrk && dt32;
+    ea.dadd = T32 ? P.dadd : 0.f;
     staged_epilogue<false>(acc, (float*)st0, (float*)st1, (float*)st2, (float*)st3, ea);
+    return;
+  }
+  if constexpr (T32) {
+    EpiArgs ea;
+    ea.m0 = m0; ea.n0 = n0; ea.M = M; ea.N = N;
+    ea.alpha = alpha; ea.beta = beta;
+    ea.C0 = C0; ea.ldc0 = P.ldc0; ea.c32 = c32;
+    ea.rs = rs;
+    ea.D = D; ea.ldd = P.ldd; ea.d32 = d32;
+    ea.Tt = Tt; ea.ldt = ldt;
+    ea.diag = diag;
+    ea.c_t32 = (P.flags & GF_C0_T32) != 0;
+    ea.dadd = P.dadd;
+    staged_epilogue<true>(acc, (float*)st0, (float*)st1, (float*)st2, (float*)st3, ea);
     return;
   }
   float* slab = (float*)st0;
@@ -453,10 +512,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
 }  // namespace
 
 mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream) {
-  if (args.p[0].flags & GF_B_KMAJOR)
-    hipLaunchKernelGGL(gemm_bf16_dl_kernel<true>, dim3(args.total_tiles), dim3(256), 0, stream, args);
+  const bool bkm = (args.p[0].flags & GF_B_KMAJOR) != 0, t32 = (args.p[0].flags & GF_T32) != 0;
+  const dim3 grid(args.total_tiles), block(256);
+  if (bkm && t32)
+    hipLaunchKernelGGL((gemm_bf16_dl_kernel<true, true>), grid, block, 0, stream, args);
+  else if (bkm)
+    hipLaunchKernelGGL((gemm_bf16_dl_kernel<true, false>), grid, block, 0, stream, args);
+  else if (t32)
+    hipLaunchKernelGGL((gemm_bf16_dl_kernel<false, true>), grid, block, 0, stream, args);
   else
-    hipLaunchKernelGGL(gemm_bf16_dl_kernel<false>, dim3(args.total_tiles), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((gemm_bf16_dl_kernel<false, false>), grid, block, 0, stream, args);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }

@@ -135,6 +135,51 @@ def test_muon_batched_matches_oracle_per_matrix(gpu_lib):
             assert rel(o[b], upd) < TOL["bf16"]
 
 
+def _batched_case(gpu_lib, shapes, seed, norm_mode="none", ns_steps=5):
+    import torch
+    r = np.random.default_rng(seed)
+    groups, host = [], []
+    for cnt, m, n in shapes:
+        w = bf16_round((0.02 * r.standard_normal((cnt, m, n))).astype(np.float32))
+        g = bf16_round(r.standard_normal((cnt, m, n)).astype(np.float32))
+        W, G = to_dev(w, "bf16"), to_dev(g, "bf16")
+        M = zeros_dev((cnt, m, n))
+        groups.append((W, G, M))
+        host.append((w, g))
+    outs = [torch.empty(W.shape, dtype=torch.float32, device="cuda") for W, _, _ in groups]
+    gpu_lib.muon_step_batched(groups, update_out=outs, lr=LR, mu=0.95, weight_decay=WD,
+                              ns_steps=ns_steps, ns_dtype="bf16", norm_mode=norm_mode)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for (w, g), out in zip(host, outs):
+        o = to_host(out)
+        for b in range(w.shape[0]):
+            _, _, upd = oracle.muon_step(w[b], g[b], np.zeros_like(w[b]), lr=LR, mu=0.95,
+                                         weight_decay=WD, ns_steps=ns_steps, norm_mode=norm_mode)
+            e = rel(o[b], upd)
+            worst = max(worst, e)
+            assert e < TOL["bf16"], f"{w.shape} matrix {b}: {e}"
+    return worst
+
+
+@pytest.mark.parametrize("norm_mode", ["none", "col_row"])
+def test_muon_tiled_workspaces_ragged(gpu_lib, norm_mode):
+    """Batches large enough (>= 128 tiles of 256 x 256) that the Newton-Schulz
+    workspaces are kept tiled, with dimensions that are not multiples of 256
+    (zero pad inside the tiles), wide and tall, and a degenerate 8-row group."""
+    log(f"muon tiled bf16 ragged {norm_mode}")
+    worst = _batched_case(gpu_lib, [(16, 520, 1032), (16, 1032, 520), (40, 8, 1000)], 31,
+                          norm_mode=norm_mode)
+    log(f"  worst update error {worst:.2e}")
+
+
+def test_muon_tiled_one_iteration(gpu_lib):
+    """One Newton-Schulz iteration: the first product is also the last, which
+    reads the tiled X0 and writes the row-major result."""
+    log("muon tiled bf16 one iteration")
+    _batched_case(gpu_lib, [(12, 776, 1288), (12, 1288, 776)], 32, ns_steps=1)
+
+
 def test_muon_full_size_o_projection(gpu_lib):
     """The 4096x4096 O projection of the 8B layer at full size, bf16, one step
     (the shape and launch configuration the benchmark times)."""
