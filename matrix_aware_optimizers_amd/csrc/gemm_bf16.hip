@@ -71,10 +71,12 @@ __device__ __forceinline__ void vm_wait_c() { __builtin_amdgcn_s_waitcnt(MAO_VMC
 
 template <bool BKM, bool T32>
 __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
-  __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE > SLAB_BYTES ? STAGE : SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char st0[(T32 || STAGE > SLAB_BYTES) ? STAGE : SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st3[STAGE];
+  // tiled kernels never use the 32-row slab, so a fifth stage fits in 160 KB
+  __shared__ __attribute__((aligned(16))) unsigned char st4[T32 ? STAGE : 16];
 
   // ---- tile --------------------------------------------------------------
   int pi, local;
@@ -264,27 +266,53 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   // wave is done with the stage of slice k - 1 -- refills that stage with
   // slice k + 3 and reads sub-step 0 of slice k + 1 under the MFMAs of
   // sub-step 1. Past the end the last slice is reloaded into a stage nobody
-  // reads again, so the loop has no branches.
+  // reads again, so the loop has no branches. The tiled kernels run a
+  // 5-stage ring the same way: slice k + 4 is issued at step k and slices
+  // k + 2 and k + 3 may be in flight at its wait, a step more of lead.
   const int nkf = T32 ? (K + KS - 1) / KS : K / KS;  // full slices (tiled: zero pad past K)
   uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+  constexpr int NST = T32 ? 5 : 4;  // ring stages
 #define MAO_RING_STEP(CUR, NXT, REF, K)                                 \
   {                                                                     \
     MAO_READ(CUR, 1, fa1, fb1)                                          \
     MAO_MFMA16(fa0, fb0)                                                \
     MAO_SCHED(BKM ? 12 : 8, 0)                                          \
     __builtin_amdgcn_sched_barrier(0);                                  \
-    vm_wait(2 * LPT);                                                   \
+    vm_wait((NST - 3) * 2 * LPT);                                       \
     asm volatile("" ::: "memory");                                      \
     __builtin_amdgcn_s_barrier();                                       \
     asm volatile("" ::: "memory");                                      \
-    issue(REF, min((K) + 3, nkf - 1) * KS);                             \
+    issue(REF, min((K) + NST - 1, nkf - 1) * KS);                       \
     MAO_READ(NXT, 0, fa0, fb0)                                          \
     MAO_MFMA16(fa1, fb1)                                                \
     MAO_SCHED(BKM ? 12 : 8, 2 * LPT)                                    \
     __builtin_amdgcn_sched_barrier(0);                                  \
   }
   int kt = 0;
-  if (nkf > 0) {
+  if (NST == 5 && nkf > 0) {
+    issue(st0, 0);
+    issue(st1, min(1, nkf - 1) * KS);
+    issue(st2, min(2, nkf - 1) * KS);
+    issue(st3, min(3, nkf - 1) * KS);
+    vm_wait(3 * 2 * LPT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    MAO_READ(st0, 0, fa0, fb0)
+    __builtin_amdgcn_sched_barrier(0);
+    for (; kt + 5 <= nkf; kt += 5) {
+      MAO_RING_STEP(st0, st1, st4, kt)
+      MAO_RING_STEP(st1, st2, st0, kt + 1)
+      MAO_RING_STEP(st2, st3, st1, kt + 2)
+      MAO_RING_STEP(st3, st4, st2, kt + 3)
+      MAO_RING_STEP(st4, st0, st3, kt + 4)
+    }
+    const int r = nkf - kt;
+    if (r > 0) MAO_RING_STEP(st0, st1, st4, kt)
+    if (r > 1) MAO_RING_STEP(st1, st2, st0, kt + 1)
+    if (r > 2) MAO_RING_STEP(st2, st3, st1, kt + 2)
+    if (r > 3) MAO_RING_STEP(st3, st4, st2, kt + 3)
+  } else if (nkf > 0) {
     issue(st0, 0);
     issue(st1, min(1, nkf - 1) * KS);
     issue(st2, min(2, nkf - 1) * KS);
@@ -402,7 +430,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
     ea.dadd = P.dadd;
     staged_epilogue<true>(acc, (float*)st0, (float*)st1, (float*)st2, (float*)st3, ea);
     return;
-  }
+  } else {
   float* slab = (float*)st0;
 
 #pragma unroll
@@ -507,6 +535,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
       }
     }
   }
+  }  // !T32
 }
 
 }  // namespace
