@@ -276,6 +276,14 @@ struct CholArgs {
 
 __device__ __forceinline__ int upk(int i, int k) { return i * NB - (i * (i - 1)) / 2 + (k - i); }
 
+// Lane l's value of v, in every lane (l a compile-time constant here).
+__device__ __forceinline__ double lane_d(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
   if (a.pred != nullptr && *a.pred == 0) return;
   __shared__ float X[NB][LDX];      // current Y (fp32), later V
@@ -308,6 +316,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
 #pragma unroll
   for (int k = 0; k < NB; ++k) y[k] = 0.0;
 
+#pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
     __syncthreads();
     // ---- partial Gram of this workgroup's rows: 36 upper 8 x 8 blocks x 7 row chunks
@@ -420,19 +429,37 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
       const double sh = 11.0 * ((double)len * nb + (double)nb * (nb + 1)) * 0x1p-53 * tr;
       for (int k = 0; k < nb; ++k) Gs[k][k] += sh;
     }
-    // ---- Cholesky G = R^T R, row k of R into Rt[.][k]
-    for (int k = 0; k < NB; ++k) {
-      __syncthreads();
-      const double piv = Gs[k][k];
-      if (!(piv > 1e-300) || !(piv < 1e300)) {
-        if (t == 0) bad = 1;
+    // ---- Cholesky G = R^T R, row k of R into Rt[.][k], by the first
+    // wavefront alone: lane j keeps column j of G in registers, the pivot
+    // comes from lane k by readlane and row k of R goes round through LDS
+    // (one wavefront's LDS accesses complete in order), so the 64 steps need
+    // no workgroup barrier.
+    __syncthreads();
+    if (t < NB) {
+      const int j = t;
+      double gc[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) gc[i] = Gs[i][j];
+      bool badl = false;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const double piv = lane_d(gc[k], k);
+        badl = badl || !(piv > 1e-300) || !(piv < 1e300);
+        const double rkk = sqrt(fmax(piv, 1e-300));
+        const double rkj = (j == k) ? rkk : gc[k] / rkk;
+        if (j >= k) Rt[j][k] = rkj;
+        dinv[j] = rkj;  // row k of R, shared (dinv is rewritten below)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = k + 1; i < NB; ++i) gc[i] = fma(-dinv[i], rkj, gc[i]);
+        // keep the updates at this step (the compiler would otherwise sink
+        // each one to the step that reads it, keeping every R entry live)
+#pragma unroll
+        for (int i = k + 1; i < NB; ++i) asm volatile("" : "+v"(gc[i]));
+        __builtin_amdgcn_wave_barrier();
       }
-      const double rkk = sqrt(fmax(piv, 1e-300));
-      if (t >= k && t < NB) Rt[t][k] = (t == k) ? rkk : Gs[k][t] / rkk;
-      if (t == 0) dinv[k] = 1.0 / rkk;
-      __syncthreads();
-      for (int i = k + 1 + (t >> 4); i < NB; i += 16)
-        for (int j = i + (t & 15); j < NB; j += 16) Gs[i][j] -= Rt[i][k] * Rt[j][k];
+      dinv[j] = 1.0 / Rt[j][j];
+      if (j == 0 && badl) bad = 1;
     }
     __syncthreads();
     if (bad) {
@@ -458,24 +485,33 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
   // ---- reconstruction: LU of -Q1 (top nb x nb block) with sign choice, T
   __syncthreads();
   if (g == 0) {
-    if (t < nb) {
+    // LU by the first wavefront: lane i keeps row i of Z = -Q1 in registers
+    // (zero outside nb x nb, which leaves the nb x nb factors unchanged), the
+    // pivot row comes from lane j by readlane; L overwrites Z below the
+    // diagonal. No workgroup barrier inside.
+    if (t < NB) {
+      const int i = t;
+      double zr[NB];
 #pragma unroll
-      for (int k = 0; k < NB; ++k)
-        if (k < nb) Gs[t][k] = -y[k];
-    }
-    for (int j = 0; j < nb; ++j) {
-      __syncthreads();
-      const double zjj = Gs[j][j];
-      const double dj = zjj >= 0.0 ? 1.0 : -1.0;
-      const double ujj = 1.0 + dj * zjj;
-      if (t == 0) {
-        dsg[j] = (float)dj;
-        Rt[j][j] = ujj;  // U diagonal (Rt reused for U, stored U[i][c] at Rt[i][c])
+      for (int c = 0; c < NB; ++c) zr[c] = (i < nb && c < nb) ? -y[c] : 0.0;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const double zjj = lane_d(zr[j], j);
+        const double dj = zjj >= 0.0 ? 1.0 : -1.0;
+        const double ujj = 1.0 + dj * zjj;
+        if (i == 0 && j < nb) {
+          dsg[j] = (float)dj;
+          Rt[j][j] = ujj;  // U diagonal (Rt reused for U, stored U[i][c] at Rt[i][c])
+        }
+        const double lij = (i > j) ? dj * zr[j] / ujj : 0.0;  // L[i][j]
+        if (i > j) zr[j] = lij;
+#pragma unroll
+        for (int cc = j + 1; cc < NB; ++cc) zr[cc] = fma(-lij, lane_d(zr[cc], j), zr[cc]);
+#pragma unroll
+        for (int cc = j + 1; cc < NB; ++cc) asm volatile("" : "+v"(zr[cc]));
       }
-      if (t > j && t < nb) Gs[t][j] = dj * Gs[t][j] / ujj;  // L[t][j]
-      __syncthreads();
-      for (int rr = j + 1 + (t >> 4); rr < nb; rr += 16)
-        for (int cc = j + 1 + (t & 15); cc < nb; cc += 16) Gs[rr][cc] -= Gs[rr][j] * Gs[j][cc];
+#pragma unroll
+      for (int c = 0; c < NB; ++c) Gs[i][c] = zr[c];
     }
     __syncthreads();
     // U strictly upper: U[i][c] = d_c Z[i][c]
