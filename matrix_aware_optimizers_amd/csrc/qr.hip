@@ -253,7 +253,8 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelArgs a) {
 // diagonal away from 1 -- is decided identically by every workgroup, which
 // then all return; the per-column Householder panel runs instead (a flag).
 constexpr int NU = NB * (NB + 1) / 2;   // packed upper-triangular entries
-constexpr int LDG = NB + 1;             // padded fp64 LDS row
+constexpr int LDG = NB + 2;             // fp64 LDS row: 16-byte aligned rows, 2 banks apart
+constexpr int LDT = NB + 4;             // fp32 LDS row of T (16-byte aligned)
 
 struct CholArgs {
   const float* S;
@@ -287,9 +288,9 @@ __device__ __forceinline__ double lane_d(double v, int l) {
 __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
   if (a.pred != nullptr && *a.pred == 0) return;
   __shared__ float X[NB][LDX];      // current Y (fp32), later V
-  __shared__ double Gs[NB][LDG];    // Gram / LU work
-  __shared__ double Rt[NB][LDG];    // Cholesky factor, transposed (Rt[k][l] = R[l][k]); later U
-  __shared__ float Tl[NB][NB + 1];
+  __shared__ __attribute__((aligned(16))) double Gs[NB][LDG];  // Gram / LU work
+  __shared__ __attribute__((aligned(16))) double Rt[NB][LDG];  // Cholesky factor R (row k = R[k][.]); later U
+  __shared__ __attribute__((aligned(16))) float Tl[NB][LDT];
   __shared__ double dinv[NB];
   __shared__ float dsg[NB];
   __shared__ double red64[TPB];
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
       const double sh = 11.0 * ((double)len * nb + (double)nb * (nb + 1)) * 0x1p-53 * tr;
       for (int k = 0; k < nb; ++k) Gs[k][k] += sh;
     }
-    // ---- Cholesky G = R^T R, row k of R into Rt[.][k], by the first
+    // ---- Cholesky G = R^T R, row k of R into Rt[k][.], by the first
     // wavefront alone: lane j keeps column j of G in registers, the pivot
     // comes from lane k by readlane and row k of R goes round through LDS
     // (one wavefront's LDS accesses complete in order), so the 64 steps need
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
         badl = badl || !(piv > 1e-300) || !(piv < 1e300);
         const double rkk = sqrt(fmax(piv, 1e-300));
         const double rkj = (j == k) ? rkk : gc[k] / rkk;
-        if (j >= k) Rt[j][k] = rkj;
+        if (j >= k) Rt[k][j] = rkj;
         dinv[j] = rkj;  // row k of R, shared (dinv is rewritten below)
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -458,7 +459,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
         for (int i = k + 1; i < NB; ++i) asm volatile("" : "+v"(gc[i]));
         __builtin_amdgcn_wave_barrier();
       }
-      dinv[j] = 1.0 / Rt[j][j];
+      dinv[j] = 1.0 / Rt[j][j];  // own write above
       if (j == 0 && badl) bad = 1;
     }
     __syncthreads();
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
     for (int k = 0; k < NB; ++k) {
       y[k] *= dinv[k];
 #pragma unroll
-      for (int j = k + 1; j < NB; ++j) y[j] = fma(-y[k], Rt[j][k], y[j]);
+      for (int j = k + 1; j < NB; ++j) y[j] = fma(-y[k], Rt[k][j], y[j]);
     }
     if (pass < 2) {
       __syncthreads();
@@ -485,60 +486,62 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
   // ---- reconstruction: LU of -Q1 (top nb x nb block) with sign choice, T
   __syncthreads();
   if (g == 0) {
-    // LU by the first wavefront: lane i keeps row i of Z = -Q1 in registers
-    // (zero outside nb x nb, which leaves the nb x nb factors unchanged), the
-    // pivot row comes from lane j by readlane; L overwrites Z below the
-    // diagonal. No workgroup barrier inside.
+    // LU and T by the first wavefront. Lane i keeps row i of Z = -Q1 in
+    // registers (zero outside nb x nb, which leaves the nb x nb factors
+    // unchanged); the pivot row comes from lane j by readlane and L
+    // overwrites Z below the diagonal. Lane i then turns its row into U
+    // (signs d_c) and solves its row of T = U L^{-T} in place, reading L[j][l]
+    // from lane j. No workgroup barrier inside.
     if (t < NB) {
       const int i = t;
-      double zr[NB];
+      double w[NB];
+      double udiag = 1.0;
 #pragma unroll
-      for (int c = 0; c < NB; ++c) zr[c] = (i < nb && c < nb) ? -y[c] : 0.0;
+      for (int c = 0; c < NB; ++c) w[c] = (i < nb && c < nb) ? -y[c] : 0.0;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const double zjj = lane_d(zr[j], j);
+        const double zjj = lane_d(w[j], j);
         const double dj = zjj >= 0.0 ? 1.0 : -1.0;
         const double ujj = 1.0 + dj * zjj;
         if (i == 0 && j < nb) {
           dsg[j] = (float)dj;
           Rt[j][j] = ujj;  // U diagonal (Rt reused for U, stored U[i][c] at Rt[i][c])
         }
-        const double lij = (i > j) ? dj * zr[j] / ujj : 0.0;  // L[i][j]
-        if (i > j) zr[j] = lij;
+        if (i == j) udiag = ujj;
+        const double lij = (i > j) ? dj * w[j] / ujj : 0.0;  // L[i][j]
+        if (i > j) w[j] = lij;
 #pragma unroll
-        for (int cc = j + 1; cc < NB; ++cc) zr[cc] = fma(-lij, lane_d(zr[cc], j), zr[cc]);
+        for (int cc = j + 1; cc < NB; ++cc) w[cc] = fma(-lij, lane_d(w[cc], j), w[cc]);
 #pragma unroll
-        for (int cc = j + 1; cc < NB; ++cc) asm volatile("" : "+v"(zr[cc]));
+        for (int cc = j + 1; cc < NB; ++cc) asm volatile("" : "+v"(w[cc]));
       }
+      __builtin_amdgcn_wave_barrier();
+      // L to Gs (rows of Y's top block), U (strictly upper) to Rt, U row in w
 #pragma unroll
-      for (int c = 0; c < NB; ++c) Gs[i][c] = zr[c];
-    }
-    __syncthreads();
-    // U strictly upper: U[i][c] = d_c Z[i][c]
-    for (int idx = t; idx < nb * nb; idx += TPB) {
-      const int i = idx / nb, c = idx % nb;
-      if (i < c) Rt[i][c] = (double)dsg[c] * Gs[i][c];
-    }
-    __syncthreads();
-    // T = U L^{-T}: row i, t_ij = U_ij - sum_{i <= l < j} t_il L_jl
-    if (t < nb) {
-      const int i = t;
-      double trow[NB];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) trow[j] = (j >= i && j < nb) ? Rt[i][j] : 0.0;
-#pragma unroll
-      for (int l = 0; l < NB; ++l) {
-        if (l >= i && l < nb) {
-#pragma unroll
-          for (int j = l + 1; j < NB; ++j)
-            if (j < nb) trow[j] = fma(-trow[l], Gs[j][l], trow[j]);
+      for (int c = 0; c < NB; ++c) {
+        if (c < i) {
+          Gs[i][c] = w[c];
+        } else if (c == i) {
+          w[c] = (i < nb) ? udiag : 0.0;
+        } else {
+          const double u = (c < nb) ? (double)dsg[c] * w[c] : 0.0;
+          if (i < nb && c < nb) Rt[i][c] = u;
+          w[c] = u;
         }
       }
+      // t_ij = U_ij - sum_{i <= l < j} t_il L_jl, l ascending
 #pragma unroll
-      for (int j = 0; j < NB; ++j) a.T[i * NB + j] = (j >= i && j < nb) ? (float)trow[j] : 0.f;
-    } else if (t < NB) {
-      for (int j = 0; j < NB; ++j) a.T[t * NB + j] = 0.f;
+      for (int l = 0; l < NB; ++l) {
+        const double m = (l >= i) ? w[l] : 0.0;
+#pragma unroll
+        for (int j = l + 1; j < NB; ++j) w[j] = fma(-m, lane_d(w[l], j), w[j]);
+#pragma unroll
+        for (int j = l + 1; j < NB; ++j) asm volatile("" : "+v"(w[j]));
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) a.T[i * NB + j] = (i < nb && j >= i && j < nb) ? (float)w[j] : 0.f;
     }
+    __syncthreads();
     for (int e = t; e < nb * nb; e += TPB) {
       const int i = e / nb, c = e % nb;
       a.bcast[i * NB + c] = (i <= c) ? Rt[i][c] : 0.0;
@@ -575,6 +578,11 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) X[k][t] = valid ? (float)z[k] : 0.f;
   }
+  // T^T beside T (in the fp64 Gram space, free once every row of Y is
+  // built), so that both products read 16-byte rows
+  __syncthreads();
+  float* Tt = (float*)&Gs[0][0];
+  for (int e = t; e < NB * NB; e += TPB) Tt[(e & 63) * LDT + (e >> 6)] = Tl[e >> 6][e & 63];
   __syncthreads();
   if (valid) {
     for (int k = 0; k < nb; ++k) a.V[(int64_t)k * a.ldV + li] = X[k][t];
@@ -585,10 +593,19 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
     for (int i = 0; i < NB; ++i) vr[i] = (i < nb) ? X[i][t] : 0.f;
     for (int c = 0; c < NB; ++c) {
       float sf[4] = {0.f, 0.f, 0.f, 0.f}, so[4] = {0.f, 0.f, 0.f, 0.f};
+      const float4* tf = (const float4*)&Tl[c][0];
+      const float4* to = (const float4*)&Tt[c * LDT];
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        sf[i & 3] = fmaf(vr[i], Tl[c][i], sf[i & 3]);
-        so[i & 3] = fmaf(vr[i], Tl[i][c], so[i & 3]);
+      for (int i4 = 0; i4 < NB / 4; ++i4) {
+        const float4 f = tf[i4], o = to[i4];
+        sf[0] = fmaf(vr[4 * i4 + 0], f.x, sf[0]);
+        sf[1] = fmaf(vr[4 * i4 + 1], f.y, sf[1]);
+        sf[2] = fmaf(vr[4 * i4 + 2], f.z, sf[2]);
+        sf[3] = fmaf(vr[4 * i4 + 3], f.w, sf[3]);
+        so[0] = fmaf(vr[4 * i4 + 0], o.x, so[0]);
+        so[1] = fmaf(vr[4 * i4 + 1], o.y, so[1]);
+        so[2] = fmaf(vr[4 * i4 + 2], o.z, so[2]);
+        so[3] = fmaf(vr[4 * i4 + 3], o.w, so[3]);
       }
       zf[c] = (sf[0] + sf[1]) + (sf[2] + sf[3]);
       zo[c] = (so[0] + so[1]) + (so[2] + so[3]);
