@@ -135,7 +135,7 @@ def test_muon_batched_matches_oracle_per_matrix(gpu_lib):
             assert rel(o[b], upd) < TOL["bf16"]
 
 
-def _batched_case(gpu_lib, shapes, seed, norm_mode="none", ns_steps=5):
+def _batched_case(gpu_lib, shapes, seed, norm_mode="none", ns_steps=5, coeffs=None):
     import torch
     r = np.random.default_rng(seed)
     groups, host = [], []
@@ -148,14 +148,16 @@ def _batched_case(gpu_lib, shapes, seed, norm_mode="none", ns_steps=5):
         host.append((w, g))
     outs = [torch.empty(W.shape, dtype=torch.float32, device="cuda") for W, _, _ in groups]
     gpu_lib.muon_step_batched(groups, update_out=outs, lr=LR, mu=0.95, weight_decay=WD,
-                              ns_steps=ns_steps, ns_dtype="bf16", norm_mode=norm_mode)
+                              ns_steps=ns_steps, ns_coeffs=coeffs, ns_dtype="bf16",
+                              norm_mode=norm_mode)
     torch.cuda.synchronize()
     worst = 0.0
     for (w, g), out in zip(host, outs):
         o = to_host(out)
         for b in range(w.shape[0]):
             _, _, upd = oracle.muon_step(w[b], g[b], np.zeros_like(w[b]), lr=LR, mu=0.95,
-                                         weight_decay=WD, ns_steps=ns_steps, norm_mode=norm_mode)
+                                         weight_decay=WD, ns_steps=ns_steps, coeffs=coeffs,
+                                         norm_mode=norm_mode)
             e = rel(o[b], upd)
             worst = max(worst, e)
             assert e < TOL["bf16"], f"{w.shape} matrix {b}: {e}"
@@ -178,6 +180,20 @@ def test_muon_tiled_one_iteration(gpu_lib):
     reads the tiled X0 and writes the row-major result."""
     log("muon tiled bf16 one iteration")
     _batched_case(gpu_lib, [(12, 776, 1288), (12, 1288, 776)], 32, ns_steps=1)
+
+
+@pytest.mark.parametrize("family", ["tuned_quintic", "with_cubic_steps"])
+def test_muon_tiled_coefficient_families(gpu_lib, family):
+    """Per-iteration coefficients through the tiled path: a tuned quintic
+    (every c != 0: the polynomial completed to a square), and a schedule whose
+    odd iterations are cubic (c = 0: the square step reads A as C0)."""
+    if family == "tuned_quintic":
+        coeffs = [(3.4445, -4.7750, 2.0315)] * 5
+    else:
+        coeffs = [(1.5, -0.5, 0.0), (15 / 8, -10 / 8, 3 / 8)] * 2 + [(1.5, -0.5, 0.0)]
+    log(f"muon tiled bf16 coefficients {family}")
+    worst = _batched_case(gpu_lib, [(16, 520, 1032), (16, 1032, 520)], 33, coeffs=coeffs)
+    log(f"  worst update error {worst:.2e}")
 
 
 def test_muon_full_size_o_projection(gpu_lib):
