@@ -318,8 +318,9 @@ def foam_alg_flops(m, n, checked=False, refreshed=False):
 
 
 class SoapLikeWorkload:
-    """A set of matrices stepped one after another by soap_step or foam_step
-    (one shared workspace), with a ring of two gradients per matrix."""
+    """A set of matrices stepped together by soap_step_many or foam_step_many
+    (equal-size QR refreshes batched), with a ring of two gradients per
+    matrix."""
 
     def __init__(self, kind, config, specs, g_dtype, w_dtype, pf=10, tol=0.1):
         import torch
@@ -336,7 +337,6 @@ class SoapLikeWorkload:
         else:
             self.hp = mao.foam_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
                                        pf=pf, tol=tol)
-        need = 0
         for idx, sp in enumerate(specs):
             if idx % 16 == 15:
                 log(f"  {idx + 1}/{len(specs)} matrices set up")
@@ -355,7 +355,6 @@ class SoapLikeWorkload:
                 st["QL"].fill_diagonal_(1.0)
                 st["QR"].fill_diagonal_(1.0)
                 cst = mao.soap_state(st["M"], st["V"], st["L"], st["R"], st["QL"], st["QR"])
-                need = max(need, self.lib.soap_workspace_size(m, n, ctypes.byref(self.hp)))
             else:
                 st = {"M": z(m, n), "R": z(n, n), "QR": z(n, n),
                       "r": torch.zeros(m, device="cuda"), "c": torch.zeros(n, device="cuda"),
@@ -363,8 +362,15 @@ class SoapLikeWorkload:
                 st["QR"].fill_diagonal_(1.0)
                 cst = mao.FoamStateC(mao.mat(st["M"]), mao.mat(st["R"]), mao.mat(st["QR"]),
                                      st["r"].data_ptr(), st["c"].data_ptr(), st["aux"].data_ptr())
-                need = max(need, self.lib.foam_workspace_size(m, n, ctypes.byref(self.hp)))
             self.items.append((sp, W, Gs, st, cst, mao.mat(W), [mao.mat(G) for G in Gs]))
+        k = len(self.items)
+        self.Ws = (mao.Mat * k)(*[it[5] for it in self.items])
+        self.Gs = [(mao.Mat * k)(*[it[6][r] for it in self.items]) for r in range(2)]
+        St = mao.SoapStateC if kind == "soap" else mao.FoamStateC
+        self.sts = (St * k)(*[it[4] for it in self.items])
+        size = (self.lib.soap_step_many_workspace_size if kind == "soap"
+                else self.lib.foam_step_many_workspace_size)
+        need = size(k, self.Ws, ctypes.byref(self.hp))
         self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.embedding = None
@@ -379,12 +385,11 @@ class SoapLikeWorkload:
         self.embedding = (w, g, torch.zeros_like(w), torch.zeros_like(w))
 
     def step(self, t: int):
-        fn = self.lib.soap_step if self.kind == "soap" else self.lib.foam_step
-        for sp, W, Gs, st, cst, wm, gms in self.items:
-            rc = fn(wm, gms[t % 2], ctypes.byref(cst), t, ctypes.byref(self.hp),
-                    ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), None, self.stream)
-            if rc != 0:
-                self.mao._check(rc, self.kind + "_step")
+        fn = self.lib.soap_step_many if self.kind == "soap" else self.lib.foam_step_many
+        rc = fn(len(self.items), self.Ws, self.Gs[t % 2], self.sts, t, ctypes.byref(self.hp),
+                ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), None, self.stream)
+        if rc != 0:
+            self.mao._check(rc, self.kind + "_step_many")
         if self.embedding is not None:
             w, g, m, v = self.embedding
             rc = self.lib.adamw_step(w.data_ptr(), 0, g[t % 2].data_ptr(), 0, m.data_ptr(),

@@ -254,6 +254,45 @@ MAO_API mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* state, 
                      float* update_out, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Many matrices per call                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes for soap_step_many / foam_step_many on these shapes (only
+ * W[i].rows and W[i].cols are read); 0 for count outside 1..4096 or an empty
+ * shape. */
+MAO_API size_t soap_step_many_workspace_size(int32_t count, const mao_mat* W,
+                                             const mao_soap_hparams* hp);
+MAO_API size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W,
+                                             const mao_foam_hparams* hp);
+
+/*
+ * soap_step_many / foam_step_many -- soap_step / foam_step on `count`
+ * matrices of any shapes (the layers of a model), with the same t and
+ * hyperparameters; results equal `count` separate calls. The QR refreshes of
+ * equal size (SOAP: the L factor of an m x n matrix is of size m, the R
+ * factor of size n; FOAM: R only) run as one batched QR each: the panels of
+ * all of them share each cooperative launch and the updates run as batched
+ * products, so that the per-panel latency is paid once per size instead of
+ * once per factor ([SMB] section 3-2 (4) for the refresh; [FOAM] section 3
+ * for FOAM's criterion, decided per matrix on the device).
+ *
+ * W, G, state: arrays of `count` (host memory, read during the call).
+ * update_out: NULL, or a host array of `count` pointers, each NULL or as in
+ * soap_step. Buffers of different matrices must not overlap (MAO_E_ALIAS).
+ * count outside 1..4096: MAO_E_SHAPE; NULL W, G or state: MAO_E_NULL; other
+ * errors as in the single-matrix calls, reported for the first failing
+ * matrix before anything is launched.
+ */
+MAO_API mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
+                                  const mao_soap_state* state, int64_t t,
+                                  const mao_soap_hparams* hp, void* workspace,
+                                  size_t workspace_bytes, float* const* update_out, void* stream);
+MAO_API mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
+                                  const mao_foam_state* state, int64_t t,
+                                  const mao_foam_hparams* hp, void* workspace,
+                                  size_t workspace_bytes, float* const* update_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* AdamW (flat)                                                              */
 /* ------------------------------------------------------------------------ */
 

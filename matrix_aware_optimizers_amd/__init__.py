@@ -80,6 +80,14 @@ EXPORTS = {
     "foam_workspace_size": (c_size_t, [c_int64, c_int64, POINTER(FoamHparams)]),
     "foam_step": (c_int32, [Mat, Mat, POINTER(FoamStateC), c_int64, POINTER(FoamHparams),
                             c_void_p, c_size_t, c_void_p, c_void_p]),
+    "soap_step_many_workspace_size": (c_size_t, [c_int32, POINTER(Mat), POINTER(SoapHparams)]),
+    "foam_step_many_workspace_size": (c_size_t, [c_int32, POINTER(Mat), POINTER(FoamHparams)]),
+    "soap_step_many": (c_int32, [c_int32, POINTER(Mat), POINTER(Mat), POINTER(SoapStateC), c_int64,
+                                 POINTER(SoapHparams), c_void_p, c_size_t,
+                                 POINTER(c_void_p), c_void_p]),
+    "foam_step_many": (c_int32, [c_int32, POINTER(Mat), POINTER(Mat), POINTER(FoamStateC), c_int64,
+                                 POINTER(FoamHparams), c_void_p, c_size_t,
+                                 POINTER(c_void_p), c_void_p]),
     "adamw_step": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int64,
                              c_int64, c_float, c_float, c_float, c_float, c_float, c_void_p,
                              c_void_p]),
@@ -295,6 +303,45 @@ def foam_step(W, G, state: dict, t: int, *, update_out=None, ws=None, **hp_kw):
     buf = ws if ws is not None else workspace(need, W.device)
     _check(lib.foam_step(mat(W), mat(G), ctypes.byref(st), t, ctypes.byref(hp), _ptr(buf),
                          buf.numel(), _ptr(update_out), _stream()), "foam_step")
+
+
+def _many_args(items, update_out):
+    n = len(items)
+    Ws = (Mat * n)(*[mat(it[0]) for it in items])
+    Gs = (Mat * n)(*[mat(it[1]) for it in items])
+    outs = None
+    if update_out is not None:
+        outs = (c_void_p * n)(*[None if o is None else o.data_ptr() for o in update_out])
+    return n, Ws, Gs, outs
+
+
+def soap_step_many(items, t: int, *, update_out=None, ws=None, **hp_kw):
+    """SOAP on several matrices in one call: ``items`` is a list of
+    (W, G, state dict) as for soap_step; equal-size QR refreshes run batched."""
+    lib = load()
+    hp = soap_hparams(**hp_kw)
+    n, Ws, Gs, outs = _many_args(items, update_out)
+    sts = (SoapStateC * n)(*[soap_state(st["M"], st["V"], st["L"], st["R"], st["QL"], st["QR"])
+                             for _, _, st in items])
+    need = lib.soap_step_many_workspace_size(n, Ws, ctypes.byref(hp))
+    buf = ws if ws is not None else workspace(need, items[0][0].device)
+    _check(lib.soap_step_many(n, Ws, Gs, sts, t, ctypes.byref(hp), _ptr(buf), buf.numel(), outs,
+                              _stream()), "soap_step_many")
+
+
+def foam_step_many(items, t: int, *, update_out=None, ws=None, **hp_kw):
+    """FOAM on several matrices in one call: ``items`` is a list of
+    (W, G, state dict) as for foam_step; equal-size QR refreshes run batched."""
+    lib = load()
+    hp = foam_hparams(**hp_kw)
+    n, Ws, Gs, outs = _many_args(items, update_out)
+    sts = (FoamStateC * n)(*[FoamStateC(mat(st["M"]), mat(st["R"]), mat(st["QR"]),
+                                        st["r"].data_ptr(), st["c"].data_ptr(),
+                                        st["aux"].data_ptr()) for _, _, st in items])
+    need = lib.foam_step_many_workspace_size(n, Ws, ctypes.byref(hp))
+    buf = ws if ws is not None else workspace(need, items[0][0].device)
+    _check(lib.foam_step_many(n, Ws, Gs, sts, t, ctypes.byref(hp), _ptr(buf), buf.numel(), outs,
+                              _stream()), "foam_step_many")
 
 
 def adamw_step(w, g, m, v, t: int, *, lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0,

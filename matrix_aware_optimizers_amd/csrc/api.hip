@@ -419,24 +419,27 @@ struct RotBufs {
   int64_t ldm, ldn;  // padded leading dims for m- and n-long rows
 };
 
-void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R) {
+// own_qr: the bases E, the QR input S, FOAM's refresh flag and the QR
+// workspace belong to this matrix; otherwise the caller points EL, ER, S and
+// flag into the shared, size-grouped QR area of a many-matrix call.
+void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool own_qr = true) {
   R.ldm = ws_ld(m);
   R.ldn = ws_ld(n);
   const int big = std::max(m, n);
   const int64_t ldb = ws_ld(big);
   R.Gf = g_bf16 ? c.take<float>((size_t)m * R.ldn) : nullptr;
   R.Gtf = c.take<float>((size_t)n * R.ldm);
-  R.EL = soap ? c.take<float>((size_t)m * R.ldm) : nullptr;
-  R.ER = c.take<float>((size_t)n * R.ldn);
-  R.S = c.take<float>((size_t)big * ldb);
+  R.EL = (soap && own_qr) ? c.take<float>((size_t)m * R.ldm) : nullptr;
+  R.ER = own_qr ? c.take<float>((size_t)n * R.ldn) : nullptr;
+  R.S = own_qr ? c.take<float>((size_t)big * ldb) : nullptr;
   R.T2t = c.take<float>((size_t)n * R.ldm);
   R.Gtil = c.take<float>((size_t)m * R.ldn);
   R.Mtil = c.take<float>((size_t)m * R.ldn);
   R.U = c.take<float>((size_t)m * R.ldn);
   R.D = soap ? nullptr : c.take<float>((size_t)n * R.ldn);
   R.small = soap ? nullptr : c.take<float>(64 + foam_moments_work_floats(m, n) + 2 * (size_t)n);
-  R.flag = soap ? nullptr : c.take<int>(4);
-  R.qr = carve_qr_work(c, big);
+  R.flag = (soap || !own_qr) ? nullptr : c.take<int>(4);
+  if (own_qr) R.qr = carve_qr_work(c, big);
 }
 
 mao_status check_step_common(const mao_mat& W, const mao_mat& G, int64_t t) {
@@ -570,15 +573,16 @@ size_t soap_workspace_size(int64_t rows, int64_t cols, const mao_soap_hparams* h
   return c.used + 256;
 }
 
-mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
-                     const mao_soap_hparams* hp, void* workspace, size_t workspace_bytes,
-                     float* update_out, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  if (!st || !hp) MAO_FAIL(MAO_E_NULL, "state or hparams is NULL");
+}  // extern "C"
+
+namespace {
+
+// Argument checks of one SOAP matrix; its buffers go to rr.
+mao_status validate_soap(const mao_mat& W, const mao_mat& G, const mao_soap_state* st, int64_t t,
+                         const float* update_out, std::vector<Range>& rr) {
+  if (!st) MAO_FAIL(MAO_E_NULL, "state is NULL");
   MAO_TRY(check_step_common(W, G, t));
-  MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
-  if (hp->refresh_every < 0) MAO_FAIL(MAO_E_HPARAM, "refresh_every=%d", hp->refresh_every);
-  const int m = (int)W.rows, n = (int)W.cols;
+  const int64_t m = W.rows, n = W.cols;
   MAO_TRY(check_state_mat("M", st->M, m, n));
   MAO_TRY(check_state_mat("V", st->V, m, n));
   MAO_TRY(check_state_mat("L", st->L, m, m));
@@ -587,44 +591,57 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
   MAO_TRY(check_state_mat("QR", st->QR, n, n));
   if (update_out && ((uintptr_t)update_out % 16 != 0 || n % 4 != 0))
     MAO_FAIL(MAO_E_LAYOUT, "update_out must be 16-byte aligned with cols %% 4 == 0");
-  std::vector<Range> rr = {mrange(W), mrange(G), mrange(st->M), mrange(st->V), mrange(st->L),
-                           mrange(st->R), mrange(st->QL), mrange(st->QR)};
+  for (const Range& r : {mrange(W), mrange(G), mrange(st->M), mrange(st->V), mrange(st->L),
+                         mrange(st->R), mrange(st->QL), mrange(st->QR)})
+    rr.push_back(r);
   if (update_out) rr.push_back(mat_range(update_out, 1, m, n, n, 0, 4));
-  MAO_TRY(check_no_overlap(rr));
-  MAO_TRY(check_workspace(workspace, workspace_bytes, soap_workspace_size(m, n, hp)));
+  return MAO_OK;
+}
 
-  Carver c(workspace);
-  RotBufs R;
-  carve_rot(c, m, n, true, true, R);
+mao_status check_soap_hp(const mao_soap_hparams* hp) {
+  if (!hp) MAO_FAIL(MAO_E_NULL, "hparams is NULL");
+  MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
+  if (hp->refresh_every < 0) MAO_FAIL(MAO_E_HPARAM, "refresh_every=%d", hp->refresh_every);
+  return MAO_OK;
+}
+
+bool soap_refresh(const mao_soap_hparams* hp, int64_t t) {
+  return hp->refresh_every > 0 && ((t - 1) % hp->refresh_every) == 0;
+}
+
+// SOAP before the refresh: momentum, fp32 G and G^T, factor EMAs with the
+// current gradient, E = Q^T of both bases.
+mao_status soap_pre(const mao_mat& W, const mao_mat& G, const mao_soap_state* st, RotBufs& R,
+                    const mao_soap_hparams* hp, hipStream_t s) {
+  const int m = (int)W.rows, n = (int)W.cols;
   const float b1 = hp->beta1, b2 = hp->beta2;
   float* M = (float*)st->M.data;
-  float* L = (float*)st->L.data;
-  float* Rf = (float*)st->R.data;
-  float* QL = (float*)st->QL.data;
-  float* QR = (float*)st->QR.data;
-  const int64_t ldM = st->M.ld, ldL = st->L.ld, ldR = st->R.ld, ldQL = st->QL.ld, ldQR = st->QR.ld;
-
   // 1. momentum
-  MAO_TRY(ema_sumsq(view(M, ldM), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr, rowblocks_for(m, 1), s));
+  MAO_TRY(ema_sumsq(view(M, st->M.ld), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr,
+                    rowblocks_for(m, 1), s));
   // fp32 G and G^T
   const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
   const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
   MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
                              view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
   // 2. factor EMAs with the current gradient
-  MAO_TRY(syrk_ema(m, n, Gf, ldG, b2, L, ldL, s));
-  MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s));
-  // 3. refresh: Q <- qr(F Q); S = (F Q)^T = Q^T F stored row-major
-  MAO_TRY(transpose(view(QL, ldQL), view(R.EL, R.ldm), m, m, 1, MAO_F32, s));
-  MAO_TRY(transpose(view(QR, ldQR), view(R.ER, R.ldn), n, n, 1, MAO_F32, s));
-  const bool refresh = hp->refresh_every > 0 && ((t - 1) % hp->refresh_every) == 0;
-  if (refresh) {
-    const int64_t ldS = ws_ld(std::max(m, n));
-    MAO_TRY(nt32(m, m, m, R.EL, R.ldm, L, ldL, R.S, ldS, nullptr, 0, s));
-    MAO_TRY(qr_core(R.S, ldS, m, R.EL, R.ldm, QL, ldQL, R.qr, nullptr, s));
-    MAO_TRY(nt32(n, n, n, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));
-    MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, QR, ldQR, R.qr, nullptr, s));
-  }
+  MAO_TRY(syrk_ema(m, n, Gf, ldG, b2, (float*)st->L.data, st->L.ld, s));
+  MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, (float*)st->R.data, st->R.ld, s));
+  // 3a. E = Q^T of both bases
+  MAO_TRY(transpose(view(st->QL.data, st->QL.ld), view(R.EL, R.ldm), m, m, 1, MAO_F32, s));
+  return transpose(view(st->QR.data, st->QR.ld), view(R.ER, R.ldn), n, n, 1, MAO_F32, s);
+}
+
+// SOAP after the refresh: rotations, Adam in the eigenbasis, rotation back,
+// weight update.
+mao_status soap_post(const mao_mat& W, const mao_mat& G, const mao_soap_state* st, RotBufs& R,
+                     int64_t t, const mao_soap_hparams* hp, float* update_out, hipStream_t s) {
+  const int m = (int)W.rows, n = (int)W.cols;
+  const float b1 = hp->beta1, b2 = hp->beta2;
+  const float* M = (const float*)st->M.data;
+  const int64_t ldM = st->M.ld;
+  const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
+  const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
   // 4. rotations: G~ = E_L (G E_R^T) via the transposed intermediate
   MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, nullptr, 0, R.T2t, R.ldm, s));
   MAO_TRY(nt32(m, n, m, R.EL, R.ldm, R.T2t, R.ldm, R.Gtil, R.ldn, nullptr, 0, s));
@@ -636,13 +653,262 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
   MAO_TRY(soap_adam(view(R.Gtil, R.ldn), view(R.Mtil, R.ldn), view(st->V.data, st->V.ld), m, n, b2,
                     bc1, bc2, hp->eps, s));
   // 6. back: U = Q_L (N Q_R^T)
-  MAO_TRY(nt32(m, n, n, R.Gtil, R.ldn, QR, ldQR, nullptr, 0, R.T2t, R.ldm, s));
+  MAO_TRY(nt32(m, n, n, R.Gtil, R.ldn, (const float*)st->QR.data, st->QR.ld, nullptr, 0, R.T2t,
+               R.ldm, s));
   float* U = update_out ? update_out : R.U;
   const int64_t ldU = update_out ? n : R.ldn;
-  MAO_TRY(nt32(m, n, m, QL, ldQL, R.T2t, R.ldm, U, ldU, nullptr, 0, s));
+  MAO_TRY(nt32(m, n, m, (const float*)st->QL.data, st->QL.ld, R.T2t, R.ldm, U, ldU, nullptr, 0, s));
   // 7. W update
   return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
                       hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+}
+
+mao_status check_foam_hp(const mao_foam_hparams* hp) {
+  if (!hp) MAO_FAIL(MAO_E_NULL, "hparams is NULL");
+  MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
+  if (hp->pf < 1) MAO_FAIL(MAO_E_HPARAM, "pf=%d must be >= 1", hp->pf);
+  if (!(hp->tol >= 0.f)) MAO_FAIL(MAO_E_HPARAM, "tol=%g must be >= 0", (double)hp->tol);
+  return MAO_OK;
+}
+
+mao_status validate_foam(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, int64_t t,
+                         const float* update_out, std::vector<Range>& rr) {
+  if (!st) MAO_FAIL(MAO_E_NULL, "state is NULL");
+  MAO_TRY(check_step_common(W, G, t));
+  const int64_t m = W.rows, n = W.cols;
+  MAO_TRY(check_state_mat("M", st->M, m, n));
+  MAO_TRY(check_state_mat("R", st->R, n, n));
+  MAO_TRY(check_state_mat("QR", st->QR, n, n));
+  if (!st->r || !st->c || !st->aux) MAO_FAIL(MAO_E_NULL, "r, c or aux is NULL");
+  if (((uintptr_t)st->r | (uintptr_t)st->c | (uintptr_t)st->aux) % 4 != 0) MAO_FAIL(MAO_E_LAYOUT, "r, c, aux misaligned");
+  if (update_out && ((uintptr_t)update_out % 16 != 0 || n % 4 != 0))
+    MAO_FAIL(MAO_E_LAYOUT, "update_out must be 16-byte aligned with cols %% 4 == 0");
+  for (const Range& r : {mrange(W), mrange(G), mrange(st->M), mrange(st->R), mrange(st->QR),
+                         Range{(uintptr_t)st->r, (uintptr_t)(st->r + m)},
+                         Range{(uintptr_t)st->c, (uintptr_t)(st->c + n)},
+                         Range{(uintptr_t)st->aux, (uintptr_t)(st->aux + 4)}})
+    rr.push_back(r);
+  if (update_out) rr.push_back(mat_range(update_out, 1, m, n, n, 0, 4));
+  return MAO_OK;
+}
+
+bool foam_checks(const mao_foam_hparams* hp, int64_t t) { return (t - 1) % hp->pf == 0; }
+
+// FOAM before the refresh: momentum, fp32 G and G^T, R EMA, E_R = QR^T; on a
+// criterion step also S = E_R R (the QR input) and the refresh flag.
+mao_status foam_pre(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, RotBufs& R,
+                    int64_t t, const mao_foam_hparams* hp, hipStream_t s) {
+  const int m = (int)W.rows, n = (int)W.cols;
+  const float b1 = hp->beta1, b2 = hp->beta2;
+  float* Rf = (float*)st->R.data;
+  const int64_t ldR = st->R.ld;
+  float* work = R.small + 64;
+  MAO_TRY(ema_sumsq(view(st->M.data, st->M.ld), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr,
+                    rowblocks_for(m, 1), s));
+  MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
+                             view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
+  MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s));
+  MAO_TRY(transpose(view(st->QR.data, st->QR.ld), view(R.ER, R.ldn), n, n, 1, MAO_F32, s));
+  if (!foam_checks(hp, t)) return no_check(st->aux, R.flag, s);
+  const int64_t ldS = R.ldn;
+  MAO_TRY(nt32(n, n, n, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));       // Q^T R
+  MAO_TRY(nt32(n, n, n, R.S, ldS, R.ER, R.ldn, R.D, R.ldn, nullptr, 0, s));    // Q^T R Q
+  return offdiag_check(view(R.D, R.ldn), n, hp->tol, work, st->aux, R.flag, s);
+}
+
+// FOAM after the refresh: rotation, factored moment, preconditioning,
+// rotation back, weight update.
+mao_status foam_post(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, RotBufs& R,
+                     int64_t t, const mao_foam_hparams* hp, float* update_out, hipStream_t s) {
+  const int m = (int)W.rows, n = (int)W.cols;
+  const float b1 = hp->beta1, b2 = hp->beta2;
+  float* tau = R.small;
+  float* work = R.small + 64;
+  const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
+  const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
+  // rotate: G_rot = G Q_R, M_rot = M Q_R
+  MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s));
+  MAO_TRY(nt32(m, n, n, (const float*)st->M.data, st->M.ld, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0, s));
+  const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
+  const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
+  MAO_TRY(foam_moments(view(R.Gtil, R.ldn), m, n, b2, bc2, (const float*)st->R.data, st->R.ld,
+                       st->r, st->c, work, tau, st->aux, s));
+  MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), m, n, st->r, st->c, tau, bc1, bc2, hp->eps, s));
+  float* U = update_out ? update_out : R.U;
+  const int64_t ldU = update_out ? n : R.ldn;
+  MAO_TRY(nt32(m, n, n, R.Mtil, R.ldn, (const float*)st->QR.data, st->QR.ld, U, ldU, nullptr, 0, s));
+  return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
+                      hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+}
+
+// ---- many matrices in one call: the QR refreshes grouped by size --------
+
+struct QrJobRef {
+  int mat;   // matrix index
+  int side;  // 0: L (SOAP), 1: R
+};
+
+struct QrGroup {
+  int n = 0;
+  std::vector<QrJobRef> jobs;
+  float* S = nullptr;
+  float* E = nullptr;
+  int* flags = nullptr;
+  char* work = nullptr;
+  int64_t ld = 0, sz = 0;  // leading dimension and per-job stride of S and E
+};
+
+// Carve per-matrix buffers, then the size groups (sorted by size): S and E of
+// every job, FOAM's refresh flags, the QR workspaces. Deterministic in the
+// shapes alone, so the size query and the step carve alike.
+void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<RotBufs>& R,
+                std::vector<QrGroup>& groups) {
+  R.assign(count, RotBufs{});
+  std::vector<std::pair<int, QrJobRef>> all;
+  for (int i = 0; i < count; ++i) {
+    const int m = (int)W[i].rows, n = (int)W[i].cols;
+    carve_rot(c, m, n, soap, true, R[i], false);
+    if (soap) all.push_back({m, QrJobRef{i, 0}});
+    all.push_back({n, QrJobRef{i, 1}});
+  }
+  std::stable_sort(all.begin(), all.end(),
+                   [](const std::pair<int, QrJobRef>& a, const std::pair<int, QrJobRef>& b) {
+                     return a.first < b.first;
+                   });
+  groups.clear();
+  for (const auto& e : all) {
+    if (groups.empty() || groups.back().n != e.first) {
+      groups.emplace_back();
+      groups.back().n = e.first;
+    }
+    groups.back().jobs.push_back(e.second);
+  }
+  for (QrGroup& g : groups) {
+    const int nj = (int)g.jobs.size();
+    g.ld = ws_ld(g.n);
+    g.sz = round_up((int64_t)g.n * g.ld, 64);
+    g.S = c.take<float>((size_t)nj * g.sz);
+    g.E = c.take<float>((size_t)nj * g.sz);
+    g.flags = c.take<int>((size_t)nj);
+    g.work = c.take<char>((size_t)nj * qr_work_stride(g.n));
+    for (int k = 0; k < nj; ++k) {
+      RotBufs& r = R[g.jobs[k].mat];
+      float* e = g.E + k * g.sz;
+      if (g.jobs[k].side == 0) {
+        r.EL = e;
+      } else {
+        r.ER = e;
+        if (!soap) {
+          r.S = g.S + k * g.sz;
+          r.flag = g.flags + k;
+        }
+      }
+    }
+  }
+}
+
+size_t many_ws(int count, const mao_mat* W, bool soap) {
+  Carver c(nullptr);
+  std::vector<RotBufs> R;
+  std::vector<QrGroup> groups;
+  carve_many(c, count, W, soap, R, groups);
+  return c.used + 256;
+}
+
+constexpr int kMaxMany = 4096;
+
+mao_status check_many(int32_t count, const mao_mat* W, const mao_mat* G, const void* st) {
+  if (count < 1 || count > kMaxMany) MAO_FAIL(MAO_E_SHAPE, "count=%d outside 1..%d", count, kMaxMany);
+  if (!W || !G || !st) MAO_FAIL(MAO_E_NULL, "W, G or state array is NULL");
+  return MAO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
+                     const mao_soap_hparams* hp, void* workspace, size_t workspace_bytes,
+                     float* update_out, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MAO_TRY(check_soap_hp(hp));
+  std::vector<Range> rr;
+  MAO_TRY(validate_soap(W, G, st, t, update_out, rr));
+  MAO_TRY(check_no_overlap(rr));
+  const int m = (int)W.rows, n = (int)W.cols;
+  MAO_TRY(check_workspace(workspace, workspace_bytes, soap_workspace_size(m, n, hp)));
+  Carver c(workspace);
+  RotBufs R;
+  carve_rot(c, m, n, true, true, R);
+  MAO_TRY(soap_pre(W, G, st, R, hp, s));
+  // 3b. refresh: Q <- qr(F Q); S = (F Q)^T = Q^T F stored row-major
+  if (soap_refresh(hp, t)) {
+    const int64_t ldS = ws_ld(std::max(m, n));
+    MAO_TRY(nt32(m, m, m, R.EL, R.ldm, (const float*)st->L.data, st->L.ld, R.S, ldS, nullptr, 0, s));
+    MAO_TRY(qr_core(R.S, ldS, m, R.EL, R.ldm, (float*)st->QL.data, st->QL.ld, R.qr, nullptr, s));
+    MAO_TRY(nt32(n, n, n, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, ldS, nullptr, 0, s));
+    MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, nullptr, s));
+  }
+  return soap_post(W, G, st, R, t, hp, update_out, s);
+}
+
+size_t soap_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_soap_hparams* hp) {
+  if (!hp || !W || count < 1 || count > kMaxMany) return 0;
+  for (int i = 0; i < count; ++i)
+    if (W[i].rows < 1 || W[i].cols < 1) return 0;
+  return many_ws(count, W, true);
+}
+
+mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
+                          const mao_soap_state* st, int64_t t, const mao_soap_hparams* hp,
+                          void* workspace, size_t workspace_bytes, float* const* update_out,
+                          void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MAO_TRY(check_soap_hp(hp));
+  MAO_TRY(check_many(count, W, G, st));
+  std::vector<Range> rr;
+  for (int i = 0; i < count; ++i)
+    MAO_TRY(validate_soap(W[i], G[i], &st[i], t, update_out ? update_out[i] : nullptr, rr));
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, true)));
+  Carver c(workspace);
+  std::vector<RotBufs> R;
+  std::vector<QrGroup> groups;
+  carve_many(c, count, W, true, R, groups);
+  for (int i = 0; i < count; ++i) MAO_TRY(soap_pre(W[i], G[i], &st[i], R[i], hp, s));
+  if (soap_refresh(hp, t)) {
+    for (QrGroup& g : groups) {
+      const int nj = (int)g.jobs.size();
+      std::vector<float*> q(nj);
+      std::vector<int64_t> ldq(nj);
+      for (int k = 0; k < nj; ++k) {
+        const int i = g.jobs[k].mat;
+        const bool left = g.jobs[k].side == 0;
+        const mao_mat& F = left ? st[i].L : st[i].R;
+        const mao_mat& Q = left ? st[i].QL : st[i].QR;
+        MAO_TRY(nt32(g.n, g.n, g.n, g.E + k * g.sz, g.ld, (const float*)F.data, F.ld, g.S + k * g.sz,
+                     g.ld, nullptr, 0, s));
+        q[k] = (float*)Q.data;
+        ldq[k] = Q.ld;
+      }
+      QrBatch b;
+      b.n = g.n;
+      b.njob = nj;
+      b.S = g.S;
+      b.ldS = g.ld;
+      b.sS = g.sz;
+      b.E = g.E;
+      b.ldE = g.ld;
+      b.sE = g.sz;
+      b.Q = q.data();
+      b.ldQ = ldq.data();
+      b.work = g.work;
+      MAO_TRY(qr_core_batched(b, s));
+    }
+  }
+  for (int i = 0; i < count; ++i)
+    MAO_TRY(soap_post(W[i], G[i], &st[i], R[i], t, hp, update_out ? update_out[i] : nullptr, s));
+  return MAO_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -659,67 +925,75 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
                      const mao_foam_hparams* hp, void* workspace, size_t workspace_bytes,
                      float* update_out, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (!st || !hp) MAO_FAIL(MAO_E_NULL, "state or hparams is NULL");
-  MAO_TRY(check_step_common(W, G, t));
-  MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
-  if (hp->pf < 1) MAO_FAIL(MAO_E_HPARAM, "pf=%d must be >= 1", hp->pf);
-  if (!(hp->tol >= 0.f)) MAO_FAIL(MAO_E_HPARAM, "tol=%g must be >= 0", (double)hp->tol);
-  const int m = (int)W.rows, n = (int)W.cols;
-  MAO_TRY(check_state_mat("M", st->M, m, n));
-  MAO_TRY(check_state_mat("R", st->R, n, n));
-  MAO_TRY(check_state_mat("QR", st->QR, n, n));
-  if (!st->r || !st->c || !st->aux) MAO_FAIL(MAO_E_NULL, "r, c or aux is NULL");
-  if (((uintptr_t)st->r | (uintptr_t)st->c | (uintptr_t)st->aux) % 4 != 0) MAO_FAIL(MAO_E_LAYOUT, "r, c, aux misaligned");
-  if (update_out && ((uintptr_t)update_out % 16 != 0 || n % 4 != 0))
-    MAO_FAIL(MAO_E_LAYOUT, "update_out must be 16-byte aligned with cols %% 4 == 0");
-  std::vector<Range> rr = {mrange(W), mrange(G), mrange(st->M), mrange(st->R), mrange(st->QR),
-                           Range{(uintptr_t)st->r, (uintptr_t)(st->r + m)},
-                           Range{(uintptr_t)st->c, (uintptr_t)(st->c + n)},
-                           Range{(uintptr_t)st->aux, (uintptr_t)(st->aux + 4)}};
-  if (update_out) rr.push_back(mat_range(update_out, 1, m, n, n, 0, 4));
+  MAO_TRY(check_foam_hp(hp));
+  std::vector<Range> rr;
+  MAO_TRY(validate_foam(W, G, st, t, update_out, rr));
   MAO_TRY(check_no_overlap(rr));
+  const int m = (int)W.rows, n = (int)W.cols;
   MAO_TRY(check_workspace(workspace, workspace_bytes, foam_workspace_size(m, n, hp)));
-
   Carver c(workspace);
   RotBufs R;
   carve_rot(c, m, n, false, true, R);
-  const float b1 = hp->beta1, b2 = hp->beta2;
-  float* M = (float*)st->M.data;
-  float* Rf = (float*)st->R.data;
-  float* QR = (float*)st->QR.data;
-  const int64_t ldM = st->M.ld, ldR = st->R.ld, ldQR = st->QR.ld;
-  float* tau = R.small;
-  float* work = R.small + 64;
+  MAO_TRY(foam_pre(W, G, st, R, t, hp, s));
+  if (foam_checks(hp, t))
+    MAO_TRY(qr_core(R.S, R.ldn, n, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, R.flag, s));
+  return foam_post(W, G, st, R, t, hp, update_out, s);
+}
 
-  MAO_TRY(ema_sumsq(view(M, ldM), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr, rowblocks_for(m, 1), s));
-  const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
-  const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
-  MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
-                             view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
-  MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s));
-  MAO_TRY(transpose(view(QR, ldQR), view(R.ER, R.ldn), n, n, 1, MAO_F32, s));
-  if ((t - 1) % hp->pf == 0) {
-    const int64_t ldS = R.ldn;
-    MAO_TRY(nt32(n, n, n, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));       // Q^T R
-    MAO_TRY(nt32(n, n, n, R.S, ldS, R.ER, R.ldn, R.D, R.ldn, nullptr, 0, s));    // Q^T R Q
-    MAO_TRY(offdiag_check(view(R.D, R.ldn), n, hp->tol, work, st->aux, R.flag, s));
-    MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, QR, ldQR, R.qr, R.flag, s));
-  } else {
-    MAO_TRY(no_check(st->aux, R.flag, s));
+size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_foam_hparams* hp) {
+  if (!hp || !W || count < 1 || count > kMaxMany) return 0;
+  for (int i = 0; i < count; ++i)
+    if (W[i].rows < 1 || W[i].cols < 1) return 0;
+  return many_ws(count, W, false);
+}
+
+mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
+                          const mao_foam_state* st, int64_t t, const mao_foam_hparams* hp,
+                          void* workspace, size_t workspace_bytes, float* const* update_out,
+                          void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MAO_TRY(check_foam_hp(hp));
+  MAO_TRY(check_many(count, W, G, st));
+  std::vector<Range> rr;
+  for (int i = 0; i < count; ++i)
+    MAO_TRY(validate_foam(W[i], G[i], &st[i], t, update_out ? update_out[i] : nullptr, rr));
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, false)));
+  Carver c(workspace);
+  std::vector<RotBufs> R;
+  std::vector<QrGroup> groups;
+  carve_many(c, count, W, false, R, groups);
+  for (int i = 0; i < count; ++i) MAO_TRY(foam_pre(W[i], G[i], &st[i], R[i], t, hp, s));
+  if (foam_checks(hp, t)) {
+    for (QrGroup& g : groups) {
+      const int nj = (int)g.jobs.size();
+      std::vector<float*> q(nj);
+      std::vector<int64_t> ldq(nj);
+      for (int k = 0; k < nj; ++k) {
+        const int i = g.jobs[k].mat;
+        q[k] = (float*)st[i].QR.data;
+        ldq[k] = st[i].QR.ld;
+      }
+      QrBatch b;
+      b.n = g.n;
+      b.njob = nj;
+      b.S = g.S;
+      b.ldS = g.ld;
+      b.sS = g.sz;
+      b.E = g.E;
+      b.ldE = g.ld;
+      b.sE = g.sz;
+      b.Q = q.data();
+      b.ldQ = ldq.data();
+      b.pred = g.flags;
+      b.spred = 1;
+      b.work = g.work;
+      MAO_TRY(qr_core_batched(b, s));
+    }
   }
-  // rotate: G_rot = G Q_R, M_rot = M Q_R
-  MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s));
-  MAO_TRY(nt32(m, n, n, M, ldM, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0, s));
-  const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
-  const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
-  MAO_TRY(foam_moments(view(R.Gtil, R.ldn), m, n, b2, bc2, Rf, ldR, st->r, st->c, work, tau,
-                       st->aux, s));
-  MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), m, n, st->r, st->c, tau, bc1, bc2, hp->eps, s));
-  float* U = update_out ? update_out : R.U;
-  const int64_t ldU = update_out ? n : R.ldn;
-  MAO_TRY(nt32(m, n, n, R.Mtil, R.ldn, QR, ldQR, U, ldU, nullptr, 0, s));
-  return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
-                      hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+  for (int i = 0; i < count; ++i)
+    MAO_TRY(foam_post(W[i], G[i], &st[i], R[i], t, hp, update_out ? update_out[i] : nullptr, s));
+  return MAO_OK;
 }
 
 // ---------------------------------------------------------------------------

@@ -29,6 +29,7 @@ struct GemmProblem {
   void* Dt;          // N x M (transposed copy of D) or nullptr
   const float* row_scale;  // D row i multiplied by row_scale[i] (or nullptr)
   const int* pred;   // skip the problem when *pred == 0 (or nullptr)
+  int64_t srs, spred;  // batch strides of row_scale and pred (elements; 0: shared)
   int64_t lda, ldb, ldc0, ldd, lddt;
   int64_t sA, sB, sC0, sD, sDt;  // batch strides (elements)
   float alpha, beta;

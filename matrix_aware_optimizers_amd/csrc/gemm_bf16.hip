@@ -82,8 +82,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   int pi, local;
   xcd_tile(args, blockIdx.x, pi, local);
   const GemmProblem& P = args.p[pi];
-  if (P.pred != nullptr && *P.pred == 0) return;
   const int b = local / P.tiles_per_batch;
+  if (P.pred != nullptr && P.pred[b * P.spred] == 0) return;
   local -= b * P.tiles_per_batch;
   int tm, tn;
   const bool syrk = (P.flags & GF_SYRK) != 0;
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   const int64_t ldt = syrk ? P.ldd : P.lddt;
   const void* C0 = P.C0 ? (const void*)((const char*)P.C0 + (int64_t)b * P.sC0 * csz) : nullptr;
   const float alpha = P.alpha, beta = P.beta;
-  const float* rs = P.row_scale;
+  const float* rs = P.row_scale ? P.row_scale + b * P.srs : nullptr;
   // A tiled D is written whole, pad included (the pad of every operand is
   // zero, so it stays zero); a row-major D or Dt stops at M x N.
   const bool dt32 = (P.flags & GF_D_T32) != 0;

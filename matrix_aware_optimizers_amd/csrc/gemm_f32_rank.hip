@@ -37,8 +37,8 @@ __global__ __launch_bounds__(256) void gemm_f32_rank_kernel(GemmArgs args) {
   int pi, local;
   xcd_tile(args, blockIdx.x, pi, local);
   const GemmProblem& P = args.p[pi];
-  if (P.pred != nullptr && *P.pred == 0) return;
   const int b = local / P.tiles_per_batch;
+  if (P.pred != nullptr && P.pred[b * P.spred] == 0) return;
   local -= b * P.tiles_per_batch;
   int tm, tn;
   {
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void gemm_f32_rank_kernel(GemmArgs args) {
   ea.C0 = P.C0 ? (const void*)((const char*)P.C0 + (int64_t)b * P.sC0 * csz) : nullptr;
   ea.ldc0 = P.ldc0;
   ea.c32 = c32;
-  ea.rs = P.row_scale;
+  ea.rs = P.row_scale ? P.row_scale + b * P.srs : nullptr;
   ea.D = P.D ? (void*)((char*)P.D + (int64_t)b * P.sD * dsz) : nullptr;
   ea.ldd = P.ldd;
   ea.d32 = d32;

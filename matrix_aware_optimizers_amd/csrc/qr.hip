@@ -81,7 +81,17 @@ __device__ void grid_barrier(unsigned* counter, unsigned target, int* err) {
   __threadfence();
 }
 
-__global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelArgs a) {
+// Up to kQrMaxJobs same-size panels per launch: job jb owns workgroups
+// [jb G, (jb + 1) G); its barriers count only its own workgroups.
+constexpr int kQrMaxJobs = 16;
+struct PanelBatch {
+  PanelArgs a[kQrMaxJobs];
+  int njob;
+};
+
+__global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
+  const int G = gridDim.x / B.njob, jb = blockIdx.x / G;
+  const PanelArgs& a = B.a[jb];
   if (a.pred != nullptr && *a.pred == 0) return;
   if (a.pred2 != nullptr && *a.pred2 == 0) return;
   __shared__ float X[NB][LDX];
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelArgs a) {
   __shared__ float qs[4][NB];
   __shared__ float tot[NB], dgv[NB], taus[NB], betas[NB];
 
-  const int t = threadIdx.x, g = blockIdx.x, G = gridDim.x;
+  const int t = threadIdx.x, g = blockIdx.x - jb * G;
   const int n = a.n, j0 = a.j0, nb = a.nb;
   const int r = j0 + g * TPB + t;
   const bool valid = r < n;
@@ -285,7 +295,15 @@ __device__ __forceinline__ double lane_d(double v, int l) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-__global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
+struct CholBatch {
+  CholArgs a[kQrMaxJobs];
+  int njob;
+};
+static_assert(sizeof(CholBatch) <= 4096 && sizeof(PanelBatch) <= 4096, "kernel argument size");
+
+__global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
+  const int G = gridDim.x / B.njob, jb = blockIdx.x / G;
+  const CholArgs& a = B.a[jb];
   if (a.pred != nullptr && *a.pred == 0) return;
   __shared__ float X[NB][LDX];      // current Y (fp32), later V
   __shared__ __attribute__((aligned(16))) double Gs[NB][LDG];  // Gram / LU work
@@ -296,7 +314,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholArgs a) {
   __shared__ double red64[TPB];
   __shared__ int bad;
 
-  const int t = threadIdx.x, g = blockIdx.x, G = gridDim.x;
+  const int t = threadIdx.x, g = blockIdx.x - jb * G;
   const int n = a.n, j0 = a.j0, nb = a.nb, len = n - j0;
   const int r = j0 + g * TPB + t;
   const bool valid = r < n;
@@ -626,8 +644,12 @@ constexpr int KSPLIT = 4;
 
 __global__ __launch_bounds__(256) void sum_parts_kernel(float* out, const float* parts,
                                                         int64_t part_stride, int nparts,
-                                                        int64_t count, const int* pred) {
-  if (pred != nullptr && *pred == 0) return;
+                                                        int64_t count, int64_t job_stride,
+                                                        const int* pred, int64_t spred) {
+  const int jb = blockIdx.y;
+  if (pred != nullptr && pred[jb * spred] == 0) return;
+  out += jb * job_stride;
+  parts += jb * job_stride;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
        i += (int64_t)gridDim.x * 256) {
     float s = parts[i];
@@ -636,13 +658,22 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(float* out, const float*
   }
 }
 
-mao_status skinny_product(int M, int nb, int K, const float* A, int64_t lda, const float* B,
-                          int64_t ldb, float* W, float* parts, const int* pred, hipStream_t stream) {
+// W_j = A_j B_j^T for njob jobs at strides sA, sB (elements); W and its split-K
+// partials at stride sW per job.
+mao_status skinny_product(int M, int nb, int K, const float* A, int64_t lda, int64_t sA,
+                          const float* B, int64_t ldb, int64_t sB, float* W, float* parts,
+                          int64_t sW, int njob, const int* pred, int64_t spred,
+                          hipStream_t stream) {
   const int chunk = (int)round_up((K + KSPLIT - 1) / KSPLIT, 64);
   const int nparts = (K + chunk - 1) / chunk;
   if (nparts <= 1 || M < 1024) {
     GemmProblem p1 = gemm_problem(M, nb, K, 1.f, A, lda, B, ldb, 0.f, nullptr, 0, W, NB, GF_D_F32);
+    p1.batch = njob;
+    p1.sA = sA;
+    p1.sB = sB;
+    p1.sD = sW;
     p1.pred = pred;
+    p1.spred = spred;
     return launch_gemm(MAO_F32, &p1, 1, stream, TAG_QR);
   }
   GemmProblem pr[KSPLIT];
@@ -651,13 +682,18 @@ mao_status skinny_product(int M, int nb, int K, const float* A, int64_t lda, con
     const int k0 = q * chunk, kc = std::min(chunk, K - k0);
     pr[q] = gemm_problem(M, nb, kc, 1.f, A + k0, lda, B + k0, ldb, 0.f, nullptr, 0,
                          parts + q * stride, NB, GF_D_F32);
+    pr[q].batch = njob;
+    pr[q].sA = sA;
+    pr[q].sB = sB;
+    pr[q].sD = sW;
     pr[q].pred = pred;
+    pr[q].spred = spred;
   }
   MAO_TRY(launch_gemm(MAO_F32, pr, nparts, stream, TAG_QR));
   const int64_t count = (int64_t)M * NB;
   const int blocks = (int)std::min<int64_t>(1024, (count + 255) / 256);
-  hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks), dim3(256), 0, stream, W, parts, stride,
-                     nparts, count, pred);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks, njob), dim3(256), 0, stream, W, parts, stride,
+                     nparts, count, sW, pred, spred);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }
@@ -713,14 +749,45 @@ size_t qr_work_bytes(int n) {
   return c.used + 256;
 }
 
-mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout, int64_t ldQ,
-                   QrWork& w, const int* pred, hipStream_t stream) {
-  const int np = panels(n);
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, w.counters, 2 * np, w.err);
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, (unsigned*)w.fail, np, w.err);
-  MAO_LAUNCH_CHECK();
+size_t qr_work_stride(int n) { return align_up(qr_work_bytes(n), 256); }
 
-  // offsets of the packed panels
+namespace {
+
+// Jobs whose panel grids fit on the device together (one workgroup per CU
+// for the panel kernels' LDS footprint), capped by the launch table.
+int jobs_per_launch(int G) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0, b1 = 0, b2 = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, qr_panel_chol_kernel, TPB, 0) != hipSuccess) b1 = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b2, qr_panel_kernel, TPB, 0) != hipSuccess) b2 = 1;
+    cached[dev] = std::max(1, cus * std::max(1, std::min(b1, b2)));
+  }
+  return std::max(1, std::min(kQrMaxJobs, cached[dev] / std::max(G, 1)));
+}
+
+}  // namespace
+
+mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
+  const int n = b.n, nj = b.njob;
+  if (nj <= 0) return MAO_OK;
+  const int np = panels(n);
+  const size_t wst = qr_work_stride(n);
+  const int64_t wsf = (int64_t)(wst / sizeof(float));  // job stride of work, in floats
+  std::vector<QrWork> w(nj);
+  for (int j = 0; j < nj; ++j) {
+    Carver c(b.work + (size_t)j * wst);
+    w[j] = carve_qr_work(c, n);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, w[j].counters, 2 * np, w[j].err);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, (unsigned*)w[j].fail, np, w[j].err);
+  }
+  MAO_LAUNCH_CHECK();
+  auto job_pred = [&](int j) -> const int* { return b.pred ? b.pred + j * b.spred : nullptr; };
+
+  // offsets of the packed panels (the same in every job's workspace)
   int64_t voff = 0, zoff = 0;
   std::vector<int64_t> vo(np), zo(np);
   for (int p = 0; p < np; ++p) {
@@ -731,86 +798,151 @@ mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Q
     zoff += round_up((int64_t)len * NB, 64);
   }
 
+  const int G = max_groups(n);
+  const int per = jobs_per_launch(G);
   for (int p = 0; p < np; ++p) {
     const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
-    const int G = (len + TPB - 1) / TPB;
-    PanelArgs a;
-    a.S = S;
-    a.ldS = ldS;
-    a.n = n;
-    a.j0 = j0;
-    a.nb = nb;
-    a.V = w.vstore + vo[p];
-    a.ldV = round_up(len, 8);
-    a.Zf = w.zf;
-    a.Zo = w.zo + zo[p];
-    a.sign = w.sign;
-    a.part = w.part;
-    a.dg = w.dg;
-    a.gram = w.gram;
-    a.T = w.T;
-    a.counter = w.counters + p;
-    a.err = w.err;
-    a.pred = pred;
-    a.pred2 = w.fail + p;
-    CholArgs ca;
-    ca.S = S;
-    ca.ldS = ldS;
-    ca.n = n;
-    ca.j0 = j0;
-    ca.nb = nb;
-    ca.V = a.V;
-    ca.ldV = a.ldV;
-    ca.Zf = a.Zf;
-    ca.Zo = a.Zo;
-    ca.sign = w.sign;
-    ca.T = w.T;
-    ca.part = w.part64;
-    ca.gram = w.gram64;
-    ca.bcast = w.bcast;
-    ca.counter = w.counters + np + p;
-    ca.err = w.err;
-    ca.pred = pred;
-    ca.fail = w.fail + p;
-    void* cargs[] = {&ca};
-    MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_chol_kernel, dim3(G), dim3(TPB),
-                                             cargs, 0, stream));
-    void* kargs[] = {&a};
-    MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_kernel, dim3(G), dim3(TPB),
-                                             kargs, 0, stream));
+    const int Gp = (len + TPB - 1) / TPB;
+    for (int c0 = 0; c0 < nj; c0 += per) {
+      const int cn = std::min(per, nj - c0);
+      CholBatch cb;
+      PanelBatch pb;
+      cb.njob = pb.njob = cn;
+      for (int q = 0; q < cn; ++q) {
+        const int j = c0 + q;
+        QrWork& wj = w[j];
+        PanelArgs& a = pb.a[q];
+        a.S = b.S + j * b.sS;
+        a.ldS = b.ldS;
+        a.n = n;
+        a.j0 = j0;
+        a.nb = nb;
+        a.V = wj.vstore + vo[p];
+        a.ldV = round_up(len, 8);
+        a.Zf = wj.zf;
+        a.Zo = wj.zo + zo[p];
+        a.sign = wj.sign;
+        a.part = wj.part;
+        a.dg = wj.dg;
+        a.gram = wj.gram;
+        a.T = wj.T;
+        a.counter = wj.counters + p;
+        a.err = wj.err;
+        a.pred = job_pred(j);
+        a.pred2 = wj.fail + p;
+        CholArgs& ca = cb.a[q];
+        ca.S = a.S;
+        ca.ldS = a.ldS;
+        ca.n = n;
+        ca.j0 = j0;
+        ca.nb = nb;
+        ca.V = a.V;
+        ca.ldV = a.ldV;
+        ca.Zf = a.Zf;
+        ca.Zo = a.Zo;
+        ca.sign = wj.sign;
+        ca.T = wj.T;
+        ca.part = wj.part64;
+        ca.gram = wj.gram64;
+        ca.bcast = wj.bcast;
+        ca.counter = wj.counters + np + p;
+        ca.err = wj.err;
+        ca.pred = a.pred;
+        ca.fail = wj.fail + p;
+      }
+      void* cargs[] = {&cb};
+      MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_chol_kernel, dim3(Gp * cn),
+                                               dim3(TPB), cargs, 0, stream));
+      void* kargs[] = {&pb};
+      MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_kernel, dim3(Gp * cn),
+                                               dim3(TPB), kargs, 0, stream));
+    }
     const int mt = n - j0 - nb;
     if (mt > 0) {
-      float* Strail = S + (int64_t)(j0 + nb) * ldS + j0;
+      float* Strail = b.S + (int64_t)(j0 + nb) * b.ldS + j0;
       // W = S_trail V^T   (mt x nb)
-      MAO_TRY(skinny_product(mt, nb, len, Strail, ldS, a.V, a.ldV, w.wbuf, w.wparts, pred, stream));
+      MAO_TRY(skinny_product(mt, nb, len, Strail, b.ldS, b.sS, w[0].vstore + vo[p], round_up(len, 8),
+                             wsf, w[0].wbuf, w[0].wparts, wsf, nj, b.pred, b.spred, stream));
       // S_trail -= W Zf^T  (mt x len)
-      GemmProblem p2 = gemm_problem(mt, len, nb, -1.f, w.wbuf, NB, w.zf, NB, 1.f, Strail, ldS,
-                                    Strail, ldS, GF_D_F32 | GF_C0_F32);
-      p2.pred = pred;
+      GemmProblem p2 = gemm_problem(mt, len, nb, -1.f, w[0].wbuf, NB, w[0].zf, NB, 1.f, Strail,
+                                    b.ldS, Strail, b.ldS, GF_D_F32 | GF_C0_F32);
+      p2.batch = nj;
+      p2.sA = p2.sB = wsf;
+      p2.sC0 = p2.sD = b.sS;
+      p2.pred = b.pred;
+      p2.spred = b.spred;
       MAO_TRY(launch_gemm(MAO_F32, &p2, 1, stream, TAG_QR));
     }
   }
 
   // explicit Q: E = Q^T, backward accumulation
-  MAO_TRY(fill_identity(view(E, ldE), n, pred, stream));
+  for (int j = 0; j < nj; ++j)
+    MAO_TRY(fill_identity(view(b.E + j * b.sE, b.ldE), n, job_pred(j), stream));
   for (int p = np - 1; p >= 0; --p) {
     const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
-    float* Esub = E + (int64_t)j0 * ldE + j0;
-    MAO_TRY(skinny_product(len, nb, len, Esub, ldE, w.vstore + vo[p], round_up(len, 8), w.wbuf,
-                           w.wparts, pred, stream));
-    GemmProblem p2 = gemm_problem(len, len, nb, -1.f, w.wbuf, NB, w.zo + zo[p], NB, 1.f, Esub, ldE,
-                                  Esub, ldE, GF_D_F32 | GF_C0_F32);
-    p2.pred = pred;
-    if (p == 0) {
-      p2.row_scale = w.sign;
-      if (Qout) {
-        p2.Dt = Qout;
-        p2.lddt = ldQ;
-      }
+    float* Esub = b.E + (int64_t)j0 * b.ldE + j0;
+    MAO_TRY(skinny_product(len, nb, len, Esub, b.ldE, b.sE, w[0].vstore + vo[p], round_up(len, 8),
+                           wsf, w[0].wbuf, w[0].wparts, wsf, nj, b.pred, b.spred, stream));
+    GemmProblem p2 = gemm_problem(len, len, nb, -1.f, w[0].wbuf, NB, w[0].zo + zo[p], NB, 1.f,
+                                  Esub, b.ldE, Esub, b.ldE, GF_D_F32 | GF_C0_F32);
+    p2.batch = nj;
+    p2.sA = p2.sB = wsf;
+    p2.sC0 = p2.sD = b.sE;
+    p2.pred = b.pred;
+    p2.spred = b.spred;
+    if (p != 0) {
+      MAO_TRY(launch_gemm(MAO_F32, &p2, 1, stream, TAG_QR));
+      continue;
     }
-    MAO_TRY(launch_gemm(MAO_F32, &p2, 1, stream, TAG_QR));
+    // last block: column signs, and each job's Q written as the transposed copy
+    p2.row_scale = w[0].sign;
+    p2.srs = wsf;
+    bool anyq = false;
+    for (int j = 0; j < nj; ++j) anyq = anyq || (b.Q && b.Q[j]);
+    if (!anyq) {
+      MAO_TRY(launch_gemm(MAO_F32, &p2, 1, stream, TAG_QR));
+      continue;
+    }
+    for (int c0 = 0; c0 < nj; c0 += kMaxProblems) {
+      const int cn = std::min(kMaxProblems, nj - c0);
+      GemmProblem pq[kMaxProblems];
+      for (int q = 0; q < cn; ++q) {
+        const int j = c0 + q;
+        pq[q] = p2;
+        pq[q].batch = 1;
+        pq[q].A = w[j].wbuf;
+        pq[q].B = w[j].zo + zo[p];
+        pq[q].C0 = pq[q].D = Esub + j * b.sE;
+        pq[q].row_scale = w[j].sign;
+        pq[q].pred = job_pred(j);
+        pq[q].spred = 0;
+        if (b.Q && b.Q[j]) {
+          pq[q].Dt = b.Q[j];
+          pq[q].lddt = b.ldQ[j];
+        }
+      }
+      MAO_TRY(launch_gemm(MAO_F32, pq, cn, stream, TAG_QR));
+    }
   }
   return MAO_OK;
+}
+
+mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout, int64_t ldQ,
+                   QrWork& w, const int* pred, hipStream_t stream) {
+  QrBatch b;
+  b.n = n;
+  b.njob = 1;
+  b.S = S;
+  b.ldS = ldS;
+  b.E = E;
+  b.ldE = ldE;
+  float* qs[1] = {Qout};
+  int64_t lq[1] = {ldQ};
+  b.Q = qs;
+  b.ldQ = lq;
+  b.pred = pred;
+  b.work = (char*)w.vstore;  // the first block carved by carve_qr_work
+  return qr_core_batched(b, stream);
 }
 
 }  // namespace mao

@@ -178,3 +178,53 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
                            2, None) == 9  # K x N B needs bf16
     assert lib.mao_gemm_nt(4, 12, 4, 1.0, FAKE, 8, FAKE + 4096, 8, 1, 0.0, None, 0, FAKE + 8192,
                            16, 2, None) == 4  # K x N B: ldb < N
+
+
+@needs_no_gpu
+def test_many_matrix_validation_codes():
+    lib = mao.load()
+    m, n = 8, 16
+    sh = mao.soap_hparams()
+    fh = mao.foam_hparams()
+
+    def soap_st(base):
+        return mao.SoapStateC(_mat(base + (1 << 20), m, n, n), _mat(base + (2 << 20), m, n, n),
+                              _mat(base + (3 << 20), m, m, 8), _mat(base + (4 << 20), n, n, n),
+                              _mat(base + (5 << 20), m, m, 8), _mat(base + (6 << 20), n, n, n))
+
+    b0, b1 = FAKE, FAKE + (64 << 20)
+    W = (mao.Mat * 2)(_mat(b0, m, n, n), _mat(b1, m, n, n))
+    G = (mao.Mat * 2)(_mat(b0 + (7 << 20), m, n, n), _mat(b1 + (7 << 20), m, n, n))
+    S = (mao.SoapStateC * 2)(soap_st(b0), soap_st(b1))
+    need = lib.soap_step_many_workspace_size(2, W, ctypes.byref(sh))
+    assert need > lib.soap_workspace_size(m, n, ctypes.byref(sh))
+    assert lib.soap_step_many_workspace_size(0, W, ctypes.byref(sh)) == 0
+    ws = ctypes.c_void_p(FAKE + (1 << 30))
+    assert lib.soap_step_many(0, W, G, S, 1, ctypes.byref(sh), ws, need, None, None) == E_SHAPE
+    assert lib.soap_step_many(2, None, G, S, 1, ctypes.byref(sh), ws, need, None, None) == E_NULL
+    assert lib.soap_step_many(2, W, G, S, 1, ctypes.byref(sh), ws, need - 1, None,
+                              None) == E_WORKSPACE
+    # the second matrix's momentum on the first one's weights
+    S2 = (mao.SoapStateC * 2)(soap_st(b0), soap_st(b1))
+    S2[1].M = _mat(b0, m, n, n)
+    assert lib.soap_step_many(2, W, G, S2, 1, ctypes.byref(sh), ws, need, None, None) == E_ALIAS
+    # a shape error in the second matrix
+    S3 = (mao.SoapStateC * 2)(soap_st(b0), soap_st(b1))
+    S3[1].L = _mat(b1 + (3 << 20), n, n, n)
+    assert lib.soap_step_many(2, W, G, S3, 1, ctypes.byref(sh), ws, need, None, None) == E_SHAPE
+
+    def foam_st(base):
+        return mao.FoamStateC(_mat(base + (1 << 20), m, n, n), _mat(base + (4 << 20), n, n, n),
+                              _mat(base + (6 << 20), n, n, n), base + (8 << 20), base + (9 << 20),
+                              base + (10 << 20))
+
+    F = (mao.FoamStateC * 2)(foam_st(b0), foam_st(b1))
+    fneed = lib.foam_step_many_workspace_size(2, W, ctypes.byref(fh))
+    assert fneed > lib.foam_workspace_size(m, n, ctypes.byref(fh))
+    assert lib.foam_step_many(2, W, G, F, 1, ctypes.byref(mao.foam_hparams(pf=0)), ws, fneed,
+                              None, None) == E_HPARAM
+    F2 = (mao.FoamStateC * 2)(foam_st(b0), foam_st(b1))
+    F2[0].r = None
+    assert lib.foam_step_many(2, W, G, F2, 1, ctypes.byref(fh), ws, fneed, None, None) == E_NULL
+    assert lib.foam_step_many(4097, W, G, F, 1, ctypes.byref(fh), ws, fneed, None,
+                              None) == E_SHAPE

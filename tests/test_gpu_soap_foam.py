@@ -201,3 +201,96 @@ def test_adamw_flat_ragged(gpu_lib, wdt):
                           w_bound(w_expect, w_prev, lr_term))
         else:
             assert rel(to_host(W), w_ref) < 1e-6
+
+
+# ---- many matrices per call ------------------------------------------------
+
+MANY_SHAPES = [(200, 328), (328, 200), (200, 328), (96, 96), (72, 264)]
+
+
+def _many_inputs(shapes, steps, seed):
+    r = np.random.default_rng(seed)
+    ws = [(0.02 * r.standard_normal((m, n))).astype(np.float32) for m, n in shapes]
+    gs = [[(r.standard_normal((m, n)) * np.exp(0.5 * r.standard_normal((m, 1)))).astype(np.float32)
+           for _ in range(steps)] for m, n in shapes]
+    return ws, gs
+
+
+def _close(a, b, tag, tol=1e-5):
+    e = rel(to_host(a), to_host(b))
+    assert e <= tol, f"{tag}: {e}"
+
+
+@pytest.mark.parametrize("refresh_every", [1, 2])
+def test_soap_many_matches_separate_calls(gpu_lib, refresh_every):
+    """soap_step_many on matrices of several shapes (QR sizes shared across
+    matrices and sides: batched groups of 2-3 factors) gives the states and
+    updates of separate soap_step calls."""
+    import torch
+    log(f"soap many vs single, refresh every {refresh_every}")
+    steps = 3
+    ws, gs = _many_inputs(MANY_SHAPES, steps, 41)
+    Ws1 = [to_dev(w) for w in ws]
+    Ws2 = [to_dev(w) for w in ws]
+    st1 = [_soap_state_dev(m, n) for m, n in MANY_SHAPES]
+    st2 = [_soap_state_dev(m, n) for m, n in MANY_SHAPES]
+    o1 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in MANY_SHAPES]
+    o2 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in MANY_SHAPES]
+    for t in range(1, steps + 1):
+        G = [to_dev(g[t - 1]) for g in gs]
+        for i in range(len(MANY_SHAPES)):
+            gpu_lib.soap_step(Ws1[i], G[i], st1[i], t, update_out=o1[i],
+                              refresh_every=refresh_every, **HP)
+        gpu_lib.soap_step_many([(Ws2[i], G[i], st2[i]) for i in range(len(MANY_SHAPES))], t,
+                               update_out=o2, refresh_every=refresh_every, **HP)
+        torch.cuda.synchronize()
+        for i in range(len(MANY_SHAPES)):
+            for k in ("M", "V", "L", "R", "QL", "QR"):
+                _close(st2[i][k], st1[i][k], f"t={t} matrix {i} {k}")
+            _close(o2[i], o1[i], f"t={t} matrix {i} update")
+            _close(Ws2[i], Ws1[i], f"t={t} matrix {i} W", 1e-6)
+
+
+def _foam_state_dev_many(m, n):
+    import torch
+    return {"M": torch.zeros((m, n), dtype=torch.float32, device="cuda"),
+            "R": torch.zeros((n, n), dtype=torch.float32, device="cuda"),
+            "QR": torch.eye(n, dtype=torch.float32, device="cuda"),
+            "r": torch.zeros(m, dtype=torch.float32, device="cuda"),
+            "c": torch.zeros(n, dtype=torch.float32, device="cuda"),
+            "aux": torch.zeros(4, dtype=torch.float32, device="cuda")}
+
+
+@pytest.mark.parametrize("pf,tol", [(1, 0.0), (2, 0.1), (1, 0.5)])
+def test_foam_many_matches_separate_calls(gpu_lib, pf, tol):
+    """foam_step_many against separate foam_step calls, with the criterion
+    every step and a refresh every time (tol 0), every other step, and a
+    tolerance under which some matrices refresh and others do not (the
+    batched QR skips a job on its own device flag)."""
+    import torch
+    log(f"foam many vs single, pf={pf} tol={tol}")
+    steps = 4
+    ws, gs = _many_inputs(MANY_SHAPES, steps, 43)
+    Ws1 = [to_dev(w) for w in ws]
+    Ws2 = [to_dev(w) for w in ws]
+    st1 = [_foam_state_dev_many(m, n) for m, n in MANY_SHAPES]
+    st2 = [_foam_state_dev_many(m, n) for m, n in MANY_SHAPES]
+    o1 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in MANY_SHAPES]
+    o2 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in MANY_SHAPES]
+    refreshed = set()
+    for t in range(1, steps + 1):
+        G = [to_dev(g[t - 1]) for g in gs]
+        for i in range(len(MANY_SHAPES)):
+            gpu_lib.foam_step(Ws1[i], G[i], st1[i], t, update_out=o1[i], pf=pf, tol=tol, **HP)
+        gpu_lib.foam_step_many([(Ws2[i], G[i], st2[i]) for i in range(len(MANY_SHAPES))], t,
+                               update_out=o2, pf=pf, tol=tol, **HP)
+        torch.cuda.synchronize()
+        for i in range(len(MANY_SHAPES)):
+            a1, a2 = to_host(st1[i]["aux"]), to_host(st2[i]["aux"])
+            assert a1[1] == a2[1] and a1[3] == a2[3], f"t={t} matrix {i} aux {a1} {a2}"
+            refreshed.add(bool(a2[1]))
+            for k in ("M", "R", "QR", "r", "c"):
+                _close(st2[i][k], st1[i][k], f"t={t} matrix {i} {k}")
+            _close(o2[i], o1[i], f"t={t} matrix {i} update")
+    if tol == 0.0:
+        assert refreshed == {True}
