@@ -393,8 +393,12 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
   bool rank = in_dtype == MAO_F32 && nkm == 0;
   for (int i = 0; i < nprob; ++i) rank = rank && probs[i].K <= 64 && !(probs[i].flags & GF_SYRK);
   rank = rank && count_tiles(probs, nprob, 256) >= 16;
+  // Results at most 64 columns wide (the QR's skinny projections) keep 64 x 64
+  // tiles however many there are: a 128-wide tile would compute half zeros.
+  bool skinny = true;
+  for (int i = 0; i < nprob; ++i) skinny = skinny && probs[i].N <= 64;
   const int bm = (rank || (in_dtype == MAO_BF16 && (nkm != 0 || nt != 0 || count_tiles(probs, nprob, 256) >= 128))) ? 256
-                 : count_tiles(probs, nprob, 128) >= 512 ? 128 : 64;
+                 : (!skinny && count_tiles(probs, nprob, 128) >= 512) ? 128 : 64;
   // Longest K first: the last tiles to start are the short ones.
   int order[kMaxProblems];
   for (int i = 0; i < nprob; ++i) order[i] = i;
