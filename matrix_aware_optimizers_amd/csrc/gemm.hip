@@ -393,11 +393,15 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
   bool rank = in_dtype == MAO_F32 && nkm == 0;
   for (int i = 0; i < nprob; ++i) rank = rank && probs[i].K <= 64 && !(probs[i].flags & GF_SYRK);
   rank = rank && count_tiles(probs, nprob, 256) >= 16;
+  // without a transposed copy the 128 x 128 rank kernel (two per CU) serves
+  bool rank128 = rank;
+  for (int i = 0; i < nprob; ++i) rank128 = rank128 && probs[i].Dt == nullptr;
   // Results at most 64 columns wide (the QR's skinny projections) keep 64 x 64
   // tiles however many there are: a 128-wide tile would compute half zeros.
   bool skinny = true;
   for (int i = 0; i < nprob; ++i) skinny = skinny && probs[i].N <= 64;
-  const int bm = (rank || (in_dtype == MAO_BF16 && (nkm != 0 || nt != 0 || count_tiles(probs, nprob, 256) >= 128))) ? 256
+  const int bm = rank128 ? 128
+                 : (rank || (in_dtype == MAO_BF16 && (nkm != 0 || nt != 0 || count_tiles(probs, nprob, 256) >= 128))) ? 256
                  : (!skinny && count_tiles(probs, nprob, 128) >= 512) ? 128 : 64;
   // Longest K first: the last tiles to start are the short ones.
   int order[kMaxProblems];
@@ -423,7 +427,9 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
   const bool timed = timing_on();
   if (timed) timing_record_begin(stream, &ev);
   mao_status st;
-  if (rank)
+  if (rank128)
+    st = launch_gemm_f32_rank128(args, stream);
+  else if (rank)
     st = launch_gemm_f32_rank(args, stream);
   else if (in_dtype == MAO_BF16)
     st = bm == 256 ? launch_gemm_bf16_direct(args, stream)

@@ -89,6 +89,8 @@ mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream);
 
 // fp32 rank-k updates, k <= 64, 256 x 256 tiles (gemm_f32_rank.hip).
 mao_status launch_gemm_f32_rank(GemmArgs& args, hipStream_t stream);
+// The same with 128 x 128 tiles, two workgroups per CU; no transposed copy.
+mao_status launch_gemm_f32_rank128(GemmArgs& args, hipStream_t stream);
 
 // Instrumentation: when enabled, every contraction launch is bracketed by HIP
 // events on its stream, with its algorithmic flop count (symmetric products

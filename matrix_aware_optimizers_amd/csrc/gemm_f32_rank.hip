@@ -140,7 +140,137 @@ __global__ __launch_bounds__(256) void gemm_f32_rank_kernel(GemmArgs args) {
     staged_epilogue<true>(acc, b0, b1, b2, b3, ea);
 }
 
+// 128 x 128 tiles for the updates without a transposed copy: 70 KB of LDS,
+// so two workgroups share a CU and one's MFMAs run under the other's memory
+// traffic. Each lane requests its 64 C0 values before the operand tiles, so
+// the C0 latency is paid under the tile loads and the MFMAs; the result is
+// written straight from the accumulators (32 consecutive columns of a row
+// per half-wavefront).
+constexpr int TS = 128;
+
+__global__ __launch_bounds__(256, 2) void gemm_f32_rank128_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(16))) float As[TS * LDK];
+  __shared__ __attribute__((aligned(16))) float Bs[TS * LDK];
+
+  int pi, local;
+  xcd_tile(args, blockIdx.x, pi, local);
+  const GemmProblem& P = args.p[pi];
+  const int b = local / P.tiles_per_batch;
+  if (P.pred != nullptr && P.pred[b * P.spred] == 0) return;
+  local -= b * P.tiles_per_batch;
+  int tm, tn;
+  {
+    constexpr int G = 8;
+    const int per_group = G * P.tiles_n;
+    const int grp = local / per_group;
+    const int first_m = grp * G;
+    const int gsz = min(G, P.tiles_m - first_m);
+    const int in = local - grp * per_group;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+  }
+  const int m0 = tm * TS, n0 = tn * TS;
+  const int M = P.M, N = P.N, K = P.K;
+  const float* A = (const float*)P.A + (int64_t)b * P.sA;
+  const float* B = (const float*)P.B + (int64_t)b * P.sB;
+  const bool d32 = (P.flags & GF_D_F32) != 0;
+  const bool c32 = (P.flags & GF_C0_F32) != 0;
+  const int dsz = d32 ? 4 : 2, csz = c32 ? 4 : 2;
+  const void* C0 = P.C0 ? (const void*)((const char*)P.C0 + (int64_t)b * P.sC0 * csz) : nullptr;
+  void* D = P.D ? (void*)((char*)P.D + (int64_t)b * P.sD * dsz) : nullptr;
+  const float* rs = P.row_scale ? P.row_scale + b * P.srs : nullptr;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  // element (i, j, v) of this lane: row m0 + 64 wm + 32 i + 8 (v / 4) + 4 h + v % 4,
+  // column n0 + 64 wn + 32 j + r32
+  float cv[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + 64 * wn + 32 * j + r32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        cv[i][j][v] = (C0 && row < M && col < N) ? c0_load(C0, c32, (int64_t)row * P.ldc0 + col) : 0.f;
+      }
+    }
+
+  {
+    const int ch = (threadIdx.x & 15) * 4, r0 = threadIdx.x >> 4;
+    float4 va[8], vb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i;
+      const int gm = m0 + row, gn = n0 + row;
+      va[i] = gm < M ? load_row4(A + (int64_t)gm * P.lda, ch, K) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vb[i] = gn < N ? load_row4(B + (int64_t)gn * P.ldb, ch, K) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i;
+      *(float4*)&As[row * LDK + ch] = va[i];
+      *(float4*)&Bs[row * LDK + ch] = vb[i];
+    }
+  }
+  __syncthreads();
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const float* pa = As + (wm * 64 + r32) * LDK + 32 * h;
+  const float* pb = Bs + (wn * 64 + r32) * LDK + 32 * h;
+#pragma unroll 1
+  for (int c = 0; c < 8; ++c) {
+    if (4 * c >= K) break;  // both lane halves past k (uniform)
+    float4 fa[2], fb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fa[i] = *(const float4*)(pa + i * 32 * LDK + 4 * c);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = *(const float4*)(pb + j * 32 * LDK + 4 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float av = e == 0 ? fa[i].x : e == 1 ? fa[i].y : e == 2 ? fa[i].z : fa[i].w;
+          const float bv = e == 0 ? fb[j].x : e == 1 ? fb[j].y : e == 2 ? fb[j].z : fb[j].w;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[i][j], 0, 0, 0);
+        }
+  }
+
+  if (!D) return;
+  const float alpha = P.alpha, beta = P.beta;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + 64 * wn + 32 * j + r32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row >= M || col >= N) continue;
+        float x = alpha * acc[i][j][v] + (C0 ? beta * cv[i][j][v] : 0.f);
+        if (rs) x *= rs[row];
+        d_store(D, d32, (int64_t)row * P.ldd + col, x);
+      }
+    }
+}
+
 }  // namespace
+
+mao_status launch_gemm_f32_rank128(GemmArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_f32_rank128_kernel, dim3(args.total_tiles), dim3(256), 0, stream, args);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
 
 mao_status launch_gemm_f32_rank(GemmArgs& args, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_f32_rank_kernel, dim3(args.total_tiles), dim3(256), 0, stream, args);
