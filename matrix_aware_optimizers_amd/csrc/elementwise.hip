@@ -567,8 +567,9 @@ int grid_for(int64_t work, int per_block = 4 * kBlock) {
 }  // namespace
 
 int rowblocks_for(int64_t rows, int64_t batch) {
-  // about 2048 blocks over the whole batch, at least one row each
-  int64_t want = (2048 + batch - 1) / batch;
+  // about 8192 blocks over the whole batch, at least one row each (measured
+  // 3-4% faster on the streaming passes than 2048)
+  int64_t want = (8192 + batch - 1) / batch;
   if (want < 1) want = 1;
   if (want > rows) want = rows;
   if (want > 65535) want = 65535;
