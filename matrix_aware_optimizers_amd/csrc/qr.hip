@@ -485,14 +485,28 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
       if (g == 0 && t == 0) *a.fail = 1;
       return;  // every workgroup decided alike
     }
-    // ---- Y <- Y R^{-1} for this thread's row (forward substitution)
+    // ---- Y <- Y R^{-1} for this thread's row (forward substitution). Row
+    // k + 1 of R is requested while row k is applied (rc / rn), and the
+    // updates are pinned to their step, so the LDS latency is hidden.
 #pragma unroll
     for (int k = 0; k < NB; ++k) y[k] = (double)X[k][t];
+    {
+      double rc[NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      y[k] *= dinv[k];
+      for (int j = 1; j < NB; ++j) rc[j] = Rt[0][j];
 #pragma unroll
-      for (int j = k + 1; j < NB; ++j) y[j] = fma(-y[k], Rt[k][j], y[j]);
+      for (int k = 0; k < NB; ++k) {
+        double rn[NB];
+#pragma unroll
+        for (int j = k + 2; j < NB; ++j) rn[j] = Rt[k + 1][j];
+        y[k] *= dinv[k];
+#pragma unroll
+        for (int j = k + 1; j < NB; ++j) y[j] = fma(-y[k], rc[j], y[j]);
+#pragma unroll
+        for (int j = k + 1; j < NB; ++j) asm volatile("" : "+v"(y[j]));
+#pragma unroll
+        for (int j = k + 2; j < NB; ++j) rc[j] = rn[j];
+      }
     }
     if (pass < 2) {
       __syncthreads();
@@ -575,6 +589,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
     if (t < nb) dsg[t] = (float)a.bcast[NB * NB + t];
   }
   for (int e = t; e < NB * NB; e += TPB) Tl[e >> 6][e & 63] = a.T[e];
+  if (t < NB) dinv[t] = (t < nb) ? 1.0 / Rt[t][t] : 1.0;  // U diagonal reciprocals
   __syncthreads();
 
   // ---- rows of Y: top block from L, the rest -q D U^{-1}
@@ -584,13 +599,34 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
     double z[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) z[k] = (k < nb) ? -(double)dsg[k] * y[k] : 0.0;
+    // z <- z U^{-1}, with the same one-row-ahead requests as the solve
+    // above; a last, narrower panel keeps the columns past nb at zero
+    if (nb == NB) {
+      double uc[NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      if (k < nb) {
-        z[k] = z[k] / Rt[k][k];
+      for (int j = 1; j < NB; ++j) uc[j] = Rt[0][j];
 #pragma unroll
-        for (int j = k + 1; j < NB; ++j)
-          if (j < nb) z[j] = fma(-z[k], Rt[k][j], z[j]);
+      for (int k = 0; k < NB; ++k) {
+        double un[NB];
+#pragma unroll
+        for (int j = k + 2; j < NB; ++j) un[j] = Rt[k + 1][j];
+        z[k] = z[k] * dinv[k];
+#pragma unroll
+        for (int j = k + 1; j < NB; ++j) z[j] = fma(-z[k], uc[j], z[j]);
+#pragma unroll
+        for (int j = k + 1; j < NB; ++j) asm volatile("" : "+v"(z[j]));
+#pragma unroll
+        for (int j = k + 2; j < NB; ++j) uc[j] = un[j];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (k < nb) {
+          z[k] = z[k] * dinv[k];
+#pragma unroll
+          for (int j = k + 1; j < NB; ++j)
+            if (j < nb) z[j] = fma(-z[k], Rt[k][j], z[j]);
+        }
       }
     }
 #pragma unroll
