@@ -22,6 +22,12 @@
  *   logical sub-matrix of a fused tensor, e.g. one of Q, K, V inside a fused
  *   QKV weight ([SMB] section 3-2 (2): fused QKV is split into logical
  *   matrices before orthogonalisation).
+ * - Buffers that must be distinct (MAO_E_ALIAS otherwise) are compared byte
+ *   by byte when both have the same row pitch (ld times the element size) and
+ *   a batch stride that is a multiple of ld: column views of one wider buffer
+ *   with disjoint column ranges (the logical Q, K and V of one fused weight,
+ *   stepped as separate groups of one muon_step_batched call) are distinct.
+ *   Other pairs are compared by the byte ranges they span.
  * - Ownership: the caller owns every buffer (weights, gradients, optimizer
  *   state, workspace, outputs). The library allocates no device memory and
  *   keeps no device state between calls. Sizes of the workspace come from the

@@ -36,17 +36,36 @@ size_t dtype_size(int dt) { return dt == MAO_BF16 ? 2 : 4; }
 bool dtype_ok(int dt) { return dt == MAO_F32 || dt == MAO_BF16; }
 bool finite(float x) { return isfinite(x) != 0; }
 
+// Bytes a buffer touches: the interval [lo, hi), and for a strided matrix
+// view whose every row starts at the same offset modulo the row pitch (one
+// matrix, or a batch stride that is a multiple of the pitch) the pitch and the
+// bytes each row covers, so that column views of one wider buffer (a fused
+// QKV weight split into its logical matrices) are told apart exactly.
 struct Range {
   uintptr_t lo, hi;
+  uint64_t pitch = 0, span = 0;  // pitch 0: no row structure known
 };
 
 Range mat_range(const void* p, int64_t count, int64_t rows, int64_t cols, int64_t ld,
                 int64_t stride, size_t es) {
   const int64_t last = (count - 1) * stride + (rows - 1) * ld + cols;
-  return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(last * (int64_t)es)};
+  Range r{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(last * (int64_t)es)};
+  if (count == 1 || stride % ld == 0) {
+    r.pitch = (uint64_t)(ld * (int64_t)es);
+    r.span = (uint64_t)(cols * (int64_t)es);
+  }
+  return r;
 }
 
-bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+bool overlap(Range a, Range b) {
+  if (!(a.lo < b.hi && b.lo < a.hi)) return false;
+  if (a.pitch == 0 || a.pitch != b.pitch) return true;
+  // rows of a cover [a.lo mod pitch, + a.span) on the circle of one pitch,
+  // rows of b [b.lo mod pitch, + b.span): disjoint arcs never share a byte
+  const uint64_t P = a.pitch;
+  const uint64_t d = ((uint64_t)(b.lo % P) + P - (uint64_t)(a.lo % P)) % P;
+  return !(d >= a.span && d + b.span <= P);
+}
 
 mao_status check_mat(const char* name, const void* data, int64_t rows, int64_t cols, int64_t ld,
                      int dtype, bool f32_only) {

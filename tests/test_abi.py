@@ -11,6 +11,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import matrix_aware_optimizers_amd as mao
@@ -123,6 +124,76 @@ def test_batched_validation_codes():
     assert lib.muon_step_batched(1, Wbad, G, M, ctypes.byref(hp), ws, need, None, None) == E_LAYOUT
     Mbad = (mao.Batch * 1)(mao.Batch(FAKE + (2 << 20), 2, 8, 16, 16, 8 * 16, mao.F32))
     assert lib.muon_step_batched(1, W, G, Mbad, ctypes.byref(hp), ws, need, None, None) == E_SHAPE
+
+
+def _alias_verdict(lib, views):
+    """muon_step_batched on bf16 W views (count, rows, cols, ld, stride, offset
+    in elements), each group's G and M far away, with no workspace: E_ALIAS if
+    the W views are judged to overlap, else E_WORKSPACE (validation passed)."""
+    hp = mao.muon_hparams()
+    n = len(views)
+    Ws = (mao.Batch * n)(*[mao.Batch(FAKE + 2 * off, c, r, k, ld, st, mao.BF16)
+                           for c, r, k, ld, st, off in views])
+    Gs = (mao.Batch * n)(*[mao.Batch(FAKE + ((8 + i) << 24), c, r, k, ld, st, mao.BF16)
+                           for i, (c, r, k, ld, st, off) in enumerate(views)])
+    Ms = (mao.Batch * n)(*[mao.Batch(FAKE + ((16 + i) << 24), c, r, k, ld, st, mao.F32)
+                           for i, (c, r, k, ld, st, off) in enumerate(views)])
+    return lib.muon_step_batched(n, Ws, Gs, Ms, ctypes.byref(hp), None, 0, None, None)
+
+
+@needs_no_gpu
+def test_fused_column_views_are_not_aliases():
+    """Logical Q, K, V matrices as column views of one fused buffer (three
+    layers, leading dimension = the fused width) pass the alias check; a view
+    that takes one column of its neighbour does not."""
+    lib = mao.load()
+    width, rows, layers = 40, 8, 3
+    st = rows * width
+    q, k, v = (layers, rows, 16, width, st, 0), (layers, rows, 8, width, st, 16), \
+        (layers, rows, 8, width, st, 24)
+    assert _alias_verdict(lib, [q, k, v]) == E_WORKSPACE
+    assert _alias_verdict(lib, [q, (layers, rows, 9, width, st, 16), (layers, rows, 8, width, st, 32)]) \
+        == E_WORKSPACE
+    assert _alias_verdict(lib, [(layers, rows, 17, width, st, 0), k, v]) == E_ALIAS
+    assert _alias_verdict(lib, [q, (layers, rows, 8, width, st, 8), v]) == E_ALIAS
+
+
+@needs_no_gpu
+def test_alias_check_against_brute_force():
+    """Random pairs of strided bf16 views: the library never passes a pair that
+    shares a byte, and decides exactly when both views have the same pitch and
+    a batch stride that is a multiple of it (brute force over the bytes)."""
+    lib = mao.load()
+    r = np.random.default_rng(7)
+    exact_cases = 0
+    for _ in range(400):
+        views = []
+        for _ in range(2):
+            ld = 8 * int(r.integers(1, 5))
+            cols = int(r.integers(1, ld + 1))
+            rows = int(r.integers(1, 4))
+            count = int(r.integers(1, 3))
+            stride = rows * ld + 8 * int(r.integers(0, 3)) if count > 1 else 0
+            off = 8 * int(r.integers(0, 12))
+            views.append((count, rows, cols, ld, stride, off))
+        touched = []
+        for c, rr, k, ld, st, off in views:
+            s = set()
+            for b in range(c):
+                for i in range(rr):
+                    e0 = off + b * st + i * ld
+                    s.update(range(2 * e0, 2 * (e0 + k)))
+            touched.append(s)
+        shares = bool(touched[0] & touched[1])
+        got = _alias_verdict(lib, views)
+        assert got in (E_ALIAS, E_WORKSPACE)
+        if shares:
+            assert got == E_ALIAS, views
+        periodic = all(c == 1 or st % ld == 0 for c, rr, k, ld, st, off in views)
+        if periodic and views[0][3] == views[1][3]:
+            exact_cases += 1
+            assert (got == E_ALIAS) == shares, views
+    assert exact_cases > 50
 
 
 @needs_no_gpu

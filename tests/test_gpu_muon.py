@@ -196,6 +196,50 @@ def test_muon_tiled_coefficient_families(gpu_lib, family):
     log(f"  worst update error {worst:.2e}")
 
 
+@pytest.mark.parametrize("layers,rows,q,kv", [(3, 96, 128, 40), (6, 1024, 1024, 256)])
+def test_muon_fused_qkv_views_sixteen_iterations(gpu_lib, layers, rows, q, kv):
+    """The logical Q, K and V matrices of a fused QKV weight, passed as
+    column views (leading dimension = the fused width) of one buffer per
+    layer, and 16 iterations with a per-iteration coefficient table. Each
+    view is stepped as its own matrix; K and V are tall (transposed
+    orientation); 8 guard columns after V stay bit-identical. The larger case
+    has enough tiles to run on the tiled iterates."""
+    import torch
+    log(f"muon fused qkv views {layers}x{rows}x({q}+{kv}+{kv}), 16 iterations")
+    coeffs = [(3.4445, -4.7750, 2.0315)] * 8 + [(15 / 8, -10 / 8, 3 / 8)] * 8
+    width = q + 2 * kv + 8
+    spans = [(0, q), (q, q + kv), (q + kv, q + 2 * kv)]
+    r = np.random.default_rng(34)
+    w = bf16_round((0.02 * r.standard_normal((layers, rows, width))).astype(np.float32))
+    g = bf16_round(r.standard_normal((layers, rows, width)).astype(np.float32))
+    W, G = to_dev(w, "bf16"), to_dev(g, "bf16")
+    Mf = zeros_dev((layers, rows, width))
+    groups = [(W[:, :, a:b], G[:, :, a:b], Mf[:, :, a:b]) for a, b in spans]
+    outs = [torch.empty((layers, rows, b - a), dtype=torch.float32, device="cuda")
+            for a, b in spans]
+    gpu_lib.muon_step_batched(groups, update_out=outs, lr=LR, mu=0.95, weight_decay=WD,
+                              ns_steps=16, ns_coeffs=coeffs, ns_dtype="bf16")
+    torch.cuda.synchronize()
+    w_gpu = to_host(W)
+    assert np.array_equal(w_gpu[:, :, q + 2 * kv:], w[:, :, q + 2 * kv:])
+    assert np.all(to_host(Mf)[:, :, q + 2 * kv:] == 0)
+    worst = 0.0
+    for (a, b), out in zip(spans, outs):
+        o = to_host(out)
+        for layer in range(layers):
+            wb, gb = w[layer, :, a:b], g[layer, :, a:b]
+            _, _, upd = oracle.muon_step(wb, gb, np.zeros_like(wb), lr=LR, mu=0.95,
+                                         weight_decay=WD, ns_steps=16, coeffs=coeffs)
+            e = rel(o[layer], upd)
+            worst = max(worst, e)
+            assert e < TOL["bf16"], f"columns {a}:{b} layer {layer}: {e}"
+            lr_term = LR * (WD * wb + o[layer])
+            w_expect = wb - lr_term
+            w_exp16 = bf16_round(w_expect.astype(np.float32))
+            assert np.all(np.abs(w_gpu[layer, :, a:b] - w_exp16) <= w_bound(w_expect, wb, lr_term))
+    log(f"  worst update error {worst:.2e}")
+
+
 def test_muon_full_size_o_projection(gpu_lib):
     """The 4096x4096 O projection of the 8B layer at full size, bf16, one step
     (the shape and launch configuration the benchmark times)."""
