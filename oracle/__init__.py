@@ -22,6 +22,9 @@ Sources (page title, then section / equation):
 * "Muon+: Towards Better Muon via One Additional Normalization Step"
   (gist.science), section 2 (momentum, orthogonalisation, normalisation,
   sqrt(m/n) update).
+* Observability ("SOAP, Muon, and Beyond", sections 2-1 and 7-2; FOAM
+  review, section 3): update RMS, Newton-Schulz residual, factor Rayleigh
+  quotients, rank-1 share, basis age.
 
 Parity status of each function is stated in its module header.
 """
@@ -31,10 +34,12 @@ from .muon import (CLASSICAL_QUINTIC, muon_plus_normalize, muon_step,
 from .adamw import adamw_step
 from .soap import SoapState, soap_init, soap_step, soap_state_bytes
 from .foam import FoamState, foam_init, foam_step, foam_state_bytes, offdiag_ratio
+from .observe import basis_ages, matrix_rms, ns_residual, rank1_share, rayleigh
 
 __all__ = [
     "jacobi_svd", "polar_svd", "qr_positive", "shampoo_polar", "sym_inv_root",
     "CLASSICAL_QUINTIC", "newton_schulz", "muon_plus_normalize", "muon_update_direction",
     "muon_step", "adamw_step", "SoapState", "soap_init", "soap_step", "soap_state_bytes",
     "FoamState", "foam_init", "foam_step", "foam_state_bytes", "offdiag_ratio",
+    "matrix_rms", "ns_residual", "rayleigh", "rank1_share", "basis_ages",
 ]

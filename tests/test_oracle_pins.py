@@ -389,3 +389,77 @@ def test_pages_arithmetic():
     assert 2.0 ** -23 == pytest.approx(p["fp32"], rel=1e-2)
     bf16_eps = float(np.finfo(np.float32).eps) * 2 ** 16
     assert bf16_eps == p["bf16"]
+
+
+# ---- observability ("SOAP, Muon, and Beyond" sections 2-1 and 7-2; FOAM
+# review section 3) --------------------------------------------------------
+
+
+def _dct_rows(n):
+    """Orthonormal DCT-II matrix (rows orthonormal), closed form."""
+    k = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    c = np.sqrt(2.0 / n) * np.cos(np.pi * (2 * j + 1) * k / (2 * n))
+    c[0, :] = np.sqrt(1.0 / n)
+    return c
+
+
+def test_matrix_rms_closed_forms():
+    assert oracle.matrix_rms(np.full((7, 13), -0.25)) == pytest.approx(0.25, rel=1e-15)
+    x = np.zeros((4, 9))
+    x[2, 5] = 3.0
+    assert oracle.matrix_rms(x) == pytest.approx(3.0 / 6.0, rel=1e-15)
+
+
+def test_ns_residual_from_known_singular_values():
+    a, b = 6, 10
+    u = _dct_rows(a).T                     # a x a orthonormal
+    v = _dct_rows(b)[:a].T                 # b x a, orthonormal columns
+    s = np.array([1.0, 0.9, 1.1, 0.5, 1.0, 0.0])
+    x = u @ np.diag(s) @ v.T               # a x b with singular values s
+    want = math.sqrt(np.mean((s * s - 1.0) ** 2))
+    assert oracle.ns_residual(x) == pytest.approx(want, rel=1e-12)
+    assert oracle.ns_residual(x.T) == pytest.approx(want, rel=1e-12)     # tall: its wide view
+    assert oracle.ns_residual(2.0 * x, 0.5) == pytest.approx(want, rel=1e-12)
+    assert oracle.ns_residual(u @ v.T) < 1e-14                           # orthonormal rows
+
+
+def test_rayleigh_quotients_in_an_eigenbasis():
+    n = 8
+    q = _dct_rows(n).T
+    lam = np.array([4.0, 0.5, 2.0, 1.0, 8.0, 0.25, 3.0, 1.5])
+    f = q @ np.diag(lam) @ q.T
+    d, kappa = oracle.rayleigh(f, q)
+    assert np.allclose(d, lam, rtol=1e-12, atol=1e-14)
+    assert kappa == pytest.approx(8.0 / 0.25, rel=1e-12)
+    d_id, _ = oracle.rayleigh(f, np.eye(n))
+    assert np.allclose(d_id, np.diag(f), rtol=0, atol=0)
+    # any orthonormal basis: every quotient lies in [lambda_min, lambda_max],
+    # so the estimate never exceeds cond(f)
+    w = oracle.qr_positive(_rng(3).standard_normal((n, n)))[0]
+    d_w, k_w = oracle.rayleigh(f, w)
+    assert d_w.min() >= 0.25 - 1e-12 and d_w.max() <= 8.0 + 1e-12
+    assert k_w <= 32.0 + 1e-9
+    _, k_neg = oracle.rayleigh(-f, q)
+    assert k_neg == float("inf")
+
+
+def test_rank1_share_closed_forms():
+    r = _rng(4)
+    a, b = np.abs(r.standard_normal(9)), np.abs(r.standard_normal(5))
+    assert oracle.rank1_share(np.outer(a, b)) == pytest.approx(1.0, rel=1e-12)
+    s = np.array([3.0, 1.0, 2.0])
+    v = np.zeros((5, 3))
+    v[[0, 1, 2], [0, 1, 2]] = s
+    assert oracle.rank1_share(v) == pytest.approx(9.0 / 14.0, rel=1e-12)
+    # two disjoint rank-1 blocks: the larger block's mass over the total
+    blk = np.zeros((6, 6))
+    blk[:3, :3] = 2.0
+    blk[3:, 3:] = 1.0
+    assert oracle.rank1_share(blk) == pytest.approx(36.0 / 45.0, rel=1e-12)
+    assert oracle.rank1_share(np.zeros((3, 4))) == 0.0
+
+
+def test_basis_age_recurrence():
+    assert oracle.basis_ages([1, 0, 0, 1, 0, 0, 0]) == [0, 1, 2, 0, 1, 2, 3]
+    assert oracle.basis_ages([0, 0]) == [1, 2]
