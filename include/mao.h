@@ -352,6 +352,90 @@ MAO_API mao_status mao_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, in
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Observability: reductions over buffers the steps already hold             */
+/* ------------------------------------------------------------------------ */
+/*
+ * [SMB] section 7-2, item 4 lists what an optimizer log should carry:
+ * layer-wise update RMS, the Newton-Schulz residual, the SOAP factor
+ * condition number and the basis update age; [FOAM] section 3 reports the
+ * rank-1 share of the rotated second moment. The calls below compute these on
+ * the device into caller-owned device floats, without synchronising, like the
+ * steps (host-side validation, caller-owned workspace, fixed-order fp64
+ * reductions, bitwise repeatable).
+ */
+
+/* Workspace bytes for mao_matrix_rms over the batch X. */
+MAO_API size_t mao_matrix_rms_workspace_size(mao_batch X);
+
+/*
+ * mao_matrix_rms -- out[b] = ||X_b||_F / sqrt(rows * cols) for every matrix of
+ * the batch (count <= 65535; X bf16 or fp32). This is [SMB] section 2-1's
+ * update RMS, ||dW||_F / sqrt(|W|), when X holds the update: applied to a
+ * step's update_out (U, before the learning rate) it gives RMS(dW) / lr of
+ * the optimizer term, weight decay excluded. out: count device floats.
+ */
+MAO_API mao_status mao_matrix_rms(mao_batch X, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for mao_ns_residual over the batch O. */
+MAO_API size_t mao_ns_residual_workspace_size(mao_batch O);
+
+/*
+ * mao_ns_residual -- the Newton-Schulz residual of each matrix of the batch:
+ * with X = scale * O_b taken in its wide orientation (a = min(rows, cols)
+ * rows), out[b] = ||X X^T - I_a||_F / sqrt(a), the RMS over the singular
+ * values s_i of X of s_i^2 - 1, which is 0 exactly when X has orthonormal rows
+ * (the polar factor U V^T that the iteration approaches, [SMB] section 2-1).
+ * O: fp32 (a muon_step update_out with scale = sqrt(cols / rows) recovers the
+ * Newton-Schulz output when norm_mode is none). The a x a product runs on the
+ * fp32 MFMA path. scale: finite, nonzero. out: count device floats.
+ */
+MAO_API mao_status mao_ns_residual(mao_batch O, float scale, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for mao_rayleigh on n x n operands. */
+MAO_API size_t mao_rayleigh_workspace_size(int64_t n);
+
+/*
+ * mao_rayleigh -- Rayleigh quotients of a Kronecker factor in its current
+ * basis: diag_out[i] = q_i^T F q_i for every column q_i of Q (F, Q fp32
+ * n x n, F a SOAP L / R or a FOAM R, Q its basis Q_L / Q_R), and, when
+ * kappa_out is not NULL, kappa_out[0] = max_i d_i / min_i d_i (+inf when
+ * min_i d_i <= 0) -- the factor condition-number estimate of [SMB] section
+ * 7-2. For orthonormal Q every d_i lies in [lambda_min(F), lambda_max(F)], so
+ * the estimate never exceeds the condition number of F, and equals it when Q
+ * diagonalises F. diag_out: n device floats; kappa_out: NULL or 1 float.
+ */
+MAO_API mao_status mao_rayleigh(mao_mat F, mao_mat Q, float* diag_out, float* kappa_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for mao_rank1_share on a rows x cols matrix. */
+MAO_API size_t mao_rank1_share_workspace_size(int64_t rows, int64_t cols);
+
+/*
+ * mao_rank1_share -- out[0] = s_1(V)^2 / ||V||_F^2, the share of the squared
+ * Frobenius mass of V (fp32 m x n, e.g. SOAP's second moment V in its
+ * rotated basis) that its best rank-1 approximation captures ([FOAM]
+ * section 3: the rank-1 share that motivates factoring the rotated moment).
+ * s_1 comes from `iters` (1..1000) steps of power iteration on V^T V from the
+ * unit all-ones vector, each normalised; the estimate is ||V v||^2 for the
+ * last unit iterate v, which never exceeds the true share beyond rounding.
+ * A zero V gives 0.
+ */
+MAO_API mao_status mao_rank1_share(mao_mat V, int32_t iters, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * mao_basis_age -- steps since FOAM last refreshed its basis ([SMB] section
+ * 7-2: basis update age), kept on the device: after a foam_step, age[0] <- 0
+ * when the step refreshed (aux[1] != 0), else age[0] + 1. The caller owns the
+ * float and sets it to 0 before the first step. (For SOAP the age is
+ * (t - 1) mod refresh_every, known on the host.) aux: the foam_state aux
+ * array; age: 1 device float.
+ */
+MAO_API mao_status mao_basis_age(const float* aux, float* age, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Measurement instrumentation (not part of any optimizer step)              */
 /* ------------------------------------------------------------------------ */
 

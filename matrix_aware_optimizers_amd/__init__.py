@@ -97,6 +97,15 @@ EXPORTS = {
     "mao_qr_workspace_size": (c_size_t, [c_int64]),
     "mao_qr": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_size_t,
                          c_void_p]),
+    "mao_matrix_rms_workspace_size": (c_size_t, [Batch]),
+    "mao_matrix_rms": (c_int32, [Batch, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mao_ns_residual_workspace_size": (c_size_t, [Batch]),
+    "mao_ns_residual": (c_int32, [Batch, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mao_rayleigh_workspace_size": (c_size_t, [c_int64]),
+    "mao_rayleigh": (c_int32, [Mat, Mat, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mao_rank1_share_workspace_size": (c_size_t, [c_int64, c_int64]),
+    "mao_rank1_share": (c_int32, [Mat, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mao_basis_age": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "mao_timing_enable": (None, [c_int32]),
     "mao_timing_collect": (c_int32, [POINTER(ctypes.c_double), POINTER(c_int64),
                                      POINTER(ctypes.c_double), c_int32]),
@@ -354,6 +363,67 @@ def adamw_step(w, g, m, v, t: int, *, lr, beta1=0.9, beta2=0.95, eps=1e-8, weigh
     _check(lib.adamw_step(_ptr(w), dtype_code(w), _ptr(g), dtype_code(g), _ptr(m), _ptr(v),
                           w.numel(), t, lr, beta1, beta2, eps, weight_decay, _ptr(update_out),
                           _stream()), "adamw_step")
+
+
+def _as_batch(X):
+    return batch(X if X.dim() == 3 else X.unsqueeze(0))
+
+
+def matrix_rms(X, out=None):
+    """||X_b||_F / sqrt(rows * cols) per matrix of a 2-D or 3-D [count, rows,
+    cols] tensor (fp32 or bf16), as a device fp32 tensor of count values."""
+    import torch
+    lib = load()
+    bx = _as_batch(X)
+    if out is None:
+        out = torch.empty(bx.count, dtype=torch.float32, device=X.device)
+    buf = workspace(lib.mao_matrix_rms_workspace_size(bx), X.device)
+    _check(lib.mao_matrix_rms(bx, _ptr(out), _ptr(buf), buf.numel(), _stream()), "mao_matrix_rms")
+    return out
+
+
+def ns_residual(O, scale=1.0, out=None):
+    """||X X^T - I||_F / sqrt(a) of X = scale * O on its wide orientation, per
+    matrix of a 2-D or 3-D fp32 tensor (device fp32 tensor of count values)."""
+    import torch
+    lib = load()
+    bo = _as_batch(O)
+    if out is None:
+        out = torch.empty(bo.count, dtype=torch.float32, device=O.device)
+    buf = workspace(lib.mao_ns_residual_workspace_size(bo), O.device)
+    _check(lib.mao_ns_residual(bo, scale, _ptr(out), _ptr(buf), buf.numel(), _stream()),
+           "mao_ns_residual")
+    return out
+
+
+def rayleigh(F, Q):
+    """(d, kappa): d_i = q_i^T F q_i for the columns of Q, kappa = max d / min d
+    (device fp32 tensors)."""
+    import torch
+    lib = load()
+    n = F.shape[0]
+    d = torch.empty(n, dtype=torch.float32, device=F.device)
+    kappa = torch.empty(1, dtype=torch.float32, device=F.device)
+    buf = workspace(lib.mao_rayleigh_workspace_size(n), F.device)
+    _check(lib.mao_rayleigh(mat(F), mat(Q), _ptr(d), _ptr(kappa), _ptr(buf), buf.numel(),
+                            _stream()), "mao_rayleigh")
+    return d, kappa
+
+
+def rank1_share(V, iters=30):
+    """s_1(V)^2 / ||V||_F^2 by power iteration (device fp32 tensor of 1 value)."""
+    import torch
+    lib = load()
+    out = torch.empty(1, dtype=torch.float32, device=V.device)
+    buf = workspace(lib.mao_rank1_share_workspace_size(V.shape[0], V.shape[1]), V.device)
+    _check(lib.mao_rank1_share(mat(V), iters, _ptr(out), _ptr(buf), buf.numel(), _stream()),
+           "mao_rank1_share")
+    return out
+
+
+def basis_age(aux, age):
+    """age <- 0 if the FOAM step that wrote aux refreshed its basis, else age + 1."""
+    _check(load().mao_basis_age(_ptr(aux), _ptr(age), _stream()), "mao_basis_age")
 
 
 TIMING_TAGS = ("ns_gram", "ns_square", "ns_apply", "other", "qr")

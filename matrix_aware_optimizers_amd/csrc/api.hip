@@ -12,6 +12,7 @@
 #include "gemm.hpp"
 #include "tiled.hpp"
 #include "qr.hpp"
+#include "observe.hpp"
 
 namespace mao {
 
@@ -842,6 +843,9 @@ mao_status check_many(int32_t count, const mao_mat* W, const mao_mat* G, const v
   return MAO_OK;
 }
 
+// row blocks of the column pass of the rank-1 power iteration
+int rank1_col_blocks(int64_t rows) { return (int)std::min<int64_t>(rows, 512); }
+
 }  // namespace
 
 extern "C" {
@@ -1084,6 +1088,167 @@ mao_status mao_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n,
   QrWork w = carve_qr_work(c, (int)n);
   MAO_TRY(transpose(view((void*)P, ldp), view(S, ld), (int)n, (int)n, 1, MAO_F32, s));
   return qr_core(S, ld, (int)n, E, ld, Q, ldq, w, nullptr, s);
+}
+
+// ---- observability ---------------------------------------------------------
+
+size_t mao_matrix_rms_workspace_size(mao_batch X) {
+  if (X.count < 1 || X.rows < 1 || X.cols < 1 || X.rows > (1 << 20)) return 0;
+  Carver c(nullptr);
+  c.take<double>((size_t)X.count * obs_rowblocks(X.rows));
+  return c.used + 256;
+}
+
+mao_status mao_matrix_rms(mao_batch X, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  MAO_TRY(check_batch("X", X, false));
+  if (X.count > 65535) MAO_FAIL(MAO_E_SHAPE, "count=%lld above 65535", (long long)X.count);
+  if (!out) MAO_FAIL(MAO_E_NULL, "out is NULL");
+  if ((uintptr_t)out % 4) MAO_FAIL(MAO_E_LAYOUT, "out not 4-byte aligned");
+  std::vector<Range> rr = {batch_range(X), Range{(uintptr_t)out, (uintptr_t)(out + X.count)}};
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, mao_matrix_rms_workspace_size(X)));
+  hipStream_t s = (hipStream_t)stream;
+  Carver c(workspace);
+  const int nrb = obs_rowblocks(X.rows);
+  double* part = c.take<double>((size_t)X.count * nrb);
+  MAO_TRY(sumsq_partials(view(X.data, X.ld, X.count > 1 ? X.stride : 0), X.dtype, (int)X.rows,
+                         (int)X.cols, (int)X.count, nrb, false, part, s));
+  return finalize_rms(part, nrb, (int)X.count, (double)X.rows * (double)X.cols, out, s);
+}
+
+size_t mao_ns_residual_workspace_size(mao_batch O) {
+  if (O.count < 1 || O.rows < 1 || O.cols < 1 || O.rows > (1 << 20) || O.cols > (1 << 20))
+    return 0;
+  const int64_t a = std::min(O.rows, O.cols), b = std::max(O.rows, O.cols);
+  Carver c(nullptr);
+  c.take<float>((size_t)O.count * a * ws_ld(a));
+  if (O.rows > O.cols) c.take<float>((size_t)O.count * a * ws_ld(b));
+  c.take<double>((size_t)O.count * obs_rowblocks(a));
+  return c.used + 256;
+}
+
+mao_status mao_ns_residual(mao_batch O, float scale, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  MAO_TRY(check_batch("O", O, true));
+  if (O.count > 65535) MAO_FAIL(MAO_E_SHAPE, "count=%lld above 65535", (long long)O.count);
+  if (!out) MAO_FAIL(MAO_E_NULL, "out is NULL");
+  if ((uintptr_t)out % 4) MAO_FAIL(MAO_E_LAYOUT, "out not 4-byte aligned");
+  if (!finite(scale) || scale == 0.f) MAO_FAIL(MAO_E_HPARAM, "scale=%g", (double)scale);
+  std::vector<Range> rr = {batch_range(O), Range{(uintptr_t)out, (uintptr_t)(out + O.count)}};
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, mao_ns_residual_workspace_size(O)));
+  hipStream_t s = (hipStream_t)stream;
+  const int rows = (int)O.rows, cols = (int)O.cols, cnt = (int)O.count;
+  const bool tall = rows > cols;
+  const int a = std::min(rows, cols), b = std::max(rows, cols);
+  const int64_t lda = ws_ld(a), ldt = ws_ld(b);
+  Carver c(workspace);
+  float* A = c.take<float>((size_t)cnt * a * lda);
+  const float* X = (const float*)O.data;
+  int64_t ldx = O.ld, sx = cnt > 1 ? O.stride : 0;
+  if (tall) {
+    float* T = c.take<float>((size_t)cnt * a * ldt);
+    MAO_TRY(transpose(view(O.data, O.ld, sx), view(T, ldt, (int64_t)a * ldt), rows, cols, cnt,
+                      MAO_F32, s));
+    X = T;
+    ldx = ldt;
+    sx = (int64_t)a * ldt;
+  }
+  const int nrb = obs_rowblocks(a);
+  double* part = c.take<double>((size_t)cnt * nrb);
+  // A = (scale X)(scale X)^T on the wide orientation, one batched launch
+  GemmProblem p = gemm_problem(a, a, b, scale * scale, X, ldx, X, ldx, 0.f, nullptr, 0, A, lda,
+                               GF_SYRK | GF_D_F32);
+  p.batch = cnt;
+  p.sA = p.sB = sx;
+  p.sD = (int64_t)a * lda;
+  MAO_TRY(launch_gemm(MAO_F32, &p, 1, s));
+  MAO_TRY(sumsq_partials(view(A, lda, (int64_t)a * lda), MAO_F32, a, a, cnt, nrb, true, part, s));
+  return finalize_rms(part, nrb, cnt, (double)a, out, s);
+}
+
+size_t mao_rayleigh_workspace_size(int64_t n) {
+  if (n < 1 || n > (1 << 20)) return 0;
+  Carver c(nullptr);
+  c.take<float>((size_t)n * ws_ld(n));
+  c.take<float>((size_t)n * ws_ld(n));
+  return c.used + 256;
+}
+
+mao_status mao_rayleigh(mao_mat F, mao_mat Q, float* diag_out, float* kappa_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  MAO_TRY(check_mat("F", F.data, F.rows, F.cols, F.ld, F.dtype, true));
+  MAO_TRY(check_mat("Q", Q.data, Q.rows, Q.cols, Q.ld, Q.dtype, true));
+  const int64_t n = F.rows;
+  if (F.cols != n || Q.rows != n || Q.cols != n) MAO_FAIL(MAO_E_SHAPE, "F and Q must be n x n");
+  if (!diag_out) MAO_FAIL(MAO_E_NULL, "diag_out is NULL");
+  if ((uintptr_t)diag_out % 4 || (uintptr_t)kappa_out % 4) MAO_FAIL(MAO_E_LAYOUT, "outputs not 4-byte aligned");
+  std::vector<Range> rr = {mrange(F), mrange(Q), Range{(uintptr_t)diag_out, (uintptr_t)(diag_out + n)}};
+  if (kappa_out) rr.push_back(Range{(uintptr_t)kappa_out, (uintptr_t)(kappa_out + 1)});
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, mao_rayleigh_workspace_size(n)));
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t ld = ws_ld(n);
+  Carver c(workspace);
+  float* Qt = c.take<float>((size_t)n * ld);
+  float* C = c.take<float>((size_t)n * ld);
+  MAO_TRY(transpose(view(Q.data, Q.ld), view(Qt, ld), (int)n, (int)n, 1, MAO_F32, s));
+  // C[i][k] = sum_j Q[j][i] F[k][j] = (F Q)[k][i]; d_i = sum_k C[i][k] Q[k][i]
+  MAO_TRY(nt32((int)n, (int)n, (int)n, Qt, ld, (const float*)F.data, F.ld, C, ld, nullptr, 0, s));
+  MAO_TRY(row_dots(view(C, ld), view(Qt, ld), (int)n, (int)n, diag_out, s));
+  if (kappa_out) MAO_TRY(kappa_of(diag_out, (int)n, kappa_out, s));
+  return MAO_OK;
+}
+
+size_t mao_rank1_share_workspace_size(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || rows > (1 << 20) || cols > (1 << 20)) return 0;
+  Carver c(nullptr);
+  c.take<float>((size_t)cols);
+  c.take<float>((size_t)rows);
+  c.take<float>((size_t)rank1_col_blocks(rows) * cols);
+  c.take<double>((size_t)obs_rowblocks(rows));
+  return c.used + 256;
+}
+
+mao_status mao_rank1_share(mao_mat V, int32_t iters, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  MAO_TRY(check_mat("V", V.data, V.rows, V.cols, V.ld, V.dtype, true));
+  if (iters < 1 || iters > 1000) MAO_FAIL(MAO_E_HPARAM, "iters=%d outside 1..1000", iters);
+  if (!out) MAO_FAIL(MAO_E_NULL, "out is NULL");
+  if ((uintptr_t)out % 4) MAO_FAIL(MAO_E_LAYOUT, "out not 4-byte aligned");
+  std::vector<Range> rr = {mrange(V), Range{(uintptr_t)out, (uintptr_t)(out + 1)}};
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, mao_rank1_share_workspace_size(V.rows, V.cols)));
+  hipStream_t s = (hipStream_t)stream;
+  const int m = (int)V.rows, n = (int)V.cols;
+  Carver c(workspace);
+  float* v = c.take<float>((size_t)n);
+  float* y = c.take<float>((size_t)m);
+  const int nrbc = rank1_col_blocks(m);
+  float* part = c.take<float>((size_t)nrbc * n);
+  const int nrb = obs_rowblocks(m);
+  double* vpart = c.take<double>((size_t)nrb);
+  const View Vv = view(V.data, V.ld);
+  MAO_TRY(sumsq_partials(Vv, MAO_F32, m, n, 1, nrb, false, vpart, s));
+  // power iteration on V^T V from the unit all-ones vector
+  MAO_TRY(fill_unit(v, n, s));
+  for (int it = 0; it < iters; ++it) {
+    MAO_TRY(gemv_rows(Vv, m, n, v, y, s));
+    MAO_TRY(gemv_cols(Vv, m, n, y, part, nrbc, v, s));
+    MAO_TRY(normalize_vec(v, n, s));
+  }
+  MAO_TRY(gemv_rows(Vv, m, n, v, y, s));
+  return share_of(y, m, vpart, nrb, out, s);
+}
+
+mao_status mao_basis_age(const float* aux, float* age, void* stream) {
+  if (!aux || !age) MAO_FAIL(MAO_E_NULL, "aux or age is NULL");
+  if ((uintptr_t)aux % 4 || (uintptr_t)age % 4) MAO_FAIL(MAO_E_LAYOUT, "not 4-byte aligned");
+  std::vector<Range> rr = {Range{(uintptr_t)aux, (uintptr_t)(aux + 4)},
+                           Range{(uintptr_t)age, (uintptr_t)(age + 1)}};
+  MAO_TRY(check_no_overlap(rr));
+  return basis_age(aux, age, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -299,3 +299,49 @@ def test_many_matrix_validation_codes():
     assert lib.foam_step_many(2, W, G, F2, 1, ctypes.byref(fh), ws, fneed, None, None) == E_NULL
     assert lib.foam_step_many(4097, W, G, F, 1, ctypes.byref(fh), ws, fneed, None,
                               None) == E_SHAPE
+
+
+@needs_no_gpu
+def test_observability_validation_codes():
+    lib = mao.load()
+    X = mao.Batch(FAKE, 2, 8, 16, 16, 8 * 16, mao.F32)
+    ws = ctypes.c_void_p(FAKE + (16 << 20))
+    out = ctypes.c_void_p(FAKE + (8 << 20))
+    need = lib.mao_matrix_rms_workspace_size(X)
+    assert need > 0
+    assert lib.mao_matrix_rms(X, None, ws, need, None) == E_NULL
+    assert lib.mao_matrix_rms(X, ctypes.c_void_p(FAKE + 8), ws, need, None) == E_ALIAS
+    assert lib.mao_matrix_rms(mao.Batch(FAKE, 70000, 1, 8, 8, 8, mao.F32), out, ws, 1 << 30,
+                              None) == E_SHAPE
+    assert lib.mao_matrix_rms(X, out, ws, need - 1, None) == E_WORKSPACE
+
+    rneed = lib.mao_ns_residual_workspace_size(X)
+    assert rneed > 0
+    assert lib.mao_ns_residual(mao.Batch(FAKE, 2, 8, 16, 16, 8 * 16, mao.BF16), 1.0, out, ws,
+                               rneed, None) == E_DTYPE
+    assert lib.mao_ns_residual(X, 0.0, out, ws, rneed, None) == E_HPARAM
+    assert lib.mao_ns_residual(X, float("inf"), out, ws, rneed, None) == E_HPARAM
+    assert lib.mao_ns_residual(X, 1.0, out, None, rneed, None) == E_WORKSPACE
+
+    F = _mat(FAKE, 16, 16, 16)
+    Q = _mat(FAKE + (1 << 20), 16, 16, 16)
+    kneed = lib.mao_rayleigh_workspace_size(16)
+    assert lib.mao_rayleigh(F, _mat(FAKE + (1 << 20), 16, 8, 8), out, None, ws, kneed, None) == E_SHAPE
+    assert lib.mao_rayleigh(F, Q, None, None, ws, kneed, None) == E_NULL
+    assert lib.mao_rayleigh(F, _mat(FAKE + 64, 16, 16, 16), out, None, ws, kneed, None) == E_ALIAS
+    assert lib.mao_rayleigh(F, Q, out, ctypes.c_void_p(FAKE + (8 << 20) + 4), ws, kneed,
+                            None) == E_ALIAS
+    assert lib.mao_rayleigh(_mat(FAKE, 16, 16, 16, mao.BF16), Q, out, None, ws, kneed,
+                            None) == E_DTYPE
+
+    V = _mat(FAKE, 8, 16, 16)
+    sneed = lib.mao_rank1_share_workspace_size(8, 16)
+    assert sneed > 0
+    assert lib.mao_rank1_share(V, 0, out, ws, sneed, None) == E_HPARAM
+    assert lib.mao_rank1_share(V, 1001, out, ws, sneed, None) == E_HPARAM
+    assert lib.mao_rank1_share(V, 10, None, ws, sneed, None) == E_NULL
+    assert lib.mao_rank1_share(V, 10, out, ws, sneed - 1, None) == E_WORKSPACE
+
+    assert lib.mao_basis_age(None, out, None) == E_NULL
+    assert lib.mao_basis_age(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 12), None) == E_ALIAS
+    assert lib.mao_basis_age(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 2), None) == E_LAYOUT
