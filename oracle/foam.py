@@ -32,9 +32,19 @@ claim fails. eps = 1e-8.
 ``q_override`` / ``refresh_override`` let a teacher-forced test finish the
 step with the other side's basis and refresh decision.
 
+Output-only variant (``side="output"``): the review's section 3 ablation
+keeps the basis on the output side instead. Reading: the mirror of the
+steps above with the factor L = b2 L + (1-b2) G G^T (m x m) and its basis
+Q_L in place of R and Q_R; G_rot = Q_L^T G, M_rot = Q_L^T M; r and c stay the
+row and column means of G_rot^2 (lengths m and n); tau = tr(L_hat) /
+(||r_hat||_1 ||c_hat||_1); U = Q_L N. The state fields R and QR then hold L
+and Q_L.
+
 Parity: pinned (exact reconstruction of SOAP's dense rotated moment on
-Rademacher K-FAC gradients; mass invariant sum(tau r c^T) = tr(R_hat);
-rho = 0 in R's eigenbasis; state size mn + 2n^2 + m + n).
+Rademacher K-FAC gradients, on either side; mass invariant
+sum(tau r c^T) = tr(R_hat); rho = 0 in R's eigenbasis; the output variant
+equals the input variant on the transposed problem; state size
+mn + 2n^2 + m + n).
 """
 from __future__ import annotations
 
@@ -57,8 +67,9 @@ class FoamState:
         return FoamState(*(x.copy() for x in (self.M, self.R, self.QR, self.r, self.c)))
 
 
-def foam_init(m: int, n: int) -> FoamState:
-    return FoamState(np.zeros((m, n)), np.zeros((n, n)), np.eye(n), np.zeros(m), np.zeros(n))
+def foam_init(m: int, n: int, side: str = "input") -> FoamState:
+    k = m if side == "output" else n
+    return FoamState(np.zeros((m, n)), np.zeros((k, k)), np.eye(k), np.zeros(m), np.zeros(n))
 
 
 def offdiag_ratio(d: np.ndarray) -> float:
@@ -77,14 +88,18 @@ def foam_checks(t: int, pf: int) -> bool:
 
 def foam_step(w, g, state: FoamState, t: int, *, lr: float, beta1: float, beta2: float,
               eps: float = 1e-8, weight_decay: float = 0.0, pf: int = 10, tol: float = 0.1,
-              q_override=None, refresh_override=None):
+              q_override=None, refresh_override=None, side: str = "input"):
     """One FOAM step. Returns (W_new, new_state, U, info); ``info`` holds rho,
-    the refresh decision, P = R Q_R (when checked), tau and N."""
+    the refresh decision, P = R Q_R (when checked), tau and N. ``side``:
+    "input" (the review's FOAM) or "output" (its output-only ablation)."""
+    if side not in ("input", "output"):
+        raise ValueError(side)
+    out_side = side == "output"
     w = np.asarray(w, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     s = state.copy()
     s.M = beta1 * s.M + (1.0 - beta1) * g
-    s.R = beta2 * s.R + (1.0 - beta2) * (g.T @ g)
+    s.R = beta2 * s.R + (1.0 - beta2) * ((g @ g.T) if out_side else (g.T @ g))
     info = {"checked": False, "refreshed": False}
     if foam_checks(t, pf):
         d = s.QR.T @ s.R @ s.QR
@@ -98,8 +113,12 @@ def foam_step(w, g, state: FoamState, t: int, *, lr: float, beta1: float, beta2:
             s.QR = qr_positive(info["P"])[0]
     if q_override is not None:
         s.QR = np.asarray(q_override, dtype=np.float64)
-    g_rot = g @ s.QR
-    m_rot = s.M @ s.QR
+    if out_side:
+        g_rot = s.QR.T @ g
+        m_rot = s.QR.T @ s.M
+    else:
+        g_rot = g @ s.QR
+        m_rot = s.M @ s.QR
     sq = g_rot * g_rot
     s.r = beta2 * s.r + (1.0 - beta2) * sq.mean(axis=1)
     s.c = beta2 * s.c + (1.0 - beta2) * sq.mean(axis=0)
@@ -111,12 +130,14 @@ def foam_step(w, g, state: FoamState, t: int, *, lr: float, beta1: float, beta2:
     tau = float(np.trace(s.R / b2) / denom) if denom > 0 else 0.0
     v_hat = tau * np.outer(r_hat, c_hat)
     n_rot = (m_rot / b1) / (np.sqrt(v_hat) + eps)
-    upd = n_rot @ s.QR.T
+    upd = (s.QR @ n_rot) if out_side else (n_rot @ s.QR.T)
     w_new = w - lr * (weight_decay * w + upd)
     info.update(tau=tau, N=n_rot, g_rot=g_rot, v_hat=v_hat)
     return w_new, s, upd, info
 
 
-def foam_state_bytes(m: int, n: int, bytes_per_elem: int = 4) -> int:
-    """{M, R, Q_R, r, c}: mn + 2n^2 + m + n elements (FOAM review, section 3)."""
-    return bytes_per_elem * (m * n + 2 * n * n + m + n)
+def foam_state_bytes(m: int, n: int, bytes_per_elem: int = 4, side: str = "input") -> int:
+    """{M, R, Q_R, r, c}: mn + 2n^2 + m + n elements (FOAM review, section 3);
+    the output variant keeps m x m factors instead."""
+    k = m if side == "output" else n
+    return bytes_per_elem * (m * n + 2 * k * k + m + n)

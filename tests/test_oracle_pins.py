@@ -332,6 +332,51 @@ def test_foam_factored_moment_exact_under_kfac():
         assert rel(uf, us) < 1e-10
 
 
+def test_foam_output_side_exact_under_kfac():
+    """Output-only FOAM (the review's section 3 ablation): with the basis Q on
+    the output side and G = Q (D_a Z D_b), Z = +-1, Q^T G is exactly
+    a_i b_j Z_ij, so tau r_hat c_hat^T reproduces SOAP's dense rotated moment
+    with Q_L = Q, Q_R = I, and the updates agree."""
+    r = _rng(30)
+    m, n = 7, 5
+    q = oracle.qr_positive(r.standard_normal((m, m)))[0]
+    alpha = np.exp(r.standard_normal(m))
+    beta = np.exp(r.standard_normal(n))
+    fs = oracle.foam_init(m, n, side="output")
+    assert fs.R.shape == (m, m) and fs.QR.shape == (m, m)
+    fs.QR = q.copy()
+    ss = oracle.soap_init(m, n)
+    ss.QL = q.copy()
+    wf = ws = np.zeros((m, n))
+    for t in range(1, 8):
+        g = rademacher_kfac_gradient(beta, alpha, q, seed=2, step=t).T
+        wf, fs, uf, fi = oracle.foam_step(wf, g, fs, t, tol=np.inf, side="output", **FOAM_HP)
+        ws, ss, us, si = oracle.soap_step(ws, g, ss, t, refresh_every=0, **FOAM_HP)
+        v_dense = ss.V / (1 - 0.95 ** t)
+        assert rel(fi["v_hat"], v_dense) < 1e-12
+        assert rel(uf, us) < 1e-10
+        assert abs(fi["v_hat"].sum() - np.trace(fs.R) / (1 - 0.95 ** t)) < 1e-10 * np.trace(fs.R)
+
+
+def test_foam_output_side_is_input_side_of_the_transpose():
+    """Stepping W with the output-side basis equals stepping W^T with the
+    input-side basis (r and c trade places), refreshes included."""
+    r = _rng(31)
+    m, n = 9, 4
+    so = oracle.foam_init(m, n, side="output")
+    si = oracle.foam_init(n, m)
+    wo = r.standard_normal((m, n))
+    wi = wo.T.copy()
+    for t in range(1, 9):
+        g = r.standard_normal((m, n)) * np.exp(r.standard_normal((m, 1)))
+        wo, so, uo, io = oracle.foam_step(wo, g, so, t, pf=3, tol=0.05, side="output", **FOAM_HP)
+        wi, si, ui, ii = oracle.foam_step(wi, g.T, si, t, pf=3, tol=0.05, **FOAM_HP)
+        assert io["checked"] == ii["checked"] and io["refreshed"] == ii["refreshed"]
+        assert rel(uo, ui.T) < 1e-12 and rel(wo, wi.T) < 1e-12
+        assert rel(so.r, si.c) < 1e-12 and rel(so.c, si.r) < 1e-12
+        assert rel(so.QR, si.QR) < 1e-12 and rel(so.M, si.M.T) < 1e-12
+
+
 def test_foam_mass_invariant_and_refresh_rule():
     r = _rng(27)
     m, n = 7, 5
