@@ -14,9 +14,12 @@ Prints one JSON line: steps/s of the whole job, the dominant kernel's
 roofline (the Newton-Schulz contraction, from HIP events around every launch
 inside the timed region) and the fp64 CPU oracle's rate on a bounded sample.
 
-Other workloads (--workload): moe (128-expert bank, batched Muon+), c1
-(256x512 fp32 Muon and SOAP), soap8b (the 8B layer under SOAP), foam760m
-(GPT-2-760M-shaped set under FOAM plus the AdamW embedding).
+Other workloads (--workload): moe (128-expert bank, batched Muon+), c1muon /
+c1soap (256x512 fp32 Muon and SOAP), soap8b (the 8B layer under SOAP),
+foam760m (GPT-2-760M-shaped set under FOAM plus the AdamW embedding),
+foam760m_output (the same with the basis on the output side), soap760m (the
+760M set under SOAP), observe8b (the observability reductions over the 8B
+layer).
 """
 from __future__ import annotations
 
@@ -322,7 +325,7 @@ class SoapLikeWorkload:
     (equal-size QR refreshes batched), with a ring of two gradients per
     matrix."""
 
-    def __init__(self, kind, config, specs, g_dtype, w_dtype, pf=10, tol=0.1):
+    def __init__(self, kind, config, specs, g_dtype, w_dtype, pf=10, tol=0.1, side="input"):
         import torch
 
         import matrix_aware_optimizers_amd as mao
@@ -336,7 +339,7 @@ class SoapLikeWorkload:
                                        refresh_every=1)
         else:
             self.hp = mao.foam_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
-                                       pf=pf, tol=tol)
+                                       pf=pf, tol=tol, side=side)
         for idx, sp in enumerate(specs):
             if idx % 16 == 15:
                 log(f"  {idx + 1}/{len(specs)} matrices set up")
@@ -356,7 +359,8 @@ class SoapLikeWorkload:
                 st["QR"].fill_diagonal_(1.0)
                 cst = mao.soap_state(st["M"], st["V"], st["L"], st["R"], st["QL"], st["QR"])
             else:
-                st = {"M": z(m, n), "R": z(n, n), "QR": z(n, n),
+                k = m if side == "output" else n
+                st = {"M": z(m, n), "R": z(k, k), "QR": z(k, k),
                       "r": torch.zeros(m, device="cuda"), "c": torch.zeros(n, device="cuda"),
                       "aux": torch.zeros(4, device="cuda")}
                 st["QR"].fill_diagonal_(1.0)
@@ -399,12 +403,13 @@ class SoapLikeWorkload:
                 self.mao._check(rc, "adamw_step")
 
 
-def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, embedding=None):
+def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, embedding=None,
+                 side="input"):
     import torch
 
     import matrix_aware_optimizers_amd as mao
     log(f"setting up {workload_name} ({len(specs)} matrices)")
-    wl = SoapLikeWorkload(kind, config, specs, g_dtype, w_dtype)
+    wl = SoapLikeWorkload(kind, config, specs, g_dtype, w_dtype, side=side)
     if embedding:
         wl.add_embedding(*embedding)
     log("warmup")
@@ -445,11 +450,86 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": workload_name, "matrices": len(specs), "optimizer": kind,
-                   "gradients": g_dtype, "weights": w_dtype},
+                   "gradients": g_dtype, "weights": w_dtype,
+                   **({"side": side} if kind == "foam" else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
                      "kernel": "gemm_nt_kernel<float> (all fp32 contractions)"},
         "kernels": per_tag,
+    }
+
+
+def run_observe(args):
+    """The observability reductions over the Llama-8B layer set, each timed on
+    its own with events on the library's stream: the update RMS of the five
+    fp32 updates (one read), their Newton-Schulz residuals (fp32 SYRK on the
+    wide orientation), the rank-1 share of a 4096 x 14336 second moment (30
+    power steps) and the Rayleigh quotients of a 4096 x 4096 factor in a
+    basis. One pass = all four."""
+    import torch
+
+    import matrix_aware_optimizers_amd as mao
+    import synth
+    specs = synth.specs("c2")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    ups = []
+    for sp in specs:
+        u = _padded_empty(torch, sp.rows, sp.cols, torch.float32)
+        u.normal_(generator=gen)
+        ups.append(u)
+    v = _padded_empty(torch, 4096, 14336, torch.float32)
+    v.normal_(generator=gen)
+    v.mul_(v)
+    f = _padded_empty(torch, 4096, 4096, torch.float32)
+    f.normal_(generator=gen)
+    f.copy_(f @ f.T / 4096.0)
+    q = torch.linalg.qr(torch.randn(4096, 4096, device="cuda", generator=gen))[0].contiguous()
+    scales = [math.sqrt(sp.cols / sp.rows) for sp in specs]
+    iters = 30
+    calls = {
+        "update_rms": lambda: [mao.matrix_rms(u) for u in ups],
+        "ns_residual": lambda: [mao.ns_residual(u, sc) for u, sc in zip(ups, scales)],
+        "rank1_share": lambda: mao.rank1_share(v, iters),
+        "rayleigh": lambda: mao.rayleigh(f, q),
+    }
+    elems = sum(sp.rows * sp.cols for sp in specs)
+    work = {
+        "update_rms": (4.0 * elems, "GB/s"),
+        "ns_residual": (float(sum(min(sp.rows, sp.cols) ** 2 * max(sp.rows, sp.cols)
+                                  for sp in specs)), "TFLOP/s"),
+        "rank1_share": (4.0 * 4096 * 14336 * (2 * iters + 2), "GB/s"),
+        "rayleigh": (2.0 * 4096 ** 3, "TFLOP/s"),
+    }
+    out, total = {}, 0.0
+    for name, fn in calls.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        amount, unit = work[name]
+        rate = amount / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+        out[name] = {"ms": round(ms, 4), unit: round(rate, 1)}
+        total += ms
+        log(f"{name}: {ms:.3f} ms, {rate:.1f} {unit}")
+    rms = out["update_rms"]["GB/s"]
+    return {
+        "metric": "observability passes/s on 8B-layer matrix set", "value": 1000.0 / total,
+        "unit": "passes/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "llama8b_layer_observability", "matrices": len(specs),
+                   "rank1_iters": iters},
+        "roofline": {"bound": "hbm", "achieved": rms, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": rms / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "sumsq_partial_kernel (update RMS)"},
+        "kernels": out,
     }
 
 
@@ -462,7 +542,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b",
                     choices=["llama8b", "moe", "c1muon", "c1soap", "soap8b", "foam760m",
-                             "soap760m"])
+                             "foam760m_output", "soap760m", "observe8b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (a known-size reference "
@@ -514,6 +594,13 @@ def main():
         import synth
         line = run_soaplike(args, "gpt2_760m_foam", "foam", "c5", synth.specs("c5"), "f32", "f32",
                             embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH))
+    elif args.workload == "foam760m_output":
+        import synth
+        line = run_soaplike(args, "gpt2_760m_foam_output_side", "foam", "c5", synth.specs("c5"),
+                            "f32", "f32", embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH),
+                            side="output")
+    elif args.workload == "observe8b":
+        line = run_observe(args)
     else:
         import synth
         line = run_soaplike(args, "gpt2_760m_soap", "soap", "c5", synth.specs("c5"), "f32", "f32")

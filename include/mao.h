@@ -62,7 +62,7 @@ extern "C" {
 #define MAO_API
 #endif
 
-#define MAO_ABI_VERSION 1
+#define MAO_ABI_VERSION 2
 #define MAO_MAX_GROUPS 8
 
 typedef enum {
@@ -218,20 +218,29 @@ MAO_API mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* state, 
 /* FOAM                                                                      */
 /* ------------------------------------------------------------------------ */
 
+/* Which side of W carries FOAM's rotation. */
+typedef enum {
+  MAO_FOAM_INPUT = 0,  /* the method: basis of G^T G (n x n), G_rot = G QR */
+  MAO_FOAM_OUTPUT = 1  /* the output-only ablation of [FOAM] section 3: basis of
+                          G G^T (m x m), G_rot = QR^T G */
+} mao_foam_side;
+
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;
   int32_t pf; /* >= 1: the refresh criterion is evaluated at t = 1, pf+1, ... */
   float tol;  /* >= 0: refresh when rho > tol */
+  int32_t side; /* mao_foam_side */
 } mao_foam_hparams;
 
-/* FOAM state, fp32, W is m x n. Initial: M = R = 0, QR = I_n, r = c = 0.
+/* FOAM state, fp32, W is m x n; k = n for MAO_FOAM_INPUT, m for
+ * MAO_FOAM_OUTPUT. Initial: M = R = 0, QR = I_k, r = c = 0.
  * aux: device float[4] written by every step: aux[0] = rho of the last
  * evaluated criterion, aux[1] = 1 if this step refreshed else 0, aux[2] = tau,
  * aux[3] = 1 if this step evaluated the criterion else 0. */
 typedef struct {
   mao_mat M;  /* m x n momentum */
-  mao_mat R;  /* n x n factor EMA of G^T G */
-  mao_mat QR; /* n x n basis, columns = basis vectors */
+  mao_mat R;  /* k x k factor EMA of G^T G (input side) or G G^T (output side) */
+  mao_mat QR; /* k x k basis, columns = basis vectors */
   float* r;   /* m, EMA of row means of G_rot^2 */
   float* c;   /* n, EMA of column means of G_rot^2 */
   float* aux; /* 4 floats */
@@ -254,6 +263,12 @@ MAO_API size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hp
  *   tau = tr(R / (1-b2^t)) / (|r_hat|_1 |c_hat|_1)  (0 if r = c = 0)
  *   N = (M_rot / (1-b1^t)) / (sqrt(tau r_hat c_hat^T) + eps)
  *   U = N QR^T;  W <- W - lr (weight_decay W + U)
+ *
+ * With hp->side = MAO_FOAM_OUTPUT (the output-only ablation of [FOAM] section
+ * 3, read as the mirror of the steps above): R <- b2 R + (1-b2) G G^T (m x m),
+ * the same criterion and refresh on that factor, G_rot = QR^T G,
+ * M_rot = QR^T M, r and c the row and column means of G_rot^2 as above, tau
+ * with tr(R_hat), U = QR N.
  */
 MAO_API mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* state, int64_t t,
                      const mao_foam_hparams* hp, void* workspace, size_t workspace_bytes,

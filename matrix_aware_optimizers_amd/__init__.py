@@ -58,7 +58,7 @@ class SoapStateC(ctypes.Structure):
 
 class FoamHparams(ctypes.Structure):
     _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
-                ("weight_decay", c_float), ("pf", c_int32), ("tol", c_float)]
+                ("weight_decay", c_float), ("pf", c_int32), ("tol", c_float), ("side", c_int32)]
 
 
 class FoamStateC(ctypes.Structure):
@@ -295,10 +295,15 @@ def soap_step(W, G, state: dict, t: int, *, update_out=None, ws=None, **hp_kw):
                          buf.numel(), _ptr(update_out), _stream()), "soap_step")
 
 
-def foam_hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, pf=10, tol=0.1):
+FOAM_SIDES = {"input": 0, "output": 1}
+
+
+def foam_hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, pf=10, tol=0.1,
+                 side="input"):
     hp = FoamHparams()
     hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay = lr, beta1, beta2, eps, weight_decay
     hp.pf, hp.tol = pf, tol
+    hp.side = FOAM_SIDES[side] if isinstance(side, str) else int(side)
     return hp
 
 

@@ -688,17 +688,22 @@ mao_status check_foam_hp(const mao_foam_hparams* hp) {
   MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
   if (hp->pf < 1) MAO_FAIL(MAO_E_HPARAM, "pf=%d must be >= 1", hp->pf);
   if (!(hp->tol >= 0.f)) MAO_FAIL(MAO_E_HPARAM, "tol=%g must be >= 0", (double)hp->tol);
+  if (hp->side != MAO_FOAM_INPUT && hp->side != MAO_FOAM_OUTPUT)
+    MAO_FAIL(MAO_E_HPARAM, "side=%d must be 0 (input) or 1 (output)", hp->side);
   return MAO_OK;
 }
 
+bool foam_out(const mao_foam_hparams* hp) { return hp->side == MAO_FOAM_OUTPUT; }
+
 mao_status validate_foam(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, int64_t t,
-                         const float* update_out, std::vector<Range>& rr) {
+                         const mao_foam_hparams* hp, const float* update_out,
+                         std::vector<Range>& rr) {
   if (!st) MAO_FAIL(MAO_E_NULL, "state is NULL");
   MAO_TRY(check_step_common(W, G, t));
-  const int64_t m = W.rows, n = W.cols;
+  const int64_t m = W.rows, n = W.cols, k = foam_out(hp) ? m : n;
   MAO_TRY(check_state_mat("M", st->M, m, n));
-  MAO_TRY(check_state_mat("R", st->R, n, n));
-  MAO_TRY(check_state_mat("QR", st->QR, n, n));
+  MAO_TRY(check_state_mat("R", st->R, k, k));
+  MAO_TRY(check_state_mat("QR", st->QR, k, k));
   if (!st->r || !st->c || !st->aux) MAO_FAIL(MAO_E_NULL, "r, c or aux is NULL");
   if (((uintptr_t)st->r | (uintptr_t)st->c | (uintptr_t)st->aux) % 4 != 0) MAO_FAIL(MAO_E_LAYOUT, "r, c, aux misaligned");
   if (update_out && ((uintptr_t)update_out % 16 != 0 || n % 4 != 0))
@@ -716,24 +721,39 @@ bool foam_checks(const mao_foam_hparams* hp, int64_t t) { return (t - 1) % hp->p
 
 // FOAM before the refresh: momentum, fp32 G and G^T, R EMA, E_R = QR^T; on a
 // criterion step also S = E_R R (the QR input) and the refresh flag.
+//
+// The output side is the input side of the transposed problem: its buffers
+// are carved for (n, m), so that Gf holds G^T (n x m) and Gtf holds G
+// (m x n), the factor is G G^T, r and c trade places and U leaves through the
+// transposed store of the last product.
 mao_status foam_pre(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, RotBufs& R,
                     int64_t t, const mao_foam_hparams* hp, hipStream_t s) {
   const int m = (int)W.rows, n = (int)W.cols;
+  const bool out = foam_out(hp);
+  const int k = out ? m : n;  // factor size
   const float b1 = hp->beta1, b2 = hp->beta2;
   float* Rf = (float*)st->R.data;
   const int64_t ldR = st->R.ld;
   float* work = R.small + 64;
   MAO_TRY(ema_sumsq(view(st->M.data, st->M.ld), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr,
                     rowblocks_for(m, 1), s));
-  MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
-                             view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
-  MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s));
-  MAO_TRY(transpose(view(st->QR.data, st->QR.ld), view(R.ER, R.ldn), n, n, 1, MAO_F32, s));
+  if (!out) {
+    MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
+                               view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
+    MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s));   // R = b2 R + (1-b2) G^T G
+  } else {
+    const bool f32 = G.dtype == MAO_F32;
+    MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
+                               view(f32 ? nullptr : R.Gtf, R.ldm), view(R.Gf, R.ldn), s));
+    const float* Gr = f32 ? (const float*)G.data : R.Gtf;
+    MAO_TRY(syrk_ema(m, n, Gr, f32 ? G.ld : R.ldm, b2, Rf, ldR, s));   // L = b2 L + (1-b2) G G^T
+  }
+  MAO_TRY(transpose(view(st->QR.data, st->QR.ld), view(R.ER, R.ldn), k, k, 1, MAO_F32, s));
   if (!foam_checks(hp, t)) return no_check(st->aux, R.flag, s);
   const int64_t ldS = R.ldn;
-  MAO_TRY(nt32(n, n, n, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));       // Q^T R
-  MAO_TRY(nt32(n, n, n, R.S, ldS, R.ER, R.ldn, R.D, R.ldn, nullptr, 0, s));    // Q^T R Q
-  return offdiag_check(view(R.D, R.ldn), n, hp->tol, work, st->aux, R.flag, s);
+  MAO_TRY(nt32(k, k, k, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));       // Q^T R
+  MAO_TRY(nt32(k, k, k, R.S, ldS, R.ER, R.ldn, R.D, R.ldn, nullptr, 0, s));    // Q^T R Q
+  return offdiag_check(view(R.D, R.ldn), k, hp->tol, work, st->aux, R.flag, s);
 }
 
 // FOAM after the refresh: rotation, factored moment, preconditioning,
@@ -744,13 +764,30 @@ mao_status foam_post(const mao_mat& W, const mao_mat& G, const mao_foam_state* s
   const float b1 = hp->beta1, b2 = hp->beta2;
   float* tau = R.small;
   float* work = R.small + 64;
+  const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
+  const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
+  if (foam_out(hp)) {
+    // transposed problem (n x m): G_rot^T = G^T Q_L, M_rot^T = M^T Q_L
+    MAO_TRY(nt32(n, m, m, R.Gf, R.ldn, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s));
+    MAO_TRY(transpose(view(st->M.data, st->M.ld), view(R.U, R.ldn), m, n, 1, MAO_F32, s));
+    MAO_TRY(nt32(n, m, m, R.U, R.ldn, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0, s));
+    // the row means of G_rot^T are W's column means (c) and vice versa
+    MAO_TRY(foam_moments(view(R.Gtil, R.ldn), n, m, b2, bc2, (const float*)st->R.data, st->R.ld,
+                         st->c, st->r, work, tau, st->aux, s));
+    MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), n, m, st->c, st->r, tau, bc1, bc2, hp->eps, s));
+    // U = Q_L N = (N^T Q_L^T)^T: the product's transposed store writes U
+    float* U = update_out ? update_out : R.T2t;
+    const int64_t ldU = update_out ? n : R.ldm;
+    MAO_TRY(nt32(n, m, m, R.Mtil, R.ldn, (const float*)st->QR.data, st->QR.ld, nullptr, 0, U, ldU,
+                 s));
+    return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
+                        hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+  }
   const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
   const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
   // rotate: G_rot = G Q_R, M_rot = M Q_R
   MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s));
   MAO_TRY(nt32(m, n, n, (const float*)st->M.data, st->M.ld, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0, s));
-  const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
-  const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
   MAO_TRY(foam_moments(view(R.Gtil, R.ldn), m, n, b2, bc2, (const float*)st->R.data, st->R.ld,
                        st->r, st->c, work, tau, st->aux, s));
   MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), m, n, st->r, st->c, tau, bc1, bc2, hp->eps, s));
@@ -781,15 +818,18 @@ struct QrGroup {
 // Carve per-matrix buffers, then the size groups (sorted by size): S and E of
 // every job, FOAM's refresh flags, the QR workspaces. Deterministic in the
 // shapes alone, so the size query and the step carve alike.
+// fout: FOAM on the output side (buffers of the transposed problem, factor
+// size m).
 void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<RotBufs>& R,
-                std::vector<QrGroup>& groups) {
+                std::vector<QrGroup>& groups, bool fout = false) {
   R.assign(count, RotBufs{});
   std::vector<std::pair<int, QrJobRef>> all;
   for (int i = 0; i < count; ++i) {
     const int m = (int)W[i].rows, n = (int)W[i].cols;
-    carve_rot(c, m, n, soap, true, R[i], false);
+    const bool t = !soap && fout;
+    carve_rot(c, t ? n : m, t ? m : n, soap, true, R[i], false);
     if (soap) all.push_back({m, QrJobRef{i, 0}});
-    all.push_back({n, QrJobRef{i, 1}});
+    all.push_back({t ? m : n, QrJobRef{i, 1}});
   }
   std::stable_sort(all.begin(), all.end(),
                    [](const std::pair<int, QrJobRef>& a, const std::pair<int, QrJobRef>& b) {
@@ -827,11 +867,11 @@ void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<R
   }
 }
 
-size_t many_ws(int count, const mao_mat* W, bool soap) {
+size_t many_ws(int count, const mao_mat* W, bool soap, bool fout = false) {
   Carver c(nullptr);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
-  carve_many(c, count, W, soap, R, groups);
+  carve_many(c, count, W, soap, R, groups, fout);
   return c.used + 256;
 }
 
@@ -844,7 +884,7 @@ mao_status check_many(int32_t count, const mao_mat* W, const mao_mat* G, const v
 }
 
 // row blocks of the column pass of the rank-1 power iteration
-int rank1_col_blocks(int64_t rows) { return (int)std::min<int64_t>(rows, 512); }
+int rank1_col_blocks(int64_t rows) { return (int)std::min<int64_t>(rows, 128); }
 
 }  // namespace
 
@@ -940,7 +980,8 @@ size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hparams* h
   if (!hp || rows < 1 || cols < 1) return 0;
   Carver c(nullptr);
   RotBufs R;
-  carve_rot(c, (int)rows, (int)cols, false, true, R);
+  const bool out = foam_out(hp);
+  carve_rot(c, (int)(out ? cols : rows), (int)(out ? rows : cols), false, true, R);
   return c.used + 256;
 }
 
@@ -950,16 +991,18 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
   hipStream_t s = (hipStream_t)stream;
   MAO_TRY(check_foam_hp(hp));
   std::vector<Range> rr;
-  MAO_TRY(validate_foam(W, G, st, t, update_out, rr));
+  MAO_TRY(validate_foam(W, G, st, t, hp, update_out, rr));
   MAO_TRY(check_no_overlap(rr));
   const int m = (int)W.rows, n = (int)W.cols;
+  const bool out = foam_out(hp);
+  const int k = out ? m : n;
   MAO_TRY(check_workspace(workspace, workspace_bytes, foam_workspace_size(m, n, hp)));
   Carver c(workspace);
   RotBufs R;
-  carve_rot(c, m, n, false, true, R);
+  carve_rot(c, out ? n : m, out ? m : n, false, true, R);
   MAO_TRY(foam_pre(W, G, st, R, t, hp, s));
   if (foam_checks(hp, t))
-    MAO_TRY(qr_core(R.S, R.ldn, n, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, R.flag, s));
+    MAO_TRY(qr_core(R.S, R.ldn, k, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, R.flag, s));
   return foam_post(W, G, st, R, t, hp, update_out, s);
 }
 
@@ -967,7 +1010,7 @@ size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_
   if (!hp || !W || count < 1 || count > kMaxMany) return 0;
   for (int i = 0; i < count; ++i)
     if (W[i].rows < 1 || W[i].cols < 1) return 0;
-  return many_ws(count, W, false);
+  return many_ws(count, W, false, foam_out(hp));
 }
 
 mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
@@ -979,13 +1022,13 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   MAO_TRY(check_many(count, W, G, st));
   std::vector<Range> rr;
   for (int i = 0; i < count; ++i)
-    MAO_TRY(validate_foam(W[i], G[i], &st[i], t, update_out ? update_out[i] : nullptr, rr));
+    MAO_TRY(validate_foam(W[i], G[i], &st[i], t, hp, update_out ? update_out[i] : nullptr, rr));
   MAO_TRY(check_no_overlap(rr));
-  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, false)));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, false, foam_out(hp))));
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
-  carve_many(c, count, W, false, R, groups);
+  carve_many(c, count, W, false, R, groups, foam_out(hp));
   for (int i = 0; i < count; ++i) MAO_TRY(foam_pre(W[i], G[i], &st[i], R[i], t, hp, s));
   if (foam_checks(hp, t)) {
     for (QrGroup& g : groups) {

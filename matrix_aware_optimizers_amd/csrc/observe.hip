@@ -10,6 +10,26 @@ namespace {
 
 constexpr int kObs = 256;
 
+// Rows start 16-byte aligned (data 16-byte aligned, ld and batch strides
+// multiples of 8 elements, checked on the host), so every lane reads 16
+// bytes: 4 fp32 or 8 bf16 values.
+__device__ __forceinline__ int vec_load(const float* p, float* v) {
+  const float4 q = *(const float4*)p;
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  return 4;
+}
+__device__ __forceinline__ int vec_load(const bf16_t* p, float* v) {
+  const uint4 q = *(const uint4*)p;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf16_to_f32((bf16_t)(w[e] & 0xffff));
+    v[2 * e + 1] = bf16_to_f32((bf16_t)(w[e] >> 16));
+  }
+  return 8;
+}
+template <typename T> constexpr int vec_width() { return 16 / (int)sizeof(T); }
+
 template <typename T>
 __global__ __launch_bounds__(kObs) void sumsq_partial_kernel(View X, int rows, int cols, int rpb,
                                                              int nrb, int sub_identity,
@@ -18,14 +38,25 @@ __global__ __launch_bounds__(kObs) void sumsq_partial_kernel(View X, int rows, i
   const int b = blockIdx.y, blk = blockIdx.x;
   const T* base = (const T*)X.p + (int64_t)b * X.stride;
   const int r0 = blk * rpb, r1 = min(rows, r0 + rpb);
+  constexpr int VW = vec_width<T>();
+  const int colsv = cols - cols % VW;
   double acc = 0.0;
   for (int i = r0; i < r1; ++i) {
     const T* row = base + (int64_t)i * X.ld;
-    for (int j = threadIdx.x; j < cols; j += kObs) {
+    float rs = 0.f;  // this row's share, fp32 (at most cols / 256 / VW + 1 terms per lane)
+    for (int j = threadIdx.x * VW; j < colsv; j += kObs * VW) {
+      float v[VW];
+      vec_load(row + j, v);
+      if (sub_identity && i >= j && i < j + VW) v[i - j] -= 1.f;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) rs = fmaf(v[e], v[e], rs);
+    }
+    for (int j = colsv + threadIdx.x; j < cols; j += kObs) {
       float v = load_f32<T>(row + j);
       if (sub_identity && i == j) v -= 1.f;
-      acc += (double)v * (double)v;
+      rs = fmaf(v, v, rs);
     }
+    acc += (double)rs;
   }
   acc = block_sum_d(acc, sc);
   if (threadIdx.x == 0) part[(int64_t)b * nrb + blk] = acc;
@@ -87,22 +118,56 @@ __global__ __launch_bounds__(kObs) void gemv_rows_kernel(View V, int m, int n, c
   const int i = blockIdx.x * (kObs / 64) + (threadIdx.x >> 6);
   if (i >= m) return;
   const float* row = (const float*)V.p + (int64_t)i * V.ld;
+  const int nv = n & ~3;
   double acc = 0.0;
-  for (int j = lane; j < n; j += 64) acc += (double)row[j] * (double)x[j];
+  // four 16-byte loads in flight per lane before they are consumed
+  int j = lane * 4;
+  for (; j + 768 < nv; j += 1024) {
+    float a[4][4], b[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      vec_load(row + j + 256 * u, a[u]);
+      vec_load(x + j + 256 * u, b[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc += (double)(a[u][0] * b[u][0] + a[u][1] * b[u][1]) +
+             (double)(a[u][2] * b[u][2] + a[u][3] * b[u][3]);
+  }
+  for (; j < nv; j += 256) {
+    float a[4], b[4];
+    vec_load(row + j, a);
+    vec_load(x + j, b);
+    acc += (double)(a[0] * b[0] + a[1] * b[1]) + (double)(a[2] * b[2] + a[3] * b[3]);
+  }
+  for (int jj = nv + lane; jj < n; jj += 64) acc += (double)row[jj] * (double)x[jj];
   acc = wave_sum_d(acc);
   if (lane == 0) y[i] = (float)acc;
 }
 
+// Each lane owns 4 adjacent columns (16-byte loads along a row).
 __global__ __launch_bounds__(kObs) void gemv_cols_partial_kernel(View V, int m, int n, int rpb,
                                                                  const float* y, float* part) {
   const int blk = blockIdx.x;
-  const int j = blockIdx.y * kObs + threadIdx.x;
+  const int j = (blockIdx.y * kObs + threadIdx.x) * 4;
   if (j >= n) return;
   const int r0 = blk * rpb, r1 = min(m, r0 + rpb);
   const float* col = (const float*)V.p + j;
-  double acc = 0.0;
-  for (int i = r0; i < r1; ++i) acc += (double)col[(int64_t)i * V.ld] * (double)y[i];
-  part[(int64_t)blk * n + j] = (float)acc;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  if (j + 3 < n) {
+#pragma unroll 4
+    for (int i = r0; i < r1; ++i) {
+      float a[4];
+      vec_load(col + (int64_t)i * V.ld, a);
+      const double yi = (double)y[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += (double)a[e] * yi;
+    }
+  } else {
+    for (int i = r0; i < r1; ++i)
+      for (int e = 0; j + e < n; ++e) acc[e] += (double)col[(int64_t)i * V.ld + e] * (double)y[i];
+  }
+  for (int e = 0; e < 4 && j + e < n; ++e) part[(int64_t)blk * n + j + e] = (float)acc[e];
 }
 
 __global__ __launch_bounds__(kObs) void gemv_cols_final_kernel(const float* part, int nrb, int n,
@@ -197,8 +262,8 @@ mao_status gemv_rows(View V, int m, int n, const float* x, float* y, hipStream_t
 mao_status gemv_cols(View V, int m, int n, const float* y, float* part, int nrb, float* z,
                      hipStream_t s) {
   const int rpb = rows_per(m, nrb);
-  hipLaunchKernelGGL(gemv_cols_partial_kernel, dim3(nrb, (n + kObs - 1) / kObs), dim3(kObs), 0,
-                     s, V, m, n, rpb, y, part);
+  hipLaunchKernelGGL(gemv_cols_partial_kernel, dim3(nrb, (n + 4 * kObs - 1) / (4 * kObs)),
+                     dim3(kObs), 0, s, V, m, n, rpb, y, part);
   MAO_LAUNCH_CHECK();
   hipLaunchKernelGGL(gemv_cols_final_kernel, dim3((n + kObs - 1) / kObs), dim3(kObs), 0, s, part,
                      nrb, n, z);

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = mao.load()
-    assert lib.mao_abi_version() == 1
+    assert lib.mao_abi_version() == 2
     for code in range(10):
         assert lib.mao_status_string(code)
     assert lib.mao_status_string(99) == b"unknown status"
@@ -227,6 +227,19 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
     fst2 = mao.FoamStateC(fst.M, fst.R, fst.QR, None, fst.c, fst.aux)
     assert lib.foam_step(W, G, ctypes.byref(fst2), 1, ctypes.byref(fh), ws, fneed, None,
                          None) == E_NULL
+    assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(mao.foam_hparams(side=2)), ws,
+                         fneed, None, None) == E_HPARAM
+    # the output side keeps m x m factors: the n x n state is the wrong shape
+    fo = mao.foam_hparams(side="output")
+    oneed = lib.foam_workspace_size(m, n, ctypes.byref(fo))
+    assert oneed > 0
+    assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(fo), ws, oneed, None,
+                         None) == E_SHAPE
+    fso = mao.FoamStateC(fst.M, _mat(FAKE + (4 << 20), m, m, 8), _mat(FAKE + (6 << 20), m, m, 8),
+                         fst.r, fst.c, fst.aux)
+    assert lib.foam_step(W, G, ctypes.byref(fso), 1, ctypes.byref(fo), ws, oneed - 1, None,
+                         None) == E_WORKSPACE
+    assert lib.foam_step_many_workspace_size(1, ctypes.byref(W), ctypes.byref(fo)) > 0
 
     assert lib.adamw_step(FAKE, 0, FAKE + 4096, 0, FAKE + 8192, FAKE + 12288, 0, 1, 1e-3, 0.9,
                           0.95, 1e-8, 0.0, None, None) == E_SHAPE

@@ -114,11 +114,12 @@ def test_soap_bf16_gradient_and_frozen_basis(gpu_lib):
 
 # ---------------------------------------------------------------------------
 
-def _foam_state_dev(m, n):
+def _foam_state_dev(m, n, side="input"):
     import torch
+    k = m if side == "output" else n
     return {"M": torch.zeros((m, n), dtype=torch.float32, device="cuda"),
-            "R": torch.zeros((n, n), dtype=torch.float32, device="cuda"),
-            "QR": torch.eye(n, dtype=torch.float32, device="cuda"),
+            "R": torch.zeros((k, k), dtype=torch.float32, device="cuda"),
+            "QR": torch.eye(k, dtype=torch.float32, device="cuda"),
             "r": torch.zeros(m, dtype=torch.float32, device="cuda"),
             "c": torch.zeros(n, dtype=torch.float32, device="cuda"),
             "aux": torch.zeros(8, dtype=torch.float32, device="cuda")}
@@ -129,24 +130,27 @@ def _host_foam(st):
                             to_host(st["r"]), to_host(st["c"]))
 
 
-@pytest.mark.parametrize("m,n,pf", [(160, 96, 3), (96, 264, 4)])
-def test_foam_teacher_forced(gpu_lib, m, n, pf):
+@pytest.mark.parametrize("m,n,pf,side", [(160, 96, 3, "input"), (96, 264, 4, "input"),
+                                         (160, 96, 3, "output"), (264, 96, 4, "output")])
+def test_foam_teacher_forced(gpu_lib, m, n, pf, side):
+    """FOAM (input side) and its output-only ablation ([FOAM] section 3),
+    teacher-forced against the oracle."""
     import torch
-    log(f"foam {m}x{n} pf={pf}")
+    log(f"foam {side} {m}x{n} pf={pf}")
     spec = synth.MatrixSpec("f", m, n, 5)
     W = to_dev(synth.init_weight("c5", spec))
-    st = _foam_state_dev(m, n)
+    st = _foam_state_dev(m, n, side)
     out = torch.empty((m, n), dtype=torch.float32, device="cuda")
     t0 = math.ceil(max(m, n) / min(m, n)) + 2
     for t in range(1, 10):
         g = synth.kronecker_gradient("c5", spec, t)
         prev = _host_foam(st)
         w_prev = to_host(W)
-        gpu_lib.foam_step(W, to_dev(g), st, t, update_out=out, pf=pf, tol=0.1, **HP)
+        gpu_lib.foam_step(W, to_dev(g), st, t, update_out=out, pf=pf, tol=0.1, side=side, **HP)
         torch.cuda.synchronize()
         new = _host_foam(st)
         aux = to_host(st["aux"])
-        _, ref, _, info = oracle.foam_step(w_prev, g, prev, t, pf=pf, tol=0.1, **HP)
+        _, ref, _, info = oracle.foam_step(w_prev, g, prev, t, pf=pf, tol=0.1, side=side, **HP)
         assert bool(aux[3]) == info["checked"]
         assert rel(new.M, ref.M) < 1e-5 and rel(new.R, ref.R) < 1e-5
         decision = info["refreshed"]
@@ -161,7 +165,8 @@ def test_foam_teacher_forced(gpu_lib, m, n, pf):
             assert np.array_equal(new.QR, prev.QR)
         w_ref, ref2, upd_ref, info2 = oracle.foam_step(w_prev, g, prev, t, pf=pf, tol=0.1,
                                                        q_override=new.QR,
-                                                       refresh_override=decision, **HP)
+                                                       refresh_override=decision, side=side,
+                                                       **HP)
         eu = rel(to_host(out), upd_ref)
         er, ec = rel(new.r, ref2.r), rel(new.c, ref2.c)
         log(f"  foam t={t}: update {eu:.2e} r {er:.2e} c {ec:.2e} rho {aux[0]:.3f} refresh {decision}")
@@ -251,39 +256,42 @@ def test_soap_many_matches_separate_calls(gpu_lib, refresh_every):
             _close(Ws2[i], Ws1[i], f"t={t} matrix {i} W", 1e-6)
 
 
-def _foam_state_dev_many(m, n):
+def _foam_state_dev_many(m, n, side="input"):
     import torch
+    k = m if side == "output" else n
     return {"M": torch.zeros((m, n), dtype=torch.float32, device="cuda"),
-            "R": torch.zeros((n, n), dtype=torch.float32, device="cuda"),
-            "QR": torch.eye(n, dtype=torch.float32, device="cuda"),
+            "R": torch.zeros((k, k), dtype=torch.float32, device="cuda"),
+            "QR": torch.eye(k, dtype=torch.float32, device="cuda"),
             "r": torch.zeros(m, dtype=torch.float32, device="cuda"),
             "c": torch.zeros(n, dtype=torch.float32, device="cuda"),
             "aux": torch.zeros(4, dtype=torch.float32, device="cuda")}
 
 
-@pytest.mark.parametrize("pf,tol", [(1, 0.0), (2, 0.1), (1, 0.5)])
-def test_foam_many_matches_separate_calls(gpu_lib, pf, tol):
+@pytest.mark.parametrize("pf,tol,side", [(1, 0.0, "input"), (2, 0.1, "input"), (1, 0.5, "input"),
+                                         (1, 0.0, "output"), (2, 0.1, "output")])
+def test_foam_many_matches_separate_calls(gpu_lib, pf, tol, side):
     """foam_step_many against separate foam_step calls, with the criterion
     every step and a refresh every time (tol 0), every other step, and a
     tolerance under which some matrices refresh and others do not (the
     batched QR skips a job on its own device flag)."""
     import torch
-    log(f"foam many vs single, pf={pf} tol={tol}")
+    log(f"foam many vs single, pf={pf} tol={tol} side={side}")
     steps = 4
     ws, gs = _many_inputs(MANY_SHAPES, steps, 43)
     Ws1 = [to_dev(w) for w in ws]
     Ws2 = [to_dev(w) for w in ws]
-    st1 = [_foam_state_dev_many(m, n) for m, n in MANY_SHAPES]
-    st2 = [_foam_state_dev_many(m, n) for m, n in MANY_SHAPES]
+    st1 = [_foam_state_dev_many(m, n, side) for m, n in MANY_SHAPES]
+    st2 = [_foam_state_dev_many(m, n, side) for m, n in MANY_SHAPES]
     o1 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in MANY_SHAPES]
     o2 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in MANY_SHAPES]
     refreshed = set()
     for t in range(1, steps + 1):
         G = [to_dev(g[t - 1]) for g in gs]
         for i in range(len(MANY_SHAPES)):
-            gpu_lib.foam_step(Ws1[i], G[i], st1[i], t, update_out=o1[i], pf=pf, tol=tol, **HP)
+            gpu_lib.foam_step(Ws1[i], G[i], st1[i], t, update_out=o1[i], pf=pf, tol=tol,
+                              side=side, **HP)
         gpu_lib.foam_step_many([(Ws2[i], G[i], st2[i]) for i in range(len(MANY_SHAPES))], t,
-                               update_out=o2, pf=pf, tol=tol, **HP)
+                               update_out=o2, pf=pf, tol=tol, side=side, **HP)
         torch.cuda.synchronize()
         for i in range(len(MANY_SHAPES)):
             a1, a2 = to_host(st1[i]["aux"]), to_host(st2[i]["aux"])
