@@ -435,7 +435,11 @@ MAO_API size_t mao_rank1_share_workspace_size(int64_t rows, int64_t cols);
  * s_1 comes from `iters` (1..1000) steps of power iteration on V^T V from the
  * unit all-ones vector, each normalised; the estimate is ||V v||^2 for the
  * last unit iterate v, which never exceeds the true share beyond rounding.
- * A zero V gives 0.
+ * A zero V gives 0. Applied to the momentum M it is 1 / stable rank of M
+ * (s_1^2 / sum s_i^2), the one-number summary of M's singular-value
+ * distribution ([SMB] section 7-2); for a signed matrix the start vector is
+ * not aligned with a Perron vector, so give it enough iterations for the gap
+ * s_2 / s_1.
  */
 MAO_API mao_status mao_rank1_share(mao_mat V, int32_t iters, float* out, void* workspace,
                                    size_t workspace_bytes, void* stream);

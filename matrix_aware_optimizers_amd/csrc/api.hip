@@ -505,12 +505,13 @@ mao_status nt32(int M, int N, int K, const float* A, int64_t lda, const float* B
   return launch_gemm(MAO_F32, &p, 1, s);
 }
 
-// F <- beta F + (1 - beta) X X^T (fp32 SYRK, in place)
-mao_status syrk_ema(int N, int K, const float* X, int64_t ldx, float beta, float* F, int64_t ldf,
-                    hipStream_t s) {
+// F <- beta F + (1 - beta) X X^T (SYRK in place, fp32 F; X fp32 or bf16:
+// bf16 products are exact in fp32, so both accumulate alike in fp32)
+mao_status syrk_ema(int N, int K, const void* X, int64_t ldx, float beta, float* F, int64_t ldf,
+                    hipStream_t s, int x_dtype = MAO_F32) {
   GemmProblem p = gemm_problem(N, N, K, 1.f - beta, X, ldx, X, ldx, beta, F, ldf, F, ldf,
                                GF_SYRK | GF_D_F32 | GF_C0_F32);
-  return launch_gemm(MAO_F32, &p, 1, s);
+  return launch_gemm(x_dtype, &p, 1, s);
 }
 
 }  // namespace
@@ -639,14 +640,22 @@ mao_status soap_pre(const mao_mat& W, const mao_mat& G, const mao_soap_state* st
   // 1. momentum
   MAO_TRY(ema_sumsq(view(M, st->M.ld), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr,
                     rowblocks_for(m, 1), s));
-  // fp32 G and G^T
-  const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
-  const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
-  MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
-                             view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
   // 2. factor EMAs with the current gradient
-  MAO_TRY(syrk_ema(m, n, Gf, ldG, b2, (float*)st->L.data, st->L.ld, s));
-  MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, (float*)st->R.data, st->R.ld, s));
+  if (G.dtype == MAO_BF16) {
+    // bf16 G: the SYRKs run on the bf16 MFMA path (exact products, fp32
+    // accumulation); G^T in bf16 goes to T2t, which is free until the
+    // rotations; the rotations take the fp32 copy of G
+    MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n, view(R.Gf, R.ldn),
+                               view(nullptr, 0), s));
+    MAO_TRY(transpose(view(G.data, G.ld), view(R.T2t, R.ldm), m, n, 1, MAO_BF16, s));
+    MAO_TRY(syrk_ema(m, n, G.data, G.ld, b2, (float*)st->L.data, st->L.ld, s, MAO_BF16));
+    MAO_TRY(syrk_ema(n, m, R.T2t, R.ldm, b2, (float*)st->R.data, st->R.ld, s, MAO_BF16));
+  } else {
+    MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n, view(nullptr, 0),
+                               view(R.Gtf, R.ldm), s));
+    MAO_TRY(syrk_ema(m, n, G.data, G.ld, b2, (float*)st->L.data, st->L.ld, s));
+    MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, (float*)st->R.data, st->R.ld, s));
+  }
   // 3a. E = Q^T of both bases
   MAO_TRY(transpose(view(st->QL.data, st->QL.ld), view(R.EL, R.ldm), m, m, 1, MAO_F32, s));
   return transpose(view(st->QR.data, st->QR.ld), view(R.ER, R.ldn), n, n, 1, MAO_F32, s);

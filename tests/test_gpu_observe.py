@@ -155,6 +155,26 @@ def test_rank1_share(gpu_lib, m, n):
     assert zero == 0.0
 
 
+def test_rank1_share_of_a_signed_momentum_is_inverse_stable_rank(gpu_lib):
+    """On a signed matrix built from known singular values the share is
+    s_1^2 / sum s_i^2 = 1 / stable rank, the summary of the momentum's
+    singular-value distribution; the all-ones start still converges."""
+    import torch
+    log("rank-1 share of a signed matrix with known singular values")
+    r = np.random.default_rng(46)
+    m, n, k = 384, 200, 200
+    u = oracle.qr_positive(r.standard_normal((m, m)))[0][:, :k]
+    v = oracle.qr_positive(r.standard_normal((n, n)))[0][:, :k]
+    s = np.concatenate([[4.0, 2.0], np.linspace(1.0, 0.01, k - 2)])
+    x = (u * s) @ v.T
+    want = s[0] ** 2 / np.sum(s * s)
+    assert want == pytest.approx(oracle.rank1_share(x), rel=1e-10)
+    got = float(to_host(gpu_lib.rank1_share(to_dev(x.astype(np.float32)), iters=40))[0])
+    torch.cuda.synchronize()
+    log(f"  share {got:.6f} (1 / stable rank {want:.6f})")
+    assert abs(got - want) <= 1e-5
+
+
 def test_basis_age_follows_foam_refreshes(gpu_lib):
     """The device age tracks the refresh flag each foam_step writes."""
     import torch
