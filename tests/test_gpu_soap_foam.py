@@ -112,6 +112,15 @@ def test_soap_bf16_gradient_and_frozen_basis(gpu_lib):
               dtype="bf16", refresh_every=0)
 
 
+def test_soap_bf16_gradient_refreshing_ragged(gpu_lib):
+    """bf16 gradients (factor EMAs on the bf16 MFMA path, in place) with a
+    refresh every step on a shape of several 256-tiles with ragged edges."""
+    log("soap bf16 refreshing 296x520")
+    spec = synth.MatrixSpec("k", 296, 520, 6)
+    _run_soap(gpu_lib, 296, 520, 6, lambda t: synth.kronecker_gradient("c3", spec, t),
+              dtype="bf16", refresh_every=1)
+
+
 # ---------------------------------------------------------------------------
 
 def _foam_state_dev(m, n, side="input"):
@@ -130,13 +139,16 @@ def _host_foam(st):
                             to_host(st["r"]), to_host(st["c"]))
 
 
-@pytest.mark.parametrize("m,n,pf,side", [(160, 96, 3, "input"), (96, 264, 4, "input"),
-                                         (160, 96, 3, "output"), (264, 96, 4, "output")])
-def test_foam_teacher_forced(gpu_lib, m, n, pf, side):
+@pytest.mark.parametrize("m,n,pf,side,gdt", [(160, 96, 3, "input", "f32"), (96, 264, 4, "input", "f32"),
+                                             (160, 96, 3, "output", "f32"),
+                                             (264, 96, 4, "output", "f32"),
+                                             (96, 160, 3, "input", "bf16"),
+                                             (160, 96, 3, "output", "bf16")])
+def test_foam_teacher_forced(gpu_lib, m, n, pf, side, gdt):
     """FOAM (input side) and its output-only ablation ([FOAM] section 3),
-    teacher-forced against the oracle."""
+    teacher-forced against the oracle, with fp32 and bf16 gradients."""
     import torch
-    log(f"foam {side} {m}x{n} pf={pf}")
+    log(f"foam {side} {m}x{n} pf={pf} {gdt} gradient")
     spec = synth.MatrixSpec("f", m, n, 5)
     W = to_dev(synth.init_weight("c5", spec))
     st = _foam_state_dev(m, n, side)
@@ -144,9 +156,12 @@ def test_foam_teacher_forced(gpu_lib, m, n, pf, side):
     t0 = math.ceil(max(m, n) / min(m, n)) + 2
     for t in range(1, 10):
         g = synth.kronecker_gradient("c5", spec, t)
+        if gdt == "bf16":
+            g = bf16_round(g)
         prev = _host_foam(st)
         w_prev = to_host(W)
-        gpu_lib.foam_step(W, to_dev(g), st, t, update_out=out, pf=pf, tol=0.1, side=side, **HP)
+        gpu_lib.foam_step(W, to_dev(g, gdt), st, t, update_out=out, pf=pf, tol=0.1, side=side,
+                          **HP)
         torch.cuda.synchronize()
         new = _host_foam(st)
         aux = to_host(st["aux"])
