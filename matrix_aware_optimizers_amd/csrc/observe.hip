@@ -170,13 +170,30 @@ __global__ __launch_bounds__(kObs) void gemv_cols_partial_kernel(View V, int m, 
   for (int e = 0; e < 4 && j + e < n; ++e) part[(int64_t)blk * n + j + e] = (float)acc[e];
 }
 
+// 64 columns per workgroup, four lanes per column: lane group g sums row
+// blocks [g q, (g + 1) q) in order with eight loads in flight, then the four
+// group sums are added in order g = 0..3 (fixed order: bitwise repeatable).
 __global__ __launch_bounds__(kObs) void gemv_cols_final_kernel(const float* part, int nrb, int n,
                                                                float* z) {
-  const int j = blockIdx.x * kObs + threadIdx.x;
-  if (j >= n) return;
+  __shared__ double gs[4][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + c;
+  const int q = (nrb + 3) / 4, b0 = g * q, b1 = min(nrb, b0 + q);
   double acc = 0.0;
-  for (int b = 0; b < nrb; ++b) acc += (double)part[(int64_t)b * n + j];
-  z[j] = (float)acc;
+  if (j < n) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(b + u) * n + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += (double)v[u];
+    }
+    for (; b < b1; ++b) acc += (double)part[(int64_t)b * n + j];
+  }
+  gs[g][c] = acc;
+  __syncthreads();
+  if (g == 0 && j < n) z[j] = (float)(((gs[0][c] + gs[1][c]) + gs[2][c]) + gs[3][c]);
 }
 
 __global__ __launch_bounds__(1024) void normalize_kernel(float* v, int n) {
@@ -265,8 +282,8 @@ mao_status gemv_cols(View V, int m, int n, const float* y, float* part, int nrb,
   hipLaunchKernelGGL(gemv_cols_partial_kernel, dim3(nrb, (n + 4 * kObs - 1) / (4 * kObs)),
                      dim3(kObs), 0, s, V, m, n, rpb, y, part);
   MAO_LAUNCH_CHECK();
-  hipLaunchKernelGGL(gemv_cols_final_kernel, dim3((n + kObs - 1) / kObs), dim3(kObs), 0, s, part,
-                     nrb, n, z);
+  hipLaunchKernelGGL(gemv_cols_final_kernel, dim3((n + 63) / 64), dim3(kObs), 0, s, part, nrb, n,
+                     z);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }
