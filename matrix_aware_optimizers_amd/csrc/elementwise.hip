@@ -38,8 +38,8 @@ template <> struct Vec4<bf16_t> {
   }
   static __device__ __forceinline__ void store(bf16_t* p, const float v[4]) {
     uint2 u;
-    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
     *(uint2*)p = u;
   }
 };
@@ -98,10 +98,10 @@ __device__ __forceinline__ void store8(T* row, int j, int cols, const float v[8]
       Vec4<float>::store((float*)row + j + 4, v + 4);
     } else {
       uint4 u;
-      u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-      u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-      u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-      u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+      u.x = pack_bf16x2(v[0], v[1]);
+      u.y = pack_bf16x2(v[2], v[3]);
+      u.z = pack_bf16x2(v[4], v[5]);
+      u.w = pack_bf16x2(v[6], v[7]);
       *(uint4*)(row + j) = u;
     }
   } else {
@@ -288,10 +288,10 @@ __global__ __launch_bounds__(kBlock) void x0_tiled_kernel(View In, int rows, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = trans ? tile[ck + e][ri] : tile[ri][ck + e];
     uint4 pk;
-    pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-    pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    pk.x = pack_bf16x2(v[0], v[1]);
+    pk.y = pack_bf16x2(v[2], v[3]);
+    pk.z = pack_bf16x2(v[4], v[5]);
+    pk.w = pack_bf16x2(v[6], v[7]);
     *(uint4*)(xb + t32_off(i0 + ri, k0 + ck, xcp)) = pk;
   }
 }

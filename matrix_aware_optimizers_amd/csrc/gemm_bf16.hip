@@ -490,8 +490,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
                 *(float4*)((float*)D + off) = make_float4(v[0], v[1], v[2], v[3]);
               } else {
                 uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                pk.x = pack_bf16x2(v[0], v[1]);
+                pk.y = pack_bf16x2(v[2], v[3]);
                 *(uint2*)((bf16_t*)D + off) = pk;
               }
             } else {
@@ -522,8 +522,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
               *(float4*)((float*)Tt + off) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
               uint2 pk;
-              pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-              pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+              pk.x = pack_bf16x2(v[0], v[1]);
+              pk.y = pack_bf16x2(v[2], v[3]);
               *(uint2*)((bf16_t*)Tt + off) = pk;
             }
           } else {
