@@ -74,19 +74,41 @@ struct EpiArgs {
   float dadd = 0.f;  // added to D[i][i], i < M
 };
 
-template <bool CHECKED>
-__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], float* b0, float* b1,
+// LB: staging addresses from eight per-lane bases (fewer live registers in the
+// tiled kernels); otherwise computed per element. HC0: the tile has a C0 term.
+// Without one the row pass issues no loads, so nothing waits on the memory
+// counter there: the counter covers loads and stores alike and retires them
+// in order, so a wait for a C0 load also waits for every store issued before
+// it.
+template <bool CHECKED, bool LB = false, bool HC0 = true>
+__device__ __forceinline__ void staged_epilogue_impl(const f32x16_t (&acc)[4][4], float* b0, float* b1,
                                                 float* b2, float* b3, const EpiArgs& e) {
   constexpr int TB = 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
+  // Staging address of acc[I][j][v]: row rb = 8 g + 4 h + i (g = v / 4,
+  // i = v % 4), column (wn 128 + 32 j + r32) ^ epi_swz(rb, I). The swizzle
+  // flips column bits 3-4 by g and bit 5 by (h ^ I) & 1, so the address is
+  // one of eight per-lane bases (parity p = (j ^ I) & 1, group g) plus a
+  // compile-time offset: no per-element address arithmetic.
+  int lb[2][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      lb[p][g] = 4 * h * TB + wn * 128 + (r32 ^ (g << 3)) + (((p ^ h) & 1) << 5);
 #define MAO_BAND(I, ST)                                                                   \
   _Pragma("unroll") for (int j = 0; j < 4; ++j)                                           \
   _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                        \
-    const int rb_ = 8 * (v >> 2) + 4 * h + (v & 3);                                       \
-    const int col_ = (wn * 128 + j * 32 + r32) ^ epi_swz(rb_, I);                         \
-    (ST)[rb_ * TB + col_] = acc[I][j][v];                                                 \
+    if constexpr (LB) {                                                                   \
+      (ST)[lb[(j ^ (I)) & 1][v >> 2] + (8 * (v >> 2) + (v & 3)) * TB + (j >> 1) * 64] =    \
+          acc[I][j][v];                                                                   \
+    } else {                                                                              \
+      const int rb_ = 8 * (v >> 2) + 4 * h + (v & 3);                                     \
+      const int col_ = (wn * 128 + j * 32 + r32) ^ epi_swz(rb_, I);                       \
+      (ST)[rb_ * TB + col_] = acc[I][j][v];                                               \
+    }                                                                                     \
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -97,7 +119,64 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], flo
       MAO_BAND(3, b3)
     }
     __syncthreads();
-    {
+    if constexpr (!HC0) {
+      // no C0: per group of four rows, the eight LDS reads are issued before
+      // any row is finished, so their latency is paid once per group
+      const int c8 = (threadIdx.x & 31) * 8;
+      const int64_t gcol = e.n0 + c8;
+      const bool cfull = !CHECKED || gcol + 8 <= e.N;
+#pragma unroll 1
+      for (int it0 = 0; it0 < 16; it0 += 4) {
+        float4 xs[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = (it0 + u) * 8 + (threadIdx.x >> 5);
+          const int band = row >> 5, rb = row & 31;
+          const float* bp = band == 0 ? b0 : band == 1 ? b1 : band == 2 ? b2 : b3;
+          const float* src = bp + rb * TB + (c8 ^ epi_swz(rb, band));
+          xs[u][0] = *(const float4*)src;
+          xs[u][1] = *(const float4*)(src + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = (it0 + u) * 8 + (threadIdx.x >> 5);
+          const int band = row >> 5, rb = row & 31;
+          const int64_t grow = e.m0 + half * 128 + row;
+          if (CHECKED && (grow >= e.M || gcol >= e.N)) continue;
+          float v[8] = {xs[u][0].x, xs[u][0].y, xs[u][0].z, xs[u][0].w,
+                        xs[u][1].x, xs[u][1].y, xs[u][1].z, xs[u][1].w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] *= e.alpha;
+          if (e.dadd != 0.f && grow < e.M) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (grow == gcol + q) v[q] += e.dadd;
+          }
+          if (e.rs) {
+            const float sc = e.rs[grow];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= sc;
+          }
+          if (e.D) {
+            const int64_t off = e.d_t32 ? t32_off(grow, gcol, e.ldd) : grow * e.ldd + gcol;
+            if (cfull && (!e.diag || grow >= gcol + 7)) {
+              store8_any(e.D, e.d32, off, v);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 8; ++q)
+                if ((!CHECKED || gcol + q < e.N) && (!e.diag || grow >= gcol + q))
+                  d_store(e.D, e.d32, off + q, v[q]);
+            }
+          }
+          if (e.Tt) {
+            float* dst = (band == 0 ? b0 : band == 1 ? b1 : band == 2 ? b2 : b3) + rb * TB +
+                         (c8 ^ epi_swz(rb, band));
+            *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          }
+        }
+      }
+    } else {
       const int c8 = (threadIdx.x & 31) * 8;
       const int64_t gcol = e.n0 + c8;
       const bool cfull = !CHECKED || gcol + 8 <= e.N;
@@ -110,7 +189,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], flo
           const int64_t grow = e.m0 + half * 128 + (it0 + u) * 8 + (threadIdx.x >> 5);
 #pragma unroll
           for (int q = 0; q < 8; ++q) cv[u][q] = 0.f;
-          if (!e.C0 || (CHECKED && (grow >= e.M || gcol >= e.N))) continue;
+          if (!HC0 || !e.C0 || (CHECKED && (grow >= e.M || gcol >= e.N))) continue;
           const int64_t off = e.c_t32 ? t32_off(grow, gcol, e.ldc0) : grow * e.ldc0 + gcol;
           if (cfull && e.c32) {
             const float* cp = (const float*)e.C0 + off;
@@ -142,7 +221,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], flo
           const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
           float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] = e.alpha * v[q] + (e.C0 ? e.beta * cv[u][q] : 0.f);
+          for (int q = 0; q < 8; ++q) v[q] = e.alpha * v[q] + ((HC0 && e.C0) ? e.beta * cv[u][q] : 0.f);
           if (e.dadd != 0.f && grow < e.M) {
 #pragma unroll
             for (int q = 0; q < 8; ++q)
@@ -199,6 +278,17 @@ __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], flo
     __syncthreads();
   }
 #undef MAO_BAND
+}
+
+template <bool CHECKED, bool LB = false>
+__device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], float* b0, float* b1,
+                                                float* b2, float* b3, const EpiArgs& e) {
+  // the tiled kernels (LB) take a C0-free copy; the others keep one general
+  // copy, which their register budget allows
+  if (!LB || e.C0)
+    staged_epilogue_impl<CHECKED, LB, true>(acc, b0, b1, b2, b3, e);
+  else
+    staged_epilogue_impl<CHECKED, LB, false>(acc, b0, b1, b2, b3, e);
 }
 
 }  // namespace mao

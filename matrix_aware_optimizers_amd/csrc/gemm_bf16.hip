@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
     ea.d_t32 = dt32;
     ea.t_t32 = syrk && dt32;
     ea.dadd = T32 ? P.dadd : 0.f;
-    staged_epilogue<false>(acc, (float*)st0, (float*)st1, (float*)st2, (float*)st3, ea);
+    staged_epilogue<false, T32>(acc, (float*)st0, (float*)st1, (float*)st2, (float*)st3, ea);
     return;
   }
   if constexpr (T32) {
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
     ea.diag = diag;
     ea.c_t32 = (P.flags & GF_C0_T32) != 0;
     ea.dadd = P.dadd;
-    staged_epilogue<true>(acc, (float*)st0, (float*)st1, (float*)st2, (float*)st3, ea);
+    staged_epilogue<true, true>(acc, (float*)st0, (float*)st1, (float*)st2, (float*)st3, ea);
     return;
   } else {
   float* slab = (float*)st0;
