@@ -248,6 +248,37 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_rank128_kernel(GemmArgs args)
 
   if (!D) return;
   const float alpha = P.alpha, beta = P.beta;
+  if (d32 && m0 + TS <= M && n0 + TS <= N && P.ldd % 4 == 0) {
+    // A full fp32 tile goes through LDS (rows 0-63 over As, 64-127 over Bs,
+    // both free once the products are done) and leaves in 16-byte pieces: a
+    // quarter of the store instructions of the per-element stores below, which
+    // the CU's store drain paces. Same values, stored in a different order.
+    __syncthreads();
+    constexpr int LT = 132;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int lc = 64 * wn + 32 * j + r32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int lr = 64 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          float x = alpha * acc[i][j][v] + (C0 ? beta * cv[i][j][v] : 0.f);
+          if (rs) x *= rs[m0 + lr];
+          float* dst = lr < 64 ? As + lr * LT + lc : Bs + (lr - 64) * LT + lc;
+          *dst = x;
+        }
+      }
+    __syncthreads();
+    const int c4 = (threadIdx.x & 31) * 4;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int lr = it * 8 + (threadIdx.x >> 5);
+      const float* src = lr < 64 ? As + lr * LT + c4 : Bs + (lr - 64) * LT + c4;
+      *(float4*)((float*)D + (int64_t)(m0 + lr) * P.ldd + n0 + c4) = *(const float4*)src;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
