@@ -53,7 +53,7 @@ def log(msg: str):
 # was taken on and is reported only while they are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_contraction_llama8b_layer_traffic.json")
 GEMM_SOURCES = [os.path.join(ROOT, "matrix_aware_optimizers_amd", "csrc", f)
-                for f in ("gemm_bf16.hip", "gemm.hip", "gemm.hpp", "epilogue.hpp", "tiled.hpp",
+                for f in ("gemm_direct.hip", "gemm.hip", "gemm.hpp", "epilogue.hpp", "tiled.hpp",
                           "common.hpp")]
 NS_KERNEL = "gemm_bf16_dl_kernel"
 COPY_KERNEL = "copyBuffer"
@@ -454,7 +454,7 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
                    **({"side": side} if kind == "foam" else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
-                     "kernel": "gemm_nt_kernel<float> (all fp32 contractions)"},
+                     "kernel": "all timed contractions of the step (gemm_f32_dl_kernel rotations and products, QR updates and projections)"},
         "kernels": per_tag,
     }
 

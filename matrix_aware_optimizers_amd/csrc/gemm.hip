@@ -400,8 +400,10 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
   // tiles however many there are: a 128-wide tile would compute half zeros.
   bool skinny = true;
   for (int i = 0; i < nprob; ++i) skinny = skinny && probs[i].N <= 64;
+  const bool big = in_dtype == MAO_BF16 ? (nkm != 0 || nt != 0 || count_tiles(probs, nprob, 256) >= 128)
+                                         : (!skinny && count_tiles(probs, nprob, 256) >= 128);
   const int bm = rank128 ? 128
-                 : (rank || (in_dtype == MAO_BF16 && (nkm != 0 || nt != 0 || count_tiles(probs, nprob, 256) >= 128))) ? 256
+                 : (rank || big) ? 256
                  : (!skinny && count_tiles(probs, nprob, 128) >= 512) ? 128 : 64;
   // Longest K first: the last tiles to start are the short ones.
   int order[kMaxProblems];
@@ -435,7 +437,8 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
     st = bm == 256 ? launch_gemm_bf16_direct(args, stream)
          : bm == 128 ? launch_cfg<bf16_t, 128, 128>(args, stream) : launch_cfg<bf16_t, 64, 64>(args, stream);
   else
-    st = bm == 128 ? launch_cfg<float, 128, 128>(args, stream) : launch_cfg<float, 64, 64>(args, stream);
+    st = bm == 256 ? launch_gemm_f32_direct(args, stream)
+         : bm == 128 ? launch_cfg<float, 128, 128>(args, stream) : launch_cfg<float, 64, 64>(args, stream);
   if (timed) {
     double flops = 0.0;
     for (int i = 0; i < n; ++i) {

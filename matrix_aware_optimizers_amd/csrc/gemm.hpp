@@ -84,8 +84,11 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
                        int tag = TAG_OTHER);
 
 // bf16 path for large problems: 256 x 256 tiles, operands streamed into a
-// four-stage LDS ring (gemm_bf16.hip). Same semantics as gemm_nt_kernel.
+// four-stage LDS ring (gemm_direct.hip). Same semantics as gemm_nt_kernel.
 mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream);
+// The same kernel on fp32 operands (N x K B only, row-major), 16 K elements
+// per slice on v_mfma_f32_32x32x2f32.
+mao_status launch_gemm_f32_direct(GemmArgs& args, hipStream_t stream);
 
 // fp32 rank-k updates, k <= 64, 256 x 256 tiles (gemm_f32_rank.hip).
 mao_status launch_gemm_f32_rank(GemmArgs& args, hipStream_t stream);

@@ -1,14 +1,18 @@
-// Large bf16 contractions (the Newton-Schulz products) with operands streamed
-// straight from memory into LDS.
+// Large contractions (the Newton-Schulz products in bf16, the SOAP / FOAM
+// rotations and factor products in fp32) with operands streamed straight from
+// memory into LDS.
 //
-// D[i][j] = alpha * sum_k A[i][k] * B(j, k) + beta * C0[i][j], bf16 inputs,
-// fp32 accumulation on v_mfma_f32_32x32x16_bf16. B is either N x K (rows
-// K-contiguous, as A) or K x N (the Newton-Schulz product B X reads X this
-// way, so no transposed copy of X is ever written).
+// D[i][j] = alpha * sum_k A[i][k] * B(j, k) + beta * C0[i][j], fp32
+// accumulation on v_mfma_f32_32x32x16_bf16 (bf16 inputs) or
+// v_mfma_f32_32x32x2f32 (fp32 inputs). B is either N x K (rows K-contiguous,
+// as A) or, for bf16, K x N (the Newton-Schulz product B X reads X this way,
+// so no transposed copy of X is ever written).
 //
 // Workgroup tile 256 x 256, 4 wavefronts in 2 x 2, each wavefront 128 x 128
 // (4 x 4 MFMA blocks, 256 fp32 accumulators per lane). K advances in slices of
-// 32 elements. Slices go global -> LDS with global_load_lds_dwordx4 (no
+// 64 bytes per row (32 bf16 or 16 fp32 elements); a 16-byte chunk feeds one
+// bf16 MFMA or four fp32 MFMAs, so an fp32 slice carries eight times the
+// matrix-core work of a bf16 one over the same loads. Slices go global -> LDS with global_load_lds_dwordx4 (no
 // staging registers) into a ring of four LDS stages, each its own LDS object,
 // which lets the wait on a slice be an exact vmcnt rather than a full drain.
 // The operand fragments of the next 16-deep MFMA step are read from LDS while
@@ -44,14 +48,17 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int TB = 256;          // tile rows and columns
-constexpr int KS = 32;           // K elements per slice
-constexpr int ROWB = 64;         // bytes per tile row per slice
+constexpr int ROWB = 64;         // bytes per tile row per slice (32 bf16 or 16 fp32 of K)
 constexpr int STAGE = 2 * TB * ROWB;  // A and B of one slice: 32 KB
 constexpr int LPT = (TB * ROWB / 16) / 256;  // 16-byte loads per thread per operand = 4
 constexpr int SLAB_LD = TB + 1;
 constexpr int SLAB_BYTES = 32 * SLAB_LD * 4;  // 32 rows of the output tile
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+__device__ __forceinline__ uint32_t u4_at(const uint4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
 
 // K x N operand B: a slice is 32 k-rows of 512 bytes (the tile's 256 columns);
 // 16-byte chunk c of k-row r sits at chunk c ^ bkswz(r), so the transposing
@@ -69,8 +76,12 @@ __device__ __forceinline__ void vm_wait_c() { __builtin_amdgcn_s_waitcnt(MAO_VMC
 
 
 
-template <bool BKM, bool T32>
-__global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
+template <typename TIn, bool BKM, bool T32>
+__device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
+  static_assert(sizeof(TIn) == 2 || (!BKM && !T32), "K x N and tiled operands are bf16 only");
+  constexpr bool F32 = sizeof(TIn) == 4;
+  constexpr int EPC = 16 / (int)sizeof(TIn);  // elements per 16-byte chunk
+  constexpr int KS = ROWB / (int)sizeof(TIn);  // K elements per slice
   __shared__ __attribute__((aligned(16))) unsigned char st0[(T32 || STAGE > SLAB_BYTES) ? STAGE : SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE];
@@ -104,8 +115,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   }
   const int m0 = tm * TB, n0 = tn * TB;
   const int M = P.M, N = P.N, K = P.K;
-  const bf16_t* A = (const bf16_t*)P.A + (int64_t)b * P.sA;
-  const bf16_t* B = (const bf16_t*)P.B + (int64_t)b * P.sB;
+  const TIn* A = (const TIn*)P.A + (int64_t)b * P.sA;
+  const TIn* B = (const TIn*)P.B + (int64_t)b * P.sB;
   const int64_t lda = P.lda, ldb = P.ldb;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -120,8 +131,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   // Tiled operands: load p of wave w copies half-block (p * 4 + w) of the
   // slice, 1 KB read whole: block (8 tm + q / 2, slice) of A (and of an N x K
   // B), block (slice, 8 tn + q / 2) of a K x N B.
-  const bf16_t* asrc[LPT];
-  const bf16_t* bsrc[LPT];
+  const TIn* asrc[LPT];
+  const TIn* bsrc[LPT];
 #pragma unroll
   for (int p = 0; p < LPT; ++p) {
     if constexpr (T32) {
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
     const int row = L >> 2, slot = L & 3;
     const int ch = slot ^ swz(row);
     const int ra = min(m0 + row, M - 1);
-    asrc[p] = A + (int64_t)ra * lda + ch * 8;
+    asrc[p] = A + (int64_t)ra * lda + ch * EPC;
     if constexpr (BKM) {
       const int kr = 8 * p + 2 * wave + (lane >> 5);
       const int lc = (lane & 31) ^ bkswz(kr);
@@ -146,7 +157,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
       bsrc[p] = B + (int64_t)kr * ldb + col;
     } else {
       const int rb = min(n0 + row, N - 1);
-      bsrc[p] = B + (int64_t)rb * ldb + ch * 8;
+      bsrc[p] = B + (int64_t)rb * ldb + ch * EPC;
     }
   }
   // K offset k0 (elements) of a slice: along rows of A (and of an N x K B),
@@ -166,9 +177,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
                                        0, 0);
   };
 
-  // MFMA operand reads. Sub-step s of a slice multiplies K elements
-  // 16 h + 8 s .. + 7 of lane half h (the same permutation on both operands).
-  // A (and an N x K B): lane (h, r32) reads 16-byte chunk 2 h + s of its rows.
+  // MFMA operand reads. Sub-step s of a slice multiplies the K elements of
+  // 16-byte chunk 2 h + s in lane half h (bf16: one 16-deep MFMA; fp32: four
+  // 2-deep MFMAs, element e of every lane's chunk in the e-th), the same
+  // permutation on both operands. A (and an N x K B): lane (h, r32) reads
+  // chunk 2 h + s of its rows.
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
   const int arow = wm * 128 + r32, brow = wn * 128 + r32;
@@ -238,20 +251,30 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
     FA[3] = *(const uint4*)(STG + ao_ + 96 * ROWB);                                         \
     MAO_BFRAG(STG, SUB, 3, FB[3])                                                           \
   }
+  // fp32: the four 2-deep steps of a sub-step run over all 16 blocks in turn,
+  // so consecutive MFMAs never accumulate into the same block.
 #define MAO_MF(FA, FB, I, J)                                                                \
-  acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, FA[I]),   \
-                                                      __builtin_bit_cast(bf16x8_t, FB[J]),   \
-                                                      acc[I][J], 0, 0, 0);
+  if constexpr (F32) {                                                                      \
+    acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(u4_at(FA[I], e_)),     \
+                                                     __uint_as_float(u4_at(FB[J], e_)),     \
+                                                     acc[I][J], 0, 0, 0);                   \
+  } else {                                                                                  \
+    acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, FA[I]), \
+                                                        __builtin_bit_cast(bf16x8_t, FB[J]), \
+                                                        acc[I][J], 0, 0, 0);                \
+  }
 #define MAO_MFMA16(FA, FB)                                                                  \
+  _Pragma("unroll") for (int e_ = 0; e_ < (F32 ? 4 : 1); ++e_) {                           \
   MAO_MF(FA, FB, 0, 0) MAO_MF(FA, FB, 0, 1) MAO_MF(FA, FB, 1, 0) MAO_MF(FA, FB, 1, 1)       \
   MAO_MF(FA, FB, 0, 2) MAO_MF(FA, FB, 1, 2) MAO_MF(FA, FB, 2, 0) MAO_MF(FA, FB, 2, 1)       \
   MAO_MF(FA, FB, 2, 2) MAO_MF(FA, FB, 0, 3) MAO_MF(FA, FB, 1, 3) MAO_MF(FA, FB, 2, 3)       \
-  MAO_MF(FA, FB, 3, 0) MAO_MF(FA, FB, 3, 1) MAO_MF(FA, FB, 3, 2) MAO_MF(FA, FB, 3, 3)
+  MAO_MF(FA, FB, 3, 0) MAO_MF(FA, FB, 3, 1) MAO_MF(FA, FB, 3, 2) MAO_MF(FA, FB, 3, 3)       \
+  }
   // Instruction order inside a sub-step: an operand read (and, in the second
   // sub-step, a direct load) after each of the first MFMAs.
 #define MAO_SCHED(NR, NV)                                                                   \
   {                                                                                         \
-    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                                    \
+    _Pragma("unroll") for (int q_ = 0; q_ < (F32 ? 64 : 16); ++q_) {                       \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                    \
       if (q_ < (NV)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                     \
       if (q_ < (NR)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     \
@@ -346,19 +369,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
       const int L = (p * 4 + wave) * 64 + lane;
       union U {
         uint4 v;
-        bf16_t e[8];
+        TIn e[EPC];
       } ua, ub;
       ua.v = make_uint4(0, 0, 0, 0);
       ub.v = make_uint4(0, 0, 0, 0);
       {
         const int row = L >> 2, slot = L & 3;
-        const int k = ktail + (slot ^ swz(row)) * 8;
+        const int k = ktail + (slot ^ swz(row)) * EPC;
         if (m0 + row < M)
-          for (int e = 0; e < 8; ++e)
+          for (int e = 0; e < EPC; ++e)
             if (k + e < K) ua.e[e] = A[(int64_t)(m0 + row) * lda + k + e];
         if constexpr (!BKM) {
           if (n0 + row < N)
-            for (int e = 0; e < 8; ++e)
+            for (int e = 0; e < EPC; ++e)
               if (k + e < K) ub.e[e] = B[(int64_t)(n0 + row) * ldb + k + e];
         }
       }
@@ -538,7 +561,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
   }  // !T32
 }
 
+template <bool BKM, bool T32>
+__global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
+  gemm_dl_body<bf16_t, BKM, T32>(args);
+}
+
+__global__ __launch_bounds__(256) void gemm_f32_dl_kernel(GemmArgs args) {
+  gemm_dl_body<float, false, false>(args);
+}
+
 }  // namespace
+
+mao_status launch_gemm_f32_direct(GemmArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_f32_dl_kernel, dim3(args.total_tiles), dim3(256), 0, stream, args);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
 
 mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream) {
   const bool bkm = (args.p[0].flags & GF_B_KMAJOR) != 0, t32 = (args.p[0].flags & GF_T32) != 0;

@@ -13,8 +13,9 @@ pytestmark = pytest.mark.gpu
 
 GEMM_SHAPES = [(1, 1, 1), (64, 64, 64), (130, 77, 203), (300, 257, 500), (513, 129, 64),
                (1024, 1000, 1536),
-               # large enough for the 256 x 256 streamed bf16 kernel, ragged in M, N, K
-               (4100, 2052, 1060), (2304, 4352, 8),
+               # large enough for the 256 x 256 streamed kernels, ragged in M, N, K;
+               # whole tiles with K a multiple of the slice
+               (4100, 2052, 1060), (2304, 4352, 8), (2048, 4096, 1024),
                # rank-k updates (k <= 64) on the fp32 256 x 256 rank kernel
                (1500, 1300, 64), (4100, 2052, 40), (1030, 1030, 1)]
 
