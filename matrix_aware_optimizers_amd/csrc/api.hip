@@ -494,24 +494,100 @@ mao_status check_adam_hp(float lr, float b1, float b2, float eps, float wd) {
   return MAO_OK;
 }
 
+// Products of one phase of a many-matrix step (none reads another's result)
+// are collected and launched together: products equal in shape, leading
+// dimensions, scalars, flags and input type form one pointer-table batch
+// (tables written into the step's workspace), up to kMaxProblems batches per
+// launch. Without a batch a product launches at once.
+struct GemmBatch {
+  struct Item {
+    GemmProblem p;
+    int dtype;
+  };
+  std::vector<Item> items;
+  const void** table = nullptr;  // device, `capacity` pointers
+  int64_t capacity = 0;
+};
+
+mao_status gemm_add(GemmBatch* gb, const GemmProblem& p, int dtype, hipStream_t s) {
+  if (gb == nullptr) {
+    GemmProblem q = p;
+    return launch_gemm(dtype, &q, 1, s);
+  }
+  gb->items.push_back({p, dtype});
+  return MAO_OK;
+}
+
+bool same_batch(const GemmBatch::Item& a, const GemmBatch::Item& b) {
+  const GemmProblem &x = a.p, &y = b.p;
+  return a.dtype == b.dtype && x.M == y.M && x.N == y.N && x.K == y.K && x.lda == y.lda &&
+         x.ldb == y.ldb && x.ldc0 == y.ldc0 && x.ldd == y.ldd && x.lddt == y.lddt &&
+         x.alpha == y.alpha && x.beta == y.beta && x.dadd == y.dadd && x.flags == y.flags &&
+         (x.C0 == nullptr) == (y.C0 == nullptr) && (x.D == nullptr) == (y.D == nullptr) &&
+         (x.Dt == nullptr) == (y.Dt == nullptr) && x.batch == 1 && y.batch == 1 &&
+         !x.row_scale && !y.row_scale && !x.pred && !y.pred && !x.ptab && !y.ptab;
+}
+
+mao_status gemm_flush(GemmBatch& gb, hipStream_t s) {
+  const int n = (int)gb.items.size();
+  if (n == 0) return MAO_OK;
+  std::vector<std::vector<int>> groups;
+  for (int i = 0; i < n; ++i) {
+    bool placed = false;
+    for (auto& g : groups)
+      if (same_batch(gb.items[g[0]], gb.items[i])) {
+        g.push_back(i);
+        placed = true;
+        break;
+      }
+    if (!placed) groups.push_back({i});
+  }
+  std::vector<const void*> tab;
+  std::vector<GemmProblem> probs[2];  // fp32, bf16 inputs
+  for (const auto& g : groups) {
+    GemmProblem p = gb.items[g[0]].p;
+    if (g.size() > 1) {
+      p.batch = (int)g.size();
+      p.ptab = gb.table + tab.size();
+      for (int i : g) {
+        const GemmProblem& q = gb.items[i].p;
+        tab.insert(tab.end(), {q.A, q.B, q.C0, q.D, q.Dt});
+      }
+    }
+    probs[gb.items[g[0]].dtype == MAO_BF16 ? 1 : 0].push_back(p);
+  }
+  if ((int64_t)tab.size() > gb.capacity) {
+    set_error("gemm batch: %zu pointer-table entries exceed the workspace's %lld", tab.size(),
+              (long long)gb.capacity);
+    return MAO_E_WORKSPACE;
+  }
+  if (!tab.empty()) MAO_TRY(write_pointer_table(gb.table, tab.data(), (int)tab.size(), s));
+  for (int d = 0; d < 2; ++d)
+    for (size_t i = 0; i < probs[d].size(); i += kMaxProblems)
+      MAO_TRY(launch_gemm(d ? MAO_BF16 : MAO_F32, probs[d].data() + i,
+                          (int)std::min<size_t>(kMaxProblems, probs[d].size() - i), s));
+  gb.items.clear();
+  return MAO_OK;
+}
+
 // D = A B^T (fp32), optional transposed copy only.
 mao_status nt32(int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb,
                 float* D, int64_t ldd, float* Dt, int64_t lddt, hipStream_t s,
-                const int* pred = nullptr) {
+                const int* pred = nullptr, GemmBatch* gb = nullptr) {
   GemmProblem p = gemm_problem(M, N, K, 1.f, A, lda, B, ldb, 0.f, nullptr, 0, D, ldd, GF_D_F32);
   p.Dt = Dt;
   p.lddt = lddt;
   p.pred = pred;
-  return launch_gemm(MAO_F32, &p, 1, s);
+  return gemm_add(gb, p, MAO_F32, s);
 }
 
 // F <- beta F + (1 - beta) X X^T (SYRK in place, fp32 F; X fp32 or bf16:
 // bf16 products are exact in fp32, so both accumulate alike in fp32)
 mao_status syrk_ema(int N, int K, const void* X, int64_t ldx, float beta, float* F, int64_t ldf,
-                    hipStream_t s, int x_dtype = MAO_F32) {
+                    hipStream_t s, int x_dtype = MAO_F32, GemmBatch* gb = nullptr) {
   GemmProblem p = gemm_problem(N, N, K, 1.f - beta, X, ldx, X, ldx, beta, F, ldf, F, ldf,
                                GF_SYRK | GF_D_F32 | GF_C0_F32);
-  return launch_gemm(x_dtype, &p, 1, s);
+  return gemm_add(gb, p, x_dtype, s);
 }
 
 }  // namespace
@@ -633,7 +709,7 @@ bool soap_refresh(const mao_soap_hparams* hp, int64_t t) {
 // SOAP before the refresh: momentum, fp32 G and G^T, factor EMAs with the
 // current gradient, E = Q^T of both bases.
 mao_status soap_pre(const mao_mat& W, const mao_mat& G, const mao_soap_state* st, RotBufs& R,
-                    const mao_soap_hparams* hp, hipStream_t s) {
+                    const mao_soap_hparams* hp, GemmBatch* gb, hipStream_t s) {
   const int m = (int)W.rows, n = (int)W.cols;
   const float b1 = hp->beta1, b2 = hp->beta2;
   float* M = (float*)st->M.data;
@@ -648,48 +724,57 @@ mao_status soap_pre(const mao_mat& W, const mao_mat& G, const mao_soap_state* st
     MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n, view(R.Gf, R.ldn),
                                view(nullptr, 0), s));
     MAO_TRY(transpose(view(G.data, G.ld), view(R.T2t, R.ldm), m, n, 1, MAO_BF16, s));
-    MAO_TRY(syrk_ema(m, n, G.data, G.ld, b2, (float*)st->L.data, st->L.ld, s, MAO_BF16));
-    MAO_TRY(syrk_ema(n, m, R.T2t, R.ldm, b2, (float*)st->R.data, st->R.ld, s, MAO_BF16));
+    MAO_TRY(syrk_ema(m, n, G.data, G.ld, b2, (float*)st->L.data, st->L.ld, s, MAO_BF16, gb));
+    MAO_TRY(syrk_ema(n, m, R.T2t, R.ldm, b2, (float*)st->R.data, st->R.ld, s, MAO_BF16, gb));
   } else {
     MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n, view(nullptr, 0),
                                view(R.Gtf, R.ldm), s));
-    MAO_TRY(syrk_ema(m, n, G.data, G.ld, b2, (float*)st->L.data, st->L.ld, s));
-    MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, (float*)st->R.data, st->R.ld, s));
+    MAO_TRY(syrk_ema(m, n, G.data, G.ld, b2, (float*)st->L.data, st->L.ld, s, MAO_F32, gb));
+    MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, (float*)st->R.data, st->R.ld, s, MAO_F32, gb));
   }
   // 3a. E = Q^T of both bases
   MAO_TRY(transpose(view(st->QL.data, st->QL.ld), view(R.EL, R.ldm), m, m, 1, MAO_F32, s));
   return transpose(view(st->QR.data, st->QR.ld), view(R.ER, R.ldn), n, n, 1, MAO_F32, s);
 }
 
-// SOAP after the refresh: rotations, Adam in the eigenbasis, rotation back,
-// weight update.
-mao_status soap_post(const mao_mat& W, const mao_mat& G, const mao_soap_state* st, RotBufs& R,
-                     int64_t t, const mao_soap_hparams* hp, float* update_out, hipStream_t s) {
+// SOAP after the refresh in seven stages (within a stage the matrices'
+// products are independent): 0-3 the rotations G~ = E_L (G E_R^T) and
+// M~ = E_L (M E_R^T) through the transposed intermediate T2t; 4 Adam in the
+// eigenbasis (N written over G~) and T2t = (N Q_R^T)^T; 5 U = Q_L T2t^T;
+// 6 the weight update.
+constexpr int kSoapPostStages = 7;
+
+mao_status soap_post(int stage, const mao_mat& W, const mao_mat& G, const mao_soap_state* st,
+                     RotBufs& R, int64_t t, const mao_soap_hparams* hp, float* update_out,
+                     GemmBatch* gb, hipStream_t s) {
   const int m = (int)W.rows, n = (int)W.cols;
   const float b1 = hp->beta1, b2 = hp->beta2;
   const float* M = (const float*)st->M.data;
   const int64_t ldM = st->M.ld;
   const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
   const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
-  // 4. rotations: G~ = E_L (G E_R^T) via the transposed intermediate
-  MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, nullptr, 0, R.T2t, R.ldm, s));
-  MAO_TRY(nt32(m, n, m, R.EL, R.ldm, R.T2t, R.ldm, R.Gtil, R.ldn, nullptr, 0, s));
-  MAO_TRY(nt32(m, n, n, M, ldM, R.ER, R.ldn, nullptr, 0, R.T2t, R.ldm, s));
-  MAO_TRY(nt32(m, n, m, R.EL, R.ldm, R.T2t, R.ldm, R.Mtil, R.ldn, nullptr, 0, s));
-  // 5. Adam in the eigenbasis (N written over G~)
-  const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
-  const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
-  MAO_TRY(soap_adam(view(R.Gtil, R.ldn), view(R.Mtil, R.ldn), view(st->V.data, st->V.ld), m, n, b2,
-                    bc1, bc2, hp->eps, s));
-  // 6. back: U = Q_L (N Q_R^T)
-  MAO_TRY(nt32(m, n, n, R.Gtil, R.ldn, (const float*)st->QR.data, st->QR.ld, nullptr, 0, R.T2t,
-               R.ldm, s));
   float* U = update_out ? update_out : R.U;
   const int64_t ldU = update_out ? n : R.ldn;
-  MAO_TRY(nt32(m, n, m, (const float*)st->QL.data, st->QL.ld, R.T2t, R.ldm, U, ldU, nullptr, 0, s));
-  // 7. W update
-  return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
-                      hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+  switch (stage) {
+    case 0: return nt32(m, n, n, Gf, ldG, R.ER, R.ldn, nullptr, 0, R.T2t, R.ldm, s, nullptr, gb);
+    case 1: return nt32(m, n, m, R.EL, R.ldm, R.T2t, R.ldm, R.Gtil, R.ldn, nullptr, 0, s, nullptr, gb);
+    case 2: return nt32(m, n, n, M, ldM, R.ER, R.ldn, nullptr, 0, R.T2t, R.ldm, s, nullptr, gb);
+    case 3: return nt32(m, n, m, R.EL, R.ldm, R.T2t, R.ldm, R.Mtil, R.ldn, nullptr, 0, s, nullptr, gb);
+    case 4: {
+      const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
+      const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
+      MAO_TRY(soap_adam(view(R.Gtil, R.ldn), view(R.Mtil, R.ldn), view(st->V.data, st->V.ld), m,
+                        n, b2, bc1, bc2, hp->eps, s));
+      return nt32(m, n, n, R.Gtil, R.ldn, (const float*)st->QR.data, st->QR.ld, nullptr, 0, R.T2t,
+                  R.ldm, s, nullptr, gb);
+    }
+    case 5:
+      return nt32(m, n, m, (const float*)st->QL.data, st->QL.ld, R.T2t, R.ldm, U, ldU, nullptr, 0,
+                  s, nullptr, gb);
+    default:
+      return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
+                          hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+  }
 }
 
 mao_status check_foam_hp(const mao_foam_hparams* hp) {
@@ -728,81 +813,114 @@ mao_status validate_foam(const mao_mat& W, const mao_mat& G, const mao_foam_stat
 
 bool foam_checks(const mao_foam_hparams* hp, int64_t t) { return (t - 1) % hp->pf == 0; }
 
-// FOAM before the refresh: momentum, fp32 G and G^T, R EMA, E_R = QR^T; on a
-// criterion step also S = E_R R (the QR input) and the refresh flag.
+// FOAM before the refresh: momentum, fp32 G and G^T, R EMA, E_R = QR^T.
 //
 // The output side is the input side of the transposed problem: its buffers
 // are carved for (n, m), so that Gf holds G^T (n x m) and Gtf holds G
 // (m x n), the factor is G G^T, r and c trade places and U leaves through the
 // transposed store of the last product.
 mao_status foam_pre(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, RotBufs& R,
-                    int64_t t, const mao_foam_hparams* hp, hipStream_t s) {
+                    const mao_foam_hparams* hp, GemmBatch* gb, hipStream_t s) {
   const int m = (int)W.rows, n = (int)W.cols;
   const bool out = foam_out(hp);
   const int k = out ? m : n;  // factor size
   const float b1 = hp->beta1, b2 = hp->beta2;
   float* Rf = (float*)st->R.data;
   const int64_t ldR = st->R.ld;
-  float* work = R.small + 64;
   MAO_TRY(ema_sumsq(view(st->M.data, st->M.ld), view(G.data, G.ld), G.dtype, m, n, 1, b1, nullptr,
                     rowblocks_for(m, 1), s));
   if (!out) {
     MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
                                view(G.dtype == MAO_F32 ? nullptr : R.Gf, R.ldn), view(R.Gtf, R.ldm), s));
-    MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s));   // R = b2 R + (1-b2) G^T G
+    MAO_TRY(syrk_ema(n, m, R.Gtf, R.ldm, b2, Rf, ldR, s, MAO_F32, gb));   // R = b2 R + (1-b2) G^T G
   } else {
     const bool f32 = G.dtype == MAO_F32;
     MAO_TRY(cast_transpose_f32(view(G.data, G.ld), G.dtype, m, n,
                                view(f32 ? nullptr : R.Gtf, R.ldm), view(R.Gf, R.ldn), s));
     const float* Gr = f32 ? (const float*)G.data : R.Gtf;
-    MAO_TRY(syrk_ema(m, n, Gr, f32 ? G.ld : R.ldm, b2, Rf, ldR, s));   // L = b2 L + (1-b2) G G^T
+    MAO_TRY(syrk_ema(m, n, Gr, f32 ? G.ld : R.ldm, b2, Rf, ldR, s, MAO_F32, gb));   // L = b2 L + (1-b2) G G^T
   }
-  MAO_TRY(transpose(view(st->QR.data, st->QR.ld), view(R.ER, R.ldn), k, k, 1, MAO_F32, s));
-  if (!foam_checks(hp, t)) return no_check(st->aux, R.flag, s);
-  const int64_t ldS = R.ldn;
-  MAO_TRY(nt32(k, k, k, R.ER, R.ldn, Rf, ldR, R.S, ldS, nullptr, 0, s));       // Q^T R
-  MAO_TRY(nt32(k, k, k, R.S, ldS, R.ER, R.ldn, R.D, R.ldn, nullptr, 0, s));    // Q^T R Q
-  return offdiag_check(view(R.D, R.ldn), k, hp->tol, work, st->aux, R.flag, s);
+  return transpose(view(st->QR.data, st->QR.ld), view(R.ER, R.ldn), k, k, 1, MAO_F32, s);
 }
 
-// FOAM after the refresh: rotation, factored moment, preconditioning,
-// rotation back, weight update.
-mao_status foam_post(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, RotBufs& R,
-                     int64_t t, const mao_foam_hparams* hp, float* update_out, hipStream_t s) {
+// FOAM's refresh criterion, stage by stage (factor size k): on a check step
+// S = E_R R (the QR input; stage 0), D = S E_R = Q^T R Q (stage 1) and the
+// off-diagonal test that sets the refresh flag (stage 2); on other steps
+// stage 2 clears the flag.
+mao_status foam_criterion(int k, const mao_foam_state* st, RotBufs& R, int64_t t,
+                          const mao_foam_hparams* hp, int stage, GemmBatch* gb, hipStream_t s) {
+  const bool check = foam_checks(hp, t);
+  if (stage == 0)
+    return check ? nt32(k, k, k, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, R.ldn,
+                        nullptr, 0, s, nullptr, gb)
+                 : MAO_OK;
+  if (stage == 1)
+    return check ? nt32(k, k, k, R.S, R.ldn, R.ER, R.ldn, R.D, R.ldn, nullptr, 0, s, nullptr, gb)
+                 : MAO_OK;
+  if (!check) return no_check(st->aux, R.flag, s);
+  return offdiag_check(view(R.D, R.ldn), k, hp->tol, R.small + 64, st->aux, R.flag, s);
+}
+
+// FOAM after the refresh, in three phases: the rotations G_rot = G Q_R and
+// M_rot = M Q_R; the factored moment, the preconditioning and the rotation
+// back U = N Q_R^T; the weight update. The output side runs the transposed
+// problem: G_rot^T = G^T Q_L, M_rot^T = M^T Q_L, and U = Q_L N leaves through
+// the transposed store of the last product.
+float* foam_u(RotBufs& R, const mao_foam_hparams* hp, int n, float* update_out, int64_t& ldU) {
+  if (update_out) {
+    ldU = n;
+    return update_out;
+  }
+  ldU = foam_out(hp) ? R.ldm : R.ldn;
+  return foam_out(hp) ? R.T2t : R.U;
+}
+
+mao_status foam_rotate(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, RotBufs& R,
+                       const mao_foam_hparams* hp, GemmBatch* gb, hipStream_t s) {
+  const int m = (int)W.rows, n = (int)W.cols;
+  if (foam_out(hp)) {
+    MAO_TRY(nt32(n, m, m, R.Gf, R.ldn, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s, nullptr, gb));
+    MAO_TRY(transpose(view(st->M.data, st->M.ld), view(R.U, R.ldn), m, n, 1, MAO_F32, s));
+    return nt32(n, m, m, R.U, R.ldn, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0, s, nullptr, gb);
+  }
+  const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
+  const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
+  MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s, nullptr, gb));
+  return nt32(m, n, n, (const float*)st->M.data, st->M.ld, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0,
+              s, nullptr, gb);
+}
+
+mao_status foam_precondition_back(const mao_mat& W, const mao_foam_state* st, RotBufs& R,
+                                  int64_t t, const mao_foam_hparams* hp, float* update_out,
+                                  GemmBatch* gb, hipStream_t s) {
   const int m = (int)W.rows, n = (int)W.cols;
   const float b1 = hp->beta1, b2 = hp->beta2;
   float* tau = R.small;
   float* work = R.small + 64;
   const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
   const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
+  int64_t ldU;
+  float* U = foam_u(R, hp, n, update_out, ldU);
   if (foam_out(hp)) {
-    // transposed problem (n x m): G_rot^T = G^T Q_L, M_rot^T = M^T Q_L
-    MAO_TRY(nt32(n, m, m, R.Gf, R.ldn, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s));
-    MAO_TRY(transpose(view(st->M.data, st->M.ld), view(R.U, R.ldn), m, n, 1, MAO_F32, s));
-    MAO_TRY(nt32(n, m, m, R.U, R.ldn, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0, s));
     // the row means of G_rot^T are W's column means (c) and vice versa
     MAO_TRY(foam_moments(view(R.Gtil, R.ldn), n, m, b2, bc2, (const float*)st->R.data, st->R.ld,
                          st->c, st->r, work, tau, st->aux, s));
     MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), n, m, st->c, st->r, tau, bc1, bc2, hp->eps, s));
-    // U = Q_L N = (N^T Q_L^T)^T: the product's transposed store writes U
-    float* U = update_out ? update_out : R.T2t;
-    const int64_t ldU = update_out ? n : R.ldm;
-    MAO_TRY(nt32(n, m, m, R.Mtil, R.ldn, (const float*)st->QR.data, st->QR.ld, nullptr, 0, U, ldU,
-                 s));
-    return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
-                        hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
+    return nt32(n, m, m, R.Mtil, R.ldn, (const float*)st->QR.data, st->QR.ld, nullptr, 0, U, ldU,
+                s, nullptr, gb);
   }
-  const float* Gf = G.dtype == MAO_F32 ? (const float*)G.data : R.Gf;
-  const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
-  // rotate: G_rot = G Q_R, M_rot = M Q_R
-  MAO_TRY(nt32(m, n, n, Gf, ldG, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s));
-  MAO_TRY(nt32(m, n, n, (const float*)st->M.data, st->M.ld, R.ER, R.ldn, R.Mtil, R.ldn, nullptr, 0, s));
   MAO_TRY(foam_moments(view(R.Gtil, R.ldn), m, n, b2, bc2, (const float*)st->R.data, st->R.ld,
                        st->r, st->c, work, tau, st->aux, s));
   MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), m, n, st->r, st->c, tau, bc1, bc2, hp->eps, s));
-  float* U = update_out ? update_out : R.U;
-  const int64_t ldU = update_out ? n : R.ldn;
-  MAO_TRY(nt32(m, n, n, R.Mtil, R.ldn, (const float*)st->QR.data, st->QR.ld, U, ldU, nullptr, 0, s));
+  return nt32(m, n, n, R.Mtil, R.ldn, (const float*)st->QR.data, st->QR.ld, U, ldU, nullptr, 0, s,
+              nullptr, gb);
+}
+
+mao_status foam_update(const mao_mat& W, RotBufs& R, const mao_foam_hparams* hp,
+                       float* update_out, hipStream_t s) {
+  const int m = (int)W.rows, n = (int)W.cols;
+  int64_t ldU;
+  float* U = foam_u(R, hp, n, update_out, ldU);
   return apply_update(view(W.data, W.ld), W.dtype, view(U, ldU), MAO_F32, m, n, 1, hp->lr,
                       hp->weight_decay, 1.f, nullptr, nullptr, view(nullptr, 0), s);
 }
@@ -829,8 +947,10 @@ struct QrGroup {
 // shapes alone, so the size query and the step carve alike.
 // fout: FOAM on the output side (buffers of the transposed problem, factor
 // size m).
+// gb: receives the pointer table of the grouped products (at most two
+// products per matrix in a phase, five pointers each).
 void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<RotBufs>& R,
-                std::vector<QrGroup>& groups, bool fout = false) {
+                std::vector<QrGroup>& groups, bool fout = false, GemmBatch* gb = nullptr) {
   R.assign(count, RotBufs{});
   std::vector<std::pair<int, QrJobRef>> all;
   for (int i = 0; i < count; ++i) {
@@ -874,6 +994,12 @@ void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<R
       }
     }
   }
+  const int64_t cap = (int64_t)2 * 5 * count;
+  const void** table = c.take<const void*>((size_t)cap);
+  if (gb) {
+    gb->table = table;
+    gb->capacity = cap;
+  }
 }
 
 size_t many_ws(int count, const mao_mat* W, bool soap, bool fout = false) {
@@ -912,7 +1038,7 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
   Carver c(workspace);
   RotBufs R;
   carve_rot(c, m, n, true, true, R);
-  MAO_TRY(soap_pre(W, G, st, R, hp, s));
+  MAO_TRY(soap_pre(W, G, st, R, hp, nullptr, s));
   // 3b. refresh: Q <- qr(F Q); S = (F Q)^T = Q^T F stored row-major
   if (soap_refresh(hp, t)) {
     const int64_t ldS = ws_ld(std::max(m, n));
@@ -921,7 +1047,9 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
     MAO_TRY(nt32(n, n, n, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, ldS, nullptr, 0, s));
     MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, nullptr, s));
   }
-  return soap_post(W, G, st, R, t, hp, update_out, s);
+  for (int stage = 0; stage < kSoapPostStages; ++stage)
+    MAO_TRY(soap_post(stage, W, G, st, R, t, hp, update_out, nullptr, s));
+  return MAO_OK;
 }
 
 size_t soap_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_soap_hparams* hp) {
@@ -946,20 +1074,27 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
-  carve_many(c, count, W, true, R, groups);
-  for (int i = 0; i < count; ++i) MAO_TRY(soap_pre(W[i], G[i], &st[i], R[i], hp, s));
+  GemmBatch gb;
+  carve_many(c, count, W, true, R, groups, false, &gb);
+  for (int i = 0; i < count; ++i) MAO_TRY(soap_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
+  MAO_TRY(gemm_flush(gb, s));
   if (soap_refresh(hp, t)) {
+    // the QR inputs S = E F of every job, grouped, before the batched QRs
+    for (QrGroup& g : groups)
+      for (int k = 0; k < (int)g.jobs.size(); ++k) {
+        const int i = g.jobs[k].mat;
+        const mao_mat& F = g.jobs[k].side == 0 ? st[i].L : st[i].R;
+        MAO_TRY(nt32(g.n, g.n, g.n, g.E + k * g.sz, g.ld, (const float*)F.data, F.ld,
+                     g.S + k * g.sz, g.ld, nullptr, 0, s, nullptr, &gb));
+      }
+    MAO_TRY(gemm_flush(gb, s));
     for (QrGroup& g : groups) {
       const int nj = (int)g.jobs.size();
       std::vector<float*> q(nj);
       std::vector<int64_t> ldq(nj);
       for (int k = 0; k < nj; ++k) {
         const int i = g.jobs[k].mat;
-        const bool left = g.jobs[k].side == 0;
-        const mao_mat& F = left ? st[i].L : st[i].R;
-        const mao_mat& Q = left ? st[i].QL : st[i].QR;
-        MAO_TRY(nt32(g.n, g.n, g.n, g.E + k * g.sz, g.ld, (const float*)F.data, F.ld, g.S + k * g.sz,
-                     g.ld, nullptr, 0, s));
+        const mao_mat& Q = g.jobs[k].side == 0 ? st[i].QL : st[i].QR;
         q[k] = (float*)Q.data;
         ldq[k] = Q.ld;
       }
@@ -978,8 +1113,12 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
       MAO_TRY(qr_core_batched(b, s));
     }
   }
-  for (int i = 0; i < count; ++i)
-    MAO_TRY(soap_post(W[i], G[i], &st[i], R[i], t, hp, update_out ? update_out[i] : nullptr, s));
+  for (int stage = 0; stage < kSoapPostStages; ++stage) {
+    for (int i = 0; i < count; ++i)
+      MAO_TRY(soap_post(stage, W[i], G[i], &st[i], R[i], t, hp,
+                        update_out ? update_out[i] : nullptr, &gb, s));
+    MAO_TRY(gemm_flush(gb, s));
+  }
   return MAO_OK;
 }
 
@@ -1009,10 +1148,14 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
   Carver c(workspace);
   RotBufs R;
   carve_rot(c, out ? n : m, out ? m : n, false, true, R);
-  MAO_TRY(foam_pre(W, G, st, R, t, hp, s));
+  MAO_TRY(foam_pre(W, G, st, R, hp, nullptr, s));
+  for (int stage = 0; stage < 3; ++stage)
+    MAO_TRY(foam_criterion(k, st, R, t, hp, stage, nullptr, s));
   if (foam_checks(hp, t))
     MAO_TRY(qr_core(R.S, R.ldn, k, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, R.flag, s));
-  return foam_post(W, G, st, R, t, hp, update_out, s);
+  MAO_TRY(foam_rotate(W, G, st, R, hp, nullptr, s));
+  MAO_TRY(foam_precondition_back(W, st, R, t, hp, update_out, nullptr, s));
+  return foam_update(W, R, hp, update_out, s);
 }
 
 size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_foam_hparams* hp) {
@@ -1037,8 +1180,17 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
-  carve_many(c, count, W, false, R, groups, foam_out(hp));
-  for (int i = 0; i < count; ++i) MAO_TRY(foam_pre(W[i], G[i], &st[i], R[i], t, hp, s));
+  GemmBatch gb;
+  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb);
+  // phases: every matrix's products of a phase go out as grouped launches
+  for (int i = 0; i < count; ++i) MAO_TRY(foam_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
+  MAO_TRY(gemm_flush(gb, s));
+  for (int stage = 0; stage < 3; ++stage) {
+    for (int i = 0; i < count; ++i)
+      MAO_TRY(foam_criterion((int)(foam_out(hp) ? W[i].rows : W[i].cols), &st[i], R[i], t, hp,
+                             stage, &gb, s));
+    MAO_TRY(gemm_flush(gb, s));
+  }
   if (foam_checks(hp, t)) {
     for (QrGroup& g : groups) {
       const int nj = (int)g.jobs.size();
@@ -1066,8 +1218,14 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
       MAO_TRY(qr_core_batched(b, s));
     }
   }
+  for (int i = 0; i < count; ++i) MAO_TRY(foam_rotate(W[i], G[i], &st[i], R[i], hp, &gb, s));
+  MAO_TRY(gemm_flush(gb, s));
   for (int i = 0; i < count; ++i)
-    MAO_TRY(foam_post(W[i], G[i], &st[i], R[i], t, hp, update_out ? update_out[i] : nullptr, s));
+    MAO_TRY(foam_precondition_back(W[i], &st[i], R[i], t, hp, update_out ? update_out[i] : nullptr,
+                                   &gb, s));
+  MAO_TRY(gemm_flush(gb, s));
+  for (int i = 0; i < count; ++i)
+    MAO_TRY(foam_update(W[i], R[i], hp, update_out ? update_out[i] : nullptr, s));
   return MAO_OK;
 }
 

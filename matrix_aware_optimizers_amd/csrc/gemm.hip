@@ -31,6 +31,7 @@
 // operand panels.
 #include "gemm.hpp"
 
+#include <algorithm>
 #include <utility>
 
 namespace mao {
@@ -107,8 +108,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int M = P.M, N = P.N, K = P.K;
-  const TIn* A = (const TIn*)P.A + (int64_t)b * P.sA;
-  const TIn* B = (const TIn*)P.B + (int64_t)b * P.sB;
+  const int dsz = (P.flags & GF_D_F32) ? 4 : 2, csz = (P.flags & GF_C0_F32) ? 4 : 2;
+  const OpPtrs ops = problem_operands(P, b, (int)sizeof(TIn), csz, dsz);
+  const TIn* A = (const TIn*)ops.A;
+  const TIn* B = (const TIn*)ops.B;
   const int64_t lda = P.lda, ldb = P.ldb;
 
   // Two register sets in flight: while slice k is multiplied out of LDS, the
@@ -215,11 +218,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs args) {
   const bool diag = syrk && (tm == tn);
   const bool d32 = (P.flags & GF_D_F32) != 0;
   const bool c32 = (P.flags & GF_C0_F32) != 0;
-  const int dsz = d32 ? 4 : 2, csz = c32 ? 4 : 2;
-  void* D = P.D ? (void*)((char*)P.D + (int64_t)b * P.sD * dsz) : nullptr;
-  void* Tt = syrk ? D : (P.Dt ? (void*)((char*)P.Dt + (int64_t)b * P.sDt * dsz) : nullptr);
+  void* D = ops.D;
+  void* Tt = syrk ? D : ops.Dt;
   const int64_t ldt = syrk ? P.ldd : P.lddt;
-  const void* C0 = P.C0 ? (const void*)((const char*)P.C0 + (int64_t)b * P.sC0 * csz) : nullptr;
+  const void* C0 = ops.C0;
   const float alpha = P.alpha, beta = P.beta;
   const float* rs = P.row_scale ? P.row_scale + b * P.srs : nullptr;
 
@@ -333,6 +335,19 @@ mao_status launch_cfg(GemmArgs& args, hipStream_t stream) {
   return MAO_OK;
 }
 
+// Pointer-table fill: the pointers travel as kernel arguments, a chunk per
+// launch (under 2 KB of arguments).
+constexpr int kFillChunk = 240;
+struct PtrFill {
+  const void** dst;
+  int n;
+  const void* p[kFillChunk];
+};
+
+__global__ __launch_bounds__(256) void ptr_fill_kernel(PtrFill a) {
+  for (int i = threadIdx.x; i < a.n; i += blockDim.x) a.dst[i] = a.p[i];
+}
+
 int count_tiles(GemmProblem* probs, int nprob, int bm) {
   int64_t total = 0;
   for (int i = 0; i < nprob; ++i) {
@@ -345,6 +360,18 @@ int count_tiles(GemmProblem* probs, int nprob, int bm) {
 }
 
 }  // namespace
+
+mao_status write_pointer_table(const void** dst, const void* const* src, int n, hipStream_t s) {
+  for (int i = 0; i < n; i += kFillChunk) {
+    PtrFill a;
+    a.dst = dst + i;
+    a.n = std::min(kFillChunk, n - i);
+    for (int k = 0; k < a.n; ++k) a.p[k] = src[i + k];
+    hipLaunchKernelGGL(ptr_fill_kernel, dim3(1), dim3(256), 0, s, a);
+    MAO_LAUNCH_CHECK();
+  }
+  return MAO_OK;
+}
 
 mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t stream, int tag) {
   if (nprob <= 0) return MAO_OK;
@@ -388,9 +415,17 @@ mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t 
       return MAO_E_UNSUPPORTED;
     }
   }
+  // Pointer-table batches run on the direct and 128 / 64 kernels only, never
+  // with tiled operands.
+  int ntab = 0;
+  for (int i = 0; i < nprob; ++i) ntab += probs[i].ptab ? 1 : 0;
+  if (ntab != 0 && (nt != 0 || ntio != 0)) {
+    set_error("launch_gemm: a pointer-table batch takes no tiled operands");
+    return MAO_E_UNSUPPORTED;
+  }
   // fp32 rank-k updates (k <= 64, the QR updates) stream their result once:
   // the 256 x 256 rank kernel moves it in whole rows.
-  bool rank = in_dtype == MAO_F32 && nkm == 0;
+  bool rank = in_dtype == MAO_F32 && nkm == 0 && ntab == 0;
   for (int i = 0; i < nprob; ++i) rank = rank && probs[i].K <= 64 && !(probs[i].flags & GF_SYRK);
   rank = rank && count_tiles(probs, nprob, 256) >= 16;
   // without a transposed copy the 128 x 128 rank kernel (two per CU) serves

@@ -29,6 +29,10 @@ struct GemmProblem {
   void* Dt;          // N x M (transposed copy of D) or nullptr
   const float* row_scale;  // D row i multiplied by row_scale[i] (or nullptr)
   const int* pred;   // skip the problem when *pred == 0 (or nullptr)
+  // Pointer-table batch (or nullptr): entry b's A, B, C0, D, Dt are
+  // ptab[5 b .. 5 b + 4] (device memory; a null C0 / D / Dt is absent), in
+  // place of the base pointers and batch strides above.
+  const void* const* ptab;
   int64_t srs, spred;  // batch strides of row_scale and pred (elements; 0: shared)
   int64_t lda, ldb, ldc0, ldd, lddt;
   int64_t sA, sB, sC0, sD, sDt;  // batch strides (elements)
@@ -74,6 +78,39 @@ __device__ __forceinline__ void xcd_tile(const GemmArgs& a, int bid, int& pi, in
   }
 }
 
+// Operands of batch entry b (byte pointers): from the problem's pointer table,
+// else base + b * stride. isz / csz / dsz: element sizes of A and B, C0, D.
+struct OpPtrs {
+  const char* A;
+  const char* B;
+  const char* C0;
+  char* D;
+  char* Dt;
+};
+__device__ __forceinline__ OpPtrs problem_operands(const GemmProblem& P, int b, int isz, int csz,
+                                                   int dsz) {
+  OpPtrs o;
+  if (P.ptab != nullptr) {
+    const void* const* e = P.ptab + 5 * (int64_t)b;
+    o.A = (const char*)e[0];
+    o.B = (const char*)e[1];
+    o.C0 = (const char*)e[2];
+    o.D = (char*)e[3];
+    o.Dt = (char*)e[4];
+    return o;
+  }
+  o.A = (const char*)P.A + (int64_t)b * P.sA * isz;
+  o.B = (const char*)P.B + (int64_t)b * P.sB * isz;
+  o.C0 = P.C0 ? (const char*)P.C0 + (int64_t)b * P.sC0 * csz : nullptr;
+  o.D = P.D ? (char*)P.D + (int64_t)b * P.sD * dsz : nullptr;
+  o.Dt = P.Dt ? (char*)P.Dt + (int64_t)b * P.sDt * dsz : nullptr;
+  return o;
+}
+
+// Writes n pointers (host values) to the device table dst, in launches of
+// kernel arguments (no host-to-device copy, nothing allocated).
+mao_status write_pointer_table(const void** dst, const void* const* src, int n, hipStream_t s);
+
 // What a launch computes, for the optional event timing (instrumentation).
 enum GemmTag : int { TAG_NS_GRAM = 0, TAG_NS_SQUARE = 1, TAG_NS_APPLY = 2, TAG_OTHER = 3,
                      TAG_QR = 4, TAG_COUNT = 8 };
@@ -108,7 +145,7 @@ inline GemmProblem gemm_problem(int M, int N, int K, float alpha, const void* A,
                                 int64_t ldc0, void* D, int64_t ldd, int flags) {
   GemmProblem p = {};
   p.A = A; p.B = B; p.C0 = C0; p.D = D; p.Dt = nullptr;
-  p.row_scale = nullptr; p.pred = nullptr;
+  p.row_scale = nullptr; p.pred = nullptr; p.ptab = nullptr;
   p.lda = lda; p.ldb = ldb; p.ldc0 = ldc0; p.ldd = ldd; p.lddt = 0;
   p.alpha = alpha; p.beta = beta;
   p.M = M; p.N = N; p.K = K; p.batch = 1;

@@ -117,6 +117,12 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
   const int M = P.M, N = P.N, K = P.K;
   const TIn* A = (const TIn*)P.A + (int64_t)b * P.sA;
   const TIn* B = (const TIn*)P.B + (int64_t)b * P.sB;
+  if constexpr (!T32) {
+    if (P.ptab != nullptr) {  // pointer-table batch (tiled launches never take one)
+      A = (const TIn*)P.ptab[5 * (int64_t)b];
+      B = (const TIn*)P.ptab[5 * (int64_t)b + 1];
+    }
+  }
   const int64_t lda = P.lda, ldb = P.ldb;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -419,6 +425,14 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
   void* Tt = syrk ? D : (P.Dt ? (void*)((char*)P.Dt + (int64_t)b * P.sDt * dsz) : nullptr);
   const int64_t ldt = syrk ? P.ldd : P.lddt;
   const void* C0 = P.C0 ? (const void*)((const char*)P.C0 + (int64_t)b * P.sC0 * csz) : nullptr;
+  if constexpr (!T32) {
+    if (P.ptab != nullptr) {
+      const OpPtrs o = problem_operands(P, b, (int)sizeof(TIn), csz, dsz);
+      D = o.D;
+      Tt = syrk ? o.D : o.Dt;
+      C0 = o.C0;
+    }
+  }
   const float alpha = P.alpha, beta = P.beta;
   const float* rs = P.row_scale ? P.row_scale + b * P.srs : nullptr;
   // A tiled D is written whole, pad included (the pad of every operand is

@@ -317,3 +317,72 @@ def test_foam_many_matches_separate_calls(gpu_lib, pf, tol, side):
             _close(o2[i], o1[i], f"t={t} matrix {i} update")
     if tol == 0.0:
         assert refreshed == {True}
+
+
+# Enough equal shapes that a phase's grouped products fill the 256 x 256
+# streamed kernel from one pointer-table batch, while the separate calls run
+# each product alone on smaller tiles: the K sums are ordered differently,
+# hence 1e-4. The factors must be well conditioned for the refreshed bases to
+# be determined to that accuracy (a rank-deficient factor leaves part of its
+# basis to rounding): FOAM's factor is G^T G of a tall gradient (or G G^T of
+# a wide one, output side), SOAP's square gradients have singular values in
+# [1, 2], so both of its factors have condition number <= 4 at every step.
+def _square_gradients(count, n, steps, seed):
+    r = np.random.default_rng(seed)
+    s = np.linspace(1.0, 2.0, n)
+    out = []
+    for _ in range(count):
+        gs = []
+        for _ in range(steps):
+            u = np.linalg.qr(r.standard_normal((n, n)))[0]
+            v = np.linalg.qr(r.standard_normal((n, n)))[0]
+            gs.append(((u * s) @ v.T).astype(np.float32))
+        out.append(gs)
+    return out
+
+
+@pytest.mark.parametrize("opt,side,gdt", [("foam", "input", "f32"), ("foam", "output", "f32"),
+                                          ("soap", None, "f32"), ("soap", None, "bf16")])
+def test_many_large_batches_match_separate_calls(gpu_lib, opt, side, gdt):
+    import torch
+    log(f"{opt} many (grouped 256-tile batches) vs single, side={side} g={gdt}")
+    steps = 2
+    if opt == "foam":
+        shapes = [(2600, 1040) if side == "input" else (1040, 2600)] * 6
+        ws, gs = _many_inputs(shapes, steps, 47)
+    else:
+        shapes = [(1040, 1040)] * 6
+        ws = _many_inputs(shapes, 1, 47)[0]
+        gs = _square_gradients(len(shapes), 1040, steps, 48)
+    Ws1 = [to_dev(w) for w in ws]
+    Ws2 = [to_dev(w) for w in ws]
+    if opt == "foam":
+        st1 = [_foam_state_dev_many(m, n, side) for m, n in shapes]
+        st2 = [_foam_state_dev_many(m, n, side) for m, n in shapes]
+        keys, kw = ("M", "R", "QR", "r", "c"), dict(pf=1, tol=0.0, side=side)
+    else:
+        st1 = [_soap_state_dev(m, n) for m, n in shapes]
+        st2 = [_soap_state_dev(m, n) for m, n in shapes]
+        keys, kw = ("M", "V", "L", "R", "QL", "QR"), dict(refresh_every=1)
+    hp = dict(HP)
+    if opt == "soap":
+        # Adam's first step divides G~ by |G~| + eps, a sign function at
+        # eps = 1e-8: an entry of G~ within rounding of zero flips between two
+        # valid summation orders, a rank-1 change of the update. eps = 1e-2
+        # (entries of G~ are ~0.05 here) keeps the division smooth; the states
+        # do not depend on eps.
+        hp["eps"] = 1e-2
+    o1 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in shapes]
+    o2 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in shapes]
+    single = gpu_lib.foam_step if opt == "foam" else gpu_lib.soap_step
+    many = gpu_lib.foam_step_many if opt == "foam" else gpu_lib.soap_step_many
+    for t in range(1, steps + 1):
+        G = [to_dev(bf16_round(g[t - 1]) if gdt == "bf16" else g[t - 1], gdt) for g in gs]
+        for i in range(len(shapes)):
+            single(Ws1[i], G[i], st1[i], t, update_out=o1[i], **kw, **hp)
+        many([(Ws2[i], G[i], st2[i]) for i in range(len(shapes))], t, update_out=o2, **kw, **hp)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            for k in keys:
+                _close(st2[i][k], st1[i][k], f"t={t} matrix {i} {k}", 1e-4)
+            _close(o2[i], o1[i], f"t={t} matrix {i} update", 1e-4)
