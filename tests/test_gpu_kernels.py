@@ -17,7 +17,9 @@ GEMM_SHAPES = [(1, 1, 1), (64, 64, 64), (130, 77, 203), (300, 257, 500), (513, 1
                # whole tiles with K a multiple of the slice
                (4100, 2052, 1060), (2304, 4352, 8), (2048, 4096, 1024),
                # rank-k updates (k <= 64) on the fp32 256 x 256 rank kernel
-               (1500, 1300, 64), (4100, 2052, 40), (1030, 1030, 1)]
+               (1500, 1300, 64), (4100, 2052, 40), (1030, 1030, 1),
+               # tall skinny products (the QR projections, 64-wide tiles)
+               (40000, 64, 300), (33000, 40, 96)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -386,3 +386,31 @@ def test_many_large_batches_match_separate_calls(gpu_lib, opt, side, gdt):
             for k in keys:
                 _close(st2[i][k], st1[i][k], f"t={t} matrix {i} {k}", 1e-4)
             _close(o2[i], o1[i], f"t={t} matrix {i} update", 1e-4)
+
+
+def test_foam_many_more_shape_groups_than_one_launch_holds(gpu_lib):
+    """Ten distinct shapes (two of them repeated): a phase's grouped products
+    split over two launches of at most eight batches each; the states and
+    updates equal those of separate calls."""
+    import torch
+    shapes = [(64 + 8 * i, 72 + 16 * i) for i in range(10)] + [(64, 72), (136, 216)]
+    log(f"foam many over {len(shapes)} matrices, 10 distinct shapes")
+    steps = 2
+    ws, gs = _many_inputs(shapes, steps, 53)
+    Ws1 = [to_dev(w) for w in ws]
+    Ws2 = [to_dev(w) for w in ws]
+    st1 = [_foam_state_dev_many(m, n) for m, n in shapes]
+    st2 = [_foam_state_dev_many(m, n) for m, n in shapes]
+    o1 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in shapes]
+    o2 = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in shapes]
+    for t in range(1, steps + 1):
+        G = [to_dev(g[t - 1]) for g in gs]
+        for i in range(len(shapes)):
+            gpu_lib.foam_step(Ws1[i], G[i], st1[i], t, update_out=o1[i], pf=1, tol=0.0, **HP)
+        gpu_lib.foam_step_many([(Ws2[i], G[i], st2[i]) for i in range(len(shapes))], t,
+                               update_out=o2, pf=1, tol=0.0, **HP)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            for k in ("M", "R", "QR", "r", "c"):
+                _close(st2[i][k], st1[i][k], f"t={t} matrix {i} {k}")
+            _close(o2[i], o1[i], f"t={t} matrix {i} update")
