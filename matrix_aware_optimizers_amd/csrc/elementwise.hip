@@ -425,34 +425,62 @@ __global__ __launch_bounds__(kBlock) void col_partial_kernel(View X, int rows, i
   colpart[(int64_t)blockIdx.y * cols + j] = acc;
 }
 
-__global__ __launch_bounds__(1024) void foam_finalize_kernel(
-    const float* rowss, const float* colpart, int nrb, int m, int n, float beta2, float bc2,
-    const float* R, int64_t ldR, float* r, float* c, float* tau_out, float* aux) {
-  __shared__ float sc[16];
+// Factored moment, wide pass. Workgroup b < nbr: r_i <- beta2 r_i + (1 -
+// beta2) rowss_i / n over rows [256 b, 256 b + 256) and the sum of the new
+// r there; workgroup nbr + b: c_j <- beta2 c_j + (1 - beta2) colsum_j / m
+// over columns [256 b, 256 b + 256), colsum_j summed from the row-block
+// partials in block order, and the sums of the new c and of diag(R) there.
+__global__ __launch_bounds__(256) void foam_rc_kernel(const float* rowss, const float* colpart,
+                                                      int nrb, int m, int n, float beta2,
+                                                      const float* R, int64_t ldR, float* r,
+                                                      float* c, float* bp, int nbr, int nbc) {
+  __shared__ float sc[4];
   const float ob = 1.f - beta2;
-  float sr = 0.f, scs = 0.f, tr = 0.f;
-  for (int i = threadIdx.x; i < m; i += blockDim.x) {
-    const float v = beta2 * r[i] + ob * (rowss[i] / (float)n);
-    r[i] = v;
-    sr += v;
+  const int b = blockIdx.x;
+  if (b < nbr) {
+    const int i = b * 256 + threadIdx.x;
+    float v = 0.f;
+    if (i < m) {
+      v = beta2 * r[i] + ob * (rowss[i] / (float)n);
+      r[i] = v;
+    }
+    v = block_sum(v, sc);
+    if (threadIdx.x == 0) bp[b] = v;
+    return;
   }
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+  const int cb = b - nbr;
+  const int j = cb * 256 + threadIdx.x;
+  float v = 0.f, d = 0.f;
+  if (j < n) {
     float s = 0.f;
     for (int k = 0; k < nrb; ++k) s += colpart[(int64_t)k * n + j];
-    const float v = beta2 * c[j] + ob * (s / (float)m);
+    v = beta2 * c[j] + ob * (s / (float)m);
     c[j] = v;
-    scs += v;
-    tr += R[(int64_t)j * ldR + j];
+    d = R[(int64_t)j * ldR + j];
   }
-  sr = block_sum(sr, sc);
-  scs = block_sum(scs, sc);
-  tr = block_sum(tr, sc);
+  v = block_sum(v, sc);
+  d = block_sum(d, sc);
   if (threadIdx.x == 0) {
-    const double denom = ((double)sr / bc2) * ((double)scs / bc2);
-    const float tau = denom > 0.0 ? (float)(((double)tr / bc2) / denom) : 0.f;
-    tau_out[0] = tau;
-    if (aux) aux[2] = tau;
+    bp[nbr + cb] = v;
+    bp[nbr + nbc + cb] = d;
   }
+}
+
+// tau = (tr(R) / bc2) / ((sum r / bc2) (sum c / bc2)) from the wide pass's
+// block sums, added in block order (0 when the denominator is 0).
+__global__ __launch_bounds__(64) void foam_tau_kernel(const float* bp, int nbr, int nbc,
+                                                      float bc2, float* tau_out, float* aux) {
+  if (threadIdx.x != 0) return;
+  double sr = 0.0, scs = 0.0, tr = 0.0;
+  for (int b = 0; b < nbr; ++b) sr += bp[b];
+  for (int b = 0; b < nbc; ++b) {
+    scs += bp[nbr + b];
+    tr += bp[nbr + nbc + b];
+  }
+  const double denom = (sr / bc2) * (scs / bc2);
+  const float tau = denom > 0.0 ? (float)((tr / bc2) / denom) : 0.f;
+  tau_out[0] = tau;
+  if (aux) aux[2] = tau;
 }
 
 __global__ __launch_bounds__(kBlock) void foam_precond_kernel(View Mr, int m, int n,
@@ -710,22 +738,26 @@ mao_status fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 mao_status foam_moments(View Gr, int m, int n, float beta2, float bc2, const float* R, int64_t ldR,
                         float* r, float* c, float* work, float* tau_out, float* aux,
                         hipStream_t s) {
-  // work: rowss[m] then colpart[nrb * n]
+  // work: rowss[m], colpart[nrb * n], then the wide pass's block sums
   float* rowss = work;
   float* colpart = work + round_up(m, 64);
   const int nrb = (int)std::min<int64_t>(64, std::max<int64_t>(1, m / 32));
+  float* bp = colpart + round_up((int64_t)nrb * n, 64);
+  const int nbr = (m + 255) / 256, nbc = (n + 255) / 256;
   hipLaunchKernelGGL(row_sumsq_kernel<float>, dim3((m + 3) / 4, 1), dim3(kBlock), 0, s, Gr, m, n, (const float*)nullptr, rowss);
   MAO_LAUNCH_CHECK();
   hipLaunchKernelGGL(col_partial_kernel, dim3((n + kBlock - 1) / kBlock, nrb), dim3(kBlock), 0, s, Gr, m, n, nrb, colpart);
   MAO_LAUNCH_CHECK();
-  hipLaunchKernelGGL(foam_finalize_kernel, dim3(1), dim3(1024), 0, s, rowss, colpart, nrb, m, n, beta2, bc2, R, ldR, r, c, tau_out, aux);
+  hipLaunchKernelGGL(foam_rc_kernel, dim3(nbr + nbc), dim3(256), 0, s, rowss, colpart, nrb, m, n, beta2, R, ldR, r, c, bp, nbr, nbc);
+  MAO_LAUNCH_CHECK();
+  hipLaunchKernelGGL(foam_tau_kernel, dim3(1), dim3(64), 0, s, bp, nbr, nbc, bc2, tau_out, aux);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }
 
 int64_t foam_moments_work_floats(int m, int n) {
   const int nrb = (int)std::min<int64_t>(64, std::max<int64_t>(1, m / 32));
-  return round_up(m, 64) + (int64_t)nrb * n;
+  return round_up(m, 64) + round_up((int64_t)nrb * n, 64) + (m + 255) / 256 + 2 * ((n + 255) / 256);
 }
 
 mao_status foam_precondition(View Mr, int m, int n, const float* r, const float* c,
