@@ -289,13 +289,18 @@ MAO_API size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W,
 /*
  * soap_step_many / foam_step_many -- soap_step / foam_step on `count`
  * matrices of any shapes (the layers of a model), with the same t and
- * hyperparameters; results equal `count` separate calls. The QR refreshes of
- * equal size (SOAP: the L factor of an m x n matrix is of size m, the R
- * factor of size n; FOAM: R only) run as one batched QR each: the panels of
- * all of them share each cooperative launch and the updates run as batched
- * products, so that the per-panel latency is paid once per size instead of
- * once per factor ([SMB] section 3-2 (4) for the refresh; [FOAM] section 3
- * for FOAM's criterion, decided per matrix on the device).
+ * hyperparameters; results equal `count` separate calls up to fp32 rounding
+ * order. The step runs in phases, and the products of one phase for all
+ * matrices go out as grouped launches (equal shapes as one batch, its
+ * per-matrix operand pointers in a table inside the workspace), which may
+ * use other tile sizes than a lone product and so sum over K in another
+ * order. The QR refreshes of equal size (SOAP: the L factor of an m x n
+ * matrix is of size m, the R factor of size n; FOAM: R only) run as one
+ * batched QR each: the panels of all of them share each cooperative launch
+ * and the updates run as batched products, so that the per-panel latency is
+ * paid once per size instead of once per factor ([SMB] section 3-2 (4) for
+ * the refresh; [FOAM] section 3 for FOAM's criterion, decided per matrix on
+ * the device).
  *
  * W, G, state: arrays of `count` (host memory, read during the call).
  * update_out: NULL, or a host array of `count` pointers, each NULL or as in
