@@ -42,7 +42,9 @@ and Q_L.
 
 Parity: pinned (exact reconstruction of SOAP's dense rotated moment on
 Rademacher K-FAC gradients, on either side; mass invariant
-sum(tau r c^T) = tr(R_hat); rho = 0 in R's eigenbasis; the output variant
+sum(tau r c^T) = tr(R_hat); rho = 0 in R's eigenbasis and no refresh at
+rho = tol; the refresh as one orthogonal-iteration step: with b2 = 0 and a
+fixed G, k refreshes give qr(R^k) and rho converges to 0; the output variant
 equals the input variant on the transposed problem; state size
 mn + 2n^2 + m + n).
 """

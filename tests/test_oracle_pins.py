@@ -148,6 +148,22 @@ def test_muon_step_one_closed_form():
     assert rel(w1, w - lr * wd * w - lr * expect_upd) < 1e-14
 
 
+def test_muon_momentum_is_an_exponential_average_of_the_gradients():
+    """M_t = mu M_{t-1} + (1-mu) G_t from M_0 = 0 unrolls to
+    sum_s (1-mu) mu^(t-s) G_s (Muon+ page, section 2, step 1); with 0
+    iterations the update is sqrt(m/n) M_t / (|M_t|_F + eps)."""
+    r = _rng(33)
+    mu = 0.9
+    gs = [r.standard_normal((4, 6)) for _ in range(6)]
+    mom = np.zeros((4, 6))
+    w = np.zeros((4, 6))
+    for t, g in enumerate(gs, start=1):
+        w, mom, upd = oracle.muon_step(w, g, mom, lr=0.0, mu=mu, weight_decay=0.0, ns_steps=0)
+        unrolled = sum((1 - mu) * mu ** (t - s) * gs[s - 1] for s in range(1, t + 1))
+        assert rel(mom, unrolled) < 1e-14
+        assert rel(upd, math.sqrt(4 / 6) * unrolled / (np.linalg.norm(unrolled) + 1e-7)) < 1e-13
+
+
 def test_muon_zero_gradient_only_decays():
     w = _rng(14).standard_normal((4, 4))
     w1, m1, upd = oracle.muon_step(w, np.zeros((4, 4)), np.zeros((4, 4)), lr=0.01, mu=0.9,
@@ -178,6 +194,14 @@ def test_muon_plus_equalises_and_is_idempotent():
     cr = oracle.muon_plus_normalize(o, "col_row", eps=0.0)
     rn = np.linalg.norm(cr, axis=1)
     assert np.allclose(rn, rn[0], rtol=1e-13)
+    # the pass applied last decides which norms come out equal: col-row ends
+    # on rows, row-col on columns (and they are different operators)
+    assert np.std(np.linalg.norm(cr, axis=0)) > 1e-3
+    rc = oracle.muon_plus_normalize(o, "row_col", eps=0.0)
+    cn2 = np.linalg.norm(rc, axis=0)
+    assert np.allclose(cn2, cn2[0], rtol=1e-13)
+    assert np.std(np.linalg.norm(rc, axis=1)) > 1e-3
+    assert rel(rc, cr) > 1e-3
 
 
 def test_muon_plus_identity_on_exact_polar_factor():
@@ -292,6 +316,54 @@ def test_soap_no_ema_converged_basis_gives_polar_factor():
     assert rel(upd, oracle.polar_svd(g)) < 1e-6
 
 
+def test_soap_factors_are_exponential_averages_with_equal_trace():
+    """L and R are EMAs of G G^T and G^T G ("SOAP, Muon, and Beyond", section
+    1-1): from zero they unroll to sum_s (1-b2) b2^(t-s) G_s G_s^T (and
+    G_s^T G_s), and because tr(G G^T) = tr(G^T G) = |G|_F^2 the two factors
+    always carry the same trace. (The refresh is scale-invariant, so nothing
+    downstream would notice a wrong factor scale.)"""
+    r = _rng(34)
+    m, n = 5, 8
+    st = oracle.soap_init(m, n)
+    w = np.zeros((m, n))
+    gs = []
+    for t in range(1, 6):
+        g = r.standard_normal((m, n))
+        gs.append(g)
+        w, st, _, _ = oracle.soap_step(w, g, st, t, **SOAP_HP)
+        wts = [(1 - 0.95) * 0.95 ** (t - s) for s in range(1, t + 1)]
+        assert rel(st.L, sum(c * x @ x.T for c, x in zip(wts, gs))) < 1e-14
+        assert rel(st.R, sum(c * x.T @ x for c, x in zip(wts, gs))) < 1e-14
+        mass = sum(c * np.sum(x * x) for c, x in zip(wts, gs))
+        assert abs(np.trace(st.L) - mass) < 1e-13 * mass
+        assert abs(np.trace(st.R) - mass) < 1e-13 * mass
+
+
+def test_soap_periodic_refresh_schedule():
+    """refresh_every = k refreshes at t = 1, k+1, 2k+1, ... (the basis is
+    needed from the first step; standard SOAP refreshes every k steps,
+    picx.dev summary, SOAP instability diagnosis): the basis is bitwise
+    unchanged on the other steps, and on a refreshing step it is the positive
+    QR of F Q_prev, checked through its defining properties."""
+    r = _rng(35)
+    m, n, k = 4, 6, 3
+    st = oracle.soap_init(m, n)
+    w = np.zeros((m, n))
+    for t in range(1, 11):
+        g = r.standard_normal((m, n))
+        prev = st.copy()
+        w, st, _, _ = oracle.soap_step(w, g, st, t, refresh_every=k, **SOAP_HP)
+        if t in (1, 4, 7, 10):
+            for f, q0, q1 in ((st.L, prev.QL, st.QL), (st.R, prev.QR, st.QR)):
+                tri = q1.T @ (f @ q0)
+                assert np.abs(np.tril(tri, -1)).max() < 1e-10 * np.abs(tri).max()
+                assert np.all(np.diag(tri) >= -1e-12)
+                assert np.allclose(q1.T @ q1, np.eye(q1.shape[0]), atol=1e-12)
+            assert not np.array_equal(st.QL, prev.QL)
+        else:
+            assert np.array_equal(st.QL, prev.QL) and np.array_equal(st.QR, prev.QR)
+
+
 def test_soap_state_size_ratio_on_760m_shapes():
     """2mn + 2m^2 + 2n^2 over AdamW's 2mn on the 760M matrix set is 4.5
     (FOAM review, section 1)."""
@@ -388,6 +460,58 @@ def test_foam_mass_invariant_and_refresh_rule():
         assert abs(info["v_hat"].sum() - np.trace(fs.R) / (1 - 0.95 ** t)) < 1e-10 * np.trace(fs.R)
         assert info["checked"] == ((t - 1) % 4 == 0)
         assert np.allclose(fs.QR.T @ fs.QR, np.eye(n), atol=1e-12)
+
+
+def _fixed_spectrum_gradient(r, m, n, ratio):
+    """G = U diag(s) V^T with s_i = ratio^i (distinct, well separated)."""
+    u = oracle.qr_positive(r.standard_normal((m, m)))[0][:, :min(m, n)]
+    v = oracle.qr_positive(r.standard_normal((n, n)))[0][:, :min(m, n)]
+    s = ratio ** np.arange(min(m, n))
+    return (u * s[None, :]) @ v.T
+
+
+def test_foam_refresh_is_one_power_iteration_step():
+    """The refresh is one step of orthogonal (subspace) iteration on R (FOAM
+    review, section 3, with the QR power step SOAP uses). With b2 = 0 and a
+    fixed G the factor is R = G^T G at every step, so after k refreshes from
+    Q_R = I the basis is qr(R^k) (R^k = Q_k (R_k ... R_1) with positive
+    triangular factors), and repeated refreshes converge to R's eigenbasis,
+    which drives rho to zero. A refresh that factors R alone, or Q_R^T R,
+    stalls at one basis and fails both checks."""
+    r = _rng(32)
+    m, n = 7, 5
+    g = _fixed_spectrum_gradient(r, m, n, 0.8)
+    hp = dict(FOAM_HP, beta2=0.0)
+    fs = oracle.foam_init(m, n)
+    w = np.zeros((m, n))
+    rr = g.T @ g
+    for k in range(1, 5):
+        w, fs, _, info = oracle.foam_step(w, g, fs, k, pf=1, tol=0.0, **hp)
+        assert info["refreshed"]
+        q_k = np.linalg.qr(np.linalg.matrix_power(rr, k))[0]
+        q_k = q_k * np.sign(np.diag(q_k.T @ fs.QR))[None, :]
+        assert np.abs(fs.QR - q_k).max() < 1e-9
+        assert np.all(np.diag(fs.QR.T @ rr @ fs.QR) > 0)
+    rhos = []
+    for t in range(5, 120):
+        w, fs, _, info = oracle.foam_step(w, g, fs, t, pf=1, tol=0.0, **hp)
+        rhos.append(info["rho"])
+    assert rhos[0] > 1e-3 and rhos[-1] < 1e-10
+    lam = np.linalg.eigvalsh(rr)[::-1]
+    d = np.diag(fs.QR.T @ rr @ fs.QR)
+    assert np.abs(d - lam).max() < 1e-12 * lam[0]
+
+
+def test_foam_refresh_needs_rho_strictly_above_tol():
+    """The criterion refreshes only when rho exceeds tol: with an exactly
+    diagonal R in the current basis (G with orthogonal columns, Q_R = I),
+    rho is exactly 0 and tol = 0 keeps the basis."""
+    g = np.zeros((6, 4))
+    g[0, 0], g[1, 1], g[2, 2], g[3, 3], g[4, 0] = 2.0, 1.5, 0.5, 0.25, 1.0
+    fs = oracle.foam_init(6, 4)
+    _, fs2, _, info = oracle.foam_step(np.zeros((6, 4)), g, fs, 1, pf=1, tol=0.0, **FOAM_HP)
+    assert info["checked"] and info["rho"] == 0.0 and not info["refreshed"]
+    assert np.array_equal(fs2.QR, np.eye(4))
 
 
 def test_offdiag_ratio_values():
