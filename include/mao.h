@@ -371,6 +371,28 @@ MAO_API size_t mao_qr_workspace_size(int64_t n);
 MAO_API mao_status mao_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Failure of the refresh. The panels of the QR synchronise their workgroups
+ * with bounded grid barriers inside cooperative launches. Should a barrier
+ * wait time out (about a second; only a device that cannot keep the grid
+ * resident would), every barrier of that QR stops waiting, the kernels exit,
+ * and the QR writes NaN to its whole output basis: mao_qr's Q, the refreshed
+ * Q_L / Q_R of soap_step and the Q_R of foam_step (and of the many-matrix
+ * calls). The step's update and weights then come out NaN rather than
+ * silently wrong; the error surfaces at the caller's next check of the
+ * results, as for any asynchronous fault.
+ *
+ * mao_dbg_qr -- mao_qr with test flags (kernel-level checks only).
+ * MAO_DBG_QR_ABORT_BARRIERS starts the QR with its time-out flag raised, so
+ * that every barrier gives up at once -- what a real time-out does -- and the
+ * NaN result above can be checked without waiting for one. Other bits:
+ * MAO_E_HPARAM.
+ */
+#define MAO_DBG_QR_ABORT_BARRIERS 1
+MAO_API mao_status mao_dbg_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n,
+                              void* workspace, size_t workspace_bytes, int32_t flags,
+                              void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Observability: reductions over buffers the steps already hold             */
 /* ------------------------------------------------------------------------ */

@@ -97,6 +97,8 @@ EXPORTS = {
     "mao_qr_workspace_size": (c_size_t, [c_int64]),
     "mao_qr": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_size_t,
                          c_void_p]),
+    "mao_dbg_qr": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_size_t,
+                             c_int32, c_void_p]),
     "mao_matrix_rms_workspace_size": (c_size_t, [Batch]),
     "mao_matrix_rms": (c_int32, [Batch, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mao_ns_residual_workspace_size": (c_size_t, [Batch]),
@@ -471,8 +473,13 @@ def gemm_nt(A, B, *, alpha=1.0, beta=0.0, C0=None, out=None, symmetric=False, b_
     return out
 
 
-def qr(P, out=None):
-    """Q of the Householder QR of square fp32 P with diag(R) >= 0."""
+DBG_QR_ABORT_BARRIERS = 1
+
+
+def qr(P, out=None, dbg_flags: int = 0):
+    """Q of the Householder QR of square fp32 P with diag(R) >= 0.
+    ``dbg_flags`` (tests only) goes to mao_dbg_qr: DBG_QR_ABORT_BARRIERS
+    starts the QR with its barrier time-out flag raised."""
     lib = load()
     n = P.shape[0]
     P = padded(P)
@@ -480,6 +487,10 @@ def qr(P, out=None):
         out = empty_matrix(n, n, device=P.device)
     need = lib.mao_qr_workspace_size(n)
     buf = workspace(need, P.device)
-    _check(lib.mao_qr(_ptr(P), P.stride(0), _ptr(out), out.stride(0), n, _ptr(buf), buf.numel(),
-                      _stream()), "mao_qr")
+    if dbg_flags:
+        _check(lib.mao_dbg_qr(_ptr(P), P.stride(0), _ptr(out), out.stride(0), n, _ptr(buf),
+                              buf.numel(), dbg_flags, _stream()), "mao_dbg_qr")
+    else:
+        _check(lib.mao_qr(_ptr(P), P.stride(0), _ptr(out), out.stride(0), n, _ptr(buf),
+                          buf.numel(), _stream()), "mao_qr")
     return out

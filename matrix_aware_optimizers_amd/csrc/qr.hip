@@ -26,13 +26,15 @@
 // dependency is carried by one grid barrier per column (partial sums of the
 // tail norm and of the dot products with the remaining panel columns, summed
 // by every workgroup in the same order). Barrier waits are bounded: on a time
-// out the kernel raises a flag and stops waiting, so it always exits.
+// out the kernel raises a flag and stops waiting, so it always exits, and the
+// flag NaN-poisons that job's basis at the end of the QR.
 #include "qr.hpp"
 
 #include "elementwise.hpp"
 #include "gemm.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 namespace mao {
@@ -667,9 +669,43 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
   }
 }
 
-__global__ void zero_u32_kernel(unsigned* p, int n, int* err) {
+__global__ void zero_u32_kernel(unsigned* p, int n, int* err, int err_init) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
-  if (threadIdx.x == 0) *err = 0;
+  if (threadIdx.x == 0) *err = err_init;
+}
+
+// A grid barrier that timed out (its flag raised) leaves the panels, and so
+// the basis, undefined. Every job whose flag is up gets E and its row-major Q
+// (when written) set to NaN, so that the step's update and weights come out
+// NaN instead of silently wrong. One launch covers up to kPoisonJobs jobs
+// (blockIdx.y); jobs with a zero predicate or a clear flag return at once.
+constexpr int kPoisonJobs = 32;
+struct PoisonArgs {
+  const int* err;      // job j's flag at err + j * err_stride
+  int64_t err_stride;  // ints
+  float* E;            // job j at E + j * sE
+  int64_t ldE, sE;
+  float* Q[kPoisonJobs];
+  int64_t ldQ[kPoisonJobs];
+  const int* pred;
+  int64_t spred;
+  int n, j0;           // n x n matrices; first job of this launch
+};
+
+__global__ __launch_bounds__(256) void qr_poison_kernel(PoisonArgs a) {
+  const int q = blockIdx.y, j = a.j0 + q;
+  if (a.pred != nullptr && a.pred[j * a.spred] == 0) return;
+  if (__hip_atomic_load(a.err + j * a.err_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+    return;
+  const float nan = __builtin_nanf("");
+  const int64_t total = (int64_t)a.n * a.n;
+  float* E = a.E + j * a.sE;
+  float* Q = a.Q[q];
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / a.n, c = i - r * a.n;
+    E[r * a.ldE + c] = nan;
+    if (Q != nullptr) Q[r * a.ldQ[q] + c] = nan;
+  }
 }
 
 // Skinny products W = A B^T (M x nb, K long -- the V^T projections of the
@@ -791,18 +827,22 @@ namespace {
 
 // Jobs whose panel grids fit on the device together (one workgroup per CU
 // for the panel kernels' LDS footprint), capped by the launch table.
+// The per-device figure is cached; threads that race on the first call both
+// compute the same value, and the atomic store/load keeps that race defined.
 int jobs_per_launch(int G) {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
+  int slots = cached[dev].load(std::memory_order_relaxed);
+  if (slots == 0) {
     int cus = 0, b1 = 0, b2 = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, qr_panel_chol_kernel, TPB, 0) != hipSuccess) b1 = 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b2, qr_panel_kernel, TPB, 0) != hipSuccess) b2 = 1;
-    cached[dev] = std::max(1, cus * std::max(1, std::min(b1, b2)));
+    slots = std::max(1, cus * std::max(1, std::min(b1, b2)));
+    cached[dev].store(slots, std::memory_order_relaxed);
   }
-  return std::max(1, std::min(kQrMaxJobs, cached[dev] / std::max(G, 1)));
+  return std::max(1, std::min(kQrMaxJobs, slots / std::max(G, 1)));
 }
 
 }  // namespace
@@ -817,8 +857,9 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
   for (int j = 0; j < nj; ++j) {
     Carver c(b.work + (size_t)j * wst);
     w[j] = carve_qr_work(c, n);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, w[j].counters, 2 * np, w[j].err);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, (unsigned*)w[j].fail, np, w[j].err);
+    const int err0 = b.abort_barriers ? 1 : 0;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, w[j].counters, 2 * np, w[j].err, err0);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, (unsigned*)w[j].fail, np, w[j].err, err0);
   }
   MAO_LAUNCH_CHECK();
   auto job_pred = [&](int j) -> const int* { return b.pred ? b.pred + j * b.spred : nullptr; };
@@ -960,12 +1001,35 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
       MAO_TRY(launch_gemm(MAO_F32, pq, cn, stream, TAG_QR));
     }
   }
+
+  for (int c0 = 0; c0 < nj; c0 += kPoisonJobs) {
+    const int cn = std::min(kPoisonJobs, nj - c0);
+    PoisonArgs pa;
+    pa.err = w[0].err;
+    pa.err_stride = (int64_t)(wst / sizeof(int));
+    pa.E = b.E;
+    pa.ldE = b.ldE;
+    pa.sE = b.sE;
+    for (int q = 0; q < kPoisonJobs; ++q) {
+      const bool has = q < cn && b.Q && b.Q[c0 + q];
+      pa.Q[q] = has ? b.Q[c0 + q] : nullptr;
+      pa.ldQ[q] = has ? b.ldQ[c0 + q] : 0;
+    }
+    pa.pred = b.pred;
+    pa.spred = b.spred;
+    pa.n = n;
+    pa.j0 = c0;
+    const int blocks = (int)std::min<int64_t>(256, ceil_div((int64_t)n * n, 256));
+    hipLaunchKernelGGL(qr_poison_kernel, dim3(blocks, cn), dim3(256), 0, stream, pa);
+    MAO_LAUNCH_CHECK();
+  }
   return MAO_OK;
 }
 
 mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout, int64_t ldQ,
-                   QrWork& w, const int* pred, hipStream_t stream) {
+                   QrWork& w, const int* pred, hipStream_t stream, bool abort_barriers) {
   QrBatch b;
+  b.abort_barriers = abort_barriers;
   b.n = n;
   b.njob = 1;
   b.S = S;

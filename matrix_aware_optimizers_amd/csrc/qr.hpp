@@ -53,6 +53,10 @@ struct QrBatch {
   const int* pred = nullptr;
   int64_t spred = 0;
   char* work = nullptr;
+  // Start every job with its barrier time-out flag raised (test hook): every
+  // grid barrier then stops waiting at once, every kernel still exits, and
+  // the job's E and Q come out NaN -- what a real time-out produces.
+  bool abort_barriers = false;
 };
 mao_status qr_core_batched(const QrBatch& b, hipStream_t stream);
 
@@ -60,7 +64,9 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream);
 // leading dimension ldS); S is overwritten. Writes E = Q^T (row-major, ldE)
 // and, if Qout != nullptr, Q (row-major, ldQ), with column signs such that
 // diag(R) >= 0. Every kernel is skipped when pred != nullptr and *pred == 0.
+// If a grid barrier times out, E and Q are set to NaN.
 mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout,
-                   int64_t ldQ, QrWork& w, const int* pred, hipStream_t stream);
+                   int64_t ldQ, QrWork& w, const int* pred, hipStream_t stream,
+                   bool abort_barriers = false);
 
 }  // namespace mao

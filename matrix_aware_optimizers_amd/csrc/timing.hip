@@ -1,5 +1,6 @@
 // Optional HIP-event timing of the contraction launches (instrumentation for
 // the benchmark's roofline figures). Disabled unless mao_timing_enable(1).
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -16,12 +17,12 @@ struct Record {
 };
 
 std::mutex g_mu;
-bool g_on = false;
+std::atomic<bool> g_on{false};
 std::vector<Record> g_records;
 
 }  // namespace
 
-bool timing_on() { return g_on; }
+bool timing_on() { return g_on.load(std::memory_order_relaxed); }
 
 void timing_record_begin(hipStream_t s, void** start) {
   hipEvent_t e = nullptr;
@@ -51,10 +52,7 @@ using namespace mao;
 
 extern "C" {
 
-MAO_API void mao_timing_enable(int on) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  g_on = on != 0;
-}
+MAO_API void mao_timing_enable(int on) { g_on.store(on != 0, std::memory_order_relaxed); }
 
 MAO_API int mao_timing_collect(double* ms, int64_t* count, double* flops, int ntags) {
   std::vector<Record> recs;

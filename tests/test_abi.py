@@ -250,6 +250,8 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
 
     assert lib.mao_qr(FAKE, 12, FAKE + (1 << 20), 16, 12, ws, 1 << 30, None) == E_LAYOUT
     assert lib.mao_qr(FAKE, 16, FAKE + 64, 16, 12, ws, 1 << 30, None) == E_ALIAS
+    assert lib.mao_dbg_qr(FAKE, 16, FAKE + (1 << 20), 16, 12, ws, 1 << 30, 2, None) == E_HPARAM
+    assert lib.mao_dbg_qr(FAKE, 16, FAKE + 64, 16, 12, ws, 1 << 30, 1, None) == E_ALIAS
     assert lib.mao_gemm_nt(4, 4, 4, 1.0, FAKE, 8, FAKE + 4096, 8, 1, 0.0, None, 0, FAKE + 8192, 8,
                            1, None) == E_SHAPE  # symmetric needs A == B
     assert lib.mao_gemm_nt(4, 4, 0, 1.0, FAKE, 8, FAKE, 8, 1, 0.0, None, 0, FAKE + 8192, 8, 0,

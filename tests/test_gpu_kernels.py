@@ -132,3 +132,23 @@ def test_qr_zero_matrix(gpu_lib):
     torch.cuda.synchronize()
     q = to_host(Q)
     assert np.array_equal(q, np.eye(n))
+
+
+def test_qr_barrier_timeout_poisons_the_basis(gpu_lib):
+    """A QR whose grid barriers time out must not hand back a plausible basis:
+    started with its time-out flag raised (every barrier gives up at once,
+    every kernel exits), the QR writes NaN to all of Q. A normal QR on the
+    same workspace right after is unaffected (the flag is reset per QR)."""
+    import torch
+    for n in (70, 300):
+        log(f"qr abort n={n}")
+        r = np.random.default_rng(17 + n)
+        p = (r.standard_normal((n, n)) / math.sqrt(n) + 2.0 * np.eye(n)).astype(np.float32)
+        P = to_dev(p)
+        Q = gpu_lib.qr(P, dbg_flags=gpu_lib.DBG_QR_ABORT_BARRIERS)
+        torch.cuda.synchronize()
+        assert torch.isnan(Q).all().item()
+        Q2 = gpu_lib.qr(P)
+        torch.cuda.synchronize()
+        q = to_host(Q2)
+        assert rel(q, oracle.qr_positive(p.astype(np.float64))[0]) < 1e-4
