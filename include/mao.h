@@ -167,6 +167,32 @@ MAO_API mao_status muon_step_batched(int32_t ngroups, const mao_batch* W, const 
                              void* workspace, size_t workspace_bytes,
                              const mao_batch* update_out, void* stream);
 
+/*
+ * muon_step_noalloc -- muon_step for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, kernels and results as muon_step, minus
+ * the workspace: the step's scratch memory is one static device array of
+ * MAO_NOALLOC_SCRATCH_BYTES inside the library, which every GPU the library
+ * runs on holds from the library's first kernel on that GPU until the process
+ * ends. The call itself allocates nothing (its first call on a device looks
+ * up that device's address of the array, once).
+ *
+ * Limits: the step must fit the array -- muon_workspace_size(rows, cols, hp)
+ * <= MAO_NOALLOC_SCRATCH_BYTES (64 MiB: square matrices up to 2304 with
+ * bf16 Newton-Schulz and 1616 with fp32; the 1536 x 2048 and 2048 x 1536
+ * expert matrices of a fine-grained MoE bank in bf16), else MAO_E_WORKSPACE
+ * before anything is enqueued.
+ * The stream must belong to the current device (MAO_E_UNSUPPORTED
+ * otherwise). All calls on one GPU share the one array and each call leaves
+ * its contents behind: calls that may overlap in time on one GPU (different
+ * streams, different host threads) race and must be serialised by the
+ * caller. Nothing in the array needs to start at zero.
+ */
+#define MAO_NOALLOC_SCRATCH_BYTES (64u << 20)
+MAO_API size_t muon_step_noalloc_max_bytes(void);
+MAO_API mao_status muon_step_noalloc(mao_mat W, mao_mat G, mao_mat M, const mao_muon_hparams* hp,
+                                     float* update_out, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* SOAP with the real-time eigenbasis refresh                                */
 /* ------------------------------------------------------------------------ */

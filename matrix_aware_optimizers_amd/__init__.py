@@ -70,6 +70,8 @@ EXPORTS = {
     "muon_workspace_size": (c_size_t, [c_int64, c_int64, POINTER(MuonHparams)]),
     "muon_step": (c_int32, [Mat, Mat, Mat, POINTER(MuonHparams), c_void_p, c_size_t, c_void_p,
                             c_void_p]),
+    "muon_step_noalloc_max_bytes": (c_size_t, []),
+    "muon_step_noalloc": (c_int32, [Mat, Mat, Mat, POINTER(MuonHparams), c_void_p, c_void_p]),
     "muon_batched_workspace_size": (c_size_t, [c_int32, POINTER(Batch), POINTER(MuonHparams)]),
     "muon_step_batched": (c_int32, [c_int32, POINTER(Batch), POINTER(Batch), POINTER(Batch),
                                     POINTER(MuonHparams), c_void_p, c_size_t, POINTER(Batch),
@@ -254,6 +256,15 @@ def muon_step(W, G, M, *, update_out=None, ws=None, **hp_kw):
     buf = ws if ws is not None else workspace(need, W.device)
     _check(lib.muon_step(mat(W), mat(G), mat(M), ctypes.byref(hp), _ptr(buf), buf.numel(),
                          _ptr(update_out), _stream()), "muon_step")
+
+
+def muon_step_noalloc(W, G, M, *, update_out=None, **hp_kw):
+    """muon_step without a workspace: the library's static scratch array
+    serves instead (no allocation here or in the library)."""
+    lib = load()
+    hp = muon_hparams(**hp_kw)
+    _check(lib.muon_step_noalloc(mat(W), mat(G), mat(M), ctypes.byref(hp), _ptr(update_out),
+                                 _stream()), "muon_step_noalloc")
 
 
 def muon_step_batched(groups, *, update_out=None, ws=None, **hp_kw):

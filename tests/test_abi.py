@@ -266,6 +266,19 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
                            16, 2, None) == 4  # K x N B: ldb < N
 
 
+def test_noalloc_limits_checked_before_any_hip_call():
+    """muon_step_noalloc rejects a step that does not fit its static scratch
+    array, and a NULL hp, before it touches the device."""
+    lib = mao.load()
+    assert lib.muon_step_noalloc_max_bytes() == 64 << 20
+    hp = mao.muon_hparams(ns_dtype="bf16")
+    big = _mat(FAKE, 4096, 4096, 4096, mao.BF16)
+    m = _mat(FAKE + (1 << 30), 4096, 4096, 4096)
+    assert lib.muon_step_noalloc(big, big, m, ctypes.byref(hp), None, None) == E_WORKSPACE
+    assert b"static array" in lib.mao_last_error()
+    assert lib.muon_step_noalloc(big, big, m, None, None, None) == E_NULL
+
+
 @needs_no_gpu
 def test_many_matrix_validation_codes():
     lib = mao.load()
