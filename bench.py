@@ -10,9 +10,12 @@ bf16 weights and gradients, fp32 momentum, synthetic seeded gradients
 (Gaussian plus a rank-16 component), a ring of two gradients per matrix so
 every step reads fresh data. Inputs are resident in HBM before timing.
 
-Prints one JSON line: steps/s of the whole job, the dominant kernel's
-roofline (the Newton-Schulz contraction, from HIP events around every launch
-inside the timed region) and the fp64 CPU oracle's rate on a bounded sample.
+Prints one JSON line: steps/s of the whole job (K timed steps, no per-launch
+instrumentation), the dominant kernel's roofline (the Newton-Schulz
+contraction, from HIP events around every launch of a second region of K
+steps), the fp64 CPU oracle's rate on a bounded sample of the workload's own
+matrices, and -- under "soap8b" -- the same 8B layer under SOAP (steps/s and
+the rate of its fp32 contractions against the fp32 and bf16 peaks).
 
 Other workloads (--workload): moe (128-expert bank, batched Muon+), c1muon /
 c1soap (256x512 fp32 Muon and SOAP), soap8b (the 8B layer under SOAP),
@@ -197,30 +200,61 @@ def moe_groups():
     return out
 
 
-def cpu_baseline_muon(sample_rows: int, sample_cols: int, total_ns_flops: float,
-                      seed_config: str, spec_index: int):
-    """The oracle (fp64, NumPy) on one matrix of the set, scaled to the whole
-    step by Newton-Schulz flops."""
-    import oracle
-    import synth
+def _host_description():
+    """nproc, CPU model and BLAS of this host (for the baseline record)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads, blas = os.cpu_count(), "unknown"
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max((d.get("num_threads", 1) for d in info), default=os.cpu_count())
+        info = [d for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+        if info:
+            threads = max(d.get("num_threads", 1) for d in info)
+            blas = ",".join(sorted({f"{d.get('internal_api')} {d.get('version')}" for d in info}))
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    spec = synth.MatrixSpec("sample", sample_rows, sample_cols, spec_index)
-    w = synth.bf16_round(synth.init_weight(seed_config, spec)).astype(np.float64)
-    g = synth.bf16_round(synth.gradient(seed_config, spec, 1)).astype(np.float64)
-    mom = np.zeros_like(w)
-    t0 = time.perf_counter()
-    oracle.muon_step(w, g, mom, lr=1e-3, mu=0.95, weight_decay=0.1, ns_steps=5)
-    dt = time.perf_counter() - t0
-    scale = total_ns_flops / ns_alg_flops(sample_rows, sample_cols)
-    return {"value": 1.0 / (dt * scale), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"one fp64 Muon step (5 iterations) of the {sample_rows}x{sample_cols} "
-                       f"matrix took {dt:.2f} s; scaled by Newton-Schulz flops "
-                       f"(x{scale:.2f}) to the whole set")}
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model, "blas": blas}, int(threads)
+
+
+def cpu_baseline_muon(groups, seed_config: str, budget_s: float = 60.0):
+    """The oracle (fp64, NumPy) on the workload's own matrices, one Muon step
+    each (5 iterations), in the set's order, until the time budget is spent;
+    the whole step's rate is the flop-weighted extrapolation from the matrices
+    that ran (exact when they all ran)."""
+    import oracle
+    import synth
+    host, threads = _host_description()
+    specs = [sp for _, sps in groups for sp in sps]
+    total = sum(ns_alg_flops(sp.rows, sp.cols) for sp in specs)
+    done, done_fl, t_all = [], 0.0, 0.0
+    for sp in specs:
+        w = synth.bf16_round(synth.init_weight(seed_config, sp)).astype(np.float64)
+        g = synth.bf16_round(synth.gradient(seed_config, sp, 1)).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.muon_step(w, g, np.zeros_like(w), lr=1e-3, mu=0.95, weight_decay=0.1, ns_steps=5)
+        dt = time.perf_counter() - t0
+        t_all += dt
+        done_fl += ns_alg_flops(sp.rows, sp.cols)
+        done.append(f"{sp.rows}x{sp.cols} {dt:.2f} s")
+        log(f"  oracle {sp.name} {sp.rows}x{sp.cols}: {dt:.2f} s")
+        if t_all >= budget_s:
+            break
+    whole = len(done) == len(specs)
+    est = t_all if whole else t_all * total / done_fl
+    what = ("the whole set, one step" if whole else
+            f"{len(done)} of {len(specs)} matrices within a {budget_s:.0f} s budget, scaled by "
+            f"Newton-Schulz flops (x{total / done_fl:.2f}) to the set")
+    return {"value": 1.0 / est, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 Muon step (5 iterations) of the workload's matrices: {what} "
+                      f"[{'; '.join(done)}]",
+            **host}
 
 
 def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
@@ -234,8 +268,7 @@ def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
     for i in range(args.warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    mao.timing_collect()
-    mao.timing_enable(True)
+    # timed region: K steps, no per-launch instrumentation
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -243,9 +276,19 @@ def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
         wl.step(args.warmup + i)
     end.record()
     torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    # second region of K steps with HIP events around every contraction
+    # launch (recorded on the library's stream): the per-kernel split
+    mao.timing_collect()
+    mao.timing_enable(True)
+    start.record()
+    for i in range(args.steps):
+        wl.step(args.warmup + args.steps + i)
+    end.record()
+    torch.cuda.synchronize()
     mao.timing_enable(False)
     tim = mao.timing_collect()
-    ms = start.elapsed_time(end) / args.steps
+    ms_instr = start.elapsed_time(end) / args.steps
     ns_ms = sum(tim[k][0] for k in ("ns_gram", "ns_square", "ns_apply"))
     ns_cnt = sum(tim[k][1] for k in ("ns_gram", "ns_square", "ns_apply"))
     ns_fl = sum(tim[k][2] for k in ("ns_gram", "ns_square", "ns_apply"))
@@ -273,6 +316,7 @@ def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
                    "ns_steps": 5, "ns_dtype": dtype, "norm_mode": norm_mode,
                    "weights": dtype, "momentum": "fp32"},
         "step_tflops_alg": wl.ns_flops() / (ms * 1e-3) / 1e12,
+        "ms_per_step_instrumented": ms_instr,
         "roofline": {"bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s",
@@ -285,8 +329,7 @@ def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline_muon(sample[0], sample[1], wl.ns_flops(), sample[2],
-                                                 sample[3])
+        line["cpu_baseline"] = cpu_baseline_muon(groups, sample[2])
     return line
 
 
@@ -404,7 +447,7 @@ class SoapLikeWorkload:
 
 
 def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, embedding=None,
-                 side="input"):
+                 side="input", split_steps=0):
     import torch
 
     import matrix_aware_optimizers_amd as mao
@@ -422,29 +465,39 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
     # steps of a second or more: wait for each step and say so, so that a long
     # run keeps printing (the added host wait per step is microseconds)
     slow = (time.perf_counter() - w0) / max(args.warmup, 1) > 1.0
-    mao.timing_collect()
-    mao.timing_enable(True)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        wl.step(t)
-        t += 1
-        if slow:
-            torch.cuda.synchronize()
-            log(f"step {i + 1}/{args.steps} done")
-    end.record()
-    torch.cuda.synchronize()
+
+    def region(steps, tag):
+        nonlocal t
+        start.record()
+        for i in range(steps):
+            wl.step(t)
+            t += 1
+            if slow:
+                torch.cuda.synchronize()
+                log(f"{tag} step {i + 1}/{steps} done")
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    # timed region without per-launch instrumentation, then a shorter one with
+    # HIP events around every contraction launch for the per-kernel split
+    ms = region(args.steps, "timed")
+    split_steps = max(1, min(args.steps, split_steps if split_steps else args.steps))
+    mao.timing_collect()
+    mao.timing_enable(True)
+    ms_instr = region(split_steps, "instrumented")
     mao.timing_enable(False)
     tim = mao.timing_collect()
-    ms = start.elapsed_time(end) / args.steps
     per_tag = {k: {"ms_total": round(v[0], 4), "launches": v[1],
                    "tflops": round(v[2] / (v[0] * 1e-3) / 1e12, 2) if v[0] > 0 else 0.0}
                for k, v in tim.items() if v[1] > 0}
     gemm_ms = sum(v[0] for v in tim.values())
     gemm_fl = sum(v[2] for v in tim.values())
     achieved = gemm_fl / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
-    log(f"{ms:.3f} ms/step; contractions {gemm_ms / args.steps:.3f} ms/step at {achieved:.1f} TFLOP/s")
+    log(f"{ms:.3f} ms/step; contractions {gemm_ms / split_steps:.3f} ms/step at "
+        f"{achieved:.1f} TFLOP/s")
     return {
         "metric": METRIC, "value": 1000.0 / ms, "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -456,7 +509,33 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
                      "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
                      "kernel": "all timed contractions of the step (gemm_f32_dl_kernel rotations and products, QR updates and projections)"},
         "kernels": per_tag,
+        "ms_per_step_instrumented": ms_instr,
+        "instrumented_steps": split_steps,
     }
+
+
+def soap8b_summary(args):
+    """The 8B layer under SOAP (soap_step_many over the five matrices, refresh
+    every step, bf16 W and G, fp32 state): steps/s from a timed region
+    without instrumentation, and the contraction split from an instrumented
+    step. The rotation / power-iteration / factor products and the QR's
+    updates are fp32 MFMA work, so their rate is given against both the fp32
+    and the bf16 dense peaks."""
+    import synth
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup = args.soap8b_steps, 2
+    line = run_soaplike(sub, "llama8b_layer_soap", "soap", "c3", synth.specs("c3"), "bf16",
+                        "bf16", split_steps=1)
+    k = line["kernels"]
+    out = {"workload": "llama8b_layer_soap", "value": line["value"], "unit": "steps/s",
+           "ms_per_step": line["ms_per_step"], "steps": sub.steps, "warmup": sub.warmup}
+    for tag, name in (("other", "rotations_and_products"), ("qr", "qr_updates")):
+        if tag in k:
+            tf = k[tag]["tflops"]
+            out[name] = {"ms_per_step": k[tag]["ms_total"] / line["instrumented_steps"],
+                         "tflops": tf, "frac_fp32_peak": tf / PEAK_F32_TFLOPS,
+                         "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
+    return out
 
 
 def run_observe(args):
@@ -544,6 +623,9 @@ def main():
                     choices=["llama8b", "moe", "c1muon", "c1soap", "soap8b", "foam760m",
                              "foam760m_output", "soap760m", "observe8b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--soap8b-steps", type=int, default=5,
+                    help="timed steps of the 8B layer under SOAP reported beside the default "
+                         "workload (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (a known-size reference "
                          "for profiler byte counters)")
@@ -575,6 +657,11 @@ def main():
     if args.workload == "llama8b":
         line = run_muon(args, "llama8b_layer_muon_bf16", llama8b_groups(), "none",
                         (4096, 4096, "c2", 1))
+        if args.soap8b_steps > 0:
+            import gc
+            gc.collect()
+            torch.cuda.empty_cache()
+            line["soap8b"] = soap8b_summary(args)
     elif args.workload == "moe":
         line = run_muon(args, "moe128_expert_bank_muonplus_bf16", moe_groups(), "col_row",
                         (1536, 2048, "c4", 0))

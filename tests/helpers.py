@@ -26,6 +26,23 @@ def to_dev(x, dtype="f32", device="cuda"):
     return view
 
 
+def tile_max_rel(a, b, tile: int = 256) -> float:
+    """Largest relative Frobenius error over the tile x tile blocks of a 2-D
+    result (ragged edge blocks included): a localised error -- one bad band
+    of one output tile -- shows here even when the whole-matrix error is
+    small."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    worst = 0.0
+    for i in range(0, b.shape[0], tile):
+        for j in range(0, b.shape[1], tile):
+            bt = b[i:i + tile, j:j + tile]
+            den = np.linalg.norm(bt)
+            e = np.linalg.norm(a[i:i + tile, j:j + tile] - bt) / (den if den > 0 else 1.0)
+            worst = max(worst, float(e))
+    return worst
+
+
 def zeros_dev(shape, dtype="f32", device="cuda"):
     return to_dev(np.zeros(shape, np.float32), dtype, device)
 

@@ -77,6 +77,8 @@ def _run_soap(gpu_lib, m, n, steps, grad, dtype="f32", refresh_every=1):
         if "PL" in info:
             _check_basis(new.QL, info["PL"], ref.QL, f"t={t} QL")
             _check_basis(new.QR, info["PR"], ref.QR, f"t={t} QR")
+        else:  # not a refreshing step: the basis is left exactly as it was
+            assert np.array_equal(new.QL, prev.QL) and np.array_equal(new.QR, prev.QR)
         # finish the step with the GPU's basis
         w_ref, ref2, upd_ref, _ = oracle.soap_step(w_prev, g, prev, t, refresh_every=0,
                                                    q_override=(new.QL, new.QR), **HP)
@@ -414,3 +416,120 @@ def test_foam_many_more_shape_groups_than_one_launch_holds(gpu_lib):
             for k in ("M", "R", "QR", "r", "c"):
                 _close(st2[i][k], st1[i][k], f"t={t} matrix {i} {k}")
             _close(o2[i], o1[i], f"t={t} matrix {i} update")
+
+
+# ---- many-matrix calls against the oracle ----------------------------------
+
+def _teacher_force_soap_many(gpu_lib, shapes, grads, steps, refresh_every, gated_tol=1e-4):
+    """soap_step_many over all matrices each step; every matrix teacher-forced
+    against the oracle (EMAs 1e-5, bases by their defining properties, update
+    and V gated from t0 = ceil(b/a) + 2)."""
+    import torch
+    Ws = [to_dev(synth.init_weight("c1", synth.MatrixSpec("w", m, n, 20 + i)))
+          for i, (m, n) in enumerate(shapes)]
+    sts = [_soap_state_dev(m, n) for m, n in shapes]
+    outs = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in shapes]
+    for t in range(1, steps + 1):
+        prevs = [_host_soap(st) for st in sts]
+        w_prevs = [to_host(W) for W in Ws]
+        G = [to_dev(grads[i][t - 1]) for i in range(len(shapes))]
+        gpu_lib.soap_step_many([(Ws[i], G[i], sts[i]) for i in range(len(shapes))], t,
+                               update_out=outs, refresh_every=refresh_every, **HP)
+        torch.cuda.synchronize()
+        worst_u = worst_v = 0.0
+        for i, (m, n) in enumerate(shapes):
+            t0 = math.ceil(max(m, n) / min(m, n)) + 2
+            new = _host_soap(sts[i])
+            g = grads[i][t - 1].astype(np.float64)
+            _, ref, _, info = oracle.soap_step(w_prevs[i], g, prevs[i], t,
+                                               refresh_every=refresh_every, **HP)
+            assert rel(new.M, ref.M) < 1e-5 and rel(new.L, ref.L) < 1e-5
+            assert rel(new.R, ref.R) < 1e-5
+            if "PL" in info:
+                _check_basis(new.QL, info["PL"], ref.QL, f"t={t} matrix {i} QL")
+                _check_basis(new.QR, info["PR"], ref.QR, f"t={t} matrix {i} QR")
+            else:
+                assert np.array_equal(new.QL, prevs[i].QL) and np.array_equal(new.QR, prevs[i].QR)
+            _, ref2, upd, _ = oracle.soap_step(w_prevs[i], g, prevs[i], t, refresh_every=0,
+                                               q_override=(new.QL, new.QR), **HP)
+            eu, ev = rel(to_host(outs[i]), upd), rel(new.V, ref2.V)
+            if t >= t0:
+                assert eu < gated_tol and ev < gated_tol, f"t={t} matrix {i}: {eu} {ev}"
+                worst_u, worst_v = max(worst_u, eu), max(worst_v, ev)
+        log(f"  soap many t={t}: worst gated update {worst_u:.2e}, V {worst_v:.2e}")
+
+
+def test_soap_many_grouped_batches_match_oracle(gpu_lib):
+    """soap_step_many on six 1040 x 1040 matrices (each phase's products one
+    pointer-table batch on the 256 x 256 kernel, the six QRs of each side one
+    batched QR), eps = 1e-8, teacher-forced against the oracle: the many-matrix
+    path itself held to the oracle, not only to separate calls."""
+    log("soap many (grouped 256-tile batches) vs oracle")
+    shapes = [(1040, 1040)] * 6
+    grads = _square_gradients(len(shapes), 1040, 4, 61)
+    _teacher_force_soap_many(gpu_lib, shapes, grads, 4, refresh_every=1)
+
+
+@pytest.mark.parametrize("refresh_every,steps", [(2, 6), (10, 12)])
+def test_soap_periodic_refresh_teacher_forced(gpu_lib, refresh_every, steps):
+    """Standard SOAP's periodic refresh (every k steps, at t = 1, k+1, ...),
+    single calls on a Kronecker ragged shape, teacher-forced: the basis is
+    refreshed exactly on the scheduled steps and frozen bitwise in between."""
+    log(f"soap refresh every {refresh_every}, {steps} steps")
+    spec = synth.MatrixSpec("k", 200, 328, 8)
+    _run_soap(gpu_lib, 200, 328, steps, lambda t: synth.kronecker_gradient("c3", spec, t),
+              refresh_every=refresh_every)
+
+
+def test_soap_many_periodic_refresh_matches_oracle(gpu_lib):
+    """soap_step_many with refresh_every = 2 over the mixed small shapes (QR
+    sizes shared across matrices and sides), teacher-forced."""
+    log("soap many refresh every 2 vs oracle")
+    ws, gs = _many_inputs(MANY_SHAPES, 6, 63)
+    _teacher_force_soap_many(gpu_lib, MANY_SHAPES, gs, 6, refresh_every=2)
+
+
+@pytest.mark.parametrize("side", ["input", "output"])
+def test_foam_many_grouped_batches_match_oracle(gpu_lib, side):
+    """foam_step_many on six 2600 x 1040 matrices (1040 x 2600 on the output
+    side), criterion and refresh every step, teacher-forced against the oracle
+    through t0 = 5."""
+    import torch
+    log(f"foam many (grouped 256-tile batches) vs oracle, side={side}")
+    shapes = [(2600, 1040) if side == "input" else (1040, 2600)] * 6
+    steps = 5
+    ws, gs = _many_inputs(shapes, steps, 67)
+    Ws = [to_dev(w) for w in ws]
+    sts = [_foam_state_dev_many(m, n, side) for m, n in shapes]
+    outs = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in shapes]
+    for t in range(1, steps + 1):
+        prevs = [_host_foam(st) for st in sts]
+        w_prevs = [to_host(W) for W in Ws]
+        G = [to_dev(g[t - 1]) for g in gs]
+        gpu_lib.foam_step_many([(Ws[i], G[i], sts[i]) for i in range(len(shapes))], t,
+                               update_out=outs, pf=1, tol=0.0, side=side, **HP)
+        torch.cuda.synchronize()
+        worst = 0.0
+        for i, (m, n) in enumerate(shapes):
+            t0 = math.ceil(max(m, n) / min(m, n)) + 2
+            new = _host_foam(sts[i])
+            aux = to_host(sts[i]["aux"])
+            g = gs[i][t - 1].astype(np.float64)
+            _, ref, _, info = oracle.foam_step(w_prevs[i], g, prevs[i], t, pf=1, tol=0.0,
+                                               side=side, **HP)
+            assert rel(new.M, ref.M) < 1e-5 and rel(new.R, ref.R) < 1e-5
+            assert aux[3] == 1.0 and abs(aux[0] - info["rho"]) < 1e-4
+            assert bool(aux[1]) == info["refreshed"]
+            if info["refreshed"]:
+                _check_basis(new.QR, info["P"], ref.QR, f"t={t} matrix {i} QR")
+            _, ref2, upd, info2 = oracle.foam_step(w_prevs[i], g, prevs[i], t, pf=1, tol=0.0,
+                                                   q_override=new.QR,
+                                                   refresh_override=bool(aux[1]), side=side,
+                                                   **HP)
+            eu = rel(to_host(outs[i]), upd)
+            er, ec = rel(new.r, ref2.r), rel(new.c, ref2.c)
+            if t >= t0:
+                assert eu < 1e-4 and er < 1e-4 and ec < 1e-4, f"t={t} matrix {i}: {eu} {er} {ec}"
+                assert abs(aux[2] - info2["tau"]) <= 1e-4 * abs(info2["tau"])
+                worst = max(worst, eu)
+        log(f"  foam many t={t}: worst gated update {worst:.2e}")
