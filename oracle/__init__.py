@@ -28,7 +28,8 @@ Sources (page title, then section / equation):
 
 Parity status of each function is stated in its module header.
 """
-from .linalg import jacobi_svd, polar_svd, qr_positive, shampoo_polar, sym_inv_root
+from .linalg import (eigh_descending, jacobi_svd, polar_svd, qr_positive, shampoo_polar,
+                     sym_inv_root)
 from .muon import (CLASSICAL_QUINTIC, muon_plus_normalize, muon_step,
                    muon_update_direction, newton_schulz)
 from .adamw import adamw_step
@@ -37,7 +38,8 @@ from .foam import FoamState, foam_init, foam_step, foam_state_bytes, offdiag_rat
 from .observe import basis_ages, matrix_rms, ns_residual, rank1_share, rayleigh
 
 __all__ = [
-    "jacobi_svd", "polar_svd", "qr_positive", "shampoo_polar", "sym_inv_root",
+    "jacobi_svd", "polar_svd", "qr_positive", "eigh_descending", "shampoo_polar",
+    "sym_inv_root",
     "CLASSICAL_QUINTIC", "newton_schulz", "muon_plus_normalize", "muon_update_direction",
     "muon_step", "adamw_step", "SoapState", "soap_init", "soap_step", "soap_state_bytes",
     "FoamState", "foam_init", "foam_step", "foam_state_bytes", "offdiag_ratio",

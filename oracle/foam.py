@@ -32,6 +32,15 @@ claim fails. eps = 1e-8.
 ``q_override`` / ``refresh_override`` let a teacher-forced test finish the
 step with the other side's basis and refresh decision.
 
+Refresh by full eigendecomposition (``refresh="eigh"``): the review's section
+1 describes FOAM's basis as the eigenvectors of R, recomputed periodically,
+and its section 3 counts the eigendecompositions it saves. With this variant a
+triggered refresh sets Q_R to the eigenvectors of R itself (not one power
+step). Readings: the columns are ordered by descending eigenvalue -- the order
+the QR power step converges to, so both refreshes name the same basis in the
+limit -- ties kept in LAPACK's order; each column's sign follows the previous
+basis (q_new . q_old >= 0; the update does not depend on signs).
+
 Output-only variant (``side="output"``): the review's section 3 ablation
 keeps the basis on the output side instead. Reading: the mirror of the
 steps above with the factor L = b2 L + (1-b2) G G^T (m x m) and its basis
@@ -44,7 +53,9 @@ Parity: pinned (exact reconstruction of SOAP's dense rotated moment on
 Rademacher K-FAC gradients, on either side; mass invariant
 sum(tau r c^T) = tr(R_hat); rho = 0 in R's eigenbasis and no refresh at
 rho = tol; the refresh as one orthogonal-iteration step: with b2 = 0 and a
-fixed G, k refreshes give qr(R^k) and rho converges to 0; the output variant
+fixed G, k refreshes give qr(R^k) and rho converges to 0; the eigh refresh
+diagonalises R with the oracle's Jacobi-SVD eigenvalues in descending order,
+equals the limit of repeated QR refreshes and leaves rho at 0; the output variant
 equals the input variant on the transposed problem; state size
 mn + 2n^2 + m + n).
 """
@@ -54,7 +65,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .linalg import qr_positive
+from .linalg import eigh_descending, qr_positive
 
 
 @dataclass
@@ -90,13 +101,19 @@ def foam_checks(t: int, pf: int) -> bool:
 
 def foam_step(w, g, state: FoamState, t: int, *, lr: float, beta1: float, beta2: float,
               eps: float = 1e-8, weight_decay: float = 0.0, pf: int = 10, tol: float = 0.1,
-              q_override=None, refresh_override=None, side: str = "input"):
+              q_override=None, refresh_override=None, side: str = "input",
+              refresh: str = "qr"):
     """One FOAM step. Returns (W_new, new_state, U, info); ``info`` holds rho,
-    the refresh decision, P = R Q_R (when checked), tau and N. ``side``:
-    "input" (the review's FOAM) or "output" (its output-only ablation)."""
+    the refresh decision, P = R Q_R (QR refresh) or the eigenvalues (eigh
+    refresh) when checked, tau and N. ``side``: "input" (the review's FOAM) or
+    "output" (its output-only ablation). ``refresh``: "qr" (one power step)
+    or "eigh" (full eigendecomposition)."""
     if side not in ("input", "output"):
         raise ValueError(side)
+    if refresh not in ("qr", "eigh"):
+        raise ValueError(refresh)
     out_side = side == "output"
+    refresh_mode_eigh = refresh == "eigh"
     w = np.asarray(w, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     s = state.copy()
@@ -110,7 +127,9 @@ def foam_step(w, g, state: FoamState, t: int, *, lr: float, beta1: float, beta2:
         if refresh_override is not None:
             refresh = bool(refresh_override)
         info.update(checked=True, rho=rho, refreshed=refresh)
-        if refresh:
+        if refresh and refresh_mode_eigh:
+            info["eigenvalues"], s.QR = eigh_descending(s.R, ref=s.QR)
+        elif refresh:
             info["P"] = s.R @ s.QR
             s.QR = qr_positive(info["P"])[0]
     if q_override is not None:

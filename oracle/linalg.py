@@ -8,6 +8,11 @@
 * ``qr_positive`` -- QR with diag(R) >= 0 (LAPACK Householder through
   ``numpy.linalg.qr``, then column signs fixed). For a full-rank input that Q
   is unique. Pinned by its defining properties in the tests.
+* ``eigh_descending`` -- eigenvectors of a symmetric matrix ordered by
+  descending eigenvalue, column signs aligned with a reference basis (LAPACK
+  through ``numpy.linalg.eigh``, then reordered). Pinned against the oracle's
+  own Jacobi SVD (eigenvalues of a PSD matrix) and against the limit of
+  repeated QR power iterations in the tests.
 * ``sym_inv_root`` / ``shampoo_polar`` -- Shampoo's (G G^T)^{-1/4} G
   (G^T G)^{-1/4} ("SOAP, Muon, and Beyond", section 1-1 and the identity of
   section 2-1; picx.dev summary, theoretical foundation), with Moore-Penrose
@@ -80,6 +85,20 @@ def qr_positive(p: np.ndarray):
     d = np.sign(np.diag(r))
     d[d == 0] = 1.0
     return q * d[None, :], r * d[:, None]
+
+
+def eigh_descending(s: np.ndarray, ref: np.ndarray | None = None):
+    """(lam, Q): S = Q diag(lam) Q^T with lam descending; where ``ref`` is given,
+    column j of Q is negated when q_j . ref_j < 0 (the sign of an eigenvector
+    is free)."""
+    w, q = np.linalg.eigh(np.asarray(s, dtype=np.float64))
+    order = np.argsort(-w, kind="stable")
+    w, q = w[order], q[:, order]
+    if ref is not None:
+        d = np.sign(np.sum(q * np.asarray(ref, dtype=np.float64), axis=0))
+        d[d == 0] = 1.0
+        q = q * d[None, :]
+    return w, q
 
 
 def sym_inv_root(s: np.ndarray, power: float, rel_floor: float = 1e-10) -> np.ndarray:

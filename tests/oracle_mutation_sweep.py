@@ -56,6 +56,8 @@ M = [
  ("oracle/foam.py", "m_rot = s.QR.T @ s.M", "m_rot = s.QR @ s.M"),
  ("oracle/foam.py", "return (t - 1) % pf == 0", "return t % pf == 0"),
  ("oracle/foam.py", "s.R = beta2 * s.R + (1.0 - beta2) * ((g @ g.T) if out_side else (g.T @ g))", "s.R = beta2 * s.R + (1.0 - beta2) * ((g @ g.T) if out_side else (g.T @ g)) * 1.001"),
+ ("oracle/linalg.py", "order = np.argsort(-w, kind=\"stable\")", "order = np.argsort(w, kind=\"stable\")"),
+ ("oracle/foam.py", "info[\"eigenvalues\"], s.QR = eigh_descending(s.R, ref=s.QR)", "info[\"eigenvalues\"], s.QR = eigh_descending(s.R @ s.QR, ref=s.QR)"),
  ("oracle/adamw.py", "(m_new / b1) / (np.sqrt(v_new / b2) + eps)", "(m_new / b1) / (np.sqrt(v_new / b2) + 1e-3)"),
  ("oracle/adamw.py", "w - lr * (weight_decay * w + upd)", "w - lr * (weight_decay * w) - lr * upd * 1.001"),
  ("oracle/linalg.py", "return q * d[None, :], r * d[:, None]", "return q, r"),

@@ -502,6 +502,51 @@ def test_foam_refresh_is_one_power_iteration_step():
     assert np.abs(d - lam).max() < 1e-12 * lam[0]
 
 
+def test_foam_eigh_refresh_diagonalises_r_in_descending_order():
+    """The eigendecomposition refresh (FOAM review, sections 1 and 3) leaves
+    Q_R^T R Q_R diagonal, with the diagonal equal to R's eigenvalues from the
+    oracle's own Jacobi SVD (R is PSD, so its singular values are its
+    eigenvalues) in descending order, and the criterion then reads rho = 0."""
+    r = _rng(36)
+    m, n = 9, 6
+    fs = oracle.foam_init(m, n)
+    w = np.zeros((m, n))
+    for t in range(1, 4):
+        g = r.standard_normal((m, n)) * np.exp(r.standard_normal((1, n)))
+        w, fs, _, info = oracle.foam_step(w, g, fs, t, pf=1, tol=0.0, refresh="eigh", **FOAM_HP)
+        assert info["refreshed"]
+        d = fs.QR.T @ fs.R @ fs.QR
+        s_ref = oracle.jacobi_svd(fs.R)[1]
+        assert np.abs(d - np.diag(np.diag(d))).max() < 1e-12 * s_ref[0]
+        assert np.abs(np.diag(d) - s_ref).max() < 1e-12 * s_ref[0]
+        assert np.all(np.diff(np.diag(d)) <= 1e-12 * s_ref[0])
+        assert np.allclose(fs.QR.T @ fs.QR, np.eye(n), atol=1e-12)
+    g = r.standard_normal((m, n))
+    _, _, _, info = oracle.foam_step(w, 0.0 * g, fs, 4, pf=1, tol=0.0, refresh="eigh",
+                                     **dict(FOAM_HP, beta2=0.999999))
+    assert info["rho"] < 1e-6
+
+
+def test_foam_eigh_refresh_is_the_limit_of_qr_refreshes():
+    """With b2 = 0 and a fixed G, repeated QR power-step refreshes converge to
+    R's eigenbasis (orthogonal iteration); one eigh refresh lands there at
+    once, with the same column order and, after sign alignment, the same
+    columns."""
+    r = _rng(37)
+    m, n = 7, 5
+    g = _fixed_spectrum_gradient(r, m, n, 0.8)
+    hp = dict(FOAM_HP, beta2=0.0)
+    fq = oracle.foam_init(m, n)
+    fe = oracle.foam_init(m, n)
+    w = np.zeros((m, n))
+    for t in range(1, 150):
+        _, fq, _, _ = oracle.foam_step(w, g, fq, t, pf=1, tol=0.0, **hp)
+    _, fe, _, info = oracle.foam_step(w, g, fe, 1, pf=1, tol=0.0, refresh="eigh", **hp)
+    signs = np.sign(np.sum(fq.QR * fe.QR, axis=0))
+    assert np.abs(fq.QR - fe.QR * signs[None, :]).max() < 1e-9
+    assert np.all(np.diff(info["eigenvalues"]) < 0)
+
+
 def test_foam_refresh_needs_rho_strictly_above_tol():
     """The criterion refreshes only when rho exceeds tol: with an exactly
     diagonal R in the current basis (G with orthogonal columns, Q_R = I),
