@@ -62,7 +62,7 @@ extern "C" {
 #define MAO_API
 #endif
 
-#define MAO_ABI_VERSION 2
+#define MAO_ABI_VERSION 3
 #define MAO_MAX_GROUPS 8
 
 typedef enum {
@@ -203,6 +203,10 @@ typedef struct {
   float weight_decay;     /* decoupled, >= 0 */
   int32_t refresh_every;  /* 1: refresh every step; k > 1: at t = 1, k+1, ...;
                              0: basis frozen */
+  int32_t back_rot_dtype; /* MAO_F32: the rotation back U = QL N QR^T on fp32
+                             MFMA; MAO_BF16: on bf16 MFMA (operands rounded to
+                             bf16, fp32 accumulation; [SMB] section 3-2 (3)
+                             allows the reduced precision on this product) */
 } mao_soap_hparams;
 
 /* SOAP optimizer state, all fp32, rows = m, cols = n of W.
@@ -251,11 +255,21 @@ typedef enum {
                           G G^T (m x m), G_rot = QR^T G */
 } mao_foam_side;
 
+/* How a refresh recomputes the basis. */
+typedef enum {
+  MAO_REFRESH_QR = 0,  /* one power-iteration step: Q <- qr(F Q) */
+  MAO_REFRESH_EIGH = 1 /* full eigendecomposition of F ([FOAM] section 1): the
+                          eigenvectors, by descending eigenvalue */
+} mao_refresh_mode;
+
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;
   int32_t pf; /* >= 1: the refresh criterion is evaluated at t = 1, pf+1, ... */
   float tol;  /* >= 0: refresh when rho > tol */
   int32_t side; /* mao_foam_side */
+  int32_t refresh; /* mao_refresh_mode; MAO_REFRESH_EIGH needs k <= 16384 */
+  int32_t back_rot_dtype; /* MAO_F32 or MAO_BF16: precision of U = N QR^T
+                             (QR N on the output side), as for SOAP */
 } mao_foam_hparams;
 
 /* FOAM state, fp32, W is m x n; k = n for MAO_FOAM_INPUT, m for
@@ -284,6 +298,10 @@ MAO_API size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hp
  *   M <- b1 M + (1-b1) G;  R <- b2 R + (1-b2) G^T G
  *   if (t-1) % pf == 0: D = QR^T R QR, rho = ||D - diag D||_F / ||D||_F;
  *                       if rho > tol: QR <- qr(R QR)       (decided on device)
+ *                       (hp->refresh = MAO_REFRESH_EIGH: QR <- the
+ *                       eigenvectors of R by descending eigenvalue, from a
+ *                       block-Jacobi diagonalisation of D warm-started in the
+ *                       current basis)
  *   G_rot = G QR;  M_rot = M QR
  *   r <- b2 r + (1-b2) rowmean(G_rot^2);  c <- b2 c + (1-b2) colmean(G_rot^2)
  *   tau = tr(R / (1-b2^t)) / (|r_hat|_1 |c_hat|_1)  (0 if r = c = 0)
@@ -383,6 +401,26 @@ MAO_API mao_status mao_gemm_nt(int64_t M, int64_t N, int64_t K, float alpha, con
                        int64_t lda, const void* B, int64_t ldb, int32_t in_dtype, float beta,
                        const float* C0, int64_t ldc0, float* D, int64_t ldd, int32_t mode,
                        void* stream);
+
+/* Workspace bytes for mao_eigh on an n x n matrix (0 outside 1..16384). */
+MAO_API size_t mao_eigh_workspace_size(int64_t n);
+
+/*
+ * mao_eigh -- eigendecomposition of a symmetric fp32 matrix F (row-major
+ * n x n, 1 <= n <= 16384; only its symmetric part (F + F^T)/2 is used), the
+ * refresh primitive of foam_step with MAO_REFRESH_EIGH ([FOAM] section 1:
+ * the basis is the eigenvectors of the factor). Q (n x n, row-major) receives
+ * the orthonormal eigenvectors as columns, ordered by descending eigenvalue
+ * (ties by index); evals (NULL or n device floats) the eigenvalues in that
+ * order; info (NULL or 13 device floats) the off-diagonal ratio
+ * ||D - diag D||_F / ||D||_F after each of up to 12 block-Jacobi sweeps (0
+ * after convergence), then the number of sweeps run. F and Q must not
+ * overlap. Accuracy: fp32 -- eigenvalues to about 1e-6 of the largest,
+ * eigenvectors to that over the eigenvalue gap.
+ */
+MAO_API mao_status mao_eigh(const float* F, int64_t ldf, float* Q, int64_t ldq, float* evals,
+                            float* info, int64_t n, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Workspace bytes for mao_qr on an n x n matrix. */
 MAO_API size_t mao_qr_workspace_size(int64_t n);

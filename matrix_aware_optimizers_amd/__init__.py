@@ -49,7 +49,8 @@ class MuonHparams(ctypes.Structure):
 
 class SoapHparams(ctypes.Structure):
     _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
-                ("weight_decay", c_float), ("refresh_every", c_int32)]
+                ("weight_decay", c_float), ("refresh_every", c_int32),
+                ("back_rot_dtype", c_int32)]
 
 
 class SoapStateC(ctypes.Structure):
@@ -58,7 +59,12 @@ class SoapStateC(ctypes.Structure):
 
 class FoamHparams(ctypes.Structure):
     _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
-                ("weight_decay", c_float), ("pf", c_int32), ("tol", c_float), ("side", c_int32)]
+                ("weight_decay", c_float), ("pf", c_int32), ("tol", c_float), ("side", c_int32),
+                ("refresh", c_int32), ("back_rot_dtype", c_int32)]
+
+
+REFRESH_MODES = {"qr": 0, "eigh": 1}
+EIGH_MAX_SWEEPS = 12
 
 
 class FoamStateC(ctypes.Structure):
@@ -96,6 +102,9 @@ EXPORTS = {
     "mao_gemm_nt": (c_int32, [c_int64, c_int64, c_int64, c_float, c_void_p, c_int64, c_void_p,
                               c_int64, c_int32, c_float, c_void_p, c_int64, c_void_p, c_int64,
                               c_int32, c_void_p]),
+    "mao_eigh_workspace_size": (c_size_t, [c_int64]),
+    "mao_eigh": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+                           c_void_p, c_size_t, c_void_p]),
     "mao_qr_workspace_size": (c_size_t, [c_int64]),
     "mao_qr": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_size_t,
                          c_void_p]),
@@ -286,10 +295,16 @@ def muon_step_batched(groups, *, update_out=None, ws=None, **hp_kw):
                                  _stream()), "muon_step_batched")
 
 
-def soap_hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, refresh_every=1):
+def _dtype_code(d):
+    return {"f32": F32, "bf16": BF16}[d] if isinstance(d, str) else int(d)
+
+
+def soap_hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, refresh_every=1,
+                 back_rot_dtype="f32"):
     hp = SoapHparams()
     hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay = lr, beta1, beta2, eps, weight_decay
     hp.refresh_every = refresh_every
+    hp.back_rot_dtype = _dtype_code(back_rot_dtype)
     return hp
 
 
@@ -312,11 +327,13 @@ FOAM_SIDES = {"input": 0, "output": 1}
 
 
 def foam_hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, pf=10, tol=0.1,
-                 side="input"):
+                 side="input", refresh="qr", back_rot_dtype="f32"):
     hp = FoamHparams()
     hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay = lr, beta1, beta2, eps, weight_decay
     hp.pf, hp.tol = pf, tol
     hp.side = FOAM_SIDES[side] if isinstance(side, str) else int(side)
+    hp.refresh = REFRESH_MODES[refresh] if isinstance(refresh, str) else int(refresh)
+    hp.back_rot_dtype = _dtype_code(back_rot_dtype)
     return hp
 
 
@@ -481,6 +498,21 @@ def gemm_nt(A, B, *, alpha=1.0, beta=0.0, C0=None, out=None, symmetric=False, b_
                            _ptr(B), B.stride(0), dtype_code(A), beta, _ptr(C0),
                            C0.stride(0) if C0 is not None else 0, _ptr(out), out.stride(0),
                            mode, _stream()), "mao_gemm_nt")
+    return out
+
+
+def eigh(F, out=None, evals=None, info=None):
+    """Eigenvectors (columns, by descending eigenvalue) of symmetric fp32 F;
+    ``evals`` / ``info`` optional fp32 device tensors of n and 13 entries."""
+    lib = load()
+    n = F.shape[0]
+    F = padded(F)
+    if out is None:
+        out = empty_matrix(n, n, device=F.device)
+    need = lib.mao_eigh_workspace_size(n)
+    buf = workspace(need, F.device)
+    _check(lib.mao_eigh(_ptr(F), F.stride(0), _ptr(out), out.stride(0), _ptr(evals), _ptr(info),
+                        n, _ptr(buf), buf.numel(), _stream()), "mao_eigh")
     return out
 
 

@@ -12,6 +12,7 @@
 #include "gemm.hpp"
 #include "tiled.hpp"
 #include "qr.hpp"
+#include "eigh.hpp"
 #include "observe.hpp"
 
 namespace mao {
@@ -436,13 +437,15 @@ struct RotBufs {
   float* small;// FOAM: tau, flag, moment work
   int* flag;
   QrWork qr;
+  char* eigh = nullptr;  // eigendecomposition workspace (FOAM's eigh refresh)
   int64_t ldm, ldn;  // padded leading dims for m- and n-long rows
 };
 
 // own_qr: the bases E, the QR input S, FOAM's refresh flag and the QR
 // workspace belong to this matrix; otherwise the caller points EL, ER, S and
 // flag into the shared, size-grouped QR area of a many-matrix call.
-void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool own_qr = true) {
+void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool own_qr = true,
+               bool eigh = false) {
   R.ldm = ws_ld(m);
   R.ldn = ws_ld(n);
   const int big = std::max(m, n);
@@ -460,6 +463,7 @@ void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool
   R.small = soap ? nullptr : c.take<float>(64 + foam_moments_work_floats(m, n) + 2 * (size_t)n);
   R.flag = (soap || !own_qr) ? nullptr : c.take<int>(4);
   if (own_qr) R.qr = carve_qr_work(c, big);
+  if (own_qr && eigh) R.eigh = c.take<char>(eigh_work_stride(n));
 }
 
 mao_status check_step_common(const mao_mat& W, const mao_mat& G, int64_t t) {
@@ -699,6 +703,8 @@ mao_status check_soap_hp(const mao_soap_hparams* hp) {
   if (!hp) MAO_FAIL(MAO_E_NULL, "hparams is NULL");
   MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
   if (hp->refresh_every < 0) MAO_FAIL(MAO_E_HPARAM, "refresh_every=%d", hp->refresh_every);
+  if (!dtype_ok(hp->back_rot_dtype)) MAO_FAIL(MAO_E_DTYPE, "back_rot_dtype=%d", hp->back_rot_dtype);
+  if (hp->back_rot_dtype == MAO_BF16) MAO_FAIL(MAO_E_UNSUPPORTED, "bf16 back-rotation");
   return MAO_OK;
 }
 
@@ -784,8 +790,14 @@ mao_status check_foam_hp(const mao_foam_hparams* hp) {
   if (!(hp->tol >= 0.f)) MAO_FAIL(MAO_E_HPARAM, "tol=%g must be >= 0", (double)hp->tol);
   if (hp->side != MAO_FOAM_INPUT && hp->side != MAO_FOAM_OUTPUT)
     MAO_FAIL(MAO_E_HPARAM, "side=%d must be 0 (input) or 1 (output)", hp->side);
+  if (hp->refresh != MAO_REFRESH_QR && hp->refresh != MAO_REFRESH_EIGH)
+    MAO_FAIL(MAO_E_HPARAM, "refresh=%d must be 0 (QR) or 1 (eigh)", hp->refresh);
+  if (!dtype_ok(hp->back_rot_dtype)) MAO_FAIL(MAO_E_DTYPE, "back_rot_dtype=%d", hp->back_rot_dtype);
+  if (hp->back_rot_dtype == MAO_BF16) MAO_FAIL(MAO_E_UNSUPPORTED, "bf16 back-rotation");
   return MAO_OK;
 }
+
+bool foam_eigh(const mao_foam_hparams* hp) { return hp->refresh == MAO_REFRESH_EIGH; }
 
 bool foam_out(const mao_foam_hparams* hp) { return hp->side == MAO_FOAM_OUTPUT; }
 
@@ -795,6 +807,9 @@ mao_status validate_foam(const mao_mat& W, const mao_mat& G, const mao_foam_stat
   if (!st) MAO_FAIL(MAO_E_NULL, "state is NULL");
   MAO_TRY(check_step_common(W, G, t));
   const int64_t m = W.rows, n = W.cols, k = foam_out(hp) ? m : n;
+  if (foam_eigh(hp) && k > kEighMaxN)
+    MAO_FAIL(MAO_E_UNSUPPORTED, "eigendecomposition refresh of a %lld x %lld factor (at most %d)",
+             (long long)k, (long long)k, kEighMaxN);
   MAO_TRY(check_state_mat("M", st->M, m, n));
   MAO_TRY(check_state_mat("R", st->R, k, k));
   MAO_TRY(check_state_mat("QR", st->QR, k, k));
@@ -939,6 +954,7 @@ struct QrGroup {
   float* E = nullptr;
   int* flags = nullptr;
   char* work = nullptr;
+  char* eigh = nullptr;    // FOAM's eigendecomposition refresh: per-job workspaces
   int64_t ld = 0, sz = 0;  // leading dimension and per-job stride of S and E
 };
 
@@ -950,7 +966,8 @@ struct QrGroup {
 // gb: receives the pointer table of the grouped products (at most two
 // products per matrix in a phase, five pointers each).
 void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<RotBufs>& R,
-                std::vector<QrGroup>& groups, bool fout = false, GemmBatch* gb = nullptr) {
+                std::vector<QrGroup>& groups, bool fout = false, GemmBatch* gb = nullptr,
+                bool eigh = false) {
   R.assign(count, RotBufs{});
   std::vector<std::pair<int, QrJobRef>> all;
   for (int i = 0; i < count; ++i) {
@@ -980,6 +997,7 @@ void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<R
     g.E = c.take<float>((size_t)nj * g.sz);
     g.flags = c.take<int>((size_t)nj);
     g.work = c.take<char>((size_t)nj * qr_work_stride(g.n));
+    if (eigh) g.eigh = c.take<char>((size_t)nj * eigh_work_stride(g.n));
     for (int k = 0; k < nj; ++k) {
       RotBufs& r = R[g.jobs[k].mat];
       float* e = g.E + k * g.sz;
@@ -1002,11 +1020,11 @@ void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<R
   }
 }
 
-size_t many_ws(int count, const mao_mat* W, bool soap, bool fout = false) {
+size_t many_ws(int count, const mao_mat* W, bool soap, bool fout = false, bool eigh = false) {
   Carver c(nullptr);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
-  carve_many(c, count, W, soap, R, groups, fout);
+  carve_many(c, count, W, soap, R, groups, fout, nullptr, eigh);
   return c.used + 256;
 }
 
@@ -1126,10 +1144,12 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
 
 size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hparams* hp) {
   if (!hp || rows < 1 || cols < 1) return 0;
+  if (foam_eigh(hp) && (hp->side == MAO_FOAM_OUTPUT ? rows : cols) > kEighMaxN) return 0;
   Carver c(nullptr);
   RotBufs R;
   const bool out = foam_out(hp);
-  carve_rot(c, (int)(out ? cols : rows), (int)(out ? rows : cols), false, true, R);
+  carve_rot(c, (int)(out ? cols : rows), (int)(out ? rows : cols), false, true, R, true,
+            foam_eigh(hp));
   return c.used + 256;
 }
 
@@ -1147,12 +1167,29 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
   MAO_TRY(check_workspace(workspace, workspace_bytes, foam_workspace_size(m, n, hp)));
   Carver c(workspace);
   RotBufs R;
-  carve_rot(c, out ? n : m, out ? m : n, false, true, R);
+  carve_rot(c, out ? n : m, out ? m : n, false, true, R, true, foam_eigh(hp));
   MAO_TRY(foam_pre(W, G, st, R, hp, nullptr, s));
   for (int stage = 0; stage < 3; ++stage)
     MAO_TRY(foam_criterion(k, st, R, t, hp, stage, nullptr, s));
-  if (foam_checks(hp, t))
+  if (foam_checks(hp, t) && foam_eigh(hp)) {
+    // D = Q^T R Q from the criterion, diagonalised in the current basis
+    EighJob job;
+    job.D = R.D;
+    job.ldD = R.ldn;
+    job.Q = (float*)st->QR.data;
+    job.ldQ = st->QR.ld;
+    job.E = R.ER;
+    job.ldE = R.ldn;
+    EighBatch eb;
+    eb.n = k;
+    eb.njob = 1;
+    eb.jobs = &job;
+    eb.pred = R.flag;
+    eb.work = R.eigh;
+    MAO_TRY(eigh_batched(eb, s));
+  } else if (foam_checks(hp, t)) {
     MAO_TRY(qr_core(R.S, R.ldn, k, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, R.flag, s));
+  }
   MAO_TRY(foam_rotate(W, G, st, R, hp, nullptr, s));
   MAO_TRY(foam_precondition_back(W, st, R, t, hp, update_out, nullptr, s));
   return foam_update(W, R, hp, update_out, s);
@@ -1160,9 +1197,11 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
 
 size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_foam_hparams* hp) {
   if (!hp || !W || count < 1 || count > kMaxMany) return 0;
-  for (int i = 0; i < count; ++i)
+  for (int i = 0; i < count; ++i) {
     if (W[i].rows < 1 || W[i].cols < 1) return 0;
-  return many_ws(count, W, false, foam_out(hp));
+    if (foam_eigh(hp) && (foam_out(hp) ? W[i].rows : W[i].cols) > kEighMaxN) return 0;
+  }
+  return many_ws(count, W, false, foam_out(hp), foam_eigh(hp));
 }
 
 mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
@@ -1176,12 +1215,13 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   for (int i = 0; i < count; ++i)
     MAO_TRY(validate_foam(W[i], G[i], &st[i], t, hp, update_out ? update_out[i] : nullptr, rr));
   MAO_TRY(check_no_overlap(rr));
-  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, false, foam_out(hp))));
+  MAO_TRY(check_workspace(workspace, workspace_bytes,
+                          many_ws(count, W, false, foam_out(hp), foam_eigh(hp))));
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
   GemmBatch gb;
-  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb);
+  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb, foam_eigh(hp));
   // phases: every matrix's products of a phase go out as grouped launches
   for (int i = 0; i < count; ++i) MAO_TRY(foam_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
   MAO_TRY(gemm_flush(gb, s));
@@ -1191,7 +1231,29 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
                              stage, &gb, s));
     MAO_TRY(gemm_flush(gb, s));
   }
-  if (foam_checks(hp, t)) {
+  if (foam_checks(hp, t) && foam_eigh(hp)) {
+    for (QrGroup& g : groups) {
+      const int nj = (int)g.jobs.size();
+      std::vector<EighJob> jobs(nj);
+      for (int k = 0; k < nj; ++k) {
+        const int i = g.jobs[k].mat;
+        jobs[k].D = R[i].D;
+        jobs[k].ldD = R[i].ldn;
+        jobs[k].Q = (float*)st[i].QR.data;
+        jobs[k].ldQ = st[i].QR.ld;
+        jobs[k].E = g.E + k * g.sz;
+        jobs[k].ldE = g.ld;
+      }
+      EighBatch eb;
+      eb.n = g.n;
+      eb.njob = nj;
+      eb.jobs = jobs.data();
+      eb.pred = g.flags;
+      eb.spred = 1;
+      eb.work = g.eigh;
+      MAO_TRY(eigh_batched(eb, s));
+    }
+  } else if (foam_checks(hp, t)) {
     for (QrGroup& g : groups) {
       const int nj = (int)g.jobs.size();
       std::vector<float*> q(nj);
@@ -1271,6 +1333,39 @@ mao_status mao_gemm_nt(int64_t M, int64_t N, int64_t K, float alpha, const void*
   GemmProblem p = gemm_problem((int)M, (int)N, (int)K, alpha, A, lda, B, ldb, beta, C0, ldc0, D, ldd,
                                GF_D_F32 | GF_C0_F32 | (sym ? GF_SYRK : 0) | (bkm ? GF_B_KMAJOR : 0));
   return launch_gemm(in_dtype, &p, 1, (hipStream_t)stream);
+}
+
+size_t mao_eigh_workspace_size(int64_t n) {
+  if (n < 1 || n > kEighMaxN) return 0;
+  return eigh_work_stride((int)n) + 256;
+}
+
+mao_status mao_eigh(const float* F, int64_t ldf, float* Q, int64_t ldq, float* evals, float* info,
+                    int64_t n, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n > kEighMaxN) MAO_FAIL(MAO_E_UNSUPPORTED, "n=%lld above %d", (long long)n, kEighMaxN);
+  MAO_TRY(check_mat("F", F, n, n, ldf, MAO_F32, true));
+  MAO_TRY(check_mat("Q", Q, n, n, ldq, MAO_F32, true));
+  if (((uintptr_t)evals | (uintptr_t)info) % 4 != 0) MAO_FAIL(MAO_E_LAYOUT, "evals / info misaligned");
+  std::vector<Range> rr = {mat_range(F, 1, n, n, ldf, 0, 4), mat_range(Q, 1, n, n, ldq, 0, 4)};
+  if (evals) rr.push_back(Range{(uintptr_t)evals, (uintptr_t)(evals + n)});
+  if (info) rr.push_back(Range{(uintptr_t)info, (uintptr_t)(info + kEighMaxSweeps + 1)});
+  MAO_TRY(check_no_overlap(rr));
+  MAO_TRY(check_workspace(workspace, workspace_bytes, mao_eigh_workspace_size(n)));
+  hipStream_t s = (hipStream_t)stream;
+  MAO_TRY(fill_identity(view(Q, ldq), (int)n, nullptr, s));
+  EighJob job;
+  job.D = F;
+  job.ldD = ldf;
+  job.Q = Q;
+  job.ldQ = ldq;
+  job.evals = evals;
+  EighBatch eb;
+  eb.n = (int)n;
+  eb.njob = 1;
+  eb.jobs = &job;
+  eb.work = (char*)workspace;
+  eb.info = info;
+  return eigh_batched(eb, s);
 }
 
 size_t mao_qr_workspace_size(int64_t n) {

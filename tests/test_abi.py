@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = mao.load()
-    assert lib.mao_abi_version() == 2
+    assert lib.mao_abi_version() == 3
     for code in range(10):
         assert lib.mao_status_string(code)
     assert lib.mao_status_string(99) == b"unknown status"
@@ -227,6 +227,13 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
     fst2 = mao.FoamStateC(fst.M, fst.R, fst.QR, None, fst.c, fst.aux)
     assert lib.foam_step(W, G, ctypes.byref(fst2), 1, ctypes.byref(fh), ws, fneed, None,
                          None) == E_NULL
+    assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(mao.foam_hparams(refresh=2)),
+                         ws, 1 << 30, None, None) == E_HPARAM
+    assert lib.foam_step(W, G, ctypes.byref(fst), 1,
+                         ctypes.byref(mao.foam_hparams(back_rot_dtype=5)), ws, 1 << 30, None,
+                         None) == E_DTYPE
+    assert lib.soap_step(W, G, ctypes.byref(st), 1, ctypes.byref(mao.soap_hparams(back_rot_dtype=7)),
+                         ws, 1 << 30, None, None) == E_DTYPE
     assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(mao.foam_hparams(side=2)), ws,
                          fneed, None, None) == E_HPARAM
     # the output side keeps m x m factors: the n x n state is the wrong shape
@@ -251,6 +258,12 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
     assert lib.mao_qr(FAKE, 12, FAKE + (1 << 20), 16, 12, ws, 1 << 30, None) == E_LAYOUT
     assert lib.mao_qr(FAKE, 16, FAKE + 64, 16, 12, ws, 1 << 30, None) == E_ALIAS
     assert lib.mao_dbg_qr(FAKE, 16, FAKE + (1 << 20), 16, 12, ws, 1 << 30, 2, None) == E_HPARAM
+    assert lib.mao_eigh_workspace_size(0) == 0 and lib.mao_eigh_workspace_size(16385) == 0
+    assert lib.mao_eigh_workspace_size(300) > 0
+    assert lib.mao_eigh(FAKE, 20000, FAKE + (1 << 34), 20000, None, None, 20000, ws, 1 << 30,
+                        None) == 9  # above the eigensolver's 16384
+    assert lib.mao_eigh(FAKE, 16, FAKE + 64, 16, None, None, 12, ws, 1 << 30, None) == E_ALIAS
+    assert lib.mao_eigh(FAKE, 16, FAKE + (1 << 20), 16, None, None, 12, ws, 16, None) == E_WORKSPACE
     assert lib.mao_dbg_qr(FAKE, 16, FAKE + 64, 16, 12, ws, 1 << 30, 1, None) == E_ALIAS
     assert lib.mao_gemm_nt(4, 4, 4, 1.0, FAKE, 8, FAKE + 4096, 8, 1, 0.0, None, 0, FAKE + 8192, 8,
                            1, None) == E_SHAPE  # symmetric needs A == B
