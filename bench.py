@@ -368,7 +368,8 @@ class SoapLikeWorkload:
     (equal-size QR refreshes batched), with a ring of two gradients per
     matrix."""
 
-    def __init__(self, kind, config, specs, g_dtype, w_dtype, pf=10, tol=0.1, side="input"):
+    def __init__(self, kind, config, specs, g_dtype, w_dtype, pf=10, tol=0.1, side="input",
+                 refresh="qr", back="f32"):
         import torch
 
         import matrix_aware_optimizers_amd as mao
@@ -379,10 +380,11 @@ class SoapLikeWorkload:
         tw = torch.bfloat16 if w_dtype == "bf16" else torch.float32
         if kind == "soap":
             self.hp = mao.soap_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
-                                       refresh_every=1)
+                                       refresh_every=1, back_rot_dtype=back)
         else:
             self.hp = mao.foam_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
-                                       pf=pf, tol=tol, side=side)
+                                       pf=pf, tol=tol, side=side, refresh=refresh,
+                                       back_rot_dtype=back)
         for idx, sp in enumerate(specs):
             if idx % 16 == 15:
                 log(f"  {idx + 1}/{len(specs)} matrices set up")
@@ -447,12 +449,13 @@ class SoapLikeWorkload:
 
 
 def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, embedding=None,
-                 side="input", split_steps=0):
+                 side="input", split_steps=0, refresh="qr", back="f32"):
     import torch
 
     import matrix_aware_optimizers_amd as mao
     log(f"setting up {workload_name} ({len(specs)} matrices)")
-    wl = SoapLikeWorkload(kind, config, specs, g_dtype, w_dtype, side=side)
+    wl = SoapLikeWorkload(kind, config, specs, g_dtype, w_dtype, side=side, refresh=refresh,
+                          back=back)
     if embedding:
         wl.add_embedding(*embedding)
     log("warmup")
@@ -503,8 +506,8 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": workload_name, "matrices": len(specs), "optimizer": kind,
-                   "gradients": g_dtype, "weights": w_dtype,
-                   **({"side": side} if kind == "foam" else {})},
+                   "gradients": g_dtype, "weights": w_dtype, "back_rotation": back,
+                   **({"side": side, "refresh": refresh} if kind == "foam" else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
                      "kernel": "all timed contractions of the step (gemm_f32_dl_kernel rotations and products, QR updates and projections)"},
@@ -525,10 +528,11 @@ def soap8b_summary(args):
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup = args.soap8b_steps, 2
     line = run_soaplike(sub, "llama8b_layer_soap", "soap", "c3", synth.specs("c3"), "bf16",
-                        "bf16", split_steps=1)
+                        "bf16", split_steps=1, back="bf16")
     k = line["kernels"]
     out = {"workload": "llama8b_layer_soap", "value": line["value"], "unit": "steps/s",
-           "ms_per_step": line["ms_per_step"], "steps": sub.steps, "warmup": sub.warmup}
+           "ms_per_step": line["ms_per_step"], "steps": sub.steps, "warmup": sub.warmup,
+           "back_rotation": "bf16"}
     for tag, name in (("other", "rotations_and_products"), ("qr", "qr_updates")):
         if tag in k:
             tf = k[tag]["tflops"]
@@ -621,7 +625,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b",
                     choices=["llama8b", "moe", "c1muon", "c1soap", "soap8b", "foam760m",
-                             "foam760m_output", "soap760m", "observe8b"])
+                             "foam760m_output", "foam760m_eigh", "soap760m", "observe8b"])
+    ap.add_argument("--back", default="bf16", choices=["f32", "bf16"],
+                    help="precision of the rotation back of the SOAP / FOAM workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--soap8b-steps", type=int, default=5,
                     help="timed steps of the 8B layer under SOAP reported beside the default "
@@ -672,25 +678,31 @@ def main():
     elif args.workload == "c1soap":
         import synth
         line = run_soaplike(args, "single_256x512_soap_f32", "soap", "c1", synth.specs("c1"),
-                            "f32", "f32")
+                            "f32", "f32", back=args.back)
     elif args.workload == "soap8b":
         import synth
         line = run_soaplike(args, "llama8b_layer_soap", "soap", "c3", synth.specs("c3"),
-                            "bf16", "bf16")
+                            "bf16", "bf16", back=args.back)
+    elif args.workload == "foam760m_eigh":
+        import synth
+        line = run_soaplike(args, "gpt2_760m_foam_eigh_refresh", "foam", "c5", synth.specs("c5"),
+                            "f32", "f32", embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH),
+                            refresh="eigh", back=args.back)
     elif args.workload == "foam760m":
         import synth
         line = run_soaplike(args, "gpt2_760m_foam", "foam", "c5", synth.specs("c5"), "f32", "f32",
-                            embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH))
+                            embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH), back=args.back)
     elif args.workload == "foam760m_output":
         import synth
         line = run_soaplike(args, "gpt2_760m_foam_output_side", "foam", "c5", synth.specs("c5"),
                             "f32", "f32", embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH),
-                            side="output")
+                            side="output", back=args.back)
     elif args.workload == "observe8b":
         line = run_observe(args)
     else:
         import synth
-        line = run_soaplike(args, "gpt2_760m_soap", "soap", "c5", synth.specs("c5"), "f32", "f32")
+        line = run_soaplike(args, "gpt2_760m_soap", "soap", "c5", synth.specs("c5"), "f32", "f32",
+                            back=args.back)
     print(json.dumps(line), flush=True)
 
 

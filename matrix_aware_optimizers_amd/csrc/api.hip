@@ -438,6 +438,11 @@ struct RotBufs {
   int* flag;
   QrWork qr;
   char* eigh = nullptr;  // eigendecomposition workspace (FOAM's eigh refresh)
+  // bf16 back rotation: N, the bases and SOAP's intermediate (N Q_R^T)^T
+  bf16_t* Nb = nullptr;
+  bf16_t* QRb = nullptr;
+  bf16_t* QLb = nullptr;
+  bf16_t* T2b = nullptr;
   int64_t ldm, ldn;  // padded leading dims for m- and n-long rows
 };
 
@@ -445,7 +450,7 @@ struct RotBufs {
 // workspace belong to this matrix; otherwise the caller points EL, ER, S and
 // flag into the shared, size-grouped QR area of a many-matrix call.
 void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool own_qr = true,
-               bool eigh = false) {
+               bool eigh = false, bool back_bf16 = false) {
   R.ldm = ws_ld(m);
   R.ldn = ws_ld(n);
   const int big = std::max(m, n);
@@ -464,6 +469,14 @@ void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool
   R.flag = (soap || !own_qr) ? nullptr : c.take<int>(4);
   if (own_qr) R.qr = carve_qr_work(c, big);
   if (own_qr && eigh) R.eigh = c.take<char>(eigh_work_stride(n));
+  if (back_bf16) {
+    R.Nb = c.take<bf16_t>((size_t)m * R.ldn);
+    R.QRb = c.take<bf16_t>((size_t)n * R.ldn);
+    if (soap) {
+      R.QLb = c.take<bf16_t>((size_t)m * R.ldm);
+      R.T2b = c.take<bf16_t>((size_t)n * R.ldm);
+    }
+  }
 }
 
 mao_status check_step_common(const mao_mat& W, const mao_mat& G, int64_t t) {
@@ -670,7 +683,7 @@ size_t soap_workspace_size(int64_t rows, int64_t cols, const mao_soap_hparams* h
   if (!hp || rows < 1 || cols < 1) return 0;
   Carver c(nullptr);
   RotBufs R;
-  carve_rot(c, (int)rows, (int)cols, true, true, R);
+  carve_rot(c, (int)rows, (int)cols, true, true, R, true, false, hp->back_rot_dtype == MAO_BF16);
   return c.used + 256;
 }
 
@@ -704,7 +717,6 @@ mao_status check_soap_hp(const mao_soap_hparams* hp) {
   MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
   if (hp->refresh_every < 0) MAO_FAIL(MAO_E_HPARAM, "refresh_every=%d", hp->refresh_every);
   if (!dtype_ok(hp->back_rot_dtype)) MAO_FAIL(MAO_E_DTYPE, "back_rot_dtype=%d", hp->back_rot_dtype);
-  if (hp->back_rot_dtype == MAO_BF16) MAO_FAIL(MAO_E_UNSUPPORTED, "bf16 back-rotation");
   return MAO_OK;
 }
 
@@ -769,12 +781,31 @@ mao_status soap_post(int stage, const mao_mat& W, const mao_mat& G, const mao_so
     case 4: {
       const float bc1 = (float)(1.0 - pow((double)b1, (double)t));
       const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
+      if (hp->back_rot_dtype == MAO_BF16) {
+        // N and Q_R in bf16, (N Q_R^T)^T stored in bf16 (bf16 MFMA, fp32 accumulation)
+        MAO_TRY(soap_adam(view(R.Gtil, R.ldn), view(R.Mtil, R.ldn), view(st->V.data, st->V.ld),
+                          m, n, b2, bc1, bc2, hp->eps, s, view(R.Nb, R.ldn)));
+        MAO_TRY(scale_cast_transpose(view(st->QR.data, st->QR.ld), n, n, 1, nullptr,
+                                     view(R.QRb, R.ldn), view(nullptr, 0), MAO_BF16, s));
+        GemmProblem p = gemm_problem(m, n, n, 1.f, R.Nb, R.ldn, R.QRb, R.ldn, 0.f, nullptr, 0,
+                                     nullptr, 0, 0);
+        p.Dt = R.T2b;
+        p.lddt = R.ldm;
+        return gemm_add(gb, p, MAO_BF16, s);
+      }
       MAO_TRY(soap_adam(view(R.Gtil, R.ldn), view(R.Mtil, R.ldn), view(st->V.data, st->V.ld), m,
                         n, b2, bc1, bc2, hp->eps, s));
       return nt32(m, n, n, R.Gtil, R.ldn, (const float*)st->QR.data, st->QR.ld, nullptr, 0, R.T2t,
                   R.ldm, s, nullptr, gb);
     }
     case 5:
+      if (hp->back_rot_dtype == MAO_BF16) {
+        MAO_TRY(scale_cast_transpose(view(st->QL.data, st->QL.ld), m, m, 1, nullptr,
+                                     view(R.QLb, R.ldm), view(nullptr, 0), MAO_BF16, s));
+        GemmProblem p = gemm_problem(m, n, m, 1.f, R.QLb, R.ldm, R.T2b, R.ldm, 0.f, nullptr, 0,
+                                     U, ldU, GF_D_F32);
+        return gemm_add(gb, p, MAO_BF16, s);
+      }
       return nt32(m, n, m, (const float*)st->QL.data, st->QL.ld, R.T2t, R.ldm, U, ldU, nullptr, 0,
                   s, nullptr, gb);
     default:
@@ -793,7 +824,6 @@ mao_status check_foam_hp(const mao_foam_hparams* hp) {
   if (hp->refresh != MAO_REFRESH_QR && hp->refresh != MAO_REFRESH_EIGH)
     MAO_FAIL(MAO_E_HPARAM, "refresh=%d must be 0 (QR) or 1 (eigh)", hp->refresh);
   if (!dtype_ok(hp->back_rot_dtype)) MAO_FAIL(MAO_E_DTYPE, "back_rot_dtype=%d", hp->back_rot_dtype);
-  if (hp->back_rot_dtype == MAO_BF16) MAO_FAIL(MAO_E_UNSUPPORTED, "bf16 back-rotation");
   return MAO_OK;
 }
 
@@ -916,19 +946,31 @@ mao_status foam_precondition_back(const mao_mat& W, const mao_foam_state* st, Ro
   const float bc2 = (float)(1.0 - pow((double)b2, (double)t));
   int64_t ldU;
   float* U = foam_u(R, hp, n, update_out, ldU);
-  if (foam_out(hp)) {
-    // the row means of G_rot^T are W's column means (c) and vice versa
-    MAO_TRY(foam_moments(view(R.Gtil, R.ldn), n, m, b2, bc2, (const float*)st->R.data, st->R.ld,
-                         st->c, st->r, work, tau, st->aux, s));
-    MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), n, m, st->c, st->r, tau, bc1, bc2, hp->eps, s));
-    return nt32(n, m, m, R.Mtil, R.ldn, (const float*)st->QR.data, st->QR.ld, nullptr, 0, U, ldU,
-                s, nullptr, gb);
+  const bool bb = hp->back_rot_dtype == MAO_BF16;
+  // problem dimensions: the output side runs the transposed problem (n x m)
+  const bool out = foam_out(hp);
+  const int pm = out ? n : m, pn = out ? m : n;
+  MAO_TRY(foam_moments(view(R.Gtil, R.ldn), pm, pn, b2, bc2, (const float*)st->R.data, st->R.ld,
+                       out ? st->c : st->r, out ? st->r : st->c, work, tau, st->aux, s));
+  MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), pm, pn, out ? st->c : st->r,
+                            out ? st->r : st->c, tau, bc1, bc2, hp->eps, s,
+                            bb ? view(R.Nb, R.ldn) : view(nullptr, 0)));
+  // rotation back U = N Q_R^T (output side: U^T, through the transposed store)
+  GemmProblem p;
+  if (bb) {
+    MAO_TRY(scale_cast_transpose(view(st->QR.data, st->QR.ld), pn, pn, 1, nullptr,
+                                 view(R.QRb, R.ldn), view(nullptr, 0), MAO_BF16, s));
+    p = gemm_problem(pm, pn, pn, 1.f, R.Nb, R.ldn, R.QRb, R.ldn, 0.f, nullptr, 0,
+                     out ? nullptr : U, out ? 0 : ldU, GF_D_F32);
+  } else {
+    p = gemm_problem(pm, pn, pn, 1.f, R.Mtil, R.ldn, st->QR.data, st->QR.ld, 0.f, nullptr, 0,
+                     out ? nullptr : U, out ? 0 : ldU, GF_D_F32);
   }
-  MAO_TRY(foam_moments(view(R.Gtil, R.ldn), m, n, b2, bc2, (const float*)st->R.data, st->R.ld,
-                       st->r, st->c, work, tau, st->aux, s));
-  MAO_TRY(foam_precondition(view(R.Mtil, R.ldn), m, n, st->r, st->c, tau, bc1, bc2, hp->eps, s));
-  return nt32(m, n, n, R.Mtil, R.ldn, (const float*)st->QR.data, st->QR.ld, U, ldU, nullptr, 0, s,
-              nullptr, gb);
+  if (out) {
+    p.Dt = U;
+    p.lddt = ldU;
+  }
+  return gemm_add(gb, p, bb ? MAO_BF16 : MAO_F32, s);
 }
 
 mao_status foam_update(const mao_mat& W, RotBufs& R, const mao_foam_hparams* hp,
@@ -967,13 +1009,13 @@ struct QrGroup {
 // products per matrix in a phase, five pointers each).
 void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<RotBufs>& R,
                 std::vector<QrGroup>& groups, bool fout = false, GemmBatch* gb = nullptr,
-                bool eigh = false) {
+                bool eigh = false, bool back_bf16 = false) {
   R.assign(count, RotBufs{});
   std::vector<std::pair<int, QrJobRef>> all;
   for (int i = 0; i < count; ++i) {
     const int m = (int)W[i].rows, n = (int)W[i].cols;
     const bool t = !soap && fout;
-    carve_rot(c, t ? n : m, t ? m : n, soap, true, R[i], false);
+    carve_rot(c, t ? n : m, t ? m : n, soap, true, R[i], false, false, back_bf16);
     if (soap) all.push_back({m, QrJobRef{i, 0}});
     all.push_back({t ? m : n, QrJobRef{i, 1}});
   }
@@ -1020,11 +1062,12 @@ void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<R
   }
 }
 
-size_t many_ws(int count, const mao_mat* W, bool soap, bool fout = false, bool eigh = false) {
+size_t many_ws(int count, const mao_mat* W, bool soap, bool fout = false, bool eigh = false,
+               bool back_bf16 = false) {
   Carver c(nullptr);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
-  carve_many(c, count, W, soap, R, groups, fout, nullptr, eigh);
+  carve_many(c, count, W, soap, R, groups, fout, nullptr, eigh, back_bf16);
   return c.used + 256;
 }
 
@@ -1055,7 +1098,7 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
   MAO_TRY(check_workspace(workspace, workspace_bytes, soap_workspace_size(m, n, hp)));
   Carver c(workspace);
   RotBufs R;
-  carve_rot(c, m, n, true, true, R);
+  carve_rot(c, m, n, true, true, R, true, false, hp->back_rot_dtype == MAO_BF16);
   MAO_TRY(soap_pre(W, G, st, R, hp, nullptr, s));
   // 3b. refresh: Q <- qr(F Q); S = (F Q)^T = Q^T F stored row-major
   if (soap_refresh(hp, t)) {
@@ -1074,7 +1117,7 @@ size_t soap_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_
   if (!hp || !W || count < 1 || count > kMaxMany) return 0;
   for (int i = 0; i < count; ++i)
     if (W[i].rows < 1 || W[i].cols < 1) return 0;
-  return many_ws(count, W, true);
+  return many_ws(count, W, true, false, false, hp->back_rot_dtype == MAO_BF16);
 }
 
 mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
@@ -1088,12 +1131,13 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   for (int i = 0; i < count; ++i)
     MAO_TRY(validate_soap(W[i], G[i], &st[i], t, update_out ? update_out[i] : nullptr, rr));
   MAO_TRY(check_no_overlap(rr));
-  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, true)));
+  const bool bb = hp->back_rot_dtype == MAO_BF16;
+  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, true, false, false, bb)));
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
   GemmBatch gb;
-  carve_many(c, count, W, true, R, groups, false, &gb);
+  carve_many(c, count, W, true, R, groups, false, &gb, false, bb);
   for (int i = 0; i < count; ++i) MAO_TRY(soap_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
   MAO_TRY(gemm_flush(gb, s));
   if (soap_refresh(hp, t)) {
@@ -1149,7 +1193,7 @@ size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hparams* h
   RotBufs R;
   const bool out = foam_out(hp);
   carve_rot(c, (int)(out ? cols : rows), (int)(out ? rows : cols), false, true, R, true,
-            foam_eigh(hp));
+            foam_eigh(hp), hp->back_rot_dtype == MAO_BF16);
   return c.used + 256;
 }
 
@@ -1167,7 +1211,8 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
   MAO_TRY(check_workspace(workspace, workspace_bytes, foam_workspace_size(m, n, hp)));
   Carver c(workspace);
   RotBufs R;
-  carve_rot(c, out ? n : m, out ? m : n, false, true, R, true, foam_eigh(hp));
+  carve_rot(c, out ? n : m, out ? m : n, false, true, R, true, foam_eigh(hp),
+            hp->back_rot_dtype == MAO_BF16);
   MAO_TRY(foam_pre(W, G, st, R, hp, nullptr, s));
   for (int stage = 0; stage < 3; ++stage)
     MAO_TRY(foam_criterion(k, st, R, t, hp, stage, nullptr, s));
@@ -1201,7 +1246,7 @@ size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_
     if (W[i].rows < 1 || W[i].cols < 1) return 0;
     if (foam_eigh(hp) && (foam_out(hp) ? W[i].rows : W[i].cols) > kEighMaxN) return 0;
   }
-  return many_ws(count, W, false, foam_out(hp), foam_eigh(hp));
+  return many_ws(count, W, false, foam_out(hp), foam_eigh(hp), hp->back_rot_dtype == MAO_BF16);
 }
 
 mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
@@ -1215,13 +1260,14 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   for (int i = 0; i < count; ++i)
     MAO_TRY(validate_foam(W[i], G[i], &st[i], t, hp, update_out ? update_out[i] : nullptr, rr));
   MAO_TRY(check_no_overlap(rr));
+  const bool bb = hp->back_rot_dtype == MAO_BF16;
   MAO_TRY(check_workspace(workspace, workspace_bytes,
-                          many_ws(count, W, false, foam_out(hp), foam_eigh(hp))));
+                          many_ws(count, W, false, foam_out(hp), foam_eigh(hp), bb)));
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
   GemmBatch gb;
-  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb, foam_eigh(hp));
+  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb, foam_eigh(hp), bb);
   // phases: every matrix's products of a phase go out as grouped launches
   for (int i = 0; i < count; ++i) MAO_TRY(foam_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
   MAO_TRY(gemm_flush(gb, s));

@@ -29,8 +29,8 @@
 // - J^T J) / 2 (the fp32 rotations that built it leave it off orthogonality
 // by far more than rounding). After each sweep the off-diagonal ratio
 // ||D - diag D||_F / ||D||_F is reduced on the device; a job whose sweep
-// rotated nothing, whose ratio fell under 1e-6, or whose ratio a sweep no
-// longer halved (the fp32 floor) is marked converged and every later kernel
+// rotated nothing, whose ratio reached the fp32 floor 8 u sqrt(kp), or whose
+// ratio a sweep no longer halved is marked converged and every later kernel
 // of that job returns at once (no host synchronisation). Finally the eigenvalues
 // (diag D) are sorted descending (ties by index) and Q's columns gathered in
 // that order, also transposed into E.
@@ -55,7 +55,7 @@ namespace {
 constexpr int EB = 64;     // block width
 constexpr int PB = 128;    // pair (two blocks)
 constexpr int LDX = 129;   // LDS row stride of 128 x 128 tiles (conflict-free columns)
-constexpr int kInnerMaxSweeps = 16;
+constexpr int kInnerMaxSweeps = 4;  // inexact inner solves: the outer sweeps converge regardless
 constexpr int kTableJobs = 16;
 
 struct EW {
@@ -164,83 +164,87 @@ __global__ __launch_bounds__(256) void eigh_init_kernel(EW w, InitTable t) {
 // 128 x 128 x 128 fp32 MFMA products out of LDS
 // ---------------------------------------------------------------------------
 
-// acc = Aop^T Bop over K = 128 for this wave's 64 x 64 quadrant: out[x][c] =
-// sum_k Aop[k][x] Bop[k][c] (both 128 x 128 in LDS, stride LDX).
-__device__ __forceinline__ void mm128(const float* Aop, const float* Bop, f32x16_t acc[2][2]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, r32 = lane & 31;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
-#pragma unroll 4
-  for (int kk = 0; kk < PB / 2; ++kk) {
-    const int k = 2 * kk + h;
-    const float a0 = Aop[k * LDX + wm * 64 + r32];
-    const float a1 = Aop[k * LDX + wm * 64 + 32 + r32];
-    const float b0 = Bop[k * LDX + wn * 64 + r32];
-    const float b1 = Bop[k * LDX + wn * 64 + 32 + r32];
-    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
-  }
-}
+// The waves of a workgroup tile the 128 x 128 result WM x WN; each wave owns
+// (128 / WM) x (128 / WN) as TM x TN 32 x 32 MFMA blocks.
+template <int WM, int WN>
+struct MM {
+  static constexpr int TM = 128 / WM / 32, TN = 128 / WN / 32;
+  typedef f32x16_t Acc[TM][TN];
 
-// acc -> LDS tile (row-major, stride LDX)
-__device__ __forceinline__ void acc_to_lds(const f32x16_t acc[2][2], float* out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, r32 = lane & 31;
+  // out[x][c] = sum_k a(k, x) B[k][c] with a(k, x) = A[x][k] (ROWS) or A[k][x]
+  template <bool ROWS>
+  static __device__ __forceinline__ void run(const float* A, const float* B, Acc& acc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int h = lane >> 5, r32 = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < TN; ++jj)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        const int col = wn * 64 + jj * 32 + r32;
-        out[row * LDX + col] = acc[i][jj][v];
+        for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+#pragma unroll 4
+    for (int kk = 0; kk < PB / 2; ++kk) {
+      const int k = 2 * kk + h;
+      float a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int x = wm * (128 / WM) + i * 32 + r32;
+        a[i] = ROWS ? A[x * LDX + k] : A[k * LDX + x];
       }
-}
-
-// acc = A Bop for a row-major A: out[x][c] = sum_k A[x][k] Bop[k][c]
-__device__ __forceinline__ void mm128_rows(const float* A, const float* Bop, f32x16_t acc[2][2]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, r32 = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int jj = 0; jj < TN; ++jj) b[jj] = B[k * LDX + wn * (128 / WN) + jj * 32 + r32];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
-#pragma unroll 4
-  for (int kk = 0; kk < PB / 2; ++kk) {
-    const int k = 2 * kk + h;
-    const float a0 = A[(wm * 64 + r32) * LDX + k];
-    const float a1 = A[(wm * 64 + 32 + r32) * LDX + k];
-    const float b0 = Bop[k * LDX + wn * 64 + r32];
-    const float b1 = Bop[k * LDX + wn * 64 + 32 + r32];
-    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        for (int jj = 0; jj < TN; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[jj], acc[i][jj], 0, 0, 0);
+    }
   }
-}
 
+  // element (row, col) held by accumulator register v of block (i, jj)
+  static __device__ __forceinline__ void at(int i, int jj, int v, int& row, int& col) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    row = wm * (128 / WM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    col = wn * (128 / WN) + jj * 32 + (lane & 31);
+  }
+
+  static __device__ __forceinline__ void to_lds(const Acc& acc, float* out) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int row, col;
+          at(i, jj, v, row, col);
+          out[row * LDX + col] = acc[i][jj][v];
+        }
+  }
+};
+
+// a dense 128 x 128 block (ld 128) into LDS, 16-byte loads
+template <int NT>
 __device__ __forceinline__ void load_j(const float* Jsrc, float* dst) {
-  for (int e = threadIdx.x; e < PB * PB; e += 256) dst[(e >> 7) * LDX + (e & 127)] = Jsrc[e];
+  for (int e = threadIdx.x; e < PB * PB / 4; e += NT) {
+    const float4 v = *(const float4*)(Jsrc + 4 * e);
+    float* d = dst + (e >> 5) * LDX + (e & 31) * 4;
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // pair kernel: diagonalise the 128 x 128 subproblem of each pair
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void eigh_pair_kernel(EW w, int r) {
+constexpr int kPairThreads = 1024;  // 16 waves: LDS latency of the rotation steps hidden
+typedef MM<4, 4> MMP;
+
+__global__ __launch_bounds__(kPairThreads) void eigh_pair_kernel(EW w, int r) {
   const int j = blockIdx.y;
   if (job_off(w, j)) return;
   JobP p = job_ptrs(w, j);
@@ -249,23 +253,58 @@ __global__ __launch_bounds__(256) void eigh_pair_kernel(EW w, int r) {
   __shared__ float Jm[PB * LDX];
   __shared__ int pi_[64], pj_[64];
   __shared__ float pc_[64], ps_[64], pt_[64];
-  __shared__ float red[4];
   __shared__ int rot_flag;
 
   const int tid = threadIdx.x;
   const PairMap pm = pair_map(blockIdx.x, r, w.nblk);
-  for (int e = tid; e < PB * PB; e += 256) {
-    const int x = e >> 7, y = e & 127;
-    A[x * LDX + y] = p.D[(int64_t)pm.g(x) * w.ldp + pm.g(y)];
-    Jm[x * LDX + y] = (x == y) ? 1.f : 0.f;
+  for (int e = tid; e < PB * PB / 4; e += kPairThreads) {
+    const int x = e >> 5, y = (e & 31) * 4;
+    const float4 v = *(const float4*)(p.D + (int64_t)pm.g(x) * w.ldp + pm.g(y));
+    float* a = A + x * LDX + y;
+    a[0] = v.x;
+    a[1] = v.y;
+    a[2] = v.z;
+    a[3] = v.w;
+    float* jr = Jm + x * LDX + y;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) jr[u] = (x == y + u) ? 1.f : 0.f;
   }
-  __syncthreads();
-  float v = tid < PB ? fabsf(A[tid * (LDX + 1)]) : 0.f;
-  v = wave_max(v);
-  if ((tid & 63) == 0) red[tid >> 6] = v;
-  __syncthreads();
-  const float scale = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // Rounding that the fp32 products leave in an entry of D follows the
+  // magnitudes in its rows and columns: a rotation is skipped below 4 u of
+  // the subproblem's largest diagonal entry as well as below 4 u of
+  // sqrt(|a d|).
+  __shared__ float red[16];
+  {
+    __syncthreads();
+    float v = tid < PB ? fabsf(A[tid * (LDX + 1)]) : 0.f;
+    v = wave_max(v);
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+  }
+  float scale = 0.f;
+#pragma unroll
+  for (int u = 0; u < kPairThreads / 64; ++u) scale = fmaxf(scale, red[u]);
   const float tau_abs = 4.f * 0x1p-24f * scale;
+  // the quads (P, Q <= P) and J column pairs this thread updates, fixed for
+  // every step (they name pair slots, not indices)
+  constexpr int kQuads = 64 * 65 / 2;
+  constexpr int kMyQuads = (kQuads + kPairThreads - 1) / kPairThreads;
+  int myP[kMyQuads], myQ[kMyQuads];
+#pragma unroll
+  for (int u = 0; u < kMyQuads; ++u) {
+    const int q = tid + u * kPairThreads;
+    int P = -1, Q = 0;
+    if (q < kQuads) {
+      P = (int)((sqrtf(8.f * (float)q + 1.f) - 1.f) * 0.5f);
+      while (P * (P + 1) / 2 > q) --P;
+      while ((P + 1) * (P + 2) / 2 <= q) ++P;
+      Q = q - P * (P + 1) / 2;
+    }
+    myP[u] = P;
+    myQ[u] = Q;
+  }
+  const int jq = tid & 63;  // J column pair; rows (tid >> 6) + 16 i
+  __syncthreads();
 
   bool rotated_any = false;
   for (int sw = 0; sw < kInnerMaxSweeps; ++sw) {
@@ -295,11 +334,10 @@ __global__ __launch_bounds__(256) void eigh_pair_kernel(EW w, int r) {
       __syncthreads();
       // D[I, I] <- R^T D R, one 2 x 2 quad of rows {i_P, j_P} x columns
       // {i_Q, j_Q} per (P, Q) with Q <= P, written with its mirror
-      for (int q = tid; q < 64 * 65 / 2; q += 256) {
-        int P = (int)((sqrtf(8.f * (float)q + 1.f) - 1.f) * 0.5f);
-        while (P * (P + 1) / 2 > q) --P;
-        while ((P + 1) * (P + 2) / 2 <= q) ++P;
-        const int Q = q - P * (P + 1) / 2;
+#pragma unroll
+      for (int u = 0; u < kMyQuads; ++u) {
+        const int P = myP[u], Q = myQ[u];
+        if (P < 0) continue;
         const int iP = pi_[P], jP = pj_[P];
         const float sP = ps_[P];
         if (P == Q) {
@@ -333,15 +371,19 @@ __global__ __launch_bounds__(256) void eigh_pair_kernel(EW w, int r) {
         A[jQ * LDX + jP] = n11;
       }
       // J <- J R
-      for (int e = tid; e < PB * 64; e += 256) {
-        const int u = e >> 6, Q = e & 63;
-        const float sQ = ps_[Q];
-        if (sQ == 0.f) continue;
-        const float cQ = pc_[Q];
-        const int iQ = pi_[Q], jQ = pj_[Q];
-        const float x0 = Jm[u * LDX + iQ], x1 = Jm[u * LDX + jQ];
-        Jm[u * LDX + iQ] = cQ * x0 - sQ * x1;
-        Jm[u * LDX + jQ] = sQ * x0 + cQ * x1;
+      {
+        const float sQ = ps_[jq];
+        if (sQ != 0.f) {
+          const float cQ = pc_[jq];
+          const int iQ = pi_[jq], jQ = pj_[jq];
+#pragma unroll
+          for (int u0 = 0; u0 < PB; u0 += kPairThreads / 64) {
+            const int u = u0 + (tid >> 6);
+            const float x0 = Jm[u * LDX + iQ], x1 = Jm[u * LDX + jQ];
+            Jm[u * LDX + iQ] = cQ * x0 - sQ * x1;
+            Jm[u * LDX + jQ] = sQ * x0 + cQ * x1;
+          }
+        }
       }
       __syncthreads();
     }
@@ -351,58 +393,58 @@ __global__ __launch_bounds__(256) void eigh_pair_kernel(EW w, int r) {
     rotated_any = true;
   }
   if (rotated_any && tid == 0) atomicOr(p.ctrl + 1, 1);
-  // J from thousands of fp32 rotations drifts from orthogonality (each
+  // J from hundreds of fp32 rotations drifts from orthogonality (each
   // rotation's rounding nudges the column norms the same way); one
   // Newton-Schulz step J <- J (3I - J^T J) / 2 squares that error away. The
   // rotated block in LDS belongs to the unpolished J, so the block is
   // recomputed from the original as J^T D[I, I] J with the polished J: every
   // part of D then moves by the same orthogonal map.
-  f32x16_t acc[2][2];
-  mm128(Jm, Jm, acc);  // J^T J
+  MMP::Acc acc;
+  MMP::run<false>(Jm, Jm, acc);  // J^T J
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        const int col = wn * 64 + jj * 32 + r32;
-        A[row * LDX + col] = (row == col ? 1.5f : 0.f) - 0.5f * acc[i][jj][v];
-      }
+  for (int v = 0; v < 16; ++v) {
+    int row, col;
+    MMP::at(0, 0, v, row, col);
+    A[row * LDX + col] = (row == col ? 1.5f : 0.f) - 0.5f * acc[0][0][v];
+  }
   __syncthreads();
-  mm128_rows(Jm, A, acc);  // J (3I - J^T J) / 2
+  MMP::run<true>(Jm, A, acc);  // J (3I - J^T J) / 2
   __syncthreads();
   float* Jout = p.J + (int64_t)blockIdx.x * PB * PB;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        const int col = wn * 64 + jj * 32 + r32;
-        Jout[row * PB + col] = acc[i][jj][v];
-        Jm[row * LDX + col] = acc[i][jj][v];
-      }
-  for (int e = tid; e < PB * PB; e += 256) {
-    const int x = e >> 7, y = e & 127;
-    A[x * LDX + y] = p.D[(int64_t)pm.g(x) * w.ldp + pm.g(y)];
+  for (int v = 0; v < 16; ++v) {
+    int row, col;
+    MMP::at(0, 0, v, row, col);
+    Jout[row * PB + col] = acc[0][0][v];
+    Jm[row * LDX + col] = acc[0][0][v];
+  }
+  for (int e = tid; e < PB * PB / 4; e += kPairThreads) {
+    const int x = e >> 5, y = (e & 31) * 4;
+    const float4 v = *(const float4*)(p.D + (int64_t)pm.g(x) * w.ldp + pm.g(y));
+    float* a = A + x * LDX + y;
+    a[0] = v.x;
+    a[1] = v.y;
+    a[2] = v.z;
+    a[3] = v.w;
   }
   __syncthreads();
-  mm128(A, Jm, acc);  // D J (D symmetric)
+  MMP::run<false>(A, Jm, acc);  // D J (D symmetric)
   __syncthreads();
-  acc_to_lds(acc, A);
+  MMP::to_lds(acc, A);
   __syncthreads();
-  mm128(Jm, A, acc);  // J^T D J
+  MMP::run<false>(Jm, A, acc);  // J^T D J
   __syncthreads();
-  acc_to_lds(acc, A);
+  MMP::to_lds(acc, A);
   __syncthreads();
-  for (int e = tid; e < PB * PB; e += 256) {
-    const int x = e >> 7, y = e & 127;
-    p.D[(int64_t)pm.g(x) * w.ldp + pm.g(y)] = 0.5f * (A[x * LDX + y] + A[y * LDX + x]);
+  for (int e = tid; e < PB * PB / 4; e += kPairThreads) {
+    const int x = e >> 5, y = (e & 31) * 4;
+    float4 v;
+    v.x = 0.5f * (A[x * LDX + y] + A[y * LDX + x]);
+    v.y = 0.5f * (A[x * LDX + y + 1] + A[(y + 1) * LDX + x]);
+    v.z = 0.5f * (A[x * LDX + y + 2] + A[(y + 2) * LDX + x]);
+    v.w = 0.5f * (A[x * LDX + y + 3] + A[(y + 3) * LDX + x]);
+    *(float4*)(p.D + (int64_t)pm.g(x) * w.ldp + pm.g(y)) = v;
   }
 }
 
@@ -410,7 +452,10 @@ __global__ __launch_bounds__(256) void eigh_pair_kernel(EW w, int r) {
 // apply kernel: off-diagonal pair blocks of D, and strips of Q
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void eigh_apply_kernel(EW w, int r) {
+constexpr int kApplyThreads = 512;
+typedef MM<4, 2> MMA;
+
+__global__ __launch_bounds__(kApplyThreads) void eigh_apply_kernel(EW w, int r) {
   const int j = blockIdx.y;
   if (job_off(w, j)) return;
   JobP p = job_ptrs(w, j);
@@ -421,7 +466,8 @@ __global__ __launch_bounds__(256) void eigh_apply_kernel(EW w, int r) {
   const int nD = npairs * (npairs - 1) / 2;
   const int bid = blockIdx.x;
   const int64_t ldp = w.ldp;
-  f32x16_t acc[2][2];
+  const int tid = threadIdx.x;
+  MMA::Acc acc;
   if (bid < nD) {
     // (P, Qp) with P < Qp: bid = Qp (Qp - 1) / 2 + P
     int Qp = (int)((1.f + sqrtf(1.f + 8.f * (float)bid)) * 0.5f);
@@ -430,28 +476,36 @@ __global__ __launch_bounds__(256) void eigh_apply_kernel(EW w, int r) {
     const int P = bid - Qp * (Qp - 1) / 2;
     const PairMap mp = pair_map(P, r, w.nblk), mq = pair_map(Qp, r, w.nblk);
     // X[k][x] = D[I_Q k][I_P x] = D[I_P x][I_Q k] (D symmetric)
-    for (int e = threadIdx.x; e < PB * PB; e += 256) {
-      const int k = e >> 7, x = e & 127;
-      X[k * LDX + x] = p.D[(int64_t)mq.g(k) * ldp + mp.g(x)];
+    for (int e = tid; e < PB * PB / 4; e += kApplyThreads) {
+      const int k = e >> 5, x = (e & 31) * 4;
+      const float4 v = *(const float4*)(p.D + (int64_t)mq.g(k) * ldp + mp.g(x));
+      float* d = X + k * LDX + x;
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
     }
-    load_j(p.J + (int64_t)Qp * PB * PB, Jb);
+    load_j<kApplyThreads>(p.J + (int64_t)Qp * PB * PB, Jb);
     __syncthreads();
-    mm128(X, Jb, acc);  // T = D[I_P, I_Q] J_Q
+    MMA::run<false>(X, Jb, acc);  // T = D[I_P, I_Q] J_Q
     __syncthreads();
-    acc_to_lds(acc, X);
-    load_j(p.J + (int64_t)P * PB * PB, Jb);
+    MMA::to_lds(acc, X);
+    load_j<kApplyThreads>(p.J + (int64_t)P * PB * PB, Jb);
     __syncthreads();
-    mm128(Jb, X, acc);  // J_P^T T
+    MMA::run<false>(Jb, X, acc);  // J_P^T T
     __syncthreads();
-    acc_to_lds(acc, X);
+    MMA::to_lds(acc, X);
     __syncthreads();
-    for (int e = threadIdx.x; e < PB * PB; e += 256) {
-      const int x = e >> 7, c = e & 127;
-      p.D[(int64_t)mp.g(x) * ldp + mq.g(c)] = X[x * LDX + c];
+    for (int e = tid; e < PB * PB / 4; e += kApplyThreads) {
+      const int x = e >> 5, c = (e & 31) * 4;
+      const float* s0 = X + x * LDX + c;
+      *(float4*)(p.D + (int64_t)mp.g(x) * ldp + mq.g(c)) = make_float4(s0[0], s0[1], s0[2], s0[3]);
     }
-    for (int e = threadIdx.x; e < PB * PB; e += 256) {
-      const int c = e >> 7, x = e & 127;
-      p.D[(int64_t)mq.g(c) * ldp + mp.g(x)] = X[x * LDX + c];
+    for (int e = tid; e < PB * PB / 4; e += kApplyThreads) {
+      const int c = e >> 5, x = (e & 31) * 4;
+      *(float4*)(p.D + (int64_t)mq.g(c) * ldp + mp.g(x)) =
+          make_float4(X[x * LDX + c], X[(x + 1) * LDX + c], X[(x + 2) * LDX + c],
+                      X[(x + 3) * LDX + c]);
     }
   } else {
     const int b2 = bid - nD;
@@ -459,19 +513,24 @@ __global__ __launch_bounds__(256) void eigh_apply_kernel(EW w, int r) {
     const int64_t u0 = (int64_t)ub * PB;
     const PairMap mp = pair_map(P, r, w.nblk);
     // X[k][x] = Q[u0 + x][I_P k]
-    for (int e = threadIdx.x; e < PB * PB; e += 256) {
-      const int x = e >> 7, k = e & 127;
-      X[k * LDX + x] = p.Q[(u0 + x) * ldp + mp.g(k)];
+    for (int e = tid; e < PB * PB / 4; e += kApplyThreads) {
+      const int x = e >> 5, k = (e & 31) * 4;
+      const float4 v = *(const float4*)(p.Q + (u0 + x) * ldp + mp.g(k));
+      X[k * LDX + x] = v.x;
+      X[(k + 1) * LDX + x] = v.y;
+      X[(k + 2) * LDX + x] = v.z;
+      X[(k + 3) * LDX + x] = v.w;
     }
-    load_j(p.J + (int64_t)P * PB * PB, Jb);
+    load_j<kApplyThreads>(p.J + (int64_t)P * PB * PB, Jb);
     __syncthreads();
-    mm128(X, Jb, acc);  // Q[strip, I_P] J_P
+    MMA::run<false>(X, Jb, acc);  // Q[strip, I_P] J_P
     __syncthreads();
-    acc_to_lds(acc, X);
+    MMA::to_lds(acc, X);
     __syncthreads();
-    for (int e = threadIdx.x; e < PB * PB; e += 256) {
-      const int x = e >> 7, c = e & 127;
-      p.Q[(u0 + x) * ldp + mp.g(c)] = X[x * LDX + c];
+    for (int e = tid; e < PB * PB / 4; e += kApplyThreads) {
+      const int x = e >> 5, c = (e & 31) * 4;
+      const float* s0 = X + x * LDX + c;
+      *(float4*)(p.Q + (u0 + x) * ldp + mp.g(c)) = make_float4(s0[0], s0[1], s0[2], s0[3]);
     }
   }
 }
@@ -524,9 +583,10 @@ __global__ __launch_bounds__(64) void eigh_conv_final_kernel(EW w, int sweep) {
     const bool rotated = p.ctrl[1] != 0;
     const float prev = __int_as_float(p.ctrl[3]);
     p.ctrl[2] = sweep + 1;
-    // converged: nothing rotated, the ratio is at fp32 level, or a sweep no
-    // longer halved it (rounding floor reached)
-    if (!rotated || rho <= 1e-6 || (sweep > 0 && rho > 0.5 * (double)prev)) p.ctrl[0] = 1;
+    // converged: nothing rotated, the ratio is at the fp32 floor
+    // (8 u sqrt(kp)), or a sweep no longer halved it
+    const double floor32 = 8.0 * 0x1p-24 * sqrt((double)w.kp);
+    if (!rotated || rho <= floor32 || (sweep > 0 && rho > 0.5 * (double)prev)) p.ctrl[0] = 1;
     p.ctrl[1] = 0;
     p.ctrl[3] = __float_as_int((float)rho);
     if (info) {
@@ -705,8 +765,9 @@ mao_status eigh_batched(const EighBatch& b, hipStream_t stream) {
   const int nQ = (int)ceil_div(n, PB) * npairs;
   for (int sweep = 0; sweep < kEighMaxSweeps; ++sweep) {
     for (int r = 0; r < w.nblk - 1; ++r) {
-      hipLaunchKernelGGL(eigh_pair_kernel, dim3(npairs, nj), dim3(256), 0, stream, w, r);
-      hipLaunchKernelGGL(eigh_apply_kernel, dim3(nD + nQ, nj), dim3(256), 0, stream, w, r);
+      hipLaunchKernelGGL(eigh_pair_kernel, dim3(npairs, nj), dim3(kPairThreads), 0, stream, w, r);
+      hipLaunchKernelGGL(eigh_apply_kernel, dim3(nD + nQ, nj), dim3(kApplyThreads), 0, stream, w,
+                         r);
     }
     hipLaunchKernelGGL(eigh_conv_partial_kernel, dim3(w.kp / 64, nj), dim3(256), 0, stream, w);
     hipLaunchKernelGGL(eigh_conv_final_kernel, dim3(nj), dim3(64), 0, stream, w, sweep);

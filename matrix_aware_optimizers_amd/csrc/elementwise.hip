@@ -367,9 +367,12 @@ __global__ __launch_bounds__(kBlock) void update_kernel(View W, View O, int rows
   }
 }
 
-__global__ __launch_bounds__(kBlock) void soap_adam_kernel(View Gt, View Mt, View V, int rows,
-                                                           int cols, float beta2, float bc1,
-                                                           float bc2, float eps, int nrb) {
+// N goes over Gt (TN = float) or to a separate bf16 copy (TN = bf16_t).
+template <typename TN>
+__global__ __launch_bounds__(kBlock) void soap_adam_kernel(View Gt, View Mt, View V, View Nout,
+                                                           int rows, int cols, float beta2,
+                                                           float bc1, float bc2, float eps,
+                                                           int nrb) {
   const Chunks ch = block_chunks(rows, cols, nrb);
   const float ob = 1.f - beta2, ib1 = 1.f / bc1, ib2 = 1.f / bc2;
 #pragma unroll 2
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(kBlock) void soap_adam_kernel(View Gt, View Mt, Vie
     int i, j;
     ch.at(q, i, j);
     float g[8], m[8], v[8];
-    float* grow = (float*)Gt.p + (int64_t)i * Gt.ld;
+    const float* grow = (const float*)Gt.p + (int64_t)i * Gt.ld;
     float* vrow = (float*)V.p + (int64_t)i * V.ld;
     load8<float>(grow, j, cols, g);
     load8<float>((const float*)Mt.p + (int64_t)i * Mt.ld, j, cols, m);
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(kBlock) void soap_adam_kernel(View Gt, View Mt, Vie
       g[e] = (m[e] * ib1) / (sqrtf(v[e] * ib2) + eps);
     }
     store8<float>(vrow, j, cols, v);
-    store8<float>(grow, j, cols, g);
+    store8<TN>((TN*)Nout.p + (int64_t)i * Nout.ld, j, cols, g);
   }
 }
 
@@ -483,7 +486,8 @@ __global__ __launch_bounds__(64) void foam_tau_kernel(const float* bp, int nbr, 
   if (aux) aux[2] = tau;
 }
 
-__global__ __launch_bounds__(kBlock) void foam_precond_kernel(View Mr, int m, int n,
+template <typename TN>
+__global__ __launch_bounds__(kBlock) void foam_precond_kernel(View Mr, View Nout, int m, int n,
                                                               const float* r, const float* c,
                                                               const float* tau, float bc1,
                                                               float bc2, float eps, int nrb) {
@@ -502,7 +506,7 @@ __global__ __launch_bounds__(kBlock) void foam_precond_kernel(View Mr, int m, in
       const float cj = (j + e < n) ? c[j + e] * ib2 : 0.f;
       x[e] = (x[e] * ib1) / (sqrtf(t * ri * cj) + eps);
     }
-    store8<float>(row, j, n, x);
+    store8<TN>((TN*)Nout.p + (int64_t)i * Nout.ld, j, n, x);
   }
 }
 
@@ -716,9 +720,12 @@ mao_status apply_update(View W, int w_dtype, View O, int o_dtype, int rows, int 
 }
 
 mao_status soap_adam(View Gt, View Mt, View V, int rows, int cols, float beta2, float bc1,
-                     float bc2, float eps, hipStream_t s) {
+                     float bc2, float eps, hipStream_t s, View Nb) {
   const int nrb = rowblocks_for(rows, 1);
-  hipLaunchKernelGGL(soap_adam_kernel, dim3(nrb), dim3(kBlock), 0, s, Gt, Mt, V, rows, cols, beta2, bc1, bc2, eps, nrb);
+  if (Nb.p != nullptr)
+    hipLaunchKernelGGL(soap_adam_kernel<bf16_t>, dim3(nrb), dim3(kBlock), 0, s, Gt, Mt, V, Nb, rows, cols, beta2, bc1, bc2, eps, nrb);
+  else
+    hipLaunchKernelGGL(soap_adam_kernel<float>, dim3(nrb), dim3(kBlock), 0, s, Gt, Mt, V, Gt, rows, cols, beta2, bc1, bc2, eps, nrb);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }
@@ -761,9 +768,13 @@ int64_t foam_moments_work_floats(int m, int n) {
 }
 
 mao_status foam_precondition(View Mr, int m, int n, const float* r, const float* c,
-                             const float* tau, float bc1, float bc2, float eps, hipStream_t s) {
+                             const float* tau, float bc1, float bc2, float eps, hipStream_t s,
+                             View Nb) {
   const int nrb = rowblocks_for(m, 1);
-  hipLaunchKernelGGL(foam_precond_kernel, dim3(nrb), dim3(kBlock), 0, s, Mr, m, n, r, c, tau, bc1, bc2, eps, nrb);
+  if (Nb.p != nullptr)
+    hipLaunchKernelGGL(foam_precond_kernel<bf16_t>, dim3(nrb), dim3(kBlock), 0, s, Mr, Nb, m, n, r, c, tau, bc1, bc2, eps, nrb);
+  else
+    hipLaunchKernelGGL(foam_precond_kernel<float>, dim3(nrb), dim3(kBlock), 0, s, Mr, Mr, m, n, r, c, tau, bc1, bc2, eps, nrb);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }

@@ -64,9 +64,10 @@ mao_status apply_update(View W, int w_dtype, View O, int o_dtype, int rows, int 
                         hipStream_t st);
 
 // SOAP Adam in the rotated space: V <- b2 V + (1-b2) Gt^2;
-// N = (Mt / bc1) / (sqrt(V / bc2) + eps), written over Gt.
+// N = (Mt / bc1) / (sqrt(V / bc2) + eps), written over Gt, or in bf16 to Nb
+// when Nb.p is set (Gt then unchanged).
 mao_status soap_adam(View Gt, View Mt, View V, int rows, int cols, float beta2, float bc1,
-                     float bc2, float eps, hipStream_t s);
+                     float bc2, float eps, hipStream_t s, View Nb = View{nullptr, 0, 0});
 
 // E <- I (n x n fp32); skipped when pred != nullptr and *pred == 0.
 mao_status fill_identity(View E, int n, const int* pred, hipStream_t s);
@@ -82,9 +83,11 @@ mao_status foam_moments(View Gr, int m, int n, float beta2, float bc2, const flo
                         int64_t ldR, float* r, float* c, float* work, float* tau_out,
                         float* aux, hipStream_t s);
 
-// N = (Mr / bc1) / (sqrt(tau * r_i/bc2 * c_j/bc2) + eps), written over Mr.
+// N = (Mr / bc1) / (sqrt(tau * r_i/bc2 * c_j/bc2) + eps), written over Mr, or in
+// bf16 to Nb when Nb.p is set.
 mao_status foam_precondition(View Mr, int m, int n, const float* r, const float* c,
-                             const float* tau, float bc1, float bc2, float eps, hipStream_t s);
+                             const float* tau, float bc1, float bc2, float eps, hipStream_t s,
+                             View Nb = View{nullptr, 0, 0});
 
 // FOAM refresh criterion on D (n x n): rho = ||offdiag||_F / ||D||_F, flag =
 // rho > tol. Writes aux[0] = rho, aux[1] = flag, aux[3] = 1 and *flag_out.

@@ -343,3 +343,32 @@ def test_soap8b_many_gate_refresh_from_a_moved_basis(soap8b_many_run):
                 assert prod[a, b] > 0
     del L2
     torch.cuda.empty_cache()
+
+
+def test_soap8b_many_bf16_back_rotation(gpu_lib):
+    """The benchmark's SOAP configuration of the 8B layer: soap_step_many with
+    the rotation back on bf16 MFMA. O and QKV stepped together to t = 4
+    (their first gated step), teacher-forced there: update within the bf16
+    tolerance (whole matrix and per 256 x 256 tile), V to 1e-4."""
+    import torch
+    log("soap 8B layer O + QKV, bf16 back rotation, 4 steps")
+    specs = [s for s in synth.specs("c3") if s.name in ("o", "qkv")]
+    Ws = [to_dev(bf16_round(synth.init_weight("c3", sp)), "bf16") for sp in specs]
+    sts = [_soap_dev_state(sp.rows, sp.cols) for sp in specs]
+    outs = [torch.empty((sp.rows, sp.cols), dtype=torch.float32, device="cuda") for sp in specs]
+    for t in range(1, 5):
+        if t == 4:
+            prevs = [_host_state(_clone_state(x)) for x in sts]
+            wps = [to_host(W) for W in Ws]
+        gs = [bf16_round(synth.gradient("c3", sp, t)) for sp in specs]
+        gpu_lib.soap_step_many([(Ws[i], to_dev(gs[i], "bf16"), sts[i]) for i in range(2)], t,
+                               update_out=outs, back_rot_dtype="bf16", **HP)
+        torch.cuda.synchronize()
+    for i, sp in enumerate(specs):
+        new = _host_state(sts[i])
+        _, ref, upd, _ = oracle.soap_step(wps[i], gs[i].astype(np.float64), prevs[i], 4,
+                                          refresh_every=0, q_override=(new.QL, new.QR), **HP)
+        got = to_host(outs[i])
+        eu, etu, ev = rel(got, upd), tile_max_rel(got, upd), rel(new.V, ref.V)
+        log(f"  {sp.name} t=4: update {eu:.2e} (tile {etu:.2e}) V {ev:.2e}")
+        assert eu < 2e-2 and etu < 2e-2 and ev < 1e-4
