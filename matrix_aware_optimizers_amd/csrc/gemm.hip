@@ -374,6 +374,9 @@ mao_status write_pointer_table(const void** dst, const void* const* src, int n, 
 }
 
 mao_status launch_gemm(int in_dtype, GemmProblem* probs, int nprob, hipStream_t stream, int tag) {
+  // contractions outside Newton-Schulz and the QR are timed apart by input
+  // type, so that each is measured against its own peak
+  if (tag == TAG_OTHER && in_dtype == MAO_BF16) tag = TAG_OTHER_BF16;
   if (nprob <= 0) return MAO_OK;
   if (nprob > kMaxProblems) {
     set_error("launch_gemm: %d problems > %d", nprob, kMaxProblems);
