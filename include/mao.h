@@ -62,7 +62,7 @@ extern "C" {
 #define MAO_API
 #endif
 
-#define MAO_ABI_VERSION 3
+#define MAO_ABI_VERSION 4
 #define MAO_MAX_GROUPS 8
 
 typedef enum {
@@ -197,6 +197,16 @@ MAO_API mao_status muon_step_noalloc(mao_mat W, mao_mat G, mao_mat M, const mao_
 /* SOAP with the real-time eigenbasis refresh                                */
 /* ------------------------------------------------------------------------ */
 
+/* Precision of the forward rotations (G~ = QL^T G QR, M~ = QL^T M QR, FOAM's
+ * G QR and M QR), which must stay fp32-accurate ([SMB] section 3-2 (3)). */
+typedef enum {
+  MAO_ROT_F32 = 0,    /* fp32 MFMA */
+  MAO_ROT_BF16X3 = 1  /* bf16 MFMA on split operands: x = hi + lo (both bf16),
+                         A B^T = hi_a hi_b^T + lo_a hi_b^T + hi_a lo_b^T as one
+                         product over three times K (fp32 accumulation;
+                         relative error about 2^-16) */
+} mao_rot_mode;
+
 typedef struct {
   float lr, beta1, beta2; /* 0 <= beta < 1 */
   float eps;              /* > 0, Adam denominator sqrt(v_hat) + eps */
@@ -207,6 +217,7 @@ typedef struct {
                              MFMA; MAO_BF16: on bf16 MFMA (operands rounded to
                              bf16, fp32 accumulation; [SMB] section 3-2 (3)
                              allows the reduced precision on this product) */
+  int32_t fwd_rot;        /* mao_rot_mode of the forward rotations */
 } mao_soap_hparams;
 
 /* SOAP optimizer state, all fp32, rows = m, cols = n of W.
@@ -237,7 +248,9 @@ MAO_API size_t soap_workspace_size(int64_t rows, int64_t cols, const mao_soap_hp
  *   N = (M~ / (1-b1^t)) / (sqrt(V / (1-b2^t)) + eps)
  *   U = QL N QR^T;  W <- W - lr (weight_decay W + U)
  *
- * Every contraction runs in fp32 (fp32 MFMA). W, G: bf16 or fp32.
+ * The factor EMAs of a bf16 G run on bf16 MFMA (exact products), the
+ * refresh in fp32; the forward rotations in fp32 or as bf16x3 (fwd_rot), the
+ * rotation back in fp32 or bf16 (back_rot_dtype). W, G: bf16 or fp32.
  * update_out: NULL or fp32 rows*cols (dense) receiving U. t >= 1.
  */
 MAO_API mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* state, int64_t t,
@@ -270,6 +283,7 @@ typedef struct {
   int32_t refresh; /* mao_refresh_mode; MAO_REFRESH_EIGH needs k <= 16384 */
   int32_t back_rot_dtype; /* MAO_F32 or MAO_BF16: precision of U = N QR^T
                              (QR N on the output side), as for SOAP */
+  int32_t fwd_rot;        /* mao_rot_mode of G_rot and M_rot */
 } mao_foam_hparams;
 
 /* FOAM state, fp32, W is m x n; k = n for MAO_FOAM_INPUT, m for

@@ -443,6 +443,13 @@ struct RotBufs {
   bf16_t* QRb = nullptr;
   bf16_t* QLb = nullptr;
   bf16_t* T2b = nullptr;
+  // bf16x3 forward rotations: split operands (split3_bf16 layouts)
+  bf16_t* X3 = nullptr;   // m x 3n': G (or [G | G]) and M (SOAP: M too)
+  bf16_t* Y3 = nullptr;   // m x 3n': FOAM's M (its G and M products share a phase)
+  bf16_t* ER3 = nullptr;  // n x 3n'
+  bf16_t* EL3 = nullptr;  // m x 3m' (SOAP)
+  bf16_t* T3 = nullptr;   // n x 3m' (SOAP)
+  int64_t ld3m = 0, ld3n = 0;
   int64_t ldm, ldn;  // padded leading dims for m- and n-long rows
 };
 
@@ -450,7 +457,7 @@ struct RotBufs {
 // workspace belong to this matrix; otherwise the caller points EL, ER, S and
 // flag into the shared, size-grouped QR area of a many-matrix call.
 void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool own_qr = true,
-               bool eigh = false, bool back_bf16 = false) {
+               bool eigh = false, bool back_bf16 = false, bool fwd3 = false) {
   R.ldm = ws_ld(m);
   R.ldn = ws_ld(n);
   const int big = std::max(m, n);
@@ -469,6 +476,18 @@ void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool
   R.flag = (soap || !own_qr) ? nullptr : c.take<int>(4);
   if (own_qr) R.qr = carve_qr_work(c, big);
   if (own_qr && eigh) R.eigh = c.take<char>(eigh_work_stride(n));
+  if (fwd3) {
+    R.ld3m = ws_ld(3 * split_width(m));
+    R.ld3n = ws_ld(3 * split_width(n));
+    R.X3 = c.take<bf16_t>((size_t)m * R.ld3n);
+    R.ER3 = c.take<bf16_t>((size_t)n * R.ld3n);
+    if (soap) {
+      R.EL3 = c.take<bf16_t>((size_t)m * R.ld3m);
+      R.T3 = c.take<bf16_t>((size_t)n * R.ld3m);
+    } else {
+      R.Y3 = c.take<bf16_t>((size_t)m * R.ld3n);
+    }
+  }
   if (back_bf16) {
     R.Nb = c.take<bf16_t>((size_t)m * R.ldn);
     R.QRb = c.take<bf16_t>((size_t)n * R.ldn);
@@ -598,6 +617,20 @@ mao_status nt32(int M, int N, int K, const float* A, int64_t lda, const float* B
   return gemm_add(gb, p, MAO_F32, s);
 }
 
+// D = A B^T (fp32 out; D or its transposed copy Dt) as bf16x3 on bf16 MFMA:
+// A3 (M x 3K', or [A | A] over 2K' when A is exact in bf16) against B3 = [hi
+// | hi | lo] (N x 3K'), both already split (split3_bf16); K' = split_width(K).
+mao_status nt3(int M, int N, int K, const bf16_t* A3, int64_t lda3, bool a_dup, const bf16_t* B3,
+               int64_t ldb3, float* D, int64_t ldd, float* Dt, int64_t lddt, hipStream_t s,
+               GemmBatch* gb) {
+  const int Kp = (int)split_width(K);
+  GemmProblem p = gemm_problem(M, N, a_dup ? 2 * Kp : 3 * Kp, 1.f, A3, lda3,
+                               a_dup ? B3 + Kp : B3, ldb3, 0.f, nullptr, 0, D, ldd, GF_D_F32);
+  p.Dt = Dt;
+  p.lddt = lddt;
+  return gemm_add(gb, p, MAO_BF16, s);
+}
+
 // F <- beta F + (1 - beta) X X^T (SYRK in place, fp32 F; X fp32 or bf16:
 // bf16 products are exact in fp32, so both accumulate alike in fp32)
 mao_status syrk_ema(int N, int K, const void* X, int64_t ldx, float beta, float* F, int64_t ldf,
@@ -683,7 +716,8 @@ size_t soap_workspace_size(int64_t rows, int64_t cols, const mao_soap_hparams* h
   if (!hp || rows < 1 || cols < 1) return 0;
   Carver c(nullptr);
   RotBufs R;
-  carve_rot(c, (int)rows, (int)cols, true, true, R, true, false, hp->back_rot_dtype == MAO_BF16);
+  carve_rot(c, (int)rows, (int)cols, true, true, R, true, false, hp->back_rot_dtype == MAO_BF16,
+            hp->fwd_rot == MAO_ROT_BF16X3);
   return c.used + 256;
 }
 
@@ -717,6 +751,8 @@ mao_status check_soap_hp(const mao_soap_hparams* hp) {
   MAO_TRY(check_adam_hp(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay));
   if (hp->refresh_every < 0) MAO_FAIL(MAO_E_HPARAM, "refresh_every=%d", hp->refresh_every);
   if (!dtype_ok(hp->back_rot_dtype)) MAO_FAIL(MAO_E_DTYPE, "back_rot_dtype=%d", hp->back_rot_dtype);
+  if (hp->fwd_rot != MAO_ROT_F32 && hp->fwd_rot != MAO_ROT_BF16X3)
+    MAO_FAIL(MAO_E_HPARAM, "fwd_rot=%d", hp->fwd_rot);
   return MAO_OK;
 }
 
@@ -773,6 +809,29 @@ mao_status soap_post(int stage, const mao_mat& W, const mao_mat& G, const mao_so
   const int64_t ldG = G.dtype == MAO_F32 ? G.ld : R.ldn;
   float* U = update_out ? update_out : R.U;
   const int64_t ldU = update_out ? n : R.ldn;
+  const bool f3 = hp->fwd_rot == MAO_ROT_BF16X3;
+  if (f3 && stage <= 3) {
+    // fp32-accurate rotations as bf16x3 products (split operands)
+    switch (stage) {
+      case 0: {
+        MAO_TRY(split3_bf16(view(R.ER, R.ldn), MAO_F32, n, n, view(R.ER3, R.ld3n), kSplitB, s));
+        const bool dup = G.dtype == MAO_BF16;
+        MAO_TRY(split3_bf16(view(G.data, G.ld), G.dtype, m, n, view(R.X3, R.ld3n),
+                            dup ? kSplitDup : kSplitA, s));
+        return nt3(m, n, n, R.X3, R.ld3n, dup, R.ER3, R.ld3n, nullptr, 0, R.T2t, R.ldm, s, gb);
+      }
+      case 1:
+        MAO_TRY(split3_bf16(view(R.EL, R.ldm), MAO_F32, m, m, view(R.EL3, R.ld3m), kSplitA, s));
+        MAO_TRY(split3_bf16(view(R.T2t, R.ldm), MAO_F32, n, m, view(R.T3, R.ld3m), kSplitB, s));
+        return nt3(m, n, m, R.EL3, R.ld3m, false, R.T3, R.ld3m, R.Gtil, R.ldn, nullptr, 0, s, gb);
+      case 2:
+        MAO_TRY(split3_bf16(view((void*)M, ldM), MAO_F32, m, n, view(R.X3, R.ld3n), kSplitA, s));
+        return nt3(m, n, n, R.X3, R.ld3n, false, R.ER3, R.ld3n, nullptr, 0, R.T2t, R.ldm, s, gb);
+      default:
+        MAO_TRY(split3_bf16(view(R.T2t, R.ldm), MAO_F32, n, m, view(R.T3, R.ld3m), kSplitB, s));
+        return nt3(m, n, m, R.EL3, R.ld3m, false, R.T3, R.ld3m, R.Mtil, R.ldn, nullptr, 0, s, gb);
+    }
+  }
   switch (stage) {
     case 0: return nt32(m, n, n, Gf, ldG, R.ER, R.ldn, nullptr, 0, R.T2t, R.ldm, s, nullptr, gb);
     case 1: return nt32(m, n, m, R.EL, R.ldm, R.T2t, R.ldm, R.Gtil, R.ldn, nullptr, 0, s, nullptr, gb);
@@ -824,6 +883,8 @@ mao_status check_foam_hp(const mao_foam_hparams* hp) {
   if (hp->refresh != MAO_REFRESH_QR && hp->refresh != MAO_REFRESH_EIGH)
     MAO_FAIL(MAO_E_HPARAM, "refresh=%d must be 0 (QR) or 1 (eigh)", hp->refresh);
   if (!dtype_ok(hp->back_rot_dtype)) MAO_FAIL(MAO_E_DTYPE, "back_rot_dtype=%d", hp->back_rot_dtype);
+  if (hp->fwd_rot != MAO_ROT_F32 && hp->fwd_rot != MAO_ROT_BF16X3)
+    MAO_FAIL(MAO_E_HPARAM, "fwd_rot=%d", hp->fwd_rot);
   return MAO_OK;
 }
 
@@ -923,6 +984,28 @@ float* foam_u(RotBufs& R, const mao_foam_hparams* hp, int n, float* update_out, 
 mao_status foam_rotate(const mao_mat& W, const mao_mat& G, const mao_foam_state* st, RotBufs& R,
                        const mao_foam_hparams* hp, GemmBatch* gb, hipStream_t s) {
   const int m = (int)W.rows, n = (int)W.cols;
+  if (hp->fwd_rot == MAO_ROT_BF16X3) {
+    // problem pm x pn: G_rot = G E_R^T (input side), or G^T E_R^T (output
+    // side, from G's fp32 transposed copy); M likewise
+    const bool out = foam_out(hp);
+    const int pm = out ? n : m, pn = out ? m : n;
+    MAO_TRY(split3_bf16(view(R.ER, R.ldn), MAO_F32, pn, pn, view(R.ER3, R.ld3n), kSplitB, s));
+    const bool dup = !out && G.dtype == MAO_BF16;
+    if (out)
+      MAO_TRY(split3_bf16(view(R.Gf, R.ldn), MAO_F32, pm, pn, view(R.X3, R.ld3n), kSplitA, s));
+    else
+      MAO_TRY(split3_bf16(view(G.data, G.ld), G.dtype, pm, pn, view(R.X3, R.ld3n),
+                          dup ? kSplitDup : kSplitA, s));
+    MAO_TRY(nt3(pm, pn, pn, R.X3, R.ld3n, dup, R.ER3, R.ld3n, R.Gtil, R.ldn, nullptr, 0, s, gb));
+    if (out) {
+      MAO_TRY(transpose(view(st->M.data, st->M.ld), view(R.U, R.ldn), m, n, 1, MAO_F32, s));
+      MAO_TRY(split3_bf16(view(R.U, R.ldn), MAO_F32, pm, pn, view(R.Y3, R.ld3n), kSplitA, s));
+    } else {
+      MAO_TRY(split3_bf16(view(st->M.data, st->M.ld), MAO_F32, pm, pn, view(R.Y3, R.ld3n),
+                          kSplitA, s));
+    }
+    return nt3(pm, pn, pn, R.Y3, R.ld3n, false, R.ER3, R.ld3n, R.Mtil, R.ldn, nullptr, 0, s, gb);
+  }
   if (foam_out(hp)) {
     MAO_TRY(nt32(n, m, m, R.Gf, R.ldn, R.ER, R.ldn, R.Gtil, R.ldn, nullptr, 0, s, nullptr, gb));
     MAO_TRY(transpose(view(st->M.data, st->M.ld), view(R.U, R.ldn), m, n, 1, MAO_F32, s));
@@ -1009,13 +1092,13 @@ struct QrGroup {
 // products per matrix in a phase, five pointers each).
 void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<RotBufs>& R,
                 std::vector<QrGroup>& groups, bool fout = false, GemmBatch* gb = nullptr,
-                bool eigh = false, bool back_bf16 = false) {
+                bool eigh = false, bool back_bf16 = false, bool fwd3 = false) {
   R.assign(count, RotBufs{});
   std::vector<std::pair<int, QrJobRef>> all;
   for (int i = 0; i < count; ++i) {
     const int m = (int)W[i].rows, n = (int)W[i].cols;
     const bool t = !soap && fout;
-    carve_rot(c, t ? n : m, t ? m : n, soap, true, R[i], false, false, back_bf16);
+    carve_rot(c, t ? n : m, t ? m : n, soap, true, R[i], false, false, back_bf16, fwd3);
     if (soap) all.push_back({m, QrJobRef{i, 0}});
     all.push_back({t ? m : n, QrJobRef{i, 1}});
   }
@@ -1063,11 +1146,11 @@ void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<R
 }
 
 size_t many_ws(int count, const mao_mat* W, bool soap, bool fout = false, bool eigh = false,
-               bool back_bf16 = false) {
+               bool back_bf16 = false, bool fwd3 = false) {
   Carver c(nullptr);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
-  carve_many(c, count, W, soap, R, groups, fout, nullptr, eigh, back_bf16);
+  carve_many(c, count, W, soap, R, groups, fout, nullptr, eigh, back_bf16, fwd3);
   return c.used + 256;
 }
 
@@ -1098,7 +1181,8 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
   MAO_TRY(check_workspace(workspace, workspace_bytes, soap_workspace_size(m, n, hp)));
   Carver c(workspace);
   RotBufs R;
-  carve_rot(c, m, n, true, true, R, true, false, hp->back_rot_dtype == MAO_BF16);
+  carve_rot(c, m, n, true, true, R, true, false, hp->back_rot_dtype == MAO_BF16,
+            hp->fwd_rot == MAO_ROT_BF16X3);
   MAO_TRY(soap_pre(W, G, st, R, hp, nullptr, s));
   // 3b. refresh: Q <- qr(F Q); S = (F Q)^T = Q^T F stored row-major
   if (soap_refresh(hp, t)) {
@@ -1117,7 +1201,8 @@ size_t soap_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_
   if (!hp || !W || count < 1 || count > kMaxMany) return 0;
   for (int i = 0; i < count; ++i)
     if (W[i].rows < 1 || W[i].cols < 1) return 0;
-  return many_ws(count, W, true, false, false, hp->back_rot_dtype == MAO_BF16);
+  return many_ws(count, W, true, false, false, hp->back_rot_dtype == MAO_BF16,
+                 hp->fwd_rot == MAO_ROT_BF16X3);
 }
 
 mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
@@ -1131,13 +1216,14 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   for (int i = 0; i < count; ++i)
     MAO_TRY(validate_soap(W[i], G[i], &st[i], t, update_out ? update_out[i] : nullptr, rr));
   MAO_TRY(check_no_overlap(rr));
-  const bool bb = hp->back_rot_dtype == MAO_BF16;
-  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, true, false, false, bb)));
+  const bool bb = hp->back_rot_dtype == MAO_BF16, f3 = hp->fwd_rot == MAO_ROT_BF16X3;
+  MAO_TRY(check_workspace(workspace, workspace_bytes,
+                          many_ws(count, W, true, false, false, bb, f3)));
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
   GemmBatch gb;
-  carve_many(c, count, W, true, R, groups, false, &gb, false, bb);
+  carve_many(c, count, W, true, R, groups, false, &gb, false, bb, f3);
   for (int i = 0; i < count; ++i) MAO_TRY(soap_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
   MAO_TRY(gemm_flush(gb, s));
   if (soap_refresh(hp, t)) {
@@ -1193,7 +1279,7 @@ size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hparams* h
   RotBufs R;
   const bool out = foam_out(hp);
   carve_rot(c, (int)(out ? cols : rows), (int)(out ? rows : cols), false, true, R, true,
-            foam_eigh(hp), hp->back_rot_dtype == MAO_BF16);
+            foam_eigh(hp), hp->back_rot_dtype == MAO_BF16, hp->fwd_rot == MAO_ROT_BF16X3);
   return c.used + 256;
 }
 
@@ -1212,7 +1298,7 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
   Carver c(workspace);
   RotBufs R;
   carve_rot(c, out ? n : m, out ? m : n, false, true, R, true, foam_eigh(hp),
-            hp->back_rot_dtype == MAO_BF16);
+            hp->back_rot_dtype == MAO_BF16, hp->fwd_rot == MAO_ROT_BF16X3);
   MAO_TRY(foam_pre(W, G, st, R, hp, nullptr, s));
   for (int stage = 0; stage < 3; ++stage)
     MAO_TRY(foam_criterion(k, st, R, t, hp, stage, nullptr, s));
@@ -1246,7 +1332,8 @@ size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_
     if (W[i].rows < 1 || W[i].cols < 1) return 0;
     if (foam_eigh(hp) && (foam_out(hp) ? W[i].rows : W[i].cols) > kEighMaxN) return 0;
   }
-  return many_ws(count, W, false, foam_out(hp), foam_eigh(hp), hp->back_rot_dtype == MAO_BF16);
+  return many_ws(count, W, false, foam_out(hp), foam_eigh(hp), hp->back_rot_dtype == MAO_BF16,
+                 hp->fwd_rot == MAO_ROT_BF16X3);
 }
 
 mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
@@ -1260,14 +1347,14 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   for (int i = 0; i < count; ++i)
     MAO_TRY(validate_foam(W[i], G[i], &st[i], t, hp, update_out ? update_out[i] : nullptr, rr));
   MAO_TRY(check_no_overlap(rr));
-  const bool bb = hp->back_rot_dtype == MAO_BF16;
+  const bool bb = hp->back_rot_dtype == MAO_BF16, f3 = hp->fwd_rot == MAO_ROT_BF16X3;
   MAO_TRY(check_workspace(workspace, workspace_bytes,
-                          many_ws(count, W, false, foam_out(hp), foam_eigh(hp), bb)));
+                          many_ws(count, W, false, foam_out(hp), foam_eigh(hp), bb, f3)));
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
   GemmBatch gb;
-  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb, foam_eigh(hp), bb);
+  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb, foam_eigh(hp), bb, f3);
   // phases: every matrix's products of a phase go out as grouped launches
   for (int i = 0; i < count; ++i) MAO_TRY(foam_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
   MAO_TRY(gemm_flush(gb, s));

@@ -395,6 +395,39 @@ __global__ __launch_bounds__(kBlock) void soap_adam_kernel(View Gt, View Mt, Vie
   }
 }
 
+// fp32-accurate products on bf16 MFMA: X = hi + lo with hi = bf16(X),
+// lo = bf16(X - hi); a row of K elements becomes 3K (or 2K) bf16 in one of
+// three orders: kSplitA [hi | lo | hi], kSplitB [hi | hi | lo] (so that
+// A3 B3^T = hi_a hi_b^T + lo_a hi_b^T + hi_a lo_b^T), kSplitDup [x | x] for an
+// operand already exact in bf16 (against the last 2K of a kSplitB operand).
+template <typename TI>
+__global__ __launch_bounds__(kBlock) void split3_kernel(View In, int rows, int K, int Kp, View Out,
+                                                        int layout, int nrb) {
+  const Chunks ch = block_chunks(rows, Kp, nrb);
+#pragma unroll 2
+  for (unsigned q = threadIdx.x; q < ch.n; q += kBlock) {
+    int i, j;
+    ch.at(q, i, j);
+    float x[8], hi[8], lo[8];
+    load8<TI>((const TI*)In.p + (int64_t)i * In.ld, j, K, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = bf16_to_f32(f32_to_bf16(x[e]));
+      lo[e] = x[e] - hi[e];
+    }
+    // columns K..Kp read as zero and are stored as zero (segment padding)
+    bf16_t* out = (bf16_t*)Out.p + (int64_t)i * Out.ld;
+    if (layout == kSplitDup) {
+      store8<bf16_t>(out, j, Kp, x);
+      store8<bf16_t>(out + Kp, j, Kp, x);
+    } else {
+      store8<bf16_t>(out, j, Kp, hi);
+      store8<bf16_t>(out + Kp, j, Kp, layout == kSplitA ? lo : hi);
+      store8<bf16_t>(out + 2 * Kp, j, Kp, layout == kSplitA ? hi : lo);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void fill_identity_kernel(View E, int n, const int* pred) {
   if (pred && *pred == 0) return;
   const int64_t total = (int64_t)n * n;
@@ -726,6 +759,17 @@ mao_status soap_adam(View Gt, View Mt, View V, int rows, int cols, float beta2, 
     hipLaunchKernelGGL(soap_adam_kernel<bf16_t>, dim3(nrb), dim3(kBlock), 0, s, Gt, Mt, V, Nb, rows, cols, beta2, bc1, bc2, eps, nrb);
   else
     hipLaunchKernelGGL(soap_adam_kernel<float>, dim3(nrb), dim3(kBlock), 0, s, Gt, Mt, V, Gt, rows, cols, beta2, bc1, bc2, eps, nrb);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
+
+mao_status split3_bf16(View In, int in_dtype, int rows, int K, View Out, int layout, hipStream_t s) {
+  const int Kp = (int)split_width(K);
+  const int nrb = rowblocks_for(rows, 1);
+  if (in_dtype == MAO_BF16)
+    hipLaunchKernelGGL(split3_kernel<bf16_t>, dim3(nrb), dim3(kBlock), 0, s, In, rows, K, Kp, Out, layout, nrb);
+  else
+    hipLaunchKernelGGL(split3_kernel<float>, dim3(nrb), dim3(kBlock), 0, s, In, rows, K, Kp, Out, layout, nrb);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
 }

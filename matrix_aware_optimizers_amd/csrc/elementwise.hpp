@@ -69,6 +69,17 @@ mao_status apply_update(View W, int w_dtype, View O, int o_dtype, int rows, int 
 mao_status soap_adam(View Gt, View Mt, View V, int rows, int cols, float beta2, float bc1,
                      float bc2, float eps, hipStream_t s, View Nb = View{nullptr, 0, 0});
 
+// bf16 split of a row-major rows x K matrix (fp32, or bf16 for kSplitDup)
+// into Out (rows x 3 Kp, or 2 Kp for kSplitDup, Kp = split_width(K) = K
+// rounded up to 8, the segments zero-padded; ld >= that): kSplitA = [hi | lo
+// | hi], kSplitB = [hi | hi | lo], kSplitDup = [x | x]. A kSplitA operand
+// times a kSplitB one over the 3 Kp is the fp32 product up to the lo.lo term
+// and the residue of the split (relative 2^-16).
+enum SplitLayout : int { kSplitA = 0, kSplitB = 1, kSplitDup = 2 };
+inline int64_t split_width(int64_t K) { return (K + 7) / 8 * 8; }
+mao_status split3_bf16(View In, int in_dtype, int rows, int K, View Out, int layout,
+                       hipStream_t s);
+
 // E <- I (n x n fp32); skipped when pred != nullptr and *pred == 0.
 mao_status fill_identity(View E, int n, const int* pred, hipStream_t s);
 

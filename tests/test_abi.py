@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = mao.load()
-    assert lib.mao_abi_version() == 3
+    assert lib.mao_abi_version() == 4
     for code in range(10):
         assert lib.mao_status_string(code)
     assert lib.mao_status_string(99) == b"unknown status"
@@ -234,6 +234,15 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
                          None) == E_DTYPE
     assert lib.soap_step(W, G, ctypes.byref(st), 1, ctypes.byref(mao.soap_hparams(back_rot_dtype=7)),
                          ws, 1 << 30, None, None) == E_DTYPE
+    assert lib.soap_step(W, G, ctypes.byref(st), 1, ctypes.byref(mao.soap_hparams(fwd_rot=2)),
+                         ws, 1 << 30, None, None) == E_HPARAM
+    assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(mao.foam_hparams(fwd_rot=-1)),
+                         ws, 1 << 30, None, None) == E_HPARAM
+    # the split operands of the bf16x3 rotations take workspace of their own
+    for f in ("soap_workspace_size", "foam_workspace_size"):
+        hp_of = mao.soap_hparams if f.startswith("soap") else mao.foam_hparams
+        assert (getattr(lib, f)(m, n, ctypes.byref(hp_of(fwd_rot="bf16x3")))
+                > getattr(lib, f)(m, n, ctypes.byref(hp_of())))
     assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(mao.foam_hparams(side=2)), ws,
                          fneed, None, None) == E_HPARAM
     # the output side keeps m x m factors: the n x n state is the wrong shape

@@ -53,7 +53,7 @@ def _check_basis(q, p, q_ref, tag):
         assert fe < 1e-4, f"{tag}: forward error {fe} at kappa {kappa:.1e}"
 
 
-def _run_soap(gpu_lib, m, n, steps, grad, dtype="f32", refresh_every=1, back="f32"):
+def _run_soap(gpu_lib, m, n, steps, grad, dtype="f32", refresh_every=1, back="f32", fwd="f32"):
     import torch
     W = to_dev(synth.init_weight("c1", synth.MatrixSpec("w", m, n, 7)), dtype)
     st = _soap_state_dev(m, n)
@@ -68,7 +68,7 @@ def _run_soap(gpu_lib, m, n, steps, grad, dtype="f32", refresh_every=1, back="f3
         prev = _host_soap(st)
         w_prev = to_host(W)
         gpu_lib.soap_step(W, to_dev(g, dtype), st, t, update_out=out, refresh_every=refresh_every,
-                          back_rot_dtype=back, **HP)
+                          back_rot_dtype=back, fwd_rot=fwd, **HP)
         torch.cuda.synchronize()
         new = _host_soap(st)
         # EMAs from the GPU's previous state
@@ -143,16 +143,18 @@ def _host_foam(st):
                             to_host(st["r"]), to_host(st["c"]))
 
 
-@pytest.mark.parametrize("m,n,pf,side,gdt", [(160, 96, 3, "input", "f32"), (96, 264, 4, "input", "f32"),
-                                             (160, 96, 3, "output", "f32"),
-                                             (264, 96, 4, "output", "f32"),
-                                             (96, 160, 3, "input", "bf16"),
-                                             (160, 96, 3, "output", "bf16")])
-def test_foam_teacher_forced(gpu_lib, m, n, pf, side, gdt):
+@pytest.mark.parametrize("m,n,pf,side,gdt,fwd", [
+    (160, 96, 3, "input", "f32", "f32"), (96, 264, 4, "input", "f32", "f32"),
+    (160, 96, 3, "output", "f32", "f32"), (264, 96, 4, "output", "f32", "f32"),
+    (96, 160, 3, "input", "bf16", "f32"), (160, 96, 3, "output", "bf16", "f32"),
+    # forward rotations as bf16x3 products on bf16 MFMA
+    (328, 136, 3, "input", "f32", "bf16x3"), (96, 264, 4, "input", "bf16", "bf16x3"),
+    (136, 328, 3, "output", "f32", "bf16x3"), (264, 96, 4, "output", "bf16", "bf16x3")])
+def test_foam_teacher_forced(gpu_lib, m, n, pf, side, gdt, fwd):
     """FOAM (input side) and its output-only ablation ([FOAM] section 3),
     teacher-forced against the oracle, with fp32 and bf16 gradients."""
     import torch
-    log(f"foam {side} {m}x{n} pf={pf} {gdt} gradient")
+    log(f"foam {side} {m}x{n} pf={pf} {gdt} gradient, {fwd} forward rotation")
     spec = synth.MatrixSpec("f", m, n, 5)
     W = to_dev(synth.init_weight("c5", spec))
     st = _foam_state_dev(m, n, side)
@@ -165,7 +167,7 @@ def test_foam_teacher_forced(gpu_lib, m, n, pf, side, gdt):
         prev = _host_foam(st)
         w_prev = to_host(W)
         gpu_lib.foam_step(W, to_dev(g, gdt), st, t, update_out=out, pf=pf, tol=0.1, side=side,
-                          **HP)
+                          fwd_rot=fwd, **HP)
         torch.cuda.synchronize()
         new = _host_foam(st)
         aux = to_host(st["aux"])
@@ -620,3 +622,76 @@ def test_many_bf16_back_rotation_matches_oracle(gpu_lib):
             if t >= 5:
                 assert rel(to_host(outs[i]), upd) < 2e-2
                 assert rel(new.r, ref2.r) < 1e-4 and rel(new.c, ref2.c) < 1e-4
+
+
+# ---- forward rotations as bf16x3 products (fwd_rot) --------------------------
+
+@pytest.mark.parametrize("shape,gdt", [((328, 200), "f32"), ((296, 520), "bf16"),
+                                       ((200, 520), "f32")])
+def test_soap_bf16x3_forward_rotation_teacher_forced(gpu_lib, shape, gdt):
+    """Q_L^T G Q_R and Q_L^T M Q_R as three bf16 products per fp32 product
+    (hi.hi + lo.hi + hi.lo): the update and V are held to the fp32 tolerance."""
+    m, n = shape
+    log(f"soap bf16x3 forward rotation {m}x{n} {gdt} gradient")
+    spec = synth.MatrixSpec("k", m, n, 14)
+    _run_soap(gpu_lib, m, n, 6, lambda t: synth.kronecker_gradient("c3", spec, t), dtype=gdt,
+              fwd="bf16x3")
+
+
+def test_soap_bf16x3_forward_with_bf16_back_rotation(gpu_lib):
+    """Both rotation options together (the configuration timed for the 8B
+    layer): V at the fp32 tolerance, the update at the bf16 one."""
+    log("soap bf16x3 forward + bf16 back 328x200")
+    spec = synth.MatrixSpec("k", 328, 200, 15)
+    _run_soap(gpu_lib, 328, 200, 6, lambda t: synth.kronecker_gradient("c3", spec, t),
+              dtype="bf16", back="bf16", fwd="bf16x3")
+
+
+def test_many_bf16x3_forward_rotation_matches_oracle(gpu_lib):
+    """soap_step_many and foam_step_many with bf16x3 forward rotations (grouped
+    bf16 products over split operands), teacher-forced at the fp32 tolerance."""
+    import torch
+    log("soap many bf16x3 forward")
+    shapes = [(1040, 1040)] * 3
+    grads = _square_gradients(len(shapes), 1040, 4, 75)
+    Ws = [to_dev(synth.init_weight("c1", synth.MatrixSpec("w", m, n, 50 + i)))
+          for i, (m, n) in enumerate(shapes)]
+    sts = [_soap_state_dev(m, n) for m, n in shapes]
+    outs = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in shapes]
+    for t in range(1, 5):
+        prevs, wps = [_host_soap(x) for x in sts], [to_host(W) for W in Ws]
+        gpu_lib.soap_step_many([(Ws[i], to_dev(grads[i][t - 1], "bf16"), sts[i])
+                                for i in range(3)], t, update_out=outs, fwd_rot="bf16x3", **HP)
+        torch.cuda.synchronize()
+        for i in range(3):
+            new = _host_soap(sts[i])
+            g = bf16_round(grads[i][t - 1].astype(np.float64))
+            _, ref2, upd, _ = oracle.soap_step(wps[i], g, prevs[i], t, refresh_every=0,
+                                               q_override=(new.QL, new.QR), **HP)
+            eu, ev = rel(to_host(outs[i]), upd), rel(new.V, ref2.V)
+            if t >= 3:
+                assert eu < 1e-4 and ev < 1e-4, f"t={t} matrix {i}: {eu} {ev}"
+        log(f"  soap many bf16x3 forward t={t} ok")
+    log("foam many bf16x3 forward")
+    for side in ("input", "output"):
+        shapes = [(2600, 1040)] * 2 if side == "input" else [(1040, 2600)] * 2
+        ws, gs = _many_inputs(shapes, 5, 77)
+        Ws = [to_dev(w) for w in ws]
+        sts = [_foam_state_dev_many(m, n, side) for m, n in shapes]
+        outs = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m, n in shapes]
+        for t in range(1, 6):
+            prevs, wps = [_host_foam(x) for x in sts], [to_host(W) for W in Ws]
+            gpu_lib.foam_step_many([(Ws[i], to_dev(gs[i][t - 1]), sts[i]) for i in range(2)], t,
+                                   update_out=outs, pf=1, tol=0.0, side=side, fwd_rot="bf16x3",
+                                   **HP)
+            torch.cuda.synchronize()
+            for i in range(2):
+                new, aux = _host_foam(sts[i]), to_host(sts[i]["aux"])
+                _, ref2, upd, _ = oracle.foam_step(wps[i], gs[i][t - 1].astype(np.float64),
+                                                   prevs[i], t, pf=1, tol=0.0, q_override=new.QR,
+                                                   refresh_override=bool(aux[1]), side=side, **HP)
+                if t >= 5:
+                    eu = rel(to_host(outs[i]), upd)
+                    assert eu < 1e-4, f"{side} t={t} matrix {i}: {eu}"
+                    assert rel(new.r, ref2.r) < 1e-4 and rel(new.c, ref2.c) < 1e-4
+            log(f"  foam many bf16x3 forward {side} t={t} ok")
