@@ -369,7 +369,7 @@ class SoapLikeWorkload:
     matrix."""
 
     def __init__(self, kind, config, specs, g_dtype, w_dtype, pf=10, tol=0.1, side="input",
-                 refresh="qr", back="f32", fwd="f32"):
+                 refresh="qr", back="f32", fwd="f32", prod="f32"):
         import torch
 
         import matrix_aware_optimizers_amd as mao
@@ -380,11 +380,12 @@ class SoapLikeWorkload:
         tw = torch.bfloat16 if w_dtype == "bf16" else torch.float32
         if kind == "soap":
             self.hp = mao.soap_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
-                                       refresh_every=1, back_rot_dtype=back, fwd_rot=fwd)
+                                       refresh_every=1, back_rot_dtype=back, fwd_rot=fwd,
+                                       refresh_prod=prod)
         else:
             self.hp = mao.foam_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
                                        pf=pf, tol=tol, side=side, refresh=refresh,
-                                       back_rot_dtype=back, fwd_rot=fwd)
+                                       back_rot_dtype=back, fwd_rot=fwd, refresh_prod=prod)
         for idx, sp in enumerate(specs):
             if idx % 16 == 15:
                 log(f"  {idx + 1}/{len(specs)} matrices set up")
@@ -449,13 +450,13 @@ class SoapLikeWorkload:
 
 
 def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, embedding=None,
-                 side="input", split_steps=0, refresh="qr", back="f32", fwd="f32"):
+                 side="input", split_steps=0, refresh="qr", back="f32", fwd="f32", prod="f32"):
     import torch
 
     import matrix_aware_optimizers_amd as mao
     log(f"setting up {workload_name} ({len(specs)} matrices)")
     wl = SoapLikeWorkload(kind, config, specs, g_dtype, w_dtype, side=side, refresh=refresh,
-                          back=back, fwd=fwd)
+                          back=back, fwd=fwd, prod=prod)
     if embedding:
         wl.add_embedding(*embedding)
     log("warmup")
@@ -510,7 +511,7 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": workload_name, "matrices": len(specs), "optimizer": kind,
                    "gradients": g_dtype, "weights": w_dtype, "back_rotation": back,
-                   "forward_rotation": fwd, **({"side": side, "refresh": refresh} if kind == "foam" else {})},
+                   "forward_rotation": fwd, "refresh_products": prod, **({"side": side, "refresh": refresh} if kind == "foam" else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
                      "kernel": "fp32 contractions of the step (gemm_f32_dl_kernel rotations and products, QR updates and projections; bf16 products under kernels.other_bf16)"},
@@ -532,11 +533,13 @@ def soap8b_summary(args):
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup = args.soap8b_steps, 2
     line = run_soaplike(sub, "llama8b_layer_soap", "soap", "c3", synth.specs("c3"), "bf16",
-                        "bf16", split_steps=1, back="bf16", fwd=args.fwd)
+                        "bf16", split_steps=1, back="bf16", fwd=args.fwd,
+                        prod=args.refresh_prod)
     k = line["kernels"]
     out = {"workload": "llama8b_layer_soap", "value": line["value"], "unit": "steps/s",
            "ms_per_step": line["ms_per_step"], "steps": sub.steps, "warmup": sub.warmup,
-           "back_rotation": "bf16", "forward_rotation": args.fwd}
+           "back_rotation": "bf16", "forward_rotation": args.fwd,
+           "refresh_products": args.refresh_prod}
     for tag, name in (("other", "rotations_and_products"), ("qr", "qr_updates"),
                       ("other_bf16", "bf16_products")):
         if tag in k:
@@ -637,6 +640,9 @@ def main():
     ap.add_argument("--fwd", default="f32", choices=["f32", "bf16x3"],
                     help="forward rotations of the SOAP / FOAM workloads: fp32 products, or "
                          "three bf16 products over hi/lo splits (fp32-accurate)")
+    ap.add_argument("--refresh-prod", default="f32", choices=["f32", "bf16x3"],
+                    help="power-iteration products L Q / R Q of SOAP and the criterion products "
+                         "of FOAM: fp32, or bf16x3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--soap8b-steps", type=int, default=5,
                     help="timed steps of the 8B layer under SOAP reported beside the default "
@@ -687,31 +693,31 @@ def main():
     elif args.workload == "c1soap":
         import synth
         line = run_soaplike(args, "single_256x512_soap_f32", "soap", "c1", synth.specs("c1"),
-                            "f32", "f32", back=args.back, fwd=args.fwd)
+                            "f32", "f32", back=args.back, fwd=args.fwd, prod=args.refresh_prod)
     elif args.workload == "soap8b":
         import synth
         line = run_soaplike(args, "llama8b_layer_soap", "soap", "c3", synth.specs("c3"),
-                            "bf16", "bf16", back=args.back, fwd=args.fwd)
+                            "bf16", "bf16", back=args.back, fwd=args.fwd, prod=args.refresh_prod)
     elif args.workload == "foam760m_eigh":
         import synth
         line = run_soaplike(args, "gpt2_760m_foam_eigh_refresh", "foam", "c5", synth.specs("c5"),
                             "f32", "f32", embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH),
-                            refresh="eigh", back=args.back, fwd=args.fwd)
+                            refresh="eigh", back=args.back, fwd=args.fwd, prod=args.refresh_prod)
     elif args.workload == "foam760m":
         import synth
         line = run_soaplike(args, "gpt2_760m_foam", "foam", "c5", synth.specs("c5"), "f32", "f32",
-                            embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH), back=args.back, fwd=args.fwd)
+                            embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH), back=args.back, fwd=args.fwd, prod=args.refresh_prod)
     elif args.workload == "foam760m_output":
         import synth
         line = run_soaplike(args, "gpt2_760m_foam_output_side", "foam", "c5", synth.specs("c5"),
                             "f32", "f32", embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH),
-                            side="output", back=args.back, fwd=args.fwd)
+                            side="output", back=args.back, fwd=args.fwd, prod=args.refresh_prod)
     elif args.workload == "observe8b":
         line = run_observe(args)
     else:
         import synth
         line = run_soaplike(args, "gpt2_760m_soap", "soap", "c5", synth.specs("c5"), "f32", "f32",
-                            back=args.back, fwd=args.fwd)
+                            back=args.back, fwd=args.fwd, prod=args.refresh_prod)
     print(json.dumps(line), flush=True)
 
 

@@ -197,8 +197,9 @@ MAO_API mao_status muon_step_noalloc(mao_mat W, mao_mat G, mao_mat M, const mao_
 /* SOAP with the real-time eigenbasis refresh                                */
 /* ------------------------------------------------------------------------ */
 
-/* Precision of the forward rotations (G~ = QL^T G QR, M~ = QL^T M QR, FOAM's
- * G QR and M QR), which must stay fp32-accurate ([SMB] section 3-2 (3)). */
+/* Precision of the products that must stay fp32-accurate ([SMB] section 3-2
+ * (3)): the forward rotations (G~ = QL^T G QR, M~ = QL^T M QR, FOAM's G QR and
+ * M QR) and the power-iteration products F Q that feed the refresh. */
 typedef enum {
   MAO_ROT_F32 = 0,    /* fp32 MFMA */
   MAO_ROT_BF16X3 = 1  /* bf16 MFMA on split operands: x = hi + lo (both bf16),
@@ -218,6 +219,8 @@ typedef struct {
                              bf16, fp32 accumulation; [SMB] section 3-2 (3)
                              allows the reduced precision on this product) */
   int32_t fwd_rot;        /* mao_rot_mode of the forward rotations */
+  int32_t refresh_prod;   /* mao_rot_mode of the power-iteration products L QL
+                             and R QR (the QR inputs) */
 } mao_soap_hparams;
 
 /* SOAP optimizer state, all fp32, rows = m, cols = n of W.
@@ -249,8 +252,9 @@ MAO_API size_t soap_workspace_size(int64_t rows, int64_t cols, const mao_soap_hp
  *   U = QL N QR^T;  W <- W - lr (weight_decay W + U)
  *
  * The factor EMAs of a bf16 G run on bf16 MFMA (exact products), the
- * refresh in fp32; the forward rotations in fp32 or as bf16x3 (fwd_rot), the
- * rotation back in fp32 or bf16 (back_rot_dtype). W, G: bf16 or fp32.
+ * refresh products in fp32 or as bf16x3 (refresh_prod), the QR in fp32; the
+ * forward rotations in fp32 or as bf16x3 (fwd_rot), the rotation back in fp32
+ * or bf16 (back_rot_dtype). W, G: bf16 or fp32.
  * update_out: NULL or fp32 rows*cols (dense) receiving U. t >= 1.
  */
 MAO_API mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* state, int64_t t,
@@ -284,6 +288,12 @@ typedef struct {
   int32_t back_rot_dtype; /* MAO_F32 or MAO_BF16: precision of U = N QR^T
                              (QR N on the output side), as for SOAP */
   int32_t fwd_rot;        /* mao_rot_mode of G_rot and M_rot */
+  int32_t refresh_prod;   /* mao_rot_mode of the criterion products S = QR^T R
+                             (the QR refresh's input) and S QR; MAO_ROT_BF16X3
+                             only with MAO_REFRESH_QR (MAO_E_UNSUPPORTED with
+                             the eigendecomposition, whose eigenvectors are
+                             only as accurate as its input relative to the
+                             eigenvalue gaps) */
 } mao_foam_hparams;
 
 /* FOAM state, fp32, W is m x n; k = n for MAO_FOAM_INPUT, m for

@@ -50,7 +50,7 @@ class MuonHparams(ctypes.Structure):
 class SoapHparams(ctypes.Structure):
     _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
                 ("weight_decay", c_float), ("refresh_every", c_int32),
-                ("back_rot_dtype", c_int32), ("fwd_rot", c_int32)]
+                ("back_rot_dtype", c_int32), ("fwd_rot", c_int32), ("refresh_prod", c_int32)]
 
 
 class SoapStateC(ctypes.Structure):
@@ -60,12 +60,17 @@ class SoapStateC(ctypes.Structure):
 class FoamHparams(ctypes.Structure):
     _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
                 ("weight_decay", c_float), ("pf", c_int32), ("tol", c_float), ("side", c_int32),
-                ("refresh", c_int32), ("back_rot_dtype", c_int32), ("fwd_rot", c_int32)]
+                ("refresh", c_int32), ("back_rot_dtype", c_int32), ("fwd_rot", c_int32),
+                ("refresh_prod", c_int32)]
 
 
 REFRESH_MODES = {"qr": 0, "eigh": 1}
 ROT_MODES = {"f32": 0, "bf16x3": 1}
 EIGH_MAX_SWEEPS = 12
+
+
+def _rot_code(mode):
+    return ROT_MODES[mode] if isinstance(mode, str) else int(mode)
 
 
 class FoamStateC(ctypes.Structure):
@@ -301,12 +306,13 @@ def _dtype_code(d):
 
 
 def soap_hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, refresh_every=1,
-                 back_rot_dtype="f32", fwd_rot="f32"):
+                 back_rot_dtype="f32", fwd_rot="f32", refresh_prod="f32"):
     hp = SoapHparams()
     hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay = lr, beta1, beta2, eps, weight_decay
     hp.refresh_every = refresh_every
     hp.back_rot_dtype = _dtype_code(back_rot_dtype)
-    hp.fwd_rot = ROT_MODES[fwd_rot] if isinstance(fwd_rot, str) else int(fwd_rot)
+    hp.fwd_rot = _rot_code(fwd_rot)
+    hp.refresh_prod = _rot_code(refresh_prod)
     return hp
 
 
@@ -329,14 +335,16 @@ FOAM_SIDES = {"input": 0, "output": 1}
 
 
 def foam_hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, pf=10, tol=0.1,
-                 side="input", refresh="qr", back_rot_dtype="f32", fwd_rot="f32"):
+                 side="input", refresh="qr", back_rot_dtype="f32", fwd_rot="f32",
+                 refresh_prod="f32"):
     hp = FoamHparams()
     hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay = lr, beta1, beta2, eps, weight_decay
     hp.pf, hp.tol = pf, tol
     hp.side = FOAM_SIDES[side] if isinstance(side, str) else int(side)
     hp.refresh = REFRESH_MODES[refresh] if isinstance(refresh, str) else int(refresh)
     hp.back_rot_dtype = _dtype_code(back_rot_dtype)
-    hp.fwd_rot = ROT_MODES[fwd_rot] if isinstance(fwd_rot, str) else int(fwd_rot)
+    hp.fwd_rot = _rot_code(fwd_rot)
+    hp.refresh_prod = _rot_code(refresh_prod)
     return hp
 
 

@@ -450,14 +450,44 @@ struct RotBufs {
   bf16_t* EL3 = nullptr;  // m x 3m' (SOAP)
   bf16_t* T3 = nullptr;   // n x 3m' (SOAP)
   int64_t ld3m = 0, ld3n = 0;
+  // bf16x3 refresh products (single-matrix calls): both operands' splits
+  bf16_t* P3a = nullptr;
+  bf16_t* P3b = nullptr;
+  int64_t ld3p = 0;
   int64_t ldm, ldn;  // padded leading dims for m- and n-long rows
 };
 
 // own_qr: the bases E, the QR input S, FOAM's refresh flag and the QR
 // workspace belong to this matrix; otherwise the caller points EL, ER, S and
 // flag into the shared, size-grouped QR area of a many-matrix call.
-void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool own_qr = true,
-               bool eigh = false, bool back_bf16 = false, bool fwd3 = false) {
+// Optional buffers of a SOAP / FOAM step, from its hyperparameters.
+struct CarveOpt {
+  bool eigh = false;       // FOAM's eigendecomposition refresh
+  bool back_bf16 = false;  // rotation back on bf16 MFMA
+  bool fwd3 = false;       // forward rotations as bf16x3
+  bool ref3 = false;       // refresh products as bf16x3
+};
+
+CarveOpt soap_opt(const mao_soap_hparams* hp) {
+  CarveOpt o;
+  o.back_bf16 = hp->back_rot_dtype == MAO_BF16;
+  o.fwd3 = hp->fwd_rot == MAO_ROT_BF16X3;
+  o.ref3 = hp->refresh_prod == MAO_ROT_BF16X3;
+  return o;
+}
+
+CarveOpt foam_opt(const mao_foam_hparams* hp) {
+  CarveOpt o;
+  o.eigh = hp->refresh == MAO_REFRESH_EIGH;
+  o.back_bf16 = hp->back_rot_dtype == MAO_BF16;
+  o.fwd3 = hp->fwd_rot == MAO_ROT_BF16X3;
+  o.ref3 = hp->refresh_prod == MAO_ROT_BF16X3;
+  return o;
+}
+
+void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool own_qr,
+               const CarveOpt& o) {
+  const bool eigh = o.eigh, back_bf16 = o.back_bf16, fwd3 = o.fwd3;
   R.ldm = ws_ld(m);
   R.ldn = ws_ld(n);
   const int big = std::max(m, n);
@@ -476,6 +506,11 @@ void carve_rot(Carver& c, int m, int n, bool soap, bool g_bf16, RotBufs& R, bool
   R.flag = (soap || !own_qr) ? nullptr : c.take<int>(4);
   if (own_qr) R.qr = carve_qr_work(c, big);
   if (own_qr && eigh) R.eigh = c.take<char>(eigh_work_stride(n));
+  if (own_qr && o.ref3) {
+    R.ld3p = ws_ld(3 * split_width(big));
+    R.P3a = c.take<bf16_t>((size_t)big * R.ld3p);
+    R.P3b = c.take<bf16_t>((size_t)big * R.ld3p);
+  }
   if (fwd3) {
     R.ld3m = ws_ld(3 * split_width(m));
     R.ld3n = ws_ld(3 * split_width(n));
@@ -631,6 +666,16 @@ mao_status nt3(int M, int N, int K, const bf16_t* A3, int64_t lda3, bool a_dup, 
   return gemm_add(gb, p, MAO_BF16, s);
 }
 
+// S = A B^T (k x k, fp32 operands and result) as bf16x3: A split into A3
+// ([hi | lo | hi]) and B into B3 ([hi | hi | lo]), k x 3k' each at ld3.
+mao_status nt3_split(int k, const float* A, int64_t lda, const float* B, int64_t ldb, float* S,
+                     int64_t ldS, bf16_t* A3, bf16_t* B3, int64_t ld3, hipStream_t s,
+                     GemmBatch* gb) {
+  MAO_TRY(split3_bf16(view((void*)A, lda), MAO_F32, k, k, view(A3, ld3), kSplitA, s));
+  MAO_TRY(split3_bf16(view((void*)B, ldb), MAO_F32, k, k, view(B3, ld3), kSplitB, s));
+  return nt3(k, k, k, A3, ld3, false, B3, ld3, S, ldS, nullptr, 0, s, gb);
+}
+
 // F <- beta F + (1 - beta) X X^T (SYRK in place, fp32 F; X fp32 or bf16:
 // bf16 products are exact in fp32, so both accumulate alike in fp32)
 mao_status syrk_ema(int N, int K, const void* X, int64_t ldx, float beta, float* F, int64_t ldf,
@@ -716,8 +761,7 @@ size_t soap_workspace_size(int64_t rows, int64_t cols, const mao_soap_hparams* h
   if (!hp || rows < 1 || cols < 1) return 0;
   Carver c(nullptr);
   RotBufs R;
-  carve_rot(c, (int)rows, (int)cols, true, true, R, true, false, hp->back_rot_dtype == MAO_BF16,
-            hp->fwd_rot == MAO_ROT_BF16X3);
+  carve_rot(c, (int)rows, (int)cols, true, true, R, true, soap_opt(hp));
   return c.used + 256;
 }
 
@@ -753,6 +797,8 @@ mao_status check_soap_hp(const mao_soap_hparams* hp) {
   if (!dtype_ok(hp->back_rot_dtype)) MAO_FAIL(MAO_E_DTYPE, "back_rot_dtype=%d", hp->back_rot_dtype);
   if (hp->fwd_rot != MAO_ROT_F32 && hp->fwd_rot != MAO_ROT_BF16X3)
     MAO_FAIL(MAO_E_HPARAM, "fwd_rot=%d", hp->fwd_rot);
+  if (hp->refresh_prod != MAO_ROT_F32 && hp->refresh_prod != MAO_ROT_BF16X3)
+    MAO_FAIL(MAO_E_HPARAM, "refresh_prod=%d", hp->refresh_prod);
   return MAO_OK;
 }
 
@@ -885,6 +931,10 @@ mao_status check_foam_hp(const mao_foam_hparams* hp) {
   if (!dtype_ok(hp->back_rot_dtype)) MAO_FAIL(MAO_E_DTYPE, "back_rot_dtype=%d", hp->back_rot_dtype);
   if (hp->fwd_rot != MAO_ROT_F32 && hp->fwd_rot != MAO_ROT_BF16X3)
     MAO_FAIL(MAO_E_HPARAM, "fwd_rot=%d", hp->fwd_rot);
+  if (hp->refresh_prod != MAO_ROT_F32 && hp->refresh_prod != MAO_ROT_BF16X3)
+    MAO_FAIL(MAO_E_HPARAM, "refresh_prod=%d", hp->refresh_prod);
+  if (hp->refresh_prod == MAO_ROT_BF16X3 && hp->refresh == MAO_REFRESH_EIGH)
+    MAO_FAIL(MAO_E_UNSUPPORTED, "bf16x3 criterion products with the eigendecomposition refresh");
   return MAO_OK;
 }
 
@@ -953,9 +1003,16 @@ mao_status foam_pre(const mao_mat& W, const mao_mat& G, const mao_foam_state* st
 // S = E_R R (the QR input; stage 0), D = S E_R = Q^T R Q (stage 1) and the
 // off-diagonal test that sets the refresh flag (stage 2); on other steps
 // stage 2 clears the flag.
+// With A3 / B3 (k x 3k' at ld3) the two products run as bf16x3.
 mao_status foam_criterion(int k, const mao_foam_state* st, RotBufs& R, int64_t t,
-                          const mao_foam_hparams* hp, int stage, GemmBatch* gb, hipStream_t s) {
+                          const mao_foam_hparams* hp, int stage, GemmBatch* gb, hipStream_t s,
+                          bf16_t* A3 = nullptr, bf16_t* B3 = nullptr, int64_t ld3 = 0) {
   const bool check = foam_checks(hp, t);
+  if (check && A3 && stage == 0)
+    return nt3_split(k, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, R.ldn, A3, B3, ld3,
+                     s, gb);
+  if (check && A3 && stage == 1)
+    return nt3_split(k, R.S, R.ldn, R.ER, R.ldn, R.D, R.ldn, A3, B3, ld3, s, gb);
   if (stage == 0)
     return check ? nt32(k, k, k, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, R.ldn,
                         nullptr, 0, s, nullptr, gb)
@@ -1081,6 +1138,11 @@ struct QrGroup {
   char* work = nullptr;
   char* eigh = nullptr;    // FOAM's eigendecomposition refresh: per-job workspaces
   int64_t ld = 0, sz = 0;  // leading dimension and per-job stride of S and E
+  // bf16x3 refresh products: per-job operand splits (one region shared by
+  // every group, so the groups' products run one group at a time)
+  bf16_t* P3a = nullptr;
+  bf16_t* P3b = nullptr;
+  int64_t ld3 = 0, sz3 = 0;
 };
 
 // Carve per-matrix buffers, then the size groups (sorted by size): S and E of
@@ -1091,14 +1153,14 @@ struct QrGroup {
 // gb: receives the pointer table of the grouped products (at most two
 // products per matrix in a phase, five pointers each).
 void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<RotBufs>& R,
-                std::vector<QrGroup>& groups, bool fout = false, GemmBatch* gb = nullptr,
-                bool eigh = false, bool back_bf16 = false, bool fwd3 = false) {
+                std::vector<QrGroup>& groups, bool fout, GemmBatch* gb, const CarveOpt& o) {
+  const bool eigh = o.eigh;
   R.assign(count, RotBufs{});
   std::vector<std::pair<int, QrJobRef>> all;
   for (int i = 0; i < count; ++i) {
     const int m = (int)W[i].rows, n = (int)W[i].cols;
     const bool t = !soap && fout;
-    carve_rot(c, t ? n : m, t ? m : n, soap, true, R[i], false, false, back_bf16, fwd3);
+    carve_rot(c, t ? n : m, t ? m : n, soap, true, R[i], false, o);
     if (soap) all.push_back({m, QrJobRef{i, 0}});
     all.push_back({t ? m : n, QrJobRef{i, 1}});
   }
@@ -1137,6 +1199,20 @@ void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<R
       }
     }
   }
+  if (o.ref3) {
+    size_t most = 0;
+    for (QrGroup& g : groups) {
+      g.ld3 = ws_ld(3 * split_width(g.n));
+      g.sz3 = round_up((int64_t)g.n * g.ld3, 64);
+      most = std::max(most, g.jobs.size() * (size_t)g.sz3);
+    }
+    bf16_t* a = c.take<bf16_t>(most);
+    bf16_t* b = c.take<bf16_t>(most);
+    for (QrGroup& g : groups) {
+      g.P3a = a;
+      g.P3b = b;
+    }
+  }
   const int64_t cap = (int64_t)2 * 5 * count;
   const void** table = c.take<const void*>((size_t)cap);
   if (gb) {
@@ -1145,12 +1221,11 @@ void carve_many(Carver& c, int count, const mao_mat* W, bool soap, std::vector<R
   }
 }
 
-size_t many_ws(int count, const mao_mat* W, bool soap, bool fout = false, bool eigh = false,
-               bool back_bf16 = false, bool fwd3 = false) {
+size_t many_ws(int count, const mao_mat* W, bool soap, bool fout, const CarveOpt& o) {
   Carver c(nullptr);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
-  carve_many(c, count, W, soap, R, groups, fout, nullptr, eigh, back_bf16, fwd3);
+  carve_many(c, count, W, soap, R, groups, fout, nullptr, o);
   return c.used + 256;
 }
 
@@ -1181,15 +1256,22 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
   MAO_TRY(check_workspace(workspace, workspace_bytes, soap_workspace_size(m, n, hp)));
   Carver c(workspace);
   RotBufs R;
-  carve_rot(c, m, n, true, true, R, true, false, hp->back_rot_dtype == MAO_BF16,
-            hp->fwd_rot == MAO_ROT_BF16X3);
+  carve_rot(c, m, n, true, true, R, true, soap_opt(hp));
   MAO_TRY(soap_pre(W, G, st, R, hp, nullptr, s));
   // 3b. refresh: Q <- qr(F Q); S = (F Q)^T = Q^T F stored row-major
   if (soap_refresh(hp, t)) {
     const int64_t ldS = ws_ld(std::max(m, n));
-    MAO_TRY(nt32(m, m, m, R.EL, R.ldm, (const float*)st->L.data, st->L.ld, R.S, ldS, nullptr, 0, s));
+    if (R.P3a)
+      MAO_TRY(nt3_split(m, R.EL, R.ldm, (const float*)st->L.data, st->L.ld, R.S, ldS, R.P3a,
+                        R.P3b, R.ld3p, s, nullptr));
+    else
+      MAO_TRY(nt32(m, m, m, R.EL, R.ldm, (const float*)st->L.data, st->L.ld, R.S, ldS, nullptr, 0, s));
     MAO_TRY(qr_core(R.S, ldS, m, R.EL, R.ldm, (float*)st->QL.data, st->QL.ld, R.qr, nullptr, s));
-    MAO_TRY(nt32(n, n, n, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, ldS, nullptr, 0, s));
+    if (R.P3a)
+      MAO_TRY(nt3_split(n, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, ldS, R.P3a,
+                        R.P3b, R.ld3p, s, nullptr));
+    else
+      MAO_TRY(nt32(n, n, n, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, ldS, nullptr, 0, s));
     MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, nullptr, s));
   }
   for (int stage = 0; stage < kSoapPostStages; ++stage)
@@ -1201,8 +1283,7 @@ size_t soap_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_
   if (!hp || !W || count < 1 || count > kMaxMany) return 0;
   for (int i = 0; i < count; ++i)
     if (W[i].rows < 1 || W[i].cols < 1) return 0;
-  return many_ws(count, W, true, false, false, hp->back_rot_dtype == MAO_BF16,
-                 hp->fwd_rot == MAO_ROT_BF16X3);
+  return many_ws(count, W, true, false, soap_opt(hp));
 }
 
 mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
@@ -1216,25 +1297,31 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   for (int i = 0; i < count; ++i)
     MAO_TRY(validate_soap(W[i], G[i], &st[i], t, update_out ? update_out[i] : nullptr, rr));
   MAO_TRY(check_no_overlap(rr));
-  const bool bb = hp->back_rot_dtype == MAO_BF16, f3 = hp->fwd_rot == MAO_ROT_BF16X3;
-  MAO_TRY(check_workspace(workspace, workspace_bytes,
-                          many_ws(count, W, true, false, false, bb, f3)));
+  const CarveOpt o = soap_opt(hp);
+  MAO_TRY(check_workspace(workspace, workspace_bytes, many_ws(count, W, true, false, o)));
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
   GemmBatch gb;
-  carve_many(c, count, W, true, R, groups, false, &gb, false, bb, f3);
+  carve_many(c, count, W, true, R, groups, false, &gb, o);
   for (int i = 0; i < count; ++i) MAO_TRY(soap_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
   MAO_TRY(gemm_flush(gb, s));
   if (soap_refresh(hp, t)) {
     // the QR inputs S = E F of every job, grouped, before the batched QRs
-    for (QrGroup& g : groups)
+    for (QrGroup& g : groups) {
       for (int k = 0; k < (int)g.jobs.size(); ++k) {
         const int i = g.jobs[k].mat;
         const mao_mat& F = g.jobs[k].side == 0 ? st[i].L : st[i].R;
-        MAO_TRY(nt32(g.n, g.n, g.n, g.E + k * g.sz, g.ld, (const float*)F.data, F.ld,
-                     g.S + k * g.sz, g.ld, nullptr, 0, s, nullptr, &gb));
+        if (o.ref3)
+          MAO_TRY(nt3_split(g.n, g.E + k * g.sz, g.ld, (const float*)F.data, F.ld, g.S + k * g.sz,
+                            g.ld, g.P3a + k * g.sz3, g.P3b + k * g.sz3, g.ld3, s, &gb));
+        else
+          MAO_TRY(nt32(g.n, g.n, g.n, g.E + k * g.sz, g.ld, (const float*)F.data, F.ld,
+                       g.S + k * g.sz, g.ld, nullptr, 0, s, nullptr, &gb));
       }
+      // bf16x3: the groups share one region of operand splits
+      if (o.ref3) MAO_TRY(gemm_flush(gb, s));
+    }
     MAO_TRY(gemm_flush(gb, s));
     for (QrGroup& g : groups) {
       const int nj = (int)g.jobs.size();
@@ -1279,7 +1366,7 @@ size_t foam_workspace_size(int64_t rows, int64_t cols, const mao_foam_hparams* h
   RotBufs R;
   const bool out = foam_out(hp);
   carve_rot(c, (int)(out ? cols : rows), (int)(out ? rows : cols), false, true, R, true,
-            foam_eigh(hp), hp->back_rot_dtype == MAO_BF16, hp->fwd_rot == MAO_ROT_BF16X3);
+            foam_opt(hp));
   return c.used + 256;
 }
 
@@ -1297,11 +1384,10 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
   MAO_TRY(check_workspace(workspace, workspace_bytes, foam_workspace_size(m, n, hp)));
   Carver c(workspace);
   RotBufs R;
-  carve_rot(c, out ? n : m, out ? m : n, false, true, R, true, foam_eigh(hp),
-            hp->back_rot_dtype == MAO_BF16, hp->fwd_rot == MAO_ROT_BF16X3);
+  carve_rot(c, out ? n : m, out ? m : n, false, true, R, true, foam_opt(hp));
   MAO_TRY(foam_pre(W, G, st, R, hp, nullptr, s));
   for (int stage = 0; stage < 3; ++stage)
-    MAO_TRY(foam_criterion(k, st, R, t, hp, stage, nullptr, s));
+    MAO_TRY(foam_criterion(k, st, R, t, hp, stage, nullptr, s, R.P3a, R.P3b, R.ld3p));
   if (foam_checks(hp, t) && foam_eigh(hp)) {
     // D = Q^T R Q from the criterion, diagonalised in the current basis
     EighJob job;
@@ -1332,8 +1418,7 @@ size_t foam_step_many_workspace_size(int32_t count, const mao_mat* W, const mao_
     if (W[i].rows < 1 || W[i].cols < 1) return 0;
     if (foam_eigh(hp) && (foam_out(hp) ? W[i].rows : W[i].cols) > kEighMaxN) return 0;
   }
-  return many_ws(count, W, false, foam_out(hp), foam_eigh(hp), hp->back_rot_dtype == MAO_BF16,
-                 hp->fwd_rot == MAO_ROT_BF16X3);
+  return many_ws(count, W, false, foam_out(hp), foam_opt(hp));
 }
 
 mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
@@ -1347,18 +1432,30 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
   for (int i = 0; i < count; ++i)
     MAO_TRY(validate_foam(W[i], G[i], &st[i], t, hp, update_out ? update_out[i] : nullptr, rr));
   MAO_TRY(check_no_overlap(rr));
-  const bool bb = hp->back_rot_dtype == MAO_BF16, f3 = hp->fwd_rot == MAO_ROT_BF16X3;
+  const CarveOpt o = foam_opt(hp);
   MAO_TRY(check_workspace(workspace, workspace_bytes,
-                          many_ws(count, W, false, foam_out(hp), foam_eigh(hp), bb, f3)));
+                          many_ws(count, W, false, foam_out(hp), o)));
   Carver c(workspace);
   std::vector<RotBufs> R;
   std::vector<QrGroup> groups;
   GemmBatch gb;
-  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb, foam_eigh(hp), bb, f3);
+  carve_many(c, count, W, false, R, groups, foam_out(hp), &gb, o);
   // phases: every matrix's products of a phase go out as grouped launches
   for (int i = 0; i < count; ++i) MAO_TRY(foam_pre(W[i], G[i], &st[i], R[i], hp, &gb, s));
   MAO_TRY(gemm_flush(gb, s));
   for (int stage = 0; stage < 3; ++stage) {
+    if (o.ref3 && stage < 2 && foam_checks(hp, t)) {
+      // bf16x3: the groups share one region of operand splits
+      for (QrGroup& g : groups) {
+        for (int k = 0; k < (int)g.jobs.size(); ++k) {
+          const int i = g.jobs[k].mat;
+          MAO_TRY(foam_criterion(g.n, &st[i], R[i], t, hp, stage, &gb, s, g.P3a + k * g.sz3,
+                                 g.P3b + k * g.sz3, g.ld3));
+        }
+        MAO_TRY(gemm_flush(gb, s));
+      }
+      continue;
+    }
     for (int i = 0; i < count; ++i)
       MAO_TRY(foam_criterion((int)(foam_out(hp) ? W[i].rows : W[i].cols), &st[i], R[i], t, hp,
                              stage, &gb, s));

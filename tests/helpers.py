@@ -69,3 +69,10 @@ def w_bound(w_expect, w_prev, lr_term):
 
 def log(msg: str):
     print(msg, flush=True)
+
+
+# Relative accuracy of one product: fp32 MFMA, or bf16x3 on split operands
+# (x = hi + lo in bf16; the dropped lo*lo term and the residual of each split
+# are each below 2^-18 of a product term).
+PRODUCT_EPS = {"f32": 2.0 ** -24, "bf16x3": 3 * 2.0 ** -18}
+

@@ -19,6 +19,7 @@ import matrix_aware_optimizers_amd as mao
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mao.h")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_LAYOUT, E_ALIAS, E_HPARAM, E_WORKSPACE = 0, 1, 2, 3, 4, 5, 6, 7
+E_UNSUPPORTED = 9
 FAKE = 0x7F0000000000  # 256-aligned, never dereferenced
 
 
@@ -238,11 +239,21 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
                          ws, 1 << 30, None, None) == E_HPARAM
     assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(mao.foam_hparams(fwd_rot=-1)),
                          ws, 1 << 30, None, None) == E_HPARAM
-    # the split operands of the bf16x3 rotations take workspace of their own
+    assert lib.soap_step(W, G, ctypes.byref(st), 1, ctypes.byref(mao.soap_hparams(refresh_prod=3)),
+                         ws, 1 << 30, None, None) == E_HPARAM
+    assert lib.foam_step(W, G, ctypes.byref(fst), 1,
+                         ctypes.byref(mao.foam_hparams(refresh_prod=-2)), ws, 1 << 30, None,
+                         None) == E_HPARAM
+    # bf16x3 criterion products feed only the QR refresh
+    assert lib.foam_step(W, G, ctypes.byref(fst), 1,
+                         ctypes.byref(mao.foam_hparams(refresh="eigh", refresh_prod="bf16x3")),
+                         ws, 1 << 30, None, None) == E_UNSUPPORTED
+    # the split operands of the bf16x3 products take workspace of their own
     for f in ("soap_workspace_size", "foam_workspace_size"):
         hp_of = mao.soap_hparams if f.startswith("soap") else mao.foam_hparams
-        assert (getattr(lib, f)(m, n, ctypes.byref(hp_of(fwd_rot="bf16x3")))
-                > getattr(lib, f)(m, n, ctypes.byref(hp_of())))
+        base = getattr(lib, f)(m, n, ctypes.byref(hp_of()))
+        for kw in ({"fwd_rot": "bf16x3"}, {"refresh_prod": "bf16x3"}):
+            assert getattr(lib, f)(m, n, ctypes.byref(hp_of(**kw))) > base
     assert lib.foam_step(W, G, ctypes.byref(fst), 1, ctypes.byref(mao.foam_hparams(side=2)), ws,
                          fneed, None, None) == E_HPARAM
     # the output side keeps m x m factors: the n x n state is the wrong shape
