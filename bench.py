@@ -15,7 +15,10 @@ instrumentation), the dominant kernel's roofline (the Newton-Schulz
 contraction, from HIP events around every launch of a second region of K
 steps), the fp64 CPU oracle's rate on a bounded sample of the workload's own
 matrices, and -- under "soap8b" -- the same 8B layer under SOAP (steps/s and
-the rate of its fp32 contractions against the fp32 and bf16 peaks).
+the rate of its contractions against the fp32 and bf16 peaks). SOAP and FOAM
+workloads run their fp32-accurate products (forward rotations, power-
+iteration and criterion products) as bf16x3 by default (--fwd,
+--refresh-prod) and the rotation back on bf16 MFMA (--back).
 
 Other workloads (--workload): moe (128-expert bank, batched Muon+), c1muon /
 c1soap (256x512 fp32 Muon and SOAP), soap8b (the 8B layer under SOAP),
@@ -523,12 +526,15 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
 
 def soap8b_summary(args):
     """The 8B layer under SOAP (soap_step_many over the five matrices, refresh
-    every step, bf16 W and G, fp32 state, rotation back in bf16): steps/s from
-    a timed region without instrumentation, and the contraction split from an
-    instrumented step. The forward rotations, power-iteration products and the
-    QR's updates are fp32 MFMA work, so their rate is given against both the
-    fp32 and the bf16 dense peaks; the bf16 products (factor SYRKs of the bf16
-    gradient, rotation back) against the bf16 peak."""
+    every step, bf16 W and G, fp32 state, rotation back in bf16, forward
+    rotations and power-iteration products as bf16x3 unless --fwd /
+    --refresh-prod say f32): steps/s from a timed region without
+    instrumentation, and the contraction split from an instrumented step.
+    fp32 MFMA work (the QR's updates and projections, and any fp32 rotation
+    or product) is given against both the fp32 and the bf16 dense peaks; the
+    bf16 products (bf16x3 products counted at the three bf16 products they
+    execute, factor SYRKs of the bf16 gradient, rotation back) against the
+    bf16 peak."""
     import synth
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup = args.soap8b_steps, 2
@@ -637,10 +643,10 @@ def main():
                              "foam760m_output", "foam760m_eigh", "soap760m", "observe8b"])
     ap.add_argument("--back", default="bf16", choices=["f32", "bf16"],
                     help="precision of the rotation back of the SOAP / FOAM workloads")
-    ap.add_argument("--fwd", default="f32", choices=["f32", "bf16x3"],
+    ap.add_argument("--fwd", default="bf16x3", choices=["f32", "bf16x3"],
                     help="forward rotations of the SOAP / FOAM workloads: fp32 products, or "
                          "three bf16 products over hi/lo splits (fp32-accurate)")
-    ap.add_argument("--refresh-prod", default="f32", choices=["f32", "bf16x3"],
+    ap.add_argument("--refresh-prod", default="bf16x3", choices=["f32", "bf16x3"],
                     help="power-iteration products L Q / R Q of SOAP and the criterion products "
                          "of FOAM: fp32, or bf16x3")
     ap.add_argument("--no-cpu-baseline", action="store_true")

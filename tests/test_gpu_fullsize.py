@@ -13,6 +13,8 @@ the benchmark times (GPU).
 * FOAM on one GPT-2-760M layer at full size, t = 1 (criterion evaluated,
   basis refreshed), teacher-forced.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -212,6 +214,54 @@ def test_foam_full_size_gpt2_layer(gpu_lib):
             assert e < 1e-4
 
 
+
+def test_foam_gpt2_layer_many_benchmark_configuration(gpu_lib):
+    """GPT-2-760M layer 0 (QKV, O, FC, PROJ) through foam_step_many in the
+    benchmark's rotation configuration (forward rotations and criterion
+    products as bf16x3, rotation back on bf16 MFMA), criterion every second
+    step (pf = 2, tol = 0.1), six steps, teacher-forced from each matrix's t0:
+    rho against the oracle's on the GPU's state, the refreshed basis by its
+    defining properties, r and c to 1e-4, the update within the bf16 tolerance
+    (whole matrix and per 256 x 256 tile)."""
+    import torch
+    specs = [s for s in synth.specs("c5") if s.name.startswith("l0.")]
+    log("foam GPT-2 layer 0, foam_step_many, benchmark configuration, 6 steps")
+    Ws = [to_dev(synth.init_weight("c5", sp)) for sp in specs]
+    z = lambda r, c: torch.zeros((r, c), dtype=torch.float32, device="cuda")
+    sts = [{"M": z(sp.rows, sp.cols), "R": z(sp.cols, sp.cols),
+            "QR": torch.eye(sp.cols, dtype=torch.float32, device="cuda"),
+            "r": torch.zeros(sp.rows, device="cuda"), "c": torch.zeros(sp.cols, device="cuda"),
+            "aux": torch.zeros(4, device="cuda")} for sp in specs]
+    outs = [torch.empty((sp.rows, sp.cols), dtype=torch.float32, device="cuda") for sp in specs]
+    t0 = [math.ceil(max(sp.rows, sp.cols) / min(sp.rows, sp.cols)) + 2 for sp in specs]
+    kw = dict(pf=2, tol=0.1, back_rot_dtype="bf16", fwd_rot="bf16x3", refresh_prod="bf16x3")
+    host = lambda st: oracle.FoamState(*(to_host(st[k]) for k in ("M", "R", "QR", "r", "c")))
+    for t in range(1, 7):
+        prevs = {i: (host(sts[i]), to_host(Ws[i])) for i in range(len(specs)) if t >= t0[i]}
+        gs = [synth.gradient("c5", sp, t) for sp in specs]
+        gpu_lib.foam_step_many([(Ws[i], to_dev(gs[i]), sts[i]) for i in range(len(specs))], t,
+                               update_out=outs, **kw, **HP)
+        torch.cuda.synchronize()
+        for i, (prev, w_prev) in prevs.items():
+            sp, new, aux = specs[i], host(sts[i]), to_host(sts[i]["aux"])
+            g = gs[i].astype(np.float64)
+            _, ref, _, info = oracle.foam_step(w_prev, g, prev, t, pf=2, tol=0.1, **HP)
+            assert bool(aux[3]) == info["checked"]
+            if info["checked"]:
+                assert abs(aux[0] - info["rho"]) < 1e-4, (sp.name, t)
+                if bool(aux[1]):
+                    _check_refreshed_basis(new.QR, info["P"], f"{sp.name} t={t} QR")
+            _, ref2, upd, _ = oracle.foam_step(w_prev, g, prev, t, pf=2, tol=0.1,
+                                               q_override=new.QR, refresh_override=bool(aux[1]),
+                                               **HP)
+            got = to_host(outs[i])
+            eu, etu = rel(got, upd), tile_max_rel(got, upd)
+            er, ec = rel(new.r, ref2.r), rel(new.c, ref2.c)
+            log(f"  {sp.name} t={t}: update {eu:.2e} (tile {etu:.2e}) r {er:.2e} c {ec:.2e} "
+                f"rho {aux[0]:.3f} refresh {bool(aux[1])}")
+            assert eu < 2e-2 and etu < 2e-2 and er < 1e-4 and ec < 1e-4, (sp.name, t)
+
+
 # ---- SOAP on the 8B layer through the many-matrix call the benchmark times --
 
 SOAP8B_STEPS = 5
@@ -345,30 +395,65 @@ def test_soap8b_many_gate_refresh_from_a_moved_basis(soap8b_many_run):
     torch.cuda.empty_cache()
 
 
-def test_soap8b_many_bf16_back_rotation(gpu_lib):
-    """The benchmark's SOAP configuration of the 8B layer: soap_step_many with
-    the rotation back on bf16 MFMA. O and QKV stepped together to t = 4
-    (their first gated step), teacher-forced there: update within the bf16
-    tolerance (whole matrix and per 256 x 256 tile), V to 1e-4."""
+def _soap8b_o_qkv(gpu_lib, steps, gated, **opts):
+    """O and QKV of the 8B layer stepped together through soap_step_many with
+    the given rotation options; teacher-forced at the steps in ``gated``.
+    Returns {(name, t): (update error, tile max, V error)}."""
     import torch
-    log("soap 8B layer O + QKV, bf16 back rotation, 4 steps")
     specs = [s for s in synth.specs("c3") if s.name in ("o", "qkv")]
     Ws = [to_dev(bf16_round(synth.init_weight("c3", sp)), "bf16") for sp in specs]
     sts = [_soap_dev_state(sp.rows, sp.cols) for sp in specs]
     outs = [torch.empty((sp.rows, sp.cols), dtype=torch.float32, device="cuda") for sp in specs]
-    for t in range(1, 5):
-        if t == 4:
+    res = {}
+    for t in range(1, steps + 1):
+        if t in gated:
             prevs = [_host_state(_clone_state(x)) for x in sts]
             wps = [to_host(W) for W in Ws]
         gs = [bf16_round(synth.gradient("c3", sp, t)) for sp in specs]
         gpu_lib.soap_step_many([(Ws[i], to_dev(gs[i], "bf16"), sts[i]) for i in range(2)], t,
-                               update_out=outs, back_rot_dtype="bf16", **HP)
+                               update_out=outs, **opts, **HP)
         torch.cuda.synchronize()
-    for i, sp in enumerate(specs):
-        new = _host_state(sts[i])
-        _, ref, upd, _ = oracle.soap_step(wps[i], gs[i].astype(np.float64), prevs[i], 4,
-                                          refresh_every=0, q_override=(new.QL, new.QR), **HP)
-        got = to_host(outs[i])
-        eu, etu, ev = rel(got, upd), tile_max_rel(got, upd), rel(new.V, ref.V)
-        log(f"  {sp.name} t=4: update {eu:.2e} (tile {etu:.2e}) V {ev:.2e}")
-        assert eu < 2e-2 and etu < 2e-2 and ev < 1e-4
+        if t not in gated:
+            continue
+        for i, sp in enumerate(specs):
+            new = _host_state(sts[i])
+            g = gs[i].astype(np.float64)
+            _, ref, upd, _ = oracle.soap_step(wps[i], g, prevs[i], t, refresh_every=0,
+                                              q_override=(new.QL, new.QR), **HP)
+            assert rel(new.L, ref.L) < 1e-5 and rel(new.R, ref.R) < 1e-5
+            _check_refreshed_basis(new.QL, ref.L @ prevs[i].QL, f"{sp.name} t={t} QL")
+            _check_refreshed_basis(new.QR, ref.R @ prevs[i].QR, f"{sp.name} t={t} QR")
+            got = to_host(outs[i])
+            res[(sp.name, t)] = (rel(got, upd), tile_max_rel(got, upd), rel(new.V, ref.V))
+            log(f"  {sp.name} t={t}: update {res[(sp.name, t)][0]:.2e} "
+                f"(tile {res[(sp.name, t)][1]:.2e}) V {res[(sp.name, t)][2]:.2e}")
+    return res
+
+
+def test_soap8b_many_benchmark_configuration(gpu_lib):
+    """The benchmark's SOAP configuration of the 8B layer: soap_step_many with
+    the forward rotations and the power-iteration products as bf16x3 and the
+    rotation back on bf16 MFMA. O and QKV stepped together to t = 5,
+    teacher-forced at t = 4 and 5: the bases by their defining properties
+    against the oracle's product, the update within the bf16 tolerance (whole
+    matrix and per 256 x 256 tile), V to 1e-4."""
+    log("soap 8B layer O + QKV, benchmark configuration, 5 steps")
+    res = _soap8b_o_qkv(gpu_lib, 5, (4, 5), back_rot_dtype="bf16", fwd_rot="bf16x3",
+                        refresh_prod="bf16x3")
+    for (name, t), (eu, etu, ev) in res.items():
+        assert eu < 2e-2 and etu < 2e-2 and ev < 1e-4, (name, t)
+
+
+def test_soap8b_many_bf16x3_rotations_fp32_update(gpu_lib):
+    """bf16x3 forward rotations and refresh products with the rotation back
+    in fp32, at the 8B shapes: the update to 1e-4 (and per tile to 1e-3) from
+    t0 + 1 = 5, the first full-rank step t0 = 4 within the bf16-MFMA
+    tolerance; V to 1e-4 at both."""
+    log("soap 8B layer O + QKV, bf16x3 rotations, fp32 rotation back, 5 steps")
+    res = _soap8b_o_qkv(gpu_lib, 5, (4, 5), fwd_rot="bf16x3", refresh_prod="bf16x3")
+    for (name, t), (eu, etu, ev) in res.items():
+        assert ev < 1e-4, (name, t)
+        if t == 5:
+            assert eu < 1e-4 and etu < 1e-3, (name, t)
+        else:
+            assert eu < 2e-2, (name, t)
