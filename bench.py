@@ -502,7 +502,7 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
                for k, v in tim.items() if v[1] > 0}
     # the roofline covers the fp32 contractions (rotations, power-iteration
     # products, QR updates) against the fp32 peak; bf16 ones are listed apart
-    f32_tags = [k for k in ("other", "qr") if k in tim]
+    f32_tags = [k for k in ("other", "qr", "qr_proj", "qr_fused") if k in tim]
     gemm_ms = sum(tim[k][0] for k in f32_tags)
     gemm_fl = sum(tim[k][2] for k in f32_tags)
     achieved = gemm_fl / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
@@ -547,11 +547,14 @@ def soap8b_summary(args):
            "back_rotation": "bf16", "forward_rotation": args.fwd,
            "refresh_products": args.refresh_prod}
     for tag, name in (("other", "rotations_and_products"), ("qr", "qr_updates"),
-                      ("other_bf16", "bf16_products")):
+                      ("qr_proj", "qr_projections"), ("qr_fused", "qr_fused_updates"),
+                      ("qr_panel", "qr_panels"), ("other_bf16", "bf16_products")):
         if tag in k:
             tf = k[tag]["tflops"]
-            out[name] = {"ms_per_step": k[tag]["ms_total"] / line["instrumented_steps"],
-                         "tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
+            out[name] = {"ms_per_step": k[tag]["ms_total"] / line["instrumented_steps"]}
+            if tag == "qr_panel":  # latency-bound factorisations: time only
+                continue
+            out[name].update({"tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS})
             if tag != "other_bf16":
                 out[name]["frac_fp32_peak"] = tf / PEAK_F32_TFLOPS
     return out

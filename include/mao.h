@@ -577,8 +577,10 @@ MAO_API mao_status mao_basis_age(const float* aux, float* age, void* stream);
  * mao_timing_enable -- when on != 0, every contraction launch made by the
  * library is bracketed by two HIP events recorded on its stream, tagged by
  * what it computes (0: Newton-Schulz Gram X X^T, 1: Newton-Schulz A A,
- * 2: Newton-Schulz B X, 3: other contractions on fp32 inputs, 4: QR updates,
- * 5: other contractions on bf16 inputs) with its
+ * 2: Newton-Schulz B X, 3: other contractions on fp32 inputs, 4: QR rank
+ * updates, 5: other contractions on bf16 inputs, 6: QR projections onto a
+ * panel's vectors, 7: QR fused update-and-projection, 8: QR panel
+ * factorisations, counted at zero flops) with its
  * algorithmic flop count (symmetric products at half cost). Off by default;
  * this is the only host-side state the library keeps, and it exists for
  * benchmarking only.

@@ -472,7 +472,8 @@ def basis_age(aux, age):
     _check(load().mao_basis_age(_ptr(aux), _ptr(age), _stream()), "mao_basis_age")
 
 
-TIMING_TAGS = ("ns_gram", "ns_square", "ns_apply", "other", "qr", "other_bf16")
+TIMING_TAGS = ("ns_gram", "ns_square", "ns_apply", "other", "qr", "other_bf16", "qr_proj",
+               "qr_fused", "qr_panel")
 
 
 def timing_enable(on: bool = True):

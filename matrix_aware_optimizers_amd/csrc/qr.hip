@@ -746,7 +746,7 @@ mao_status skinny_product(int M, int nb, int K, const float* A, int64_t lda, int
     p1.sD = sW;
     p1.pred = pred;
     p1.spred = spred;
-    return launch_gemm(MAO_F32, &p1, 1, stream, TAG_QR);
+    return launch_gemm(MAO_F32, &p1, 1, stream, TAG_QR_PROJ);
   }
   GemmProblem pr[KSPLIT];
   const int64_t stride = (int64_t)M * NB;
@@ -761,7 +761,7 @@ mao_status skinny_product(int M, int nb, int K, const float* A, int64_t lda, int
     pr[q].pred = pred;
     pr[q].spred = spred;
   }
-  MAO_TRY(launch_gemm(MAO_F32, pr, nparts, stream, TAG_QR));
+  MAO_TRY(launch_gemm(MAO_F32, pr, nparts, stream, TAG_QR_PROJ));
   const int64_t count = (int64_t)M * NB;
   const int blocks = (int)std::min<int64_t>(1024, (count + 255) / 256);
   hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks, njob), dim3(256), 0, stream, W, parts, stride,
@@ -771,6 +771,15 @@ mao_status skinny_product(int M, int nb, int K, const float* A, int64_t lda, int
 }
 
 int panels(int n) { return (n + NB - 1) / NB; }
+
+// Column splits of a fused panel update over an M x L block: enough
+// workgroups to give every CU about two, while each split keeps at least four
+// 64-column chunks.
+int fused_splits(int M, int L, int njob) {
+  const int strips = (M + NB - 1) / NB, chunks = (L + NB - 1) / NB;
+  const int want = (512 + njob * strips - 1) / (njob * strips);
+  return std::max(1, std::min({kQrFusedMaxSplits, want, chunks / 4}));
+}
 int max_groups(int n) { return (n + TPB - 1) / TPB; }
 
 int64_t vstore_floats(int n) {
@@ -799,8 +808,10 @@ QrWork carve_qr_work(Carver& c, int n) {
   w.vstore = c.take<float>(vstore_floats(n));
   w.zo = c.take<float>(zo_floats(n));
   w.zf = c.take<float>((size_t)n * NB);
+  w.zf2 = c.take<float>((size_t)n * NB);
   w.wbuf = c.take<float>((size_t)n * NB);
-  w.wparts = c.take<float>((size_t)KSPLIT * n * NB);
+  // split-K partials of the projections, or two regions of fused-update slices
+  w.wparts = c.take<float>((size_t)std::max(KSPLIT, 2 * kQrFusedMaxSplits) * n * NB);
   w.sign = c.take<float>(n);
   w.part = c.take<float>((size_t)2 * G * NB);
   w.dg = c.take<float>(2 * NB);
@@ -875,10 +886,46 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
     zoff += round_up((int64_t)len * NB, 64);
   }
 
+  // Factorisation with one panel of look-ahead. W_{p-1} is the projection of
+  // panel p-1's trailing rows onto its vectors. Before panel p is factored,
+  // only its own rows take panel p-1's update; the rest of the trailing rows
+  // take it afterwards in one fused pass that also projects them onto panel
+  // p's vectors (W_p). Only columns >= j0 are updated: the R block left of
+  // them is never read again (the basis comes from the vectors alone). V T^T
+  // of consecutive panels alternate between zf and zf2; W alternates between
+  // the two slice regions of wparts (wbuf for the first panel's plain
+  // projection).
   const int G = max_groups(n);
   const int per = jobs_per_launch(G);
+  const int64_t wsl = (int64_t)n * NB;  // slice stride
+  float* wprev = w[0].wbuf;
+  int sprev = 1;
+  float* wnext = w[0].wparts;
   for (int p = 0; p < np; ++p) {
     const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
+    const int mt = n - j0 - nb;
+    float* zf_prev = ((p - 1) & 1) ? w[0].zf2 : w[0].zf;
+    if (p > 0) {
+      // panel p's rows take panel p-1's update (one 64-column chunk per workgroup)
+      QrFusedArgs fa;
+      fa.C = b.S + (int64_t)j0 * b.ldS + j0;
+      fa.ldC = b.ldS;
+      fa.sC = b.sS;
+      fa.W = wprev;
+      fa.sW = wsf;
+      fa.wslices_in = sprev;
+      fa.wslice = wsl;
+      fa.Z = zf_prev + (int64_t)NB * NB;  // V T^T rows of the columns >= j0
+      fa.sZ = wsf;
+      fa.M = nb;
+      fa.L = len;
+      fa.nb = NB;  // panel p-1 is a full panel
+      fa.nbn = 0;
+      fa.splits = (len + NB - 1) / NB;
+      fa.pred = b.pred;
+      fa.spred = b.spred;
+      MAO_TRY(qr_fused_update(fa, nj, stream));
+    }
     const int Gp = (len + TPB - 1) / TPB;
     for (int c0 = 0; c0 < nj; c0 += per) {
       const int cn = std::min(per, nj - c0);
@@ -896,7 +943,7 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
         a.nb = nb;
         a.V = wj.vstore + vo[p];
         a.ldV = round_up(len, 8);
-        a.Zf = wj.zf;
+        a.Zf = (p & 1) ? wj.zf2 : wj.zf;
         a.Zo = wj.zo + zo[p];
         a.sign = wj.sign;
         a.part = wj.part;
@@ -927,78 +974,149 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
         ca.pred = a.pred;
         ca.fail = wj.fail + p;
       }
+      void* ev = nullptr;
+      const bool timed = timing_on();
+      if (timed) timing_record_begin(stream, &ev);
       void* cargs[] = {&cb};
       MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_chol_kernel, dim3(Gp * cn),
                                                dim3(TPB), cargs, 0, stream));
       void* kargs[] = {&pb};
       MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_kernel, dim3(Gp * cn),
                                                dim3(TPB), kargs, 0, stream));
+      if (timed) timing_record_end(stream, ev, TAG_QR_PANEL, 0.0);
     }
-    const int mt = n - j0 - nb;
-    if (mt > 0) {
-      float* Strail = b.S + (int64_t)(j0 + nb) * b.ldS + j0;
-      // W = S_trail V^T   (mt x nb)
+    if (mt <= 0) continue;
+    float* Strail = b.S + (int64_t)(j0 + nb) * b.ldS + j0;
+    if (p == 0) {
+      // W_0 = S_trail V_0^T   (mt x nb)
       MAO_TRY(skinny_product(mt, nb, len, Strail, b.ldS, b.sS, w[0].vstore + vo[p], round_up(len, 8),
                              wsf, w[0].wbuf, w[0].wparts, wsf, nj, b.pred, b.spred, stream));
-      // S_trail -= W Zf^T  (mt x len)
-      GemmProblem p2 = gemm_problem(mt, len, nb, -1.f, w[0].wbuf, NB, w[0].zf, NB, 1.f, Strail,
-                                    b.ldS, Strail, b.ldS, GF_D_F32 | GF_C0_F32);
-      p2.batch = nj;
-      p2.sA = p2.sB = wsf;
-      p2.sC0 = p2.sD = b.sS;
-      p2.pred = b.pred;
-      p2.spred = b.spred;
-      MAO_TRY(launch_gemm(MAO_F32, &p2, 1, stream, TAG_QR));
+      continue;
     }
+    // the rest of the trailing rows: panel p-1's update, then W_p = S_trail V_p^T
+    QrFusedArgs fc;
+    fc.C = Strail;
+    fc.ldC = b.ldS;
+    fc.sC = b.sS;
+    fc.W = wprev + (int64_t)nb * NB;  // W_{p-1} rows of S rows >= j0 + nb
+    fc.sW = wsf;
+    fc.wslices_in = sprev;
+    fc.wslice = wsl;
+    fc.Z = zf_prev + (int64_t)NB * NB;
+    fc.sZ = wsf;
+    fc.Vn = w[0].vstore + vo[p];
+    fc.ldV = round_up(len, 8);
+    fc.sV = wsf;
+    fc.Wn = wnext;
+    fc.sWn = wsf;
+    fc.M = mt;
+    fc.L = len;
+    fc.nb = NB;
+    fc.nbn = nb;
+    fc.splits = fused_splits(mt, len, nj);
+    fc.pred = b.pred;
+    fc.spred = b.spred;
+    MAO_TRY(qr_fused_update(fc, nj, stream));
+    wprev = wnext;
+    sprev = fc.splits;
+    wnext = wnext == w[0].wparts ? w[0].wparts + kQrFusedMaxSplits * wsl : w[0].wparts;
   }
 
-  // explicit Q: E = Q^T, backward accumulation
+  // explicit Q: E = Q^T, backward accumulation. The last panel's projection
+  // is a plain product (into wbuf); every later one comes out of the previous
+  // panel's fused update as partial slices, in two regions of wparts used in
+  // turn.
   for (int j = 0; j < nj; ++j)
     MAO_TRY(fill_identity(view(b.E + j * b.sE, b.ldE), n, job_pred(j), stream));
-  for (int p = np - 1; p >= 0; --p) {
-    const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
+  float* wcur = w[0].wbuf;
+  int s_in = 1;
+  wnext = w[0].wparts;
+  {
+    const int p = np - 1, j0 = p * NB, len = n - j0, nb = std::min(NB, len);
     float* Esub = b.E + (int64_t)j0 * b.ldE + j0;
     MAO_TRY(skinny_product(len, nb, len, Esub, b.ldE, b.sE, w[0].vstore + vo[p], round_up(len, 8),
-                           wsf, w[0].wbuf, w[0].wparts, wsf, nj, b.pred, b.spred, stream));
-    GemmProblem p2 = gemm_problem(len, len, nb, -1.f, w[0].wbuf, NB, w[0].zo + zo[p], NB, 1.f,
+                           wsf, wcur, w[0].wparts, wsf, nj, b.pred, b.spred, stream));
+  }
+  for (int p = np - 1; p >= 1; --p) {
+    const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
+    const int pp = p - 1, lenn = n - pp * NB, nbn = std::min(NB, lenn);
+    QrFusedArgs fa;
+    fa.C = b.E + (int64_t)j0 * b.ldE + j0;
+    fa.ldC = b.ldE;
+    fa.sC = b.sE;
+    fa.sW = wsf;
+    fa.Z = w[0].zo + zo[p];
+    fa.sZ = wsf;
+    // panel pp's vectors start NB columns left of this block
+    fa.Vn = w[0].vstore + vo[pp] + NB;
+    fa.ldV = round_up(lenn, 8);
+    fa.sV = wsf;
+    fa.Wn = wnext + (int64_t)NB * NB;
+    fa.sWn = wsf;
+    fa.Wt = wnext;
+    fa.Vt = w[0].vstore + vo[pp];
+    fa.trows = NB;
+    fa.M = len;
+    fa.L = len;
+    fa.nb = nb;
+    fa.nbn = nbn;
+    fa.pred = b.pred;
+    fa.spred = b.spred;
+    fa.W = wcur;
+    fa.wslices_in = s_in;
+    fa.wslice = wsl;
+    fa.splits = fused_splits(len, len, nj);
+    MAO_TRY(qr_fused_update(fa, nj, stream));
+    wcur = wnext;
+    s_in = fa.splits;
+    wnext = wnext == w[0].wparts ? w[0].wparts + kQrFusedMaxSplits * wsl : w[0].wparts;
+  }
+  if (s_in > 1) {
+    const int64_t count = (int64_t)n * NB;
+    const int blocks = (int)std::min<int64_t>(1024, (count + 255) / 256);
+    hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks, nj), dim3(256), 0, stream, w[0].wbuf, wcur,
+                       wsl, s_in, count, wsf, b.pred, b.spred);
+    MAO_LAUNCH_CHECK();
+    wcur = w[0].wbuf;
+  }
+  {
+    // first block: column signs, and each job's Q written as the transposed copy
+    const int len = n, nb = std::min(NB, len);
+    float* Esub = b.E;
+    GemmProblem p2 = gemm_problem(len, len, nb, -1.f, wcur, NB, w[0].zo + zo[0], NB, 1.f,
                                   Esub, b.ldE, Esub, b.ldE, GF_D_F32 | GF_C0_F32);
     p2.batch = nj;
     p2.sA = p2.sB = wsf;
     p2.sC0 = p2.sD = b.sE;
     p2.pred = b.pred;
     p2.spred = b.spred;
-    if (p != 0) {
-      MAO_TRY(launch_gemm(MAO_F32, &p2, 1, stream, TAG_QR));
-      continue;
-    }
-    // last block: column signs, and each job's Q written as the transposed copy
     p2.row_scale = w[0].sign;
     p2.srs = wsf;
     bool anyq = false;
     for (int j = 0; j < nj; ++j) anyq = anyq || (b.Q && b.Q[j]);
     if (!anyq) {
       MAO_TRY(launch_gemm(MAO_F32, &p2, 1, stream, TAG_QR));
-      continue;
-    }
-    for (int c0 = 0; c0 < nj; c0 += kMaxProblems) {
-      const int cn = std::min(kMaxProblems, nj - c0);
-      GemmProblem pq[kMaxProblems];
-      for (int q = 0; q < cn; ++q) {
-        const int j = c0 + q;
-        pq[q] = p2;
-        pq[q].batch = 1;
-        pq[q].A = w[j].wbuf;
-        pq[q].B = w[j].zo + zo[p];
-        pq[q].C0 = pq[q].D = Esub + j * b.sE;
-        pq[q].row_scale = w[j].sign;
-        pq[q].pred = job_pred(j);
-        pq[q].spred = 0;
-        if (b.Q && b.Q[j]) {
-          pq[q].Dt = b.Q[j];
-          pq[q].lddt = b.ldQ[j];
+    } else {
+      for (int c0 = 0; c0 < nj; c0 += kMaxProblems) {
+        const int cn = std::min(kMaxProblems, nj - c0);
+        GemmProblem pq[kMaxProblems];
+        for (int q = 0; q < cn; ++q) {
+          const int j = c0 + q;
+          pq[q] = p2;
+          pq[q].batch = 1;
+          pq[q].A = wcur + j * wsf;
+          pq[q].B = w[j].zo + zo[0];
+          pq[q].C0 = pq[q].D = Esub + j * b.sE;
+          pq[q].row_scale = w[j].sign;
+          pq[q].pred = job_pred(j);
+          pq[q].spred = 0;
+          if (b.Q && b.Q[j]) {
+            pq[q].Dt = b.Q[j];
+            pq[q].lddt = b.ldQ[j];
+          }
         }
+        MAO_TRY(launch_gemm(MAO_F32, pq, cn, stream, TAG_QR));
       }
-      MAO_TRY(launch_gemm(MAO_F32, pq, cn, stream, TAG_QR));
     }
   }
 

@@ -11,7 +11,8 @@ constexpr int kQrThreads = 256; // positions per panel workgroup
 struct QrWork {
   float* vstore;     // packed V panels
   float* zo;         // packed V T panels (orgqr)
-  float* zf;         // one V T^T panel (n x 64)
+  float* zf;         // V T^T of the even panels (n x 64)
+  float* zf2;        // V T^T of the odd panels (the factorisation looks one panel ahead)
   float* wbuf;       // n x 64 intermediate
   float* wparts;     // 4 x n x 64 split-K partials of it
   float* sign;       // n
@@ -59,6 +60,40 @@ struct QrBatch {
   bool abort_barriers = false;
 };
 mao_status qr_core_batched(const QrBatch& b, hipStream_t stream);
+
+// Fused panel step (qr_update.hip), per job j (pointers advanced by j times
+// their stride): C (M x L, ld ldC) <- C - W Z^T with W (M x nb) the sum of
+// wslices_in slices wslice floats apart and Z (L x nb), both at leading
+// dimension 64; then, when nbn > 0, Wn (M x nbn, ld 64) = C Vn^T, the nbn
+// rows of Vn (ld ldV) spanning C's L columns, written as `splits` partial
+// slices (one per column range; wslice floats apart) whose sum is Wn
+// (splits <= kQrFusedMaxSplits; without the projection any count). With Wt != nullptr,
+// also Wt[c][i] = Vt[i][c] for c < trows in slice 0 and zero in the others
+// (ld 64; Vt at ld ldV and stride sV). Jobs whose predicate (pred[j spred])
+// is zero are skipped. nb, nbn <= 64.
+constexpr int kQrFusedMaxSplits = 4;
+struct QrFusedArgs {
+  float* C = nullptr;
+  int64_t ldC = 0, sC = 0;
+  const float* W = nullptr;
+  int64_t sW = 0;
+  const float* Z = nullptr;
+  int64_t sZ = 0;
+  const float* Vn = nullptr;
+  int64_t ldV = 0, sV = 0;
+  float* Wn = nullptr;
+  int64_t sWn = 0;
+  float* Wt = nullptr;
+  const float* Vt = nullptr;
+  int trows = 0;
+  int M = 0, L = 0, nb = 0, nbn = 0;
+  int splits = 1, wslices_in = 1;
+  int64_t wslice = 0;
+  const int* pred = nullptr;
+  int64_t spred = 0;
+  int strips = 0;  // set by qr_fused_update
+};
+mao_status qr_fused_update(const QrFusedArgs& a, int njob, hipStream_t stream);
 
 // Householder QR of P given column-major in S (S[j][i] = P[i][j], n x n,
 // leading dimension ldS); S is overwritten. Writes E = Q^T (row-major, ldE)

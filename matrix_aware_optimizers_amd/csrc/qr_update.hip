@@ -1,0 +1,233 @@
+// Fused panel step of the blocked Householder QR: one pass over the block
+// that a 64-column panel updates applies the panel's reflector and projects
+// the updated rows onto the next panel's Householder vectors,
+//
+//   C <- C - W Z^T              (C: M x L, W: M x nb, Z: L x nb)
+//   Wn = C[:, 0:L] Vn^T         (Vn: nbn vectors as rows over C's columns)
+//
+// so the projection the next panel needs costs no second read of C (the
+// separate route reads C once for the projection and once more, with the
+// write, for the update: 12 bytes per element and panel against 8 here).
+//
+// Workgroup = 64 rows of C ("strip") and one of S contiguous column ranges
+// ("split"; S raises the workgroup count when a panel's block has few
+// strips), 4 wavefronts in 2 x 2; the workgroup walks its columns in chunks
+// of 64. Per chunk: C's 64 x 64 block comes in by 16-byte loads into LDS,
+// the update (v_mfma_f32_32x32x2f32, W's fragment held in registers for the
+// whole strip, Z's chunk in LDS) turns it into D in place, D leaves by
+// 16-byte stores, and the projection of D onto the chunk of Vn (both in LDS)
+// accumulates in registers. The next chunk's C, Z and Vn are loaded into
+// registers while the current chunk's products run. Split s writes its
+// partial projection into slice s of Wn; the consumer sums the slices (the
+// next panel's call when it loads W, or a summing pass).
+//
+// Optionally one more workgroup per job writes the first rows of Wn that
+// come from identity rows of the next block (the explicit-Q accumulation:
+// rows of E above the current panel are still rows of I, so their
+// projection is a transposed copy of the vectors): Wt[c][i] = Vt[i][c] in
+// slice 0, zero in the other slices.
+#include "gemm.hpp"
+#include "qr.hpp"
+
+namespace mao {
+
+namespace {
+
+constexpr int FR = 64;       // rows per strip
+constexpr int FC = 64;       // columns per chunk
+constexpr int FK = 64;       // panel width (NB)
+constexpr int LDF = FK + 4;  // LDS row pitch (floats)
+
+__device__ __forceinline__ float4 ld4(const float* p, int k, int lim) {
+  if (k + 4 <= lim) return *(const float4*)(p + k);
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (k + e < lim) ? p[k + e] : 0.f;
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float comp(const float4& a, int e) {
+  return e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
+}
+
+__global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
+  __shared__ __attribute__((aligned(16))) float Zs[FC * LDF];
+  __shared__ __attribute__((aligned(16))) float Vs[FK * LDF];
+  __shared__ __attribute__((aligned(16))) float Ds[FR * LDF];  // C, then D, in place
+
+  const int job = blockIdx.y;
+  if (a.pred != nullptr && a.pred[job * a.spred] == 0) return;
+  const int t = threadIdx.x;
+
+  if ((int)blockIdx.x == a.strips * a.splits) {
+    // identity rows: Wt[c][i] = Vt[i][c] (slice 0), zero in later slices
+    const float* Vt = a.Vt + job * a.sV;
+    float* Wt = a.Wt + job * a.sWn;
+    for (int q = t; q < a.trows * FK; q += 256) {
+      const int c = q / FK, i = q % FK;
+      if (i >= a.nbn) continue;
+      Wt[(int64_t)c * FK + i] = Vt[(int64_t)i * a.ldV + c];
+      for (int sl = 1; sl < a.splits; ++sl) Wt[sl * a.wslice + (int64_t)c * FK + i] = 0.f;
+    }
+    return;
+  }
+
+  const int strip = blockIdx.x % a.strips, split = blockIdx.x / a.strips;
+  const int r0 = strip * FR;
+  const int M = a.M, L = a.L, nb = a.nb, nbn = a.nbn;
+  const int nchunks = (L + FC - 1) / FC;
+  const int per = (nchunks + a.splits - 1) / a.splits;
+  const int ch0 = split * per, ch1 = min(nchunks, ch0 + per);
+  float* C = a.C + job * a.sC;
+  const float* W = a.W + job * a.sW;
+  const float* Z = a.Z + job * a.sZ;
+  const float* Vn = a.Vn + job * a.sV;
+
+  const int lane = t & 63, wave = t >> 6;
+  const int rb = wave >> 1, cb = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+
+  // this lane's row of W (k = 32 h .. 32 h + 31): the sum of the producer's
+  // slices, kept for every chunk
+  float wf[32];
+  {
+    const int row = r0 + rb * 32 + r32;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) wf[q] = 0.f;
+    if (row < M) {
+      for (int sl = 0; sl < a.wslices_in; ++sl) {
+        const float* wr = W + sl * a.wslice + (int64_t)row * FK;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 v = ld4(wr, 32 * h + 4 * q, nb);
+          wf[4 * q + 0] += v.x;
+          wf[4 * q + 1] += v.y;
+          wf[4 * q + 2] += v.z;
+          wf[4 * q + 3] += v.w;
+        }
+      }
+    }
+  }
+
+  // chunk loads: thread -> 4-float piece (t % 16) of rows t / 16 + 16 i
+  const int pc = (t & 15) * 4, pr = t >> 4;
+  float4 zr[4], vr[4], cr[4];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = pr + 16 * i;  // Z row (chunk column) / vector index / C row
+      const int zc = c0 + row;
+      zr[i] = zc < L ? ld4(Z + (int64_t)zc * FK, pc, nb) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vr[i] = row < nbn ? ld4(Vn + (int64_t)row * a.ldV + c0, pc, L - c0)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int cm = r0 + row;
+      cr[i] = cm < M ? ld4(C + (int64_t)cm * a.ldC + c0, pc, L - c0)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+
+  f32x16_t accp;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) accp[v] = 0.f;
+
+  if (ch0 < ch1) load_chunk(ch0 * FC);
+#pragma unroll 1
+  for (int ch = ch0; ch < ch1; ++ch) {
+    const int c0 = ch * FC;
+    __syncthreads();  // the previous chunk's reads of Zs, Vs, Ds are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = pr + 16 * i;
+      *(float4*)&Zs[row * LDF + pc] = zr[i];
+      *(float4*)&Vs[row * LDF + pc] = vr[i];
+      *(float4*)&Ds[row * LDF + pc] = cr[i];
+    }
+    __syncthreads();
+    if (ch + 1 < ch1) load_chunk(c0 + FC);  // in flight during the products
+
+    // update: acc = W[rows of rb] Z[cols of cb]^T over k < 64
+    f32x16_t acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    const float* zb = Zs + (cb * 32 + r32) * LDF + 32 * h;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 zv = *(const float4*)(zb + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wf[4 * q + e], comp(zv, e), acc, 0, 0, 0);
+    }
+    // D = C - acc in place (each element read and written by one lane)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rl = rb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+      float* d = &Ds[rl * LDF + cb * 32 + r32];
+      *d = *d - acc[v];
+    }
+    __syncthreads();
+    // D back to C in 16-byte pieces
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = pr + 16 * i, cm = r0 + row, col = c0 + pc;
+      if (cm >= M || col >= L) continue;
+      const float4 d = *(const float4*)&Ds[row * LDF + pc];
+      float* dst = C + (int64_t)cm * a.ldC + col;
+      if (col + 4 <= L) {
+        *(float4*)dst = d;
+      } else {
+        for (int e = 0; col + e < L; ++e) dst[e] = comp(d, e);
+      }
+    }
+    // projection: accp += D[rows of rb] Vn[vectors of cb]^T over the chunk
+    if (nbn == 0) continue;  // update only
+    const float* db = Ds + (rb * 32 + r32) * LDF + 32 * h;
+    const float* vb = Vs + (cb * 32 + r32) * LDF + 32 * h;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 dv = *(const float4*)(db + 4 * q);
+      const float4 vv = *(const float4*)(vb + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        accp = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(dv, e), comp(vv, e), accp, 0, 0, 0);
+    }
+  }
+
+  // this split's partial Wn rows of the strip
+  const int vec = cb * 32 + r32;
+  if (vec < nbn) {
+    float* Wn = a.Wn + job * a.sWn + split * a.wslice;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = r0 + rb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (row < M) Wn[(int64_t)row * FK + vec] = accp[v];
+    }
+  }
+}
+
+}  // namespace
+
+mao_status qr_fused_update(const QrFusedArgs& args, int njob, hipStream_t stream) {
+  QrFusedArgs a = args;
+  if (njob <= 0 || a.M <= 0 || a.L <= 0) return MAO_OK;
+  // the panel widths and the identity rows fit one 64-wide fragment
+  if (a.nb < 1 || a.nb > FK || a.nbn < 0 || a.nbn > FK) return MAO_E_SHAPE;
+  if (a.Wt != nullptr && (a.trows < 0 || a.trows > FK)) return MAO_E_SHAPE;
+  // without a projection (nbn = 0) nothing is written per split, so any
+  // number of column ranges may run side by side
+  if (a.splits < 1 || (a.nbn > 0 && a.splits > kQrFusedMaxSplits) || a.wslices_in < 1 ||
+      a.wslices_in > kQrFusedMaxSplits)
+    return MAO_E_SHAPE;
+  a.strips = (a.M + FR - 1) / FR;
+  const int extra = a.Wt != nullptr ? 1 : 0;
+  void* ev = nullptr;
+  const bool timed = timing_on();
+  if (timed) timing_record_begin(stream, &ev);
+  hipLaunchKernelGGL(qr_fused_update_kernel, dim3(a.strips * a.splits + extra, njob), dim3(256), 0, stream, a);
+  MAO_LAUNCH_CHECK();
+  if (timed)
+    timing_record_end(stream, ev, TAG_QR_FUSED,
+                      2.0 * a.M * (double)a.L * (a.nb + a.nbn) * njob);
+  return MAO_OK;
+}
+
+}  // namespace mao
