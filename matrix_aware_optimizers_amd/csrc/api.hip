@@ -1266,13 +1266,15 @@ mao_status soap_step(mao_mat W, mao_mat G, const mao_soap_state* st, int64_t t,
                         R.P3b, R.ld3p, s, nullptr));
     else
       MAO_TRY(nt32(m, m, m, R.EL, R.ldm, (const float*)st->L.data, st->L.ld, R.S, ldS, nullptr, 0, s));
-    MAO_TRY(qr_core(R.S, ldS, m, R.EL, R.ldm, (float*)st->QL.data, st->QL.ld, R.qr, nullptr, s));
+    MAO_TRY(qr_core(R.S, ldS, m, R.EL, R.ldm, (float*)st->QL.data, st->QL.ld, R.qr, nullptr, s,
+                    false, R.P3a != nullptr));
     if (R.P3a)
       MAO_TRY(nt3_split(n, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, ldS, R.P3a,
                         R.P3b, R.ld3p, s, nullptr));
     else
       MAO_TRY(nt32(n, n, n, R.ER, R.ldn, (const float*)st->R.data, st->R.ld, R.S, ldS, nullptr, 0, s));
-    MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, nullptr, s));
+    MAO_TRY(qr_core(R.S, ldS, n, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, nullptr, s,
+                    false, R.P3a != nullptr));
   }
   for (int stage = 0; stage < kSoapPostStages; ++stage)
     MAO_TRY(soap_post(stage, W, G, st, R, t, hp, update_out, nullptr, s));
@@ -1345,6 +1347,7 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
       b.Q = q.data();
       b.ldQ = ldq.data();
       b.work = g.work;
+      b.fact_bf16x3 = o.ref3;
       MAO_TRY(qr_core_batched(b, s));
     }
   }
@@ -1405,7 +1408,8 @@ mao_status foam_step(mao_mat W, mao_mat G, const mao_foam_state* st, int64_t t,
     eb.work = R.eigh;
     MAO_TRY(eigh_batched(eb, s));
   } else if (foam_checks(hp, t)) {
-    MAO_TRY(qr_core(R.S, R.ldn, k, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, R.flag, s));
+    MAO_TRY(qr_core(R.S, R.ldn, k, R.ER, R.ldn, (float*)st->QR.data, st->QR.ld, R.qr, R.flag, s,
+                    false, R.P3a != nullptr));
   }
   MAO_TRY(foam_rotate(W, G, st, R, hp, nullptr, s));
   MAO_TRY(foam_precondition_back(W, st, R, t, hp, update_out, nullptr, s));
@@ -1507,6 +1511,7 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
       b.pred = g.flags;
       b.spred = 1;
       b.work = g.work;
+      b.fact_bf16x3 = o.ref3;
       MAO_TRY(qr_core_batched(b, s));
     }
   }

@@ -922,6 +922,7 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
       fa.nb = NB;  // panel p-1 is a full panel
       fa.nbn = 0;
       fa.splits = (len + NB - 1) / NB;
+      fa.x3 = b.fact_bf16x3;
       fa.pred = b.pred;
       fa.spred = b.spred;
       MAO_TRY(qr_fused_update(fa, nj, stream));
@@ -1014,6 +1015,7 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
     fc.nb = NB;
     fc.nbn = nb;
     fc.splits = fused_splits(mt, len, nj);
+    fc.x3 = b.fact_bf16x3;
     fc.pred = b.pred;
     fc.spred = b.spred;
     MAO_TRY(qr_fused_update(fc, nj, stream));
@@ -1145,9 +1147,11 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
 }
 
 mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout, int64_t ldQ,
-                   QrWork& w, const int* pred, hipStream_t stream, bool abort_barriers) {
+                   QrWork& w, const int* pred, hipStream_t stream, bool abort_barriers,
+                   bool fact_bf16x3) {
   QrBatch b;
   b.abort_barriers = abort_barriers;
+  b.fact_bf16x3 = fact_bf16x3;
   b.n = n;
   b.njob = 1;
   b.S = S;

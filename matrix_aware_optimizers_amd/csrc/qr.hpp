@@ -58,6 +58,9 @@ struct QrBatch {
   // grid barrier then stops waiting at once, every kernel still exits, and
   // the job's E and Q come out NaN -- what a real time-out produces.
   bool abort_barriers = false;
+  // the factorisation's panel updates as bf16x3 products (for a QR input
+  // that is itself a bf16x3 product); the explicit Q is accumulated in fp32
+  bool fact_bf16x3 = false;
 };
 mao_status qr_core_batched(const QrBatch& b, hipStream_t stream);
 
@@ -89,6 +92,7 @@ struct QrFusedArgs {
   int M = 0, L = 0, nb = 0, nbn = 0;
   int splits = 1, wslices_in = 1;
   int64_t wslice = 0;
+  bool x3 = false;  // both products as bf16x3 on bf16 MFMA
   const int* pred = nullptr;
   int64_t spred = 0;
   int strips = 0;  // set by qr_fused_update
@@ -102,6 +106,6 @@ mao_status qr_fused_update(const QrFusedArgs& a, int njob, hipStream_t stream);
 // If a grid barrier times out, E and Q are set to NaN.
 mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout,
                    int64_t ldQ, QrWork& w, const int* pred, hipStream_t stream,
-                   bool abort_barriers = false);
+                   bool abort_barriers = false, bool fact_bf16x3 = false);
 
 }  // namespace mao

@@ -21,6 +21,14 @@
 // partial projection into slice s of Wn; the consumer sums the slices (the
 // next panel's call when it loads W, or a summing pass).
 //
+// With x3 set both products run as bf16x3 on bf16 MFMA (v_mfma_f32_32x32x16
+// _bf16): every fp32 operand x splits into hi = bf16(x) and lo = bf16(x -
+// hi), and A B^T = hi_A hi_B^T + lo_A hi_B^T + hi_A lo_B^T (about 2^-17
+// relative per product instead of 2^-24). The factorisation takes this when
+// the power-iteration product it factors is itself bf16x3: its rounding
+// only perturbs the matrix factored, the reflectors stay exactly orthogonal
+// and the explicit-Q accumulation keeps fp32.
+//
 // Optionally one more workgroup per job writes the first rows of Wn that
 // come from identity rows of the next block (the explicit-Q accumulation:
 // rows of E above the current panel are still rows of I, so their
@@ -50,6 +58,31 @@ __device__ __forceinline__ float comp(const float4& a, int e) {
   return e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
 }
 
+// Eight fp32 values (two float4) split into bf16 hi and lo fragments.
+__device__ __forceinline__ void split8(const float4& x0, const float4& x1, uint4& hi, uint4& lo) {
+  const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    const float r0 = v[2 * i] - __uint_as_float(h[i] << 16);
+    const float r1 = v[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u);
+    l[i] = pack_bf16x2(r0, r1);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ f32x16_t mfma3(const uint4& ah, const uint4& al, const uint4& bh,
+                                          const uint4& bl, f32x16_t acc) {
+  const bf16x8_t AH = __builtin_bit_cast(bf16x8_t, ah), AL = __builtin_bit_cast(bf16x8_t, al);
+  const bf16x8_t BH = __builtin_bit_cast(bf16x8_t, bh), BL = __builtin_bit_cast(bf16x8_t, bl);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AH, BH, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AL, BH, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(AH, BL, acc, 0, 0, 0);
+}
+
+template <bool X3>
 __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
   __shared__ __attribute__((aligned(16))) float Zs[FC * LDF];
   __shared__ __attribute__((aligned(16))) float Vs[FK * LDF];
@@ -87,8 +120,10 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
   const int rb = wave >> 1, cb = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
 
-  // this lane's row of W (k = 32 h .. 32 h + 31): the sum of the producer's
-  // slices, kept for every chunk
+  // this lane's 32 values of its row of W -- the sum of the producer's
+  // slices, kept for every chunk. fp32: k = 32 h .. 32 h + 31 (one k per
+  // 2-deep MFMA); bf16x3: k = 16 s + 8 h .. + 7 for the 16-deep steps s,
+  // split into hi / lo fragments.
   float wf[32];
   {
     const int row = r0 + rb * 32 + r32;
@@ -99,7 +134,8 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
         const float* wr = W + sl * a.wslice + (int64_t)row * FK;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const float4 v = ld4(wr, 32 * h + 4 * q, nb);
+          const int k = X3 ? 16 * (q >> 1) + 8 * h + 4 * (q & 1) : 32 * h + 4 * q;
+          const float4 v = ld4(wr, k, nb);
           wf[4 * q + 0] += v.x;
           wf[4 * q + 1] += v.y;
           wf[4 * q + 2] += v.z;
@@ -107,6 +143,14 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
         }
       }
     }
+  }
+  uint4 wh[4], wl[4];
+  if (X3) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      split8(make_float4(wf[8 * st], wf[8 * st + 1], wf[8 * st + 2], wf[8 * st + 3]),
+             make_float4(wf[8 * st + 4], wf[8 * st + 5], wf[8 * st + 6], wf[8 * st + 7]), wh[st],
+             wl[st]);
   }
 
   // chunk loads: thread -> 4-float piece (t % 16) of rows t / 16 + 16 i
@@ -149,13 +193,23 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
     f32x16_t acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-    const float* zb = Zs + (cb * 32 + r32) * LDF + 32 * h;
+    if (X3) {
+      const float* zb = Zs + (cb * 32 + r32) * LDF + 8 * h;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 zv = *(const float4*)(zb + 4 * q);
+      for (int st = 0; st < 4; ++st) {
+        uint4 zh, zl;
+        split8(*(const float4*)(zb + 16 * st), *(const float4*)(zb + 16 * st + 4), zh, zl);
+        acc = mfma3(wh[st], wl[st], zh, zl, acc);
+      }
+    } else {
+      const float* zb = Zs + (cb * 32 + r32) * LDF + 32 * h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wf[4 * q + e], comp(zv, e), acc, 0, 0, 0);
+      for (int q = 0; q < 8; ++q) {
+        const float4 zv = *(const float4*)(zb + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wf[4 * q + e], comp(zv, e), acc, 0, 0, 0);
+      }
     }
     // D = C - acc in place (each element read and written by one lane)
 #pragma unroll
@@ -180,15 +234,27 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
     }
     // projection: accp += D[rows of rb] Vn[vectors of cb]^T over the chunk
     if (nbn == 0) continue;  // update only
-    const float* db = Ds + (rb * 32 + r32) * LDF + 32 * h;
-    const float* vb = Vs + (cb * 32 + r32) * LDF + 32 * h;
+    if (X3) {
+      const float* db = Ds + (rb * 32 + r32) * LDF + 8 * h;
+      const float* vb = Vs + (cb * 32 + r32) * LDF + 8 * h;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 dv = *(const float4*)(db + 4 * q);
-      const float4 vv = *(const float4*)(vb + 4 * q);
+      for (int st = 0; st < 4; ++st) {
+        uint4 dh, dl, vh, vl;
+        split8(*(const float4*)(db + 16 * st), *(const float4*)(db + 16 * st + 4), dh, dl);
+        split8(*(const float4*)(vb + 16 * st), *(const float4*)(vb + 16 * st + 4), vh, vl);
+        accp = mfma3(dh, dl, vh, vl, accp);
+      }
+    } else {
+      const float* db = Ds + (rb * 32 + r32) * LDF + 32 * h;
+      const float* vb = Vs + (cb * 32 + r32) * LDF + 32 * h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        accp = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(dv, e), comp(vv, e), accp, 0, 0, 0);
+      for (int q = 0; q < 8; ++q) {
+        const float4 dv = *(const float4*)(db + 4 * q);
+        const float4 vv = *(const float4*)(vb + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          accp = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(dv, e), comp(vv, e), accp, 0, 0, 0);
+      }
     }
   }
 
@@ -222,7 +288,12 @@ mao_status qr_fused_update(const QrFusedArgs& args, int njob, hipStream_t stream
   void* ev = nullptr;
   const bool timed = timing_on();
   if (timed) timing_record_begin(stream, &ev);
-  hipLaunchKernelGGL(qr_fused_update_kernel, dim3(a.strips * a.splits + extra, njob), dim3(256), 0, stream, a);
+  if (a.x3)
+    hipLaunchKernelGGL(qr_fused_update_kernel<true>, dim3(a.strips * a.splits + extra, njob),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(qr_fused_update_kernel<false>, dim3(a.strips * a.splits + extra, njob),
+                       dim3(256), 0, stream, a);
   MAO_LAUNCH_CHECK();
   if (timed)
     timing_record_end(stream, ev, TAG_QR_FUSED,
