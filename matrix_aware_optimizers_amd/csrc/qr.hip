@@ -922,7 +922,7 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
       fa.nb = NB;  // panel p-1 is a full panel
       fa.nbn = 0;
       fa.splits = (len + NB - 1) / NB;
-      fa.x3 = b.fact_bf16x3;
+      fa.prec = b.fact_bf16x3 ? kQrBf16x3 : kQrBf16x6;
       fa.pred = b.pred;
       fa.spred = b.spred;
       MAO_TRY(qr_fused_update(fa, nj, stream));
@@ -1015,7 +1015,7 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
     fc.nb = NB;
     fc.nbn = nb;
     fc.splits = fused_splits(mt, len, nj);
-    fc.x3 = b.fact_bf16x3;
+    fc.prec = b.fact_bf16x3 ? kQrBf16x3 : kQrBf16x6;
     fc.pred = b.pred;
     fc.spred = b.spred;
     MAO_TRY(qr_fused_update(fc, nj, stream));
@@ -1068,6 +1068,7 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
     fa.wslices_in = s_in;
     fa.wslice = wsl;
     fa.splits = fused_splits(len, len, nj);
+    fa.prec = kQrBf16x6;
     MAO_TRY(qr_fused_update(fa, nj, stream));
     wcur = wnext;
     s_in = fa.splits;

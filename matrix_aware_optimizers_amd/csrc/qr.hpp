@@ -75,6 +75,9 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream);
 // (ld 64; Vt at ld ldV and stride sV). Jobs whose predicate (pred[j spred])
 // is zero are skipped. nb, nbn <= 64.
 constexpr int kQrFusedMaxSplits = 4;
+// Arithmetic of the fused products on bf16 MFMA: bf16x3 (about 2^-17
+// relative) or bf16x6 (three-way splits, fp32-equivalent).
+enum QrPrec : int { kQrBf16x3 = 1, kQrBf16x6 = 2 };
 struct QrFusedArgs {
   float* C = nullptr;
   int64_t ldC = 0, sC = 0;
@@ -92,7 +95,7 @@ struct QrFusedArgs {
   int M = 0, L = 0, nb = 0, nbn = 0;
   int splits = 1, wslices_in = 1;
   int64_t wslice = 0;
-  bool x3 = false;  // both products as bf16x3 on bf16 MFMA
+  int prec = kQrBf16x6;  // QrPrec of both products
   const int* pred = nullptr;
   int64_t spred = 0;
   int strips = 0;  // set by qr_fused_update

@@ -13,21 +13,28 @@
 // ("split"; S raises the workgroup count when a panel's block has few
 // strips), 4 wavefronts in 2 x 2; the workgroup walks its columns in chunks
 // of 64. Per chunk: C's 64 x 64 block comes in by 16-byte loads into LDS,
-// the update (v_mfma_f32_32x32x2f32, W's fragment held in registers for the
-// whole strip, Z's chunk in LDS) turns it into D in place, D leaves by
+// the update (W's fragments held in registers for the whole strip, Z's
+// chunk in LDS) turns it into D in place, D leaves by
 // 16-byte stores, and the projection of D onto the chunk of Vn (both in LDS)
 // accumulates in registers. The next chunk's C, Z and Vn are loaded into
 // registers while the current chunk's products run. Split s writes its
 // partial projection into slice s of Wn; the consumer sums the slices (the
 // next panel's call when it loads W, or a summing pass).
 //
-// With x3 set both products run as bf16x3 on bf16 MFMA (v_mfma_f32_32x32x16
-// _bf16): every fp32 operand x splits into hi = bf16(x) and lo = bf16(x -
-// hi), and A B^T = hi_A hi_B^T + lo_A hi_B^T + hi_A lo_B^T (about 2^-17
-// relative per product instead of 2^-24). The factorisation takes this when
-// the power-iteration product it factors is itself bf16x3: its rounding
-// only perturbs the matrix factored, the reflectors stay exactly orthogonal
-// and the explicit-Q accumulation keeps fp32.
+// The products run on bf16 MFMA in one of two arithmetics (QrPrec):
+//  * bf16x3 (v_mfma_f32_32x32x16_bf16, fp32 accumulation): every fp32
+//    operand x splits into hi = bf16(x) and lo = bf16(x - hi), A B^T = hi hi +
+//    lo hi + hi lo (about 2^-17 relative per product). The factorisation
+//    takes this when the power-iteration product it factors is itself
+//    bf16x3: its rounding only perturbs the matrix factored, and the
+//    reflectors stay exactly orthogonal;
+//  * bf16x6, fp32-equivalent: x = hi + mid + lo exactly (three bf16 of 8
+//    significant bits each cover fp32's 24), and the six products hh, hm, mh,
+//    mm, hl, lh keep every term down to 2^-16 of the leading one; the
+//    dropped ml, lm, ll are below 2^-24 relative. 6 bf16 products cost 6/16
+//    of one fp32 product on the matrix cores. The explicit-Q accumulation
+//    runs this way, and the factorisation when its input is an fp32
+//    product.
 //
 // Optionally one more workgroup per job writes the first rows of Wn that
 // come from identity rows of the next block (the explicit-Q accumulation:
@@ -73,6 +80,42 @@ __device__ __forceinline__ void split8(const float4& x0, const float4& x1, uint4
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
+// Eight fp32 values split into bf16 hi, mid and lo fragments (x = hi + mid +
+// lo exactly for normal x).
+__device__ __forceinline__ void split8x3(const float4& x0, const float4& x1, uint4& hi, uint4& mid,
+                                         uint4& lo) {
+  const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    const float r0 = v[2 * i] - __uint_as_float(h[i] << 16);
+    const float r1 = v[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u);
+    m[i] = pack_bf16x2(r0, r1);
+    l[i] = pack_bf16x2(r0 - __uint_as_float(m[i] << 16), r1 - __uint_as_float(m[i] & 0xffff0000u));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  mid = make_uint4(m[0], m[1], m[2], m[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ f32x16_t mfma_bf(const uint4& a, const uint4& b, f32x16_t acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+
+// hh + mh + hm + mm + lh + hl, smallest terms first
+__device__ __forceinline__ f32x16_t mfma6(const uint4& ah, const uint4& am, const uint4& al,
+                                          const uint4& bh, const uint4& bm, const uint4& bl,
+                                          f32x16_t acc) {
+  acc = mfma_bf(al, bh, acc);
+  acc = mfma_bf(ah, bl, acc);
+  acc = mfma_bf(am, bm, acc);
+  acc = mfma_bf(am, bh, acc);
+  acc = mfma_bf(ah, bm, acc);
+  return mfma_bf(ah, bh, acc);
+}
+
 __device__ __forceinline__ f32x16_t mfma3(const uint4& ah, const uint4& al, const uint4& bh,
                                           const uint4& bl, f32x16_t acc) {
   const bf16x8_t AH = __builtin_bit_cast(bf16x8_t, ah), AL = __builtin_bit_cast(bf16x8_t, al);
@@ -82,8 +125,9 @@ __device__ __forceinline__ f32x16_t mfma3(const uint4& ah, const uint4& al, cons
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(AH, BL, acc, 0, 0, 0);
 }
 
-template <bool X3>
+template <int PREC>
 __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
+  constexpr bool X6 = PREC == kQrBf16x6;
   __shared__ __attribute__((aligned(16))) float Zs[FC * LDF];
   __shared__ __attribute__((aligned(16))) float Vs[FK * LDF];
   __shared__ __attribute__((aligned(16))) float Ds[FR * LDF];  // C, then D, in place
@@ -121,9 +165,8 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
   const int h = lane >> 5, r32 = lane & 31;
 
   // this lane's 32 values of its row of W -- the sum of the producer's
-  // slices, kept for every chunk. fp32: k = 32 h .. 32 h + 31 (one k per
-  // 2-deep MFMA); bf16x3: k = 16 s + 8 h .. + 7 for the 16-deep steps s,
-  // split into hi / lo fragments.
+  // slices, kept for every chunk: k = 16 s + 8 h .. + 7 for the 16-deep
+  // steps s (lane half h), split into bf16 fragments.
   float wf[32];
   {
     const int row = r0 + rb * 32 + r32;
@@ -134,7 +177,7 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
         const float* wr = W + sl * a.wslice + (int64_t)row * FK;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const int k = X3 ? 16 * (q >> 1) + 8 * h + 4 * (q & 1) : 32 * h + 4 * q;
+          const int k = 16 * (q >> 1) + 8 * h + 4 * (q & 1);
           const float4 v = ld4(wr, k, nb);
           wf[4 * q + 0] += v.x;
           wf[4 * q + 1] += v.y;
@@ -144,13 +187,17 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
       }
     }
   }
-  uint4 wh[4], wl[4];
-  if (X3) {
+  uint4 wh[4], wm[4], wl[4];
+  {
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-      split8(make_float4(wf[8 * st], wf[8 * st + 1], wf[8 * st + 2], wf[8 * st + 3]),
-             make_float4(wf[8 * st + 4], wf[8 * st + 5], wf[8 * st + 6], wf[8 * st + 7]), wh[st],
-             wl[st]);
+    for (int st = 0; st < 4; ++st) {
+      const float4 x0 = make_float4(wf[8 * st], wf[8 * st + 1], wf[8 * st + 2], wf[8 * st + 3]);
+      const float4 x1 = make_float4(wf[8 * st + 4], wf[8 * st + 5], wf[8 * st + 6], wf[8 * st + 7]);
+      if (X6)
+        split8x3(x0, x1, wh[st], wm[st], wl[st]);
+      else
+        split8(x0, x1, wh[st], wl[st]);
+    }
   }
 
   // chunk loads: thread -> 4-float piece (t % 16) of rows t / 16 + 16 i
@@ -193,22 +240,19 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
     f32x16_t acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-    if (X3) {
+    {
       const float* zb = Zs + (cb * 32 + r32) * LDF + 8 * h;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        uint4 zh, zl;
-        split8(*(const float4*)(zb + 16 * st), *(const float4*)(zb + 16 * st + 4), zh, zl);
-        acc = mfma3(wh[st], wl[st], zh, zl, acc);
-      }
-    } else {
-      const float* zb = Zs + (cb * 32 + r32) * LDF + 32 * h;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 zv = *(const float4*)(zb + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wf[4 * q + e], comp(zv, e), acc, 0, 0, 0);
+        const float4 z0 = *(const float4*)(zb + 16 * st), z1 = *(const float4*)(zb + 16 * st + 4);
+        uint4 zh, zm, zl;
+        if (X6) {
+          split8x3(z0, z1, zh, zm, zl);
+          acc = mfma6(wh[st], wm[st], wl[st], zh, zm, zl, acc);
+        } else {
+          split8(z0, z1, zh, zl);
+          acc = mfma3(wh[st], wl[st], zh, zl, acc);
+        }
       }
     }
     // D = C - acc in place (each element read and written by one lane)
@@ -234,26 +278,24 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
     }
     // projection: accp += D[rows of rb] Vn[vectors of cb]^T over the chunk
     if (nbn == 0) continue;  // update only
-    if (X3) {
+    {
       const float* db = Ds + (rb * 32 + r32) * LDF + 8 * h;
       const float* vb = Vs + (cb * 32 + r32) * LDF + 8 * h;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        uint4 dh, dl, vh, vl;
-        split8(*(const float4*)(db + 16 * st), *(const float4*)(db + 16 * st + 4), dh, dl);
-        split8(*(const float4*)(vb + 16 * st), *(const float4*)(vb + 16 * st + 4), vh, vl);
-        accp = mfma3(dh, dl, vh, vl, accp);
-      }
-    } else {
-      const float* db = Ds + (rb * 32 + r32) * LDF + 32 * h;
-      const float* vb = Vs + (cb * 32 + r32) * LDF + 32 * h;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 dv = *(const float4*)(db + 4 * q);
-        const float4 vv = *(const float4*)(vb + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          accp = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(dv, e), comp(vv, e), accp, 0, 0, 0);
+        const float4 d0 = *(const float4*)(db + 16 * st), d1 = *(const float4*)(db + 16 * st + 4);
+        const float4 v0 = *(const float4*)(vb + 16 * st), v1 = *(const float4*)(vb + 16 * st + 4);
+        if (X6) {
+          uint4 dh, dm, dl, vh, vm, vl;
+          split8x3(d0, d1, dh, dm, dl);
+          split8x3(v0, v1, vh, vm, vl);
+          accp = mfma6(dh, dm, dl, vh, vm, vl, accp);
+        } else {
+          uint4 dh, dl, vh, vl;
+          split8(d0, d1, dh, dl);
+          split8(v0, v1, vh, vl);
+          accp = mfma3(dh, dl, vh, vl, accp);
+        }
       }
     }
   }
@@ -275,6 +317,7 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
 mao_status qr_fused_update(const QrFusedArgs& args, int njob, hipStream_t stream) {
   QrFusedArgs a = args;
   if (njob <= 0 || a.M <= 0 || a.L <= 0) return MAO_OK;
+  if (a.prec != kQrBf16x3 && a.prec != kQrBf16x6) return MAO_E_UNSUPPORTED;
   // the panel widths and the identity rows fit one 64-wide fragment
   if (a.nb < 1 || a.nb > FK || a.nbn < 0 || a.nbn > FK) return MAO_E_SHAPE;
   if (a.Wt != nullptr && (a.trows < 0 || a.trows > FK)) return MAO_E_SHAPE;
@@ -288,12 +331,11 @@ mao_status qr_fused_update(const QrFusedArgs& args, int njob, hipStream_t stream
   void* ev = nullptr;
   const bool timed = timing_on();
   if (timed) timing_record_begin(stream, &ev);
-  if (a.x3)
-    hipLaunchKernelGGL(qr_fused_update_kernel<true>, dim3(a.strips * a.splits + extra, njob),
-                       dim3(256), 0, stream, a);
+  const dim3 grid(a.strips * a.splits + extra, njob);
+  if (a.prec == kQrBf16x3)
+    hipLaunchKernelGGL(qr_fused_update_kernel<kQrBf16x3>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(qr_fused_update_kernel<false>, dim3(a.strips * a.splits + extra, njob),
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(qr_fused_update_kernel<kQrBf16x6>, grid, dim3(256), 0, stream, a);
   MAO_LAUNCH_CHECK();
   if (timed)
     timing_record_end(stream, ev, TAG_QR_FUSED,
