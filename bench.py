@@ -381,6 +381,9 @@ class SoapLikeWorkload:
         self.items = []
         tg = torch.bfloat16 if g_dtype == "bf16" else torch.float32
         tw = torch.bfloat16 if w_dtype == "bf16" else torch.float32
+        if kind == "foam" and refresh == "eigh":
+            prod = "f32"  # the eigendecomposition takes fp32 criterion products
+        self.prod = prod
         if kind == "soap":
             self.hp = mao.soap_hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
                                        refresh_every=1, back_rot_dtype=back, fwd_rot=fwd,
@@ -514,7 +517,7 @@ def run_soaplike(args, workload_name, kind, config, specs, g_dtype, w_dtype, emb
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": workload_name, "matrices": len(specs), "optimizer": kind,
                    "gradients": g_dtype, "weights": w_dtype, "back_rotation": back,
-                   "forward_rotation": fwd, "refresh_products": prod, **({"side": side, "refresh": refresh} if kind == "foam" else {})},
+                   "forward_rotation": fwd, "refresh_products": wl.prod, **({"side": side, "refresh": refresh} if kind == "foam" else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
                      "kernel": "fp32 contractions of the step (gemm_f32_dl_kernel rotations and products, QR updates and projections; bf16 products under kernels.other_bf16)"},
