@@ -580,7 +580,8 @@ MAO_API mao_status mao_basis_age(const float* aux, float* age, void* stream);
  * 2: Newton-Schulz B X, 3: other contractions on fp32 inputs, 4: QR rank
  * updates, 5: other contractions on bf16 inputs, 6: QR projections onto a
  * panel's vectors, 7: QR fused update-and-projection, 8: QR panel
- * factorisations, counted at zero flops) with its
+ * factorisations, counted at zero flops, 9: launches gated by a device-side
+ * flag, such as FOAM's refresh, whose flops assume every job ran) with its
  * algorithmic flop count (symmetric products at half cost). Off by default;
  * this is the only host-side state the library keeps, and it exists for
  * benchmarking only.

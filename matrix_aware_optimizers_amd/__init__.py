@@ -473,7 +473,7 @@ def basis_age(aux, age):
 
 
 TIMING_TAGS = ("ns_gram", "ns_square", "ns_apply", "other", "qr", "other_bf16", "qr_proj",
-               "qr_fused", "qr_panel")
+               "qr_fused", "qr_panel", "gated")
 
 
 def timing_enable(on: bool = True):

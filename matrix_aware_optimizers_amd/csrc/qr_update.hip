@@ -338,7 +338,7 @@ mao_status qr_fused_update(const QrFusedArgs& args, int njob, hipStream_t stream
     hipLaunchKernelGGL(qr_fused_update_kernel<kQrBf16x6>, grid, dim3(256), 0, stream, a);
   MAO_LAUNCH_CHECK();
   if (timed)
-    timing_record_end(stream, ev, TAG_QR_FUSED,
+    timing_record_end(stream, ev, a.pred != nullptr ? TAG_GATED : TAG_QR_FUSED,
                       2.0 * a.M * (double)a.L * (a.nb + a.nbn) * njob);
   return MAO_OK;
 }
