@@ -699,7 +699,8 @@ def main():
     if args.write_traffic:
         write_traffic(*args.write_traffic,
                       command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python3 "
-                              "bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy")
+                              "bench.py --steps 2 --warmup 1 --no-cpu-baseline --soap8b-steps 0 "
+                              "--calibrate-copy")
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build's step runs whole matrices on one device "
