@@ -1325,17 +1325,22 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
       if (o.ref3) MAO_TRY(gemm_flush(gb, s));
     }
     MAO_TRY(gemm_flush(gb, s));
-    for (QrGroup& g : groups) {
+    // every size group in one refresh: their panels share launches
+    std::vector<std::vector<float*>> q(groups.size());
+    std::vector<std::vector<int64_t>> ldq(groups.size());
+    std::vector<QrBatch> batches(groups.size());
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const QrGroup& g = groups[gi];
       const int nj = (int)g.jobs.size();
-      std::vector<float*> q(nj);
-      std::vector<int64_t> ldq(nj);
+      q[gi].resize(nj);
+      ldq[gi].resize(nj);
       for (int k = 0; k < nj; ++k) {
         const int i = g.jobs[k].mat;
         const mao_mat& Q = g.jobs[k].side == 0 ? st[i].QL : st[i].QR;
-        q[k] = (float*)Q.data;
-        ldq[k] = Q.ld;
+        q[gi][k] = (float*)Q.data;
+        ldq[gi][k] = Q.ld;
       }
-      QrBatch b;
+      QrBatch& b = batches[gi];
       b.n = g.n;
       b.njob = nj;
       b.S = g.S;
@@ -1344,12 +1349,12 @@ mao_status soap_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
       b.E = g.E;
       b.ldE = g.ld;
       b.sE = g.sz;
-      b.Q = q.data();
-      b.ldQ = ldq.data();
+      b.Q = q[gi].data();
+      b.ldQ = ldq[gi].data();
       b.work = g.work;
       b.fact_bf16x3 = o.ref3;
-      MAO_TRY(qr_core_batched(b, s));
     }
+    MAO_TRY(qr_core_multi(batches.data(), (int)batches.size(), s));
   }
   for (int stage = 0; stage < kSoapPostStages; ++stage) {
     for (int i = 0; i < count; ++i)
@@ -1488,16 +1493,20 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
       MAO_TRY(eigh_batched(eb, s));
     }
   } else if (foam_checks(hp, t)) {
-    for (QrGroup& g : groups) {
+    std::vector<std::vector<float*>> q(groups.size());
+    std::vector<std::vector<int64_t>> ldq(groups.size());
+    std::vector<QrBatch> batches(groups.size());
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const QrGroup& g = groups[gi];
       const int nj = (int)g.jobs.size();
-      std::vector<float*> q(nj);
-      std::vector<int64_t> ldq(nj);
+      q[gi].resize(nj);
+      ldq[gi].resize(nj);
       for (int k = 0; k < nj; ++k) {
         const int i = g.jobs[k].mat;
-        q[k] = (float*)st[i].QR.data;
-        ldq[k] = st[i].QR.ld;
+        q[gi][k] = (float*)st[i].QR.data;
+        ldq[gi][k] = st[i].QR.ld;
       }
-      QrBatch b;
+      QrBatch& b = batches[gi];
       b.n = g.n;
       b.njob = nj;
       b.S = g.S;
@@ -1506,14 +1515,14 @@ mao_status foam_step_many(int32_t count, const mao_mat* W, const mao_mat* G,
       b.E = g.E;
       b.ldE = g.ld;
       b.sE = g.sz;
-      b.Q = q.data();
-      b.ldQ = ldq.data();
+      b.Q = q[gi].data();
+      b.ldQ = ldq[gi].data();
       b.pred = g.flags;
       b.spred = 1;
       b.work = g.work;
       b.fact_bf16x3 = o.ref3;
-      MAO_TRY(qr_core_batched(b, s));
     }
+    MAO_TRY(qr_core_multi(batches.data(), (int)batches.size(), s));
   }
   for (int i = 0; i < count; ++i) MAO_TRY(foam_rotate(W[i], G[i], &st[i], R[i], hp, &gb, s));
   MAO_TRY(gemm_flush(gb, s));

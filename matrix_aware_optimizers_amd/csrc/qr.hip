@@ -62,6 +62,7 @@ struct PanelArgs {
   int* err;
   const int* pred;
   const int* pred2;  // run only when *pred2 != 0 (the fast panel gave up)
+  int g0, G;         // this job's workgroups [g0, g0 + G) of the launch
 };
 
 __device__ void grid_barrier(unsigned* counter, unsigned target, int* err) {
@@ -83,17 +84,25 @@ __device__ void grid_barrier(unsigned* counter, unsigned target, int* err) {
   __threadfence();
 }
 
-// Up to kQrMaxJobs same-size panels per launch: job jb owns workgroups
-// [jb G, (jb + 1) G); its barriers count only its own workgroups.
+// Up to kQrMaxJobs panels per launch, of any sizes: job jb owns workgroups
+// [g0, g0 + G) (G = ceil(len / 256) for its panel); its barriers count only
+// its own workgroups.
 constexpr int kQrMaxJobs = 16;
 struct PanelBatch {
   PanelArgs a[kQrMaxJobs];
   int njob;
 };
 
+template <typename Args>
+__device__ __forceinline__ int job_of(const Args* a, int njob) {
+  int jb = 0;
+  while (jb + 1 < njob && (int)blockIdx.x >= a[jb + 1].g0) ++jb;
+  return jb;
+}
+
 __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
-  const int G = gridDim.x / B.njob, jb = blockIdx.x / G;
-  const PanelArgs& a = B.a[jb];
+  const PanelArgs& a = B.a[job_of(B.a, B.njob)];
+  const int G = a.G;
   if (a.pred != nullptr && *a.pred == 0) return;
   if (a.pred2 != nullptr && *a.pred2 == 0) return;
   __shared__ float X[NB][LDX];
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
   __shared__ float qs[4][NB];
   __shared__ float tot[NB], dgv[NB], taus[NB], betas[NB];
 
-  const int t = threadIdx.x, g = blockIdx.x - jb * G;
+  const int t = threadIdx.x, g = blockIdx.x - a.g0;
   const int n = a.n, j0 = a.j0, nb = a.nb;
   const int r = j0 + g * TPB + t;
   const bool valid = r < n;
@@ -285,6 +294,7 @@ struct CholArgs {
   int* err;
   const int* pred;
   int* fail;       // set to 1 when the panel falls back to the Householder kernel
+  int g0, G;       // this job's workgroups [g0, g0 + G) of the launch
 };
 
 __device__ __forceinline__ int upk(int i, int k) { return i * NB - (i * (i - 1)) / 2 + (k - i); }
@@ -304,8 +314,8 @@ struct CholBatch {
 static_assert(sizeof(CholBatch) <= 4096 && sizeof(PanelBatch) <= 4096, "kernel argument size");
 
 __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
-  const int G = gridDim.x / B.njob, jb = blockIdx.x / G;
-  const CholArgs& a = B.a[jb];
+  const CholArgs& a = B.a[job_of(B.a, B.njob)];
+  const int G = a.G;
   if (a.pred != nullptr && *a.pred == 0) return;
   __shared__ float X[NB][LDX];      // current Y (fp32), later V
   __shared__ __attribute__((aligned(16))) double Gs[NB][LDG];  // Gram / LU work
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
   __shared__ double red64[TPB];
   __shared__ int bad;
 
-  const int t = threadIdx.x, g = blockIdx.x - jb * G;
+  const int t = threadIdx.x, g = blockIdx.x - a.g0;
   const int n = a.n, j0 = a.j0, nb = a.nb, len = n - j0;
   const int r = j0 + g * TPB + t;
   const bool valid = r < n;
@@ -836,11 +846,11 @@ size_t qr_work_stride(int n) { return align_up(qr_work_bytes(n), 256); }
 
 namespace {
 
-// Jobs whose panel grids fit on the device together (one workgroup per CU
-// for the panel kernels' LDS footprint), capped by the launch table.
+// Workgroups of the panel kernels that fit on the device at once (one per CU
+// for their LDS footprint): the most one cooperative panel launch may hold.
 // The per-device figure is cached; threads that race on the first call both
 // compute the same value, and the atomic store/load keeps that race defined.
-int jobs_per_launch(int G) {
+int panel_slots() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -853,38 +863,63 @@ int jobs_per_launch(int G) {
     slots = std::max(1, cus * std::max(1, std::min(b1, b2)));
     cached[dev].store(slots, std::memory_order_relaxed);
   }
-  return std::max(1, std::min(kQrMaxJobs, slots / std::max(G, 1)));
+  return slots;
 }
 
 }  // namespace
 
-mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
-  const int n = b.n, nj = b.njob;
-  if (nj <= 0) return MAO_OK;
-  const int np = panels(n);
-  const size_t wst = qr_work_stride(n);
-  const int64_t wsf = (int64_t)(wst / sizeof(float));  // job stride of work, in floats
-  std::vector<QrWork> w(nj);
-  for (int j = 0; j < nj; ++j) {
-    Carver c(b.work + (size_t)j * wst);
-    w[j] = carve_qr_work(c, n);
-    const int err0 = b.abort_barriers ? 1 : 0;
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, w[j].counters, 2 * np, w[j].err, err0);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, (unsigned*)w[j].fail, np, w[j].err, err0);
-  }
-  MAO_LAUNCH_CHECK();
-  auto job_pred = [&](int j) -> const int* { return b.pred ? b.pred + j * b.spred : nullptr; };
+namespace {
 
-  // offsets of the packed panels (the same in every job's workspace)
-  int64_t voff = 0, zoff = 0;
-  std::vector<int64_t> vo(np), zo(np);
-  for (int p = 0; p < np; ++p) {
-    const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
-    vo[p] = voff;
-    zo[p] = zoff;
-    voff += round_up((int64_t)nb * round_up(len, 8), 64);
-    zoff += round_up((int64_t)len * NB, 64);
+// One size group of a refresh: its jobs, workspaces and the state the
+// factorisation carries from panel to panel.
+struct QrRun {
+  const QrBatch* b = nullptr;
+  int n = 0, nj = 0, np = 0;
+  size_t wst = 0;
+  int64_t wsf = 0, wsl = 0;  // job stride of the workspace and slice stride of W, in floats
+  std::vector<QrWork> w;
+  std::vector<int64_t> vo, zo;  // offsets of the packed panels (the same in every job)
+  float* wprev = nullptr;       // W_{p-1}, as sprev slices
+  int sprev = 1;
+  float* wnext = nullptr;
+
+  const int* job_pred(int j) const { return b->pred ? b->pred + j * b->spred : nullptr; }
+  int prec() const { return b->fact_bf16x3 ? kQrBf16x3 : kQrBf16x6; }
+
+  mao_status setup(const QrBatch& batch, hipStream_t stream) {
+    b = &batch;
+    n = batch.n;
+    nj = batch.njob;
+    np = panels(n);
+    wst = qr_work_stride(n);
+    wsf = (int64_t)(wst / sizeof(float));
+    wsl = (int64_t)n * NB;
+    w.resize(nj);
+    for (int j = 0; j < nj; ++j) {
+      Carver c(batch.work + (size_t)j * wst);
+      w[j] = carve_qr_work(c, n);
+      const int err0 = batch.abort_barriers ? 1 : 0;
+      hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, w[j].counters, 2 * np, w[j].err, err0);
+      hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, (unsigned*)w[j].fail, np, w[j].err, err0);
+    }
+    MAO_LAUNCH_CHECK();
+    int64_t voff = 0, zoff = 0;
+    vo.resize(np);
+    zo.resize(np);
+    for (int p = 0; p < np; ++p) {
+      const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
+      vo[p] = voff;
+      zo[p] = zoff;
+      voff += round_up((int64_t)nb * round_up(len, 8), 64);
+      zoff += round_up((int64_t)len * NB, 64);
+    }
+    wprev = w[0].wbuf;
+    sprev = 1;
+    wnext = w[0].wparts;
+    return MAO_OK;
   }
+
+  float* zf_of(int p) const { return (p & 1) ? w[0].zf2 : w[0].zf; }
 
   // Factorisation with one panel of look-ahead. W_{p-1} is the projection of
   // panel p-1's trailing rows onto its vectors. Before panel p is factored,
@@ -895,115 +930,97 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
   // of consecutive panels alternate between zf and zf2; W alternates between
   // the two slice regions of wparts (wbuf for the first panel's plain
   // projection).
-  const int G = max_groups(n);
-  const int per = jobs_per_launch(G);
-  const int64_t wsl = (int64_t)n * NB;  // slice stride
-  float* wprev = w[0].wbuf;
-  int sprev = 1;
-  float* wnext = w[0].wparts;
-  for (int p = 0; p < np; ++p) {
+  mao_status before_panel(int p, hipStream_t stream) {
+    if (p == 0 || p >= np) return MAO_OK;
+    const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
+    // panel p's rows take panel p-1's update (one 64-column chunk per workgroup)
+    QrFusedArgs fa;
+    fa.C = b->S + (int64_t)j0 * b->ldS + j0;
+    fa.ldC = b->ldS;
+    fa.sC = b->sS;
+    fa.W = wprev;
+    fa.sW = wsf;
+    fa.wslices_in = sprev;
+    fa.wslice = wsl;
+    fa.Z = zf_of(p - 1) + (int64_t)NB * NB;  // V T^T rows of the columns >= j0
+    fa.sZ = wsf;
+    fa.M = nb;
+    fa.L = len;
+    fa.nb = NB;  // panel p-1 is a full panel
+    fa.nbn = 0;
+    fa.splits = (len + NB - 1) / NB;
+    fa.prec = prec();
+    fa.pred = b->pred;
+    fa.spred = b->spred;
+    return qr_fused_update(fa, nj, stream);
+  }
+
+  // The arguments of job j's panel p for both panel kernels.
+  void panel_args(int p, int j, PanelArgs& a, CholArgs& ca) const {
+    const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
+    const QrWork& wj = w[j];
+    a.S = b->S + j * b->sS;
+    a.ldS = b->ldS;
+    a.n = n;
+    a.j0 = j0;
+    a.nb = nb;
+    a.V = wj.vstore + vo[p];
+    a.ldV = round_up(len, 8);
+    a.Zf = (p & 1) ? wj.zf2 : wj.zf;
+    a.Zo = wj.zo + zo[p];
+    a.sign = wj.sign;
+    a.part = wj.part;
+    a.dg = wj.dg;
+    a.gram = wj.gram;
+    a.T = wj.T;
+    a.counter = wj.counters + p;
+    a.err = wj.err;
+    a.pred = job_pred(j);
+    a.pred2 = wj.fail + p;
+    a.G = (len + TPB - 1) / TPB;
+    ca.S = a.S;
+    ca.ldS = a.ldS;
+    ca.n = n;
+    ca.j0 = j0;
+    ca.nb = nb;
+    ca.V = a.V;
+    ca.ldV = a.ldV;
+    ca.Zf = a.Zf;
+    ca.Zo = a.Zo;
+    ca.sign = wj.sign;
+    ca.T = wj.T;
+    ca.part = wj.part64;
+    ca.gram = wj.gram64;
+    ca.bcast = wj.bcast;
+    ca.counter = wj.counters + np + p;
+    ca.err = wj.err;
+    ca.pred = a.pred;
+    ca.fail = wj.fail + p;
+    ca.G = a.G;
+  }
+
+  mao_status after_panel(int p, hipStream_t stream) {
+    if (p >= np) return MAO_OK;
     const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
     const int mt = n - j0 - nb;
-    float* zf_prev = ((p - 1) & 1) ? w[0].zf2 : w[0].zf;
-    if (p > 0) {
-      // panel p's rows take panel p-1's update (one 64-column chunk per workgroup)
-      QrFusedArgs fa;
-      fa.C = b.S + (int64_t)j0 * b.ldS + j0;
-      fa.ldC = b.ldS;
-      fa.sC = b.sS;
-      fa.W = wprev;
-      fa.sW = wsf;
-      fa.wslices_in = sprev;
-      fa.wslice = wsl;
-      fa.Z = zf_prev + (int64_t)NB * NB;  // V T^T rows of the columns >= j0
-      fa.sZ = wsf;
-      fa.M = nb;
-      fa.L = len;
-      fa.nb = NB;  // panel p-1 is a full panel
-      fa.nbn = 0;
-      fa.splits = (len + NB - 1) / NB;
-      fa.prec = b.fact_bf16x3 ? kQrBf16x3 : kQrBf16x6;
-      fa.pred = b.pred;
-      fa.spred = b.spred;
-      MAO_TRY(qr_fused_update(fa, nj, stream));
-    }
-    const int Gp = (len + TPB - 1) / TPB;
-    for (int c0 = 0; c0 < nj; c0 += per) {
-      const int cn = std::min(per, nj - c0);
-      CholBatch cb;
-      PanelBatch pb;
-      cb.njob = pb.njob = cn;
-      for (int q = 0; q < cn; ++q) {
-        const int j = c0 + q;
-        QrWork& wj = w[j];
-        PanelArgs& a = pb.a[q];
-        a.S = b.S + j * b.sS;
-        a.ldS = b.ldS;
-        a.n = n;
-        a.j0 = j0;
-        a.nb = nb;
-        a.V = wj.vstore + vo[p];
-        a.ldV = round_up(len, 8);
-        a.Zf = (p & 1) ? wj.zf2 : wj.zf;
-        a.Zo = wj.zo + zo[p];
-        a.sign = wj.sign;
-        a.part = wj.part;
-        a.dg = wj.dg;
-        a.gram = wj.gram;
-        a.T = wj.T;
-        a.counter = wj.counters + p;
-        a.err = wj.err;
-        a.pred = job_pred(j);
-        a.pred2 = wj.fail + p;
-        CholArgs& ca = cb.a[q];
-        ca.S = a.S;
-        ca.ldS = a.ldS;
-        ca.n = n;
-        ca.j0 = j0;
-        ca.nb = nb;
-        ca.V = a.V;
-        ca.ldV = a.ldV;
-        ca.Zf = a.Zf;
-        ca.Zo = a.Zo;
-        ca.sign = wj.sign;
-        ca.T = wj.T;
-        ca.part = wj.part64;
-        ca.gram = wj.gram64;
-        ca.bcast = wj.bcast;
-        ca.counter = wj.counters + np + p;
-        ca.err = wj.err;
-        ca.pred = a.pred;
-        ca.fail = wj.fail + p;
-      }
-      void* ev = nullptr;
-      const bool timed = timing_on();
-      if (timed) timing_record_begin(stream, &ev);
-      void* cargs[] = {&cb};
-      MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_chol_kernel, dim3(Gp * cn),
-                                               dim3(TPB), cargs, 0, stream));
-      void* kargs[] = {&pb};
-      MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_kernel, dim3(Gp * cn),
-                                               dim3(TPB), kargs, 0, stream));
-      if (timed) timing_record_end(stream, ev, TAG_QR_PANEL, 0.0);
-    }
-    if (mt <= 0) continue;
-    float* Strail = b.S + (int64_t)(j0 + nb) * b.ldS + j0;
+    if (mt <= 0) return MAO_OK;
+    float* Strail = b->S + (int64_t)(j0 + nb) * b->ldS + j0;
     if (p == 0) {
       // W_0 = S_trail V_0^T   (mt x nb)
-      MAO_TRY(skinny_product(mt, nb, len, Strail, b.ldS, b.sS, w[0].vstore + vo[p], round_up(len, 8),
-                             wsf, w[0].wbuf, w[0].wparts, wsf, nj, b.pred, b.spred, stream));
-      continue;
+      return skinny_product(mt, nb, len, Strail, b->ldS, b->sS, w[0].vstore + vo[p],
+                            round_up(len, 8), wsf, w[0].wbuf, w[0].wparts, wsf, nj, b->pred,
+                            b->spred, stream);
     }
     // the rest of the trailing rows: panel p-1's update, then W_p = S_trail V_p^T
     QrFusedArgs fc;
     fc.C = Strail;
-    fc.ldC = b.ldS;
-    fc.sC = b.sS;
+    fc.ldC = b->ldS;
+    fc.sC = b->sS;
     fc.W = wprev + (int64_t)nb * NB;  // W_{p-1} rows of S rows >= j0 + nb
     fc.sW = wsf;
     fc.wslices_in = sprev;
     fc.wslice = wsl;
-    fc.Z = zf_prev + (int64_t)NB * NB;
+    fc.Z = zf_of(p - 1) + (int64_t)NB * NB;
     fc.sZ = wsf;
     fc.Vn = w[0].vstore + vo[p];
     fc.ldV = round_up(len, 8);
@@ -1015,37 +1032,120 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
     fc.nb = NB;
     fc.nbn = nb;
     fc.splits = fused_splits(mt, len, nj);
-    fc.prec = b.fact_bf16x3 ? kQrBf16x3 : kQrBf16x6;
-    fc.pred = b.pred;
-    fc.spred = b.spred;
+    fc.prec = prec();
+    fc.pred = b->pred;
+    fc.spred = b->spred;
     MAO_TRY(qr_fused_update(fc, nj, stream));
     wprev = wnext;
     sprev = fc.splits;
     wnext = wnext == w[0].wparts ? w[0].wparts + kQrFusedMaxSplits * wsl : w[0].wparts;
+    return MAO_OK;
   }
 
+  mao_status finish(hipStream_t stream);
+};
+
+// Panel launches of one panel index over jobs of any sizes: each launch takes
+// jobs while their workgroups fit the device at once (the panel kernels need
+// all of them resident) and the job table has room.
+struct PanelRef {
+  const QrRun* run;
+  int j;
+};
+
+mao_status launch_panels(const std::vector<PanelRef>& jobs, int p, hipStream_t stream) {
+  const int slots = panel_slots();
+  size_t k = 0;
+  while (k < jobs.size()) {
+    CholBatch cb;
+    PanelBatch pb;
+    int ng = 0, cn = 0;
+    while (k < jobs.size() && cn < kQrMaxJobs) {
+      PanelArgs a;
+      CholArgs ca;
+      jobs[k].run->panel_args(p, jobs[k].j, a, ca);
+      if (cn > 0 && ng + a.G > slots) break;
+      a.g0 = ca.g0 = ng;
+      ng += a.G;
+      pb.a[cn] = a;
+      cb.a[cn] = ca;
+      ++cn;
+      ++k;
+    }
+    cb.njob = pb.njob = cn;
+    void* ev = nullptr;
+    const bool timed = timing_on();
+    if (timed) timing_record_begin(stream, &ev);
+    void* cargs[] = {&cb};
+    MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_chol_kernel, dim3(ng),
+                                             dim3(TPB), cargs, 0, stream));
+    void* kargs[] = {&pb};
+    MAO_HIP_CHECK(hipLaunchCooperativeKernel((const void*)qr_panel_kernel, dim3(ng), dim3(TPB),
+                                             kargs, 0, stream));
+    if (timed) timing_record_end(stream, ev, TAG_QR_PANEL, 0.0);
+  }
+  return MAO_OK;
+}
+
+}  // namespace
+
+mao_status qr_core_multi(const QrBatch* batches, int ngroups, hipStream_t stream) {
+  std::vector<QrRun> runs;
+  runs.reserve(ngroups);
+  int np = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    if (batches[g].njob <= 0) continue;
+    runs.emplace_back();
+    MAO_TRY(runs.back().setup(batches[g], stream));
+    np = std::max(np, runs.back().np);
+  }
+  // panel index by panel index over every size: the panels of all groups
+  // share launches (the groups are independent; each keeps its own order)
+  std::vector<PanelRef> jobs;
+  for (int p = 0; p < np; ++p) {
+    jobs.clear();
+    for (QrRun& r : runs) {
+      if (p >= r.np) continue;
+      MAO_TRY(r.before_panel(p, stream));
+      for (int j = 0; j < r.nj; ++j) jobs.push_back(PanelRef{&r, j});
+    }
+    MAO_TRY(launch_panels(jobs, p, stream));
+    for (QrRun& r : runs) MAO_TRY(r.after_panel(p, stream));
+  }
+  for (QrRun& r : runs) MAO_TRY(r.finish(stream));
+  return MAO_OK;
+}
+
+mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
+  return qr_core_multi(&b, 1, stream);
+}
+
+namespace {
+
+mao_status QrRun::finish(hipStream_t stream) {
+  const QrBatch& bb = *b;
   // explicit Q: E = Q^T, backward accumulation. The last panel's projection
   // is a plain product (into wbuf); every later one comes out of the previous
   // panel's fused update as partial slices, in two regions of wparts used in
   // turn.
   for (int j = 0; j < nj; ++j)
-    MAO_TRY(fill_identity(view(b.E + j * b.sE, b.ldE), n, job_pred(j), stream));
+    MAO_TRY(fill_identity(view(bb.E + j * bb.sE, bb.ldE), n, job_pred(j), stream));
   float* wcur = w[0].wbuf;
   int s_in = 1;
-  wnext = w[0].wparts;
+  float* wnext = w[0].wparts;
   {
     const int p = np - 1, j0 = p * NB, len = n - j0, nb = std::min(NB, len);
-    float* Esub = b.E + (int64_t)j0 * b.ldE + j0;
-    MAO_TRY(skinny_product(len, nb, len, Esub, b.ldE, b.sE, w[0].vstore + vo[p], round_up(len, 8),
-                           wsf, wcur, w[0].wparts, wsf, nj, b.pred, b.spred, stream));
+    float* Esub = bb.E + (int64_t)j0 * bb.ldE + j0;
+    MAO_TRY(skinny_product(len, nb, len, Esub, bb.ldE, bb.sE, w[0].vstore + vo[p], round_up(len, 8),
+                           wsf, wcur, w[0].wparts, wsf, nj, bb.pred, bb.spred, stream));
   }
   for (int p = np - 1; p >= 1; --p) {
     const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
     const int pp = p - 1, lenn = n - pp * NB, nbn = std::min(NB, lenn);
     QrFusedArgs fa;
-    fa.C = b.E + (int64_t)j0 * b.ldE + j0;
-    fa.ldC = b.ldE;
-    fa.sC = b.sE;
+    fa.C = bb.E + (int64_t)j0 * bb.ldE + j0;
+    fa.ldC = bb.ldE;
+    fa.sC = bb.sE;
     fa.sW = wsf;
     fa.Z = w[0].zo + zo[p];
     fa.sZ = wsf;
@@ -1062,8 +1162,8 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
     fa.L = len;
     fa.nb = nb;
     fa.nbn = nbn;
-    fa.pred = b.pred;
-    fa.spred = b.spred;
+    fa.pred = bb.pred;
+    fa.spred = bb.spred;
     fa.W = wcur;
     fa.wslices_in = s_in;
     fa.wslice = wsl;
@@ -1078,25 +1178,25 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
     const int64_t count = (int64_t)n * NB;
     const int blocks = (int)std::min<int64_t>(1024, (count + 255) / 256);
     hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks, nj), dim3(256), 0, stream, w[0].wbuf, wcur,
-                       wsl, s_in, count, wsf, b.pred, b.spred);
+                       wsl, s_in, count, wsf, bb.pred, bb.spred);
     MAO_LAUNCH_CHECK();
     wcur = w[0].wbuf;
   }
   {
     // first block: column signs, and each job's Q written as the transposed copy
     const int len = n, nb = std::min(NB, len);
-    float* Esub = b.E;
+    float* Esub = bb.E;
     GemmProblem p2 = gemm_problem(len, len, nb, -1.f, wcur, NB, w[0].zo + zo[0], NB, 1.f,
-                                  Esub, b.ldE, Esub, b.ldE, GF_D_F32 | GF_C0_F32);
+                                  Esub, bb.ldE, Esub, bb.ldE, GF_D_F32 | GF_C0_F32);
     p2.batch = nj;
     p2.sA = p2.sB = wsf;
-    p2.sC0 = p2.sD = b.sE;
-    p2.pred = b.pred;
-    p2.spred = b.spred;
+    p2.sC0 = p2.sD = bb.sE;
+    p2.pred = bb.pred;
+    p2.spred = bb.spred;
     p2.row_scale = w[0].sign;
     p2.srs = wsf;
     bool anyq = false;
-    for (int j = 0; j < nj; ++j) anyq = anyq || (b.Q && b.Q[j]);
+    for (int j = 0; j < nj; ++j) anyq = anyq || (bb.Q && bb.Q[j]);
     if (!anyq) {
       MAO_TRY(launch_gemm(MAO_F32, &p2, 1, stream, TAG_QR));
     } else {
@@ -1109,13 +1209,13 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
           pq[q].batch = 1;
           pq[q].A = wcur + j * wsf;
           pq[q].B = w[j].zo + zo[0];
-          pq[q].C0 = pq[q].D = Esub + j * b.sE;
+          pq[q].C0 = pq[q].D = Esub + j * bb.sE;
           pq[q].row_scale = w[j].sign;
           pq[q].pred = job_pred(j);
           pq[q].spred = 0;
-          if (b.Q && b.Q[j]) {
-            pq[q].Dt = b.Q[j];
-            pq[q].lddt = b.ldQ[j];
+          if (bb.Q && bb.Q[j]) {
+            pq[q].Dt = bb.Q[j];
+            pq[q].lddt = bb.ldQ[j];
           }
         }
         MAO_TRY(launch_gemm(MAO_F32, pq, cn, stream, TAG_QR));
@@ -1128,16 +1228,16 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
     PoisonArgs pa;
     pa.err = w[0].err;
     pa.err_stride = (int64_t)(wst / sizeof(int));
-    pa.E = b.E;
-    pa.ldE = b.ldE;
-    pa.sE = b.sE;
+    pa.E = bb.E;
+    pa.ldE = bb.ldE;
+    pa.sE = bb.sE;
     for (int q = 0; q < kPoisonJobs; ++q) {
-      const bool has = q < cn && b.Q && b.Q[c0 + q];
-      pa.Q[q] = has ? b.Q[c0 + q] : nullptr;
-      pa.ldQ[q] = has ? b.ldQ[c0 + q] : 0;
+      const bool has = q < cn && bb.Q && bb.Q[c0 + q];
+      pa.Q[q] = has ? bb.Q[c0 + q] : nullptr;
+      pa.ldQ[q] = has ? bb.ldQ[c0 + q] : 0;
     }
-    pa.pred = b.pred;
-    pa.spred = b.spred;
+    pa.pred = bb.pred;
+    pa.spred = bb.spred;
     pa.n = n;
     pa.j0 = c0;
     const int blocks = (int)std::min<int64_t>(256, ceil_div((int64_t)n * n, 256));
@@ -1146,6 +1246,8 @@ mao_status qr_core_batched(const QrBatch& b, hipStream_t stream) {
   }
   return MAO_OK;
 }
+
+}  // namespace
 
 mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout, int64_t ldQ,
                    QrWork& w, const int* pred, hipStream_t stream, bool abort_barriers,

@@ -63,6 +63,10 @@ struct QrBatch {
   bool fact_bf16x3 = false;
 };
 mao_status qr_core_batched(const QrBatch& b, hipStream_t stream);
+// Several batches of different sizes refreshed together: panel by panel, the
+// panels of every batch share cooperative launches (the batches are
+// independent; each keeps its own order of steps).
+mao_status qr_core_multi(const QrBatch* batches, int ngroups, hipStream_t stream);
 
 // Fused panel step (qr_update.hip), per job j (pointers advanced by j times
 // their stride): C (M x L, ld ldC) <- C - W Z^T with W (M x nb) the sum of
