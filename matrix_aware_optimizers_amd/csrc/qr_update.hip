@@ -16,8 +16,8 @@
 // the update (W's fragments held in registers for the whole strip, Z's
 // chunk in LDS) turns it into D in place, D leaves by
 // 16-byte stores, and the projection of D onto the chunk of Vn (both in LDS)
-// accumulates in registers. The next chunk's C, Z and Vn are loaded into
-// registers while the current chunk's products run. Split s writes its
+// accumulates in registers. The next chunk's Z and Vn, and C two chunks
+// ahead, are loaded into registers while the current chunk's products run. Split s writes its
 // partial projection into slice s of Wn; the consumer sums the slices (the
 // next panel's call when it loads W, or a summing pass).
 //
@@ -200,18 +200,26 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
     }
   }
 
-  // chunk loads: thread -> 4-float piece (t % 16) of rows t / 16 + 16 i
+  // chunk loads: thread -> 4-float piece (t % 16) of rows t / 16 + 16 i.
+  // Z's and Vn's chunks are loaded one chunk ahead, C's two chunks ahead
+  // (two register buffers used in turn: the HBM read has two chunks' products
+  // to arrive in).
   const int pc = (t & 15) * 4, pr = t >> 4;
-  float4 zr[4], vr[4], cr[4];
-  auto load_chunk = [&](int c0) {
+  float4 zr[4], vr[4], cr0[4], cr1[4];
+  auto load_zv = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = pr + 16 * i;  // Z row (chunk column) / vector index / C row
+      const int row = pr + 16 * i;  // Z row (chunk column) / vector index
       const int zc = c0 + row;
       zr[i] = zc < L ? ld4(Z + (int64_t)zc * FK, pc, nb) : make_float4(0.f, 0.f, 0.f, 0.f);
       vr[i] = row < nbn ? ld4(Vn + (int64_t)row * a.ldV + c0, pc, L - c0)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
-      const int cm = r0 + row;
+    }
+  };
+  auto load_c = [&](int c0, float4 (&cr)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cm = r0 + pr + 16 * i;
       cr[i] = cm < M ? ld4(C + (int64_t)cm * a.ldC + c0, pc, L - c0)
                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -221,9 +229,7 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
 #pragma unroll
   for (int v = 0; v < 16; ++v) accp[v] = 0.f;
 
-  if (ch0 < ch1) load_chunk(ch0 * FC);
-#pragma unroll 1
-  for (int ch = ch0; ch < ch1; ++ch) {
+  auto step = [&](int ch, float4 (&cr)[4]) __attribute__((always_inline)) {
     const int c0 = ch * FC;
     __syncthreads();  // the previous chunk's reads of Zs, Vs, Ds are done
 #pragma unroll
@@ -234,7 +240,8 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
       *(float4*)&Ds[row * LDF + pc] = cr[i];
     }
     __syncthreads();
-    if (ch + 1 < ch1) load_chunk(c0 + FC);  // in flight during the products
+    if (ch + 1 < ch1) load_zv(c0 + FC);     // in flight during the products
+    if (ch + 2 < ch1) load_c(c0 + 2 * FC, cr);
 
     // update: acc = W[rows of rb] Z[cols of cb]^T over k < 64
     f32x16_t acc;
@@ -277,27 +284,36 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
       }
     }
     // projection: accp += D[rows of rb] Vn[vectors of cb]^T over the chunk
-    if (nbn == 0) continue;  // update only
-    {
-      const float* db = Ds + (rb * 32 + r32) * LDF + 8 * h;
-      const float* vb = Vs + (cb * 32 + r32) * LDF + 8 * h;
+    if (nbn == 0) return;  // update only
+    const float* db = Ds + (rb * 32 + r32) * LDF + 8 * h;
+    const float* vb = Vs + (cb * 32 + r32) * LDF + 8 * h;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const float4 d0 = *(const float4*)(db + 16 * st), d1 = *(const float4*)(db + 16 * st + 4);
-        const float4 v0 = *(const float4*)(vb + 16 * st), v1 = *(const float4*)(vb + 16 * st + 4);
-        if (X6) {
-          uint4 dh, dm, dl, vh, vm, vl;
-          split8x3(d0, d1, dh, dm, dl);
-          split8x3(v0, v1, vh, vm, vl);
-          accp = mfma6(dh, dm, dl, vh, vm, vl, accp);
-        } else {
-          uint4 dh, dl, vh, vl;
-          split8(d0, d1, dh, dl);
-          split8(v0, v1, vh, vl);
-          accp = mfma3(dh, dl, vh, vl, accp);
-        }
+    for (int st = 0; st < 4; ++st) {
+      const float4 d0 = *(const float4*)(db + 16 * st), d1 = *(const float4*)(db + 16 * st + 4);
+      const float4 v0 = *(const float4*)(vb + 16 * st), v1 = *(const float4*)(vb + 16 * st + 4);
+      if (X6) {
+        uint4 dh, dm, dl, vh, vm, vl;
+        split8x3(d0, d1, dh, dm, dl);
+        split8x3(v0, v1, vh, vm, vl);
+        accp = mfma6(dh, dm, dl, vh, vm, vl, accp);
+      } else {
+        uint4 dh, dl, vh, vl;
+        split8(d0, d1, dh, dl);
+        split8(v0, v1, vh, vl);
+        accp = mfma3(dh, dl, vh, vl, accp);
       }
     }
+  };
+
+  if (ch0 < ch1) {
+    load_zv(ch0 * FC);
+    load_c(ch0 * FC, cr0);
+  }
+  if (ch0 + 1 < ch1) load_c((ch0 + 1) * FC, cr1);
+#pragma unroll 1
+  for (int ch = ch0; ch < ch1; ch += 2) {
+    step(ch, cr0);
+    if (ch + 1 < ch1) step(ch + 1, cr1);
   }
 
   // this split's partial Wn rows of the strip
