@@ -15,7 +15,9 @@ instrumentation), the dominant kernel's roofline (the Newton-Schulz
 contraction, from HIP events around every launch of a second region of K
 steps), the fp64 CPU oracle's rate on a bounded sample of the workload's own
 matrices, and -- under "soap8b" -- the same 8B layer under SOAP (steps/s and
-the rate of its contractions against the fp32 and bf16 peaks). SOAP and FOAM
+the rate of its contractions against the fp32 and bf16 peaks), and under "moe"
+and "foam760m" the MoE expert bank under Muon+ and the GPT-2-760M set under
+FOAM (steps/s and their dominant kernel's roofline). SOAP and FOAM
 workloads run their fp32-accurate products (forward rotations, power-
 iteration and criterion products) as bf16x3 by default (--fwd,
 --refresh-prod) and the rotation back on bf16 MFMA (--back).
@@ -593,6 +595,39 @@ def soap8b_summary(args):
     return out
 
 
+def other_configs(args):
+    """The MoE expert bank under Muon+ and the GPT-2-760M set under FOAM
+    (the pages' other two workloads at full size), each timed on its own for
+    --others-steps steps (FOAM: from t = 2, so its criterion and refresh at
+    t = 11 fall inside a 10-step region); compact lines next to the default
+    one."""
+    import gc
+
+    import torch
+
+    import synth
+    out = {}
+    for name in ("moe", "foam760m"):
+        gc.collect()
+        torch.cuda.empty_cache()
+        sub = argparse.Namespace(**vars(args))
+        sub.steps, sub.warmup, sub.no_cpu_baseline = args.others_steps, 1 if name == "foam760m" else 2, True
+        if name == "moe":
+            line = run_muon(sub, "moe128_expert_bank_muonplus_bf16", moe_groups(), "col_row",
+                            (1536, 2048, "c4", 0))
+        else:
+            line = run_soaplike(sub, "gpt2_760m_foam", "foam", "c5", synth.specs("c5"), "f32", "f32",
+                                embedding=(synth.GPT2_VOCAB, synth.GPT2_760M_WIDTH),
+                                back=args.back, fwd=args.fwd, prod=args.refresh_prod)
+        r = line["roofline"]
+        out[name] = {"workload": line["config"]["workload"], "value": line["value"],
+                     "unit": line["unit"], "ms_per_step": line["ms_per_step"],
+                     "steps": sub.steps, "warmup": sub.warmup,
+                     "roofline": {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                                    "kernel")}}
+    return out
+
+
 def run_observe(args):
     """The observability reductions over the Llama-8B layer set, each timed on
     its own with events on the library's stream: the update RMS of the five
@@ -689,6 +724,9 @@ def main():
     ap.add_argument("--soap8b-steps", type=int, default=5,
                     help="timed steps of the 8B layer under SOAP reported beside the default "
                          "workload (0: skip)")
+    ap.add_argument("--others-steps", type=int, default=10,
+                    help="timed steps of the MoE bank (Muon+) and of GPT-2-760M (FOAM) reported "
+                         "beside the default workload (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (a known-size reference "
                          "for profiler byte counters)")
@@ -700,7 +738,7 @@ def main():
         write_traffic(*args.write_traffic,
                       command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python3 "
                               "bench.py --steps 2 --warmup 1 --no-cpu-baseline --soap8b-steps 0 "
-                              "--calibrate-copy")
+                              "--others-steps 0 --calibrate-copy")
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build's step runs whole matrices on one device "
@@ -726,6 +764,8 @@ def main():
             gc.collect()
             torch.cuda.empty_cache()
             line["soap8b"] = soap8b_summary(args)
+        if args.others_steps > 0:
+            line.update(other_configs(args))
     elif args.workload == "moe":
         line = run_muon(args, "moe128_expert_bank_muonplus_bf16", moe_groups(), "col_row",
                         (1536, 2048, "c4", 0))
