@@ -833,6 +833,8 @@ QrWork carve_qr_work(Carver& c, int n) {
   w.part64 = c.take<double>((size_t)G * NU);
   w.gram64 = c.take<double>(NU);
   w.bcast = c.take<double>(NB * NB + NB);
+  w.zsp = c.take<bf16_t>((size_t)3 * n * NB);
+  w.vsp = c.take<bf16_t>((size_t)3 * NB * round_up(n, 8));
   return w;
 }
 
@@ -921,6 +923,53 @@ struct QrRun {
 
   float* zf_of(int p) const { return (p & 1) ? w[0].zf2 : w[0].zf; }
 
+  // the split operands of this group's fused passes: Z parts zpart apart at
+  // row pitch 64, vector parts vpart apart at row pitch ldvp
+  int64_t zpart() const { return (int64_t)n * NB; }
+  int64_t ldvp() const { return round_up(n, 8); }
+  int64_t vpart() const { return (int64_t)NB * ldvp(); }
+  int64_t wsb() const { return (int64_t)(wst / sizeof(bf16_t)); }  // job stride, in bf16
+  int parts(int prec) const { return prec == kQrBf16x6 ? 3 : 2; }
+
+  // Z (zrows x 64, columns >= znb zero) and/or V (vrows x vcols at ldv) of
+  // every job into their bf16 parts
+  mao_status presplit(const float* Z, int zrows, int znb, const float* V, int64_t ldv, int vrows,
+                      int vcols, int prec, hipStream_t stream) const {
+    QrSplitArgs sa;
+    sa.Z = Z;
+    sa.sZ = wsf;
+    sa.zrows = Z ? zrows : 0;
+    sa.znb = znb;
+    sa.Zp = w[0].zsp;
+    sa.sZp = wsb();
+    sa.zpart = zpart();
+    sa.V = V;
+    sa.ldV = ldv;
+    sa.sV = wsf;
+    sa.vrows = V ? vrows : 0;
+    sa.vcols = vcols;
+    sa.Vp = w[0].vsp;
+    sa.sVp = wsb();
+    sa.vpart = vpart();
+    sa.ldVp = ldvp();
+    sa.parts = parts(prec);
+    sa.pred = b->pred;
+    sa.spred = b->spred;
+    return qr_presplit(sa, nj, stream);
+  }
+
+  // the fused-pass arguments that point at the split operands (Z from row
+  // zrow0 of its parts, Vn from column vcol0 of its parts)
+  void split_args(QrFusedArgs& f, int zrow0, int vcol0) const {
+    f.Zp = w[0].zsp + (int64_t)zrow0 * NB;
+    f.sZp = wsb();
+    f.zpart = zpart();
+    f.Vp = w[0].vsp + vcol0;
+    f.ldVp = ldvp();
+    f.sVp = wsb();
+    f.vpart = vpart();
+  }
+
   // Factorisation with one panel of look-ahead. W_{p-1} is the projection of
   // panel p-1's trailing rows onto its vectors. Before panel p is factored,
   // only its own rows take panel p-1's update; the rest of the trailing rows
@@ -933,6 +982,8 @@ struct QrRun {
   mao_status before_panel(int p, hipStream_t stream) {
     if (p == 0 || p >= np) return MAO_OK;
     const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
+    // V T^T of panel p-1 (len + NB rows) split once for this step's two passes
+    MAO_TRY(presplit(zf_of(p - 1), len + NB, NB, nullptr, 0, 0, 0, prec(), stream));
     // panel p's rows take panel p-1's update (one 64-column chunk per workgroup)
     QrFusedArgs fa;
     fa.C = b->S + (int64_t)j0 * b->ldS + j0;
@@ -942,8 +993,7 @@ struct QrRun {
     fa.sW = wsf;
     fa.wslices_in = sprev;
     fa.wslice = wsl;
-    fa.Z = zf_of(p - 1) + (int64_t)NB * NB;  // V T^T rows of the columns >= j0
-    fa.sZ = wsf;
+    split_args(fa, NB, 0);  // V T^T rows of the columns >= j0
     fa.M = nb;
     fa.L = len;
     fa.nb = NB;  // panel p-1 is a full panel
@@ -1012,6 +1062,7 @@ struct QrRun {
                             b->spred, stream);
     }
     // the rest of the trailing rows: panel p-1's update, then W_p = S_trail V_p^T
+    MAO_TRY(presplit(nullptr, 0, 0, w[0].vstore + vo[p], round_up(len, 8), nb, len, prec(), stream));
     QrFusedArgs fc;
     fc.C = Strail;
     fc.ldC = b->ldS;
@@ -1020,11 +1071,7 @@ struct QrRun {
     fc.sW = wsf;
     fc.wslices_in = sprev;
     fc.wslice = wsl;
-    fc.Z = zf_of(p - 1) + (int64_t)NB * NB;
-    fc.sZ = wsf;
-    fc.Vn = w[0].vstore + vo[p];
-    fc.ldV = round_up(len, 8);
-    fc.sV = wsf;
+    split_args(fc, NB, 0);
     fc.Wn = wnext;
     fc.sWn = wsf;
     fc.M = mt;
@@ -1142,15 +1189,16 @@ mao_status QrRun::finish(hipStream_t stream) {
   for (int p = np - 1; p >= 1; --p) {
     const int j0 = p * NB, len = n - j0, nb = std::min(NB, len);
     const int pp = p - 1, lenn = n - pp * NB, nbn = std::min(NB, lenn);
+    // V T of panel p and the vectors of panel pp, split
+    MAO_TRY(presplit(w[0].zo + zo[p], len, nb, w[0].vstore + vo[pp], round_up(lenn, 8), nbn,
+                     lenn, kQrBf16x6, stream));
     QrFusedArgs fa;
     fa.C = bb.E + (int64_t)j0 * bb.ldE + j0;
     fa.ldC = bb.ldE;
     fa.sC = bb.sE;
     fa.sW = wsf;
-    fa.Z = w[0].zo + zo[p];
-    fa.sZ = wsf;
     // panel pp's vectors start NB columns left of this block
-    fa.Vn = w[0].vstore + vo[pp] + NB;
+    split_args(fa, 0, NB);
     fa.ldV = round_up(lenn, 8);
     fa.sV = wsf;
     fa.Wn = wnext + (int64_t)NB * NB;

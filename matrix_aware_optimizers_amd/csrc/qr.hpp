@@ -26,6 +26,8 @@ struct QrWork {
   double* part64;    // Gmax x 2080 Gram partials
   double* gram64;    // 2080
   double* bcast;     // 64 x 64 + 64
+  bf16_t* zsp;       // a panel's Z split into up to 3 bf16 parts (3 x n x 64)
+  bf16_t* vsp;       // its vectors split likewise (3 x 64 x round_up(n, 8))
 };
 
 size_t qr_work_bytes(int n);
@@ -87,10 +89,14 @@ struct QrFusedArgs {
   int64_t ldC = 0, sC = 0;
   const float* W = nullptr;
   int64_t sW = 0;
-  const float* Z = nullptr;
-  int64_t sZ = 0;
-  const float* Vn = nullptr;
-  int64_t ldV = 0, sV = 0;
+  // Z and Vn split into bf16 parts by qr_presplit (2 for bf16x3, 3 for
+  // bf16x6): Z's parts at row pitch 64, zpart apart; Vn's at ldVp, vpart
+  // apart; sZp / sVp between jobs
+  const bf16_t* Zp = nullptr;
+  int64_t sZp = 0, zpart = 0;
+  const bf16_t* Vp = nullptr;
+  int64_t ldVp = 0, sVp = 0, vpart = 0;
+  int64_t ldV = 0, sV = 0;  // Vt (the identity rows' source) at ldV, sV
   float* Wn = nullptr;
   int64_t sWn = 0;
   float* Wt = nullptr;
@@ -105,6 +111,25 @@ struct QrFusedArgs {
   int strips = 0;  // set by qr_fused_update
 };
 mao_status qr_fused_update(const QrFusedArgs& a, int njob, hipStream_t stream);
+
+// A panel's Z (zrows x 64, ld 64, columns >= znb zero) and V (vrows x vcols,
+// ld ldV) split into `parts` bf16 arrays for qr_fused_update, per job.
+struct QrSplitArgs {
+  const float* Z = nullptr;
+  int64_t sZ = 0;
+  int zrows = 0, znb = 0;
+  bf16_t* Zp = nullptr;
+  int64_t sZp = 0, zpart = 0;
+  const float* V = nullptr;
+  int64_t ldV = 0, sV = 0;
+  int vrows = 0, vcols = 0;
+  bf16_t* Vp = nullptr;
+  int64_t sVp = 0, vpart = 0, ldVp = 0;
+  int parts = 3;
+  const int* pred = nullptr;
+  int64_t spred = 0;
+};
+mao_status qr_presplit(const QrSplitArgs& a, int njob, hipStream_t stream);
 
 // Householder QR of P given column-major in S (S[j][i] = P[i][j], n x n,
 // leading dimension ldS); S is overwritten. Writes E = Q^T (row-major, ldE)

@@ -14,12 +14,15 @@
 // strips), 4 wavefronts in 2 x 2; the workgroup walks its columns in chunks
 // of 64. Per chunk: C's 64 x 64 block comes in by 16-byte loads into LDS,
 // the update (W's fragments held in registers for the whole strip, Z's
-// chunk in LDS) turns it into D in place, D leaves by
+// chunk in LDS as bf16 parts) turns it into D in place, D leaves by
 // 16-byte stores, and the projection of D onto the chunk of Vn (both in LDS)
 // accumulates in registers. The next chunk's Z and Vn, and C two chunks
 // ahead, are loaded into registers while the current chunk's products run. Split s writes its
 // partial projection into slice s of Wn; the consumer sums the slices (the
 // next panel's call when it loads W, or a summing pass).
+//
+// Z and V come split already (qr_presplit_kernel, once per panel for all
+// strips): only D is split inside the pass.
 //
 // The products run on bf16 MFMA in one of two arithmetics (QrPrec):
 //  * bf16x3 (v_mfma_f32_32x32x16_bf16, fp32 accumulation): every fp32
@@ -125,11 +128,16 @@ __device__ __forceinline__ f32x16_t mfma3(const uint4& ah, const uint4& al, cons
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(AH, BL, acc, 0, 0, 0);
 }
 
+// LDS pitch of a bf16 part row (64 values + 8: the 16-byte operand reads of
+// 8 consecutive rows fall on distinct banks)
+constexpr int LDP = FK + 8;
+
 template <int PREC>
-__global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
+__global__ __launch_bounds__(256, 2) void qr_fused_update_kernel(QrFusedArgs a) {
   constexpr bool X6 = PREC == kQrBf16x6;
-  __shared__ __attribute__((aligned(16))) float Zs[FC * LDF];
-  __shared__ __attribute__((aligned(16))) float Vs[FK * LDF];
+  constexpr int NP = X6 ? 3 : 2;  // bf16 parts of a split operand
+  __shared__ __attribute__((aligned(16))) bf16_t Zs[NP][FC * LDP];  // Z chunk: column x k
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[NP][FK * LDP];  // Vn chunk: vector x column
   __shared__ __attribute__((aligned(16))) float Ds[FR * LDF];  // C, then D, in place
 
   const int job = blockIdx.y;
@@ -157,8 +165,8 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
   const int ch0 = split * per, ch1 = min(nchunks, ch0 + per);
   float* C = a.C + job * a.sC;
   const float* W = a.W + job * a.sW;
-  const float* Z = a.Z + job * a.sZ;
-  const float* Vn = a.Vn + job * a.sV;
+  const bf16_t* Zp = a.Zp + job * a.sZp;
+  const bf16_t* Vp = a.Vp + job * a.sVp;
 
   const int lane = t & 63, wave = t >> 6;
   const int rb = wave >> 1, cb = wave & 1;
@@ -200,21 +208,30 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
     }
   }
 
-  // chunk loads: thread -> 4-float piece (t % 16) of rows t / 16 + 16 i.
-  // Z's and Vn's chunks are loaded one chunk ahead, C's two chunks ahead
-  // (two register buffers used in turn: the HBM read has two chunks' products
-  // to arrive in).
+  // chunk loads. C: thread -> 4-float piece (t % 16) of rows t / 16 + 16 i.
+  // Z and Vn parts: thread -> 16-byte piece (t % 8) of rows t / 8 + 32 i of
+  // every part (Z rows past L and Vn columns past L read as zero; the parts
+  // are zero past nb and past Vn's columns). Z's and Vn's chunks are loaded
+  // one chunk ahead, C's two chunks ahead (two register buffers used in
+  // turn: the HBM read has two chunks' products to arrive in).
   const int pc = (t & 15) * 4, pr = t >> 4;
-  float4 zr[4], vr[4], cr0[4], cr1[4];
+  const int qc = (t & 7) * 8, qr = t >> 3;
+  uint4 zr[2 * NP], vr[2 * NP];
+  float4 cr0[4], cr1[4];
   auto load_zv = [&](int c0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = pr + 16 * i;  // Z row (chunk column) / vector index
-      const int zc = c0 + row;
-      zr[i] = zc < L ? ld4(Z + (int64_t)zc * FK, pc, nb) : make_float4(0.f, 0.f, 0.f, 0.f);
-      vr[i] = row < nbn ? ld4(Vn + (int64_t)row * a.ldV + c0, pc, L - c0)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int x = 0; x < NP; ++x)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = qr + 32 * i;  // Z row (chunk column) / vector index
+        const int zc = c0 + row;
+        uint4 z = make_uint4(0u, 0u, 0u, 0u), v = make_uint4(0u, 0u, 0u, 0u);
+        if (zc < L) z = *(const uint4*)(Zp + x * a.zpart + (int64_t)zc * FK + qc);
+        if (row < nbn && c0 + qc < L)
+          v = *(const uint4*)(Vp + x * a.vpart + (int64_t)row * a.ldVp + c0 + qc);
+        zr[2 * x + i] = z;
+        vr[2 * x + i] = v;
+      }
   };
   auto load_c = [&](int c0, float4 (&cr)[4]) {
 #pragma unroll
@@ -233,12 +250,15 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
     const int c0 = ch * FC;
     __syncthreads();  // the previous chunk's reads of Zs, Vs, Ds are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = pr + 16 * i;
-      *(float4*)&Zs[row * LDF + pc] = zr[i];
-      *(float4*)&Vs[row * LDF + pc] = vr[i];
-      *(float4*)&Ds[row * LDF + pc] = cr[i];
-    }
+    for (int x = 0; x < NP; ++x)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = qr + 32 * i;
+        *(uint4*)&Zs[x][row * LDP + qc] = zr[2 * x + i];
+        *(uint4*)&Vs[x][row * LDP + qc] = vr[2 * x + i];
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(float4*)&Ds[(pr + 16 * i) * LDF + pc] = cr[i];
     __syncthreads();
     if (ch + 1 < ch1) load_zv(c0 + FC);     // in flight during the products
     if (ch + 2 < ch1) load_c(c0 + 2 * FC, cr);
@@ -248,16 +268,15 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
     {
-      const float* zb = Zs + (cb * 32 + r32) * LDF + 8 * h;
+      const int zo = (cb * 32 + r32) * LDP + 8 * h;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const float4 z0 = *(const float4*)(zb + 16 * st), z1 = *(const float4*)(zb + 16 * st + 4);
-        uint4 zh, zm, zl;
+        const uint4 zh = *(const uint4*)&Zs[0][zo + 16 * st];
+        const uint4 zl = *(const uint4*)&Zs[NP - 1][zo + 16 * st];
         if (X6) {
-          split8x3(z0, z1, zh, zm, zl);
+          const uint4 zm = *(const uint4*)&Zs[1][zo + 16 * st];
           acc = mfma6(wh[st], wm[st], wl[st], zh, zm, zl, acc);
         } else {
-          split8(z0, z1, zh, zl);
           acc = mfma3(wh[st], wl[st], zh, zl, acc);
         }
       }
@@ -286,20 +305,20 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
     // projection: accp += D[rows of rb] Vn[vectors of cb]^T over the chunk
     if (nbn == 0) return;  // update only
     const float* db = Ds + (rb * 32 + r32) * LDF + 8 * h;
-    const float* vb = Vs + (cb * 32 + r32) * LDF + 8 * h;
+    const int vo = (cb * 32 + r32) * LDP + 8 * h;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const float4 d0 = *(const float4*)(db + 16 * st), d1 = *(const float4*)(db + 16 * st + 4);
-      const float4 v0 = *(const float4*)(vb + 16 * st), v1 = *(const float4*)(vb + 16 * st + 4);
+      const uint4 vh = *(const uint4*)&Vs[0][vo + 16 * st];
+      const uint4 vl = *(const uint4*)&Vs[NP - 1][vo + 16 * st];
       if (X6) {
-        uint4 dh, dm, dl, vh, vm, vl;
+        const uint4 vm = *(const uint4*)&Vs[1][vo + 16 * st];
+        uint4 dh, dm, dl;
         split8x3(d0, d1, dh, dm, dl);
-        split8x3(v0, v1, vh, vm, vl);
         accp = mfma6(dh, dm, dl, vh, vm, vl, accp);
       } else {
-        uint4 dh, dl, vh, vl;
+        uint4 dh, dl;
         split8(d0, d1, dh, dl);
-        split8(v0, v1, vh, vl);
         accp = mfma3(dh, dl, vh, vl, accp);
       }
     }
@@ -328,7 +347,63 @@ __global__ __launch_bounds__(256) void qr_fused_update_kernel(QrFusedArgs a) {
   }
 }
 
+// Z (zrows x 64 at leading dimension 64, columns >= znb taken as zero) and
+// V (vrows x vcols at ldV) of a panel split into their bf16 parts, 8 values
+// per thread and part: Z's parts at row pitch 64, V's at ldVp (zero from
+// vcols to the next multiple of 8).
+__global__ __launch_bounds__(256) void qr_presplit_kernel(QrSplitArgs a) {
+  const int job = blockIdx.y;
+  if (a.pred != nullptr && a.pred[job * a.spred] == 0) return;
+  const int64_t zq = (int64_t)a.zrows * 8;  // 8-value pieces of Z
+  const int vc8 = (a.vcols + 7) / 8;
+  const int64_t total = zq + (int64_t)a.vrows * vc8;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    float x[8];
+    bf16_t* dst;
+    int64_t part;
+    if (q < zq) {
+      const int row = (int)(q >> 3), c = (int)(q & 7) * 8;
+      const float* src = a.Z + job * a.sZ + (int64_t)row * FK + c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = c + e < a.znb ? src[e] : 0.f;
+      dst = a.Zp + job * a.sZp + (int64_t)row * FK + c;
+      part = a.zpart;
+    } else {
+      const int64_t v = q - zq;
+      const int row = (int)(v / vc8), c = (int)(v % vc8) * 8;
+      const float* src = a.V + job * a.sV + (int64_t)row * a.ldV + c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = c + e < a.vcols ? src[e] : 0.f;
+      dst = a.Vp + job * a.sVp + (int64_t)row * a.ldVp + c;
+      part = a.vpart;
+    }
+    const float4 x0 = make_float4(x[0], x[1], x[2], x[3]), x1 = make_float4(x[4], x[5], x[6], x[7]);
+    uint4 hi, mid, lo;
+    if (a.parts == 3) {
+      split8x3(x0, x1, hi, mid, lo);
+      *(uint4*)(dst + part) = mid;
+      *(uint4*)(dst + 2 * part) = lo;
+    } else {
+      split8(x0, x1, hi, lo);
+      *(uint4*)(dst + part) = lo;
+    }
+    *(uint4*)dst = hi;
+  }
+}
+
 }  // namespace
+
+mao_status qr_presplit(const QrSplitArgs& a, int njob, hipStream_t stream) {
+  if (njob <= 0) return MAO_OK;
+  if (a.parts != 2 && a.parts != 3) return MAO_E_UNSUPPORTED;
+  const int64_t total = (int64_t)a.zrows * 8 + (int64_t)a.vrows * ((a.vcols + 7) / 8);
+  if (total <= 0) return MAO_OK;
+  const int blocks = (int)std::min<int64_t>(1024, (total + 255) / 256);
+  hipLaunchKernelGGL(qr_presplit_kernel, dim3(blocks, njob), dim3(256), 0, stream, a);
+  MAO_LAUNCH_CHECK();
+  return MAO_OK;
+}
 
 mao_status qr_fused_update(const QrFusedArgs& args, int njob, hipStream_t stream) {
   QrFusedArgs a = args;
