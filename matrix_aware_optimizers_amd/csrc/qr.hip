@@ -62,7 +62,9 @@ struct PanelArgs {
   int* err;
   const int* pred;
   const int* pred2;  // run only when *pred2 != 0 (the fast panel gave up)
-  int g0, G;         // this job's workgroups [g0, g0 + G) of the launch
+  int g0, G;         // the segment's first workgroup in the launch; workgroups per job
+  int cnt;           // jobs in the segment (consecutive jobs of one size)
+  int64_t wst, sS, spred;  // job strides: workspace (bytes), S (floats), pred (ints)
 };
 
 __device__ void grid_barrier(unsigned* counter, unsigned target, int* err) {
@@ -84,34 +86,51 @@ __device__ void grid_barrier(unsigned* counter, unsigned target, int* err) {
   __threadfence();
 }
 
-// Up to kQrMaxJobs panels per launch, of any sizes: job jb owns workgroups
-// [g0, g0 + G) (G = ceil(len / 256) for its panel); its barriers count only
-// its own workgroups.
+// Up to kQrMaxJobs segments per launch, of any sizes. A segment is cnt
+// consecutive jobs of one size whose buffers sit at fixed strides; it owns
+// workgroups [g0, g0 + cnt G) (G = ceil(len / 256) for its panel), job i of
+// it the i-th run of G, and a job's barriers count only its own workgroups.
 constexpr int kQrMaxJobs = 16;
 struct PanelBatch {
   PanelArgs a[kQrMaxJobs];
   int njob;
 };
 
+// a workspace pointer of job 0 moved off bytes on (never null)
+template <typename T>
+__device__ __forceinline__ T* at_bytes(T* p, int64_t off) {
+  return (T*)((char*)p + off);
+}
+
+// The segment of this workgroup, its job in the segment (*jl) and its index
+// in that job's workgroups (*g).
 template <typename Args>
-__device__ __forceinline__ int job_of(const Args* a, int njob) {
-  int jb = 0;
-  while (jb + 1 < njob && (int)blockIdx.x >= a[jb + 1].g0) ++jb;
-  return jb;
+__device__ __forceinline__ int seg_of(const Args* a, int njob, int* jl, int* g) {
+  int sg = 0;
+  while (sg + 1 < njob && (int)blockIdx.x >= a[sg + 1].g0) ++sg;
+  const int rel = (int)blockIdx.x - a[sg].g0;
+  *jl = rel / a[sg].G;
+  *g = rel - *jl * a[sg].G;
+  return sg;
 }
 
 __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
-  const PanelArgs& a = B.a[job_of(B.a, B.njob)];
+  int jl, g;
+  const PanelArgs& a = B.a[seg_of(B.a, B.njob, &jl, &g)];
+  // job jl's buffers: workspace pointers ob bytes on, S so floats on (offsets
+  // applied at each use, so the pointers stay reloadable kernel arguments)
+  const int64_t ob = jl * a.wst, so = jl * a.sS;
+  const int* const pred = a.pred ? a.pred + jl * a.spred : nullptr;
   const int G = a.G;
-  if (a.pred != nullptr && *a.pred == 0) return;
-  if (a.pred2 != nullptr && *a.pred2 == 0) return;
+  if (pred != nullptr && *pred == 0) return;
+  if (a.pred2 != nullptr && *at_bytes(a.pred2, ob) == 0) return;
   __shared__ float X[NB][LDX];
   __shared__ float red[NB][LDX];
   __shared__ float Tl[NB][NB + 1];
   __shared__ float qs[4][NB];
   __shared__ float tot[NB], dgv[NB], taus[NB], betas[NB];
 
-  const int t = threadIdx.x, g = blockIdx.x - a.g0;
+  const int t = threadIdx.x;
   const int n = a.n, j0 = a.j0, nb = a.nb;
   const int r = j0 + g * TPB + t;
   const bool valid = r < n;
@@ -120,7 +139,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
     float xv[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      xv[u] = (valid && k0 + u < nb) ? a.S[(int64_t)(j0 + k0 + u) * a.ldS + r] : 0.f;
+      xv[u] = (valid && k0 + u < nb) ? (a.S + so)[(int64_t)(j0 + k0 + u) * a.ldS + r] : 0.f;
 #pragma unroll
     for (int u = 0; u < 16; ++u) X[k0 + u][t] = xv[u];
   }
@@ -133,7 +152,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
     const bool below = valid && r > j;
     const bool pivot = valid && r == j;
     for (int k = jj; k < nb; ++k) red[k][t] = below ? xa * X[k][t] : 0.f;
-    float* dgb = a.dg + (jj & 1) * NB;
+    float* dgb = at_bytes(a.dg, ob) + (jj & 1) * NB;
     if (pivot)
       for (int k = jj; k < nb; ++k) dgb[k] = X[k][t];
     __syncthreads();
@@ -145,9 +164,9 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
       qs[q][v] = s;
     }
     __syncthreads();
-    float* pb = a.part + (size_t)(jj & 1) * G * NB;
+    float* pb = at_bytes(a.part, ob) + (size_t)(jj & 1) * G * NB;
     if (t < NB) pb[g * NB + t] = qs[0][t] + qs[1][t] + qs[2][t] + qs[3][t];
-    grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+    grid_barrier(at_bytes(a.counter, ob), ++bar * (unsigned)G, at_bytes(a.err, ob));
     {
       // every thread sums a quarter of the workgroups' partials of one value
       // (independent loads in flight together), then a fixed-order combine
@@ -192,7 +211,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
 
   // V panel out (nb x len)
   if (valid)
-    for (int k = 0; k < nb; ++k) a.V[(int64_t)k * a.ldV + (r - j0)] = X[k][t];
+    for (int k = 0; k < nb; ++k) at_bytes(a.V, ob)[(int64_t)k * a.ldV + (r - j0)] = X[k][t];
 
   // partial Gram V^T V (strictly upper part)
   for (int e = t; e < NB * NB; e += TPB) {
@@ -200,9 +219,9 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
     float s = 0.f;
     if (i < k && k < nb)
       for (int u = 0; u < TPB; ++u) s += X[i][u] * X[k][u];
-    a.gram[(size_t)g * NB * NB + e] = s;
+    at_bytes(a.gram, ob)[(size_t)g * NB * NB + e] = s;
   }
-  grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+  grid_barrier(at_bytes(a.counter, ob), ++bar * (unsigned)G, at_bytes(a.err, ob));
 
   if (g == 0) {
     for (int e = t; e < NB * NB; e += TPB) {
@@ -210,7 +229,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
       const int i = e >> 6, k = e & 63;
       if (i < k && k < nb) {
 #pragma unroll 8
-        for (int gg = 0; gg < G; ++gg) s += a.gram[(size_t)gg * NB * NB + e];
+        for (int gg = 0; gg < G; ++gg) s += at_bytes(a.gram, ob)[(size_t)gg * NB * NB + e];
       }
       red[i][k] = s;
     }
@@ -227,16 +246,16 @@ __global__ __launch_bounds__(TPB) void qr_panel_kernel(PanelBatch B) {
       }
       __syncthreads();
     }
-    for (int e = t; e < NB * NB; e += TPB) a.T[e] = Tl[e >> 6][e & 63];
-    if (t < nb) a.sign[j0 + t] = betas[t] < 0.f ? -1.f : 1.f;
+    for (int e = t; e < NB * NB; e += TPB) at_bytes(a.T, ob)[e] = Tl[e >> 6][e & 63];
+    if (t < nb) at_bytes(a.sign, ob)[j0 + t] = betas[t] < 0.f ? -1.f : 1.f;
   }
-  grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+  grid_barrier(at_bytes(a.counter, ob), ++bar * (unsigned)G, at_bytes(a.err, ob));
 
-  for (int e = t; e < NB * NB; e += TPB) Tl[e >> 6][e & 63] = a.T[e];
+  for (int e = t; e < NB * NB; e += TPB) Tl[e >> 6][e & 63] = at_bytes(a.T, ob)[e];
   __syncthreads();
   if (valid) {
-    float* zf = a.Zf + (int64_t)(r - j0) * NB;
-    float* zo = a.Zo + (int64_t)(r - j0) * NB;
+    float* zf = at_bytes(a.Zf, ob) + (int64_t)(r - j0) * NB;
+    float* zo = at_bytes(a.Zo, ob) + (int64_t)(r - j0) * NB;
     float vr[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) vr[i] = (i < nb) ? X[i][t] : 0.f;
@@ -294,8 +313,11 @@ struct CholArgs {
   int* err;
   const int* pred;
   int* fail;       // set to 1 when the panel falls back to the Householder kernel
-  int g0, G;       // this job's workgroups [g0, g0 + G) of the launch
+  int g0, G;       // the segment's first workgroup in the launch; workgroups per job
+  int cnt;         // jobs in the segment
+  int64_t wst, sS, spred;  // job strides: workspace (bytes), S (floats), pred (ints)
 };
+
 
 __device__ __forceinline__ int upk(int i, int k) { return i * NB - (i * (i - 1)) / 2 + (k - i); }
 
@@ -314,9 +336,14 @@ struct CholBatch {
 static_assert(sizeof(CholBatch) <= 4096 && sizeof(PanelBatch) <= 4096, "kernel argument size");
 
 __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
-  const CholArgs& a = B.a[job_of(B.a, B.njob)];
+  int jl, g;
+  const CholArgs& a = B.a[seg_of(B.a, B.njob, &jl, &g)];
+  // job jl's buffers: workspace pointers ob bytes on, S so floats on (offsets
+  // applied at each use, so the pointers stay reloadable kernel arguments)
+  const int64_t ob = jl * a.wst, so = jl * a.sS;
+  const int* const pred = a.pred ? a.pred + jl * a.spred : nullptr;
   const int G = a.G;
-  if (a.pred != nullptr && *a.pred == 0) return;
+  if (pred != nullptr && *pred == 0) return;
   __shared__ float X[NB][LDX];      // current Y (fp32), later V
   __shared__ __attribute__((aligned(16))) double Gs[NB][LDG];  // Gram / LU work
   __shared__ __attribute__((aligned(16))) double Rt[NB][LDG];  // Cholesky factor R (row k = R[k][.]); later U
@@ -326,7 +353,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
   __shared__ double red64[TPB];
   __shared__ int bad;
 
-  const int t = threadIdx.x, g = blockIdx.x - a.g0;
+  const int t = threadIdx.x;
   const int n = a.n, j0 = a.j0, nb = a.nb, len = n - j0;
   const int r = j0 + g * TPB + t;
   const bool valid = r < n;
@@ -336,7 +363,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
     float xv[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      xv[u] = (valid && k0 + u < nb) ? a.S[(int64_t)(j0 + k0 + u) * a.ldS + r] : 0.f;
+      xv[u] = (valid && k0 + u < nb) ? (a.S + so)[(int64_t)(j0 + k0 + u) * a.ldS + r] : 0.f;
 #pragma unroll
     for (int u = 0; u < 16; ++u) X[k0 + u][t] = xv[u];
   }
@@ -394,10 +421,10 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
       __syncthreads();
       for (int idx = t; idx < NB * NB; idx += TPB) {
         const int i = idx / NB, k = idx % NB;
-        if (i <= k) a.part[(size_t)g * NU + upk(i, k)] = Gs[i][k];
+        if (i <= k) at_bytes(a.part, ob)[(size_t)g * NU + upk(i, k)] = Gs[i][k];
       }
     }
-    grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+    grid_barrier(at_bytes(a.counter, ob), ++bar * (unsigned)G, at_bytes(a.err, ob));
     // ---- reduce the partials: workgroup g owns a contiguous range of entries;
     // `sub` threads share an entry, each summing every sub-th partial (loads
     // in flight together), then one of them adds the sub sums in order.
@@ -412,16 +439,16 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
         if (t < slots && e < e1) {
           int gg = q;
           for (; gg + 3 * sub < G; gg += 4 * sub) {
-            const double v0 = a.part[(size_t)gg * NU + e];
-            const double v1 = a.part[(size_t)(gg + sub) * NU + e];
-            const double v2 = a.part[(size_t)(gg + 2 * sub) * NU + e];
-            const double v3 = a.part[(size_t)(gg + 3 * sub) * NU + e];
+            const double v0 = at_bytes(a.part, ob)[(size_t)gg * NU + e];
+            const double v1 = at_bytes(a.part, ob)[(size_t)(gg + sub) * NU + e];
+            const double v2 = at_bytes(a.part, ob)[(size_t)(gg + 2 * sub) * NU + e];
+            const double v3 = at_bytes(a.part, ob)[(size_t)(gg + 3 * sub) * NU + e];
             sum += v0;
             sum += v1;
             sum += v2;
             sum += v3;
           }
-          for (; gg < G; gg += sub) sum += a.part[(size_t)gg * NU + e];
+          for (; gg < G; gg += sub) sum += at_bytes(a.part, ob)[(size_t)gg * NU + e];
         }
         __syncthreads();
         red64[t] = sum;
@@ -429,19 +456,19 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
         if (t < slots && q == 0 && e < e1) {
           double tot = 0.0;
           for (int u = 0; u < sub; ++u) tot += red64[t + u];
-          a.gram[e] = tot;
+          at_bytes(a.gram, ob)[e] = tot;
         }
         __syncthreads();
       }
     }
-    grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+    grid_barrier(at_bytes(a.counter, ob), ++bar * (unsigned)G, at_bytes(a.err, ob));
     // ---- Gram into LDS (symmetric), identity on the padded columns, shift
     {
       double gv[NB * NB / TPB];
 #pragma unroll
       for (int u = 0; u < NB * NB / TPB; ++u) {
         const int idx = t + u * TPB, i = idx >> 6, k = idx & 63;
-        gv[u] = (i < nb && k < nb) ? a.gram[i <= k ? upk(i, k) : upk(k, i)] : (i == k ? 1.0 : 0.0);
+        gv[u] = (i < nb && k < nb) ? at_bytes(a.gram, ob)[i <= k ? upk(i, k) : upk(k, i)] : (i == k ? 1.0 : 0.0);
       }
 #pragma unroll
       for (int u = 0; u < NB * NB / TPB; ++u) {
@@ -494,7 +521,7 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
     }
     __syncthreads();
     if (bad) {
-      if (g == 0 && t == 0) *a.fail = 1;
+      if (g == 0 && t == 0) *at_bytes(a.fail, ob) = 1;
       return;  // every workgroup decided alike
     }
     // ---- Y <- Y R^{-1} for this thread's row (forward substitution). Row
@@ -583,24 +610,24 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
         for (int j = l + 1; j < NB; ++j) asm volatile("" : "+v"(w[j]));
       }
 #pragma unroll
-      for (int j = 0; j < NB; ++j) a.T[i * NB + j] = (i < nb && j >= i && j < nb) ? (float)w[j] : 0.f;
+      for (int j = 0; j < NB; ++j) at_bytes(a.T, ob)[i * NB + j] = (i < nb && j >= i && j < nb) ? (float)w[j] : 0.f;
     }
     __syncthreads();
     for (int e = t; e < nb * nb; e += TPB) {
       const int i = e / nb, c = e % nb;
-      a.bcast[i * NB + c] = (i <= c) ? Rt[i][c] : 0.0;
+      at_bytes(a.bcast, ob)[i * NB + c] = (i <= c) ? Rt[i][c] : 0.0;
     }
     if (t < nb) {
-      a.bcast[NB * NB + t] = (double)dsg[t];
-      a.sign[j0 + t] = dsg[t];
+      at_bytes(a.bcast, ob)[NB * NB + t] = (double)dsg[t];
+      at_bytes(a.sign, ob)[j0 + t] = dsg[t];
     }
   }
-  grid_barrier(a.counter, ++bar * (unsigned)G, a.err);
+  grid_barrier(at_bytes(a.counter, ob), ++bar * (unsigned)G, at_bytes(a.err, ob));
   if (g != 0) {
-    for (int e = t; e < nb * nb; e += TPB) Rt[e / nb][e % nb] = a.bcast[(e / nb) * NB + e % nb];
-    if (t < nb) dsg[t] = (float)a.bcast[NB * NB + t];
+    for (int e = t; e < nb * nb; e += TPB) Rt[e / nb][e % nb] = at_bytes(a.bcast, ob)[(e / nb) * NB + e % nb];
+    if (t < nb) dsg[t] = (float)at_bytes(a.bcast, ob)[NB * NB + t];
   }
-  for (int e = t; e < NB * NB; e += TPB) Tl[e >> 6][e & 63] = a.T[e];
+  for (int e = t; e < NB * NB; e += TPB) Tl[e >> 6][e & 63] = at_bytes(a.T, ob)[e];
   if (t < NB) dinv[t] = (t < nb) ? 1.0 / Rt[t][t] : 1.0;  // U diagonal reciprocals
   __syncthreads();
 
@@ -651,9 +678,9 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
   for (int e = t; e < NB * NB; e += TPB) Tt[(e & 63) * LDT + (e >> 6)] = Tl[e >> 6][e & 63];
   __syncthreads();
   if (valid) {
-    for (int k = 0; k < nb; ++k) a.V[(int64_t)k * a.ldV + li] = X[k][t];
-    float* zf = a.Zf + (int64_t)li * NB;
-    float* zo = a.Zo + (int64_t)li * NB;
+    for (int k = 0; k < nb; ++k) at_bytes(a.V, ob)[(int64_t)k * a.ldV + li] = X[k][t];
+    float* zf = at_bytes(a.Zf, ob) + (int64_t)li * NB;
+    float* zo = at_bytes(a.Zo, ob) + (int64_t)li * NB;
     float vr[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) vr[i] = (i < nb) ? X[i][t] : 0.f;
@@ -785,10 +812,25 @@ int panels(int n) { return (n + NB - 1) / NB; }
 // Column splits of a fused panel update over an M x L block: enough
 // workgroups to give every CU about two, while each split keeps at least four
 // 64-column chunks.
+// Column ranges per strip of a fused pass. Every workgroup walks its chunks
+// one after another, so a pass takes (rounds of resident workgroups) x
+// (chunks per workgroup + about 3 for loading W and writing Wn); the split
+// count minimising that is taken (at least 4 chunks per range).
 int fused_splits(int M, int L, int njob) {
   const int strips = (M + NB - 1) / NB, chunks = (L + NB - 1) / NB;
-  const int want = (512 + njob * strips - 1) / (njob * strips);
-  return std::max(1, std::min({kQrFusedMaxSplits, want, chunks / 4}));
+  const int64_t slots = qr_fused_slots();
+  int best = 1;
+  int64_t best_t = INT64_MAX;
+  for (int sp = 1; sp <= kQrFusedMaxSplits; ++sp) {
+    if (sp > 1 && chunks / sp < 4) break;
+    const int64_t wg = (int64_t)njob * strips * sp;
+    const int64_t t = ((wg + slots - 1) / slots) * ((chunks + sp - 1) / sp + 3);
+    if (t < best_t) {
+      best_t = t;
+      best = sp;
+    }
+  }
+  return best;
 }
 int max_groups(int n) { return (n + TPB - 1) / TPB; }
 
@@ -1092,32 +1134,42 @@ struct QrRun {
   mao_status finish(hipStream_t stream);
 };
 
-// Panel launches of one panel index over jobs of any sizes: each launch takes
-// jobs while their workgroups fit the device at once (the panel kernels need
-// all of them resident) and the job table has room.
-struct PanelRef {
-  const QrRun* run;
-  int j;
-};
-
-mao_status launch_panels(const std::vector<PanelRef>& jobs, int p, hipStream_t stream) {
+// Panel launches of one panel index over the jobs of every size group: each
+// launch takes jobs while their workgroups fit the device at once (the panel
+// kernels need all of them resident), as segments of consecutive jobs of one
+// group, while the segment table has room.
+mao_status launch_panels(const std::vector<const QrRun*>& runs, int p, hipStream_t stream) {
   const int slots = panel_slots();
-  size_t k = 0;
-  while (k < jobs.size()) {
+  size_t r = 0;
+  int j = 0;
+  while (r < runs.size()) {
     CholBatch cb;
     PanelBatch pb;
     int ng = 0, cn = 0;
-    while (k < jobs.size() && cn < kQrMaxJobs) {
+    while (r < runs.size() && cn < kQrMaxJobs) {
+      const QrRun& run = *runs[r];
       PanelArgs a;
       CholArgs ca;
-      jobs[k].run->panel_args(p, jobs[k].j, a, ca);
-      if (cn > 0 && ng + a.G > slots) break;
+      run.panel_args(p, j, a, ca);
+      int cnt = std::min(run.nj - j, (slots - ng) / a.G);
+      if (cnt <= 0) {
+        if (cn > 0) break;
+        cnt = 1;
+      }
       a.g0 = ca.g0 = ng;
-      ng += a.G;
+      a.cnt = ca.cnt = cnt;
+      a.wst = ca.wst = (int64_t)run.wst;
+      a.sS = ca.sS = run.b->sS;
+      a.spred = ca.spred = run.b->spred;
+      ng += cnt * a.G;
       pb.a[cn] = a;
       cb.a[cn] = ca;
       ++cn;
-      ++k;
+      j += cnt;
+      if (j == run.nj) {
+        ++r;
+        j = 0;
+      }
     }
     cb.njob = pb.njob = cn;
     void* ev = nullptr;
@@ -1148,15 +1200,15 @@ mao_status qr_core_multi(const QrBatch* batches, int ngroups, hipStream_t stream
   }
   // panel index by panel index over every size: the panels of all groups
   // share launches (the groups are independent; each keeps its own order)
-  std::vector<PanelRef> jobs;
+  std::vector<const QrRun*> live;
   for (int p = 0; p < np; ++p) {
-    jobs.clear();
+    live.clear();
     for (QrRun& r : runs) {
       if (p >= r.np) continue;
       MAO_TRY(r.before_panel(p, stream));
-      for (int j = 0; j < r.nj; ++j) jobs.push_back(PanelRef{&r, j});
+      live.push_back(&r);
     }
-    MAO_TRY(launch_panels(jobs, p, stream));
+    MAO_TRY(launch_panels(live, p, stream));
     for (QrRun& r : runs) MAO_TRY(r.after_panel(p, stream));
   }
   for (QrRun& r : runs) MAO_TRY(r.finish(stream));
