@@ -111,6 +111,8 @@ struct QrFusedArgs {
   int strips = 0;  // set by qr_fused_update
 };
 mao_status qr_fused_update(const QrFusedArgs& a, int njob, hipStream_t stream);
+// Workgroups of qr_fused_update's kernel resident on the current device at once.
+int qr_fused_slots();
 
 // A panel's Z (zrows x 64, ld 64, columns >= znb zero) and V (vrows x vcols,
 // ld ldV) split into `parts` bf16 arrays for qr_fused_update, per job.

@@ -44,6 +44,8 @@
 // rows of E above the current panel are still rows of I, so their
 // projection is a transposed copy of the vectors): Wt[c][i] = Vt[i][c] in
 // slice 0, zero in the other slices.
+#include <atomic>
+
 #include "gemm.hpp"
 #include "qr.hpp"
 
@@ -403,6 +405,23 @@ mao_status qr_presplit(const QrSplitArgs& a, int njob, hipStream_t stream) {
   hipLaunchKernelGGL(qr_presplit_kernel, dim3(blocks, njob), dim3(256), 0, stream, a);
   MAO_LAUNCH_CHECK();
   return MAO_OK;
+}
+
+// Cached per device; threads racing on the first call store the same value.
+int qr_fused_slots() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int slots = cached[dev].load(std::memory_order_relaxed);
+  if (slots == 0) {
+    int cus = 0, b3 = 0, b6 = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b3, qr_fused_update_kernel<kQrBf16x3>, 256, 0) != hipSuccess) b3 = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b6, qr_fused_update_kernel<kQrBf16x6>, 256, 0) != hipSuccess) b6 = 1;
+    slots = std::max(1, cus * std::max(1, std::min(b3, b6)));
+    cached[dev].store(slots, std::memory_order_relaxed);
+  }
+  return slots;
 }
 
 mao_status qr_fused_update(const QrFusedArgs& args, int njob, hipStream_t stream) {
