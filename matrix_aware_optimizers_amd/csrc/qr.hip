@@ -488,10 +488,9 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
       for (int k = 0; k < nb; ++k) Gs[k][k] += sh;
     }
     // ---- Cholesky G = R^T R, row k of R into Rt[k][.], by the first
-    // wavefront alone: lane j keeps column j of G in registers, the pivot
-    // comes from lane k by readlane and row k of R goes round through LDS
-    // (one wavefront's LDS accesses complete in order), so the 64 steps need
-    // no workgroup barrier.
+    // wavefront alone: lane j keeps column j of G in registers and computes
+    // R[k][j]; the pivot and the row's other entries come from their lanes
+    // by readlane, so the 64 steps touch LDS only to store R.
     __syncthreads();
     if (t < NB) {
       const int j = t;
@@ -506,15 +505,13 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
         const double rkk = sqrt(fmax(piv, 1e-300));
         const double rkj = (j == k) ? rkk : gc[k] / rkk;
         if (j >= k) Rt[k][j] = rkj;
-        dinv[j] = rkj;  // row k of R, shared (dinv is rewritten below)
-        __builtin_amdgcn_wave_barrier();
+        // G[i][j] -= R[k][i] R[k][j], R[k][i] from lane i
 #pragma unroll
-        for (int i = k + 1; i < NB; ++i) gc[i] = fma(-dinv[i], rkj, gc[i]);
+        for (int i = k + 1; i < NB; ++i) gc[i] = fma(-lane_d(rkj, i), rkj, gc[i]);
         // keep the updates at this step (the compiler would otherwise sink
         // each one to the step that reads it, keeping every R entry live)
 #pragma unroll
         for (int i = k + 1; i < NB; ++i) asm volatile("" : "+v"(gc[i]));
-        __builtin_amdgcn_wave_barrier();
       }
       dinv[j] = 1.0 / Rt[j][j];  // own write above
       if (j == 0 && badl) bad = 1;
