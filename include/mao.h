@@ -473,10 +473,14 @@ MAO_API mao_status mao_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, in
  * mao_dbg_qr -- mao_qr with test flags (kernel-level checks only).
  * MAO_DBG_QR_ABORT_BARRIERS starts the QR with its time-out flag raised, so
  * that every barrier gives up at once -- what a real time-out does -- and the
- * NaN result above can be checked without waiting for one. Other bits:
- * MAO_E_HPARAM.
+ * NaN result above can be checked without waiting for one.
+ * MAO_DBG_QR_NO_FALLBACK: a CholeskyQR panel that breaks down (and would fall
+ * back to the per-column Householder panel, with the same result) raises the
+ * time-out flag instead, so Q comes out NaN -- a test of a well-conditioned
+ * P then shows that the fast panels ran. Other bits: MAO_E_HPARAM.
  */
 #define MAO_DBG_QR_ABORT_BARRIERS 1
+#define MAO_DBG_QR_NO_FALLBACK 2
 MAO_API mao_status mao_dbg_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n,
                               void* workspace, size_t workspace_bytes, int32_t flags,
                               void* stream);

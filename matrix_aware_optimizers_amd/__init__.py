@@ -529,6 +529,7 @@ def eigh(F, out=None, evals=None, info=None):
 
 
 DBG_QR_ABORT_BARRIERS = 1
+DBG_QR_NO_FALLBACK = 2
 
 
 def qr(P, out=None, dbg_flags: int = 0):

@@ -1629,7 +1629,8 @@ mao_status mao_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n,
 
 mao_status mao_dbg_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_t n,
                       void* workspace, size_t workspace_bytes, int32_t flags, void* stream) {
-  if (flags & ~MAO_DBG_QR_ABORT_BARRIERS) MAO_FAIL(MAO_E_HPARAM, "flags=%d", flags);
+  if (flags & ~(MAO_DBG_QR_ABORT_BARRIERS | MAO_DBG_QR_NO_FALLBACK))
+    MAO_FAIL(MAO_E_HPARAM, "flags=%d", flags);
   MAO_TRY(check_mat("P", P, n, n, ldp, MAO_F32, true));
   MAO_TRY(check_mat("Q", Q, n, n, ldq, MAO_F32, true));
   std::vector<Range> rr = {mat_range(P, 1, n, n, ldp, 0, 4), mat_range(Q, 1, n, n, ldq, 0, 4)};
@@ -1643,7 +1644,8 @@ mao_status mao_dbg_qr(const float* P, int64_t ldp, float* Q, int64_t ldq, int64_
   QrWork w = carve_qr_work(c, (int)n);
   MAO_TRY(transpose(view((void*)P, ldp), view(S, ld), (int)n, (int)n, 1, MAO_F32, s));
   return qr_core(S, ld, (int)n, E, ld, Q, ldq, w, nullptr, s,
-                 (flags & MAO_DBG_QR_ABORT_BARRIERS) != 0);
+                 (flags & MAO_DBG_QR_ABORT_BARRIERS) != 0, false,
+                 (flags & MAO_DBG_QR_NO_FALLBACK) != 0);
 }
 
 // ---- observability ---------------------------------------------------------

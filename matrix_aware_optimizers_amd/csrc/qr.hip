@@ -42,6 +42,7 @@ namespace mao {
 namespace {
 
 constexpr int NB = kQrNB;
+typedef __attribute__((ext_vector_type(4))) double f64x4_t;
 constexpr int TPB = kQrThreads;
 constexpr int LDX = TPB + 1;  // padded LDS row
 
@@ -313,6 +314,7 @@ struct CholArgs {
   int* err;
   const int* pred;
   int* fail;       // set to 1 when the panel falls back to the Householder kernel
+  int no_fallback; // test hook: a breakdown raises the job's time-out flag instead
   int g0, G;       // the segment's first workgroup in the launch; workgroups per job
   int cnt;         // jobs in the segment
   int64_t wst, sS, spred;  // job strides: workspace (bytes), S (floats), pred (ints)
@@ -377,51 +379,34 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
     __syncthreads();
-    // ---- partial Gram of this workgroup's rows: 36 upper 8 x 8 blocks x 7 row chunks
+    // ---- partial Gram of this workgroup's rows on fp64 MFMA (products of
+    // fp32 values are exact in fp64): the 10 upper 16 x 16 blocks (I <= J)
+    // of X^T X over the 256 rows, 4 rows per step, blocks dealt to the
+    // wavefronts in turn
     {
-      double acc[8][8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int w = 0; w < 8; ++w) acc[u][w] = 0.0;
-      const int blk = t % 36, chunk = t / 36;
-      int bi = 0, rem = blk;
-      while (rem >= 8 - bi) {
-        rem -= 8 - bi;
-        ++bi;
-      }
-      const int bk = bi + rem;
-      if (chunk < 7) {
-        const int r0 = chunk * 37, r1 = min(TPB, r0 + 37);
-        for (int q = r0; q < r1; ++q) {
-          double va[8], vb[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            va[u] = (double)X[bi * 8 + u][q];
-            vb[u] = (double)X[bk * 8 + u][q];
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int w = 0; w < 8; ++w) acc[u][w] = fma(va[u], vb[w], acc[u][w]);
+      const int wv = t >> 6, ln = t & 63;
+      for (int blk = wv; blk < 10; blk += 4) {
+        int I = 0, rem = blk;
+        while (rem >= 4 - I) {
+          rem -= 4 - I;
+          ++I;
         }
-      }
-      for (int c = 0; c < 7; ++c) {
-        __syncthreads();
-        if (chunk == c) {
+        const int J = I + rem;
+        f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+        const float* xa = &X[16 * I + (ln & 15)][ln >> 4];
+        const float* xb = &X[16 * J + (ln & 15)][ln >> 4];
+#pragma unroll 8
+        for (int kk = 0; kk < TPB / 4; ++kk)
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[4 * kk], (double)xb[4 * kk], acc, 0,
+                                                     0, 0);
+        // A[i][k] comes from lane i + 16 k, B[k][j] from lane j + 16 k, and
+        // lane ln's v-th result is G[16 I + 4 v + ln / 16][16 J + ln % 16]
+        // (the fp64 16 x 16 layout, checked on the GPU)
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-              const int i = bi * 8 + u, k = bk * 8 + w;
-              if (i <= k) Gs[i][k] = (c == 0 ? 0.0 : Gs[i][k]) + acc[u][w];
-            }
+        for (int v = 0; v < 4; ++v) {
+          const int gi = 16 * I + 4 * v + (ln >> 4), gk = 16 * J + (ln & 15);
+          if (gi <= gk) at_bytes(a.part, ob)[(size_t)g * NU + upk(gi, gk)] = acc[v];
         }
-      }
-      __syncthreads();
-      for (int idx = t; idx < NB * NB; idx += TPB) {
-        const int i = idx / NB, k = idx % NB;
-        if (i <= k) at_bytes(a.part, ob)[(size_t)g * NU + upk(i, k)] = Gs[i][k];
       }
     }
     grid_barrier(at_bytes(a.counter, ob), ++bar * (unsigned)G, at_bytes(a.err, ob));
@@ -518,7 +503,11 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
     }
     __syncthreads();
     if (bad) {
-      if (g == 0 && t == 0) *at_bytes(a.fail, ob) = 1;
+      if (g == 0 && t == 0) {
+        *at_bytes(a.fail, ob) = 1;
+        // test hook: no fallback -- the job's barriers give up, its basis is NaN
+        if (a.no_fallback) atomicExch(at_bytes(a.err, ob), 1);
+      }
       return;  // every workgroup decided alike
     }
     // ---- Y <- Y R^{-1} for this thread's row (forward substitution). Row
@@ -681,24 +670,38 @@ __global__ __launch_bounds__(TPB) void qr_panel_chol_kernel(CholBatch B) {
     float vr[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) vr[i] = (i < nb) ? X[i][t] : 0.f;
-    for (int c = 0; c < NB; ++c) {
-      float sf[4] = {0.f, 0.f, 0.f, 0.f}, so[4] = {0.f, 0.f, 0.f, 0.f};
-      const float4* tf = (const float4*)&Tl[c][0];
-      const float4* to = (const float4*)&Tt[c * LDT];
+    // four columns at a time, so that each row leaves in 16-byte pieces
+    // (each column summed as four interleaved partial sums)
+    for (int c4 = 0; c4 < NB; c4 += 4) {
+      float sf[4][4], so[4][4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sf[cc][q] = so[cc][q] = 0.f;
 #pragma unroll
       for (int i4 = 0; i4 < NB / 4; ++i4) {
-        const float4 f = tf[i4], o = to[i4];
-        sf[0] = fmaf(vr[4 * i4 + 0], f.x, sf[0]);
-        sf[1] = fmaf(vr[4 * i4 + 1], f.y, sf[1]);
-        sf[2] = fmaf(vr[4 * i4 + 2], f.z, sf[2]);
-        sf[3] = fmaf(vr[4 * i4 + 3], f.w, sf[3]);
-        so[0] = fmaf(vr[4 * i4 + 0], o.x, so[0]);
-        so[1] = fmaf(vr[4 * i4 + 1], o.y, so[1]);
-        so[2] = fmaf(vr[4 * i4 + 2], o.z, so[2]);
-        so[3] = fmaf(vr[4 * i4 + 3], o.w, so[3]);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const float4 f = ((const float4*)&Tl[c4 + cc][0])[i4];
+          const float4 o = ((const float4*)&Tt[(c4 + cc) * LDT])[i4];
+          sf[cc][0] = fmaf(vr[4 * i4 + 0], f.x, sf[cc][0]);
+          sf[cc][1] = fmaf(vr[4 * i4 + 1], f.y, sf[cc][1]);
+          sf[cc][2] = fmaf(vr[4 * i4 + 2], f.z, sf[cc][2]);
+          sf[cc][3] = fmaf(vr[4 * i4 + 3], f.w, sf[cc][3]);
+          so[cc][0] = fmaf(vr[4 * i4 + 0], o.x, so[cc][0]);
+          so[cc][1] = fmaf(vr[4 * i4 + 1], o.y, so[cc][1]);
+          so[cc][2] = fmaf(vr[4 * i4 + 2], o.z, so[cc][2]);
+          so[cc][3] = fmaf(vr[4 * i4 + 3], o.w, so[cc][3]);
+        }
       }
-      zf[c] = (sf[0] + sf[1]) + (sf[2] + sf[3]);
-      zo[c] = (so[0] + so[1]) + (so[2] + so[3]);
+      float rf[4], ro[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        rf[cc] = (sf[cc][0] + sf[cc][1]) + (sf[cc][2] + sf[cc][3]);
+        ro[cc] = (so[cc][0] + so[cc][1]) + (so[cc][2] + so[cc][3]);
+      }
+      *(float4*)(zf + c4) = make_float4(rf[0], rf[1], rf[2], rf[3]);
+      *(float4*)(zo + c4) = make_float4(ro[0], ro[1], ro[2], ro[3]);
     }
   }
 }
@@ -1085,6 +1088,7 @@ struct QrRun {
     ca.err = wj.err;
     ca.pred = a.pred;
     ca.fail = wj.fail + p;
+    ca.no_fallback = b->no_fallback ? 1 : 0;
     ca.G = a.G;
   }
 
@@ -1348,9 +1352,10 @@ mao_status QrRun::finish(hipStream_t stream) {
 
 mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout, int64_t ldQ,
                    QrWork& w, const int* pred, hipStream_t stream, bool abort_barriers,
-                   bool fact_bf16x3) {
+                   bool fact_bf16x3, bool no_fallback) {
   QrBatch b;
   b.abort_barriers = abort_barriers;
+  b.no_fallback = no_fallback;
   b.fact_bf16x3 = fact_bf16x3;
   b.n = n;
   b.njob = 1;

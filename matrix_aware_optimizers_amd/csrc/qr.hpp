@@ -63,6 +63,10 @@ struct QrBatch {
   // the factorisation's panel updates as bf16x3 products (for a QR input
   // that is itself a bf16x3 product); the explicit Q is accumulated in fp32
   bool fact_bf16x3 = false;
+  // test hook: a CholeskyQR panel that breaks down raises the job's time-out
+  // flag (NaN basis) instead of falling back to the per-column panel, so that
+  // a test can tell the fast panel ran
+  bool no_fallback = false;
 };
 mao_status qr_core_batched(const QrBatch& b, hipStream_t stream);
 // Several batches of different sizes refreshed together: panel by panel, the
@@ -140,6 +144,7 @@ mao_status qr_presplit(const QrSplitArgs& a, int njob, hipStream_t stream);
 // If a grid barrier times out, E and Q are set to NaN.
 mao_status qr_core(float* S, int64_t ldS, int n, float* E, int64_t ldE, float* Qout,
                    int64_t ldQ, QrWork& w, const int* pred, hipStream_t stream,
-                   bool abort_barriers = false, bool fact_bf16x3 = false);
+                   bool abort_barriers = false, bool fact_bf16x3 = false,
+                   bool no_fallback = false);
 
 }  // namespace mao

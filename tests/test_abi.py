@@ -277,7 +277,7 @@ def test_soap_foam_adamw_qr_gemm_validation_codes():
 
     assert lib.mao_qr(FAKE, 12, FAKE + (1 << 20), 16, 12, ws, 1 << 30, None) == E_LAYOUT
     assert lib.mao_qr(FAKE, 16, FAKE + 64, 16, 12, ws, 1 << 30, None) == E_ALIAS
-    assert lib.mao_dbg_qr(FAKE, 16, FAKE + (1 << 20), 16, 12, ws, 1 << 30, 2, None) == E_HPARAM
+    assert lib.mao_dbg_qr(FAKE, 16, FAKE + (1 << 20), 16, 12, ws, 1 << 30, 4, None) == E_HPARAM
     assert lib.mao_eigh_workspace_size(0) == 0 and lib.mao_eigh_workspace_size(16385) == 0
     assert lib.mao_eigh_workspace_size(300) > 0
     assert lib.mao_eigh(FAKE, 20000, FAKE + (1 << 34), 20000, None, None, 20000, ws, 1 << 30,

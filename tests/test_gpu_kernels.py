@@ -152,3 +152,26 @@ def test_qr_barrier_timeout_poisons_the_basis(gpu_lib):
         torch.cuda.synchronize()
         q = to_host(Q2)
         assert rel(q, oracle.qr_positive(p.astype(np.float64))[0]) < 1e-4
+
+
+def test_qr_cholesky_panels_run_without_fallback(gpu_lib):
+    """The per-column Householder panel that a CholeskyQR breakdown falls back
+    to gives the same basis, so a broken fast panel would still pass every
+    other QR test (only slower). With the fallback turned into a NaN basis
+    (test flag), a well-conditioned P -- Gaussian, several panels and
+    workgroups per panel, a ragged last panel -- must come out finite and
+    equal, bit for bit, to the ordinary call: the CholeskyQR panels factored
+    every panel themselves."""
+    import torch
+    for n in (70, 300, 1100, 4096):
+        log(f"qr no-fallback n={n}")
+        r = np.random.default_rng(29 + n)
+        p = r.standard_normal((n, n)).astype(np.float32)
+        P = to_dev(p)
+        Q1 = gpu_lib.qr(P, dbg_flags=gpu_lib.DBG_QR_NO_FALLBACK)
+        Q2 = gpu_lib.qr(P)
+        torch.cuda.synchronize()
+        assert torch.isfinite(Q1).all().item()
+        assert torch.equal(Q1, Q2)
+        if n <= 300:
+            assert rel(to_host(Q1), oracle.qr_positive(p.astype(np.float64))[0]) < 1e-4
