@@ -280,6 +280,173 @@ __device__ __forceinline__ void staged_epilogue_impl(const f32x16_t (&acc)[4][4]
 #undef MAO_BAND
 }
 
+// Four lanes 4k + q (q = 0..3) each hold x[0..3], rows r..r+3 of column
+// 4k + q; afterwards lane 4k + q holds row r + q, columns 4k..4k+3. Two
+// butterfly steps over quad-permuting DPP moves (lane bit 0, then bit 1),
+// each lane sending the two values whose element index differs from its own
+// lane index in that bit.
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(float& x0, float& x1, float& x2, float& x3, bool b1,
+                                               bool b2) {
+  // lane bit 0: elements 1, 3 (bit clear) or 0, 2 (bit set) come from lane ^ 1
+  const float r0 = dpp_xor1(b1 ? x0 : x1), r1 = dpp_xor1(b1 ? x2 : x3);
+  const float n0 = b1 ? r0 : x0, n1 = b1 ? x1 : r0, n2 = b1 ? r1 : x2, n3 = b1 ? x3 : r1;
+  // lane bit 1: elements 2, 3 (bit clear) or 0, 1 (bit set) come from lane ^ 2
+  const float s0 = dpp_xor2(b2 ? n0 : n2), s1 = dpp_xor2(b2 ? n1 : n3);
+  x0 = b2 ? s0 : n0;
+  x1 = b2 ? s1 : n1;
+  x2 = b2 ? n2 : s0;
+  x3 = b2 ? n3 : s1;
+}
+
+// Epilogue of a tile whose bf16 D is tiled (tiled.hpp) and has no C0, row
+// scale, diagonal term or transposed copy: D = alpha * acc straight from the
+// accumulators, no LDS. A 32 x 32 MFMA result gives lane (h, c) rows
+// 8 g + 4 h + i (i = 0..3) of column c; after a quad transpose lane
+// (h, 4 k + q) holds row 8 g + 4 h + q, columns 4 k..4 k + 3, which it
+// writes as 8 bytes. One store instruction of a wavefront then covers rows
+// 8 g..8 g + 7 of a block, 512 contiguous bytes.
+__device__ __forceinline__ void direct_epilogue_t32(const f32x16_t (&acc)[4][4], int m0, int n0,
+                                                    float alpha, bf16_t* D, int64_t ldd) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int q = r32 & 3, k = r32 >> 2;
+  const bool qb1 = (q & 1) != 0, qb2 = (q & 2) != 0;
+  const int64_t cpb = ldd >> 5;  // blocks per block row
+  bf16_t* base = D + ((((int64_t)(m0 >> 5) + wm * 4) * cpb + (n0 >> 5) + wn * 4) << 10);
+  int inner[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int r = 8 * g + 4 * h + q;
+    inner[g] = r * 32 + (((k >> 1) ^ t32_swz(r)) << 3) + 4 * (k & 1);
+  }
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16_t* blk = base + (((int64_t)I * cpb + j) << 10);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x0 = acc[I][j][4 * g] * alpha, x1 = acc[I][j][4 * g + 1] * alpha;
+        float x2 = acc[I][j][4 * g + 2] * alpha, x3 = acc[I][j][4 * g + 3] * alpha;
+        quad_transpose(x0, x1, x2, x3, qb1, qb2);
+        uint2 pk;
+        pk.x = pack_bf16x2(x0, x1);
+        pk.y = pack_bf16x2(x2, x3);
+        *(uint2*)(blk + inner[g]) = pk;
+      }
+      // keep the scheduler from hoisting the next block's accumulator reads
+      // (their registers would spill)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The same for a tile of a symmetric product computed on the lower tile
+// triangle (tm >= tn) of a tiled bf16 D: D = alpha * acc (+ beta * C0, + dadd
+// on the diagonal below row M), written in place and mirrored. Before the
+// quad transpose lane (h, c) holds rows 8 g + 4 h + i of column c, which are
+// four consecutive columns of row c of the mirror block: the mirror is
+// written from there as 8 bytes, and C0 is read there too (C0 is a symmetric
+// tiled matrix, so its mirrored entries are its own). On a diagonal tile the
+// blocks above the diagonal come from the mirror only, and a diagonal 32 x 32
+// block takes its lower part (diagonal included) from D and its strict upper
+// part from the mirror, element by element.
+template <bool HC0>
+__device__ __forceinline__ void direct_epilogue_t32_syrk(const f32x16_t (&acc)[4][4], int m0, int n0,
+                                                         bool diag, float alpha, const bf16_t* C0,
+                                                         int64_t ldc0, float beta, float dadd, int M,
+                                                         bf16_t* D, int64_t ldd) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int q = r32 & 3, k = r32 >> 2;
+  const bool qb1 = (q & 1) != 0, qb2 = (q & 2) != 0;
+  if (diag && wm < wn) return;  // every block of this quarter lies above the diagonal
+  const int64_t cpb = ldd >> 5, cpc = ldc0 >> 5;
+  int inner[4], innm[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int r = 8 * g + 4 * h + q;
+    inner[g] = r * 32 + (((k >> 1) ^ t32_swz(r)) << 3) + 4 * (k & 1);
+    innm[g] = r32 * 32 + ((g ^ t32_swz(r32)) << 3) + 4 * h;
+  }
+  const int bi0 = (m0 >> 5) + wm * 4, bj0 = (n0 >> 5) + wn * 4;
+  // C0 of a row of four blocks is requested one row ahead (two buffers)
+  uint2 cb[2][4][4];
+  auto load_row = [&](int I, uint2 (&dst)[4][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16_t* blk = C0 + ((((int64_t)bj0 + j) * cpc + bi0 + I) << 10);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) dst[j][g] = *(const uint2*)(blk + innm[g]);
+    }
+  };
+  if constexpr (HC0) load_row(0, cb[0]);
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    if constexpr (HC0) {
+      if (I < 3) load_row(I + 1, cb[(I + 1) & 1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int BI = wm * 4 + I, BJ = wn * 4 + j;  // block within the tile
+      if (diag && BI < BJ) continue;
+      const bool dblk = diag && BI == BJ;
+      bf16_t* dp = D + ((((int64_t)bi0 + I) * cpb + bj0 + j) << 10);
+      bf16_t* mp = D + ((((int64_t)bj0 + j) * cpb + bi0 + I) << 10);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x0 = acc[I][j][4 * g] * alpha, x1 = acc[I][j][4 * g + 1] * alpha;
+        float x2 = acc[I][j][4 * g + 2] * alpha, x3 = acc[I][j][4 * g + 3] * alpha;
+        if constexpr (HC0) {
+          const uint2 c = cb[I & 1][j][g];
+          x0 += beta * bf16_to_f32((bf16_t)(c.x & 0xffff));
+          x1 += beta * bf16_to_f32((bf16_t)(c.x >> 16));
+          x2 += beta * bf16_to_f32((bf16_t)(c.y & 0xffff));
+          x3 += beta * bf16_to_f32((bf16_t)(c.y >> 16));
+        }
+        // mirror: row r32 of block (BJ, BI), columns 8 g + 4 h .. + 3
+        if (!dblk) {
+          uint2 pk;
+          pk.x = pack_bf16x2(x0, x1);
+          pk.y = pack_bf16x2(x2, x3);
+          *(uint2*)(mp + innm[g]) = pk;
+        } else {
+          const int c0 = 8 * g + 4 * h;
+          const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (c0 + i > r32) mp[innm[g] + i] = f32_to_bf16(xs[i]);
+        }
+        quad_transpose(x0, x1, x2, x3, qb1, qb2);
+        if (!dblk) {
+          uint2 pk;
+          pk.x = pack_bf16x2(x0, x1);
+          pk.y = pack_bf16x2(x2, x3);
+          *(uint2*)(dp + inner[g]) = pk;
+        } else {
+          // row r of the diagonal block, columns 4 k + e: the lower part
+          const int r = 8 * g + 4 * h + q;
+          const bool in_m = m0 + BI * 32 + r < M;
+          float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (r == 4 * k + e && in_m) xs[e] += dadd;
+            if (r >= 4 * k + e) dp[inner[g] + e] = f32_to_bf16(xs[e]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 template <bool CHECKED, bool LB = false>
 __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], float* b0, float* b1,
                                                 float* b2, float* b3, const EpiArgs& e) {
