@@ -111,6 +111,18 @@ __device__ __forceinline__ void store8(T* row, int j, int cols, const float v[8]
   }
 }
 
+// 8 fp32 values from p[j..j+7] that may not be 16-byte aligned (per-matrix
+// vectors at a stride of cols elements): vector loads when aligned, else
+// element by element; zero past cols.
+__device__ __forceinline__ void load8_f32_any(const float* p, int j, int cols, float v[8]) {
+  if (j + 8 <= cols && ((uintptr_t)(p + j) & 15) == 0) {
+    load8<float>(p, j, cols, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (j + e < cols) ? p[j + e] : 0.f;
+  }
+}
+
 // Row range of this block for a matrix split into nrb row-blocks.
 __device__ __forceinline__ void row_range(int rows, int nrb, int& r0, int& r1) {
   const int per = (rows + nrb - 1) / nrb;
@@ -306,13 +318,20 @@ __global__ __launch_bounds__(kBlock) void row_sumsq_kernel(View X, int rows, int
   const TX* row = (const TX*)X.p + (int64_t)b * X.stride + (int64_t)i * X.ld;
   const float* wb = w ? w + (int64_t)b * cols : nullptr;
   float acc = 0.f;
-  for (int j = lane * 4; j < cols; j += 256) {
-    float v[4];
-    load4<TX>(row, j, cols, v);
+  // one wavefront per row, 8 consecutive elements per lane and step (16- or
+  // 32-byte loads, weights as two 16-byte loads), four steps in flight
+#pragma unroll 4
+  for (int j = lane * 8; j < cols; j += 512) {
+    float v[8];
+    load8<TX>(row, j, cols, v);
+    if (wb) {
+      float wt[8];
+      load8_f32_any(wb, j, cols, wt);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float wt = (wb && j + e < cols) ? wb[j + e] : 1.f;
-      acc += wt * v[e] * v[e];
+      for (int e = 0; e < 8; ++e) acc += wt[e] * v[e] * v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += v[e] * v[e];
     }
   }
   acc = wave_sum(acc);
@@ -356,10 +375,11 @@ __global__ __launch_bounds__(kBlock) void update_kernel(View W, View O, int rows
     load8<TW>(wrow, j, cols, w);
     load8<TO>(Ob + (int64_t)i * O.ld, j, cols, o);
     const float si = s * (rsb ? rsb[i] : 1.f);
+    float cj[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+    if (csb) load8_f32_any(csb, j, cols, cj);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float cj = (csb && j + e < cols) ? csb[j + e] : 1.f;
-      o[e] = si * cj * o[e];
+      o[e] = si * cj[e] * o[e];
       w[e] = w[e] - lr * (wd * w[e] + o[e]);
     }
     store8<TW>(wrow, j, cols, w);
