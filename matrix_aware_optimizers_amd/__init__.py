@@ -142,6 +142,14 @@ def load(path: str | None = None):
     if _lib is not None:
         return _lib
     p = path or LIB_PATH
+    # torch first: its bundled HIP runtime has the soname the library needs,
+    # so both then share one runtime. Loaded the other way round, the system
+    # runtime comes first and the library's launches fail ("no ROCm-capable
+    # device") once torch has initialised the device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(p):
         raise RuntimeError(f"{p} not found: build it with `python -m matrix_aware_optimizers_amd.build`")
     lib = ctypes.CDLL(p)

@@ -447,6 +447,68 @@ __device__ __forceinline__ void direct_epilogue_t32_syrk(const f32x16_t (&acc)[4
   }
 }
 
+// Interior tile of a row-major fp32 result without C0 or row scale:
+// D = alpha * acc and/or its transposed copy Dt, straight from the
+// accumulators in 16-byte pieces (D after the quad transpose, Dt before it:
+// column c of a block is row c of Dt). With `diag` the tile is a diagonal
+// tile of a symmetric product and Dt is D's mirror (the same matrix): the
+// blocks above the diagonal come from the mirror only, and a diagonal block
+// takes its lower part from D and its strict upper part from the mirror.
+__device__ __forceinline__ void direct_epilogue_f32(const f32x16_t (&acc)[4][4], int m0, int n0,
+                                                    bool diag, float alpha, float* D, int64_t ldd,
+                                                    float* Dt, int64_t ldt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int q = r32 & 3, k = r32 >> 2;
+  const bool qb1 = (q & 1) != 0, qb2 = (q & 2) != 0;
+  if (diag && wm < wn) return;
+  // this wavefront's 128 x 128 quarter: D rows from rb, columns from cb
+  const int64_t rb = m0 + wm * 128, cb = n0 + wn * 128;
+  float* dq = D ? D + (rb + 4 * h + q) * ldd + cb + 4 * k : nullptr;  // + (32 I + 8 g) ldd + 32 j
+  float* tq = Dt ? Dt + (cb + r32) * ldt + rb + 4 * h : nullptr;       // + 32 j ldt + 32 I + 8 g
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int BI = wm * 4 + I, BJ = wn * 4 + j;
+      if (diag && BI < BJ) continue;
+      const bool dblk = diag && BI == BJ;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x0 = acc[I][j][4 * g] * alpha, x1 = acc[I][j][4 * g + 1] * alpha;
+        float x2 = acc[I][j][4 * g + 2] * alpha, x3 = acc[I][j][4 * g + 3] * alpha;
+        if (tq) {
+          float* t = tq + 32 * j * ldt + 32 * I + 8 * g;
+          if (!dblk) {
+            *(float4*)t = make_float4(x0, x1, x2, x3);
+          } else {
+            // strict upper part: row r32 of the block, columns 8 g + 4 h + i
+            const int c0 = 8 * g + 4 * h;
+            if (c0 + 0 > r32) t[0] = x0;
+            if (c0 + 1 > r32) t[1] = x1;
+            if (c0 + 2 > r32) t[2] = x2;
+            if (c0 + 3 > r32) t[3] = x3;
+          }
+        }
+        if (dq) {
+          quad_transpose(x0, x1, x2, x3, qb1, qb2);
+          float* d = dq + (32 * I + 8 * g) * ldd + 32 * j;
+          if (!dblk) {
+            *(float4*)d = make_float4(x0, x1, x2, x3);
+          } else {
+            const int r = 8 * g + 4 * h + q;
+            if (r >= 4 * k + 0) d[0] = x0;
+            if (r >= 4 * k + 1) d[1] = x1;
+            if (r >= 4 * k + 2) d[2] = x2;
+            if (r >= 4 * k + 3) d[3] = x3;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <bool CHECKED, bool LB = false>
 __device__ __forceinline__ void staged_epilogue(const f32x16_t (&acc)[4][4], float* b0, float* b1,
                                                 float* b2, float* b3, const EpiArgs& e) {

@@ -457,6 +457,13 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
       return;
     }
   }
+  if constexpr (!T32) {  // fp32 results of the SOAP / FOAM products
+    if (d32 && m0 + TB <= M && n0 + TB <= N && C0 == nullptr && rs == nullptr &&
+        (D != nullptr || Tt != nullptr)) {
+      direct_epilogue_f32(acc, m0, n0, diag, alpha, (float*)D, P.ldd, (float*)Tt, ldt);
+      return;
+    }
+  }
   if ((m0 + TB <= M && n0 + TB <= N) || (T32 && dt32)) {
     EpiArgs ea;
     ea.m0 = m0; ea.n0 = n0; ea.M = M; ea.N = N;
