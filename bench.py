@@ -36,6 +36,7 @@ import ctypes
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -276,12 +277,16 @@ def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
     # timed region: K steps, no per-launch instrumentation
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     start.record()
     for i in range(args.steps):
         wl.step(args.warmup + i)
+        marks[i].record()  # one event between steps: per-step median and p90
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    per_step = sorted([start.elapsed_time(marks[0])] +
+                      [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
     # second region of K steps with HIP events around every contraction
     # launch (recorded on the library's stream): the per-kernel split
     mao.timing_collect()
@@ -302,7 +307,9 @@ def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
         f"{achieved:.1f} TFLOP/s")
     per_tag = {k: {"ms_total": round(v[0], 4), "launches": v[1],
                    "tflops": round(v[2] / (v[0] * 1e-3) / 1e12, 2) if v[0] > 0 else 0.0}
-               for k, v in tim.items() if v[1] > 0}
+               for k, v in tim.items() if v[1] > 0 and k != "elementwise"}
+    ew_ms, ew_n, ew_bytes = tim.get("elementwise", (0.0, 0, 0.0))
+    ew_gbs = ew_bytes / (ew_ms * 1e-3) / 1e9 if ew_ms > 0 else 0.0
     line = {
         "metric": METRIC,
         "value": 1000.0 / ms,
@@ -331,6 +338,13 @@ def run_muon(args, workload_name, groups, norm_mode, sample, dtype="bf16"):
                      "launches": ns_cnt, "avg_launch_ms": ns_ms / max(ns_cnt, 1),
                      "alg_tflop_per_launch": ns_fl / max(ns_cnt, 1) / 1e12},
         "kernels": per_tag,
+        "ms_per_step_median": statistics.median(per_step),
+        "ms_per_step_p90": per_step[min(len(per_step) - 1, int(0.9 * len(per_step)))],
+        # the memory-bound passes (momentum EMA with its norm, X0 cast, Muon+
+        # sums of squares, update): algorithmic bytes / their event time
+        "elementwise": {"ms_per_step": ew_ms / args.steps, "launches": ew_n,
+                        "bytes_per_step": ew_bytes / args.steps, "achieved_gbs": ew_gbs,
+                        "peak_gbs": PEAK_HBM_GBS, "frac": ew_gbs / PEAK_HBM_GBS},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -625,6 +639,8 @@ def other_configs(args):
                      "steps": sub.steps, "warmup": sub.warmup,
                      "roofline": {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac",
                                                     "kernel")}}
+        if "elementwise" in line:
+            out[name]["elementwise"] = line["elementwise"]
     return out
 
 

@@ -586,7 +586,11 @@ MAO_API mao_status mao_basis_age(const float* aux, float* age, void* stream);
  * panel's vectors, 7: QR fused update-and-projection, 8: QR panel
  * factorisations, counted at zero flops, 9: launches gated by a device-side
  * flag, such as FOAM's refresh, whose flops assume every job ran) with its
- * algorithmic flop count (symmetric products at half cost). Off by default;
+ * algorithmic flop count (symmetric products at half cost); the memory-bound
+ * passes of a Muon step (momentum EMA with its norm, X0 cast, Muon+ sums of
+ * squares, update) are bracketed the same way under tag 10 with the bytes
+ * they must move in place of flops. Tags at or past ntags are not
+ * reported. Off by default;
  * this is the only host-side state the library keeps, and it exists for
  * benchmarking only.
  * mao_timing_collect -- waits for the recorded events, sums elapsed

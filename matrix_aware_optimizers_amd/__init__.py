@@ -481,7 +481,7 @@ def basis_age(aux, age):
 
 
 TIMING_TAGS = ("ns_gram", "ns_square", "ns_apply", "other", "qr", "other_bf16", "qr_proj",
-               "qr_fused", "qr_panel", "gated")
+               "qr_fused", "qr_panel", "gated", "elementwise")
 
 
 def timing_enable(on: bool = True):
@@ -490,7 +490,8 @@ def timing_enable(on: bool = True):
 
 
 def timing_collect() -> dict:
-    """{tag: (total_ms, launches, algorithmic_flops)} since the last collect."""
+    """{tag: (total_ms, launches, algorithmic_flops)} since the last collect
+    (for "elementwise": algorithmic bytes in place of flops)."""
     n = len(TIMING_TAGS)
     ms = (ctypes.c_double * n)()
     cnt = (c_int64 * n)()

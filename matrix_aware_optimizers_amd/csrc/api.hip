@@ -238,6 +238,20 @@ size_t muon_ws(int32_t ng, const mao_batch* W, const mao_muon_hparams* hp) {
   return c.used + 256;
 }
 
+// Benchmark instrumentation of a memory-bound pass: HIP events around it
+// when timing is on, tagged TAG_ELEMWISE with the bytes it must move.
+struct PassTimer {
+  hipStream_t s;
+  double bytes;
+  void* ev = nullptr;
+  PassTimer(hipStream_t s_, double b, bool on = true) : s(s_), bytes(b) {
+    if (on && timing_on()) timing_record_begin(s, &ev);
+  }
+  ~PassTimer() {
+    if (ev) timing_record_end(s, ev, TAG_ELEMWISE, bytes);
+  }
+};
+
 mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const mao_batch* M,
                     const mao_muon_hparams* hp, void* ws, const mao_batch* out, hipStream_t s) {
   int64_t rows[MAO_MAX_GROUPS], cols[MAO_MAX_GROUPS], count[MAO_MAX_GROUPS];
@@ -263,10 +277,16 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
     MuonGroupBufs& B = bufs[g];
     const int64_t mstride = M[g].count > 1 ? M[g].stride : 0;
     const int64_t gstride = G[g].count > 1 ? G[g].stride : 0;
-    MAO_TRY(ema_sumsq(view(M[g].data, M[g].ld, mstride), view(G[g].data, G[g].ld, gstride),
-                      G[g].dtype, B.rows, B.cols, B.count, hp->mu, B.partial, B.nrb, s));
-    MAO_TRY(finalize_inv_norm(B.partial, B.nrb, B.count, hp->eps, B.scale, s));
+    const double elems = (double)B.rows * B.cols * B.count;
+    {
+      // M read and written (fp32), G read
+      PassTimer pt(s, elems * (8.0 + dtype_size(G[g].dtype)));
+      MAO_TRY(ema_sumsq(view(M[g].data, M[g].ld, mstride), view(G[g].data, G[g].ld, gstride),
+                        G[g].dtype, B.rows, B.cols, B.count, hp->mu, B.partial, B.nrb, s));
+      MAO_TRY(finalize_inv_norm(B.partial, B.nrb, B.count, hp->eps, B.scale, s));
+    }
     if (B.t32) {
+      PassTimer pt(s, elems * (4.0 + 2.0));  // M read, X0 written (bf16)
       MAO_TRY(scale_cast_tiled(view(M[g].data, M[g].ld, mstride), B.rows, B.cols, B.count, B.scale,
                                !B.wide, B.X[0], B.ap, B.bp, B.ap * B.bp, s));
       continue;
@@ -274,6 +294,8 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
     View xa = view(B.X[0], B.ldx, (int64_t)B.a * B.ldx);
     View xb = (!kmajor || (hp->ns_steps == 0 && need_t(B))) ? view(B.Xt[0], B.ldxt, (int64_t)B.b * B.ldxt)
                                                              : view(nullptr, 0, 0);
+    // M read, X0 (and X0^T where it is read) written
+    PassTimer pt(s, elems * (4.0 + (xb.p ? 2.0 : 1.0) * dtype_size(xdt)));
     MAO_TRY(scale_cast_transpose(view(M[g].data, M[g].ld, mstride), B.rows, B.cols, B.count,
                                  B.scale, B.wide ? xa : xb, B.wide ? xb : xa, xdt, s));
   }
@@ -378,28 +400,36 @@ mao_status run_muon(int32_t ng, const mao_batch* W, const mao_batch* G, const ma
     const float* rs = nullptr;
     const float* cs = nullptr;
     const int mode = hp->norm_mode;
-    if (mode == MAO_NORM_COL || mode == MAO_NORM_COL_ROW) {
-      MAO_TRY(row_sumsq(Ot, xdt, B.cols, B.rows, B.count, nullptr, B.ss_c, s));
-      MAO_TRY(equalise_scales(B.ss_c, B.cols, B.count, hp->norm_eps, B.cs, B.sq, s));
-      cs = B.cs;
-      if (mode == MAO_NORM_COL_ROW) {
-        MAO_TRY(row_sumsq(O, xdt, B.rows, B.cols, B.count, B.sq, B.ss_r, s));
-        MAO_TRY(equalise_scales(B.ss_r, B.rows, B.count, hp->norm_eps, B.rs, nullptr, s));
-        rs = B.rs;
-      }
-    } else if (mode == MAO_NORM_ROW || mode == MAO_NORM_ROW_COL) {
-      MAO_TRY(row_sumsq(O, xdt, B.rows, B.cols, B.count, nullptr, B.ss_r, s));
-      MAO_TRY(equalise_scales(B.ss_r, B.rows, B.count, hp->norm_eps, B.rs, B.sq, s));
-      rs = B.rs;
-      if (mode == MAO_NORM_ROW_COL) {
-        MAO_TRY(row_sumsq(Ot, xdt, B.cols, B.rows, B.count, B.sq, B.ss_c, s));
-        MAO_TRY(equalise_scales(B.ss_c, B.cols, B.count, hp->norm_eps, B.cs, nullptr, s));
+    const double elems = (double)B.rows * B.cols * B.count;
+    // the Muon+ sums of squares read the result once per axis
+    const int naxes = (mode == MAO_NORM_COL_ROW || mode == MAO_NORM_ROW_COL) ? 2 : mode != MAO_NORM_NONE;
+    {
+      PassTimer pt_norm(s, elems * naxes * dtype_size(xdt), naxes > 0);
+      if (mode == MAO_NORM_COL || mode == MAO_NORM_COL_ROW) {
+        MAO_TRY(row_sumsq(Ot, xdt, B.cols, B.rows, B.count, nullptr, B.ss_c, s));
+        MAO_TRY(equalise_scales(B.ss_c, B.cols, B.count, hp->norm_eps, B.cs, B.sq, s));
         cs = B.cs;
+        if (mode == MAO_NORM_COL_ROW) {
+          MAO_TRY(row_sumsq(O, xdt, B.rows, B.cols, B.count, B.sq, B.ss_r, s));
+          MAO_TRY(equalise_scales(B.ss_r, B.rows, B.count, hp->norm_eps, B.rs, nullptr, s));
+          rs = B.rs;
+        }
+      } else if (mode == MAO_NORM_ROW || mode == MAO_NORM_ROW_COL) {
+        MAO_TRY(row_sumsq(O, xdt, B.rows, B.cols, B.count, nullptr, B.ss_r, s));
+        MAO_TRY(equalise_scales(B.ss_r, B.rows, B.count, hp->norm_eps, B.rs, B.sq, s));
+        rs = B.rs;
+        if (mode == MAO_NORM_ROW_COL) {
+          MAO_TRY(row_sumsq(Ot, xdt, B.cols, B.rows, B.count, B.sq, B.ss_c, s));
+          MAO_TRY(equalise_scales(B.ss_c, B.cols, B.count, hp->norm_eps, B.cs, nullptr, s));
+          cs = B.cs;
+        }
       }
     }
     const float scale = sqrtf((float)B.rows / (float)B.cols);
     View outv = view(nullptr, 0, 0);
     if (out && out[g].data) outv = view(out[g].data, out[g].ld, out[g].count > 1 ? out[g].stride : 0);
+    // W read and written, the result read, the optional fp32 update written
+    PassTimer pt(s, elems * (2.0 * dtype_size(W[g].dtype) + dtype_size(xdt) + (outv.p ? 4.0 : 0.0)));
     MAO_TRY(apply_update(view(W[g].data, W[g].ld, W[g].count > 1 ? W[g].stride : 0), W[g].dtype,
                          O, xdt, B.rows, B.cols, B.count, hp->lr, hp->weight_decay, scale, rs, cs,
                          outv, s));

@@ -5,8 +5,9 @@
 // D = alpha * acc + beta * C0, rows scaled by row_scale, written to D and/or
 // its transpose Dt (the SYRK mirror when D == Dt on a symmetric result).
 //
-// The tile goes through LDS in two halves of 128 rows, as four 32-row bands of
-// 256 floats (one 32 KB buffer each). Row pass: each thread finishes 8
+// Staged epilogue (staged_epilogue): the tile goes through LDS in two halves
+// of 128 rows, as four 32-row bands of 256 floats (one 32 KB buffer each).
+// Row pass: each thread finishes 8
 // consecutive columns of a row -- C0 read and D written in 16- (bf16) or
 // 32-byte (fp32) pieces, one whole row per 32 lanes -- and, when a transposed
 // copy is due, puts the finished values back. Column pass: 16 lanes cover 128
@@ -19,6 +20,11 @@
 // tiled (tiled.hpp); a run of 8 columns starting at a multiple of 8 is one
 // contiguous chunk in either layout. A diagonal term dadd is added to D[i][i]
 // for i < M (never to the zero pad of a tiled D).
+//
+// Direct epilogues (direct_epilogue_*): for the cases that need no LDS --
+// tiled bf16 results without a transposed copy or row scale, and interior
+// tiles of row-major fp32 results without C0 -- each lane's values go out
+// from the accumulators after a 4 x 4 transpose across groups of four lanes.
 #pragma once
 
 #include "common.hpp"

@@ -114,7 +114,7 @@ mao_status write_pointer_table(const void** dst, const void* const* src, int n, 
 // What a launch computes, for the optional event timing (instrumentation).
 enum GemmTag : int { TAG_NS_GRAM = 0, TAG_NS_SQUARE = 1, TAG_NS_APPLY = 2, TAG_OTHER = 3,
                      TAG_QR = 4, TAG_OTHER_BF16 = 5, TAG_QR_PROJ = 6, TAG_QR_FUSED = 7,
-                     TAG_QR_PANEL = 8, TAG_GATED = 9, TAG_COUNT = 10 };
+                     TAG_QR_PANEL = 8, TAG_GATED = 9, TAG_ELEMWISE = 10, TAG_COUNT = 11 };
 
 // Enqueue one grouped launch. in_dtype: MAO_BF16 or MAO_F32. All problems of
 // a launch share the input dtype. Host-side shape checks are the caller's.
@@ -135,7 +135,9 @@ mao_status launch_gemm_f32_rank128(GemmArgs& args, hipStream_t stream);
 
 // Instrumentation: when enabled, every contraction launch is bracketed by HIP
 // events on its stream, with its algorithmic flop count (symmetric products
-// at half cost). Off by default.
+// at half cost), and the Muon step's memory-bound passes under
+// TAG_ELEMWISE with their algorithmic bytes in place of flops. Off by
+// default.
 bool timing_on();
 void timing_record_begin(hipStream_t s, void** start);
 void timing_record_end(hipStream_t s, void* start, int tag, double flops);

@@ -32,11 +32,13 @@
 // copied with no clamping, every direct load reading 1 KB in one piece, and
 // a K x N slice sits in LDS as 8 blocks of 32 k-rows x 64 bytes.
 //
-// Epilogue (epilogue.hpp): interior tiles, and every tile of a tiled D, go
-// through LDS in two halves of 128 rows and are written as whole rows in 16-
-// or 32-byte pieces (C0 blend, row scale, transposed copy or SYRK mirror on
-// the way). Edge tiles of a row-major D use 32-row bands through LDS (the
-// tiled kernels use the checked staged epilogue instead).
+// Epilogue (epilogue.hpp). The tiled bf16 results between Newton-Schulz
+// iterations, and interior tiles of fp32 results without C0, leave straight
+// from the accumulators (a quad transpose across lanes, 8- or 16-byte
+// stores, no LDS). Other interior tiles, and every other tile of a tiled D,
+// go through LDS in two halves of 128 rows and are written as whole rows in
+// 16- or 32-byte pieces (C0 blend, row scale, transposed copy or SYRK mirror
+// on the way). Edge tiles of a row-major D use 32-row bands through LDS.
 #include "epilogue.hpp"
 #include "gemm.hpp"
 

@@ -275,3 +275,34 @@ def test_muon_deterministic(gpu_lib):
         torch.cuda.synchronize()
         outs.append(out.clone())
     assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("norm_mode", ["none", "col_row"])
+def test_timing_elementwise_tag(gpu_lib, norm_mode):
+    """The benchmark instrumentation of a Muon step's memory-bound passes:
+    with timing on, the EMA, the X0 cast, the Muon+ sums of squares (one read
+    of the result per axis) and the update are bracketed under the
+    "elementwise" tag and credited with the bytes they must move (bf16 W and
+    G, fp32 M, bf16 Newton-Schulz iterates); contractions keep their tags."""
+    import torch
+    m, n = 384, 640
+    r = np.random.default_rng(41)
+    W = to_dev(bf16_round((0.02 * r.standard_normal((m, n))).astype(np.float32)), "bf16")
+    G = to_dev(bf16_round(r.standard_normal((m, n)).astype(np.float32)), "bf16")
+    M = zeros_dev((m, n))
+    gpu_lib.timing_collect()
+    gpu_lib.timing_enable(True)
+    try:
+        gpu_lib.muon_step(W, G, M, lr=LR, mu=0.95, weight_decay=WD, ns_steps=5, ns_dtype="bf16",
+                          norm_mode=norm_mode)
+        torch.cuda.synchronize()
+    finally:
+        gpu_lib.timing_enable(False)
+    tim = gpu_lib.timing_collect()
+    ms, launches, nbytes = tim["elementwise"]
+    axes = 2 if norm_mode == "col_row" else 0
+    expect = m * n * ((8 + 2) + (4 + 2) + 2 * axes + (2 * 2 + 2))
+    assert launches == (4 if axes else 3)
+    assert nbytes == expect
+    assert ms > 0.0
+    assert sum(tim[k][1] for k in ("ns_gram", "ns_square", "ns_apply")) == 15
