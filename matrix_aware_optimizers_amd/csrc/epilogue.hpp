@@ -310,6 +310,14 @@ __device__ __forceinline__ void quad_transpose(float& x0, float& x1, float& x2, 
   x3 = b2 ? n3 : s1;
 }
 
+// alpha * v, or v itself when the product's alpha is one (UNIT): the
+// direct epilogues are bound by instruction issue, and the multiply costs
+// about an eighth of their time.
+template <bool UNIT>
+__device__ __forceinline__ float scale_by(float v, float alpha) {
+  return UNIT ? v : v * alpha;
+}
+
 // Epilogue of a tile whose bf16 D is tiled (tiled.hpp) and has no C0, row
 // scale, diagonal term or transposed copy: D = alpha * acc straight from the
 // accumulators, no LDS. A 32 x 32 MFMA result gives lane (h, c) rows
@@ -317,6 +325,7 @@ __device__ __forceinline__ void quad_transpose(float& x0, float& x1, float& x2, 
 // (h, 4 k + q) holds row 8 g + 4 h + q, columns 4 k..4 k + 3, which it
 // writes as 8 bytes. One store instruction of a wavefront then covers rows
 // 8 g..8 g + 7 of a block, 512 contiguous bytes.
+template <bool UNIT>
 __device__ __forceinline__ void direct_epilogue_t32(const f32x16_t (&acc)[4][4], int m0, int n0,
                                                     float alpha, bf16_t* D, int64_t ldd) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -339,8 +348,8 @@ __device__ __forceinline__ void direct_epilogue_t32(const f32x16_t (&acc)[4][4],
       bf16_t* blk = base + (((int64_t)I * cpb + j) << 10);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float x0 = acc[I][j][4 * g] * alpha, x1 = acc[I][j][4 * g + 1] * alpha;
-        float x2 = acc[I][j][4 * g + 2] * alpha, x3 = acc[I][j][4 * g + 3] * alpha;
+        float x0 = scale_by<UNIT>(acc[I][j][4 * g], alpha), x1 = scale_by<UNIT>(acc[I][j][4 * g + 1], alpha);
+        float x2 = scale_by<UNIT>(acc[I][j][4 * g + 2], alpha), x3 = scale_by<UNIT>(acc[I][j][4 * g + 3], alpha);
         quad_transpose(x0, x1, x2, x3, qb1, qb2);
         uint2 pk;
         pk.x = pack_bf16x2(x0, x1);
@@ -363,7 +372,7 @@ __device__ __forceinline__ void direct_epilogue_t32(const f32x16_t (&acc)[4][4],
 // blocks above the diagonal come from the mirror only, and a diagonal 32 x 32
 // block takes its lower part (diagonal included) from D and its strict upper
 // part from the mirror, element by element.
-template <bool HC0>
+template <bool HC0, bool UNIT>
 __device__ __forceinline__ void direct_epilogue_t32_syrk(const f32x16_t (&acc)[4][4], int m0, int n0,
                                                          bool diag, float alpha, const bf16_t* C0,
                                                          int64_t ldc0, float beta, float dadd, int M,
@@ -408,8 +417,8 @@ __device__ __forceinline__ void direct_epilogue_t32_syrk(const f32x16_t (&acc)[4
       bf16_t* mp = D + ((((int64_t)bj0 + j) * cpb + bi0 + I) << 10);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float x0 = acc[I][j][4 * g] * alpha, x1 = acc[I][j][4 * g + 1] * alpha;
-        float x2 = acc[I][j][4 * g + 2] * alpha, x3 = acc[I][j][4 * g + 3] * alpha;
+        float x0 = scale_by<UNIT>(acc[I][j][4 * g], alpha), x1 = scale_by<UNIT>(acc[I][j][4 * g + 1], alpha);
+        float x2 = scale_by<UNIT>(acc[I][j][4 * g + 2], alpha), x3 = scale_by<UNIT>(acc[I][j][4 * g + 3], alpha);
         if constexpr (HC0) {
           const uint2 c = cb[I & 1][j][g];
           x0 += beta * bf16_to_f32((bf16_t)(c.x & 0xffff));

@@ -443,19 +443,25 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
   if constexpr (T32 && BKM) {  // the B X products between iterations
     if (dt32 && !syrk && !d32 && C0 == nullptr && Tt == nullptr && rs == nullptr &&
         P.dadd == 0.f && D != nullptr) {
-      direct_epilogue_t32(acc, m0, n0, alpha, (bf16_t*)D, P.ldd);
+      if (alpha == 1.f)
+        direct_epilogue_t32<true>(acc, m0, n0, alpha, (bf16_t*)D, P.ldd);
+      else
+        direct_epilogue_t32<false>(acc, m0, n0, alpha, (bf16_t*)D, P.ldd);
       return;
     }
   }
   if constexpr (T32 && !BKM) {  // the symmetric products X X^T and A A + b A + a I
     if (syrk && dt32 && !d32 && rs == nullptr && D != nullptr &&
         (C0 == nullptr || ((P.flags & GF_C0_T32) != 0 && !c32))) {
-      if (C0 == nullptr)
-        direct_epilogue_t32_syrk<false>(acc, m0, n0, diag, alpha, nullptr, 0, 0.f, P.dadd, M,
-                                        (bf16_t*)D, P.ldd);
+      if (C0 == nullptr && alpha == 1.f)
+        direct_epilogue_t32_syrk<false, true>(acc, m0, n0, diag, alpha, nullptr, 0, 0.f, P.dadd, M,
+                                              (bf16_t*)D, P.ldd);
+      else if (C0 == nullptr)
+        direct_epilogue_t32_syrk<false, false>(acc, m0, n0, diag, alpha, nullptr, 0, 0.f, P.dadd,
+                                               M, (bf16_t*)D, P.ldd);
       else
-        direct_epilogue_t32_syrk<true>(acc, m0, n0, diag, alpha, (const bf16_t*)C0, P.ldc0, beta,
-                                       P.dadd, M, (bf16_t*)D, P.ldd);
+        direct_epilogue_t32_syrk<true, false>(acc, m0, n0, diag, alpha, (const bf16_t*)C0, P.ldc0,
+                                              beta, P.dadd, M, (bf16_t*)D, P.ldd);
       return;
     }
   }
