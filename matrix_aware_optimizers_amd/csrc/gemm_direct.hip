@@ -78,9 +78,13 @@ __device__ __forceinline__ void vm_wait_c() { __builtin_amdgcn_s_waitcnt(MAO_VMC
 
 
 
-template <typename TIn, bool BKM, bool T32>
+// DIRECT: every problem of the launch takes the direct tiled epilogue (the
+// launcher checks it), so the staged epilogue is not compiled in and its
+// register demand does not shape the rest of the kernel.
+template <typename TIn, bool BKM, bool T32, bool DIRECT = false>
 __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
   static_assert(sizeof(TIn) == 2 || (!BKM && !T32), "K x N and tiled operands are bf16 only");
+  static_assert(!DIRECT || T32, "direct-only launches are tiled");
   constexpr bool F32 = sizeof(TIn) == 4;
   constexpr int EPC = 16 / (int)sizeof(TIn);  // elements per 16-byte chunk
   constexpr int KS = ROWB / (int)sizeof(TIn);  // K elements per slice
@@ -417,6 +421,15 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
   vm_wait(0);
   asm volatile("" ::: "memory");
   __syncthreads();
+  if constexpr (DIRECT) {
+    // the accumulators stay in AGPRs, read block by block by the epilogue:
+    // held in VGPRs all at once, they leave the epilogue's addresses nowhere
+    // to live but scratch
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+  }
 
   // ---- epilogue through LDS, 32 rows of the tile at a time ------------------
   const bool diag = syrk && (tm == tn);
@@ -441,8 +454,8 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
   // zero, so it stays zero); a row-major D or Dt stops at M x N.
   const bool dt32 = (P.flags & GF_D_T32) != 0;
   if constexpr (T32 && BKM) {  // the B X products between iterations
-    if (dt32 && !syrk && !d32 && C0 == nullptr && Tt == nullptr && rs == nullptr &&
-        P.dadd == 0.f && D != nullptr) {
+    if (DIRECT || (dt32 && !syrk && !d32 && C0 == nullptr && Tt == nullptr && rs == nullptr &&
+                   P.dadd == 0.f && D != nullptr)) {
       if (alpha == 1.f)
         direct_epilogue_t32<true>(acc, m0, n0, alpha, (bf16_t*)D, P.ldd);
       else
@@ -451,8 +464,8 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
     }
   }
   if constexpr (T32 && !BKM) {  // the symmetric products X X^T and A A + b A + a I
-    if (syrk && dt32 && !d32 && rs == nullptr && D != nullptr &&
-        (C0 == nullptr || ((P.flags & GF_C0_T32) != 0 && !c32))) {
+    if (DIRECT || (syrk && dt32 && !d32 && rs == nullptr && D != nullptr &&
+                   (C0 == nullptr || ((P.flags & GF_C0_T32) != 0 && !c32)))) {
       if (C0 == nullptr && alpha == 1.f)
         direct_epilogue_t32_syrk<false, true>(acc, m0, n0, diag, alpha, nullptr, 0, 0.f, P.dadd, M,
                                               (bf16_t*)D, P.ldd);
@@ -465,6 +478,7 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
       return;
     }
   }
+  if constexpr (!DIRECT) {
   if constexpr (!T32) {  // fp32 results of the SOAP / FOAM products
     if (d32 && m0 + TB <= M && n0 + TB <= N && C0 == nullptr && rs == nullptr &&
         (D != nullptr || Tt != nullptr)) {
@@ -607,11 +621,12 @@ __device__ __forceinline__ void gemm_dl_body(const GemmArgs& args) {
     }
   }
   }  // !T32
+  }  // !DIRECT
 }
 
-template <bool BKM, bool T32>
+template <bool BKM, bool T32, bool DIRECT = false>
 __global__ __launch_bounds__(256) void gemm_bf16_dl_kernel(GemmArgs args) {
-  gemm_dl_body<bf16_t, BKM, T32>(args);
+  gemm_dl_body<bf16_t, BKM, T32, DIRECT>(args);
 }
 
 __global__ __launch_bounds__(256) void gemm_f32_dl_kernel(GemmArgs args) {
@@ -629,7 +644,26 @@ mao_status launch_gemm_f32_direct(GemmArgs& args, hipStream_t stream) {
 mao_status launch_gemm_bf16_direct(GemmArgs& args, hipStream_t stream) {
   const bool bkm = (args.p[0].flags & GF_B_KMAJOR) != 0, t32 = (args.p[0].flags & GF_T32) != 0;
   const dim3 grid(args.total_tiles), block(256);
-  if (bkm && t32)
+  // every problem's result leaves by the direct tiled epilogue: the
+  // Newton-Schulz products between iterations (the kernel's own test, per
+  // problem)
+  bool direct = t32;
+  for (int i = 0; i < args.nprob && direct; ++i) {
+    const GemmProblem& p = args.p[i];
+    const bool syrk = (p.flags & GF_SYRK) != 0;
+    direct = (p.flags & GF_D_T32) != 0 && (p.flags & GF_D_F32) == 0 && p.row_scale == nullptr &&
+             p.D != nullptr;
+    if (bkm)
+      direct = direct && !syrk && p.C0 == nullptr && p.Dt == nullptr && p.dadd == 0.f;
+    else
+      direct = direct && syrk &&
+               (p.C0 == nullptr || ((p.flags & GF_C0_T32) != 0 && (p.flags & GF_C0_F32) == 0));
+  }
+  if (direct && bkm)
+    hipLaunchKernelGGL((gemm_bf16_dl_kernel<true, true, true>), grid, block, 0, stream, args);
+  else if (direct)
+    hipLaunchKernelGGL((gemm_bf16_dl_kernel<false, true, true>), grid, block, 0, stream, args);
+  else if (bkm && t32)
     hipLaunchKernelGGL((gemm_bf16_dl_kernel<true, true>), grid, block, 0, stream, args);
   else if (bkm)
     hipLaunchKernelGGL((gemm_bf16_dl_kernel<true, false>), grid, block, 0, stream, args);
