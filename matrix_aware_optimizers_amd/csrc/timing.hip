@@ -30,7 +30,11 @@ void timing_record_begin(hipStream_t s, void** start) {
     *start = nullptr;
     return;
   }
-  hipEventRecord(e, s);
+  if (hipEventRecord(e, s) != hipSuccess) {  // nothing is timed for this launch
+    (void)hipEventDestroy(e);
+    *start = nullptr;
+    return;
+  }
   *start = (void*)e;
 }
 
@@ -38,10 +42,14 @@ void timing_record_end(hipStream_t s, void* start, int tag, double flops) {
   if (!start) return;
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) {
-    hipEventDestroy((hipEvent_t)start);
+    (void)hipEventDestroy((hipEvent_t)start);
     return;
   }
-  hipEventRecord(e, s);
+  if (hipEventRecord(e, s) != hipSuccess) {
+    (void)hipEventDestroy(e);
+    (void)hipEventDestroy((hipEvent_t)start);
+    return;
+  }
   std::lock_guard<std::mutex> lk(g_mu);
   g_records.push_back(Record{(hipEvent_t)start, e, tag, flops});
 }
@@ -75,8 +83,8 @@ MAO_API int mao_timing_collect(double* ms, int64_t* count, double* flops, int nt
       if (flops) flops[r.tag] += r.flops;
       ++n;
     }
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
   }
   return n;
 }
